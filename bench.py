@@ -1,0 +1,241 @@
+"""Benchmark of the block-scaled FP8 MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|longctx|r3|tiny]
+
+A step is one full layer forward (gate logits, routing, activation quantisation, dispatch,
+grouped GEMM1 + SwiGLU + h quantisation, grouped GEMM2, combine) over one batch of synthetic
+tokens whose inputs and quantised weights are already resident in HBM.  The default workload is
+the decode-shaped layer (256 tokens, hidden 4096, 64 experts, FFN 1408, top-6).  Prints one JSON
+line: layer tokens/s, per-stage times from HIP events recorded on the launch stream, the grouped
+GEMM's TFLOP/s, the roofline of the dominant kernel, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0       # dense fp8 MFMA (published, no sparsity)
+PEAK_FP32_TFLOPS = 78.6        # fp32 FMA without packed instructions: 256 CU x 4 SIMD x 16 lanes x 2 x 2.4 GHz
+RIDGE_FP8 = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+STAGES = ["gate_logits", "route", "quant_x", "dispatch", "gemm1_swiglu", "gemm2", "combine"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def stage_model(cfg, counts, n_active1):
+    """Algorithmic bytes and flops of each stage (inputs read once, outputs written once)."""
+    T, H, E, F, k = cfg.T, cfg.H, cfg.E, cfg.F, cfg.k
+    ab = 4 if cfg.act == "f32" else 2
+    sig = 4.0 / 128
+    rows = int(sum(counts))
+    G = cfg.groups
+    act_groups = n_active1
+    w1 = act_groups * (2 * F * H) * (1 + 4.0 / (128 * 128))
+    w2 = act_groups * (H * F) * (1 + 4.0 / (128 * 128))
+    return {
+        "gate_logits": dict(bytes=T * H * ab + E * H * 4 + T * E * 4, flops=2.0 * T * H * E, bound="alu"),
+        "route": dict(bytes=T * E * 4 + T * k * 8, flops=0.0, bound="hbm"),
+        "quant_x": dict(bytes=T * H * (ab + 1 + sig), flops=0.0, bound="hbm"),
+        "dispatch": dict(bytes=T * k * 4 + T * H * (1 + sig) + rows * H * (1 + sig) + T * k * 4 + rows * 4,
+                         flops=0.0, bound="hbm"),
+        "gemm1_swiglu": dict(bytes=rows * H * (1 + sig) + w1 + rows * F * (1 + sig), flops=4.0 * H * F * rows,
+                             bound=None),
+        "gemm2": dict(bytes=rows * F * (1 + sig) + w2 + rows * H * ab, flops=2.0 * H * F * rows, bound=None),
+        "combine": dict(bytes=rows * H * ab + T * k * 8 + T * H * ab, flops=0.0, bound="hbm"),
+        "_rows": rows, "_groups": G,
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}): the layer's multi-GPU form (expert "
+              "parallel dispatch/combine over xGMI) is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_scaled_fp8_top_amd as M
+    import synth
+    from block_scaled_fp8_top_amd.layer import MoELayer, MoELayerWeights, quantize_expert_weights
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    M.lib()  # fail loudly if the HIP library is missing
+    dev = "cuda"
+    cfg = synth.CONFIGS[a.workload]
+    sf = 0 if cfg.score_fn == "softmax" else 1
+    rcfg = M.router_cfg(cfg.E, cfg.k, sf, cfg.renorm, cfg.n_group, cfg.topk_group, cfg.group_score_topk)
+    wg, b = synth.make_gate(cfg, 0, dev)
+    w1q, w1s, w2q, w2s = quantize_expert_weights(cfg.groups, cfg.H, cfg.F,
+                                                 lambda g: synth.make_expert(cfg, g, 0, dev), device=dev)
+    weights = MoELayerWeights(wg=wg, bias=b, w1q=w1q, w1s=w1s, w2q=w2q, w2s=w2s, cfg=rcfg, shared=cfg.shared)
+    act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
+    layer = MoELayer(weights, cfg.T, act, dev)
+    x = synth.make_x(cfg, dev)
+    torch.cuda.synchronize()
+
+    for _ in range(a.warmup):
+        layer.forward(x)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, HIP events between stages on the launch stream
+    K = a.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        layer.forward(x, events=ev[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    stage_ms = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)]))
+                for i, name in enumerate(STAGES)}
+
+    counts = layer.disp.counts.cpu().numpy()
+    n_active = int((counts > 0).sum())
+    model = stage_model(cfg, counts, n_active)
+    stages = {}
+    for name in STAGES:
+        m = model[name]
+        t = stage_ms[name] * 1e-3
+        d = {"ms": round(stage_ms[name], 4), "GB_s": round(m["bytes"] / t / 1e9, 1)}
+        if m["flops"]:
+            d["TFLOP_s"] = round(m["flops"] / t / 1e12, 2)
+        if name.startswith("gemm"):
+            intensity = m["flops"] / m["bytes"]
+            d["bound"] = "mfma" if intensity >= RIDGE_FP8 else "hbm"
+            d["frac"] = round((m["flops"] / t / 1e12 / PEAK_FP8_TFLOPS) if d["bound"] == "mfma"
+                              else (m["bytes"] / t / 1e9 / PEAK_HBM_GBS), 4)
+        elif m["bound"] == "alu":
+            d["bound"] = "alu"
+            d["frac"] = round(m["flops"] / t / 1e12 / PEAK_FP32_TFLOPS, 4)
+        else:
+            d["bound"] = "hbm"
+            d["frac"] = round(m["bytes"] / t / 1e9 / PEAK_HBM_GBS, 4)
+        stages[name] = d
+
+    gemm_ms = stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]
+    gemm_flops = model["gemm1_swiglu"]["flops"] + model["gemm2"]["flops"]
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    dom = max(STAGES, key=lambda n: stage_ms[n])
+    dm = model[dom]
+    dt = stage_ms[dom] * 1e-3
+    bound = stages[dom]["bound"]
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(dm["flops"] / dt / 1e12, 2), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s"}
+    elif bound == "alu":
+        roof = {"bound": "alu", "achieved": round(dm["flops"] / dt / 1e12, 2), "peak": PEAK_FP32_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(dm["bytes"] / dt / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = dom
+
+    if a.copy_probe_mb:
+        n = a.copy_probe_mb * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, x, dev)
+
+    tokens_per_s = cfg.T / (ms_per_step * 1e-3)
+    line = {
+        "metric": "MoE layer tokens/s + grouped FP8 GEMM TFLOP/s (% of fp8 MFMA peak), 1 GPU",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 x fp8-e4m3 -> fp32 (GEMM); fp32 router; " + ("bf16" if cfg.act == "bf16" else "fp32") + " activations",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) weights, random-init)",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
+                   "shared_experts": int(cfg.shared), "ffn": cfg.F, "top_k": cfg.k, "score": cfg.score_fn,
+                   "rows": model["_rows"], "active_experts": n_active, "parallelism": "none (1 GPU)"},
+        "gemm_tflops": round(gemm_tflops, 2),
+        "gemm_frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+        "stages": stages,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+def cpu_baseline(cfg, x, dev):
+    """The CPU oracle on a bounded sample of the same workload, timed on this host: the whole
+    batch for small layers, else a seeded token sample evaluated per token."""
+    import numpy as np
+
+    import oracle as O
+    import oracle.layer as L
+    import synth
+
+    wg, b = synth.make_gate(cfg, 0, dev)
+    rc = O.router_cfg(cfg.E, cfg.k, 0 if cfg.score_fn == "softmax" else 1, cfg.renorm, cfg.n_group,
+                      cfg.topk_group, cfg.group_score_topk)
+
+    def expert(e):
+        w1, w2 = synth.make_expert(cfg, e, 0, dev)
+        return L.quantize_expert(w1.cpu().numpy(), w2.cpu().numpy())
+
+    ol = L.OracleLayer(wg=wg.cpu().numpy(), bias=None if b is None else b.cpu().numpy(), cfg=rc, shared=cfg.shared,
+                       act=cfg.act, F=cfg.F, expert=expert)
+    xh = x.float().cpu().numpy()
+    if cfg.T <= 256:
+        toks = np.arange(cfg.T)
+        for g in range(cfg.groups):          # weight quantisation is offline on the GPU side too
+            ol.get(g)
+        t0 = time.perf_counter()
+        L.forward_dispatch(ol, xh)
+        dt = time.perf_counter() - t0
+        sample = f"whole batch ({cfg.T} tokens), dispatch path, expert weights pre-quantised"
+    else:
+        n = 4
+        toks = synth.sample_tokens(cfg.T, n, cfg.seed + 99)
+        pre = L.forward_sampled(ol, xh[toks[:1]])   # warm the expert cache for token 0 only
+        del pre
+        r0 = O.moe_route(O.moe_gate_logits(xh[toks], ol.wg, ol.bias), rc)[0]
+        for e in set(r0.reshape(-1).tolist()) | ({cfg.E} if cfg.shared else set()):
+            ol.get(e)
+        t0 = time.perf_counter()
+        L.forward_sampled(ol, xh[toks])
+        dt = time.perf_counter() - t0
+        sample = f"{len(toks)} seeded tokens of {cfg.T}, per-token path, expert weights pre-quantised"
+    return {"value": round(len(toks) / dt, 3), "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

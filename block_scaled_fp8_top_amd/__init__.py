@@ -1,0 +1,325 @@
+"""Python binding of libmoe_fp8 (block-scaled FP8 Mixture-of-Experts layer for MI355X / gfx950).
+
+Argument marshalling only: every function checks devices, dtypes, shapes and contiguity, then
+passes raw device pointers and the current HIP stream to the C ABI declared in
+``include/moe_fp8.h``.  All computation happens in the HIP kernels; there is no fallback.  If the
+library has not been built, importing works but the first call raises ``MoeLibraryMissing``
+(build with ``python -m block_scaled_fp8_top_amd.build``).
+
+torch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_fp8.so")
+
+MOE_OK = 0
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_EPI_STORE, MOE_EPI_SWIGLU_QUANT = 0, 1
+MOE_OP_DISPATCH, MOE_OP_GROUPED_GEMM = 1, 2
+
+EXPORTED = ("moe_gate_logits", "moe_route", "moe_replay_route", "moe_router_score_eval", "moe_quant_fp8_block",
+            "moe_dispatch", "moe_grouped_gemm_fp8", "moe_combine", "moe_workspace_bytes", "moe_status_str",
+            "moe_version")
+
+
+class MoeLibraryMissing(RuntimeError):
+    pass
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: status {code} ({status_str(code)})")
+        self.code = code
+
+
+class RouterCfg(ctypes.Structure):
+    _fields_ = [("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("score_fn", ctypes.c_int32),
+                ("renormalize", ctypes.c_int32), ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
+                ("group_score_topk", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded shared library (raises MoeLibraryMissing if it was never built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise MoeLibraryMissing(f"{LIB_PATH} not found; build it with `python -m block_scaled_fp8_top_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    cfgp = ctypes.POINTER(RouterCfg)
+    sig = {
+        "moe_gate_logits": [P, ctypes.c_int, P, P, I64, I32, I32, P, P],
+        "moe_route": [P, I64, cfgp, P, P, P, I64, P],
+        "moe_replay_route": [P, I64, cfgp, P, I64, P, P, P, P],
+        "moe_router_score_eval": [P, I64, ctypes.c_int, P, P],
+        "moe_quant_fp8_block": [P, ctypes.c_int, I64, I64, I32, I32, P, P, P],
+        "moe_dispatch": [P, I64, I32, I32, I32, P, P, I32, P, P, P, P, P, P, P, SZ, P],
+        "moe_grouped_gemm_fp8": [P, P, P, I32, I64, P, P, I32, I32, I32, P, ctypes.c_int, P, P, SZ, P],
+        "moe_combine": [P, ctypes.c_int, P, P, I64, I32, I32, P, P, ctypes.c_int, P],
+        "moe_workspace_bytes": [ctypes.c_int, I64, I32, I32, I32, I32],
+        "moe_status_str": [ctypes.c_int],
+        "moe_version": [],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    L.moe_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_status_str.restype = ctypes.c_char_p
+    L.moe_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_str(code: int) -> str:
+    return lib().moe_status_str(int(code)).decode()
+
+
+def version() -> str:
+    return lib().moe_version().decode()
+
+
+def workspace_bytes(op: int, rows_or_T: int, k: int, E: int, N: int = 0, K: int = 0) -> int:
+    return int(lib().moe_workspace_bytes(op, rows_or_T, k, E, N, K))
+
+
+# ----------------------------------------------------------------------------- marshalling helpers
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _act_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"activation dtype {t.dtype} unsupported (float32 or bfloat16)")
+
+
+def _check(code: int, what: str):
+    if code != MOE_OK:
+        raise MoeError(code, what)
+
+
+FP8 = torch.uint8  # e4m3 codes are carried as raw bytes
+
+
+def router_cfg(num_experts, top_k, score_fn, renormalize, n_group=1, topk_group=1, group_score_topk=2) -> RouterCfg:
+    sf = score_fn if isinstance(score_fn, int) else (MOE_SCORE_SOFTMAX if score_fn == "softmax" else MOE_SCORE_SIGMOID)
+    return RouterCfg(num_experts, top_k, sf, int(bool(renormalize)), n_group, topk_group, group_score_topk)
+
+
+# ----------------------------------------------------------------------------- the seven calls
+def moe_gate_logits(x: torch.Tensor, wg: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    T, H = x.shape
+    E = wg.shape[0]
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    _dev(wg, "wg", torch.float32, (E, H))
+    if bias is not None:
+        _dev(bias, "bias", torch.float32, (E,))
+    out = torch.empty((T, E), dtype=torch.float32, device=x.device) if out is None else _dev(out, "out", torch.float32, (T, E))
+    _check(lib().moe_gate_logits(_p(x), _act_code(x), _p(wg), _p(bias), T, H, E, _p(out), _stream(stream)),
+           "moe_gate_logits")
+    return out
+
+
+def moe_route(logits: torch.Tensor, cfg: RouterCfg, record: Optional[torch.Tensor] = None, topk_idx=None,
+              topk_w=None, stream=None):
+    """Returns (topk_idx [T,k] int32, topk_w [T,k] fp32).  ``record`` is one layer of the routing
+    payload, an int32 [k, seq_len>=T] view (contiguous rows)."""
+    T, E = logits.shape
+    _dev(logits, "logits", torch.float32)
+    if E != cfg.num_experts:
+        raise ValueError("logits width != num_experts")
+    k = cfg.top_k
+    idx = torch.empty((T, k), dtype=torch.int32, device=logits.device) if topk_idx is None else _dev(topk_idx, "topk_idx", torch.int32, (T, k))
+    w = torch.empty((T, k), dtype=torch.float32, device=logits.device) if topk_w is None else _dev(topk_w, "topk_w", torch.float32, (T, k))
+    rec_ptr, rec_ld = None, 0
+    if record is not None:
+        if record.device.type != "cuda" or record.dtype != torch.int32 or record.dim() != 2 or record.shape[0] != k \
+                or record.stride(1) != 1:
+            raise ValueError("record must be a cuda int32 [k, seq_len] view with unit column stride")
+        rec_ptr, rec_ld = _p(record), record.stride(0)
+        if record.shape[1] < T:
+            raise ValueError("record seq_len < T")
+    _check(lib().moe_route(_p(logits), T, ctypes.byref(cfg), _p(idx), _p(w), rec_ptr, rec_ld, _stream(stream)),
+           "moe_route")
+    return idx, w
+
+
+def moe_replay_route(logits: torch.Tensor, cfg: RouterCfg, replay: torch.Tensor, bad_count: Optional[torch.Tensor] = None,
+                     topk_idx=None, topk_w=None, stream=None):
+    """Returns (topk_idx, topk_w).  ``replay``: int32 [k, seq_len>=T] view of one payload layer;
+    ``bad_count``: optional cuda int32 [1] accumulator of rejected tokens."""
+    T, E = logits.shape
+    _dev(logits, "logits", torch.float32)
+    k = cfg.top_k
+    if replay.device.type != "cuda" or replay.dtype != torch.int32 or replay.dim() != 2 or replay.shape[0] != k \
+            or replay.stride(1) != 1 or replay.shape[1] < T:
+        raise ValueError("replay must be a cuda int32 [k, seq_len>=T] view with unit column stride")
+    if bad_count is not None:
+        _dev(bad_count, "bad_count", torch.int32, (1,))
+    idx = torch.empty((T, k), dtype=torch.int32, device=logits.device) if topk_idx is None else _dev(topk_idx, "topk_idx", torch.int32, (T, k))
+    w = torch.empty((T, k), dtype=torch.float32, device=logits.device) if topk_w is None else _dev(topk_w, "topk_w", torch.float32, (T, k))
+    _check(lib().moe_replay_route(_p(logits), T, ctypes.byref(cfg), _p(replay), replay.stride(0), _p(idx), _p(w),
+                                  _p(bad_count), _stream(stream)), "moe_replay_route")
+    return idx, w
+
+
+def moe_router_score_eval(x: torch.Tensor, score_fn, out=None, stream=None) -> torch.Tensor:
+    """The router's fixed exp (score_fn softmax) or sigmoid, elementwise on fp32 x."""
+    _dev(x, "x", torch.float32)
+    sf = score_fn if isinstance(score_fn, int) else (MOE_SCORE_SOFTMAX if score_fn == "softmax" else MOE_SCORE_SIGMOID)
+    out = torch.empty_like(x) if out is None else _dev(out, "out", torch.float32, x.shape)
+    _check(lib().moe_router_score_eval(_p(x), x.numel(), sf, _p(out), _stream(stream)), "moe_router_score_eval")
+    return out
+
+
+def moe_quant_fp8_block(x: torch.Tensor, block_rows: int, q=None, scales=None, stream=None):
+    """x: [rows, cols] or [batch, rows, cols] fp32/bf16 -> (codes uint8 same shape, scales fp32)."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    xx = x if x.dim() == 3 else x.unsqueeze(0)
+    B, R, C = xx.shape
+    if block_rows not in (1, 128) or C % 128 or R % block_rows:
+        raise ValueError("cols must be a multiple of 128 and rows a multiple of block_rows (1 or 128)")
+    sshape = (B, R // block_rows, C // 128) if x.dim() == 3 else (R // block_rows, C // 128)
+    q = torch.empty(x.shape, dtype=FP8, device=x.device) if q is None else _dev(q, "q", FP8, x.shape)
+    scales = torch.empty(sshape, dtype=torch.float32, device=x.device) if scales is None else _dev(scales, "scales", torch.float32, sshape)
+    _check(lib().moe_quant_fp8_block(_p(x), _act_code(x), B, R, C, block_rows, _p(q), _p(scales), _stream(stream)),
+           "moe_quant_fp8_block")
+    return q, scales
+
+
+@dataclass
+class Dispatched:
+    counts: torch.Tensor      # [G] int32
+    offsets: torch.Tensor     # [G+1] int32
+    dest_row: torch.Tensor    # [T,k] int32
+    src_token: torch.Tensor   # [max_rows] int32
+    aq: Optional[torch.Tensor]   # [max_rows, H] uint8 (rows beyond offsets[G] unwritten)
+    as_: Optional[torch.Tensor]  # [max_rows, H/128] fp32
+    max_rows: int
+
+
+def moe_dispatch(topk_idx: torch.Tensor, num_experts: int, append_shared: bool, xq: Optional[torch.Tensor] = None,
+                 xs: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                 out: Optional[Dispatched] = None, stream=None) -> Dispatched:
+    T, k = topk_idx.shape
+    _dev(topk_idx, "topk_idx", torch.int32)
+    dev = topk_idx.device
+    G = num_experts + (1 if append_shared else 0)
+    max_rows = T * k + (T if append_shared else 0)
+    H = 0
+    if xq is not None:
+        H = xq.shape[1]
+        _dev(xq, "xq", FP8, (T, H))
+        _dev(xs, "xs", torch.float32, (T, H // 128))
+    ws_need = workspace_bytes(MOE_OP_DISPATCH, T, k, num_experts)
+    if workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < ws_need:
+        raise ValueError("workspace too small")
+    if out is None:
+        out = Dispatched(
+            counts=torch.empty(G, dtype=torch.int32, device=dev),
+            offsets=torch.empty(G + 1, dtype=torch.int32, device=dev),
+            dest_row=torch.empty((T, k), dtype=torch.int32, device=dev),
+            src_token=torch.empty(max(max_rows, 1), dtype=torch.int32, device=dev),
+            aq=torch.empty((max_rows, H), dtype=FP8, device=dev) if xq is not None else None,
+            as_=torch.empty((max_rows, H // 128), dtype=torch.float32, device=dev) if xq is not None else None,
+            max_rows=max_rows)
+    _check(lib().moe_dispatch(_p(topk_idx), T, k, num_experts, int(bool(append_shared)), _p(xq), _p(xs), H,
+                              _p(out.counts), _p(out.offsets), _p(out.dest_row), _p(out.src_token), _p(out.aq),
+                              _p(out.as_), _p(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(stream)), "moe_dispatch")
+    return out
+
+
+def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tensor, b: torch.Tensor, bs: torch.Tensor,
+                         epilogue: int = MOE_EPI_STORE, out_dtype=torch.bfloat16, out=None, out_scales=None,
+                         workspace: Optional[torch.Tensor] = None, stream=None):
+    """a [max_rows,K] uint8, as_ [max_rows,K/128], offsets [G+1] (device), b [G,N,K] uint8, bs [G,N/128,K/128].
+    STORE -> out [max_rows,N] (bf16/fp32); SWIGLU_QUANT -> (h codes [max_rows,N/2] uint8, scales [max_rows,N/256])."""
+    max_rows, K = a.shape
+    G, N, Kb = b.shape
+    if Kb != K:
+        raise ValueError("K mismatch")
+    _dev(a, "a", FP8)
+    _dev(as_, "as", torch.float32, (max_rows, K // 128))
+    _dev(offsets, "offsets", torch.int32, (G + 1,))
+    _dev(b, "b", FP8)
+    _dev(bs, "bs", torch.float32, (G, N // 128, K // 128))
+    dev = a.device
+    ws_need = workspace_bytes(MOE_OP_GROUPED_GEMM, max_rows, 0, G, N, K)
+    if workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < ws_need:
+        raise ValueError("workspace too small")
+    if epilogue == MOE_EPI_STORE:
+        code = MOE_BF16 if out_dtype == torch.bfloat16 else MOE_F32
+        out = torch.empty((max_rows, N), dtype=out_dtype, device=dev) if out is None else _dev(out, "out", out_dtype, (max_rows, N))
+        osc = None
+    else:
+        code = MOE_FP8_E4M3
+        F = N // 2
+        out = torch.empty((max_rows, F), dtype=FP8, device=dev) if out is None else _dev(out, "out", FP8, (max_rows, F))
+        osc = torch.empty((max_rows, F // 128), dtype=torch.float32, device=dev) if out_scales is None else \
+            _dev(out_scales, "out_scales", torch.float32, (max_rows, F // 128))
+    _check(lib().moe_grouped_gemm_fp8(_p(a), _p(as_), _p(offsets), G, max_rows, _p(b), _p(bs), N, K, epilogue, _p(out),
+                                      code, _p(osc), _p(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)), "moe_grouped_gemm_fp8")
+    return out if epilogue == MOE_EPI_STORE else (out, osc)
+
+
+def moe_combine(y: torch.Tensor, dest_row: torch.Tensor, topk_w: torch.Tensor, shared_first_row: Optional[torch.Tensor] = None,
+                out_dtype=None, out=None, stream=None) -> torch.Tensor:
+    """out[t] = sum_j w[t,j] y[dest_row[t,j]] (+ y[shared_first_row + t]); shared_first_row is a
+    one-element device int32 view (e.g. offsets[E:E+1])."""
+    _dev(y, "y", (torch.float32, torch.bfloat16))
+    T, k = dest_row.shape
+    H = y.shape[1]
+    _dev(dest_row, "dest_row", torch.int32)
+    _dev(topk_w, "topk_w", torch.float32, (T, k))
+    if shared_first_row is not None:
+        _dev(shared_first_row, "shared_first_row", torch.int32, (1,))
+    od = y.dtype if out_dtype is None else out_dtype
+    out = torch.empty((T, H), dtype=od, device=y.device) if out is None else _dev(out, "out", od, (T, H))
+    _check(lib().moe_combine(_p(y), _act_code(y), _p(dest_row), _p(topk_w), T, k, H, _p(shared_first_row), _p(out),
+                             _act_code(out), _stream(stream)), "moe_combine")
+    return out
+
+
+from .layer import MoELayerWeights, MoELayer, quantize_expert_weights  # noqa: E402,F401

@@ -1,0 +1,90 @@
+// Combine: out[t,:] = sum_j w[t,j] * y[dest_row[t,j],:] (+ y[shared_first_row + t,:]).
+//
+// One workgroup per token; each thread owns 8 consecutive columns (16-byte bf16 or 2 x 16-byte
+// fp32 loads).  Accumulation is fp32 with fused multiply-adds in slot order, the shared row
+// added last, one rounding to the output dtype.  No atomics: each output element has one owner.
+#include "common.h"
+
+namespace {
+
+template <bool YBF16>
+__device__ __forceinline__ void load8y(const void* y, int64_t off, float (&v)[8]) {
+  if (YBF16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(y) + off);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(w[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(y) + off);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+template <bool YBF16, bool OBF16>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y, const int32_t* __restrict__ dest,
+                                                      const float* __restrict__ w, int k, int H,
+                                                      const int32_t* __restrict__ shared_first_row,
+                                                      void* __restrict__ out) {
+  const int64_t t = blockIdx.x;
+  const int32_t* d = dest + t * k;
+  const float* wt = w + t * k;
+  const int64_t srow = shared_first_row ? (int64_t)(*shared_first_row) + t : -1;
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int32_t row = d[j];
+      if (row < 0) continue;
+      const float wj = wt[j];
+      float v[8];
+      load8y<YBF16>(y, (int64_t)row * H + c, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wj, v[q], acc[q]);
+    }
+    if (srow >= 0) {
+      float v[8];
+      load8y<YBF16>(y, srow * H + c, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = acc[q] + v[q];
+    }
+    if (OBF16) {
+      uint32_t p[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) p[q] = (uint32_t)f32_to_bf16(acc[2 * q]) | ((uint32_t)f32_to_bf16(acc[2 * q + 1]) << 16);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + t * H + c) = make_uint4(p[0], p[1], p[2], p[3]);
+    } else {
+      float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + t * H + c);
+      o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" int moe_combine(const void* y, int y_dtype, const int32_t* dest_row, const float* topk_w, int64_t T,
+                           int32_t k, int32_t H, const int32_t* shared_first_row, void* out, int out_dtype,
+                           void* stream) {
+  if (T < 0 || k < 1 || k > 64 || H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
+  if ((y_dtype != MOE_BF16 && y_dtype != MOE_F32) || (out_dtype != MOE_BF16 && out_dtype != MOE_F32))
+    return MOE_ERR_DTYPE;
+  if (T == 0) return MOE_OK;
+  if (!y || !dest_row || !topk_w || !out) return MOE_ERR_NULL;
+  if (T > INT32_MAX) return MOE_ERR_SHAPE;
+  hipStream_t st = as_stream(stream);
+  const unsigned grid = (unsigned)T;
+  const bool yb = y_dtype == MOE_BF16, ob = out_dtype == MOE_BF16;
+  if (yb && ob)
+    combine_kernel<true, true><<<grid, 256, 0, st>>>(y, dest_row, topk_w, k, H, shared_first_row, out);
+  else if (yb)
+    combine_kernel<true, false><<<grid, 256, 0, st>>>(y, dest_row, topk_w, k, H, shared_first_row, out);
+  else if (ob)
+    combine_kernel<false, true><<<grid, 256, 0, st>>>(y, dest_row, topk_w, k, H, shared_first_row, out);
+  else
+    combine_kernel<false, false><<<grid, 256, 0, st>>>(y, dest_row, topk_w, k, H, shared_first_row, out);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}

@@ -1,0 +1,83 @@
+// Device and host helpers shared by the HIP kernels of libmoe_fp8 (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_fp8.h"
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
+
+#define MOE_CHECK_LAUNCH()                                  \
+  do {                                                      \
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+static inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ------------------------------------------------------------------------------------------
+// bf16 <-> fp32.  bf16 is the upper half of an fp32 pattern, so widening is exact; narrowing
+// rounds to nearest even (finite inputs).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ------------------------------------------------------------------------------------------
+// OCP FP8 E4M3 encode: round to nearest even, saturating to +-448, sign of zero kept.
+// gfx950's v_cvt_pk_fp8_f32 rounds to nearest even on [-448, 448] but returns NaN beyond 464,
+// so the value is clamped to the largest finite magnitude first (clamping commutes with
+// saturating rounding: every |v| >= 448 maps to 448 either way).  fminf/fmaxf keep -0.
+__device__ __forceinline__ float e4m3_clamp(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+
+// two values -> low 16 bits of the result (byte 0 = a, byte 1 = b)
+__device__ __forceinline__ uint32_t e4m3_pack2(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false) & 0xFFFFu;
+}
+
+// four values -> one 32-bit word (byte i = value i)
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), w, true);
+  return (uint32_t)w;
+}
+
+// ------------------------------------------------------------------------------------------
+// Fixed fp32 exponential used by the router (softmax and sigmoid scores), so that scores that
+// feed routing decisions are reproducible bit for bit: Cody & Waite (1980) reduction
+// x = n*ln2 + r with ln2 = hi + lo (hi has few enough bits that n*hi is exact for |n| <= 127),
+// degree-6 Taylor polynomial of e^r by Horner's rule with fused multiply-adds, exact scaling by
+// 2^n.  The input is clamped to [-86, 88] so the result is a normal, finite fp32 number.
+// Every step is one IEEE fp32 operation; the build uses -ffp-contract=off.
+__device__ __forceinline__ float router_exp(float x) {
+  x = fminf(fmaxf(x, -86.0f), 88.0f);
+  const float n = rintf(x * 0x1.715476p+0f);
+  float r = __builtin_fmaf(-n, 0x1.62e400p-1f, x);
+  r = __builtin_fmaf(-n, 0x1.7f7d1cp-20f, r);
+  float p = 0x1.6c16c2p-10f;
+  p = __builtin_fmaf(p, r, 0x1.111112p-7f);
+  p = __builtin_fmaf(p, r, 0x1.555556p-5f);
+  p = __builtin_fmaf(p, r, 0x1.555556p-3f);
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  return p * __uint_as_float((uint32_t)((int)n + 127) << 23);
+}
+
+__device__ __forceinline__ float router_sigmoid(float z) { return 1.0f / (1.0f + router_exp(-z)); }
+
+// ------------------------------------------------------------------------------------------
+// wave64 helpers
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
+static inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }

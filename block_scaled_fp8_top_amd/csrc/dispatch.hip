@@ -1,0 +1,198 @@
+// Dispatch: a stable counting sort of the flattened [T,k] expert ids into expert-contiguous
+// groups, then the permutation of the quantised activation rows and their scales.
+//
+//   1. count:   the T*k slots are cut into chunks of CHUNK; each chunk's expert histogram goes to
+//               the workspace (LDS integer atomics: exact counts, order-free).
+//   2. scan:    one workgroup turns the per-chunk histograms into expert totals, the exclusive
+//               prefix `offsets`, and each chunk's starting row per expert.
+//   3. scatter: one wavefront per chunk walks its slots in order, 64 at a time; lanes holding the
+//               same expert find each other with ballots over the bits of the expert id, so each
+//               slot's row is (chunk base) + (earlier slots of the chunk with that expert) --
+//               exactly the stable order.  Also fills the shared expert's rows.
+//   4. permute: rows [0, offsets[G]) copy xq[src_token[row]] and xs[src_token[row]].
+#include <algorithm>
+
+#include "common.h"
+
+namespace {
+
+constexpr int CHUNK = 1024;   // slots per chunk
+constexpr int MAXE = 1024;
+
+__global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ idx, int64_t nslots, int E,
+                                                    int32_t* __restrict__ chunk_counts) {
+  __shared__ int hist[MAXE];
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int64_t s0 = (int64_t)blockIdx.x * CHUNK;
+  for (int i = threadIdx.x; i < CHUNK; i += 256) {
+    const int64_t s = s0 + i;
+    if (s < nslots) {
+      const int e = idx[s];
+      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// one workgroup of 1024 threads; thread e owns expert e
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ chunk_counts, int nchunks, int E,
+                                                    int append_shared, int64_t T, int32_t* __restrict__ chunk_base,
+                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  __shared__ int part[1024];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = chunk_counts[(int64_t)c * E + e];
+      chunk_base[(int64_t)c * E + e] = total;
+      total += v;
+    }
+  }
+  // inclusive block scan of totals over e (Hillis-Steele; integers, so order does not matter)
+  part[e] = total;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = e >= o ? part[e - o] : 0;
+    __syncthreads();
+    part[e] += v;
+    __syncthreads();
+  }
+  const int excl = part[e] - total;
+  if (e < E) {
+    counts[e] = total;
+    offsets[e] = excl;
+    for (int c = 0; c < nchunks; ++c) chunk_base[(int64_t)c * E + e] += excl;
+  }
+  if (e == 0) {
+    const int routed = part[E - 1];
+    offsets[E] = routed;
+    if (append_shared) {
+      counts[E] = (int32_t)T;
+      offsets[E + 1] = routed + (int32_t)T;
+    }
+  }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ idx, int64_t nslots, int k, int E,
+                                                     int64_t T, int append_shared,
+                                                     const int32_t* __restrict__ chunk_base,
+                                                     const int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token) {
+  __shared__ int running[MAXE];
+  const int lane = threadIdx.x;
+  const int chunk = blockIdx.x;
+  for (int e = lane; e < E; e += 64) running[e] = chunk_base[(int64_t)chunk * E + e];
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t s0 = (int64_t)chunk * CHUNK;
+  for (int i = 0; i < CHUNK; i += 64) {
+    const int64_t s = s0 + i + lane;
+    const bool in = s < nslots;
+    const int e = in ? idx[s] : -1;
+    const bool valid = in && e >= 0 && e < E;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < BITS; ++b) {
+      const uint64_t m = __ballot(valid && ((e >> b) & 1));
+      peers &= ((e >> b) & 1) ? m : ~m;
+    }
+    int pos = -1;
+    if (valid) {
+      const int rank = __popcll(peers & lt);
+      pos = running[e] + rank;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (valid && (peers & lt) == 0) running[e] += __popcll(peers);  // group leader advances the base
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (in) dest_row[s] = pos;
+    if (valid) src_token[pos] = (int32_t)(s / k);
+    if (s0 + i + 64 >= nslots) break;
+  }
+  if (append_shared) {
+    const int32_t base = offsets[E];
+    for (int64_t t = (int64_t)chunk * 64 + lane; t < T; t += (int64_t)gridDim.x * 64) src_token[base + t] = (int32_t)t;
+  }
+}
+
+// rows [0, offsets[G]): one row per 64-lane group, 16-byte copies
+__global__ __launch_bounds__(256) void permute_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
+                                                      int H, const int32_t* __restrict__ src_token,
+                                                      const int32_t* __restrict__ total_rows, int64_t max_rows,
+                                                      uint8_t* __restrict__ aq, float* __restrict__ as) {
+  const int64_t rows = *total_rows;
+  const int lane = threadIdx.x & 63;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64; row < rows && row < max_rows;
+       row += (int64_t)gridDim.x * 4) {
+    const int64_t t = src_token[row];
+    const uint4* src = reinterpret_cast<const uint4*>(xq + t * H);
+    uint4* dst = reinterpret_cast<uint4*>(aq + row * H);
+    for (int c = lane; c < H / 16; c += 64) dst[c] = src[c];
+    const int nsc = H / 128;
+    for (int c = lane; c < nsc; c += 64) as[row * nsc + c] = xs[t * nsc + c];
+  }
+}
+
+int64_t nchunks_for(int64_t T, int k) { return ceil_div64(T * k, CHUNK); }
+
+}  // namespace
+
+size_t moe_dispatch_workspace(int64_t T, int32_t k, int32_t E) {
+  return (size_t)(2 * nchunks_for(T, k) * (int64_t)E * 4 + 256);
+}
+
+extern "C" int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_t append_shared,
+                            const uint8_t* xq, const float* xs, int32_t H, int32_t* counts, int32_t* offsets,
+                            int32_t* dest_row, int32_t* src_token, uint8_t* aq, float* as, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (T < 0 || k < 1 || k > 64 || E < 1 || E > MAXE) return MOE_ERR_SHAPE;
+  if (T * (int64_t)k + T > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
+  const bool copy_rows = xq || aq;
+  if (copy_rows && (H < 128 || H % 128 != 0)) return MOE_ERR_SHAPE;
+  if (!counts || !offsets) return MOE_ERR_NULL;
+  if (T > 0 && (!topk_idx || !dest_row || !src_token)) return MOE_ERR_NULL;
+  if (copy_rows && (!xq || !xs || !aq || !as)) return MOE_ERR_NULL;
+  const int64_t nch = nchunks_for(T, k);
+  if (!workspace || workspace_bytes < moe_dispatch_workspace(T, k, E)) return MOE_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  int32_t* chunk_counts = reinterpret_cast<int32_t*>(workspace);
+  int32_t* chunk_base = chunk_counts + nch * E;
+  const int64_t nslots = T * k;
+  if (nch > 0) {
+    count_kernel<<<(unsigned)nch, 256, 0, st>>>(topk_idx, nslots, E, chunk_counts);
+    MOE_CHECK_LAUNCH();
+  }
+  scan_kernel<<<1, 1024, 0, st>>>(chunk_counts, (int)nch, E, append_shared, T, chunk_base, counts, offsets);
+  MOE_CHECK_LAUNCH();
+  if (nch > 0) {
+    int bits = 1;
+    while ((1 << bits) < E) ++bits;
+    const unsigned g = (unsigned)nch;
+    switch (bits) {
+#define CASE_BITS(B)                                                                                                  \
+  case B:                                                                                                             \
+    scatter_kernel<B><<<g, 64, 0, st>>>(topk_idx, nslots, k, E, T, append_shared, chunk_base, offsets, dest_row,      \
+                                        src_token);                                                                   \
+    break;
+      CASE_BITS(1) CASE_BITS(2) CASE_BITS(3) CASE_BITS(4) CASE_BITS(5)
+      CASE_BITS(6) CASE_BITS(7) CASE_BITS(8) CASE_BITS(9) CASE_BITS(10)
+#undef CASE_BITS
+      default:
+        return MOE_ERR_SHAPE;
+    }
+    MOE_CHECK_LAUNCH();
+  }
+  if (copy_rows && T > 0) {
+    const int G = E + (append_shared ? 1 : 0);
+    const int64_t max_rows = nslots + (append_shared ? T : 0);
+    const int64_t grid = std::min<int64_t>(ceil_div64(max_rows, 4), 65536);
+    permute_kernel<<<(unsigned)grid, 256, 0, st>>>(xq, xs, H, src_token, offsets + G, max_rows, aq, as);
+    MOE_CHECK_LAUNCH();
+  }
+  return MOE_OK;
+}

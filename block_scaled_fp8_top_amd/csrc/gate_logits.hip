@@ -1,0 +1,144 @@
+// Router gate projection: logits[t,e] = fp32 fma chain over h ascending (+ bias).
+//
+// The chain order is part of the contract (it makes routing reproducible bit for bit), so the
+// contraction cannot use matrix cores or split K: it is fp32 VALU work.  Each thread owns a
+// TT x TE register tile of outputs and walks h in order; x and Wg are staged through LDS in
+// chunks of HC columns (x converted to fp32 on the way), padded so that the 16-byte LDS reads of
+// different rows fall in different banks.
+#include "common.h"
+
+namespace {
+
+constexpr int HC = 32;        // h columns per LDS chunk
+constexpr int PAD = HC + 4;   // padded LDS row (floats)
+constexpr int NT = 256;       // threads per workgroup: 16 (experts) x 16 (tokens)
+
+template <int TT, int TE, bool BF16>
+__global__ __launch_bounds__(NT) void gate_logits_kernel(const void* __restrict__ xv, const float* __restrict__ wg,
+                                                         const float* __restrict__ bias, int64_t T, int H, int E,
+                                                         float* __restrict__ z) {
+  constexpr int BT = 16 * TT, BE = 16 * TE;
+  __shared__ __attribute__((aligned(16))) float xs[BT * PAD];
+  __shared__ __attribute__((aligned(16))) float ws[BE * PAD];
+  const int tid = threadIdx.x;
+  const int tx = tid % 16, ty = tid / 16;
+  const int64_t t0 = (int64_t)blockIdx.x * BT;
+  const int e0 = blockIdx.y * BE;
+
+  float acc[TT][TE];
+#pragma unroll
+  for (int i = 0; i < TT; ++i)
+#pragma unroll
+    for (int j = 0; j < TE; ++j) acc[i][j] = 0.0f;
+
+  for (int h0 = 0; h0 < H; h0 += HC) {
+    const int hc = min(HC, H - h0);  // multiple of 8
+    // ---- stage x[t0 .. t0+BT) x [h0 .. h0+HC) as fp32, 8 values per item
+    for (int it = tid; it < BT * (HC / 8); it += NT) {
+      const int r = it / (HC / 8), c8 = (it % (HC / 8)) * 8;
+      const int64_t t = t0 + r;
+      float v[8];
+      if (t < T && c8 < hc) {
+        if (BF16) {
+          const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(xv) + t * H + h0 + c8);
+          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[2 * q] = __uint_as_float(w4[q] << 16);
+            v[2 * q + 1] = __uint_as_float(w4[q] & 0xFFFF0000u);
+          }
+        } else {
+          const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(xv) + t * H + h0 + c8);
+          const float4 a = p[0], b = p[1];
+          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = 0.0f;
+      }
+      float4* d = reinterpret_cast<float4*>(&xs[r * PAD + c8]);
+      d[0] = make_float4(v[0], v[1], v[2], v[3]);
+      d[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    // ---- stage Wg[e0 .. e0+BE) x [h0 .. h0+HC)
+    for (int it = tid; it < BE * (HC / 8); it += NT) {
+      const int r = it / (HC / 8), c8 = (it % (HC / 8)) * 8;
+      const int e = e0 + r;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+      if (e < E && c8 < hc) {
+        const float4* p = reinterpret_cast<const float4*>(wg + (int64_t)e * H + h0 + c8);
+        a = p[0];
+        b = p[1];
+      }
+      float4* d = reinterpret_cast<float4*>(&ws[r * PAD + c8]);
+      d[0] = a;
+      d[1] = b;
+    }
+    __syncthreads();
+    // ---- the chain, 4 h at a time, strictly ascending
+    for (int hh = 0; hh < hc; hh += 4) {
+      float4 xr[TT], wr[TE];
+#pragma unroll
+      for (int i = 0; i < TT; ++i) xr[i] = *reinterpret_cast<const float4*>(&xs[(ty * TT + i) * PAD + hh]);
+#pragma unroll
+      for (int j = 0; j < TE; ++j) wr[j] = *reinterpret_cast<const float4*>(&ws[(tx * TE + j) * PAD + hh]);
+#pragma unroll
+      for (int i = 0; i < TT; ++i)
+#pragma unroll
+        for (int j = 0; j < TE; ++j) {
+          float a = acc[i][j];
+          a = __builtin_fmaf(xr[i].x, wr[j].x, a);
+          a = __builtin_fmaf(xr[i].y, wr[j].y, a);
+          a = __builtin_fmaf(xr[i].z, wr[j].z, a);
+          a = __builtin_fmaf(xr[i].w, wr[j].w, a);
+          acc[i][j] = a;
+        }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < TT; ++i) {
+    const int64_t t = t0 + ty * TT + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < TE; ++j) {
+      const int e = e0 + tx * TE + j;
+      if (e >= E) continue;
+      float v = acc[i][j];
+      if (bias) v = v + bias[e];
+      z[t * E + e] = v;
+    }
+  }
+}
+
+template <int TT, int TE>
+int launch(const void* x, bool bf16, const float* wg, const float* bias, int64_t T, int H, int E, float* z,
+           hipStream_t st) {
+  dim3 grid((unsigned)ceil_div64(T, 16 * TT), (unsigned)ceil_div64(E, 16 * TE));
+  if (bf16)
+    gate_logits_kernel<TT, TE, true><<<grid, NT, 0, st>>>(x, wg, bias, T, H, E, z);
+  else
+    gate_logits_kernel<TT, TE, false><<<grid, NT, 0, st>>>(x, wg, bias, T, H, E, z);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_gate_logits(const void* x, int x_dtype, const float* wg, const float* bias, int64_t T, int32_t H,
+                               int32_t E, float* logits, void* stream) {
+  if (T < 0 || H < 1 || E < 1 || H % 8 != 0) return MOE_ERR_SHAPE;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !wg || !logits) return MOE_ERR_NULL;
+  if (E > 65535 * 16 || T > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
+  const bool bf16 = x_dtype == MOE_BF16;
+  hipStream_t st = as_stream(stream);
+  // Larger register tiles amortise LDS reads; use them only when they still give >= 512
+  // workgroups (two per CU), because each output is one long dependent chain.
+  const int64_t wg44 = ceil_div64(T, 64) * ceil_div64(E, 64);
+  const int64_t wg22 = ceil_div64(T, 32) * ceil_div64(E, 32);
+  if (wg44 >= 512) return launch<4, 4>(x, bf16, wg, bias, T, H, E, logits, st);
+  if (wg22 >= 512) return launch<2, 2>(x, bf16, wg, bias, T, H, E, logits, st);
+  return launch<1, 1>(x, bf16, wg, bias, T, H, E, logits, st);
+}

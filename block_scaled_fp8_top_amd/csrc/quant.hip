@@ -1,0 +1,120 @@
+// Block-scaled FP8 e4m3 quantisation (1x128 activation blocks, 128x128 weight blocks).
+//
+// Per block: amax = max |x|; s = amax / 448 (IEEE fp32 division; 1 for an all-zero block);
+// q = e4m3(x / s) with x / s an IEEE fp32 division (hipcc emits correctly rounded fp32 division by
+// default), rounded to nearest even and saturated at 448 by the clamp-then-convert in common.h.
+// HBM-bound: every input byte is read once and every code written once.
+#include "common.h"
+
+namespace {
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* x, int64_t i, float (&v)[8]) {
+  if (BF16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + i);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(w[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + i);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+__device__ __forceinline__ uint2 encode8(const float (&v)[8], float s) {
+  float r[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) r[q] = v[q] / s;
+  return make_uint2(e4m3_pack4(r[0], r[1], r[2], r[3]), e4m3_pack4(r[4], r[5], r[6], r[7]));
+}
+
+// 1x128: 16 lanes per block, 8 consecutive values per lane.  Blocks are contiguous in memory
+// (rows are contiguous and cols % 128 == 0), so block b covers x[128 b, 128 b + 128) and its
+// scale is scales[b].
+template <bool BF16>
+__global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict__ x, int64_t nblocks,
+                                                          uint8_t* __restrict__ q, float* __restrict__ scales) {
+  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t b = gt >> 4;
+  const int sub = threadIdx.x & 15;
+  // every lane of a 16-lane group shares b; whole groups are in or out of range
+  if (b >= nblocks) return;
+  float v[8];
+  load8<BF16>(x, b * 128 + sub * 8, v);
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  const float s = m == 0.0f ? 1.0f : m / 448.0f;
+  *reinterpret_cast<uint2*>(q + b * 128 + sub * 8) = encode8(v, s);
+  if (sub == 0) scales[b] = s;
+}
+
+// 128x128: one workgroup of 256 threads per block; thread (r16 = tid / 16, c = tid % 16) handles
+// rows r16 + 16 p (p < 8), columns 8c .. 8c+7.
+template <bool BF16>
+__global__ __launch_bounds__(256) void quant_128x128_kernel(const void* __restrict__ x, int64_t rows, int cols,
+                                                            uint8_t* __restrict__ q, float* __restrict__ scales) {
+  __shared__ float red[4];
+  const int64_t rb_n = rows / 128;
+  const int cb_n = cols / 128;
+  const int64_t blk = blockIdx.x;
+  const int64_t b = blk / (rb_n * cb_n);
+  const int64_t rb = (blk / cb_n) % rb_n;
+  const int cb = (int)(blk % cb_n);
+  const int tid = threadIdx.x, r16 = tid / 16, c = tid % 16;
+  const int64_t base = b * rows * cols + (rb * 128) * (int64_t)cols + cb * 128 + c * 8;
+  float v[8][8];
+  float m = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    load8<BF16>(x, base + (int64_t)(r16 + 16 * p) * cols, v[p]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[p][i]));
+  }
+  m = wave_max(m);
+  if ((tid & 63) == 0) red[tid / 64] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = m == 0.0f ? 1.0f : m / 448.0f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p)
+    *reinterpret_cast<uint2*>(q + base + (int64_t)(r16 + 16 * p) * cols) = encode8(v[p], s);
+  if (tid == 0) scales[blk] = s;
+}
+
+}  // namespace
+
+extern "C" int moe_quant_fp8_block(const void* x, int x_dtype, int64_t batch, int64_t rows, int32_t cols,
+                                   int32_t block_rows, uint8_t* q, float* scales, void* stream) {
+  if (block_rows != 1 && block_rows != 128) return MOE_ERR_ARG;
+  if (batch < 0 || rows < 0 || cols < 0 || cols % 128 != 0 || rows % block_rows != 0) return MOE_ERR_SHAPE;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  const int64_t nblocks = batch * (rows / block_rows) * (cols / 128);
+  if (nblocks == 0) return MOE_OK;
+  if (!x || !q || !scales) return MOE_ERR_NULL;
+  hipStream_t st = as_stream(stream);
+  const bool bf16 = x_dtype == MOE_BF16;
+  if (block_rows == 1) {
+    const int64_t threads = nblocks * 16;
+    const int64_t grid = ceil_div64(threads, 256);
+    if (grid > INT32_MAX) return MOE_ERR_SHAPE;
+    if (bf16)
+      quant_1x128_kernel<true><<<(unsigned)grid, 256, 0, st>>>(x, nblocks, q, scales);
+    else
+      quant_1x128_kernel<false><<<(unsigned)grid, 256, 0, st>>>(x, nblocks, q, scales);
+  } else {
+    if (nblocks > INT32_MAX) return MOE_ERR_SHAPE;
+    if (bf16)
+      quant_128x128_kernel<true><<<(unsigned)nblocks, 256, 0, st>>>(x, rows, cols, q, scales);
+    else
+      quant_128x128_kernel<false><<<(unsigned)nblocks, 256, 0, st>>>(x, rows, cols, q, scales);
+  }
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}

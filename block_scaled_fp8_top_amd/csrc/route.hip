@@ -1,0 +1,321 @@
+// Top-k router and router replay, one wavefront (64 lanes) per token.
+//
+// Lane l holds experts e = l + 64*j (j < EPL).  Scores (softmax or sigmoid with the fixed
+// router_exp), the optional group limit, the top-k selection by (logit desc, expert asc) and the
+// weights follow the router contract in moe_fp8.h step for step, so that indices and weights are
+// reproducible bit for bit.  Sequential sums (the softmax denominator over experts, the
+// renormalisation over slots) are taken in the stated order by a single lane or redundantly by
+// every lane, never as a tree.
+#include <float.h>
+
+#include "common.h"
+
+namespace {
+
+constexpr int WAVES = 4;  // tokens per workgroup
+constexpr int MAX_GROUPS = 64;
+
+struct Cand {
+  float z;
+  int e;
+};
+
+// strict order: a before b when its logit is larger, or equal with a lower expert index
+__device__ __forceinline__ bool before(float za, int ea, float zb, int eb) { return za > zb || (za == zb && ea < eb); }
+
+__device__ __forceinline__ Cand wave_best(Cand c) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float oz = __shfl_xor(c.z, o, 64);
+    const int oe = __shfl_xor(c.e, o, 64);
+    if (before(oz, oe, c.z, c.e)) {
+      c.z = oz;
+      c.e = oe;
+    }
+  }
+  return c;
+}
+
+// Scores of all experts into sc[] (LDS), keys into key[] (LDS).  Returns nothing; the wave is
+// synchronised on exit (LDS visible to every lane).
+template <int EPL>
+__device__ __forceinline__ void token_scores(const float* __restrict__ zrow, int E, int score_fn, int lane,
+                                             float (&z)[EPL], float* key, float* sc) {
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    z[j] = e < E ? zrow[e] : -FLT_MAX;
+    if (e < E) key[e] = z[j];
+  }
+  if (score_fn == MOE_SCORE_SOFTMAX) {
+    float m = -FLT_MAX;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (lane + 64 * j < E) m = fmaxf(m, z[j]);
+    m = wave_max(m);
+    float p[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      p[j] = router_exp(z[j] - m);
+      if (e < E) sc[e] = p[j];
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    float S = 0.0f;
+    if (lane == 0)
+      for (int e = 0; e < E; ++e) S = S + sc[e];
+    S = __shfl(S, 0, 64);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E) sc[e] = p[j] / S;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E) sc[e] = router_sigmoid(z[j]);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+}
+
+template <int EPL>
+__global__ __launch_bounds__(64 * WAVES) void route_kernel(const float* __restrict__ logits, int64_t T,
+                                                           moe_router_cfg cfg, int32_t* __restrict__ topk_idx,
+                                                           float* __restrict__ topk_w, int32_t* __restrict__ record,
+                                                           int64_t record_ld) {
+  __shared__ float key_s[WAVES][64 * EPL];
+  __shared__ float sc_s[WAVES][64 * EPL];
+  const int lane = threadIdx.x % 64, wv = threadIdx.x / 64;
+  const int64_t t = (int64_t)blockIdx.x * WAVES + wv;
+  if (t >= T) return;
+  const int E = cfg.num_experts, k = cfg.top_k;
+  float* key = key_s[wv];
+  float* sc = sc_s[wv];
+  float z[EPL];
+  token_scores<EPL>(logits + t * E, E, cfg.score_fn, lane, z, key, sc);
+
+  // ---- group limit: lane g < n_group scores group g; lane 0 keeps the best topk_group groups
+  uint64_t allowed_groups = ~0ull;
+  int gs = E;
+  if (cfg.n_group > 1) {
+    gs = E / cfg.n_group;
+    float gscore = -FLT_MAX;
+    if (lane < cfg.n_group) {
+      const int base = lane * gs;
+      uint64_t taken_lo = 0;  // selection bits for the first 64 members (group_score_topk is small)
+      float sum = 0.0f;
+      int prev[8];
+      for (int r = 0; r < cfg.group_score_topk; ++r) {
+        int best = -1;
+        float bz = 0.0f;
+        for (int i = 0; i < gs; ++i) {
+          bool used = false;
+          if (i < 64) used = (taken_lo >> i) & 1ull;
+          else
+            for (int q = 0; q < r; ++q) used |= prev[q] == i;
+          if (used) continue;
+          const float zi = key[base + i];
+          if (best < 0 || before(zi, base + i, bz, base + best)) {
+            best = i;
+            bz = zi;
+          }
+        }
+        if (best < 64) taken_lo |= 1ull << best;
+        prev[r] = best;
+        sum = sum + sc[base + best];
+      }
+      gscore = sum;
+    }
+    // lane 0 gathers the group scores (ascending group order) and keeps topk_group of them
+    uint64_t keep = 0;
+    for (int r = 0; r < cfg.topk_group; ++r) {
+      int best = -1;
+      float bs = 0.0f;
+      for (int g = 0; g < cfg.n_group; ++g) {
+        const float s = __shfl(gscore, g, 64);
+        if ((keep >> g) & 1ull) continue;
+        if (best < 0 || s > bs) {
+          best = g;
+          bs = s;
+        }
+      }
+      keep |= 1ull << best;
+    }
+    allowed_groups = keep;
+  }
+
+  // ---- top-k by (logit desc, expert asc) among allowed experts
+  uint32_t taken = 0;  // bit j: expert lane + 64*j already selected
+  int my_e = -1;
+#pragma unroll 1
+  for (int r = 0; r < k; ++r) {
+    Cand c{-FLT_MAX, 0x7FFFFFFF};
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      if (e >= E || ((taken >> j) & 1u)) continue;
+      if (!((allowed_groups >> (e / gs)) & 1ull)) continue;
+      if (c.e == 0x7FFFFFFF || before(z[j], e, c.z, c.e)) {
+        c.z = z[j];
+        c.e = e;
+      }
+    }
+    c = wave_best(c);
+    if (lane == (c.e & 63)) taken |= 1u << (c.e >> 6);
+    if (lane == r) my_e = c.e;
+  }
+  // ---- weights
+  const float my_s = lane < k ? sc[my_e] : 0.0f;
+  float w = my_s;
+  if (cfg.renormalize) {
+    float d = 0.0f;
+    for (int r = 0; r < k; ++r) d = d + __shfl(my_s, r, 64);
+    w = my_s / d;
+  }
+  if (lane < k) {
+    topk_idx[t * k + lane] = my_e;
+    topk_w[t * k + lane] = w;
+    if (record) record[lane * record_ld + t] = my_e;
+  }
+}
+
+template <int EPL>
+__global__ __launch_bounds__(64 * WAVES) void replay_kernel(const float* __restrict__ logits, int64_t T,
+                                                            moe_router_cfg cfg, const int32_t* __restrict__ replay,
+                                                            int64_t replay_ld, int32_t* __restrict__ topk_idx,
+                                                            float* __restrict__ topk_w, int32_t* __restrict__ bad) {
+  __shared__ float key_s[WAVES][64 * EPL];
+  __shared__ float sc_s[WAVES][64 * EPL];
+  const int lane = threadIdx.x % 64, wv = threadIdx.x / 64;
+  const int64_t t = (int64_t)blockIdx.x * WAVES + wv;
+  if (t >= T) return;
+  const int E = cfg.num_experts, k = cfg.top_k;
+  const int my_e = lane < k ? replay[lane * replay_ld + t] : 0;
+  bool ok = my_e >= 0 && my_e < E;
+  for (int q = 0; q < k; ++q) {
+    const int oe = __shfl(my_e, q, 64);
+    if (q < lane && oe == my_e) ok = false;
+  }
+  const bool all_ok = __ballot(lane < k && !ok) == 0;
+  if (!all_ok) {
+    if (lane < k) {
+      topk_idx[t * k + lane] = -1;
+      topk_w[t * k + lane] = 0.0f;
+    }
+    if (lane == 0 && bad) atomicAdd(bad, 1);
+    return;
+  }
+  float my_s;
+  if (cfg.score_fn == MOE_SCORE_SOFTMAX) {
+    float z[EPL];
+    token_scores<EPL>(logits + t * E, E, cfg.score_fn, lane, z, key_s[wv], sc_s[wv]);
+    my_s = lane < k ? sc_s[wv][my_e] : 0.0f;
+  } else {
+    my_s = lane < k ? router_sigmoid(logits[t * E + my_e]) : 0.0f;
+  }
+  float w = my_s;
+  if (cfg.renormalize) {
+    float d = 0.0f;
+    for (int r = 0; r < k; ++r) d = d + __shfl(my_s, r, 64);
+    w = my_s / d;
+  }
+  if (lane < k) {
+    topk_idx[t * k + lane] = my_e;
+    topk_w[t * k + lane] = w;
+  }
+}
+
+__global__ __launch_bounds__(256) void score_eval_kernel(const float* __restrict__ x, int64_t n, int score_fn,
+                                                        float* __restrict__ y) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  y[i] = score_fn == MOE_SCORE_SOFTMAX ? router_exp(x[i]) : router_sigmoid(x[i]);
+}
+
+int check_cfg(const moe_router_cfg* c) {
+  if (!c) return MOE_ERR_NULL;
+  const int E = c->num_experts, k = c->top_k;
+  if (E < 1 || E > 1024 || k < 1 || k > 64 || k > E) return MOE_ERR_ARG;
+  if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_ARG;
+  if (c->n_group > 1) {
+    if (c->n_group > MAX_GROUPS || E % c->n_group != 0) return MOE_ERR_ARG;
+    const int gs = E / c->n_group;
+    if (c->topk_group < 1 || c->topk_group > c->n_group) return MOE_ERR_ARG;
+    if (c->group_score_topk < 1 || c->group_score_topk > gs || c->group_score_topk > 8) return MOE_ERR_ARG;
+    if (k > c->topk_group * gs) return MOE_ERR_ARG;
+  } else if (c->n_group < 1) {
+    return MOE_ERR_ARG;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+#define DISPATCH_EPL(E, BODY)                  \
+  do {                                         \
+    if ((E) <= 64) {                           \
+      constexpr int EPL = 1;                   \
+      BODY;                                    \
+    } else if ((E) <= 128) {                   \
+      constexpr int EPL = 2;                   \
+      BODY;                                    \
+    } else if ((E) <= 256) {                   \
+      constexpr int EPL = 4;                   \
+      BODY;                                    \
+    } else if ((E) <= 512) {                   \
+      constexpr int EPL = 8;                   \
+      BODY;                                    \
+    } else {                                   \
+      constexpr int EPL = 16;                  \
+      BODY;                                    \
+    }                                          \
+  } while (0)
+
+extern "C" int moe_route(const float* logits, int64_t T, const moe_router_cfg* cfg, int32_t* topk_idx, float* topk_w,
+                         int32_t* record, int64_t record_ld, void* stream) {
+  const int rc = check_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  if (T < 0 || T > (int64_t)INT32_MAX * WAVES) return MOE_ERR_SHAPE;
+  if (record && record_ld < T) return MOE_ERR_ARG;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !topk_w) return MOE_ERR_NULL;
+  const moe_router_cfg c = *cfg;
+  const unsigned grid = (unsigned)ceil_div64(T, WAVES);
+  hipStream_t st = as_stream(stream);
+  DISPATCH_EPL(c.num_experts, (route_kernel<EPL><<<grid, 64 * WAVES, 0, st>>>(logits, T, c, topk_idx, topk_w,
+                                                                               record, record_ld)));
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+extern "C" int moe_replay_route(const float* logits, int64_t T, const moe_router_cfg* cfg, const int32_t* replay,
+                                int64_t replay_ld, int32_t* topk_idx, float* topk_w, int32_t* bad_count,
+                                void* stream) {
+  const int rc = check_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  if (T < 0 || T > (int64_t)INT32_MAX * WAVES) return MOE_ERR_SHAPE;
+  if (replay_ld < T) return MOE_ERR_ARG;
+  if (T == 0) return MOE_OK;
+  if (!logits || !replay || !topk_idx || !topk_w) return MOE_ERR_NULL;
+  const moe_router_cfg c = *cfg;
+  const unsigned grid = (unsigned)ceil_div64(T, WAVES);
+  hipStream_t st = as_stream(stream);
+  DISPATCH_EPL(c.num_experts, (replay_kernel<EPL><<<grid, 64 * WAVES, 0, st>>>(logits, T, c, replay, replay_ld,
+                                                                                topk_idx, topk_w, bad_count)));
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+extern "C" int moe_router_score_eval(const float* x, int64_t n, int score_fn, float* y, void* stream) {
+  if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_ARG;
+  if (n < 0 || ceil_div64(n, 256) > INT32_MAX) return MOE_ERR_SHAPE;
+  if (n == 0) return MOE_OK;
+  if (!x || !y) return MOE_ERR_NULL;
+  score_eval_kernel<<<(unsigned)ceil_div64(n, 256), 256, 0, as_stream(stream)>>>(x, n, score_fn, y);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}

@@ -1,0 +1,137 @@
+"""One MoE layer forward composed from the C-ABI calls, with buffers allocated once.
+
+forward(x) enqueues, on the current stream and without any host synchronisation:
+  moe_gate_logits -> moe_route (optionally recording into the routing payload) or
+  moe_replay_route -> moe_quant_fp8_block (x, 1x128) -> moe_dispatch -> moe_grouped_gemm_fp8
+  (W1, SwiGLU + 1x128 quantisation of h) -> moe_grouped_gemm_fp8 (W2) -> moe_combine.
+
+This is the layer that "RL at 1T Scale: prime-rl Performance Deep Dive" runs in FP8 at inference
+(section "FP8 inference") and in block-scaled FP8 in the trainer (section "FP8 training"), with
+router replay (section "Router replay") as a mode of the same forward.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+import block_scaled_fp8_top_amd as M
+
+
+@dataclass
+class MoELayerWeights:
+    """Router gate and 128x128-block-quantised expert weights (group E is the shared expert)."""
+    wg: torch.Tensor                 # [E,H] fp32
+    bias: Optional[torch.Tensor]     # [E] fp32
+    w1q: torch.Tensor                # [G,2F,H] e4m3 bytes
+    w1s: torch.Tensor                # [G,2F/128,H/128] fp32
+    w2q: torch.Tensor                # [G,H,F] e4m3 bytes
+    w2s: torch.Tensor                # [G,H/128,F/128] fp32
+    cfg: M.RouterCfg
+    shared: bool
+
+    @property
+    def E(self) -> int:
+        return int(self.cfg.num_experts)
+
+    @property
+    def H(self) -> int:
+        return int(self.wg.shape[1])
+
+    @property
+    def F(self) -> int:
+        return int(self.w2q.shape[2])
+
+    @property
+    def groups(self) -> int:
+        return int(self.w1q.shape[0])
+
+
+def quantize_expert_weights(groups: int, H: int, F: int, master, device="cuda", stream=None):
+    """Allocate the quantised weight tensors and fill expert g from ``master(g) -> (w1 [2F,H], w2 [H,F])``
+    (fp32 or bf16 device tensors), one expert at a time so the fp32 masters never coexist."""
+    w1q = torch.empty((groups, 2 * F, H), dtype=torch.uint8, device=device)
+    w1s = torch.empty((groups, 2 * F // 128, H // 128), dtype=torch.float32, device=device)
+    w2q = torch.empty((groups, H, F), dtype=torch.uint8, device=device)
+    w2s = torch.empty((groups, H // 128, F // 128), dtype=torch.float32, device=device)
+    for g in range(groups):
+        w1, w2 = master(g)
+        M.moe_quant_fp8_block(w1, 128, q=w1q[g], scales=w1s[g], stream=stream)
+        M.moe_quant_fp8_block(w2, 128, q=w2q[g], scales=w2s[g], stream=stream)
+    return w1q, w1s, w2q, w2s
+
+
+class MoELayer:
+    """Preallocated buffers for up to ``T_max`` tokens; ``forward`` returns a view of the output."""
+
+    def __init__(self, weights: MoELayerWeights, T_max: int, act_dtype=torch.bfloat16, device="cuda"):
+        self.w = weights
+        self.T_max = T_max
+        self.act = act_dtype
+        E, H, F, k = weights.E, weights.H, weights.F, int(weights.cfg.top_k)
+        G = weights.groups
+        self.max_rows = T_max * k + (T_max if weights.shared else 0)
+        d = device
+        self.logits = torch.empty((T_max, E), dtype=torch.float32, device=d)
+        self.idx = torch.empty((T_max, k), dtype=torch.int32, device=d)
+        self.wts = torch.empty((T_max, k), dtype=torch.float32, device=d)
+        self.xq = torch.empty((T_max, H), dtype=torch.uint8, device=d)
+        self.xs = torch.empty((T_max, H // 128), dtype=torch.float32, device=d)
+        self.disp = M.Dispatched(
+            counts=torch.empty(G, dtype=torch.int32, device=d),
+            offsets=torch.empty(G + 1, dtype=torch.int32, device=d),
+            dest_row=torch.empty((T_max, k), dtype=torch.int32, device=d),
+            src_token=torch.empty(self.max_rows, dtype=torch.int32, device=d),
+            aq=torch.empty((self.max_rows, H), dtype=torch.uint8, device=d),
+            as_=torch.empty((self.max_rows, H // 128), dtype=torch.float32, device=d),
+            max_rows=self.max_rows)
+        self.hq = torch.empty((self.max_rows, F), dtype=torch.uint8, device=d)
+        self.hs = torch.empty((self.max_rows, F // 128), dtype=torch.float32, device=d)
+        self.y = torch.empty((self.max_rows, H), dtype=act_dtype, device=d)
+        self.out = torch.empty((T_max, H), dtype=act_dtype, device=d)
+        ws = max(M.workspace_bytes(M.MOE_OP_DISPATCH, T_max, k, E),
+                 M.workspace_bytes(M.MOE_OP_GROUPED_GEMM, self.max_rows, 0, G, 2 * F, H),
+                 M.workspace_bytes(M.MOE_OP_GROUPED_GEMM, self.max_rows, 0, G, H, F))
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=d)
+        self.bad = torch.zeros(1, dtype=torch.int32, device=d)
+
+    def forward(self, x: torch.Tensor, replay: Optional[torch.Tensor] = None, record: Optional[torch.Tensor] = None,
+                stream=None, events=None) -> torch.Tensor:
+        """``events``: optional list of 8 timing events (torch.cuda.Event), recorded on the launch
+        stream before the first stage and after each of the seven stages."""
+        T = x.shape[0]
+        if T != self.T_max:
+            raise ValueError(f"layer buffers are sized for T={self.T_max}, got {T}")
+        w = self.w
+        st = torch.cuda.current_stream() if stream is None else stream
+
+        def mark(i):
+            if events is not None:
+                events[i].record(st)
+
+        mark(0)
+        M.moe_gate_logits(x, w.wg, w.bias, out=self.logits, stream=stream)
+        mark(1)
+        if replay is not None:
+            M.moe_replay_route(self.logits, w.cfg, replay, bad_count=self.bad, topk_idx=self.idx, topk_w=self.wts,
+                               stream=stream)
+        else:
+            M.moe_route(self.logits, w.cfg, record=record, topk_idx=self.idx, topk_w=self.wts, stream=stream)
+        mark(2)
+        M.moe_quant_fp8_block(x, 1, q=self.xq, scales=self.xs, stream=stream)
+        mark(3)
+        M.moe_dispatch(self.idx, w.E, w.shared, self.xq, self.xs, workspace=self.workspace, out=self.disp,
+                       stream=stream)
+        mark(4)
+        M.moe_grouped_gemm_fp8(self.disp.aq, self.disp.as_, self.disp.offsets, w.w1q, w.w1s,
+                               epilogue=M.MOE_EPI_SWIGLU_QUANT, out=self.hq, out_scales=self.hs,
+                               workspace=self.workspace, stream=stream)
+        mark(5)
+        M.moe_grouped_gemm_fp8(self.hq, self.hs, self.disp.offsets, w.w2q, w.w2s, epilogue=M.MOE_EPI_STORE,
+                               out_dtype=self.act, out=self.y, workspace=self.workspace, stream=stream)
+        mark(6)
+        shared_row = self.disp.offsets[w.E:w.E + 1] if w.shared else None
+        M.moe_combine(self.y, self.disp.dest_row, self.wts, shared_row, out=self.out, stream=stream)
+        mark(7)
+        return self.out

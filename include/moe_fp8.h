@@ -1,0 +1,196 @@
+/*
+ * moe_fp8.h -- C ABI of the block-scaled FP8 Mixture-of-Experts layer for AMD Instinct MI355X
+ * (gfx950).  Shared library: libmoe_fp8.so.
+ *
+ * The layer is the MoE block that "RL at 1T Scale: prime-rl Performance Deep Dive" (Prime
+ * Intellect blog) runs both at inference and in the trainer:
+ *   - a top-k router, whose decisions inference records in a [num_layers, top_k, seq_len]
+ *     routing payload and the trainer replays in place of the router (section "Router replay");
+ *   - dispatch of tokens to their experts and the combine back to token order, the layer's two
+ *     exchange points (sections "Wide EP" and "Parallelism / EP");
+ *   - block-scaled FP8 as proposed by DeepSeek V3, used by inference and by training so that both
+ *     run the same precision (sections "FP8 inference" and "FP8 training"): activations with one
+ *     fp32 scale per 1x128 block, weights with one per 128x128 block, e4m3 codes, fp32 accumulation.
+ *
+ * Calling order for one layer forward on one GPU:
+ *   moe_gate_logits -> moe_route | moe_replay_route -> moe_quant_fp8_block (x, 1x128)
+ *   -> moe_dispatch -> moe_grouped_gemm_fp8 (W1, SwiGLU + 1x128 re-quantisation)
+ *   -> moe_grouped_gemm_fp8 (W2) -> moe_combine.
+ * Expert weights are quantised once with moe_quant_fp8_block (128x128 blocks).
+ *
+ * Conventions (all entry points):
+ *   - Pointers are device pointers allocated and owned by the caller unless stated otherwise; the
+ *     library allocates no device memory and keeps no state between calls.  Scratch memory is a
+ *     caller-provided workspace of at least moe_workspace_bytes(...) bytes.
+ *   - Every call enqueues work on `stream` (a hipStream_t passed as void*, NULL = default stream),
+ *     never synchronises and returns an int status: MOE_OK or a negative MOE_ERR_* code.  Argument
+ *     checks run on the host before any launch; on an error nothing is enqueued.
+ *   - Row-major layouts.  Activations [rows, K] (K contiguous); activation scales [rows, K/128];
+ *     expert weights [groups, N, K] (K contiguous, i.e. Y = A * W^T); weight scales
+ *     [groups, N/128, K/128].  W1 rows [0, F) are the gate projection and rows [F, 2F) the up
+ *     projection.  Indices are int32; scales fp32; codes are OCP FP8 E4M3 ("e4m3fn") bytes.
+ *   - Deterministic: identical inputs give bitwise identical outputs (no floating-point atomics).
+ *   - Data errors found on the device (a replayed expert id outside [0, E) or repeated within a
+ *     token) are counted in an optional device int32 counter; that token is routed to no expert
+ *     (index -1, weight 0) and is skipped by dispatch and combine.
+ */
+#ifndef MOE_FP8_H
+#define MOE_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_ERR_NULL (-1)      /* a required pointer is NULL                                  */
+#define MOE_ERR_SHAPE (-2)     /* a size is out of range or not a multiple of 128 where needed */
+#define MOE_ERR_DTYPE (-3)     /* unsupported dtype code                                     */
+#define MOE_ERR_ARG (-4)       /* inconsistent router configuration or other argument         */
+#define MOE_ERR_HIP (-5)       /* the HIP runtime reported an error at launch                 */
+#define MOE_ERR_WORKSPACE (-6) /* workspace missing or smaller than moe_workspace_bytes()     */
+
+/* dtype codes */
+#define MOE_F32 0
+#define MOE_BF16 1
+#define MOE_FP8_E4M3 2
+
+/* router score functions */
+#define MOE_SCORE_SOFTMAX 0
+#define MOE_SCORE_SIGMOID 1
+
+/* grouped-GEMM epilogues */
+#define MOE_EPI_STORE 0        /* out = A * W^T in out_dtype (bf16 or fp32)                   */
+#define MOE_EPI_SWIGLU_QUANT 1 /* h = silu(gate) * up, then 1x128 FP8 quantisation of h     */
+
+/* workspace query op codes */
+#define MOE_OP_DISPATCH 1
+#define MOE_OP_GROUPED_GEMM 2
+
+/* Router configuration.
+ *   num_experts      E routed experts, 1 <= E <= 1024
+ *   top_k            experts per token, 1 <= top_k <= min(E, 64)
+ *   score_fn         MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID
+ *   renormalize      0: weight = score of the expert; 1: weights divided by their sum over the slots
+ *   n_group          1 = no group limit; else experts form n_group contiguous groups (E % n_group == 0)
+ *   topk_group       groups kept (1 <= topk_group <= n_group; top_k <= topk_group * E / n_group)
+ *   group_score_topk a group's score is the sum of its best group_score_topk expert scores
+ */
+typedef struct {
+  int32_t num_experts, top_k, score_fn, renormalize, n_group, topk_group, group_score_topk;
+} moe_router_cfg;
+
+/* Router gate projection (the first step of "the router" whose decisions the blog's section
+ * "Router replay" records).  logits[t,e] = sum_h x[t,h] * wg[e,h] (+ bias[e]) computed as one fp32
+ * fused-multiply-add chain in ascending h starting from +0, then one fp32 add of the bias, so the
+ * routing decided from it is reproducible bit for bit.
+ *   x       [T,H] in x_dtype (MOE_F32 or MOE_BF16)      wg [E,H] fp32     bias [E] fp32 or NULL
+ *   logits  [T,E] fp32 (output)
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (T < 0, H < 1 or H % 8 != 0, E < 1), MOE_ERR_DTYPE, MOE_ERR_HIP.
+ * T == 0 is a no-op. */
+int moe_gate_logits(const void* x, int x_dtype, const float* wg, const float* bias, int64_t T, int32_t H,
+                    int32_t E, float* logits, void* stream);
+
+/* Top-k router (blog section "Router replay": the routing decisions that inference captures).
+ * Per token: scores (softmax: exp(z - max z) / sum, the sum in ascending expert order;
+ * sigmoid: 1 / (1 + exp(-z)); exp is a fixed Cody-Waite reduction + degree-6 polynomial in fp32),
+ * optional group limit, selection of top_k experts by logit descending (ties: lower expert id),
+ * slot j = j-th best; weight = score, or score / (sum of the slot scores in slot order) when
+ * renormalised.
+ *   logits    [T,E] fp32          topk_idx [T,top_k] int32 (out)     topk_w [T,top_k] fp32 (out)
+ *   record    NULL, or one layer of the routing payload [top_k, record_ld] int32 (record_ld >= T):
+ *             record[j*record_ld + t] = topk_idx[t,j]
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ARG (invalid cfg, record_ld < T), MOE_ERR_HIP. */
+int moe_route(const float* logits, int64_t T, const moe_router_cfg* cfg, int32_t* topk_idx, float* topk_w,
+              int32_t* record, int64_t record_ld, void* stream);
+
+/* Router replay (blog section "Router replay": recorded decisions replayed on the trainer in place
+ * of the router).  topk_idx[t,j] = replay[j*replay_ld + t] unchanged; weights recomputed from the
+ * current logits with cfg's score function and normalisation (group limits do not apply).  A token
+ * with an id outside [0,E) or a repeated id gets index -1 and weight 0 in every slot and adds 1 to
+ * *bad_count (device int32, accumulated, not reset; may be NULL).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ARG (invalid cfg, replay_ld < T), MOE_ERR_HIP. */
+int moe_replay_route(const float* logits, int64_t T, const moe_router_cfg* cfg, const int32_t* replay,
+                     int64_t replay_ld, int32_t* topk_idx, float* topk_w, int32_t* bad_count, void* stream);
+
+/* The router's fixed score function, elementwise, for validating the bit-exact routing contract:
+ * y[i] = exp(x[i]) as used in the softmax scores (score_fn MOE_SCORE_SOFTMAX), or
+ * y[i] = 1 / (1 + exp(-x[i])) (MOE_SCORE_SIGMOID); exp is the Cody-Waite + degree-6 polynomial fp32
+ * evaluation described at moe_route, with its input clamped to [-86, 88].  x, y: [n] fp32.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ARG (score_fn), MOE_ERR_HIP. */
+int moe_router_score_eval(const float* x, int64_t n, int score_fn, float* y, void* stream);
+
+/* Block-scaled FP8 quantisation (blog section "FP8 training": block-scaled FP8 as in DeepSeek V3).
+ * x is [batch, rows, cols] in x_dtype (MOE_F32 or MOE_BF16); blocks are block_rows x 128 with
+ * block_rows = 1 (activations) or 128 (weights).  Per block: amax = max |x|; s = amax / 448 (IEEE
+ * fp32 division; s = 1 if amax == 0); q = e4m3(x / s), x / s an IEEE fp32 division, rounded to
+ * nearest even, magnitudes above 448 saturated to 448, sign of zero kept.
+ *   q       [batch, rows, cols] e4m3 bytes (out)
+ *   scales  [batch, rows/block_rows, cols/128] fp32 (out)
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (cols % 128, rows % block_rows), MOE_ERR_ARG (block_rows),
+ *         MOE_ERR_DTYPE, MOE_ERR_HIP. */
+int moe_quant_fp8_block(const void* x, int x_dtype, int64_t batch, int64_t rows, int32_t cols, int32_t block_rows,
+                        uint8_t* q, float* scales, void* stream);
+
+/* Dispatch (blog sections "Wide EP" / "Parallelism / EP": tokens are sent to their experts).
+ * A stable counting sort of the [T,k] expert ids: group e holds the rows of every (t,j) with
+ * topk_idx[t,j] == e, in ascending token order; with append_shared, group E holds one row per token
+ * (the always-on shared expert), in token order.  G = E + (append_shared ? 1 : 0) groups.
+ *   counts    [G] int32 (out)        offsets [G+1] int32 exclusive prefix of counts (out)
+ *   dest_row  [T,k] int32: row of slot (t,j), or -1 for a slot with index -1 (out)
+ *   src_token [T*k + (append_shared ? T : 0)] int32: token of each row; entries beyond offsets[G]
+ *             are left untouched (out)
+ *   xq, xs    the 1x128-quantised activations [T,H] and scales [T,H/128]; aq, as receive the
+ *             permuted copies [rows,H] and [rows,H/128] (rows = offsets[G]).  If xq and aq are both
+ *             NULL only the index outputs are produced.
+ *   workspace >= moe_workspace_bytes(MOE_OP_DISPATCH, T, k, E, 0, 0) bytes.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (H % 128, E > 1024), MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
+int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_t append_shared,
+                 const uint8_t* xq, const float* xs, int32_t H, int32_t* counts, int32_t* offsets, int32_t* dest_row,
+                 int32_t* src_token, uint8_t* aq, float* as, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Grouped block-scaled FP8 GEMM (blog sections "FP8 inference" / "FP8 training": the FP8 expert
+ * GEMMs).  For each group g and each row r in [offsets[g], offsets[g+1]):
+ *   acc[r,n] = sum over 128-wide K blocks kb of (as[r,kb] * bs[g,n/128,kb]) * sum_{k in kb} a[r,k]*b[g,n,k]
+ * with fp32 accumulation (e4m3 products accumulated exactly inside each 128-block, then promoted).
+ *   a  [max_rows, K] e4m3, as [max_rows, K/128] fp32; offsets [groups+1] device int32, offsets[groups] <= max_rows
+ *   b  [groups, N, K] e4m3, bs [groups, N/128, K/128] fp32
+ *   epilogue MOE_EPI_STORE:        out [max_rows, N] in out_dtype (MOE_BF16 or MOE_F32)
+ *   epilogue MOE_EPI_SWIGLU_QUANT: N = 2F; h[r,f] = silu(acc[r,f]) * acc[r,F+f] in fp32, quantised
+ *            1x128 as in moe_quant_fp8_block: out [max_rows, F] e4m3 (out_dtype MOE_FP8_E4M3),
+ *            out_scales [max_rows, F/128] fp32
+ *   Rows beyond offsets[groups] are not written.  workspace >= moe_workspace_bytes(MOE_OP_GROUPED_GEMM,
+ *   max_rows, 0, groups, N, K).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (N, K % 128; F % 128 for SwiGLU), MOE_ERR_DTYPE, MOE_ERR_ARG,
+ *         MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
+int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int32_t* offsets, int32_t groups, int64_t max_rows,
+                         const uint8_t* b, const float* bs, int32_t N, int32_t K, int32_t epilogue, void* out,
+                         int out_dtype, float* out_scales, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Combine (blog sections "Wide EP" / "Parallelism / EP": expert outputs return to token order).
+ *   out[t,:] = sum_{j<k, dest_row[t,j] >= 0} topk_w[t,j] * y[dest_row[t,j],:]  (+ y[*shared_first_row + t,:])
+ * accumulated in fp32 in slot order, the shared row last, then rounded to out_dtype.
+ *   y [rows,H] in y_dtype (MOE_BF16 or MOE_F32); dest_row, topk_w [T,k]; out [T,H] in out_dtype.
+ *   shared_first_row: NULL (no shared expert) or a device int32 holding the first row of the shared
+ *   group (pass &offsets[E] from moe_dispatch).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (H % 8), MOE_ERR_DTYPE, MOE_ERR_HIP. */
+int moe_combine(const void* y, int y_dtype, const int32_t* dest_row, const float* topk_w, int64_t T, int32_t k,
+                int32_t H, const int32_t* shared_first_row, void* out, int out_dtype, void* stream);
+
+/* Workspace bytes needed by moe_dispatch (op MOE_OP_DISPATCH: rows_or_T = T, k, E) or
+ * moe_grouped_gemm_fp8 (op MOE_OP_GROUPED_GEMM: rows_or_T = max_rows, E = groups, N, K). */
+size_t moe_workspace_bytes(int op, int64_t rows_or_T, int32_t k, int32_t E, int32_t N, int32_t K);
+
+/* Static description of a status code. */
+const char* moe_status_str(int status);
+
+/* Library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_FP8_H */

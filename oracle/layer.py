@@ -183,3 +183,34 @@ def rel_err(got, ref) -> float:
     if den == 0.0:
         return float(np.max(np.abs(got))) if got.size else 0.0
     return float(np.max(np.abs(got - ref))) / den
+
+
+def forward_sampled(layer: OracleLayer, x_rows: np.ndarray, replay_rows: Optional[np.ndarray] = None) -> dict:
+    """Per-token evaluation of sampled tokens, in matrix form: route each token, then apply each
+    used expert once to all sampled rows that selected it (no dispatch permutation, no shared
+    state between tokens beyond the expert weights).  Same values as ``forward_token``."""
+    E, F = layer.E, layer.F
+    z = O.moe_gate_logits(x_rows, layer.wg, layer.bias)
+    idx, w, bad = route_or_replay(layer, z, replay_rows)
+    xq, xs = O.moe_quant_fp8_block(x_rows, 1)
+    n, H = x_rows.shape
+    ys = {}
+    users = {}
+    for t in range(n):
+        for j in range(idx.shape[1]):
+            if idx[t, j] >= 0:
+                users.setdefault(int(idx[t, j]), []).append((t, j))
+    for e, lst in users.items():
+        rows = np.array([t for t, _ in lst])
+        y_act = expert_ffn(layer.get(e), xq[rows], xs[rows], F, layer.act)[5]
+        for (t, j), yr in zip(lst, y_act):
+            ys[(t, j)] = yr
+    out = np.zeros((n, H), np.float64)
+    for t in range(n):
+        for j in range(idx.shape[1]):
+            if idx[t, j] >= 0:
+                out[t] += float(w[t, j]) * ys[(t, j)].astype(np.float64)
+    if layer.shared:
+        y_act = expert_ffn(layer.get(E), xq, xs, F, layer.act)[5]
+        out += y_act.astype(np.float64)
+    return dict(z=z, idx=idx, w=w, bad=bad, xq=xq, xs=xs, out=out, experts=sorted(users))

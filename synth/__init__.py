@@ -182,9 +182,9 @@ def tie_logits(T: int, E: int, levels: int, seed: int, device="cpu") -> torch.Te
 def random_codes(shape, seed: int, part: int, device="cpu") -> torch.Tensor:
     """Uniformly random finite e4m3 bytes (every code except the two NaNs 0x7F / 0xFF)."""
     g = _gen(device, stream_seed(seed, STAGE, 1, 0, part))
-    c = torch.randint(0, 254, tuple(shape), generator=g, device=device, dtype=torch.int32)
-    c = c + (c >= 0x7F).to(torch.int32)          # skip 0x7F
-    return c.to(torch.uint8)
+    c = torch.randint(0, 254, tuple(shape), generator=g, device=device, dtype=torch.uint8)
+    c += (c >= 0x7F).to(torch.uint8)              # skip 0x7F; 0xFE is the largest code drawn
+    return c
 
 
 def random_scales(shape, seed: int, part: int, device="cpu", lo: float = 2.0 ** -12, hi: float = 2.0 ** -4):

@@ -1,0 +1,152 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/moe_fp8.h
+declares, and rejects bad arguments on the host with the documented status codes before any
+launch (so null device pointers are never touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import block_scaled_fp8_top_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_fp8.h")
+OK, NULL, SHAPE, DTYPE, ARG, HIP, WS = 0, -1, -2, -3, -4, -5, -6
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(M.LIB_PATH):
+        from block_scaled_fp8_top_amd import build
+        build.build(verbose=False)
+    return M.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in moe_fp8.h but not exported"
+    assert set(names) == set(M.EXPORTED)
+
+
+def test_status_strings_and_version(L):
+    for code in (OK, NULL, SHAPE, DTYPE, ARG, HIP, WS):
+        assert M.status_str(code)
+    assert M.status_str(-99) == "unknown status"
+    assert "gfx950" in M.version()
+
+
+def test_workspace_sizes(L):
+    a = M.workspace_bytes(M.MOE_OP_DISPATCH, 16384, 8, 256)
+    b = M.workspace_bytes(M.MOE_OP_DISPATCH, 16385, 8, 256)
+    assert 0 < a <= b
+    assert M.workspace_bytes(M.MOE_OP_GROUPED_GEMM, 147456, 0, 257, 4096, 6144) > 0
+    assert M.workspace_bytes(99, 1, 1, 1) == 0 and M.workspace_bytes(M.MOE_OP_DISPATCH, -1, 1, 1) == 0
+
+
+def _cfg(**kw):
+    d = dict(num_experts=256, top_k=8, score_fn=1, renormalize=1, n_group=8, topk_group=4, group_score_topk=2)
+    d.update(kw)
+    return M.RouterCfg(*[d[f] for f, _ in M.RouterCfg._fields_])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, NULL),                                        # valid cfg, null pointers
+    ({"num_experts": 0}, ARG), ({"num_experts": 1025}, ARG), ({"top_k": 0}, ARG), ({"top_k": 65}, ARG),
+    ({"num_experts": 4, "top_k": 5, "n_group": 1}, ARG), ({"score_fn": 2}, ARG), ({"n_group": 7}, ARG),
+    ({"n_group": 0}, ARG), ({"topk_group": 9}, ARG), ({"topk_group": 0}, ARG), ({"group_score_topk": 0}, ARG),
+    ({"group_score_topk": 33}, ARG), ({"topk_group": 1, "top_k": 33}, ARG), ({"n_group": 128, "num_experts": 1024}, ARG),
+])
+def test_route_validation(L, kw, code):
+    cfg = _cfg(**kw)
+    assert L.moe_route(None, 10, ctypes.byref(cfg), None, None, None, 0, None) == code
+    assert L.moe_replay_route(None, 10, ctypes.byref(cfg), None, 10, None, None, None, None) == code
+
+
+def test_route_validation_other(L):
+    cfg = _cfg()
+    assert L.moe_route(None, 10, None, None, None, None, 0, None) == NULL
+    assert L.moe_route(None, -1, ctypes.byref(cfg), None, None, None, 0, None) == SHAPE
+    assert L.moe_route(None, 0, ctypes.byref(cfg), None, None, None, 0, None) == OK          # empty: no-op
+    assert L.moe_route(None, 10, ctypes.byref(cfg), None, None, ctypes.c_void_p(16), 9, None) == ARG  # record_ld < T
+    assert L.moe_replay_route(None, 10, ctypes.byref(cfg), None, 9, None, None, None, None) == ARG
+    assert L.moe_router_score_eval(None, 5, 2, None, None) == ARG
+    assert L.moe_router_score_eval(None, 5, 0, None, None) == NULL
+    assert L.moe_router_score_eval(None, 0, 0, None, None) == OK
+
+
+def test_gate_logits_validation(L):
+    assert L.moe_gate_logits(None, 0, None, None, 4, 128, 8, None, None) == NULL
+    assert L.moe_gate_logits(None, 0, None, None, 4, 100, 8, None, None) == SHAPE     # H % 8
+    assert L.moe_gate_logits(None, 0, None, None, 4, 128, 0, None, None) == SHAPE
+    assert L.moe_gate_logits(None, 2, None, None, 4, 128, 8, None, None) == DTYPE
+    assert L.moe_gate_logits(None, 1, None, None, 0, 128, 8, None, None) == OK
+
+
+def test_quant_validation(L):
+    assert L.moe_quant_fp8_block(None, 0, 1, 4, 100, 1, None, None, None) == SHAPE     # cols % 128
+    assert L.moe_quant_fp8_block(None, 0, 1, 100, 128, 128, None, None, None) == SHAPE # rows % 128
+    assert L.moe_quant_fp8_block(None, 0, 1, 128, 128, 64, None, None, None) == ARG
+    assert L.moe_quant_fp8_block(None, 2, 1, 128, 128, 1, None, None, None) == DTYPE
+    assert L.moe_quant_fp8_block(None, 0, 1, 128, 128, 1, None, None, None) == NULL
+    assert L.moe_quant_fp8_block(None, 0, 0, 128, 128, 1, None, None, None) == OK
+
+
+def test_dispatch_validation(L):
+    P = ctypes.c_void_p(256)  # never dereferenced: every case fails on the host first
+    args = lambda T=10, k=2, E=8, H=256, xq=None, ws=None, wsb=0: (P, T, k, E, 0, xq, xq, H, P, P, P, P, xq, xq, ws, wsb, None)
+    assert L.moe_dispatch(*args(E=1025)) == SHAPE
+    assert L.moe_dispatch(*args(k=0)) == SHAPE
+    assert L.moe_dispatch(*args(xq=P, H=200)) == SHAPE
+    assert L.moe_dispatch(*args()) == WS
+    assert L.moe_dispatch(*args(ws=P, wsb=16)) == WS
+    assert L.moe_dispatch(P, 10, 2, 8, 0, P, None, 256, P, P, P, P, P, P, P, 1 << 20, None) == NULL
+
+
+def test_gemm_validation(L):
+    P = ctypes.c_void_p(256)
+    g = lambda N=256, K=256, epi=0, od=1, ws=P, wsb=1 << 20, osc=None, groups=4: (
+        P, P, P, groups, 100, P, P, N, K, epi, P, od, osc, ws, wsb, None)
+    assert L.moe_grouped_gemm_fp8(*g(N=200)) == SHAPE
+    assert L.moe_grouped_gemm_fp8(*g(K=100)) == SHAPE
+    assert L.moe_grouped_gemm_fp8(*g(od=2)) == DTYPE
+    assert L.moe_grouped_gemm_fp8(*g(epi=1, od=1)) == DTYPE
+    assert L.moe_grouped_gemm_fp8(*g(epi=1, od=2, N=384)) == SHAPE    # F = 192 not a multiple of 128
+    assert L.moe_grouped_gemm_fp8(*g(epi=1, od=2)) == NULL            # out_scales missing
+    assert L.moe_grouped_gemm_fp8(*g(epi=7)) == ARG
+    assert L.moe_grouped_gemm_fp8(*g(groups=0)) == SHAPE
+    assert L.moe_grouped_gemm_fp8(*g(wsb=8)) == WS
+
+
+def test_combine_validation(L):
+    P = ctypes.c_void_p(256)
+    assert L.moe_combine(P, 1, P, P, 4, 2, 100, None, P, 1, None) == SHAPE
+    assert L.moe_combine(P, 2, P, P, 4, 2, 128, None, P, 1, None) == DTYPE
+    assert L.moe_combine(None, 1, P, P, 4, 2, 128, None, P, 1, None) == NULL
+    assert L.moe_combine(None, 1, None, None, 0, 2, 128, None, None, 1, None) == OK
+
+
+def test_binding_rejects_host_tensors(L):
+    x = torch.zeros(4, 128)
+    with pytest.raises(ValueError):
+        M.moe_quant_fp8_block(x, 1)
+    with pytest.raises(ValueError):
+        M.moe_gate_logits(x, torch.zeros(8, 128))
+
+
+def test_product_package_does_not_touch_the_oracle():
+    """The HIP path's package never imports or loads the oracle."""
+    pkg = os.path.join(ROOT, "block_scaled_fp8_top_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in src and "from oracle" not in src and "moe_oracle" not in src, f

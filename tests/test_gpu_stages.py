@@ -1,0 +1,370 @@
+"""Per-stage parity of the HIP path against the CPU oracle, at every workload's full size.
+
+Each stage gets the same seeded synthetic inputs on both sides.  Integer, byte and index outputs
+(logits of the router's fixed chain, routing indices and weights, FP8 codes and scales, counts,
+offsets, permutation) must match bit for bit; GEMM and combine outputs within a max-abs-normalised
+error of 2e-2.  Large outputs are compared on sampled rows that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_top_amd as M
+import oracle as O
+import synth
+from gpu_helpers import DEV, TOL, assert_equal, cfgs_for, host, rel_err, rows_host
+
+pytestmark = pytest.mark.gpu
+NAMES = ["tiny", "decode", "prefill", "longctx", "r3"]
+
+
+def _cleanup():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------- quantisation
+@pytest.mark.parametrize("name", NAMES)
+def test_quant_activations_1x128(name):
+    cfg = synth.CONFIGS[name]
+    x = synth.make_x(cfg, DEV)
+    q, s = M.moe_quant_fp8_block(x, 1)
+    rq, rs = O.moe_quant_fp8_block(host(x), 1)
+    assert_equal("codes", host(q), rq)
+    assert_equal("scales", host(s), rs)
+    del x, q, s
+    _cleanup()
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_quant_weights_128x128(name):
+    cfg = synth.CONFIGS[name]
+    experts = sorted({0, cfg.E - 1} | ({cfg.E} if cfg.shared else set()))
+    for e in experts:
+        w1, w2 = synth.make_expert(cfg, e, 0, DEV)
+        for w in (w1, w2):
+            q, s = M.moe_quant_fp8_block(w, 128)
+            rq, rs = O.moe_quant_fp8_block(host(w), 128)
+            assert_equal(f"W codes e={e}", host(q), rq)
+            assert_equal(f"W scales e={e}", host(s), rs)
+    # batched [2, N, K] call, bf16 input
+    wb = torch.stack([synth.make_expert(cfg, e, 0, DEV)[1] for e in experts[:2]]).to(torch.bfloat16)
+    q, s = M.moe_quant_fp8_block(wb, 128)
+    rq, rs = O.moe_quant_fp8_block(host(wb), 128)
+    assert_equal("batched codes", host(q), rq)
+    assert_equal("batched scales", host(s), rs)
+    _cleanup()
+
+
+def test_quant_edge_values():
+    """Zero blocks, signed zeros, a block whose amax is tiny, and values at code boundaries."""
+    x = torch.zeros((4, 384), dtype=torch.float32)
+    x[0, 128:256] = -0.0
+    x[1, :128] = torch.linspace(-448, 448, 128)
+    x[1, 128:256] = 1e-30
+    x[2, :] = torch.tensor([1.0625, 1.1875, -3.0, 0.1] * 96)
+    x[3, 256:] = synth.randn((128,), 5, synth.STAGE, part=30) * 1e4
+    q, s = M.moe_quant_fp8_block(x.to(DEV), 1)
+    rq, rs = O.moe_quant_fp8_block(x.numpy(), 1)
+    assert_equal("codes", host(q), rq)
+    assert_equal("scales", host(s), rs)
+
+
+# ----------------------------------------------------------------------------- gate logits
+@pytest.mark.parametrize("name", NAMES)
+def test_gate_logits(name):
+    cfg = synth.CONFIGS[name]
+    x = synth.make_x(cfg, DEV)
+    wg, b = synth.make_gate(cfg, 0, DEV)
+    z = M.moe_gate_logits(x, wg, b)
+    rows = np.arange(cfg.T) if cfg.T <= 256 else synth.sample_tokens(cfg.T, 96, cfg.seed)
+    rz = O.moe_gate_logits(host(x)[rows], host(wg), None if b is None else host(b))
+    assert_equal("logits", host(z)[rows], rz)
+    del x, z
+    _cleanup()
+
+
+def test_gate_logits_ragged_fp32():
+    """T and E not multiples of the register tiles, H not a multiple of the LDS chunk."""
+    T, H, E = 77, 136, 13
+    x = synth.randn((T, H), 6, synth.STAGE, part=31, device=DEV)
+    wg = synth.randn((E, H), 6, synth.STAGE, part=32, device=DEV, std=0.1)
+    b = synth.randn((E,), 6, synth.STAGE, part=33, device=DEV)
+    z = M.moe_gate_logits(x, wg, b)
+    assert_equal("logits", host(z), O.moe_gate_logits(host(x), host(wg), host(b)))
+    z0 = M.moe_gate_logits(x[:0], wg)
+    assert z0.shape == (0, E)
+
+
+# ----------------------------------------------------------------------------- router / replay
+@pytest.mark.parametrize("name", NAMES)
+def test_route_and_record(name):
+    cfg = synth.CONFIGS[name]
+    gcfg, ocfg = cfgs_for(cfg)
+    T, k = cfg.T, cfg.k
+    z = synth.make_logits(cfg, device=DEV)
+    payload = torch.full((2, k, T + 3), -5, dtype=torch.int32, device=DEV)
+    idx, w = M.moe_route(z, gcfg, record=payload[1])
+    opay = np.full((k, T + 3), -5, np.int32)
+    oidx, ow = O.moe_route(host(z), ocfg, record=opay)
+    assert_equal("idx", host(idx), oidx)
+    assert_equal("weights", host(w), ow)
+    assert_equal("record", host(payload[1]), opay)
+    assert np.all(host(payload[0]) == -5)
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_replay(name):
+    cfg = synth.CONFIGS[name]
+    gcfg, ocfg = cfgs_for(cfg)
+    T, k = cfg.T, cfg.k
+    z = synth.make_logits(cfg, device=DEV)
+    payload = torch.empty((k, T), dtype=torch.int32, device=DEV)
+    idx, w = M.moe_route(z, gcfg, record=payload)
+    opay = np.empty((k, T), np.int32)
+    O.moe_route(host(z), ocfg, record=opay)
+    assert_equal("record", host(payload), opay)
+    bad = torch.zeros(1, dtype=torch.int32, device=DEV)
+    # replay of the recorded routing on the same logits reproduces the router bit for bit
+    ridx, rw = M.moe_replay_route(z, gcfg, payload, bad_count=bad)
+    assert_equal("replay idx", host(ridx), host(idx))
+    assert_equal("replay w", host(rw), host(w))
+    # on different logits: indices kept, weights from the current logits
+    z2 = synth.make_logits(cfg, device=DEV, part=1)
+    ridx2, rw2 = M.moe_replay_route(z2, gcfg, payload, bad_count=bad)
+    oidx2, ow2, obad = O.moe_replay_route(host(z2), ocfg, opay)
+    assert_equal("replay2 idx", host(ridx2), oidx2)
+    assert_equal("replay2 w", host(rw2), ow2)
+    assert int(bad.item()) == 0 and obad == 0
+    # planted bad entries (out of range, negative, repeated) in both copies
+    bad_tokens = [1, T // 2, T - 1]
+    opay[0, 1] = cfg.E
+    opay[k - 1, T // 2] = -3
+    opay[min(1, k - 1), T - 1] = opay[0, T - 1] if k > 1 else cfg.E + 7
+    gpay = torch.from_numpy(opay).to(DEV)
+    ridx3, rw3 = M.moe_replay_route(z2, gcfg, gpay, bad_count=bad)
+    oidx3, ow3, obad3 = O.moe_replay_route(host(z2), ocfg, opay)
+    assert obad3 == len(bad_tokens) and int(bad.item()) == obad3
+    assert_equal("replay3 idx", host(ridx3), oidx3)
+    assert_equal("replay3 w", host(rw3), ow3)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill"])
+def test_route_ties(name):
+    """Logits on a coarse grid: many exact ties, broken toward the lower expert index."""
+    cfg = synth.CONFIGS[name]
+    gcfg, ocfg = cfgs_for(cfg)
+    z = synth.tie_logits(4096, cfg.E, 5, cfg.seed, device=DEV)
+    idx, w = M.moe_route(z, gcfg)
+    oidx, ow = O.moe_route(host(z), ocfg)
+    assert_equal("idx", host(idx), oidx)
+    assert_equal("w", host(w), ow)
+
+
+@pytest.mark.parametrize("E,k,score,ng,tg,gt", [(1024, 64, 0, 1, 1, 2), (1024, 8, 1, 64, 7, 3), (96, 5, 1, 3, 2, 1),
+                                                (2, 2, 0, 1, 1, 2), (1, 1, 1, 1, 1, 2), (130, 3, 0, 1, 1, 2)])
+def test_route_extreme_shapes(E, k, score, ng, tg, gt):
+    """Largest supported E and k, E not a multiple of 64, many groups, k = E, one token."""
+    for T in (1, 333):
+        z = synth.randn((T, E), 7, synth.STAGE, part=34, device=DEV) * 3
+        gcfg = M.router_cfg(E, k, score, True, ng, tg, gt)
+        ocfg = O.router_cfg(E, k, score, True, ng, tg, gt)
+        idx, w = M.moe_route(z, gcfg)
+        oidx, ow = O.moe_route(host(z), ocfg)
+        assert_equal(f"idx T={T}", host(idx), oidx)
+        assert_equal(f"w T={T}", host(w), ow)
+
+
+# ----------------------------------------------------------------------------- dispatch
+@pytest.mark.parametrize("name", NAMES)
+def test_dispatch(name):
+    cfg = synth.CONFIGS[name]
+    T, k, E, H = cfg.T, cfg.k, cfg.E, cfg.H
+    idx = synth.routing_indices(cfg, T).numpy()
+    idx[3, 0] = -1                      # a dropped slot (as left by a rejected replay token)
+    idx[T - 1, :] = -1
+    xq = synth.random_codes((T, H), cfg.seed, 40, device=DEV)
+    xs = synth.random_scales((T, H // 128), cfg.seed, 41, device=DEV)
+    d = M.moe_dispatch(torch.from_numpy(idx).to(DEV), E, cfg.shared, xq, xs)
+    oc, oo, od, osrc = O.moe_dispatch(idx, E, cfg.shared)
+    assert_equal("counts", host(d.counts), oc)
+    assert_equal("offsets", host(d.offsets), oo)
+    assert_equal("dest_row", host(d.dest_row), od)
+    nrows = int(oo[-1])
+    assert_equal("src_token", host(d.src_token)[:nrows], osrc)
+    rows = np.arange(nrows) if nrows <= 4096 else np.unique(np.concatenate(
+        [synth.sample_tokens(nrows, 2048, cfg.seed), oo[:-1][oo[:-1] < nrows], np.maximum(oo[1:] - 1, 0)]))
+    xqh, xsh = host(xq), host(xs)
+    assert_equal("aq rows", rows_host(d.aq, rows), O.permute_rows(xqh, osrc[rows]))
+    assert_equal("as rows", rows_host(d.as_, rows), O.permute_rows(xsh, osrc[rows]))
+    # index-only mode
+    d2 = M.moe_dispatch(torch.from_numpy(idx).to(DEV), E, cfg.shared)
+    assert_equal("dest_row (index only)", host(d2.dest_row), od)
+    del xq, xs, d, d2
+    _cleanup()
+
+
+def test_dispatch_all_one_expert_and_tiny():
+    """Every slot on one expert (all others empty), and a single token."""
+    for T, k, E in ((5000, 4, 16), (1, 3, 7)):
+        idx = np.stack([np.full(T, 2, np.int32)] + [np.full(T, (2 + j) % E, np.int32) for j in range(1, k)], 1)
+        d = M.moe_dispatch(torch.from_numpy(idx).to(DEV), E, True)
+        oc, oo, od, osrc = O.moe_dispatch(idx, E, True)
+        assert_equal("counts", host(d.counts), oc)
+        assert_equal("offsets", host(d.offsets), oo)
+        assert_equal("dest", host(d.dest_row), od)
+        assert_equal("src", host(d.src_token)[:oo[-1]], osrc)
+
+
+# ----------------------------------------------------------------------------- grouped GEMM
+def _gemm_case(cfg, which, part):
+    """Random codes/scales with the workload's group sizes; offsets from the oracle dispatch of
+    synthetic routing indices."""
+    G = cfg.groups
+    N, K = (2 * cfg.F, cfg.H) if which == "w1" else (cfg.H, cfg.F)
+    idx = synth.routing_indices(cfg, cfg.T, seed_part=part).numpy()
+    _, offsets, _, _ = O.moe_dispatch(idx, cfg.E, cfg.shared)
+    rows = int(offsets[-1])
+    a = synth.random_codes((rows, K), cfg.seed, 50 + part, device=DEV)
+    as_ = synth.random_scales((rows, K // 128), cfg.seed, 51 + part, device=DEV, lo=2.0 ** -10, hi=2.0 ** -6)
+    b = synth.random_codes((G, N, K), cfg.seed, 52 + part, device=DEV)
+    bs = synth.random_scales((G, N // 128, K // 128), cfg.seed, 53 + part, device=DEV, lo=2.0 ** -10, hi=2.0 ** -6)
+    return offsets, a, as_, b, bs, N, K
+
+
+def _sample_rows(offsets, n, seed):
+    rows = int(offsets[-1])
+    nonempty = [g for g in range(len(offsets) - 1) if offsets[g + 1] > offsets[g]]
+    pick = set()
+    rng = np.random.default_rng(seed)
+    for g in rng.choice(nonempty, size=min(6, len(nonempty)), replace=False):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        pick |= {lo, hi - 1, min(lo + 127, hi - 1), min(lo + 128, hi - 1)}   # group edges and a tile edge
+    pick |= set(synth.sample_tokens(rows, n, seed).tolist())
+    return np.array(sorted(pick))
+
+
+def _oracle_rows(a, as_, offsets, b, bs, rows):
+    """fp64 reference rows, one group's dequantised weights at a time."""
+    grp = np.searchsorted(offsets, rows, side="right") - 1
+    a_h, as_h = rows_host(a, rows), rows_host(as_, rows)
+    pos = {int(r): i for i, r in enumerate(rows)}
+    out = {}
+    for g in np.unique(grp):
+        rr = rows[grp == g]
+        ii = [pos[int(r)] for r in rr]
+        wd = O.dequant_weight(host(b[g]), host(bs[g]))
+        ref = O.dequant_act(a_h[ii], as_h[ii]) @ wd.T
+        for r, v in zip(rr, ref):
+            out[int(r)] = v
+    return np.stack([out[int(r)] for r in rows]), grp
+
+
+@pytest.mark.parametrize("name", NAMES)
+@pytest.mark.parametrize("which", ["w1", "w2"])
+def test_grouped_gemm_store(name, which):
+    cfg = synth.CONFIGS[name]
+    offsets, a, as_, b, bs, N, K = _gemm_case(cfg, which, 0 if which == "w1" else 5)
+    goff = torch.from_numpy(offsets).to(DEV)
+    y32 = M.moe_grouped_gemm_fp8(a, as_, goff, b, bs, M.MOE_EPI_STORE, torch.float32)
+    ybf = M.moe_grouped_gemm_fp8(a, as_, goff, b, bs, M.MOE_EPI_STORE, torch.bfloat16)
+    rows = _sample_rows(offsets, 24, cfg.seed)
+    ref, _ = _oracle_rows(a, as_, offsets, b, bs, rows)
+    e32 = rel_err(rows_host(y32, rows), ref)
+    ebf = rel_err(rows_host(ybf, rows), ref)
+    print(f"{name} {which}: fp32-out err {e32:.3e}, bf16-out err {ebf:.3e}")
+    # uniformly random codes are heavy-tailed (log-uniform magnitudes), so fp32 accumulation error
+    # relative to max |ref| reaches ~1e-4; the contract bound for GEMM outputs is TOL
+    assert e32 < 1e-3 and ebf < TOL
+    del a, as_, b, bs, y32, ybf
+    _cleanup()
+
+
+def test_grouped_gemm_exact_integers():
+    """Integer codes in [-8,8] with unit or common power-of-two scales: every partial and total
+    is an exact fp32 integer, so the result is bitwise equal in any accumulation order."""
+    offsets = np.array([0, 130, 130, 131, 400, 657], np.int64)   # an empty group, a 1-row group, ragged tails
+    G, N, K = 5, 384, 1024
+    rows = int(offsets[-1])
+    a, ai = synth.integer_codes((rows, K), 60, 0, device=DEV)
+    b, bi = synth.integer_codes((G, N, K), 60, 1, device=DEV)
+    for sa, sb in ((1.0, 1.0), (0.25, 8.0)):
+        as_ = torch.full((rows, K // 128), sa, dtype=torch.float32, device=DEV)
+        bs = torch.full((G, N // 128, K // 128), sb, dtype=torch.float32, device=DEV)
+        y = M.moe_grouped_gemm_fp8(a, as_, torch.from_numpy(offsets.astype(np.int32)).to(DEV), b, bs,
+                                   M.MOE_EPI_STORE, torch.float32)
+        ref = O.moe_grouped_gemm_fp8(host(a), host(as_), offsets, host(b), host(bs))
+        assert_equal(f"exact integer GEMM (scales {sa},{sb})", host(y), ref.astype(np.float32))
+        assert np.array_equal(ref, sa * sb * np.concatenate(
+            [ai[offsets[g]:offsets[g + 1]].numpy() @ bi[g].numpy().T for g in range(G)]))
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_grouped_gemm_swiglu_quant(name):
+    cfg = synth.CONFIGS[name]
+    offsets, a, as_, b, bs, N, K = _gemm_case(cfg, "w1", 9)
+    F = N // 2
+    goff = torch.from_numpy(offsets).to(DEV)
+    hq, hs = M.moe_grouped_gemm_fp8(a, as_, goff, b, bs, M.MOE_EPI_SWIGLU_QUANT)
+    rows = _sample_rows(offsets, 16, cfg.seed + 1)
+    g1, _ = _oracle_rows(a, as_, offsets, b, bs, rows)
+    h = O.swiglu(g1, F)
+    rq, rs = O.moe_quant_fp8_block(h, 1)
+    gq, gs = rows_host(hq, rows), rows_host(hs, rows)
+    # h depends on the GEMM's last bits (fp32 accumulation of heavy-tailed random codes, ~1e-4
+    # relative to the block max), so scales agree to that level and codes to within one e4m3 step
+    assert np.max(np.abs(gs / rs - 1)) < 1e-3
+    tab = O.e4m3_table()
+    dg = tab[gq] * np.repeat(gs, 128, 1)
+    dr = tab[rq] * np.repeat(rs, 128, 1)
+    step = np.abs(dr) / 8 + np.repeat(rs, 128, 1) * 2.0 ** -9
+    assert np.all(np.abs(dg - dr) <= step * 1.0001)
+    frac = np.mean(gq != rq)
+    print(f"{name}: h code mismatch fraction {frac:.2e}, deq(h) err vs fp64 h {rel_err(dg, h):.3e}")
+    assert frac < 1e-2
+    del a, as_, b, bs, hq, hs
+    _cleanup()
+
+
+# ----------------------------------------------------------------------------- combine
+@pytest.mark.parametrize("name", NAMES)
+def test_combine(name):
+    cfg = synth.CONFIGS[name]
+    T, k, E, H = cfg.T, cfg.k, cfg.E, cfg.H
+    idx = synth.routing_indices(cfg, T, seed_part=3).numpy()
+    idx[2, 1 % k] = -1
+    _, offsets, dest, _ = O.moe_dispatch(idx, E, cfg.shared)
+    rows = int(offsets[-1])
+    act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
+    y = synth.randn((rows, H), cfg.seed, synth.STAGE, part=70, device=DEV).to(act)
+    w = torch.rand((T, k), generator=torch.Generator().manual_seed(cfg.seed), dtype=torch.float32)
+    gdest = torch.from_numpy(dest).to(DEV)
+    goff = torch.from_numpy(offsets).to(DEV)
+    shared = goff[E:E + 1] if cfg.shared else None
+    out = M.moe_combine(y, gdest, w.to(DEV), shared)
+    toks = np.arange(T) if T <= 512 else synth.sample_tokens(T, 256, cfg.seed)
+    # the rows those tokens read, gathered on the device and renumbered
+    need = np.unique(dest[toks][dest[toks] >= 0])
+    yh = rows_host(y, need)
+    ren = np.full(rows, -1, np.int64)
+    ren[need] = np.arange(len(need))
+    dsub = np.where(dest[toks] >= 0, ren[np.maximum(dest[toks], 0)], -1).astype(np.int32)
+    ysh = rows_host(y, offsets[E] + toks) if cfg.shared else None
+    ref = O.moe_combine(yh, dsub, w.numpy()[toks], ysh)
+    err = rel_err(rows_host(out, toks), ref)
+    print(f"{name}: combine err {err:.3e}")
+    assert err < TOL
+    # fp32 in/out is accurate to fp32 rounding
+    out32 = M.moe_combine(y.float(), gdest, w.to(DEV), shared, out_dtype=torch.float32)
+    assert rel_err(rows_host(out32, toks), ref) < 1e-5
+    del y, out, out32
+    _cleanup()
+
+
+def test_combine_pure_gather_is_exact():
+    T, H = 300, 256
+    y = synth.randn((T, H), 8, synth.STAGE, part=71, device=DEV)
+    perm = torch.randperm(T, generator=torch.Generator().manual_seed(8)).to(torch.int32)
+    out = M.moe_combine(y, perm[:, None].contiguous().to(DEV), torch.ones((T, 1), device=DEV), None,
+                        out_dtype=torch.float32)
+    assert_equal("gather", host(out), host(y)[perm.numpy()])
