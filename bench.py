@@ -23,7 +23,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0       # dense fp8 MFMA (published, no sparsity)
-PEAK_FP32_TFLOPS = 78.6        # fp32 FMA without packed instructions: 256 CU x 4 SIMD x 16 lanes x 2 x 2.4 GHz
+PEAK_FP32_TFLOPS = 157.3       # published fp32 vector peak (a non-packed fma loop reaches 110 on the box)
 RIDGE_FP8 = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 
 STAGES = ["gate_logits", "route", "quant_x", "dispatch", "gemm1_swiglu", "gemm2", "combine"]

@@ -111,6 +111,123 @@ __global__ __launch_bounds__(NT) void gate_logits_kernel(const void* __restrict_
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Small problems (decode-sized T*E): one wavefront per 8 tokens x 8 experts, one logit per lane.
+// Each output is a chain of H dependent fmas, so the launch is latency-bound; chunks of 256 columns
+// of x and Wg are copied global -> LDS by DMA (global_load_lds) into a 4-slot ring three chunks
+// ahead of the chain, so the chain never waits on memory.  Wg rows are padded by 16 bytes (bank
+// spread); x rows are stored in pairs, one DMA instruction per pair.
+constexpr int CH = 256;                       // columns per chunk
+constexpr int NSLOT = 4;
+constexpr int WROW = CH * 4 + 16;             // padded Wg row in LDS (bytes)
+
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(g) : "memory", "m0");
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(64) void gate_logits_chain_kernel(const void* __restrict__ xv, const float* __restrict__ wg,
+                                                               const float* __restrict__ bias, int64_t T, int H,
+                                                               int E, float* __restrict__ z) {
+  constexpr int XB = BF16 ? 2 : 4;                       // bytes per x element
+  constexpr int XPAIR = 2 * CH * XB + 64;                // two x rows per DMA unit (+64 B pad between pairs)
+  constexpr int XINST = BF16 ? 1 : 2;                    // DMA instructions per x row pair
+  constexpr int XSLOT = 4 * XPAIR, WSLOT = 8 * WROW;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[NSLOT][XSLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t ws[NSLOT][WSLOT];
+  const int lane = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * 8;
+  const int e0 = blockIdx.y * 8;
+  const int tt = lane >> 3, ee = lane & 7;
+  const int nchunk = (H + CH - 1) / CH;
+
+  // DMA sources (rows clamped into range; columns past H fetch column 0 of the same row).
+  //  bf16: instruction p carries rows 2p (lanes 0-31) and 2p+1 (lanes 32-63), 8 columns per lane;
+  //  fp32: instruction (p, q) carries row 2p+q, 4 columns per lane.
+  // In LDS, row r of a slot starts at (r / 2) * XPAIR + (r % 2) * CH * XB.
+  const uint32_t xbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&xs[0][0]);
+  const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&ws[0][0]);
+  const char* wrow[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) wrow[r] = reinterpret_cast<const char*>(wg + (int64_t)min(e0 + r, E - 1) * H);
+
+  auto issue = [&](int c, int slot) {
+    const int h0 = c * CH;
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr)
+#pragma unroll
+      for (int q = 0; q < XINST; ++q) {
+        const int row = 2 * pr + (BF16 ? (lane >> 5) : q);
+        const int col = BF16 ? (lane & 31) * 8 : lane * 4;
+        const int h = h0 + col < H ? h0 + col : 0;
+        const int64_t t = min(t0 + row, T - 1);
+        dma16(reinterpret_cast<const char*>(xv) + (t * H + h) * XB, xbase + slot * XSLOT + pr * XPAIR + q * CH * XB);
+      }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int h = h0 + lane * 4 < H ? h0 + lane * 4 : 0;
+      dma16(wrow[r] + (int64_t)h * 4, wbase + slot * WSLOT + r * WROW);
+    }
+  };
+
+  for (int c = 0; c < NSLOT - 1 && c < nchunk; ++c) issue(c, c);
+  float acc = 0.0f;
+  for (int c = 0; c < nchunk; ++c) {
+    const int left = min(nchunk - 1 - c, NSLOT - 2);   // chunks issued after c that may stay in flight
+    if (left == 2) {
+      if (BF16) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+    } else if (left == 1) {
+      if (BF16) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (c + NSLOT - 1 < nchunk) issue(c + NSLOT - 1, (c + NSLOT - 1) % NSLOT);
+    const int slot = c % NSLOT;
+    const uint8_t* xr = &xs[slot][(tt >> 1) * XPAIR + (tt & 1) * CH * XB];
+    const uint8_t* wr = &ws[slot][ee * WROW];
+    const int hc = min(CH, H - c * CH);
+#pragma unroll 4
+    for (int hh = 0; hh < hc; hh += 8) {
+      float xv8[8];
+      if (BF16) {
+        const uint4 u = *reinterpret_cast<const uint4*>(xr + hh * 2);
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xv8[2 * q] = __uint_as_float(w4[q] << 16);
+          xv8[2 * q + 1] = __uint_as_float(w4[q] & 0xFFFF0000u);
+        }
+      } else {
+        const float4 a = *reinterpret_cast<const float4*>(xr + hh * 4);
+        const float4 b = *reinterpret_cast<const float4*>(xr + hh * 4 + 16);
+        xv8[0] = a.x; xv8[1] = a.y; xv8[2] = a.z; xv8[3] = a.w; xv8[4] = b.x; xv8[5] = b.y; xv8[6] = b.z; xv8[7] = b.w;
+      }
+      const float4 w0 = *reinterpret_cast<const float4*>(wr + hh * 4);
+      const float4 w1 = *reinterpret_cast<const float4*>(wr + hh * 4 + 16);
+      acc = __builtin_fmaf(xv8[0], w0.x, acc);
+      acc = __builtin_fmaf(xv8[1], w0.y, acc);
+      acc = __builtin_fmaf(xv8[2], w0.z, acc);
+      acc = __builtin_fmaf(xv8[3], w0.w, acc);
+      acc = __builtin_fmaf(xv8[4], w1.x, acc);
+      acc = __builtin_fmaf(xv8[5], w1.y, acc);
+      acc = __builtin_fmaf(xv8[6], w1.z, acc);
+      acc = __builtin_fmaf(xv8[7], w1.w, acc);
+    }
+  }
+  const int64_t t = t0 + tt;
+  const int e = e0 + ee;
+  if (t < T && e < E) {
+    float v = acc;
+    if (bias) v = v + bias[e];
+    z[t * E + e] = v;
+  }
+}
+
 template <int TT, int TE>
 int launch(const void* x, bool bf16, const float* wg, const float* bias, int64_t T, int H, int E, float* z,
            hipStream_t st) {
@@ -134,6 +251,15 @@ extern "C" int moe_gate_logits(const void* x, int x_dtype, const float* wg, cons
   if (E > 65535 * 16 || T > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
   const bool bf16 = x_dtype == MOE_BF16;
   hipStream_t st = as_stream(stream);
+  if (T * (int64_t)E <= 131072) {
+    dim3 grid((unsigned)ceil_div64(T, 8), (unsigned)ceil_div64(E, 8));
+    if (bf16)
+      gate_logits_chain_kernel<true><<<grid, 64, 0, st>>>(x, wg, bias, T, H, E, logits);
+    else
+      gate_logits_chain_kernel<false><<<grid, 64, 0, st>>>(x, wg, bias, T, H, E, logits);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+  }
   // Larger register tiles amortise LDS reads; use them only when they still give >= 512
   // workgroups (two per CU), because each output is one long dependent chain.
   const int64_t wg44 = ceil_div64(T, 64) * ceil_div64(E, 64);
