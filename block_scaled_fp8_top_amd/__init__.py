@@ -67,7 +67,7 @@ def lib():
         "moe_router_score_eval": [P, I64, ctypes.c_int, P, P],
         "moe_quant_fp8_block": [P, ctypes.c_int, I64, I64, I32, I32, P, P, P],
         "moe_dispatch": [P, I64, I32, I32, I32, P, P, I32, P, P, P, P, P, P, P, SZ, P],
-        "moe_grouped_gemm_fp8": [P, P, P, I32, I64, P, P, I32, I32, I32, P, ctypes.c_int, P, P, SZ, P],
+        "moe_grouped_gemm_fp8": [P, P, P, I32, I64, P, P, I32, I32, I32, I32, P, ctypes.c_int, P, P, SZ, P],
         "moe_combine": [P, ctypes.c_int, P, P, I64, I32, I32, P, P, ctypes.c_int, P],
         "moe_workspace_bytes": [ctypes.c_int, I64, I32, I32, I32, I32],
         "moe_status_str": [ctypes.c_int],
@@ -270,9 +270,10 @@ def moe_dispatch(topk_idx: torch.Tensor, num_experts: int, append_shared: bool, 
 
 def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tensor, b: torch.Tensor, bs: torch.Tensor,
                          epilogue: int = MOE_EPI_STORE, out_dtype=torch.bfloat16, out=None, out_scales=None,
-                         workspace: Optional[torch.Tensor] = None, stream=None):
+                         workspace: Optional[torch.Tensor] = None, stream=None, tile_rows: int = 0):
     """a [max_rows,K] uint8, as_ [max_rows,K/128], offsets [G+1] (device), b [G,N,K] uint8, bs [G,N/128,K/128].
-    STORE -> out [max_rows,N] (bf16/fp32); SWIGLU_QUANT -> (h codes [max_rows,N/2] uint8, scales [max_rows,N/256])."""
+    STORE -> out [max_rows,N] (bf16/fp32); SWIGLU_QUANT -> (h codes [max_rows,N/2] uint8, scales [max_rows,N/256]).
+    tile_rows: 32 or 128 rows per workgroup tile, 0 = chosen from the average group size."""
     max_rows, K = a.shape
     G, N, Kb = b.shape
     if Kb != K:
@@ -298,7 +299,8 @@ def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tens
         out = torch.empty((max_rows, F), dtype=FP8, device=dev) if out is None else _dev(out, "out", FP8, (max_rows, F))
         osc = torch.empty((max_rows, F // 128), dtype=torch.float32, device=dev) if out_scales is None else \
             _dev(out_scales, "out_scales", torch.float32, (max_rows, F // 128))
-    _check(lib().moe_grouped_gemm_fp8(_p(a), _p(as_), _p(offsets), G, max_rows, _p(b), _p(bs), N, K, epilogue, _p(out),
+    _check(lib().moe_grouped_gemm_fp8(_p(a), _p(as_), _p(offsets), G, max_rows, _p(b), _p(bs), N, K, epilogue,
+                                      tile_rows, _p(out),
                                       code, _p(osc), _p(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream)), "moe_grouped_gemm_fp8")
     return out if epilogue == MOE_EPI_STORE else (out, osc)

@@ -6,19 +6,25 @@
 // every MFMA produces a fresh 128-wide partial P that is promoted into the fp32 accumulator with
 // its scale product: acc = fma(P, as * bs, acc).
 //
-// Workgroup tile: BM = 128 rows x BN = 256 (virtual) columns, 8 wavefronts in a 2 x 4 grid, each
-// computing 64 x 64 as 4 x 4 MFMA tiles of 16 x 16.
+// Workgroup tile: BM rows x BN = 256 (virtual) columns, 8 wavefronts.  Two row-tile heights:
+//   BM = 128: waves in a 2 x 4 grid, each 64 x 64 (4 x 4 MFMA tiles of 16 x 16), 3-stage LDS ring
+//             (48 KB per stage) - for groups of hundreds of rows, where the tile's operand bytes per
+//             flop decide the speed;
+//   BM = 32:  waves in a 1 x 8 grid, each 32 x 32 (2 x 2 MFMA tiles), 4-stage ring (36 KB per
+//             stage) - for groups of a few dozen rows (decode), where the kernel streams the
+//             weights: a 128-row tile would spend most of its DMA and LDS on rows past the group
+//             end, and the deeper ring keeps more weight bytes in flight per CU.
 //
 // Data movement: the A and B K-slices (128 bytes per row) and the tile's activation scales go
-// straight from global memory into a 3-stage LDS ring with global_load_lds (no registers in
-// between), issued two K steps ahead; each wavefront waits for its own loads with an explicit
-// vmcnt and a bare s_barrier publishes the stage (a __syncthreads fence would drain every load in
-// flight).  Rows are stored with a 16-byte-chunk XOR swizzle (chunk c of row r at slot
-// c ^ ((r >> 1) & 7): the 16 rows one MFMA operand read touches then hit 16 distinct bank groups),
-// applied on the global side: lane L of a DMA instruction writes LDS slot L, so it
-// fetches the chunk that belongs there.  Weight scales travel through scalar loads in a 3-deep ring.
+// straight from global memory into the LDS ring with global_load_lds (no registers in between),
+// issued NSTAGE-1 K steps ahead; each wavefront waits for its own loads with an explicit vmcnt and
+// a bare s_barrier publishes the stage (a __syncthreads fence would drain every load in flight).
+// Rows are stored with a 16-byte-chunk XOR swizzle (chunk c of row r at slot c ^ ((r >> 1) & 7):
+// the 16 rows one MFMA operand read touches then hit 16 distinct bank groups), applied on the
+// global side: lane L of a DMA instruction writes LDS slot L, so it fetches the chunk that belongs
+// there.  Weight scales travel through scalar loads in a ring as deep as the DMA lookahead.
 //
-// Tile order: a one-workgroup kernel turns `offsets` into the list of 128-row tiles (never
+// Tile order: a one-workgroup kernel turns `offsets` into the list of BM-row tiles (never
 // straddling a group).  The grid is one-dimensional; hardware workgroup ids are dealt to the 8
 // XCDs round-robin, so they are renumbered to make each XCD's ids contiguous, and logical tiles
 // run expert by expert, N-tile-major, so the workgroups alive on one XCD share the same A rows and
@@ -26,19 +32,35 @@
 //
 // Epilogue STORE writes out in bf16 or fp32.  Epilogue SWIGLU_QUANT maps the 256 virtual columns
 // of a tile to 128 gate columns [f0, f0+128) and the matching 128 up columns [F+f0, F+f0+128); each
-// wave holds gate and up of the same 32 h columns in the same lanes, forms h = silu(gate) * up in
-// fp32, and the tile's 128 h columns are one 1x128 quantisation block (amax across the 4 waves of
-// a row through LDS).
+// wave holds gate and up of the same h columns in the same lanes, forms h = silu(gate) * up in
+// fp32, and the tile's 128 h columns are one 1x128 quantisation block (amax across the waves of a
+// row through LDS).
 #include <algorithm>
 
 #include "common.h"
 
 namespace {
 
-constexpr int BM = 128, BN = 256, BK = 128;
+constexpr int BN = 256, BK = 128;
 constexpr int NTHREADS = 512;
-constexpr int NSTAGE = 3;
-constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
+constexpr int MIN_BM = 32;
+
+template <int BM_>
+struct Tile {
+  static constexpr int BM = BM_;
+  static constexpr int WM = BM_ >= 128 ? 2 : 1;             // wave grid WM x WN
+  static constexpr int WN = 8 / WM;
+  static constexpr int MS = BM_ / WM / 16;                   // 16 x 16 MFMA tiles per wave along M
+  static constexpr int NS = BN / WN / 16;                    // ... along N
+  static constexpr int NSTAGE = BM_ >= 128 ? 3 : 4;
+  static constexpr int A_BYTES = BM_ * BK, B_BYTES = BN * BK;
+  static constexpr int A_INSTR = BM_ / 8;                    // 1 KB DMA instructions per A slice
+  static constexpr int A_PW = A_INSTR >= 8 ? A_INSTR / 8 : 1;
+  static constexpr int S_INSTR = BM_ >= 64 ? BM_ / 64 : 1;   // 256-byte scale DMA instructions
+  static constexpr int AS_W = BM_ >= 64 ? BM_ : 64;          // floats per scale-ring slot
+  static_assert(WM * WN == 8 && MS >= 1 && NS >= 2 && NS % 2 == 0, "tile shape");
+  static_assert(A_INSTR % 8 == 0 || A_INSTR < 8, "A slice split");
+};
 
 // Global -> LDS DMA of 16 (or 4) bytes per lane: lane L's bytes land at lds_addr + 16 L (4 L).
 // Issued through inline assembly so that the compiler's conservative wait insertion (it cannot tell
@@ -58,7 +80,7 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chu
 
 // ------------------------------------------------------------------------------------------------
 // tiles[i] = {group, first row, index of the group's first tile, number of tiles of the group}
-__global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restrict__ offsets, int groups,
+__global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restrict__ offsets, int groups, int bm,
                                                         int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
                                                         int max_tiles) {
   __shared__ int part[1024];
@@ -68,7 +90,7 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
   for (int g0 = 0; g0 < groups; g0 += 1024) {
     const int g = g0 + threadIdx.x;
     int nt = 0;
-    if (g < groups) nt = (offsets[g + 1] - offsets[g] + BM - 1) / BM;
+    if (g < groups) nt = (offsets[g + 1] - offsets[g] + bm - 1) / bm;
     part[threadIdx.x] = nt;
     __syncthreads();
     for (int o = 1; o < 1024; o <<= 1) {
@@ -79,7 +101,7 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
     }
     const int start = carry + part[threadIdx.x] - nt;
     if (g < groups)
-      for (int i = 0; i < nt && start + i < max_tiles; ++i) tiles[start + i] = make_int4(g, offsets[g] + i * BM, start, nt);
+      for (int i = 0; i < nt && start + i < max_tiles; ++i) tiles[start + i] = make_int4(g, offsets[g] + i * bm, start, nt);
     __syncthreads();
     if (threadIdx.x == 1023) carry += part[1023];
     __syncthreads();
@@ -87,25 +109,33 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
   if (threadIdx.x == 0) *ntiles = min(carry, max_tiles);
 }
 
-// wait until at most n of this wave's vector memory instructions are outstanding (immediate operand)
+// wait until at most n of this wave's vector memory instructions are outstanding (n is
+// wave-uniform; s_waitcnt takes an immediate)
 __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+#define WAIT_CASE(N) \
+  case N: asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory"); break;
+    WAIT_CASE(1) WAIT_CASE(2) WAIT_CASE(3) WAIT_CASE(4) WAIT_CASE(5) WAIT_CASE(6) WAIT_CASE(7) WAIT_CASE(8)
+    WAIT_CASE(9) WAIT_CASE(10) WAIT_CASE(11) WAIT_CASE(12) WAIT_CASE(13) WAIT_CASE(14) WAIT_CASE(15)
+#undef WAIT_CASE
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
 }
 
 // ------------------------------------------------------------------------------------------------
-template <int EPI, bool OUT_BF16>
+template <int BM, int EPI, bool OUT_BF16>
 __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const int32_t* __restrict__ offsets,
     const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles, int ny, const uint8_t* __restrict__ b,
     const float* __restrict__ bs, int N, int K, void* __restrict__ out, float* __restrict__ out_scales) {
+  using T = Tile<BM>;
+  constexpr int WM = T::WM, WN = T::WN, MS = T::MS, NS = T::NS, HS = NS / 2, NSTAGE = T::NSTAGE;
+  constexpr int A_BYTES = T::A_BYTES, B_BYTES = T::B_BYTES, AS_W = T::AS_W;
+  constexpr int WROWS = MS * 16;   // rows per wave
   __shared__ __attribute__((aligned(1024))) uint8_t a_lds[NSTAGE][A_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t b_lds[NSTAGE][B_BYTES];
-  __shared__ __attribute__((aligned(16))) float as_lds[4][BM];   // scale ring: slot kb & 3
-  __shared__ float red[2][4][64];
+  __shared__ __attribute__((aligned(16))) float as_lds[4][AS_W];   // scale ring: slot kb & 3
+  __shared__ float red[WM][WN][WROWS];
 
   // ---- logical tile: XCD-contiguous renumbering, then expert-major, N-tile-major order
   const int nwg = gridDim.x;
@@ -123,20 +153,26 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   const int KB = K / BK;
   const int F = N / 2;                                   // SwiGLU only
   const int n0 = nt_idx * (EPI == 1 ? 128 : BN);         // first h column (SwiGLU) or output column
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
 
   const uint8_t* bg = b + (size_t)g * N * K;
   const float* bsg = bs + (size_t)g * (N / 128) * KB;
 
-  // ---- this lane's DMA sources: A rows j*8 + lane/8 for j = 2*wave + {0,1}; B rows for j = 4*wave + {0..3}
+  // ---- this lane's DMA sources.  A slice: instruction i covers rows 8i .. 8i+7; wave w issues
+  // instructions w*A_PW + j (or just w, for slices of fewer than 8 instructions).  B slice:
+  // instructions 4w .. 4w+3.  Lane: row 8i + lane/8, 16-byte chunk lane%8 (swizzled).
   const int drow = lane >> 3, dslot = lane & 7;
-  // 32-bit byte offsets from a / from this group's weights (both < 2^32 for every supported shape)
-  uint32_t aoff0, aoff1, boff[4];
-  {
-    const int r0 = (2 * wave) * 8 + drow, r1 = r0 + 8;
-    aoff0 = (uint32_t)min(row0 + r0, row_end - 1) * (uint32_t)K + ((dslot ^ ((r0 >> 1) & 7)) << 4);   // rows past the
-    aoff1 = (uint32_t)min(row0 + r1, row_end - 1) * (uint32_t)K + ((dslot ^ ((r1 >> 1) & 7)) << 4);   // group end: any row
+  const bool has_a = T::A_INSTR >= 8 || wave < T::A_INSTR;
+  const int a_i0 = T::A_INSTR >= 8 ? wave * T::A_PW : wave;
+  // 32-bit byte offsets from a / from this group's weights (both < 2^32 for every supported shape);
+  // rows past the group end read the group's last row (any valid row would do)
+  uint32_t aoff[T::A_PW], boff[4];
+#pragma unroll
+  for (int j = 0; j < T::A_PW; ++j) {
+    const int r = (a_i0 + j) * 8 + drow;
+    aoff[j] = (uint32_t)min(row0 + r, row_end - 1) * (uint32_t)K + ((dslot ^ ((r >> 1) & 7)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -146,58 +182,63 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     else n = min(n0 + r, N - 1);
     boff[i] = (uint32_t)n * (uint32_t)K + ((dslot ^ ((r >> 1) & 7)) << 4);
   }
-  const float* ssrc = as + (size_t)min(row0 + (wave & 1) * 64 + lane, row_end - 1) * KB;   // waves 0, 1
-  const bool scale_loader = wave < 2;
-  const int per_stage = scale_loader ? 7 : 6;   // vector memory instructions per stage for this wave
+  // activation scales: the last S_INSTR waves each bring 64 rows' scales (4 bytes per lane)
+  const bool scale_loader = wave >= 8 - T::S_INSTR;
+  const int sidx = wave - (8 - T::S_INSTR);
+  const float* ssrc = as + (size_t)min(row0 + max(sidx, 0) * 64 + lane, row_end - 1) * KB;
+  // vector memory instructions per stage for this wave
+  const int per_stage = (has_a ? T::A_PW : 0) + 4 + (scale_loader ? 1 : 0);
 
   // ---- wave's B rows in the LDS tile and its B scale row-blocks
-  int b_lrow[4];
+  int b_lrow[NS];
 #pragma unroll
-  for (int ns = 0; ns < 4; ++ns) {
-    if (EPI == 1) b_lrow[ns] = ns < 2 ? wn * 32 + ns * 16 : 128 + wn * 32 + (ns - 2) * 16;
-    else b_lrow[ns] = wn * 64 + ns * 16;
+  for (int ns = 0; ns < NS; ++ns) {
+    if (EPI == 1) b_lrow[ns] = ns < HS ? wn * HS * 16 + ns * 16 : 128 + wn * HS * 16 + (ns - HS) * 16;
+    else b_lrow[ns] = wn * NS * 16 + ns * 16;
   }
-  const int nb_lo = EPI == 1 ? n0 / 128 : min(n0 + wn * 64, N - 1) / 128;
+  const int nb_lo = EPI == 1 ? n0 / 128 : min(n0 + wn * NS * 16, N - 1) / 128;
   const int nb_hi = EPI == 1 ? (F + n0) / 128 : nb_lo;
-  const bool wave_active = EPI == 1 ? true : (n0 + wn * 64 < N);
+  const bool wave_active = EPI == 1 ? true : (n0 + wn * NS * 16 < N);
 
   // wave-uniform LDS destinations of this wave's DMA instructions, stage 0; stage s adds s * stride
-  const uint32_t a_dst = lds_u32(&a_lds[0][(2 * wave) * 1024]);
+  const uint32_t a_dst = lds_u32(&a_lds[0][a_i0 * 1024]);
   const uint32_t b_dst = lds_u32(&b_lds[0][(4 * wave) * 1024]);
-  const uint32_t s_dst = lds_u32(&as_lds[0][(wave & 1) * 64]);
-#define GEMM_ISSUE(KBV, ST)                                                   \
-  do {                                                                        \
-    const uint32_t ko_ = (uint32_t)(KBV) * BK;                                \
-    const uint32_t ao_ = a_dst + (uint32_t)(ST) * A_BYTES;                    \
-    const uint32_t bo_ = b_dst + (uint32_t)(ST) * B_BYTES;                    \
-    dma16(a + (aoff0 + ko_), ao_);                                            \
-    dma16(a + (aoff1 + ko_), ao_ + 1024);                                     \
-    dma16(bg + (boff[0] + ko_), bo_);                                         \
-    dma16(bg + (boff[1] + ko_), bo_ + 1024);                                  \
-    dma16(bg + (boff[2] + ko_), bo_ + 2048);                                  \
-    dma16(bg + (boff[3] + ko_), bo_ + 3072);                                  \
-    if (scale_loader) dma4(ssrc + (KBV), s_dst + (uint32_t)((KBV) & 3) * BM * 4); \
+  const uint32_t s_dst = lds_u32(&as_lds[0][max(sidx, 0) * 64]);
+#define GEMM_ISSUE(KBV, ST)                                                           \
+  do {                                                                                \
+    const uint32_t ko_ = (uint32_t)(KBV) * BK;                                        \
+    if (has_a) {                                                                      \
+      const uint32_t ao_ = a_dst + (uint32_t)(ST) * A_BYTES;                          \
+      _Pragma("unroll") for (int j_ = 0; j_ < T::A_PW; ++j_)                           \
+        dma16(a + (aoff[j_] + ko_), ao_ + 1024 * j_);                                 \
+    }                                                                                 \
+    const uint32_t bo_ = b_dst + (uint32_t)(ST) * B_BYTES;                            \
+    dma16(bg + (boff[0] + ko_), bo_);                                                 \
+    dma16(bg + (boff[1] + ko_), bo_ + 1024);                                          \
+    dma16(bg + (boff[2] + ko_), bo_ + 2048);                                          \
+    dma16(bg + (boff[3] + ko_), bo_ + 3072);                                          \
+    if (scale_loader) dma4(ssrc + (KBV), s_dst + (uint32_t)((KBV) & 3) * AS_W * 4);   \
   } while (0)
 
-  floatx4 acc[4][4];
+  floatx4 acc[MS][NS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MS; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NS; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int lr = lane & 15;         // row within a 16-row operand tile
   const int kc = (lane >> 4) * 2;   // first of the two 16-byte K chunks this lane supplies
   // operand fragments of one K step, read from LDS stage ST
-  intx8 af[4], bf[4];
+  intx8 af[MS], bf[NS];
 #define GEMM_READ(ST)                                                                                   \
   do {                                                                                                  \
-    _Pragma("unroll") for (int ms = 0; ms < 4; ++ms) {                                                  \
-      const int r_ = wm * 64 + ms * 16 + lr;                                                            \
+    _Pragma("unroll") for (int ms = 0; ms < MS; ++ms) {                                                 \
+      const int r_ = wm * WROWS + ms * 16 + lr;                                                         \
       const intx4 lo_ = *reinterpret_cast<const intx4*>(&a_lds[ST][swz(r_, kc)]);                       \
       const intx4 hi_ = *reinterpret_cast<const intx4*>(&a_lds[ST][swz(r_, kc + 1)]);                   \
       af[ms] = intx8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};                   \
     }                                                                                                   \
-    _Pragma("unroll") for (int ns = 0; ns < 4; ++ns) {                                                  \
+    _Pragma("unroll") for (int ns = 0; ns < NS; ++ns) {                                                 \
       const int r_ = b_lrow[ns] + lr;                                                                   \
       const intx4 lo_ = *reinterpret_cast<const intx4*>(&b_lds[ST][swz(r_, kc)]);                       \
       const intx4 hi_ = *reinterpret_cast<const intx4*>(&b_lds[ST][swz(r_, kc + 1)]);                   \
@@ -205,54 +246,69 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     }                                                                                                   \
   } while (0)
 
-  GEMM_ISSUE(0, 0);
-  if (KB > 1) GEMM_ISSUE(1, 1);
-  float sbl0 = bsg[nb_lo * KB], sbh0 = bsg[nb_hi * KB];
-  float sbl1 = KB > 1 ? bsg[nb_lo * KB + 1] : 0.f, sbh1 = KB > 1 ? bsg[nb_hi * KB + 1] : 0.f;
+  // weight scales of the next NSTAGE-1 K steps, in scalar registers (slot 0 = current step)
+  constexpr int D = NSTAGE - 1;
+  float sbl[D], sbh[D];
+#pragma unroll
+  for (int s = 0; s < D; ++s) {
+    if (s < KB) {
+      GEMM_ISSUE(s, s);
+      sbl[s] = bsg[nb_lo * KB + s];
+      sbh[s] = bsg[nb_hi * KB + s];
+    } else {
+      sbl[s] = sbh[s] = 0.f;
+    }
+  }
+  int st = 0;   // LDS stage of step kb
   for (int kb = 0; kb < KB; ++kb) {
-    const int st = kb % NSTAGE;
-    wait_vm(kb + 1 < KB ? per_stage : 0);
+    // stages kb+1 .. kb+D-1 may stay in flight
+    wait_vm(per_stage * min(D - 1, KB - 1 - kb));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    float sbl2 = 0.f, sbh2 = 0.f;
-    if (kb + 2 < KB) {
-      GEMM_ISSUE(kb + 2, (kb + 2) % NSTAGE);
-      sbl2 = bsg[nb_lo * KB + kb + 2];
-      sbh2 = bsg[nb_hi * KB + kb + 2];
+    float sbl_n = 0.f, sbh_n = 0.f;
+    if (kb + D < KB) {
+      const int ist = st == 0 ? NSTAGE - 1 : st - 1;   // (kb + D) % NSTAGE: the stage read last step
+      GEMM_ISSUE(kb + D, ist);
+      sbl_n = bsg[nb_lo * KB + kb + D];
+      sbh_n = bsg[nb_hi * KB + kb + D];
     }
     if (wave_active) {
       GEMM_READ(st);
-      const float* srow = &as_lds[kb & 3][wm * 64 + (lane >> 4) * 4];
-      floatx4 p[4][4];
+      const float* srow = &as_lds[kb & 3][wm * WROWS + (lane >> 4) * 4];
+      floatx4 p[MS][NS];
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms)
+      for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns)
+        for (int ns = 0; ns < NS; ++ns)
           p[ms][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[ms], bf[ns], floatx4{0.f, 0.f, 0.f, 0.f},
                                                                        0, 0, 0, 0, 0, 0);
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms) {
+      for (int ms = 0; ms < MS; ++ms) {
         const floatx4 sa = *reinterpret_cast<const floatx4*>(srow + ms * 16);
         floatx4 c_lo, c_hi;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          c_lo[i] = sa[i] * sbl0;
-          c_hi[i] = sa[i] * sbh0;
+          c_lo[i] = sa[i] * sbl[0];
+          c_hi[i] = sa[i] * sbh[0];
         }
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) {
-          const bool hi = EPI == 1 && ns >= 2;
+        for (int ns = 0; ns < NS; ++ns) {
+          const bool hi = EPI == 1 && ns >= HS;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             acc[ms][ns][i] = __builtin_fmaf(p[ms][ns][i], hi ? c_hi[i] : c_lo[i], acc[ms][ns][i]);
         }
       }
     }
-    sbl0 = sbl1;
-    sbh0 = sbh1;
-    sbl1 = sbl2;
-    sbh1 = sbh2;
+#pragma unroll
+    for (int s = 0; s + 1 < D; ++s) {
+      sbl[s] = sbl[s + 1];
+      sbh[s] = sbh[s + 1];
+    }
+    sbl[D - 1] = sbl_n;
+    sbh[D - 1] = sbh_n;
+    st = st + 1 == NSTAGE ? 0 : st + 1;
   }
 #undef GEMM_READ
 #undef GEMM_ISSUE
@@ -261,14 +317,14 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   if (EPI == 0) {
     if (!wave_active) return;
 #pragma unroll
-    for (int ms = 0; ms < 4; ++ms)
+    for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = row0 + wm * 64 + ms * 16 + (lane >> 4) * 4 + i;
+        const int r = row0 + wm * WROWS + ms * 16 + (lane >> 4) * 4 + i;
         if (r >= row_end) continue;
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) {
-          const int col = n0 + wn * 64 + ns * 16 + lr;
+        for (int ns = 0; ns < NS; ++ns) {
+          const int col = n0 + wn * NS * 16 + ns * 16 + lr;
           if (OUT_BF16)
             reinterpret_cast<uint16_t*>(out)[(size_t)r * N + col] = f32_to_bf16(acc[ms][ns][i]);
           else
@@ -276,16 +332,16 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
         }
       }
   } else {
-    // h for this lane: rows (ms, i), columns wn*32 + hs*16 + lr (hs = 0, 1)
-    float h[4][2][4];
+    // h for this lane: rows (ms, i), columns wn*HS*16 + hs*16 + lr (hs < HS)
+    float h[MS][HS][4];
 #pragma unroll
-    for (int ms = 0; ms < 4; ++ms)
+    for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float mx = 0.0f;
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          const float gt = acc[ms][hs][i], up = acc[ms][hs + 2][i];
+        for (int hs = 0; hs < HS; ++hs) {
+          const float gt = acc[ms][hs][i], up = acc[ms][hs + HS][i];
           const float v = (gt * up) / (1.0f + __expf(-gt));
           h[ms][hs][i] = v;
           mx = fmaxf(mx, fabsf(v));
@@ -298,17 +354,19 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     uint8_t* hq = reinterpret_cast<uint8_t*>(out);
     const int FB = F / 128;
 #pragma unroll
-    for (int ms = 0; ms < 4; ++ms)
+    for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int lrow = ms * 16 + (lane >> 4) * 4 + i;
-        const float amax = fmaxf(fmaxf(red[wm][0][lrow], red[wm][1][lrow]), fmaxf(red[wm][2][lrow], red[wm][3][lrow]));
+        float amax = red[wm][0][lrow];
+#pragma unroll
+        for (int w = 1; w < WN; ++w) amax = fmaxf(amax, red[wm][w][lrow]);
         const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
-        const int r = row0 + wm * 64 + lrow;
+        const int r = row0 + wm * WROWS + lrow;
         if (r >= row_end) continue;
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          const int col = n0 + wn * 32 + hs * 16 + lr;
+        for (int hs = 0; hs < HS; ++hs) {
+          const int col = n0 + wn * HS * 16 + hs * 16 + lr;
           hq[(size_t)r * F + col] = (uint8_t)(e4m3_pack2(h[ms][hs][i] / sc, 0.0f) & 0xFF);
         }
         if (wn == 0 && lr == 0) out_scales[(size_t)r * FB + n0 / 128] = sc;
@@ -316,19 +374,40 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   }
 }
 
-int max_tiles_for(int64_t max_rows, int groups) { return (int)(ceil_div64(max_rows, BM) + groups); }
+int64_t max_tiles_for(int64_t max_rows, int groups, int bm) { return ceil_div64(max_rows, bm) + groups; }
+
+// Row-tile height when the caller leaves it open: short groups (average of at most 64 rows)
+// stream weights through the 32-row tile, longer ones use the 128-row tile.
+int auto_tile_rows(int64_t max_rows, int groups) { return max_rows <= (int64_t)groups * 64 ? 32 : 128; }
+
+template <int BM>
+void launch(unsigned grid, hipStream_t st, int epilogue, int out_dtype, const uint8_t* a, const float* as,
+            const int32_t* offsets, const int4* tiles, const int32_t* ntiles, int ny, const uint8_t* b, const float* bs,
+            int N, int K, void* out, float* out_scales) {
+  if (epilogue == MOE_EPI_STORE) {
+    if (out_dtype == MOE_BF16)
+      grouped_gemm_kernel<BM, 0, true><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+                                                                  nullptr);
+    else
+      grouped_gemm_kernel<BM, 0, false><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b, bs, N, K,
+                                                                   out, nullptr);
+  } else {
+    grouped_gemm_kernel<BM, 1, false><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+                                                                 out_scales);
+  }
+}
 
 }  // namespace
 
 size_t moe_gemm_workspace(int64_t max_rows, int32_t groups) {
-  return (size_t)max_tiles_for(max_rows, groups) * sizeof(int4) + 256;
+  return (size_t)max_tiles_for(max_rows, groups, MIN_BM) * sizeof(int4) + 256;
 }
 
 extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int32_t* offsets, int32_t groups,
                                     int64_t max_rows, const uint8_t* b, const float* bs, int32_t N, int32_t K,
-                                    int32_t epilogue, void* out, int out_dtype, float* out_scales, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
-  if (groups < 1 || groups > 4096 || max_rows < 0 || max_rows > INT32_MAX - 2 * BM) return MOE_ERR_SHAPE;
+                                    int32_t epilogue, int32_t tile_rows, void* out, int out_dtype, float* out_scales,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (groups < 1 || groups > 4096 || max_rows < 0 || max_rows > INT32_MAX - 256) return MOE_ERR_SHAPE;
   if (N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return MOE_ERR_SHAPE;
   if (epilogue == MOE_EPI_STORE) {
     if (out_dtype != MOE_BF16 && out_dtype != MOE_F32) return MOE_ERR_DTYPE;
@@ -338,31 +417,28 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int
   } else {
     return MOE_ERR_ARG;
   }
+  // byte offsets inside a and inside one group's weights are 32-bit in the kernel
+  if ((max_rows + 1) * (int64_t)K > (int64_t)UINT32_MAX || (int64_t)N * K > (int64_t)UINT32_MAX) return MOE_ERR_SHAPE;
+  if (tile_rows != 0 && tile_rows != 32 && tile_rows != 128) return MOE_ERR_ARG;
   if (max_rows == 0) return MOE_OK;
   if (!a || !as || !offsets || !b || !bs || !out) return MOE_ERR_NULL;
   if (epilogue == MOE_EPI_SWIGLU_QUANT && !out_scales) return MOE_ERR_NULL;
   if (!workspace || workspace_bytes < moe_gemm_workspace(max_rows, groups)) return MOE_ERR_WORKSPACE;
+  const int bm = tile_rows != 0 ? tile_rows : auto_tile_rows(max_rows, groups);
   hipStream_t st = as_stream(stream);
-  const int mt = max_tiles_for(max_rows, groups);
+  const int64_t mt = max_tiles_for(max_rows, groups, bm);
+  const int ny = (int)(epilogue == MOE_EPI_STORE ? ceil_div64(N, BN) : N / 256);
+  const int64_t nwg = mt * ny;
+  if (nwg > INT32_MAX) return MOE_ERR_SHAPE;
   int4* tiles = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(workspace) + 256);
   int32_t* ntiles = reinterpret_cast<int32_t*>(workspace);
-  tile_map_kernel<<<1, 1024, 0, st>>>(offsets, groups, tiles, ntiles, mt);
+  tile_map_kernel<<<1, 1024, 0, st>>>(offsets, groups, bm, tiles, ntiles, (int)mt);
   MOE_CHECK_LAUNCH();
-  const int ny = (int)(epilogue == MOE_EPI_STORE ? ceil_div64(N, BN) : N / 256);
-  const int64_t nwg = (int64_t)mt * ny;
-  if (nwg > INT32_MAX) return MOE_ERR_SHAPE;
   const unsigned grid = (unsigned)nwg;
-  if (epilogue == MOE_EPI_STORE) {
-    if (out_dtype == MOE_BF16)
-      grouped_gemm_kernel<0, true><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                                                              nullptr);
-    else
-      grouped_gemm_kernel<0, false><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                                                               nullptr);
-  } else {
-    grouped_gemm_kernel<1, false><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                                                             out_scales);
-  }
+  if (bm == 32)
+    launch<32>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
+  else
+    launch<128>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

@@ -162,13 +162,16 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32
  *   epilogue MOE_EPI_SWIGLU_QUANT: N = 2F; h[r,f] = silu(acc[r,f]) * acc[r,F+f] in fp32, quantised
  *            1x128 as in moe_quant_fp8_block: out [max_rows, F] e4m3 (out_dtype MOE_FP8_E4M3),
  *            out_scales [max_rows, F/128] fp32
+ *   tile_rows: rows per workgroup tile, 32 or 128, or 0 to choose from the average group size
+ *            (32 when max_rows <= 64 * groups).  The result is the same for either height.
  *   Rows beyond offsets[groups] are not written.  workspace >= moe_workspace_bytes(MOE_OP_GROUPED_GEMM,
  *   max_rows, 0, groups, N, K).
- * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (N, K % 128; F % 128 for SwiGLU), MOE_ERR_DTYPE, MOE_ERR_ARG,
- *         MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (N, K % 128; F % 128 for SwiGLU; (max_rows+1)*K or N*K at or
+ *         above 2^32), MOE_ERR_DTYPE, MOE_ERR_ARG (epilogue, tile_rows), MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
 int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int32_t* offsets, int32_t groups, int64_t max_rows,
-                         const uint8_t* b, const float* bs, int32_t N, int32_t K, int32_t epilogue, void* out,
-                         int out_dtype, float* out_scales, void* workspace, size_t workspace_bytes, void* stream);
+                         const uint8_t* b, const float* bs, int32_t N, int32_t K, int32_t epilogue, int32_t tile_rows,
+                         void* out, int out_dtype, float* out_scales, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* Combine (blog sections "Wide EP" / "Parallelism / EP": expert outputs return to token order).
  *   out[t,:] = sum_{j<k, dest_row[t,j] >= 0} topk_w[t,j] * y[dest_row[t,j],:]  (+ y[*shared_first_row + t,:])

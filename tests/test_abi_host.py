@@ -113,8 +113,8 @@ def test_dispatch_validation(L):
 
 def test_gemm_validation(L):
     P = ctypes.c_void_p(256)
-    g = lambda N=256, K=256, epi=0, od=1, ws=P, wsb=1 << 20, osc=None, groups=4: (
-        P, P, P, groups, 100, P, P, N, K, epi, P, od, osc, ws, wsb, None)
+    g = lambda N=256, K=256, epi=0, od=1, ws=P, wsb=1 << 20, osc=None, groups=4, tr=0, rows=100: (
+        P, P, P, groups, rows, P, P, N, K, epi, tr, P, od, osc, ws, wsb, None)
     assert L.moe_grouped_gemm_fp8(*g(N=200)) == SHAPE
     assert L.moe_grouped_gemm_fp8(*g(K=100)) == SHAPE
     assert L.moe_grouped_gemm_fp8(*g(od=2)) == DTYPE
@@ -124,6 +124,9 @@ def test_gemm_validation(L):
     assert L.moe_grouped_gemm_fp8(*g(epi=7)) == ARG
     assert L.moe_grouped_gemm_fp8(*g(groups=0)) == SHAPE
     assert L.moe_grouped_gemm_fp8(*g(wsb=8)) == WS
+    assert L.moe_grouped_gemm_fp8(*g(tr=64)) == ARG                   # tile height neither 32 nor 128
+    assert L.moe_grouped_gemm_fp8(*g(rows=1 << 20, K=4096)) == SHAPE   # 2^32 bytes of activations
+    assert L.moe_grouped_gemm_fp8(*g(N=1 << 17, K=1 << 15)) == SHAPE   # 2^32 bytes of one group's weights
 
 
 def test_combine_validation(L):

@@ -5,6 +5,8 @@ Each stage gets the same seeded synthetic inputs on both sides.  Integer, byte a
 offsets, permutation) must match bit for bit; GEMM and combine outputs within a max-abs-normalised
 error of 2e-2.  Large outputs are compared on sampled rows that the oracle computes one by one.
 """
+import itertools
+
 import numpy as np
 import pytest
 import torch
@@ -16,6 +18,7 @@ from gpu_helpers import DEV, TOL, assert_equal, cfgs_for, host, rel_err, rows_ho
 
 pytestmark = pytest.mark.gpu
 NAMES = ["tiny", "decode", "prefill", "longctx", "r3"]
+TILES = [32, 128]   # both row-tile heights of the grouped GEMM, whichever the shape would pick
 
 
 def _cleanup():
@@ -243,7 +246,7 @@ def _sample_rows(offsets, n, seed):
     rng = np.random.default_rng(seed)
     for g in rng.choice(nonempty, size=min(6, len(nonempty)), replace=False):
         lo, hi = int(offsets[g]), int(offsets[g + 1])
-        pick |= {lo, hi - 1, min(lo + 127, hi - 1), min(lo + 128, hi - 1)}   # group edges and a tile edge
+        pick |= {lo, hi - 1} | {min(lo + d, hi - 1) for d in (31, 32, 127, 128)}   # group and tile edges
     pick |= set(synth.sample_tokens(rows, n, seed).tolist())
     return np.array(sorted(pick))
 
@@ -266,17 +269,18 @@ def _oracle_rows(a, as_, offsets, b, bs, rows):
 
 @pytest.mark.parametrize("name", NAMES)
 @pytest.mark.parametrize("which", ["w1", "w2"])
-def test_grouped_gemm_store(name, which):
+@pytest.mark.parametrize("tile", TILES)
+def test_grouped_gemm_store(name, which, tile):
     cfg = synth.CONFIGS[name]
     offsets, a, as_, b, bs, N, K = _gemm_case(cfg, which, 0 if which == "w1" else 5)
     goff = torch.from_numpy(offsets).to(DEV)
-    y32 = M.moe_grouped_gemm_fp8(a, as_, goff, b, bs, M.MOE_EPI_STORE, torch.float32)
-    ybf = M.moe_grouped_gemm_fp8(a, as_, goff, b, bs, M.MOE_EPI_STORE, torch.bfloat16)
+    y32 = M.moe_grouped_gemm_fp8(a, as_, goff, b, bs, M.MOE_EPI_STORE, torch.float32, tile_rows=tile)
+    ybf = M.moe_grouped_gemm_fp8(a, as_, goff, b, bs, M.MOE_EPI_STORE, torch.bfloat16, tile_rows=tile)
     rows = _sample_rows(offsets, 24, cfg.seed)
     ref, _ = _oracle_rows(a, as_, offsets, b, bs, rows)
     e32 = rel_err(rows_host(y32, rows), ref)
     ebf = rel_err(rows_host(ybf, rows), ref)
-    print(f"{name} {which}: fp32-out err {e32:.3e}, bf16-out err {ebf:.3e}")
+    print(f"{name} {which} tile {tile}: fp32-out err {e32:.3e}, bf16-out err {ebf:.3e}")
     # uniformly random codes are heavy-tailed (log-uniform magnitudes), so fp32 accumulation error
     # relative to max |ref| reaches ~1e-4; the contract bound for GEMM outputs is TOL
     assert e32 < 1e-3 and ebf < TOL
@@ -292,24 +296,25 @@ def test_grouped_gemm_exact_integers():
     rows = int(offsets[-1])
     a, ai = synth.integer_codes((rows, K), 60, 0, device=DEV)
     b, bi = synth.integer_codes((G, N, K), 60, 1, device=DEV)
-    for sa, sb in ((1.0, 1.0), (0.25, 8.0)):
+    for (sa, sb), tile in itertools.product(((1.0, 1.0), (0.25, 8.0)), TILES):
         as_ = torch.full((rows, K // 128), sa, dtype=torch.float32, device=DEV)
         bs = torch.full((G, N // 128, K // 128), sb, dtype=torch.float32, device=DEV)
         y = M.moe_grouped_gemm_fp8(a, as_, torch.from_numpy(offsets.astype(np.int32)).to(DEV), b, bs,
-                                   M.MOE_EPI_STORE, torch.float32)
+                                   M.MOE_EPI_STORE, torch.float32, tile_rows=tile)
         ref = O.moe_grouped_gemm_fp8(host(a), host(as_), offsets, host(b), host(bs))
-        assert_equal(f"exact integer GEMM (scales {sa},{sb})", host(y), ref.astype(np.float32))
+        assert_equal(f"exact integer GEMM (scales {sa},{sb}, tile {tile})", host(y), ref.astype(np.float32))
         assert np.array_equal(ref, sa * sb * np.concatenate(
             [ai[offsets[g]:offsets[g + 1]].numpy() @ bi[g].numpy().T for g in range(G)]))
 
 
 @pytest.mark.parametrize("name", NAMES)
-def test_grouped_gemm_swiglu_quant(name):
+@pytest.mark.parametrize("tile", TILES)
+def test_grouped_gemm_swiglu_quant(name, tile):
     cfg = synth.CONFIGS[name]
     offsets, a, as_, b, bs, N, K = _gemm_case(cfg, "w1", 9)
     F = N // 2
     goff = torch.from_numpy(offsets).to(DEV)
-    hq, hs = M.moe_grouped_gemm_fp8(a, as_, goff, b, bs, M.MOE_EPI_SWIGLU_QUANT)
+    hq, hs = M.moe_grouped_gemm_fp8(a, as_, goff, b, bs, M.MOE_EPI_SWIGLU_QUANT, tile_rows=tile)
     rows = _sample_rows(offsets, 16, cfg.seed + 1)
     g1, _ = _oracle_rows(a, as_, offsets, b, bs, rows)
     h = O.swiglu(g1, F)
