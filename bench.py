@@ -5,7 +5,10 @@
 A step is one full layer forward (gate logits, routing, activation quantisation, dispatch,
 grouped GEMM1 + SwiGLU + h quantisation, grouped GEMM2, combine) over one batch of synthetic
 tokens whose inputs and quantised weights are already resident in HBM.  The default workload is
-the decode-shaped layer (256 tokens, hidden 4096, 64 experts, FFN 1408, top-6).  Prints one JSON
+the decode-shaped layer (256 tokens, hidden 4096, 64 experts, FFN 1408, top-6).  Consecutive steps
+cycle through several copies of the layer (weights packed for the grouped GEMM, plus buffers), at
+least 2 GiB of weights in all, as consecutive layers of a model would: a step never finds its
+weights in the 256 MB Infinity Cache left behind by the step before.  Prints one JSON
 line: layer tokens/s, per-stage times from HIP events recorded on the launch stream, the grouped
 GEMM's TFLOP/s, the roofline of the dominant kernel, and the CPU oracle timed on a bounded sample.
 """
@@ -36,6 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="layer copies cycled through by consecutive steps (0: enough for 2 GiB of weights, >= 2)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -77,7 +82,9 @@ def main():
 
     import block_scaled_fp8_top_amd as M
     import synth
-    from block_scaled_fp8_top_amd.layer import MoELayer, MoELayerWeights, quantize_expert_weights
+    from dataclasses import replace
+
+    from block_scaled_fp8_top_amd.layer import MoELayer, MoELayerWeights, pack_expert_weights, quantize_expert_weights
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -90,14 +97,24 @@ def main():
     wg, b = synth.make_gate(cfg, 0, dev)
     w1q, w1s, w2q, w2s = quantize_expert_weights(cfg.groups, cfg.H, cfg.F,
                                                  lambda g: synth.make_expert(cfg, g, 0, dev), device=dev)
-    weights = MoELayerWeights(wg=wg, bias=b, w1q=w1q, w1s=w1s, w2q=w2q, w2s=w2s, cfg=rcfg, shared=cfg.shared)
+    weights = pack_expert_weights(MoELayerWeights(wg=wg, bias=b, w1q=w1q, w1s=w1s, w2q=w2q, w2s=w2s, cfg=rcfg,
+                                                  shared=cfg.shared), keep_rowmajor=False)
+    del w1q, w2q
+    wbytes = weights.w1p.data.numel() + weights.w2p.data.numel()
+    copies = a.copies if a.copies > 0 else max(2, math.ceil((2 << 30) / wbytes))
     act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
-    layer = MoELayer(weights, cfg.T, act, dev)
+    layers = [MoELayer(weights, cfg.T, act, dev)]
+    for _ in range(1, copies):
+        wc = replace(weights, w1p=replace(weights.w1p, data=weights.w1p.data.clone()),
+                     w2p=replace(weights.w2p, data=weights.w2p.data.clone()), w1s=weights.w1s.clone(),
+                     w2s=weights.w2s.clone())
+        layers.append(MoELayer(wc, cfg.T, act, dev))
+    layer = layers[0]
     x = synth.make_x(cfg, dev)
     torch.cuda.synchronize()
 
-    for _ in range(a.warmup):
-        layer.forward(x)
+    for s in range(a.warmup):
+        layers[s % copies].forward(x)
     torch.cuda.synchronize()
 
     # ---- timed region: K steps, HIP events between stages on the launch stream
@@ -106,7 +123,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
-        layer.forward(x, events=ev[s])
+        layers[s % copies].forward(x, events=ev[s])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
@@ -183,7 +200,8 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) weights, random-init)",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
                    "shared_experts": int(cfg.shared), "ffn": cfg.F, "top_k": cfg.k, "score": cfg.score_fn,
-                   "rows": model["_rows"], "active_experts": n_active, "parallelism": "none (1 GPU)"},
+                   "rows": model["_rows"], "active_experts": n_active, "layer_copies": copies,
+                   "weight_layout": "packed", "parallelism": "none (1 GPU)"},
         "gemm_tflops": round(gemm_tflops, 2),
         "gemm_frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
         "stages": stages,

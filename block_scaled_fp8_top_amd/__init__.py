@@ -25,10 +25,11 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_EPI_STORE, MOE_EPI_SWIGLU_QUANT = 0, 1
 MOE_OP_DISPATCH, MOE_OP_GROUPED_GEMM = 1, 2
+MOE_B_ROWMAJOR, MOE_B_PACKED = 0, 1
 
 EXPORTED = ("moe_gate_logits", "moe_route", "moe_replay_route", "moe_router_score_eval", "moe_quant_fp8_block",
-            "moe_dispatch", "moe_grouped_gemm_fp8", "moe_combine", "moe_workspace_bytes", "moe_status_str",
-            "moe_version")
+            "moe_dispatch", "moe_pack_weights_fp8", "moe_packed_weight_bytes", "moe_grouped_gemm_fp8", "moe_combine",
+            "moe_workspace_bytes", "moe_status_str", "moe_version")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -67,7 +68,9 @@ def lib():
         "moe_router_score_eval": [P, I64, ctypes.c_int, P, P],
         "moe_quant_fp8_block": [P, ctypes.c_int, I64, I64, I32, I32, P, P, P],
         "moe_dispatch": [P, I64, I32, I32, I32, P, P, I32, P, P, P, P, P, P, P, SZ, P],
-        "moe_grouped_gemm_fp8": [P, P, P, I32, I64, P, P, I32, I32, I32, I32, P, ctypes.c_int, P, P, SZ, P],
+        "moe_pack_weights_fp8": [P, I32, I32, I32, I32, P, P],
+        "moe_packed_weight_bytes": [I32, I32, I32, I32],
+        "moe_grouped_gemm_fp8": [P, P, P, I32, I64, P, I32, P, I32, I32, I32, I32, P, ctypes.c_int, P, P, SZ, P],
         "moe_combine": [P, ctypes.c_int, P, P, I64, I32, I32, P, P, ctypes.c_int, P],
         "moe_workspace_bytes": [ctypes.c_int, I64, I32, I32, I32, I32],
         "moe_status_str": [ctypes.c_int],
@@ -78,6 +81,7 @@ def lib():
         fn.argtypes = args
         fn.restype = ctypes.c_int
     L.moe_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_packed_weight_bytes.restype = ctypes.c_size_t
     L.moe_status_str.restype = ctypes.c_char_p
     L.moe_version.restype = ctypes.c_char_p
     _lib = L
@@ -268,20 +272,57 @@ def moe_dispatch(topk_idx: torch.Tensor, num_experts: int, append_shared: bool, 
     return out
 
 
-def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tensor, b: torch.Tensor, bs: torch.Tensor,
+def packed_weight_bytes(groups: int, N: int, K: int, epilogue: int) -> int:
+    return int(lib().moe_packed_weight_bytes(groups, N, K, epilogue))
+
+
+@dataclass
+class PackedWeight:
+    """A [G,N,K] e4m3 weight rearranged by moe_pack_weights_fp8 for one GEMM epilogue."""
+    data: torch.Tensor   # [G, packed bytes per group] uint8
+    G: int
+    N: int
+    K: int
+    epilogue: int
+
+
+def moe_pack_weights_fp8(b: torch.Tensor, epilogue: int, out: Optional[torch.Tensor] = None, stream=None) -> PackedWeight:
+    """b [G,N,K] e4m3 bytes (device) -> the packed layout the grouped GEMM streams for ``epilogue``."""
+    _dev(b, "b", FP8)
+    G, N, K = b.shape
+    nbytes = packed_weight_bytes(G, N, K, epilogue)
+    if nbytes == 0:
+        raise MoeError(MOE_ERR_SHAPE, f"moe_pack_weights_fp8: unsupported shape {tuple(b.shape)} / epilogue {epilogue}")
+    if out is None:
+        out = torch.empty((G, nbytes // G), dtype=torch.uint8, device=b.device)
+    else:
+        _dev(out, "out", torch.uint8, (G, nbytes // G))
+    _check(lib().moe_pack_weights_fp8(_p(b), G, N, K, epilogue, _p(out), _stream(stream)), "moe_pack_weights_fp8")
+    return PackedWeight(out, G, N, K, epilogue)
+
+
+def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tensor, b, bs: torch.Tensor,
                          epilogue: int = MOE_EPI_STORE, out_dtype=torch.bfloat16, out=None, out_scales=None,
                          workspace: Optional[torch.Tensor] = None, stream=None, tile_rows: int = 0):
-    """a [max_rows,K] uint8, as_ [max_rows,K/128], offsets [G+1] (device), b [G,N,K] uint8, bs [G,N/128,K/128].
+    """a [max_rows,K] uint8, as_ [max_rows,K/128], offsets [G+1] (device), b [G,N,K] uint8 or a
+    PackedWeight packed for this epilogue, bs [G,N/128,K/128].
     STORE -> out [max_rows,N] (bf16/fp32); SWIGLU_QUANT -> (h codes [max_rows,N/2] uint8, scales [max_rows,N/256]).
     tile_rows: 32 or 128 rows per workgroup tile, 0 = chosen from the average group size."""
     max_rows, K = a.shape
-    G, N, Kb = b.shape
+    if isinstance(b, PackedWeight):
+        if b.epilogue != epilogue:
+            raise ValueError("weight was packed for another epilogue")
+        G, N, Kb, b_layout, b_t = b.G, b.N, b.K, MOE_B_PACKED, b.data
+        _dev(b_t, "b", torch.uint8, (G, packed_weight_bytes(G, N, Kb, epilogue) // G))
+    else:
+        G, N, Kb = b.shape
+        b_layout, b_t = MOE_B_ROWMAJOR, b
+        _dev(b, "b", FP8)
     if Kb != K:
         raise ValueError("K mismatch")
     _dev(a, "a", FP8)
     _dev(as_, "as", torch.float32, (max_rows, K // 128))
     _dev(offsets, "offsets", torch.int32, (G + 1,))
-    _dev(b, "b", FP8)
     _dev(bs, "bs", torch.float32, (G, N // 128, K // 128))
     dev = a.device
     ws_need = workspace_bytes(MOE_OP_GROUPED_GEMM, max_rows, 0, G, N, K)
@@ -299,8 +340,8 @@ def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tens
         out = torch.empty((max_rows, F), dtype=FP8, device=dev) if out is None else _dev(out, "out", FP8, (max_rows, F))
         osc = torch.empty((max_rows, F // 128), dtype=torch.float32, device=dev) if out_scales is None else \
             _dev(out_scales, "out_scales", torch.float32, (max_rows, F // 128))
-    _check(lib().moe_grouped_gemm_fp8(_p(a), _p(as_), _p(offsets), G, max_rows, _p(b), _p(bs), N, K, epilogue,
-                                      tile_rows, _p(out),
+    _check(lib().moe_grouped_gemm_fp8(_p(a), _p(as_), _p(offsets), G, max_rows, _p(b_t), b_layout, _p(bs), N, K,
+                                      epilogue, tile_rows, _p(out),
                                       code, _p(osc), _p(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream)), "moe_grouped_gemm_fp8")
     return out if epilogue == MOE_EPI_STORE else (out, osc)
@@ -324,4 +365,4 @@ def moe_combine(y: torch.Tensor, dest_row: torch.Tensor, topk_w: torch.Tensor, s
     return out
 
 
-from .layer import MoELayerWeights, MoELayer, quantize_expert_weights  # noqa: E402,F401
+from .layer import MoELayerWeights, MoELayer, pack_expert_weights, quantize_expert_weights  # noqa: E402,F401

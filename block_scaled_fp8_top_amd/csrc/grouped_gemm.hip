@@ -22,7 +22,11 @@
 // Rows are stored with a 16-byte-chunk XOR swizzle (chunk c of row r at slot c ^ ((r >> 1) & 7):
 // the 16 rows one MFMA operand read touches then hit 16 distinct bank groups), applied on the
 // global side: lane L of a DMA instruction writes LDS slot L, so it fetches the chunk that belongs
-// there.  Weight scales travel through scalar loads in a ring as deep as the DMA lookahead.
+// there.  Weights may come pre-packed (moe_pack_weights_fp8): each K step of a 256-row panel is
+// then one contiguous 32 KB block holding exactly that LDS image, and every DMA instruction reads
+// 1 KB of consecutive bytes instead of eight 128-byte row pieces K bytes apart, which keeps HBM
+// streaming near its peak.  Weight scales travel through scalar loads in a ring as deep as the DMA
+// lookahead.
 //
 // Tile order: a one-workgroup kernel turns `offsets` into the list of BM-row tiles (never
 // straddling a group).  The grid is one-dimensional; hardware workgroup ids are dealt to the 8
@@ -78,6 +82,35 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
+// Weight row held by virtual row r (0..255) of panel nt: SwiGLU panels pair gate rows
+// [128 nt, 128 nt + 128) with up rows [F + 128 nt, ...); STORE panels are rows [256 nt, 256 nt + 256).
+__device__ __forceinline__ int panel_row(int epi, int nt, int r, int F) {
+  return epi == 1 ? (r < 128 ? nt * 128 + r : F + nt * 128 + (r - 128)) : nt * BN + r;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Packed weights: packed[g][nt][kb] is the 32 KB LDS image of K step kb of panel nt: 16-byte unit
+// u = 64 i + L (DMA instruction i, lane L) holds chunk (L % 8) ^ ((r >> 1) & 7) of virtual row
+// r = 8 i + L / 8.  One thread per 16-byte unit; rows past N (STORE panels) are zero.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __restrict__ b, int N, int K, int ny, int epi,
+                                                           int64_t units, uint8_t* __restrict__ packed) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int KB = K / BK;
+  const int w = (int)(u & 2047);                // unit within the 32 KB block
+  const int64_t blk = u >> 11;                  // (g, nt, kb) block index
+  const int kb = (int)(blk % KB);
+  const int64_t gnt = blk / KB;
+  const int nt = (int)(gnt % ny);
+  const int64_t g = gnt / ny;
+  const int r = (w >> 6) * 8 + ((w & 63) >> 3);
+  const int chunk = (w & 7) ^ ((r >> 1) & 7);
+  const int n = panel_row(epi, nt, r, N / 2);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (n < N) v = *reinterpret_cast<const uint4*>(b + ((size_t)g * N + n) * K + (size_t)kb * BK + chunk * 16);
+  *reinterpret_cast<uint4*>(packed + (size_t)u * 16) = v;
+}
+
 // ------------------------------------------------------------------------------------------------
 // tiles[i] = {group, first row, index of the group's first tile, number of tiles of the group}
 __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restrict__ offsets, int groups, int bm,
@@ -123,7 +156,7 @@ __device__ __forceinline__ void wait_vm(int n) {
 }
 
 // ------------------------------------------------------------------------------------------------
-template <int BM, int EPI, bool OUT_BF16>
+template <int BM, int EPI, bool OUT_BF16, bool PACKED>
 __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const int32_t* __restrict__ offsets,
     const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles, int ny, const uint8_t* __restrict__ b,
@@ -157,12 +190,14 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  const uint8_t* bg = b + (size_t)g * N * K;
+  // this group's weights: row-major [N, K], or ny packed panels of 256 x K bytes
+  const uint8_t* bg = b + (size_t)g * (PACKED ? (size_t)ny * BN : (size_t)N) * K;
   const float* bsg = bs + (size_t)g * (N / 128) * KB;
 
   // ---- this lane's DMA sources.  A slice: instruction i covers rows 8i .. 8i+7; wave w issues
   // instructions w*A_PW + j (or just w, for slices of fewer than 8 instructions).  B slice:
-  // instructions 4w .. 4w+3.  Lane: row 8i + lane/8, 16-byte chunk lane%8 (swizzled).
+  // instructions 4w .. 4w+3.  Lane: row 8i + lane/8, 16-byte chunk lane%8 (swizzled); for packed
+  // weights the lane's 16 bytes sit at 1024 i + 16 lane of the K step's block.
   const int drow = lane >> 3, dslot = lane & 7;
   const bool has_a = T::A_INSTR >= 8 || wave < T::A_INSTR;
   const int a_i0 = T::A_INSTR >= 8 ? wave * T::A_PW : wave;
@@ -176,11 +211,13 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = (4 * wave + i) * 8 + drow;
-    int n;
-    if (EPI == 1) n = r < 128 ? n0 + r : F + n0 + (r - 128);
-    else n = min(n0 + r, N - 1);
-    boff[i] = (uint32_t)n * (uint32_t)K + ((dslot ^ ((r >> 1) & 7)) << 4);
+    if (PACKED) {
+      boff[i] = (uint32_t)nt_idx * (uint32_t)(BN * K) + (uint32_t)((4 * wave + i) * 1024 + lane * 16);
+    } else {
+      const int r = (4 * wave + i) * 8 + drow;
+      const int n = min(panel_row(EPI, nt_idx, r, F), N - 1);
+      boff[i] = (uint32_t)n * (uint32_t)K + ((dslot ^ ((r >> 1) & 7)) << 4);
+    }
   }
   // activation scales: the last S_INSTR waves each bring 64 rows' scales (4 bytes per lane)
   const bool scale_loader = wave >= 8 - T::S_INSTR;
@@ -207,16 +244,17 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
 #define GEMM_ISSUE(KBV, ST)                                                           \
   do {                                                                                \
     const uint32_t ko_ = (uint32_t)(KBV) * BK;                                        \
+    const uint32_t kob_ = PACKED ? (uint32_t)(KBV) * B_BYTES : ko_;                   \
     if (has_a) {                                                                      \
       const uint32_t ao_ = a_dst + (uint32_t)(ST) * A_BYTES;                          \
       _Pragma("unroll") for (int j_ = 0; j_ < T::A_PW; ++j_)                           \
         dma16(a + (aoff[j_] + ko_), ao_ + 1024 * j_);                                 \
     }                                                                                 \
     const uint32_t bo_ = b_dst + (uint32_t)(ST) * B_BYTES;                            \
-    dma16(bg + (boff[0] + ko_), bo_);                                                 \
-    dma16(bg + (boff[1] + ko_), bo_ + 1024);                                          \
-    dma16(bg + (boff[2] + ko_), bo_ + 2048);                                          \
-    dma16(bg + (boff[3] + ko_), bo_ + 3072);                                          \
+    dma16(bg + (boff[0] + kob_), bo_);                                                 \
+    dma16(bg + (boff[1] + kob_), bo_ + 1024);                                          \
+    dma16(bg + (boff[2] + kob_), bo_ + 2048);                                          \
+    dma16(bg + (boff[3] + kob_), bo_ + 3072);                                          \
     if (scale_loader) dma4(ssrc + (KBV), s_dst + (uint32_t)((KBV) & 3) * AS_W * 4);   \
   } while (0)
 
@@ -380,22 +418,25 @@ int64_t max_tiles_for(int64_t max_rows, int groups, int bm) { return ceil_div64(
 // stream weights through the 32-row tile, longer ones use the 128-row tile.
 int auto_tile_rows(int64_t max_rows, int groups) { return max_rows <= (int64_t)groups * 64 ? 32 : 128; }
 
-template <int BM>
+template <int BM, bool PACKED>
 void launch(unsigned grid, hipStream_t st, int epilogue, int out_dtype, const uint8_t* a, const float* as,
             const int32_t* offsets, const int4* tiles, const int32_t* ntiles, int ny, const uint8_t* b, const float* bs,
             int N, int K, void* out, float* out_scales) {
   if (epilogue == MOE_EPI_STORE) {
     if (out_dtype == MOE_BF16)
-      grouped_gemm_kernel<BM, 0, true><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                                                                  nullptr);
+      grouped_gemm_kernel<BM, 0, true, PACKED><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b, bs, N,
+                                                                          K, out, nullptr);
     else
-      grouped_gemm_kernel<BM, 0, false><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b, bs, N, K,
-                                                                   out, nullptr);
+      grouped_gemm_kernel<BM, 0, false, PACKED><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b, bs, N,
+                                                                           K, out, nullptr);
   } else {
-    grouped_gemm_kernel<BM, 1, false><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                                                                 out_scales);
+    grouped_gemm_kernel<BM, 1, false, PACKED><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b, bs, N,
+                                                                         K, out, out_scales);
   }
 }
+
+// panels per group: ceil(N / 256) for STORE, N / 256 for SwiGLU (N % 256 == 0 there)
+int64_t panels(int32_t N, int32_t epilogue) { return epilogue == MOE_EPI_STORE ? ceil_div64(N, BN) : N / BN; }
 
 }  // namespace
 
@@ -403,10 +444,33 @@ size_t moe_gemm_workspace(int64_t max_rows, int32_t groups) {
   return (size_t)max_tiles_for(max_rows, groups, MIN_BM) * sizeof(int4) + 256;
 }
 
+extern "C" size_t moe_packed_weight_bytes(int32_t groups, int32_t N, int32_t K, int32_t epilogue) {
+  if (groups < 1 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return 0;
+  if (epilogue != MOE_EPI_STORE && epilogue != MOE_EPI_SWIGLU_QUANT) return 0;
+  if (epilogue == MOE_EPI_SWIGLU_QUANT && N % 256 != 0) return 0;
+  return (size_t)groups * (size_t)panels(N, epilogue) * BN * (size_t)K;
+}
+
+extern "C" int moe_pack_weights_fp8(const uint8_t* b, int32_t groups, int32_t N, int32_t K, int32_t epilogue,
+                                    uint8_t* packed, void* stream) {
+  if (epilogue != MOE_EPI_STORE && epilogue != MOE_EPI_SWIGLU_QUANT) return MOE_ERR_ARG;
+  if (groups < 1 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return MOE_ERR_SHAPE;
+  if (epilogue == MOE_EPI_SWIGLU_QUANT && N % 256 != 0) return MOE_ERR_SHAPE;
+  const int64_t ny = panels(N, epilogue);
+  if (ny * BN * (int64_t)K > (int64_t)UINT32_MAX) return MOE_ERR_SHAPE;
+  if (!b || !packed) return MOE_ERR_NULL;
+  const int64_t units = (int64_t)groups * ny * BN * K / 16;
+  const int64_t blocks = (units + 255) / 256;
+  if (blocks > INT32_MAX) return MOE_ERR_SHAPE;
+  pack_weights_kernel<<<(unsigned)blocks, 256, 0, as_stream(stream)>>>(b, N, K, (int)ny, epilogue, units, packed);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
 extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int32_t* offsets, int32_t groups,
-                                    int64_t max_rows, const uint8_t* b, const float* bs, int32_t N, int32_t K,
-                                    int32_t epilogue, int32_t tile_rows, void* out, int out_dtype, float* out_scales,
-                                    void* workspace, size_t workspace_bytes, void* stream) {
+                                    int64_t max_rows, const uint8_t* b, int32_t b_layout, const float* bs, int32_t N,
+                                    int32_t K, int32_t epilogue, int32_t tile_rows, void* out, int out_dtype,
+                                    float* out_scales, void* workspace, size_t workspace_bytes, void* stream) {
   if (groups < 1 || groups > 4096 || max_rows < 0 || max_rows > INT32_MAX - 256) return MOE_ERR_SHAPE;
   if (N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return MOE_ERR_SHAPE;
   if (epilogue == MOE_EPI_STORE) {
@@ -418,8 +482,10 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int
     return MOE_ERR_ARG;
   }
   // byte offsets inside a and inside one group's weights are 32-bit in the kernel
-  if ((max_rows + 1) * (int64_t)K > (int64_t)UINT32_MAX || (int64_t)N * K > (int64_t)UINT32_MAX) return MOE_ERR_SHAPE;
+  if ((max_rows + 1) * (int64_t)K > (int64_t)UINT32_MAX || panels(N, epilogue) * BN * (int64_t)K > (int64_t)UINT32_MAX)
+    return MOE_ERR_SHAPE;
   if (tile_rows != 0 && tile_rows != 32 && tile_rows != 128) return MOE_ERR_ARG;
+  if (b_layout != MOE_B_ROWMAJOR && b_layout != MOE_B_PACKED) return MOE_ERR_ARG;
   if (max_rows == 0) return MOE_OK;
   if (!a || !as || !offsets || !b || !bs || !out) return MOE_ERR_NULL;
   if (epilogue == MOE_EPI_SWIGLU_QUANT && !out_scales) return MOE_ERR_NULL;
@@ -427,7 +493,7 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int
   const int bm = tile_rows != 0 ? tile_rows : auto_tile_rows(max_rows, groups);
   hipStream_t st = as_stream(stream);
   const int64_t mt = max_tiles_for(max_rows, groups, bm);
-  const int ny = (int)(epilogue == MOE_EPI_STORE ? ceil_div64(N, BN) : N / 256);
+  const int ny = (int)panels(N, epilogue);
   const int64_t nwg = mt * ny;
   if (nwg > INT32_MAX) return MOE_ERR_SHAPE;
   int4* tiles = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(workspace) + 256);
@@ -435,10 +501,15 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int
   tile_map_kernel<<<1, 1024, 0, st>>>(offsets, groups, bm, tiles, ntiles, (int)mt);
   MOE_CHECK_LAUNCH();
   const unsigned grid = (unsigned)nwg;
-  if (bm == 32)
-    launch<32>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
+  const bool pk = b_layout == MOE_B_PACKED;
+  if (bm == 32 && pk)
+    launch<32, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
+  else if (bm == 32)
+    launch<32, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
+  else if (pk)
+    launch<128, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
   else
-    launch<128>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
+    launch<128, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

@@ -11,7 +11,7 @@ router replay (section "Router replay") as a mode of the same forward.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 from typing import Optional
 
 import torch
@@ -21,15 +21,18 @@ import block_scaled_fp8_top_amd as M
 
 @dataclass
 class MoELayerWeights:
-    """Router gate and 128x128-block-quantised expert weights (group E is the shared expert)."""
+    """Router gate and 128x128-block-quantised expert weights (group E is the shared expert).
+    The forward streams the packed copies (w1p, w2p) when present, else the row-major codes."""
     wg: torch.Tensor                 # [E,H] fp32
     bias: Optional[torch.Tensor]     # [E] fp32
-    w1q: torch.Tensor                # [G,2F,H] e4m3 bytes
+    w1q: Optional[torch.Tensor]      # [G,2F,H] e4m3 bytes (None once packed without a row-major copy)
     w1s: torch.Tensor                # [G,2F/128,H/128] fp32
-    w2q: torch.Tensor                # [G,H,F] e4m3 bytes
+    w2q: Optional[torch.Tensor]      # [G,H,F] e4m3 bytes
     w2s: torch.Tensor                # [G,H/128,F/128] fp32
     cfg: M.RouterCfg
     shared: bool
+    w1p: Optional[M.PackedWeight] = None   # w1q packed for the SwiGLU epilogue
+    w2p: Optional[M.PackedWeight] = None   # w2q packed for the store epilogue
 
     @property
     def E(self) -> int:
@@ -41,11 +44,21 @@ class MoELayerWeights:
 
     @property
     def F(self) -> int:
-        return int(self.w2q.shape[2])
+        return int(self.w2s.shape[2]) * 128
 
     @property
     def groups(self) -> int:
-        return int(self.w1q.shape[0])
+        return int(self.w1s.shape[0])
+
+
+def pack_expert_weights(weights: MoELayerWeights, keep_rowmajor: bool = True, stream=None) -> MoELayerWeights:
+    """Weights with packed copies of w1 (SwiGLU panels) and w2 (store panels) for the grouped GEMM;
+    without ``keep_rowmajor`` the row-major codes are dropped."""
+    w1p = M.moe_pack_weights_fp8(weights.w1q, M.MOE_EPI_SWIGLU_QUANT, stream=stream)
+    w2p = M.moe_pack_weights_fp8(weights.w2q, M.MOE_EPI_STORE, stream=stream)
+    if keep_rowmajor:
+        return replace(weights, w1p=w1p, w2p=w2p)
+    return replace(weights, w1q=None, w2q=None, w1p=w1p, w2p=w2p)
 
 
 def quantize_expert_weights(groups: int, H: int, F: int, master, device="cuda", stream=None):
@@ -124,11 +137,11 @@ class MoELayer:
         M.moe_dispatch(self.idx, w.E, w.shared, self.xq, self.xs, workspace=self.workspace, out=self.disp,
                        stream=stream)
         mark(4)
-        M.moe_grouped_gemm_fp8(self.disp.aq, self.disp.as_, self.disp.offsets, w.w1q, w.w1s,
+        M.moe_grouped_gemm_fp8(self.disp.aq, self.disp.as_, self.disp.offsets, w.w1p or w.w1q, w.w1s,
                                epilogue=M.MOE_EPI_SWIGLU_QUANT, out=self.hq, out_scales=self.hs,
                                workspace=self.workspace, stream=stream)
         mark(5)
-        M.moe_grouped_gemm_fp8(self.hq, self.hs, self.disp.offsets, w.w2q, w.w2s, epilogue=M.MOE_EPI_STORE,
+        M.moe_grouped_gemm_fp8(self.hq, self.hs, self.disp.offsets, w.w2p or w.w2q, w.w2s, epilogue=M.MOE_EPI_STORE,
                                out_dtype=self.act, out=self.y, workspace=self.workspace, stream=stream)
         mark(6)
         shared_row = self.disp.offsets[w.E:w.E + 1] if w.shared else None

@@ -66,6 +66,10 @@ extern "C" {
 #define MOE_EPI_STORE 0        /* out = A * W^T in out_dtype (bf16 or fp32)                   */
 #define MOE_EPI_SWIGLU_QUANT 1 /* h = silu(gate) * up, then 1x128 FP8 quantisation of h     */
 
+/* weight layouts accepted by moe_grouped_gemm_fp8 */
+#define MOE_B_ROWMAJOR 0       /* b [groups, N, K] e4m3, row-major                             */
+#define MOE_B_PACKED 1         /* b rearranged by moe_pack_weights_fp8 for the same epilogue    */
+
 /* workspace query op codes */
 #define MOE_OP_DISPATCH 1
 #define MOE_OP_GROUPED_GEMM 2
@@ -152,12 +156,32 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32
                  const uint8_t* xq, const float* xs, int32_t H, int32_t* counts, int32_t* offsets, int32_t* dest_row,
                  int32_t* src_token, uint8_t* aq, float* as, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Weight packing for the grouped GEMM (a layout transform, not part of the method).  The GEMM's
+ * workgroups read each expert's weights as panels of 256 rows (for MOE_EPI_SWIGLU_QUANT: 128 gate
+ * rows [f0, f0+128) followed by the matching up rows [F+f0, F+f0+128)), 128 bytes of K at a time;
+ * in row-major order those are 256 separate 128-byte pieces at a stride of K bytes.  The packed
+ * layout stores every (group, panel, K step) as one contiguous 32 KB block, already in the order
+ * and 16-byte-chunk swizzle the GEMM keeps in LDS, so each K step streams one block from HBM.
+ *   b      [groups, N, K] e4m3 row-major (device, read)
+ *   packed [moe_packed_weight_bytes(groups, N, K, epilogue)] bytes (device, written); panels of a
+ *          STORE weight with N % 256 != 0 are padded with zero rows
+ *   epilogue: the epilogue of the GEMM calls that will use the packed weight (it fixes the panels)
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (N, K % 128; N % 256 for SwiGLU; a panel row of K bytes
+ *         times the panels of one group at or above 2^32), MOE_ERR_ARG (epilogue), MOE_ERR_HIP. */
+int moe_pack_weights_fp8(const uint8_t* b, int32_t groups, int32_t N, int32_t K, int32_t epilogue, uint8_t* packed,
+                         void* stream);
+
+/* Bytes of a packed weight: groups * ceil(N / 256) * 256 * K (equal to the row-major size when
+ * N % 256 == 0).  0 for invalid shapes. */
+size_t moe_packed_weight_bytes(int32_t groups, int32_t N, int32_t K, int32_t epilogue);
+
 /* Grouped block-scaled FP8 GEMM (blog sections "FP8 inference" / "FP8 training": the FP8 expert
  * GEMMs).  For each group g and each row r in [offsets[g], offsets[g+1]):
  *   acc[r,n] = sum over 128-wide K blocks kb of (as[r,kb] * bs[g,n/128,kb]) * sum_{k in kb} a[r,k]*b[g,n,k]
  * with fp32 accumulation (e4m3 products accumulated exactly inside each 128-block, then promoted).
  *   a  [max_rows, K] e4m3, as [max_rows, K/128] fp32; offsets [groups+1] device int32, offsets[groups] <= max_rows
- *   b  [groups, N, K] e4m3, bs [groups, N/128, K/128] fp32
+ *   b  [groups, N, K] e4m3 (b_layout MOE_B_ROWMAJOR) or the same weight after moe_pack_weights_fp8
+ *      with this call's epilogue (b_layout MOE_B_PACKED); bs [groups, N/128, K/128] fp32
  *   epilogue MOE_EPI_STORE:        out [max_rows, N] in out_dtype (MOE_BF16 or MOE_F32)
  *   epilogue MOE_EPI_SWIGLU_QUANT: N = 2F; h[r,f] = silu(acc[r,f]) * acc[r,F+f] in fp32, quantised
  *            1x128 as in moe_quant_fp8_block: out [max_rows, F] e4m3 (out_dtype MOE_FP8_E4M3),
@@ -166,12 +190,13 @@ int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32
  *            (32 when max_rows <= 64 * groups).  The result is the same for either height.
  *   Rows beyond offsets[groups] are not written.  workspace >= moe_workspace_bytes(MOE_OP_GROUPED_GEMM,
  *   max_rows, 0, groups, N, K).
- * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (N, K % 128; F % 128 for SwiGLU; (max_rows+1)*K or N*K at or
- *         above 2^32), MOE_ERR_DTYPE, MOE_ERR_ARG (epilogue, tile_rows), MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (N, K % 128; F % 128 for SwiGLU; (max_rows+1)*K or one group's
+ *         weight bytes at or above 2^32), MOE_ERR_DTYPE, MOE_ERR_ARG (epilogue, tile_rows, b_layout),
+ *         MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
 int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int32_t* offsets, int32_t groups, int64_t max_rows,
-                         const uint8_t* b, const float* bs, int32_t N, int32_t K, int32_t epilogue, int32_t tile_rows,
-                         void* out, int out_dtype, float* out_scales, void* workspace, size_t workspace_bytes,
-                         void* stream);
+                         const uint8_t* b, int32_t b_layout, const float* bs, int32_t N, int32_t K, int32_t epilogue,
+                         int32_t tile_rows, void* out, int out_dtype, float* out_scales, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* Combine (blog sections "Wide EP" / "Parallelism / EP": expert outputs return to token order).
  *   out[t,:] = sum_{j<k, dest_row[t,j] >= 0} topk_w[t,j] * y[dest_row[t,j],:]  (+ y[*shared_first_row + t,:])

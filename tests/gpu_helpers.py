@@ -12,7 +12,7 @@ import block_scaled_fp8_top_amd as M
 import oracle as O
 import oracle.layer as L
 import synth
-from block_scaled_fp8_top_amd.layer import MoELayer, MoELayerWeights, quantize_expert_weights
+from block_scaled_fp8_top_amd.layer import MoELayer, MoELayerWeights, pack_expert_weights, quantize_expert_weights
 
 DEV = "cuda"
 TOL = 2e-2          # max |gpu - ref| / max |ref| for GEMM and combine outputs
@@ -29,8 +29,9 @@ def gpu_weights(cfg: synth.LayerConfig, layer: int = 0, perturbed: bool = False)
     wg, b = synth.make_gate(cfg, layer, DEV, perturbed=perturbed)
     w1q, w1s, w2q, w2s = quantize_expert_weights(
         cfg.groups, cfg.H, cfg.F, lambda g: synth.make_expert(cfg, g, layer, DEV, perturbed=perturbed), device=DEV)
-    return MoELayerWeights(wg=wg, bias=b, w1q=w1q, w1s=w1s, w2q=w2q, w2s=w2s, cfg=cfgs_for(cfg)[0],
-                           shared=cfg.shared)
+    # the layer streams the packed copies; the row-major codes stay for the weight checks
+    return pack_expert_weights(MoELayerWeights(wg=wg, bias=b, w1q=w1q, w1s=w1s, w2q=w2q, w2s=w2s,
+                                               cfg=cfgs_for(cfg)[0], shared=cfg.shared))
 
 
 def oracle_layer(cfg: synth.LayerConfig, layer: int = 0, perturbed: bool = False) -> L.OracleLayer:

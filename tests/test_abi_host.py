@@ -113,8 +113,8 @@ def test_dispatch_validation(L):
 
 def test_gemm_validation(L):
     P = ctypes.c_void_p(256)
-    g = lambda N=256, K=256, epi=0, od=1, ws=P, wsb=1 << 20, osc=None, groups=4, tr=0, rows=100: (
-        P, P, P, groups, rows, P, P, N, K, epi, tr, P, od, osc, ws, wsb, None)
+    g = lambda N=256, K=256, epi=0, od=1, ws=P, wsb=1 << 20, osc=None, groups=4, tr=0, rows=100, bl=0: (
+        P, P, P, groups, rows, P, bl, P, N, K, epi, tr, P, od, osc, ws, wsb, None)
     assert L.moe_grouped_gemm_fp8(*g(N=200)) == SHAPE
     assert L.moe_grouped_gemm_fp8(*g(K=100)) == SHAPE
     assert L.moe_grouped_gemm_fp8(*g(od=2)) == DTYPE
@@ -127,6 +127,25 @@ def test_gemm_validation(L):
     assert L.moe_grouped_gemm_fp8(*g(tr=64)) == ARG                   # tile height neither 32 nor 128
     assert L.moe_grouped_gemm_fp8(*g(rows=1 << 20, K=4096)) == SHAPE   # 2^32 bytes of activations
     assert L.moe_grouped_gemm_fp8(*g(N=1 << 17, K=1 << 15)) == SHAPE   # 2^32 bytes of one group's weights
+    assert L.moe_grouped_gemm_fp8(*g(bl=2)) == ARG                    # unknown weight layout
+
+
+def test_pack_validation(L):
+    P = ctypes.c_void_p(256)
+    assert L.moe_pack_weights_fp8(P, 4, 256, 256, 7, P, None) == ARG
+    assert L.moe_pack_weights_fp8(P, 4, 384, 256, 1, P, None) == SHAPE      # SwiGLU panels need N % 256
+    assert L.moe_pack_weights_fp8(P, 4, 200, 256, 0, P, None) == SHAPE
+    assert L.moe_pack_weights_fp8(P, 0, 256, 256, 0, P, None) == SHAPE
+    assert L.moe_pack_weights_fp8(None, 4, 256, 256, 0, P, None) == NULL
+    assert L.moe_pack_weights_fp8(P, 4, 1 << 17, 1 << 15, 0, P, None) == SHAPE
+
+
+def test_packed_weight_bytes(L):
+    assert M.packed_weight_bytes(4, 256, 512, M.MOE_EPI_STORE) == 4 * 256 * 512
+    assert M.packed_weight_bytes(4, 384, 512, M.MOE_EPI_STORE) == 4 * 512 * 512      # padded to 2 panels
+    assert M.packed_weight_bytes(257, 4096, 6144, M.MOE_EPI_SWIGLU_QUANT) == 257 * 4096 * 6144
+    assert M.packed_weight_bytes(4, 384, 512, M.MOE_EPI_SWIGLU_QUANT) == 0
+    assert M.packed_weight_bytes(4, 256, 100, M.MOE_EPI_STORE) == 0
 
 
 def test_combine_validation(L):

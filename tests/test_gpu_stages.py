@@ -299,12 +299,64 @@ def test_grouped_gemm_exact_integers():
     for (sa, sb), tile in itertools.product(((1.0, 1.0), (0.25, 8.0)), TILES):
         as_ = torch.full((rows, K // 128), sa, dtype=torch.float32, device=DEV)
         bs = torch.full((G, N // 128, K // 128), sb, dtype=torch.float32, device=DEV)
-        y = M.moe_grouped_gemm_fp8(a, as_, torch.from_numpy(offsets.astype(np.int32)).to(DEV), b, bs,
-                                   M.MOE_EPI_STORE, torch.float32, tile_rows=tile)
+        goff = torch.from_numpy(offsets.astype(np.int32)).to(DEV)
         ref = O.moe_grouped_gemm_fp8(host(a), host(as_), offsets, host(b), host(bs))
-        assert_equal(f"exact integer GEMM (scales {sa},{sb}, tile {tile})", host(y), ref.astype(np.float32))
+        for bw in (b, M.moe_pack_weights_fp8(b, M.MOE_EPI_STORE)):   # N = 384: a zero-padded packed panel
+            y = M.moe_grouped_gemm_fp8(a, as_, goff, bw, bs, M.MOE_EPI_STORE, torch.float32, tile_rows=tile)
+            assert_equal(f"exact integer GEMM (scales {sa},{sb}, tile {tile}, {type(bw).__name__})", host(y),
+                         ref.astype(np.float32))
         assert np.array_equal(ref, sa * sb * np.concatenate(
             [ai[offsets[g]:offsets[g + 1]].numpy() @ bi[g].numpy().T for g in range(G)]))
+
+
+def _expected_pack(b: np.ndarray, epi: int) -> np.ndarray:
+    """The packed layout written out: block (g, panel, K step) = 2048 units of 16 bytes; unit
+    64 i + L holds chunk (L % 8) ^ ((r >> 1) & 7) of panel row r = 8 i + L / 8."""
+    G, N, K = b.shape
+    KB, F = K // 128, N // 2
+    ny = N // 256 if epi == M.MOE_EPI_SWIGLU_QUANT else -(-N // 256)
+    u = np.arange(2048)
+    r = (u >> 6) * 8 + ((u & 63) >> 3)
+    chunk = (u & 7) ^ ((r >> 1) & 7)
+    out = np.zeros((G, ny, KB, 2048, 16), np.uint8)
+    for nt in range(ny):
+        if epi == M.MOE_EPI_SWIGLU_QUANT:
+            n = np.where(r < 128, nt * 128 + r, F + nt * 128 + r - 128)
+        else:
+            n = nt * 256 + r
+        ok = n < N
+        for kb in range(KB):
+            cols = kb * 128 + chunk[:, None] * 16 + np.arange(16)
+            out[:, nt, kb, ok] = b[:, n[ok][:, None], cols[ok]]
+    return out.reshape(G, -1)
+
+
+@pytest.mark.parametrize("epi,N", [(M.MOE_EPI_STORE, 384), (M.MOE_EPI_STORE, 512), (M.MOE_EPI_SWIGLU_QUANT, 512)])
+def test_pack_weights_layout(epi, N):
+    G, K = 3, 384
+    b = synth.random_codes((G, N, K), 7, N + epi, device=DEV)
+    pw = M.moe_pack_weights_fp8(b, epi)
+    assert_equal(f"packed weight (epilogue {epi}, N {N})", host(pw.data), _expected_pack(host(b), epi))
+
+
+@pytest.mark.parametrize("name", NAMES)
+@pytest.mark.parametrize("tile", TILES)
+def test_grouped_gemm_packed_equals_rowmajor(name, tile):
+    """Packing only moves bytes: every output, code and scale is bitwise the row-major result."""
+    cfg = synth.CONFIGS[name]
+    for which, epi in (("w1", M.MOE_EPI_SWIGLU_QUANT), ("w2", M.MOE_EPI_STORE)):
+        offsets, a, as_, b, bs, N, K = _gemm_case(cfg, which, 11)
+        goff = torch.from_numpy(offsets).to(DEV)
+        pw = M.moe_pack_weights_fp8(b, epi)
+        r0 = M.moe_grouped_gemm_fp8(a, as_, goff, b, bs, epi, torch.float32, tile_rows=tile)
+        r1 = M.moe_grouped_gemm_fp8(a, as_, goff, pw, bs, epi, torch.float32, tile_rows=tile)
+        rows = int(offsets[-1])
+        if epi == M.MOE_EPI_STORE:
+            assert torch.equal(r0[:rows].view(torch.int32), r1[:rows].view(torch.int32)), f"{name} {which}"
+        else:
+            assert torch.equal(r0[0][:rows], r1[0][:rows]) and torch.equal(r0[1][:rows], r1[1][:rows]), f"{name} {which}"
+        del a, as_, b, bs, pw, r0, r1
+        _cleanup()
 
 
 @pytest.mark.parametrize("name", NAMES)
