@@ -29,10 +29,11 @@
 // lookahead.
 //
 // Tile order: a one-workgroup kernel turns `offsets` into the list of BM-row tiles (never
-// straddling a group).  The grid is one-dimensional; hardware workgroup ids are dealt to the 8
-// XCDs round-robin, so they are renumbered to make each XCD's ids contiguous, and logical tiles
-// run expert by expert, N-tile-major, so the workgroups alive on one XCD share the same A rows and
-// B columns in that XCD's L2.
+// straddling a group).  The grid is one-dimensional and sized for the worst case; hardware
+// workgroup ids are dealt to the 8 XCDs round-robin, so the ids that carry a tile are renumbered
+// to make each XCD's share contiguous (and equal), and logical tiles run expert by expert,
+// N-tile-major, so the workgroups alive on one XCD share the same A rows and B columns in that
+// XCD's L2.
 //
 // Epilogue STORE writes out in bf16 or fp32.  Epilogue SWIGLU_QUANT maps the 256 virtual columns
 // of a tile to 128 gate columns [f0, f0+128) and the matching 128 up columns [F+f0, F+f0+128); each
@@ -56,8 +57,8 @@ struct Tile {
   static constexpr int WN = 8 / WM;
   static constexpr int MS = BM_ / WM / 16;                   // 16 x 16 MFMA tiles per wave along M
   static constexpr int NS = BN / WN / 16;                    // ... along N
-  static constexpr int NSTAGE = BM_ >= 128 ? 3 : 4;
   static constexpr int A_BYTES = BM_ * BK, B_BYTES = BN * BK;
+  static constexpr int NSTAGE = 4 * (A_BYTES + B_BYTES) <= 150 * 1024 ? 4 : 3;   // ring within 160 KB of LDS
   static constexpr int A_INSTR = BM_ / 8;                    // 1 KB DMA instructions per A slice
   static constexpr int A_PW = A_INSTR >= 8 ? A_INSTR / 8 : 1;
   static constexpr int S_INSTR = BM_ >= 64 ? BM_ / 64 : 1;   // 256-byte scale DMA instructions
@@ -156,6 +157,26 @@ __device__ __forceinline__ void wait_vm(int n) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// Where unit u (a tile-row block x panel pair, in logical order) sits: group, rows, panel.
+struct Unit {
+  int g, row0, row_end, nt;
+};
+__device__ __forceinline__ Unit unit_at(int u, int ny, const int4* __restrict__ tiles, const int32_t* __restrict__ offsets,
+                                        int bm) {
+  const int q = u / ny;
+  const int4 tq = tiles[q];
+  const int local = u - tq.z * ny;
+  Unit r;
+  r.nt = local / tq.w;
+  r.g = tq.x;
+  r.row0 = offsets[r.g] + (local - r.nt * tq.w) * bm;
+  r.row_end = min(r.row0 + bm, offsets[r.g + 1]);
+  return r;
+}
+
+// Persistent workgroups: workgroup w takes units me(w), me(w) + G, me(w) + 2G, ... (G = grid size),
+// and its K steps over all of them form one stream: the DMA lookahead runs into the next unit while
+// the current unit's last steps and epilogue execute, so no unit pays the pipeline fill again.
 template <int BM, int EPI, bool OUT_BF16, bool PACKED>
 __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const int32_t* __restrict__ offsets,
@@ -165,98 +186,110 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   constexpr int WM = T::WM, WN = T::WN, MS = T::MS, NS = T::NS, HS = NS / 2, NSTAGE = T::NSTAGE;
   constexpr int A_BYTES = T::A_BYTES, B_BYTES = T::B_BYTES, AS_W = T::AS_W;
   constexpr int WROWS = MS * 16;   // rows per wave
+  constexpr int D = NSTAGE - 1;    // DMA lookahead in K steps
   __shared__ __attribute__((aligned(1024))) uint8_t a_lds[NSTAGE][A_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t b_lds[NSTAGE][B_BYTES];
-  __shared__ __attribute__((aligned(16))) float as_lds[4][AS_W];   // scale ring: slot kb & 3
+  __shared__ __attribute__((aligned(16))) float as_lds[4][AS_W];   // activation-scale ring: slot (step & 3)
+  __shared__ __attribute__((aligned(16))) float bsc_lds[4][64];    // weight-scale ring: [0] low, [1] high block
   __shared__ float red[WM][WN][WROWS];
 
-  // ---- logical tile: XCD-contiguous renumbering, then expert-major, N-tile-major order
-  const int nwg = gridDim.x;
+  // ---- this workgroup's units: each round of G consecutive logical units is split into
+  // XCD-contiguous equal shares (hardware ids are dealt to the 8 XCDs round-robin)
+  const int real = *ntiles * ny;
+  const int G = gridDim.x;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int L = xcd * (nwg >> 3) + min(xcd, nwg & 7) + slot;
-  const int q = L / ny;
-  if (q >= *ntiles) return;
-  const int4 tq = tiles[q];
-  const int local = L - tq.z * ny;
-  const int nt_idx = local / tq.w;
-  const int mt_idx = local - nt_idx * tq.w;
-  const int g = tq.x;
-  const int row0 = offsets[g] + mt_idx * BM;
-  const int row_end = min(row0 + BM, offsets[g + 1]);
+  const int me = xcd * (G >> 3) + min(xcd, G & 7) + slot;
+  if (me >= real) return;
+  const int nunits = (real - me + G - 1) / G;
   const int KB = K / BK;
-  const int F = N / 2;                                   // SwiGLU only
-  const int n0 = nt_idx * (EPI == 1 ? 128 : BN);         // first h column (SwiGLU) or output column
+  const int total = nunits * KB;   // K steps of this workgroup
+  const int F = N / 2;             // SwiGLU only
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
+  const size_t gstride = (PACKED ? (size_t)ny * BN : (size_t)N) * K;   // bytes of one group's weights
 
-  // this group's weights: row-major [N, K], or ny packed panels of 256 x K bytes
-  const uint8_t* bg = b + (size_t)g * (PACKED ? (size_t)ny * BN : (size_t)N) * K;
-  const float* bsg = bs + (size_t)g * (N / 128) * KB;
-
-  // ---- this lane's DMA sources.  A slice: instruction i covers rows 8i .. 8i+7; wave w issues
-  // instructions w*A_PW + j (or just w, for slices of fewer than 8 instructions).  B slice:
-  // instructions 4w .. 4w+3.  Lane: row 8i + lane/8, 16-byte chunk lane%8 (swizzled); for packed
-  // weights the lane's 16 bytes sit at 1024 i + 16 lane of the K step's block.
+  // ---- DMA roles.  A slice: instruction i covers rows 8i .. 8i+7; wave w issues instructions
+  // w*A_PW + j (or just w, for slices of fewer than 8 instructions).  B slice: instructions
+  // 4w .. 4w+3.  Lane: row 8i + lane/8, 16-byte chunk lane%8 (swizzled); for packed weights the
+  // lane's 16 bytes sit at 1024 i + 16 lane of the K step's block.
   const int drow = lane >> 3, dslot = lane & 7;
   const bool has_a = T::A_INSTR >= 8 || wave < T::A_INSTR;
   const int a_i0 = T::A_INSTR >= 8 ? wave * T::A_PW : wave;
-  // 32-bit byte offsets from a / from this group's weights (both < 2^32 for every supported shape);
-  // rows past the group end read the group's last row (any valid row would do)
-  uint32_t aoff[T::A_PW], boff[4];
-#pragma unroll
-  for (int j = 0; j < T::A_PW; ++j) {
-    const int r = (a_i0 + j) * 8 + drow;
-    aoff[j] = (uint32_t)min(row0 + r, row_end - 1) * (uint32_t)K + ((dslot ^ ((r >> 1) & 7)) << 4);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (PACKED) {
-      boff[i] = (uint32_t)nt_idx * (uint32_t)(BN * K) + (uint32_t)((4 * wave + i) * 1024 + lane * 16);
-    } else {
-      const int r = (4 * wave + i) * 8 + drow;
-      const int n = min(panel_row(EPI, nt_idx, r, F), N - 1);
-      boff[i] = (uint32_t)n * (uint32_t)K + ((dslot ^ ((r >> 1) & 7)) << 4);
-    }
-  }
-  // activation scales: the last S_INSTR waves each bring 64 rows' scales (4 bytes per lane)
-  const bool scale_loader = wave >= 8 - T::S_INSTR;
-  const int sidx = wave - (8 - T::S_INSTR);
-  const float* ssrc = as + (size_t)min(row0 + max(sidx, 0) * 64 + lane, row_end - 1) * KB;
-  // vector memory instructions per stage for this wave
-  const int per_stage = (has_a ? T::A_PW : 0) + 4 + (scale_loader ? 1 : 0);
+  const bool scale_loader = wave >= 8 - T::S_INSTR;   // the last S_INSTR waves bring 64 rows' scales each
+  const int sidx = max(wave - (8 - T::S_INSTR), 0);
+  // wave 0 also brings the step's two weight scales (lane 0: low 128-column block, lane 1: high)
+  const bool bscale_loader = wave == 0;
+  const int per_stage = (has_a ? T::A_PW : 0) + 4 + (scale_loader ? 1 : 0) + (bscale_loader ? 1 : 0);
 
-  // ---- wave's B rows in the LDS tile and its B scale row-blocks
+  // issue-side context of the unit whose steps are being issued: 32-bit byte offsets from a and
+  // from the unit's group weights (both < 2^32 for every accepted shape); rows past the tile's end
+  // read the tile's last row (any valid row would do)
+  uint32_t aoff[T::A_PW], boff[4];
+  const uint8_t* bg = b;
+  const float* ssrc = as;
+  const float* bsrc = bs;   // this lane's weight-scale row (low block for lane != 1)
+  int ii = 0, ik = 0;   // unit index and K step of the next step to issue
+#define GEMM_ISSUE_CTX(I)                                                                           \
+  do {                                                                                              \
+    const Unit un_ = unit_at(me + (I) * G, ny, tiles, offsets, BM);                                 \
+    _Pragma("unroll") for (int j_ = 0; j_ < T::A_PW; ++j_) {                                        \
+      const int r_ = (a_i0 + j_) * 8 + drow;                                                        \
+      aoff[j_] = (uint32_t)min(un_.row0 + r_, un_.row_end - 1) * (uint32_t)K + ((dslot ^ ((r_ >> 1) & 7)) << 4); \
+    }                                                                                               \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                              \
+      if (PACKED) {                                                                                 \
+        boff[i_] = (uint32_t)un_.nt * (uint32_t)(BN * K) + (uint32_t)((4 * wave + i_) * 1024 + lane * 16); \
+      } else {                                                                                      \
+        const int r_ = (4 * wave + i_) * 8 + drow;                                                  \
+        const int n_ = min(panel_row(EPI, un_.nt, r_, F), N - 1);                                   \
+        boff[i_] = (uint32_t)n_ * (uint32_t)K + ((dslot ^ ((r_ >> 1) & 7)) << 4);                   \
+      }                                                                                             \
+    }                                                                                               \
+    bg = b + (size_t)un_.g * gstride;                                                               \
+    ssrc = as + (size_t)min(un_.row0 + sidx * 64 + lane, un_.row_end - 1) * KB;                     \
+    const int nlo_ = EPI == 1 ? un_.nt : min(un_.nt * BN, N - 1) / 128;                             \
+    const int nhi_ = EPI == 1 ? (F / 128) + un_.nt : min(un_.nt * BN + 128, N - 1) / 128;           \
+    bsrc = bs + ((size_t)un_.g * (N / 128) + (lane == 1 ? nhi_ : nlo_)) * KB;                       \
+  } while (0)
+
+  // wave-uniform LDS destinations of this wave's DMA instructions, stage 0; stage s adds s * stride
+  const uint32_t a_dst = lds_u32(&a_lds[0][a_i0 * 1024]);
+  const uint32_t b_dst = lds_u32(&b_lds[0][(4 * wave) * 1024]);
+  const uint32_t s_dst = lds_u32(&as_lds[0][sidx * 64]);
+  const uint32_t bsc_dst = lds_u32(&bsc_lds[0][0]);
+  // issue K step ik of unit ii (global step SV) into LDS stage ST, then advance (ii, ik)
+#define GEMM_ISSUE(SV, ST)                                                                \
+  do {                                                                                    \
+    const uint32_t ko_ = (uint32_t)ik * BK;                                               \
+    const uint32_t kob_ = PACKED ? (uint32_t)ik * B_BYTES : ko_;                          \
+    if (has_a) {                                                                          \
+      const uint32_t ao_ = a_dst + (uint32_t)(ST) * A_BYTES;                              \
+      _Pragma("unroll") for (int j_ = 0; j_ < T::A_PW; ++j_)                               \
+        dma16(a + (aoff[j_] + ko_), ao_ + 1024 * j_);                                     \
+    }                                                                                     \
+    const uint32_t bo_ = b_dst + (uint32_t)(ST) * B_BYTES;                                \
+    dma16(bg + (boff[0] + kob_), bo_);                                                    \
+    dma16(bg + (boff[1] + kob_), bo_ + 1024);                                             \
+    dma16(bg + (boff[2] + kob_), bo_ + 2048);                                             \
+    dma16(bg + (boff[3] + kob_), bo_ + 3072);                                             \
+    if (scale_loader) dma4(ssrc + ik, s_dst + (uint32_t)((SV) & 3) * AS_W * 4);           \
+    if (bscale_loader) dma4(bsrc + ik, bsc_dst + (uint32_t)((SV) & 3) * 256);             \
+    if (++ik == KB) {                                                                     \
+      ik = 0;                                                                             \
+      if (++ii < nunits) GEMM_ISSUE_CTX(ii);                                              \
+    }                                                                                     \
+  } while (0)
+
+  // ---- compute-side context of the unit being accumulated
+  int ci = 0, ck = 0;   // unit index and K step being computed
+  Unit cu = unit_at(me, ny, tiles, offsets, BM);
   int b_lrow[NS];
 #pragma unroll
   for (int ns = 0; ns < NS; ++ns) {
     if (EPI == 1) b_lrow[ns] = ns < HS ? wn * HS * 16 + ns * 16 : 128 + wn * HS * 16 + (ns - HS) * 16;
     else b_lrow[ns] = wn * NS * 16 + ns * 16;
   }
-  const int nb_lo = EPI == 1 ? n0 / 128 : min(n0 + wn * NS * 16, N - 1) / 128;
-  const int nb_hi = EPI == 1 ? (F + n0) / 128 : nb_lo;
-  const bool wave_active = EPI == 1 ? true : (n0 + wn * NS * 16 < N);
-
-  // wave-uniform LDS destinations of this wave's DMA instructions, stage 0; stage s adds s * stride
-  const uint32_t a_dst = lds_u32(&a_lds[0][a_i0 * 1024]);
-  const uint32_t b_dst = lds_u32(&b_lds[0][(4 * wave) * 1024]);
-  const uint32_t s_dst = lds_u32(&as_lds[0][max(sidx, 0) * 64]);
-#define GEMM_ISSUE(KBV, ST)                                                           \
-  do {                                                                                \
-    const uint32_t ko_ = (uint32_t)(KBV) * BK;                                        \
-    const uint32_t kob_ = PACKED ? (uint32_t)(KBV) * B_BYTES : ko_;                   \
-    if (has_a) {                                                                      \
-      const uint32_t ao_ = a_dst + (uint32_t)(ST) * A_BYTES;                          \
-      _Pragma("unroll") for (int j_ = 0; j_ < T::A_PW; ++j_)                           \
-        dma16(a + (aoff[j_] + ko_), ao_ + 1024 * j_);                                 \
-    }                                                                                 \
-    const uint32_t bo_ = b_dst + (uint32_t)(ST) * B_BYTES;                            \
-    dma16(bg + (boff[0] + kob_), bo_);                                                 \
-    dma16(bg + (boff[1] + kob_), bo_ + 1024);                                          \
-    dma16(bg + (boff[2] + kob_), bo_ + 2048);                                          \
-    dma16(bg + (boff[3] + kob_), bo_ + 3072);                                          \
-    if (scale_loader) dma4(ssrc + (KBV), s_dst + (uint32_t)((KBV) & 3) * AS_W * 4);   \
-  } while (0)
 
   floatx4 acc[MS][NS];
 #pragma unroll
@@ -284,36 +317,32 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     }                                                                                                   \
   } while (0)
 
-  // weight scales of the next NSTAGE-1 K steps, in scalar registers (slot 0 = current step)
-  constexpr int D = NSTAGE - 1;
-  float sbl[D], sbh[D];
+  // ---- prologue: steps 0 .. D-1 in flight
+  GEMM_ISSUE_CTX(0);
 #pragma unroll
-  for (int s = 0; s < D; ++s) {
-    if (s < KB) {
-      GEMM_ISSUE(s, s);
-      sbl[s] = bsg[nb_lo * KB + s];
-      sbh[s] = bsg[nb_hi * KB + s];
-    } else {
-      sbl[s] = sbh[s] = 0.f;
-    }
-  }
-  int st = 0;   // LDS stage of step kb
-  for (int kb = 0; kb < KB; ++kb) {
-    // stages kb+1 .. kb+D-1 may stay in flight
-    wait_vm(per_stage * min(D - 1, KB - 1 - kb));
+  for (int s = 0; s < D; ++s)
+    if (s < total) GEMM_ISSUE(s, s);
+
+  int st = 0;   // LDS stage of step s
+  for (int s = 0; s < total; ++s) {
+    // steps s+1 .. s+D-1 may stay in flight.  Epilogue stores also count in vmcnt; leaving them
+    // out of the allowance only makes this wait stricter.
+    wait_vm(per_stage * min(D - 1, total - 1 - s));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    float sbl_n = 0.f, sbh_n = 0.f;
-    if (kb + D < KB) {
-      const int ist = st == 0 ? NSTAGE - 1 : st - 1;   // (kb + D) % NSTAGE: the stage read last step
-      GEMM_ISSUE(kb + D, ist);
-      sbl_n = bsg[nb_lo * KB + kb + D];
-      sbh_n = bsg[nb_hi * KB + kb + D];
+    if (s + D < total) {
+      const int ist = st == 0 ? NSTAGE - 1 : st - 1;   // (s + D) % NSTAGE: the stage read last step
+      GEMM_ISSUE(s + D, ist);
     }
+    const bool wave_active = EPI == 1 ? true : (cu.nt * BN + wn * NS * 16 < N);
     if (wave_active) {
       GEMM_READ(st);
-      const float* srow = &as_lds[kb & 3][wm * WROWS + (lane >> 4) * 4];
+      const float* srow = &as_lds[s & 3][wm * WROWS + (lane >> 4) * 4];
+      // weight scales of this step: SwiGLU gate columns use the low block and up columns the high
+      // one; a STORE wave's 16*NS columns lie in block (wn * NS * 16) / 128 of the panel
+      const float sb_lo = bsc_lds[s & 3][EPI == 1 ? 0 : (wn * NS * 16) / 128];
+      const float sb_hi = bsc_lds[s & 3][1];
       floatx4 p[MS][NS];
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms)
@@ -327,8 +356,8 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
         floatx4 c_lo, c_hi;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          c_lo[i] = sa[i] * sbl[0];
-          c_hi[i] = sa[i] * sbh[0];
+          c_lo[i] = sa[i] * sb_lo;
+          c_hi[i] = sa[i] * sb_hi;
         }
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
@@ -339,77 +368,84 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
         }
       }
     }
-#pragma unroll
-    for (int s = 0; s + 1 < D; ++s) {
-      sbl[s] = sbl[s + 1];
-      sbh[s] = sbh[s + 1];
-    }
-    sbl[D - 1] = sbl_n;
-    sbh[D - 1] = sbh_n;
     st = st + 1 == NSTAGE ? 0 : st + 1;
+
+    if (++ck < KB) continue;
+    // ---- epilogue of unit ci, then move on
+    const int row0 = cu.row0, row_end = cu.row_end;
+    if (EPI == 0) {
+      if (wave_active) {
+        const int c0 = cu.nt * BN + wn * NS * 16 + lr;
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = row0 + wm * WROWS + ms * 16 + (lane >> 4) * 4 + i;
+            if (r >= row_end) continue;
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) {
+              if (OUT_BF16)
+                reinterpret_cast<uint16_t*>(out)[(size_t)r * N + c0 + ns * 16] = f32_to_bf16(acc[ms][ns][i]);
+              else
+                reinterpret_cast<float*>(out)[(size_t)r * N + c0 + ns * 16] = acc[ms][ns][i];
+            }
+          }
+      }
+    } else {
+      // h for this lane: rows (ms, i), columns wn*HS*16 + hs*16 + lr (hs < HS) of the 128-wide block
+      float h[MS][HS][4];
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float mx = 0.0f;
+#pragma unroll
+          for (int hs = 0; hs < HS; ++hs) {
+            const float gt = acc[ms][hs][i], up = acc[ms][hs + HS][i];
+            const float v = (gt * up) / (1.0f + __expf(-gt));
+            h[ms][hs][i] = v;
+            mx = fmaxf(mx, fabsf(v));
+          }
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+          if (lr == 0) red[wm][wn][ms * 16 + (lane >> 4) * 4 + i] = mx;
+        }
+      // publish the row maxima (LDS only: a __syncthreads fence would also drain the DMA in flight)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      uint8_t* hq = reinterpret_cast<uint8_t*>(out);
+      const int FB = F / 128;
+      const int f0 = cu.nt * 128;
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int lrow = ms * 16 + (lane >> 4) * 4 + i;
+          float amax = red[wm][0][lrow];
+#pragma unroll
+          for (int w = 1; w < WN; ++w) amax = fmaxf(amax, red[wm][w][lrow]);
+          const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+          const int r = row0 + wm * WROWS + lrow;
+          if (r >= row_end) continue;
+#pragma unroll
+          for (int hs = 0; hs < HS; ++hs) {
+            const int col = f0 + wn * HS * 16 + hs * 16 + lr;
+            hq[(size_t)r * F + col] = (uint8_t)(e4m3_pack2(h[ms][hs][i] / sc, 0.0f) & 0xFF);
+          }
+          if (wn == 0 && lr == 0) out_scales[(size_t)r * FB + cu.nt] = sc;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+      for (int j = 0; j < NS; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    ck = 0;
+    if (++ci < nunits) cu = unit_at(me + ci * G, ny, tiles, offsets, BM);
   }
 #undef GEMM_READ
 #undef GEMM_ISSUE
-
-  // ---- epilogue
-  if (EPI == 0) {
-    if (!wave_active) return;
-#pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = row0 + wm * WROWS + ms * 16 + (lane >> 4) * 4 + i;
-        if (r >= row_end) continue;
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns) {
-          const int col = n0 + wn * NS * 16 + ns * 16 + lr;
-          if (OUT_BF16)
-            reinterpret_cast<uint16_t*>(out)[(size_t)r * N + col] = f32_to_bf16(acc[ms][ns][i]);
-          else
-            reinterpret_cast<float*>(out)[(size_t)r * N + col] = acc[ms][ns][i];
-        }
-      }
-  } else {
-    // h for this lane: rows (ms, i), columns wn*HS*16 + hs*16 + lr (hs < HS)
-    float h[MS][HS][4];
-#pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float mx = 0.0f;
-#pragma unroll
-        for (int hs = 0; hs < HS; ++hs) {
-          const float gt = acc[ms][hs][i], up = acc[ms][hs + HS][i];
-          const float v = (gt * up) / (1.0f + __expf(-gt));
-          h[ms][hs][i] = v;
-          mx = fmaxf(mx, fabsf(v));
-        }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        if (lr == 0) red[wm][wn][ms * 16 + (lane >> 4) * 4 + i] = mx;
-      }
-    __syncthreads();
-    uint8_t* hq = reinterpret_cast<uint8_t*>(out);
-    const int FB = F / 128;
-#pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int lrow = ms * 16 + (lane >> 4) * 4 + i;
-        float amax = red[wm][0][lrow];
-#pragma unroll
-        for (int w = 1; w < WN; ++w) amax = fmaxf(amax, red[wm][w][lrow]);
-        const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
-        const int r = row0 + wm * WROWS + lrow;
-        if (r >= row_end) continue;
-#pragma unroll
-        for (int hs = 0; hs < HS; ++hs) {
-          const int col = n0 + wn * HS * 16 + hs * 16 + lr;
-          hq[(size_t)r * F + col] = (uint8_t)(e4m3_pack2(h[ms][hs][i] / sc, 0.0f) & 0xFF);
-        }
-        if (wn == 0 && lr == 0) out_scales[(size_t)r * FB + n0 / 128] = sc;
-      }
-  }
+#undef GEMM_ISSUE_CTX
 }
 
 int64_t max_tiles_for(int64_t max_rows, int groups, int bm) { return ceil_div64(max_rows, bm) + groups; }
@@ -433,6 +469,18 @@ void launch(unsigned grid, hipStream_t st, int epilogue, int out_dtype, const ui
     grouped_gemm_kernel<BM, 1, false, PACKED><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b, bs, N,
                                                                          K, out, out_scales);
   }
+}
+
+// compute units of the current device, queried once per device
+int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  if (dev < 64) cached[dev] = n;
+  return n;
 }
 
 // panels per group: ceil(N / 256) for STORE, N / 256 for SwiGLU (N % 256 == 0 there)
@@ -484,7 +532,7 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int
   // byte offsets inside a and inside one group's weights are 32-bit in the kernel
   if ((max_rows + 1) * (int64_t)K > (int64_t)UINT32_MAX || panels(N, epilogue) * BN * (int64_t)K > (int64_t)UINT32_MAX)
     return MOE_ERR_SHAPE;
-  if (tile_rows != 0 && tile_rows != 32 && tile_rows != 128) return MOE_ERR_ARG;
+  if (tile_rows != 0 && tile_rows != 32 && tile_rows != 64 && tile_rows != 128) return MOE_ERR_ARG;
   if (b_layout != MOE_B_ROWMAJOR && b_layout != MOE_B_PACKED) return MOE_ERR_ARG;
   if (max_rows == 0) return MOE_OK;
   if (!a || !as || !offsets || !b || !bs || !out) return MOE_ERR_NULL;
@@ -498,14 +546,22 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int
   if (nwg > INT32_MAX) return MOE_ERR_SHAPE;
   int4* tiles = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(workspace) + 256);
   int32_t* ntiles = reinterpret_cast<int32_t*>(workspace);
+  const int cus = compute_units();
+  if (cus <= 0) return MOE_ERR_HIP;
   tile_map_kernel<<<1, 1024, 0, st>>>(offsets, groups, bm, tiles, ntiles, (int)mt);
   MOE_CHECK_LAUNCH();
-  const unsigned grid = (unsigned)nwg;
+  // one persistent workgroup per compute unit (the LDS ring admits one per CU), never more than
+  // the worst-case number of units
+  const unsigned grid = (unsigned)std::min<int64_t>(nwg, cus);
   const bool pk = b_layout == MOE_B_PACKED;
   if (bm == 32 && pk)
     launch<32, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
   else if (bm == 32)
     launch<32, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
+  else if (bm == 64 && pk)
+    launch<64, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
+  else if (bm == 64)
+    launch<64, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
   else if (pk)
     launch<128, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
   else

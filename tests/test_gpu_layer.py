@@ -113,6 +113,40 @@ def test_layer_deterministic_and_chunk_concatenation():
     assert torch.equal(torch.cat([a0, a1]).view(torch.int16), both.view(torch.int16))
 
 
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_layer_graph_replay_matches_eager(name):
+    """The whole forward captured in one HIP graph: every replay, with unrelated eager work and
+    synchronisations in between, reproduces the eager outputs bit for bit (no memset nodes, no
+    host synchronisation, all buffers preallocated)."""
+    cfg = synth.CONFIGS[name]
+    gw = gpu_weights(cfg)
+    lay = MoELayer(gw, cfg.T, _act(cfg))
+    other = MoELayer(gw, cfg.T, _act(cfg))
+    x = synth.make_x(cfg, DEV)
+    x2 = synth.make_x(cfg, DEV, chunk=1)
+    ref = lay.forward(x).clone()
+    ref_idx, ref_w = lay.idx.clone(), lay.wts.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            lay.forward(x)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(4):
+        lay.out.zero_()
+        lay.idx.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lay.out.view(torch.int16 if lay.out.dtype == torch.bfloat16 else torch.int32),
+                           ref.view(torch.int16 if ref.dtype == torch.bfloat16 else torch.int32)), f"replay {rep}"
+        assert torch.equal(lay.idx, ref_idx) and torch.equal(lay.wts.view(torch.int32), ref_w.view(torch.int32))
+        other.forward(x2)   # eager work on other buffers between replays
+        torch.cuda.synchronize()
+    del g, lay, other, gw
+    _free()
+
+
 def test_r3_stack_record_replay():
     """The prefill layer 4 deep at 32768 tokens: pass A routes with W and records the
     [num_layers, top_k, seq_len] payload; pass B replays it on W' = W + N(0, 1e-3); pass C
