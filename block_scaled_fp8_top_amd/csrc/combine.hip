@@ -1,8 +1,10 @@
 // Combine: out[t,:] = sum_j w[t,j] * y[dest_row[t,j],:] (+ y[shared_first_row + t,:]).
 //
-// One workgroup per token; each thread owns 8 consecutive columns (16-byte bf16 or 2 x 16-byte
-// fp32 loads).  Accumulation is fp32 with fused multiply-adds in slot order, the shared row
-// added last, one rounding to the output dtype.  No atomics: each output element has one owner.
+// One workgroup per (token, 2048-column slice); each thread owns 8 consecutive columns (16-byte
+// bf16 or 2 x 16-byte fp32 loads).  The rows of up to 8 slots are loaded together (all loads in
+// flight before the first use), then accumulated in fp32 with fused multiply-adds in slot order,
+// the shared row added last, one rounding to the output dtype.  No atomics: each output element
+// has one owner.
 #include "common.h"
 
 namespace {
@@ -33,16 +35,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   const int32_t* d = dest + t * k;
   const float* wt = w + t * k;
   const int64_t srow = shared_first_row ? (int64_t)(*shared_first_row) + t : -1;
-  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
+  if (c < H) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int32_t row = d[j];
-      if (row < 0) continue;
-      const float wj = wt[j];
-      float v[8];
-      load8y<YBF16>(y, (int64_t)row * H + c, v);
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      int32_t row[8];
+      float v[8][8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wj, v[q], acc[q]);
+      for (int j = 0; j < 8; ++j) {
+        row[j] = j0 + j < k ? d[j0 + j] : -1;
+        if (row[j] >= 0) load8y<YBF16>(y, (int64_t)row[j] * H + c, v[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (row[j] < 0) continue;
+        const float wj = wt[j0 + j];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wj, v[j][q], acc[q]);
+      }
     }
     if (srow >= 0) {
       float v[8];
@@ -75,7 +85,7 @@ extern "C" int moe_combine(const void* y, int y_dtype, const int32_t* dest_row, 
   if (!y || !dest_row || !topk_w || !out) return MOE_ERR_NULL;
   if (T > INT32_MAX) return MOE_ERR_SHAPE;
   hipStream_t st = as_stream(stream);
-  const unsigned grid = (unsigned)T;
+  const dim3 grid((unsigned)T, (unsigned)ceil_div64(H, 256 * 8));
   const bool yb = y_dtype == MOE_BF16, ob = out_dtype == MOE_BF16;
   if (yb && ob)
     combine_kernel<true, true><<<grid, 256, 0, st>>>(y, dest_row, topk_w, k, H, shared_first_row, out);

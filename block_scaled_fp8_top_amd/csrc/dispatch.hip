@@ -10,6 +10,9 @@
 //               slot's row is (chunk base) + (earlier slots of the chunk with that expert) --
 //               exactly the stable order.  Also fills the shared expert's rows.
 //   4. permute: rows [0, offsets[G]) copy xq[src_token[row]] and xs[src_token[row]].
+//
+// Small batches (decode: up to SMALL_MAX slots) run steps 1-3 in one workgroup instead
+// (small_dispatch_kernel), which gives the same stable order.
 #include <algorithm>
 
 #include "common.h"
@@ -138,6 +141,92 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint8_t* __restrict_
   }
 }
 
+constexpr int SMALL_MAX = 8192;       // slots
+constexpr int SMALL_CNT = 16384;      // (64-slot pieces) x experts counters in LDS
+
+// One workgroup for the whole batch.  The slots are cut into pieces of 64 (one wavefront step);
+// within a piece, lanes holding the same expert find each other with ballots over the expert id
+// bits, giving each slot its rank among the piece's earlier slots of that expert, and the group
+// leader records the piece's count for the expert.  Thread e then turns its expert's piece counts
+// into running bases (pieces in order), a block scan gives the expert offsets, and every slot's
+// row is offset + piece base + rank: the stable order.
+template <int BITS>
+__global__ __launch_bounds__(1024) void small_dispatch_kernel(const int32_t* __restrict__ idx, int nslots, int k, int E,
+                                                              int T, int append_shared, int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ dest_row,
+                                                              int32_t* __restrict__ src_token) {
+  __shared__ int sidx[SMALL_MAX];
+  __shared__ uint8_t srank[SMALL_MAX];
+  __shared__ int cnt[SMALL_CNT];      // [piece][e]
+  __shared__ int part[1024];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int npiece = (nslots + 63) / 64;
+  for (int i = tid; i < npiece * E; i += 1024) cnt[i] = 0;
+  for (int s = tid; s < nslots; s += 1024) sidx[s] = idx[s];
+  __syncthreads();
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int q = wave; q < npiece; q += 16) {
+    const int s = q * 64 + lane;
+    const bool in = s < nslots;
+    const int e = in ? sidx[s] : -1;
+    const bool valid = in && e >= 0 && e < E;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int bt = 0; bt < BITS; ++bt) {
+      const uint64_t m = __ballot(valid && ((e >> bt) & 1));
+      peers &= ((e >> bt) & 1) ? m : ~m;
+    }
+    if (valid) {
+      srank[s] = (uint8_t)__popcll(peers & lt);
+      if ((peers & lt) == 0) cnt[q * E + e] = __popcll(peers);   // group leader
+    } else if (in) {
+      dest_row[s] = -1;
+    }
+  }
+  __syncthreads();
+  // expert e: running bases over the pieces, then the block scan of the totals
+  int total = 0;
+  if (tid < E) {
+    for (int q = 0; q < npiece; ++q) {
+      const int c = cnt[q * E + tid];
+      cnt[q * E + tid] = total;
+      total += c;
+    }
+  }
+  part[tid] = total;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  const int routed = part[E - 1];
+  if (tid < E) {
+    counts[tid] = total;
+    offsets[tid] = part[tid] - total;
+  }
+  if (tid == 0) {
+    offsets[E] = routed;
+    if (append_shared) {
+      counts[E] = T;
+      offsets[E + 1] = routed + T;
+    }
+  }
+  __syncthreads();   // part[] now holds inclusive sums: offset of e = part[e] - (its total)
+  for (int s = tid; s < nslots; s += 1024) {
+    const int e = sidx[s];
+    if (e < 0 || e >= E) continue;
+    const int first = e == 0 ? 0 : part[e - 1];
+    const int row = first + cnt[(s >> 6) * E + e] + srank[s];
+    dest_row[s] = row;
+    src_token[row] = s / k;
+  }
+  if (append_shared)
+    for (int t = tid; t < T; t += 1024) src_token[routed + t] = t;
+}
+
 int64_t nchunks_for(int64_t T, int k) { return ceil_div64(T * k, CHUNK); }
 
 }  // namespace
@@ -163,6 +252,23 @@ extern "C" int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32
   int32_t* chunk_counts = reinterpret_cast<int32_t*>(workspace);
   int32_t* chunk_base = chunk_counts + nch * E;
   const int64_t nslots = T * k;
+  int bits = 1;
+  while ((1 << bits) < E) ++bits;
+  if (nslots <= SMALL_MAX && ceil_div64(nslots, 64) * E <= SMALL_CNT) {
+    switch (bits) {
+#define CASE_SMALL(B)                                                                                   \
+  case B:                                                                                               \
+    small_dispatch_kernel<B><<<1, 1024, 0, st>>>(topk_idx, (int)nslots, k, E, (int)T, append_shared, counts, \
+                                                 offsets, dest_row, src_token);                          \
+    break;
+      CASE_SMALL(1) CASE_SMALL(2) CASE_SMALL(3) CASE_SMALL(4) CASE_SMALL(5)
+      CASE_SMALL(6) CASE_SMALL(7) CASE_SMALL(8) CASE_SMALL(9) CASE_SMALL(10)
+#undef CASE_SMALL
+      default:
+        return MOE_ERR_SHAPE;
+    }
+    MOE_CHECK_LAUNCH();
+  } else {
   if (nch > 0) {
     count_kernel<<<(unsigned)nch, 256, 0, st>>>(topk_idx, nslots, E, chunk_counts);
     MOE_CHECK_LAUNCH();
@@ -170,8 +276,6 @@ extern "C" int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32
   scan_kernel<<<1, 1024, 0, st>>>(chunk_counts, (int)nch, E, append_shared, T, chunk_base, counts, offsets);
   MOE_CHECK_LAUNCH();
   if (nch > 0) {
-    int bits = 1;
-    while ((1 << bits) < E) ++bits;
     const unsigned g = (unsigned)nch;
     switch (bits) {
 #define CASE_BITS(B)                                                                                                  \
@@ -186,6 +290,7 @@ extern "C" int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32
         return MOE_ERR_SHAPE;
     }
     MOE_CHECK_LAUNCH();
+  }
   }
   if (copy_rows && T > 0) {
     const int G = E + (append_shared ? 1 : 0);

@@ -113,13 +113,15 @@ __global__ __launch_bounds__(NT) void gate_logits_kernel(const void* __restrict_
 
 // ------------------------------------------------------------------------------------------------
 // Small problems (decode-sized T*E): one wavefront per 8 tokens x 8 experts, one logit per lane.
-// Each output is a chain of H dependent fmas, so the launch is latency-bound; chunks of 256 columns
-// of x and Wg are copied global -> LDS by DMA (global_load_lds) into a 4-slot ring three chunks
-// ahead of the chain, so the chain never waits on memory.  Wg rows are padded by 16 bytes (bank
-// spread); x rows are stored in pairs, one DMA instruction per pair.
+// Each output is a chain of H dependent fmas, so the launch is latency-bound and the per-lane
+// instruction count per fma decides the time.  Chunks of 256 columns of x and Wg are copied
+// global -> LDS by DMA (global_load_lds) into a ring of NSLOT slots, NSLOT-1 chunks ahead of the
+// chain (as deep as the 6-bit vmcnt allows: five chunks for bf16 x, three for fp32); bf16 x
+// is widened to fp32 once per chunk into a separate LDS block (each of the 64 lanes converts 32
+// values, instead of every lane converting its whole row), so the chain loop is one 16-byte LDS
+// read of x, one of Wg and four fmas per 4 columns.  LDS rows are padded by 16 bytes (bank spread).
 constexpr int CH = 256;                       // columns per chunk
-constexpr int NSLOT = 4;
-constexpr int WROW = CH * 4 + 16;             // padded Wg row in LDS (bytes)
+constexpr int WROW = CH * 4 + 16;             // padded fp32 row in LDS (bytes): Wg and widened x
 
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(g) : "memory", "m0");
@@ -130,11 +132,13 @@ __global__ __launch_bounds__(64) void gate_logits_chain_kernel(const void* __res
                                                                const float* __restrict__ bias, int64_t T, int H,
                                                                int E, float* __restrict__ z) {
   constexpr int XB = BF16 ? 2 : 4;                       // bytes per x element
-  constexpr int XPAIR = 2 * CH * XB + 64;                // two x rows per DMA unit (+64 B pad between pairs)
-  constexpr int XINST = BF16 ? 1 : 2;                    // DMA instructions per x row pair
-  constexpr int XSLOT = 4 * XPAIR, WSLOT = 8 * WROW;
+  constexpr int NSLOT = BF16 ? 6 : 4;
+  constexpr int XROW = BF16 ? CH * 2 : WROW;             // raw x row in the ring (bytes)
+  constexpr int XSLOT = 8 * XROW, WSLOT = 8 * WROW;
+  constexpr int XINST = CH * XB / 1024;                  // DMA instructions per x row (1 KB each)
   __shared__ __attribute__((aligned(16))) uint8_t xs[NSLOT][XSLOT];
   __shared__ __attribute__((aligned(16))) uint8_t ws[NSLOT][WSLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t xf[BF16 ? 8 * WROW : 16];   // widened x of the current chunk
   const int lane = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * 8;
   const int e0 = blockIdx.y * 8;
@@ -142,9 +146,8 @@ __global__ __launch_bounds__(64) void gate_logits_chain_kernel(const void* __res
   const int nchunk = (H + CH - 1) / CH;
 
   // DMA sources (rows clamped into range; columns past H fetch column 0 of the same row).
-  //  bf16: instruction p carries rows 2p (lanes 0-31) and 2p+1 (lanes 32-63), 8 columns per lane;
-  //  fp32: instruction (p, q) carries row 2p+q, 4 columns per lane.
-  // In LDS, row r of a slot starts at (r / 2) * XPAIR + (r % 2) * CH * XB.
+  //  bf16 x: one instruction per pair of rows (lanes 0-31: row 2p, lanes 32-63: row 2p+1; 8 columns
+  //  per lane), landing as two consecutive 512-byte rows; fp32 x and Wg: one instruction per row.
   const uint32_t xbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&xs[0][0]);
   const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&ws[0][0]);
   const char* wrow[8];
@@ -153,70 +156,109 @@ __global__ __launch_bounds__(64) void gate_logits_chain_kernel(const void* __res
 
   auto issue = [&](int c, int slot) {
     const int h0 = c * CH;
+    if (BF16) {
 #pragma unroll
-    for (int pr = 0; pr < 4; ++pr)
-#pragma unroll
-      for (int q = 0; q < XINST; ++q) {
-        const int row = 2 * pr + (BF16 ? (lane >> 5) : q);
-        const int col = BF16 ? (lane & 31) * 8 : lane * 4;
+      for (int pr = 0; pr < 4; ++pr) {
+        const int col = (lane & 31) * 8;
         const int h = h0 + col < H ? h0 + col : 0;
-        const int64_t t = min(t0 + row, T - 1);
-        dma16(reinterpret_cast<const char*>(xv) + (t * H + h) * XB, xbase + slot * XSLOT + pr * XPAIR + q * CH * XB);
+        const int64_t t = min(t0 + 2 * pr + (lane >> 5), T - 1);
+        dma16(reinterpret_cast<const char*>(xv) + (t * H + h) * 2, xbase + slot * XSLOT + pr * 2 * XROW);
       }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int h = h0 + lane * 4 < H ? h0 + lane * 4 : 0;
+        const int64_t t = min(t0 + r, T - 1);
+        dma16(reinterpret_cast<const char*>(xv) + (t * H + h) * 4, xbase + slot * XSLOT + r * XROW);
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int h = h0 + lane * 4 < H ? h0 + lane * 4 : 0;
       dma16(wrow[r] + (int64_t)h * 4, wbase + slot * WSLOT + r * WROW);
     }
   };
+  constexpr int PER_CHUNK = (BF16 ? 4 : 8) + 8;          // DMA instructions per chunk
+  static_assert(XINST <= 1, "x row chunk fits one DMA instruction");
+  static_assert((NSLOT - 1) * PER_CHUNK <= 63 && NSLOT <= 6, "in-flight DMA fits vmcnt");
 
   for (int c = 0; c < NSLOT - 1 && c < nchunk; ++c) issue(c, c);
   float acc = 0.0f;
   for (int c = 0; c < nchunk; ++c) {
     const int left = min(nchunk - 1 - c, NSLOT - 2);   // chunks issued after c that may stay in flight
-    if (left == 2) {
-      if (BF16) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-    } else if (left == 1) {
-      if (BF16) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    switch (left) {
+      case 4: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * PER_CHUNK) : "memory"); break;
+      case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER_CHUNK) : "memory"); break;
+      case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER_CHUNK) : "memory"); break;
+      case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER_CHUNK) : "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (c + NSLOT - 1 < nchunk) issue(c + NSLOT - 1, (c + NSLOT - 1) % NSLOT);
     const int slot = c % NSLOT;
-    const uint8_t* xr = &xs[slot][(tt >> 1) * XPAIR + (tt & 1) * CH * XB];
-    const uint8_t* wr = &ws[slot][ee * WROW];
-    const int hc = min(CH, H - c * CH);
-#pragma unroll 4
-    for (int hh = 0; hh < hc; hh += 8) {
-      float xv8[8];
-      if (BF16) {
-        const uint4 u = *reinterpret_cast<const uint4*>(xr + hh * 2);
-        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+    const uint8_t* xr;
+    if (BF16) {
+      // widen: lane L converts row L/8, columns 32 (L%8) .. +32
+      const int r = lane >> 3, c0 = (lane & 7) * 32;
+      const uint8_t* src = &xs[slot][r * XROW + c0 * 2];
+      uint8_t* dst = &xf[r * WROW + c0 * 4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          xv8[2 * q] = __uint_as_float(w4[q] << 16);
-          xv8[2 * q + 1] = __uint_as_float(w4[q] & 0xFFFF0000u);
-        }
-      } else {
-        const float4 a = *reinterpret_cast<const float4*>(xr + hh * 4);
-        const float4 b = *reinterpret_cast<const float4*>(xr + hh * 4 + 16);
-        xv8[0] = a.x; xv8[1] = a.y; xv8[2] = a.z; xv8[3] = a.w; xv8[4] = b.x; xv8[5] = b.y; xv8[6] = b.z; xv8[7] = b.w;
+      for (int q = 0; q < 4; ++q) {
+        const uint4 u = *reinterpret_cast<const uint4*>(src + q * 16);
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+        float4 lo, hi;
+        lo.x = __uint_as_float(w4[0] << 16); lo.y = __uint_as_float(w4[0] & 0xFFFF0000u);
+        lo.z = __uint_as_float(w4[1] << 16); lo.w = __uint_as_float(w4[1] & 0xFFFF0000u);
+        hi.x = __uint_as_float(w4[2] << 16); hi.y = __uint_as_float(w4[2] & 0xFFFF0000u);
+        hi.z = __uint_as_float(w4[3] << 16); hi.w = __uint_as_float(w4[3] & 0xFFFF0000u);
+        *reinterpret_cast<float4*>(dst + q * 32) = lo;
+        *reinterpret_cast<float4*>(dst + q * 32 + 16) = hi;
       }
-      const float4 w0 = *reinterpret_cast<const float4*>(wr + hh * 4);
-      const float4 w1 = *reinterpret_cast<const float4*>(wr + hh * 4 + 16);
-      acc = __builtin_fmaf(xv8[0], w0.x, acc);
-      acc = __builtin_fmaf(xv8[1], w0.y, acc);
-      acc = __builtin_fmaf(xv8[2], w0.z, acc);
-      acc = __builtin_fmaf(xv8[3], w0.w, acc);
-      acc = __builtin_fmaf(xv8[4], w1.x, acc);
-      acc = __builtin_fmaf(xv8[5], w1.y, acc);
-      acc = __builtin_fmaf(xv8[6], w1.z, acc);
-      acc = __builtin_fmaf(xv8[7], w1.w, acc);
+      xr = &xf[tt * WROW];   // one wavefront: its LDS writes land before its later LDS reads
+    } else {
+      xr = &xs[slot][tt * XROW];
+    }
+    const uint8_t* wr = &ws[slot][ee * WROW];
+    const int hc = min(CH, H - c * CH);   // a multiple of 8
+    if (hc == CH) {
+      // full chunk: 8 batches of 32 columns, fully unrolled; the next batch's LDS reads are issued
+      // before this batch's fmas so their latency overlaps the chain
+      constexpr int U = 8, NB = CH / (4 * U);
+      float4 xb[2][U], wb[2][U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        xb[0][u] = *reinterpret_cast<const float4*>(xr + u * 16);
+        wb[0][u] = *reinterpret_cast<const float4*>(wr + u * 16);
+      }
+#pragma unroll
+      for (int bt = 0; bt < NB; ++bt) {
+        if (bt + 1 < NB) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            xb[(bt + 1) & 1][u] = *reinterpret_cast<const float4*>(xr + ((bt + 1) * 4 * U + 4 * u) * 4);
+            wb[(bt + 1) & 1][u] = *reinterpret_cast<const float4*>(wr + ((bt + 1) * 4 * U + 4 * u) * 4);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float4 xv4 = xb[bt & 1][u], wv4 = wb[bt & 1][u];
+          acc = __builtin_fmaf(xv4.x, wv4.x, acc);
+          acc = __builtin_fmaf(xv4.y, wv4.y, acc);
+          acc = __builtin_fmaf(xv4.z, wv4.z, acc);
+          acc = __builtin_fmaf(xv4.w, wv4.w, acc);
+        }
+      }
+    } else {
+      for (int hh = 0; hh < hc; hh += 4) {   // the last, partial chunk
+        const float4 xv4 = *reinterpret_cast<const float4*>(xr + hh * 4);
+        const float4 wv4 = *reinterpret_cast<const float4*>(wr + hh * 4);
+        acc = __builtin_fmaf(xv4.x, wv4.x, acc);
+        acc = __builtin_fmaf(xv4.y, wv4.y, acc);
+        acc = __builtin_fmaf(xv4.z, wv4.z, acc);
+        acc = __builtin_fmaf(xv4.w, wv4.w, acc);
+      }
     }
   }
   const int64_t t = t0 + tt;

@@ -223,6 +223,23 @@ def test_dispatch_all_one_expert_and_tiny():
         assert_equal("src", host(d.src_token)[:oo[-1]], osrc)
 
 
+@pytest.mark.parametrize("T,k,E", [(2048, 4, 64), (2049, 4, 64), (100, 8, 1024), (300, 6, 2), (1, 1, 1),
+                                   (1024, 8, 256), (640, 2, 1000)])
+def test_dispatch_small_and_chunked_paths(T, k, E):
+    """Batches on both sides of the one-workgroup path's limits (8192 slots, 16384 piece x expert
+    counters), every expert-id width, and dropped (-1) slots."""
+    rng = np.random.default_rng(T * 7 + k * 3 + E)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    idx[rng.random((T, k)) < 0.05] = -1
+    for shared in (False, True):
+        d = M.moe_dispatch(torch.from_numpy(idx).to(DEV), E, shared)
+        oc, oo, od, osrc = O.moe_dispatch(idx, E, shared)
+        assert_equal("counts", host(d.counts), oc)
+        assert_equal("offsets", host(d.offsets), oo)
+        assert_equal("dest_row", host(d.dest_row), od)
+        assert_equal("src_token", host(d.src_token)[:oo[-1]], osrc)
+
+
 # ----------------------------------------------------------------------------- grouped GEMM
 def _gemm_case(cfg, which, part):
     """Random codes/scales with the workload's group sizes; offsets from the oracle dispatch of
