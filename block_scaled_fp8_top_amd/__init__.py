@@ -307,7 +307,7 @@ def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tens
     """a [max_rows,K] uint8, as_ [max_rows,K/128], offsets [G+1] (device), b [G,N,K] uint8 or a
     PackedWeight packed for this epilogue, bs [G,N/128,K/128].
     STORE -> out [max_rows,N] (bf16/fp32); SWIGLU_QUANT -> (h codes [max_rows,N/2] uint8, scales [max_rows,N/256]).
-    tile_rows: 32, 64 or 128 rows per workgroup tile, 0 = chosen from the average group size."""
+    tile_rows: 32, 48, 64 or 128 rows per workgroup tile, 0 = chosen from the average group size."""
     max_rows, K = a.shape
     if isinstance(b, PackedWeight):
         if b.epilogue != epilogue:

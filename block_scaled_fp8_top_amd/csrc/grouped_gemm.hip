@@ -6,14 +6,15 @@
 // every MFMA produces a fresh 128-wide partial P that is promoted into the fp32 accumulator with
 // its scale product: acc = fma(P, as * bs, acc).
 //
-// Workgroup tile: BM rows x BN = 256 (virtual) columns, 8 wavefronts.  Two row-tile heights:
+// Workgroup tile: BM rows x BN = 256 (virtual) columns, 8 wavefronts.  Row-tile heights:
 //   BM = 128: waves in a 2 x 4 grid, each 64 x 64 (4 x 4 MFMA tiles of 16 x 16), 3-stage LDS ring
 //             (48 KB per stage) - for groups of hundreds of rows, where the tile's operand bytes per
 //             flop decide the speed;
-//   BM = 32:  waves in a 1 x 8 grid, each 32 x 32 (2 x 2 MFMA tiles), 4-stage ring (36 KB per
-//             stage) - for groups of a few dozen rows (decode), where the kernel streams the
-//             weights: a 128-row tile would spend most of its DMA and LDS on rows past the group
-//             end, and the deeper ring keeps more weight bytes in flight per CU.
+//   BM = 32, 48, 64: waves in a 1 x 8 grid, each BM x 32 (BM/16 x 2 MFMA tiles), a 4-stage ring
+//             for 32 and 48 rows (36 / 38 KB per stage), 3 stages for 64 - for groups of a few
+//             dozen rows (decode), where the kernel streams the weights: a 128-row tile would spend
+//             most of its DMA and LDS on rows past the group end, and the deeper ring keeps more
+//             weight bytes in flight per CU.
 //
 // Data movement: the A and B K-slices (128 bytes per row) and the tile's activation scales go
 // straight from global memory into the LDS ring with global_load_lds (no registers in between),
@@ -29,11 +30,10 @@
 // lookahead.
 //
 // Tile order: a one-workgroup kernel turns `offsets` into the list of BM-row tiles (never
-// straddling a group).  The grid is one-dimensional and sized for the worst case; hardware
-// workgroup ids are dealt to the 8 XCDs round-robin, so the ids that carry a tile are renumbered
-// to make each XCD's share contiguous (and equal), and logical tiles run expert by expert,
-// N-tile-major, so the workgroups alive on one XCD share the same A rows and B columns in that
-// XCD's L2.
+// straddling a group); a unit is one (tile, 256-column panel) pair, logical units run expert by
+// expert, panel-major.  One persistent workgroup per CU takes every G-th unit; each round of G
+// units is renumbered XCD-contiguously (hardware ids are dealt to the 8 XCDs round-robin) so that
+// neighbouring units, which share A rows or B panels, share an L2.
 //
 // Epilogue STORE writes out in bf16 or fp32.  Epilogue SWIGLU_QUANT maps the 256 virtual columns
 // of a tile to 128 gate columns [f0, f0+128) and the matching 128 up columns [F+f0, F+f0+128); each
@@ -58,7 +58,7 @@ struct Tile {
   static constexpr int MS = BM_ / WM / 16;                   // 16 x 16 MFMA tiles per wave along M
   static constexpr int NS = BN / WN / 16;                    // ... along N
   static constexpr int A_BYTES = BM_ * BK, B_BYTES = BN * BK;
-  static constexpr int NSTAGE = 4 * (A_BYTES + B_BYTES) <= 150 * 1024 ? 4 : 3;   // ring within 160 KB of LDS
+  static constexpr int NSTAGE = 4 * (A_BYTES + B_BYTES) <= 155 * 1024 ? 4 : 3;   // ring within 160 KB of LDS
   static constexpr int A_INSTR = BM_ / 8;                    // 1 KB DMA instructions per A slice
   static constexpr int A_PW = A_INSTR >= 8 ? A_INSTR / 8 : 1;
   static constexpr int S_INSTR = BM_ >= 64 ? BM_ / 64 : 1;   // 256-byte scale DMA instructions
@@ -82,6 +82,30 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
 }
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 4); }
+
+typedef uint32_t uint32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t uint32x4 __attribute__((ext_vector_type(4)));
+
+// 4 x 4 transpose inside each quad of lanes (DPP quad permutations, no LDS): on entry lane q of
+// the quad holds v[i] = M[i][q], on exit v[i] = M[q][i].  Two butterfly steps: across lane pairs
+// q ^ 1 the elements whose index bit 0 differs from q's are exchanged, then across q ^ 2 bit 1.
+__device__ __forceinline__ float dpp_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void quad_transpose(float (&v)[4], int q) {
+  float t[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[i] = dpp_xor1(v[i ^ 1]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = ((i ^ q) & 1) ? t[i] : v[i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[i] = dpp_xor2(v[i ^ 2]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = ((i ^ q) & 2) ? t[i] : v[i];
+}
 
 // Weight row held by virtual row r (0..255) of panel nt: SwiGLU panels pair gate rows
 // [128 nt, 128 nt + 128) with up rows [F + 128 nt, ...); STORE panels are rows [256 nt, 256 nt + 256).
@@ -149,8 +173,11 @@ __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {
 #define WAIT_CASE(N) \
   case N: asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory"); break;
-    WAIT_CASE(1) WAIT_CASE(2) WAIT_CASE(3) WAIT_CASE(4) WAIT_CASE(5) WAIT_CASE(6) WAIT_CASE(7) WAIT_CASE(8)
-    WAIT_CASE(9) WAIT_CASE(10) WAIT_CASE(11) WAIT_CASE(12) WAIT_CASE(13) WAIT_CASE(14) WAIT_CASE(15)
+#define WAIT_CASE8(B) WAIT_CASE(B) WAIT_CASE(B + 1) WAIT_CASE(B + 2) WAIT_CASE(B + 3) WAIT_CASE(B + 4) \
+  WAIT_CASE(B + 5) WAIT_CASE(B + 6) WAIT_CASE(B + 7)
+    WAIT_CASE(1) WAIT_CASE(2) WAIT_CASE(3) WAIT_CASE(4) WAIT_CASE(5) WAIT_CASE(6) WAIT_CASE(7)
+    WAIT_CASE8(8) WAIT_CASE8(16) WAIT_CASE8(24) WAIT_CASE8(32) WAIT_CASE8(40) WAIT_CASE8(48) WAIT_CASE8(56)
+#undef WAIT_CASE8
 #undef WAIT_CASE
     default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
@@ -198,6 +225,8 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   const int real = *ntiles * ny;
   const int G = gridDim.x;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  // each round's units XCD-contiguous: neighbouring units share A rows or B panels (a group's
+  // tiles of one panel are adjacent), and so share an L2
   const int me = xcd * (G >> 3) + min(xcd, G & 7) + slot;
   if (me >= real) return;
   const int nunits = (real - me + G - 1) / G;
@@ -323,11 +352,19 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   for (int s = 0; s < D; ++s)
     if (s < total) GEMM_ISSUE(s, s);
 
-  int st = 0;   // LDS stage of step s
+  int st = 0;         // LDS stage of step s
+  int recent[D];       // epilogue store instructions issued at the end of steps s-D .. s-1
+#pragma unroll
+  for (int j = 0; j < D; ++j) recent[j] = 0;
   for (int s = 0; s < total; ++s) {
-    // steps s+1 .. s+D-1 may stay in flight.  Epilogue stores also count in vmcnt; leaving them
-    // out of the allowance only makes this wait stricter.
-    wait_vm(per_stage * min(D - 1, total - 1 - s));
+    // Wait for this wave's DMA of step s.  vmcnt retires vector memory instructions in issue
+    // order, so the ones allowed to stay outstanding are exactly those issued after step s's
+    // DMA: the DMA of steps s+1 .. s+D-1 and the epilogue stores of the last D steps (each
+    // epilogue issues a fixed, wave-uniform number of stores; no store is skipped by a branch).
+    int later = per_stage * min(D - 1, total - 1 - s);
+#pragma unroll
+    for (int j = 0; j < D; ++j) later += recent[j];
+    wait_vm(min(later, 63));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -369,27 +406,45 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
       }
     }
     st = st + 1 == NSTAGE ? 0 : st + 1;
+#pragma unroll
+    for (int j = 0; j + 1 < D; ++j) recent[j] = recent[j + 1];
+    recent[D - 1] = 0;
 
     if (++ck < KB) continue;
-    // ---- epilogue of unit ci, then move on
-    const int row0 = cu.row0, row_end = cu.row_end;
+    // ---- epilogue of unit ci, then move on.  Each 16 x 16 result tile is transposed within lane
+    // quads (lane 4j+q then holds row 4(lane/16)+q, columns 4j..4j+3) so every lane writes one
+    // contiguous piece per tile; stores go through a buffer resource bounded by the unit's valid
+    // rows, so rows past the group end are dropped by the hardware instead of by a branch, and
+    // every wave issues a fixed number of stores.
+    const int row0 = cu.row0, nrows = cu.row_end - cu.row0;
+    const int q4 = lane & 3, tr = (lane >> 4) * 4 + q4;   // row within a 16-row tile after the transpose
+    const int tc = lr & ~3;                                // first of the lane's 4 columns
     if (EPI == 0) {
       if (wave_active) {
-        const int c0 = cu.nt * BN + wn * NS * 16 + lr;
+        constexpr int EB = OUT_BF16 ? 2 : 4;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<uint8_t*>(out) + (size_t)row0 * N * EB, 0, nrows * N * EB, 0x00020000);
+        const int c0 = cu.nt * BN + wn * NS * 16 + tc;
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = row0 + wm * WROWS + ms * 16 + (lane >> 4) * 4 + i;
-            if (r >= row_end) continue;
+          for (int ns = 0; ns < NS; ++ns) {
+            float v[4] = {acc[ms][ns][0], acc[ms][ns][1], acc[ms][ns][2], acc[ms][ns][3]};
+            quad_transpose(v, q4);
+            const int off = ((wm * WROWS + ms * 16 + tr) * N + c0 + ns * 16) * EB;
+            if (OUT_BF16) {
+              uint32x2 w;
+              w[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+              w[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+              __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, 0);
+            } else {
+              uint32x4 w;
 #pragma unroll
-            for (int ns = 0; ns < NS; ++ns) {
-              if (OUT_BF16)
-                reinterpret_cast<uint16_t*>(out)[(size_t)r * N + c0 + ns * 16] = f32_to_bf16(acc[ms][ns][i]);
-              else
-                reinterpret_cast<float*>(out)[(size_t)r * N + c0 + ns * 16] = acc[ms][ns][i];
+              for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(v[i]);
+              __builtin_amdgcn_raw_buffer_store_b128(w, rs, off, 0, 0);
             }
           }
+        recent[D - 1] = MS * NS;
       }
     } else {
       // h for this lane: rows (ms, i), columns wn*HS*16 + hs*16 + lr (hs < HS) of the 128-wide block
@@ -414,27 +469,34 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      uint8_t* hq = reinterpret_cast<uint8_t*>(out);
       const int FB = F / 128;
-      const int f0 = cu.nt * 128;
+      const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<uint8_t*>(out) + (size_t)row0 * F, 0, nrows * F, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+          out_scales + (size_t)row0 * FB, 0, nrows * FB * 4, 0x00020000);
+      const int f0 = cu.nt * 128 + wn * HS * 16 + tc;
 #pragma unroll
-      for (int ms = 0; ms < MS; ++ms)
+      for (int ms = 0; ms < MS; ++ms) {
+        const int lrow = ms * 16 + tr;   // this lane's row (after the transpose) within the wave's rows
+        float amax = red[wm][0][lrow];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int lrow = ms * 16 + (lane >> 4) * 4 + i;
-          float amax = red[wm][0][lrow];
+        for (int w = 1; w < WN; ++w) amax = fmaxf(amax, red[wm][w][lrow]);
+        const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+        const int row = wm * WROWS + lrow;
 #pragma unroll
-          for (int w = 1; w < WN; ++w) amax = fmaxf(amax, red[wm][w][lrow]);
-          const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
-          const int r = row0 + wm * WROWS + lrow;
-          if (r >= row_end) continue;
-#pragma unroll
-          for (int hs = 0; hs < HS; ++hs) {
-            const int col = f0 + wn * HS * 16 + hs * 16 + lr;
-            hq[(size_t)r * F + col] = (uint8_t)(e4m3_pack2(h[ms][hs][i] / sc, 0.0f) & 0xFF);
-          }
-          if (wn == 0 && lr == 0) out_scales[(size_t)r * FB + cu.nt] = sc;
+        for (int hs = 0; hs < HS; ++hs) {
+          float v[4] = {h[ms][hs][0], h[ms][hs][1], h[ms][hs][2], h[ms][hs][3]};
+          quad_transpose(v, q4);
+          const uint32_t codes = e4m3_pack4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
+          __builtin_amdgcn_raw_buffer_store_b32(codes, rq, row * F + f0 + hs * 16, 0, 0);
         }
+        // the row's scale: one lane per row (column group 0) of wave column 0; other lanes aim past
+        // the buffer's end, which the hardware drops
+        if (wn == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc,
+                                                (lr >> 2) == 0 ? (row * FB + cu.nt) * 4 : 0x7FFFFFF0, 0, 0);
+      }
+      recent[D - 1] = MS * HS + (wn == 0 ? MS : 0);
     }
 #pragma unroll
     for (int i = 0; i < MS; ++i)
@@ -450,9 +512,13 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
 
 int64_t max_tiles_for(int64_t max_rows, int groups, int bm) { return ceil_div64(max_rows, bm) + groups; }
 
-// Row-tile height when the caller leaves it open: short groups (average of at most 64 rows)
-// stream weights through the 32-row tile, longer ones use the 128-row tile.
-int auto_tile_rows(int64_t max_rows, int groups) { return max_rows <= (int64_t)groups * 64 ? 32 : 128; }
+// Row-tile height when the caller leaves it open: the smallest height that holds twice the
+// average group, so that few groups need a second tile (which streams the same weight panel
+// again); short groups then stream weights through 32- or 64-row tiles, long ones use 128.
+int auto_tile_rows(int64_t max_rows, int groups) {
+  const int64_t avg2 = 2 * ceil_div64(max_rows, groups);
+  return avg2 <= 32 ? 32 : avg2 <= 48 ? 48 : avg2 <= 64 ? 64 : 128;
+}
 
 template <int BM, bool PACKED>
 void launch(unsigned grid, hipStream_t st, int epilogue, int out_dtype, const uint8_t* a, const float* as,
@@ -532,7 +598,7 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int
   // byte offsets inside a and inside one group's weights are 32-bit in the kernel
   if ((max_rows + 1) * (int64_t)K > (int64_t)UINT32_MAX || panels(N, epilogue) * BN * (int64_t)K > (int64_t)UINT32_MAX)
     return MOE_ERR_SHAPE;
-  if (tile_rows != 0 && tile_rows != 32 && tile_rows != 64 && tile_rows != 128) return MOE_ERR_ARG;
+  if (tile_rows != 0 && tile_rows != 32 && tile_rows != 48 && tile_rows != 64 && tile_rows != 128) return MOE_ERR_ARG;
   if (b_layout != MOE_B_ROWMAJOR && b_layout != MOE_B_PACKED) return MOE_ERR_ARG;
   if (max_rows == 0) return MOE_OK;
   if (!a || !as || !offsets || !b || !bs || !out) return MOE_ERR_NULL;
@@ -558,6 +624,10 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int
     launch<32, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
   else if (bm == 32)
     launch<32, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
+  else if (bm == 48 && pk)
+    launch<48, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
+  else if (bm == 48)
+    launch<48, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
   else if (bm == 64 && pk)
     launch<64, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
   else if (bm == 64)

@@ -186,8 +186,9 @@ size_t moe_packed_weight_bytes(int32_t groups, int32_t N, int32_t K, int32_t epi
  *   epilogue MOE_EPI_SWIGLU_QUANT: N = 2F; h[r,f] = silu(acc[r,f]) * acc[r,F+f] in fp32, quantised
  *            1x128 as in moe_quant_fp8_block: out [max_rows, F] e4m3 (out_dtype MOE_FP8_E4M3),
  *            out_scales [max_rows, F/128] fp32
- *   tile_rows: rows per workgroup tile, 32, 64 or 128, or 0 to choose from the average group size
- *            (32 when max_rows <= 64 * groups).  The result is the same for either height.
+ *   tile_rows: rows per workgroup tile, 32, 48, 64 or 128, or 0 to choose from the average group size
+ *            (the smallest height >= 2 * ceil(max_rows / groups)).  The result is the same for every
+ *            height.
  *   Rows beyond offsets[groups] are not written.  workspace >= moe_workspace_bytes(MOE_OP_GROUPED_GEMM,
  *   max_rows, 0, groups, N, K).
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (N, K % 128; F % 128 for SwiGLU; (max_rows+1)*K or one group's

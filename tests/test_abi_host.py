@@ -124,7 +124,7 @@ def test_gemm_validation(L):
     assert L.moe_grouped_gemm_fp8(*g(epi=7)) == ARG
     assert L.moe_grouped_gemm_fp8(*g(groups=0)) == SHAPE
     assert L.moe_grouped_gemm_fp8(*g(wsb=8)) == WS
-    assert L.moe_grouped_gemm_fp8(*g(tr=48)) == ARG                   # tile height not 32, 64 or 128
+    assert L.moe_grouped_gemm_fp8(*g(tr=40)) == ARG                   # tile height not 32, 48, 64 or 128
     assert L.moe_grouped_gemm_fp8(*g(rows=1 << 20, K=4096)) == SHAPE   # 2^32 bytes of activations
     assert L.moe_grouped_gemm_fp8(*g(N=1 << 17, K=1 << 15)) == SHAPE   # 2^32 bytes of one group's weights
     assert L.moe_grouped_gemm_fp8(*g(bl=2)) == ARG                    # unknown weight layout

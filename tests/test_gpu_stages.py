@@ -18,7 +18,7 @@ from gpu_helpers import DEV, TOL, assert_equal, cfgs_for, host, rel_err, rows_ho
 
 pytestmark = pytest.mark.gpu
 NAMES = ["tiny", "decode", "prefill", "longctx", "r3"]
-TILES = [32, 64, 128]   # every row-tile height of the grouped GEMM, whichever the shape would pick
+TILES = [32, 48, 64, 128]   # every row-tile height of the grouped GEMM, whichever the shape would pick
 
 
 def _cleanup():
