@@ -28,8 +28,9 @@ MOE_OP_DISPATCH, MOE_OP_GROUPED_GEMM = 1, 2
 MOE_B_ROWMAJOR, MOE_B_PACKED = 0, 1
 
 EXPORTED = ("moe_gate_logits", "moe_route", "moe_replay_route", "moe_router_score_eval", "moe_quant_fp8_block",
-            "moe_dispatch", "moe_pack_weights_fp8", "moe_packed_weight_bytes", "moe_grouped_gemm_fp8", "moe_combine",
-            "moe_workspace_bytes", "moe_status_str", "moe_version")
+            "moe_dispatch", "moe_pack_weights_fp8", "moe_packed_weight_bytes", "moe_grouped_gemm_plan",
+            "moe_grouped_gemm_fp8_planned", "moe_grouped_gemm_fp8", "moe_combine", "moe_workspace_bytes",
+            "moe_status_str", "moe_version")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -40,6 +41,12 @@ class MoeError(RuntimeError):
     def __init__(self, code: int, what: str):
         super().__init__(f"{what}: status {code} ({status_str(code)})")
         self.code = code
+
+
+class GemmPlan(ctypes.Structure):
+    """Host half of a grouped-GEMM tile plan (the tile list itself lives in the workspace)."""
+    _fields_ = [("tile_rows", ctypes.c_int32), ("groups", ctypes.c_int32), ("max_rows", ctypes.c_int64),
+                ("workspace", ctypes.c_void_p)]
 
 
 class RouterCfg(ctypes.Structure):
@@ -71,6 +78,9 @@ def lib():
         "moe_pack_weights_fp8": [P, I32, I32, I32, I32, P, P],
         "moe_packed_weight_bytes": [I32, I32, I32, I32],
         "moe_grouped_gemm_fp8": [P, P, P, I32, I64, P, I32, P, I32, I32, I32, I32, P, ctypes.c_int, P, P, SZ, P],
+        "moe_grouped_gemm_plan": [P, I32, I64, I32, P, SZ, ctypes.POINTER(GemmPlan), P],
+        "moe_grouped_gemm_fp8_planned": [ctypes.POINTER(GemmPlan), P, P, P, P, I32, P, I32, I32, I32, P, ctypes.c_int,
+                                         P, P],
         "moe_combine": [P, ctypes.c_int, P, P, I64, I32, I32, P, P, ctypes.c_int, P],
         "moe_workspace_bytes": [ctypes.c_int, I64, I32, I32, I32, I32],
         "moe_status_str": [ctypes.c_int],
@@ -301,13 +311,31 @@ def moe_pack_weights_fp8(b: torch.Tensor, epilogue: int, out: Optional[torch.Ten
     return PackedWeight(out, G, N, K, epilogue)
 
 
+def moe_grouped_gemm_plan(offsets: torch.Tensor, max_rows: int, workspace: torch.Tensor, tile_rows: int = 0,
+                          stream=None):
+    """Tile plan of the groups in ``offsets`` [G+1] (device) for up to max_rows rows, written into
+    ``workspace``; returns the host plan to pass as ``plan=`` to moe_grouped_gemm_fp8.  The
+    workspace must not be reused until the GEMMs that use the plan have run."""
+    G = offsets.shape[0] - 1
+    _dev(offsets, "offsets", torch.int32, (G + 1,))
+    plan = GemmPlan()
+    _check(lib().moe_grouped_gemm_plan(_p(offsets), G, max_rows, tile_rows, _p(workspace),
+                                       workspace.numel() * workspace.element_size(), ctypes.byref(plan),
+                                       _stream(stream)), "moe_grouped_gemm_plan")
+    plan._keep = workspace   # the tile list lives there
+    return plan
+
+
 def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tensor, b, bs: torch.Tensor,
                          epilogue: int = MOE_EPI_STORE, out_dtype=torch.bfloat16, out=None, out_scales=None,
-                         workspace: Optional[torch.Tensor] = None, stream=None, tile_rows: int = 0):
+                         workspace: Optional[torch.Tensor] = None, stream=None, tile_rows: int = 0,
+                         plan: Optional[GemmPlan] = None):
     """a [max_rows,K] uint8, as_ [max_rows,K/128], offsets [G+1] (device), b [G,N,K] uint8 or a
     PackedWeight packed for this epilogue, bs [G,N/128,K/128].
     STORE -> out [max_rows,N] (bf16/fp32); SWIGLU_QUANT -> (h codes [max_rows,N/2] uint8, scales [max_rows,N/256]).
-    tile_rows: 32, 48, 64 or 128 rows per workgroup tile, 0 = chosen from the average group size."""
+    tile_rows: 32, 48, 64 or 128 rows per workgroup tile, 0 = chosen from the average group size.
+    plan: a plan from moe_grouped_gemm_plan for these offsets and max_rows (then no workspace is
+    needed and tile_rows is the plan's)."""
     max_rows, K = a.shape
     if isinstance(b, PackedWeight):
         if b.epilogue != epilogue:
@@ -325,11 +353,15 @@ def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tens
     _dev(offsets, "offsets", torch.int32, (G + 1,))
     _dev(bs, "bs", torch.float32, (G, N // 128, K // 128))
     dev = a.device
-    ws_need = workspace_bytes(MOE_OP_GROUPED_GEMM, max_rows, 0, G, N, K)
-    if workspace is None:
-        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
-    elif workspace.numel() * workspace.element_size() < ws_need:
-        raise ValueError("workspace too small")
+    if plan is not None:
+        if plan.groups != G or plan.max_rows != max_rows:
+            raise ValueError("plan was made for other groups / rows")
+    else:
+        ws_need = workspace_bytes(MOE_OP_GROUPED_GEMM, max_rows, 0, G, N, K)
+        if workspace is None:
+            workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+        elif workspace.numel() * workspace.element_size() < ws_need:
+            raise ValueError("workspace too small")
     if epilogue == MOE_EPI_STORE:
         code = MOE_BF16 if out_dtype == torch.bfloat16 else MOE_F32
         out = torch.empty((max_rows, N), dtype=out_dtype, device=dev) if out is None else _dev(out, "out", out_dtype, (max_rows, N))
@@ -340,6 +372,11 @@ def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tens
         out = torch.empty((max_rows, F), dtype=FP8, device=dev) if out is None else _dev(out, "out", FP8, (max_rows, F))
         osc = torch.empty((max_rows, F // 128), dtype=torch.float32, device=dev) if out_scales is None else \
             _dev(out_scales, "out_scales", torch.float32, (max_rows, F // 128))
+    if plan is not None:
+        _check(lib().moe_grouped_gemm_fp8_planned(ctypes.byref(plan), _p(a), _p(as_), _p(offsets), _p(b_t), b_layout,
+                                                  _p(bs), N, K, epilogue, _p(out), code, _p(osc), _stream(stream)),
+               "moe_grouped_gemm_fp8_planned")
+        return out if epilogue == MOE_EPI_STORE else (out, osc)
     _check(lib().moe_grouped_gemm_fp8(_p(a), _p(as_), _p(offsets), G, max_rows, _p(b_t), b_layout, _p(bs), N, K,
                                       epilogue, tile_rows, _p(out),
                                       code, _p(osc), _p(workspace), workspace.numel() * workspace.element_size(),

@@ -581,10 +581,11 @@ extern "C" int moe_pack_weights_fp8(const uint8_t* b, int32_t groups, int32_t N,
   return MOE_OK;
 }
 
-extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int32_t* offsets, int32_t groups,
-                                    int64_t max_rows, const uint8_t* b, int32_t b_layout, const float* bs, int32_t N,
-                                    int32_t K, int32_t epilogue, int32_t tile_rows, void* out, int out_dtype,
-                                    float* out_scales, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// argument checks shared by the one-call and the planned entry points
+int check_gemm_args(int64_t max_rows, int32_t groups, int32_t N, int32_t K, int32_t epilogue, int out_dtype,
+                    int32_t b_layout) {
   if (groups < 1 || groups > 4096 || max_rows < 0 || max_rows > INT32_MAX - 256) return MOE_ERR_SHAPE;
   if (N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return MOE_ERR_SHAPE;
   if (epilogue == MOE_EPI_STORE) {
@@ -598,24 +599,56 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int
   // byte offsets inside a and inside one group's weights are 32-bit in the kernel
   if ((max_rows + 1) * (int64_t)K > (int64_t)UINT32_MAX || panels(N, epilogue) * BN * (int64_t)K > (int64_t)UINT32_MAX)
     return MOE_ERR_SHAPE;
-  if (tile_rows != 0 && tile_rows != 32 && tile_rows != 48 && tile_rows != 64 && tile_rows != 128) return MOE_ERR_ARG;
   if (b_layout != MOE_B_ROWMAJOR && b_layout != MOE_B_PACKED) return MOE_ERR_ARG;
-  if (max_rows == 0) return MOE_OK;
-  if (!a || !as || !offsets || !b || !bs || !out) return MOE_ERR_NULL;
-  if (epilogue == MOE_EPI_SWIGLU_QUANT && !out_scales) return MOE_ERR_NULL;
-  if (!workspace || workspace_bytes < moe_gemm_workspace(max_rows, groups)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_grouped_gemm_plan(const int32_t* offsets, int32_t groups, int64_t max_rows, int32_t tile_rows,
+                                     void* workspace, size_t workspace_bytes, moe_gemm_plan* plan, void* stream) {
+  if (!plan) return MOE_ERR_NULL;
+  if (groups < 1 || groups > 4096 || max_rows < 0 || max_rows > INT32_MAX - 256) return MOE_ERR_SHAPE;
+  if (tile_rows != 0 && tile_rows != 32 && tile_rows != 48 && tile_rows != 64 && tile_rows != 128) return MOE_ERR_ARG;
   const int bm = tile_rows != 0 ? tile_rows : auto_tile_rows(max_rows, groups);
+  plan->tile_rows = bm;
+  plan->groups = groups;
+  plan->max_rows = max_rows;
+  plan->workspace = workspace;
+  if (max_rows == 0) return MOE_OK;
+  if (!offsets) return MOE_ERR_NULL;
+  if (!workspace || workspace_bytes < moe_gemm_workspace(max_rows, groups)) return MOE_ERR_WORKSPACE;
+  const int64_t mt = max_tiles_for(max_rows, groups, bm);
+  int4* tiles = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(workspace) + 256);
+  int32_t* ntiles = reinterpret_cast<int32_t*>(workspace);
+  tile_map_kernel<<<1, 1024, 0, as_stream(stream)>>>(offsets, groups, bm, tiles, ntiles, (int)mt);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+extern "C" int moe_grouped_gemm_fp8_planned(const moe_gemm_plan* plan, const uint8_t* a, const float* as,
+                                            const int32_t* offsets, const uint8_t* b, int32_t b_layout,
+                                            const float* bs, int32_t N, int32_t K, int32_t epilogue, void* out,
+                                            int out_dtype, float* out_scales, void* stream) {
+  if (!plan) return MOE_ERR_NULL;
+  const int64_t max_rows = plan->max_rows;
+  const int32_t groups = plan->groups;
+  const int bm = plan->tile_rows;
+  int rc = check_gemm_args(max_rows, groups, N, K, epilogue, out_dtype, b_layout);
+  if (rc != MOE_OK) return rc;
+  if (bm != 32 && bm != 48 && bm != 64 && bm != 128) return MOE_ERR_ARG;
+  if (max_rows == 0) return MOE_OK;
+  if (!a || !as || !offsets || !b || !bs || !out || !plan->workspace) return MOE_ERR_NULL;
+  if (epilogue == MOE_EPI_SWIGLU_QUANT && !out_scales) return MOE_ERR_NULL;
   hipStream_t st = as_stream(stream);
   const int64_t mt = max_tiles_for(max_rows, groups, bm);
   const int ny = (int)panels(N, epilogue);
   const int64_t nwg = mt * ny;
   if (nwg > INT32_MAX) return MOE_ERR_SHAPE;
-  int4* tiles = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(workspace) + 256);
-  int32_t* ntiles = reinterpret_cast<int32_t*>(workspace);
+  const int4* tiles = reinterpret_cast<const int4*>(reinterpret_cast<const uint8_t*>(plan->workspace) + 256);
+  const int32_t* ntiles = reinterpret_cast<const int32_t*>(plan->workspace);
   const int cus = compute_units();
   if (cus <= 0) return MOE_ERR_HIP;
-  tile_map_kernel<<<1, 1024, 0, st>>>(offsets, groups, bm, tiles, ntiles, (int)mt);
-  MOE_CHECK_LAUNCH();
   // one persistent workgroup per compute unit (the LDS ring admits one per CU), never more than
   // the worst-case number of units
   const unsigned grid = (unsigned)std::min<int64_t>(nwg, cus);
@@ -638,4 +671,23 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int
     launch<128, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
+}
+
+extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int32_t* offsets, int32_t groups,
+                                    int64_t max_rows, const uint8_t* b, int32_t b_layout, const float* bs, int32_t N,
+                                    int32_t K, int32_t epilogue, int32_t tile_rows, void* out, int out_dtype,
+                                    float* out_scales, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_gemm_args(max_rows, groups, N, K, epilogue, out_dtype, b_layout);
+  if (rc != MOE_OK) return rc;
+  if (tile_rows != 0 && tile_rows != 32 && tile_rows != 48 && tile_rows != 64 && tile_rows != 128) return MOE_ERR_ARG;
+  if (max_rows == 0) return MOE_OK;
+  if (!a || !as || !offsets || !b || !bs || !out) return MOE_ERR_NULL;
+  if (epilogue == MOE_EPI_SWIGLU_QUANT && !out_scales) return MOE_ERR_NULL;
+  if (!workspace || workspace_bytes < moe_gemm_workspace(max_rows, groups)) return MOE_ERR_WORKSPACE;
+  if (compute_units() <= 0) return MOE_ERR_HIP;
+  moe_gemm_plan plan;
+  rc = moe_grouped_gemm_plan(offsets, groups, max_rows, tile_rows, workspace, workspace_bytes, &plan, stream);
+  if (rc != MOE_OK) return rc;
+  return moe_grouped_gemm_fp8_planned(&plan, a, as, offsets, b, b_layout, bs, N, K, epilogue, out, out_dtype,
+                                      out_scales, stream);
 }

@@ -2,8 +2,9 @@
 
 forward(x) enqueues, on the current stream and without any host synchronisation:
   moe_gate_logits -> moe_route (optionally recording into the routing payload) or
-  moe_replay_route -> moe_quant_fp8_block (x, 1x128) -> moe_dispatch -> moe_grouped_gemm_fp8
-  (W1, SwiGLU + 1x128 quantisation of h) -> moe_grouped_gemm_fp8 (W2) -> moe_combine.
+  moe_replay_route -> moe_quant_fp8_block (x, 1x128) -> moe_dispatch -> moe_grouped_gemm_plan ->
+  moe_grouped_gemm_fp8_planned (W1, SwiGLU + 1x128 quantisation of h) -> moe_grouped_gemm_fp8_planned
+  (W2) -> moe_combine.
 
 This is the layer that "RL at 1T Scale: prime-rl Performance Deep Dive" runs in FP8 at inference
 (section "FP8 inference") and in block-scaled FP8 in the trainer (section "FP8 training"), with
@@ -103,10 +104,9 @@ class MoELayer:
         self.hs = torch.empty((self.max_rows, F // 128), dtype=torch.float32, device=d)
         self.y = torch.empty((self.max_rows, H), dtype=act_dtype, device=d)
         self.out = torch.empty((T_max, H), dtype=act_dtype, device=d)
-        ws = max(M.workspace_bytes(M.MOE_OP_DISPATCH, T_max, k, E),
-                 M.workspace_bytes(M.MOE_OP_GROUPED_GEMM, self.max_rows, 0, G, 2 * F, H),
-                 M.workspace_bytes(M.MOE_OP_GROUPED_GEMM, self.max_rows, 0, G, H, F))
-        self.workspace = torch.empty(ws, dtype=torch.uint8, device=d)
+        self.workspace = torch.empty(M.workspace_bytes(M.MOE_OP_DISPATCH, T_max, k, E), dtype=torch.uint8, device=d)
+        self.gemm_ws = torch.empty(M.workspace_bytes(M.MOE_OP_GROUPED_GEMM, self.max_rows, 0, G, 0, 0),
+                                   dtype=torch.uint8, device=d)
         self.bad = torch.zeros(1, dtype=torch.int32, device=d)
 
     def forward(self, x: torch.Tensor, replay: Optional[torch.Tensor] = None, record: Optional[torch.Tensor] = None,
@@ -136,13 +136,15 @@ class MoELayer:
         mark(3)
         M.moe_dispatch(self.idx, w.E, w.shared, self.xq, self.xs, workspace=self.workspace, out=self.disp,
                        stream=stream)
+        # one tile plan for both expert GEMMs (same groups); it lives in the GEMM workspace
+        plan = M.moe_grouped_gemm_plan(self.disp.offsets, self.max_rows, self.gemm_ws, stream=stream)
         mark(4)
         M.moe_grouped_gemm_fp8(self.disp.aq, self.disp.as_, self.disp.offsets, w.w1p or w.w1q, w.w1s,
-                               epilogue=M.MOE_EPI_SWIGLU_QUANT, out=self.hq, out_scales=self.hs,
-                               workspace=self.workspace, stream=stream)
+                               epilogue=M.MOE_EPI_SWIGLU_QUANT, out=self.hq, out_scales=self.hs, plan=plan,
+                               stream=stream)
         mark(5)
         M.moe_grouped_gemm_fp8(self.hq, self.hs, self.disp.offsets, w.w2p or w.w2q, w.w2s, epilogue=M.MOE_EPI_STORE,
-                               out_dtype=self.act, out=self.y, workspace=self.workspace, stream=stream)
+                               out_dtype=self.act, out=self.y, plan=plan, stream=stream)
         mark(6)
         shared_row = self.disp.offsets[w.E:w.E + 1] if w.shared else None
         M.moe_combine(self.y, self.disp.dest_row, self.wts, shared_row, out=self.out, stream=stream)

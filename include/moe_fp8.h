@@ -199,6 +199,29 @@ int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int32_t* offse
                          int32_t tile_rows, void* out, int out_dtype, float* out_scales, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Grouped GEMM in two steps, so that one tile plan serves several GEMMs over the same groups
+ * (the layer's W1 and W2 GEMMs) and the GEMM launch itself is a single kernel.
+ * moe_grouped_gemm_plan writes the list of row tiles of `offsets` (device) into `workspace`
+ * (>= moe_workspace_bytes(MOE_OP_GROUPED_GEMM, max_rows, 0, groups, 0, 0) bytes, caller-owned, and
+ * holding the plan until the last GEMM that uses it has run) and fills `plan` (host) with the tile
+ * height (tile_rows as in moe_grouped_gemm_fp8) and the sizes.  moe_grouped_gemm_fp8_planned then
+ * computes exactly what moe_grouped_gemm_fp8 computes, for the groups, max_rows and tile height of
+ * the plan, with the same `offsets` contents.
+ * Errors: as moe_grouped_gemm_fp8 (MOE_ERR_NULL also for a NULL plan). */
+typedef struct moe_gemm_plan {
+  int32_t tile_rows;   /* chosen row-tile height */
+  int32_t groups;
+  int64_t max_rows;
+  void* workspace;     /* where the tile list lives */
+} moe_gemm_plan;
+
+int moe_grouped_gemm_plan(const int32_t* offsets, int32_t groups, int64_t max_rows, int32_t tile_rows,
+                          void* workspace, size_t workspace_bytes, moe_gemm_plan* plan, void* stream);
+
+int moe_grouped_gemm_fp8_planned(const moe_gemm_plan* plan, const uint8_t* a, const float* as, const int32_t* offsets,
+                                 const uint8_t* b, int32_t b_layout, const float* bs, int32_t N, int32_t K,
+                                 int32_t epilogue, void* out, int out_dtype, float* out_scales, void* stream);
+
 /* Combine (blog sections "Wide EP" / "Parallelism / EP": expert outputs return to token order).
  *   out[t,:] = sum_{j<k, dest_row[t,j] >= 0} topk_w[t,j] * y[dest_row[t,j],:]  (+ y[*shared_first_row + t,:])
  * accumulated in fp32 in slot order, the shared row last, then rounded to out_dtype.

@@ -130,6 +130,31 @@ def test_gemm_validation(L):
     assert L.moe_grouped_gemm_fp8(*g(bl=2)) == ARG                    # unknown weight layout
 
 
+def test_gemm_plan_validation(L):
+    P = ctypes.c_void_p(256)
+    plan = M.GemmPlan()
+    assert L.moe_grouped_gemm_plan(P, 4, 100, 40, P, 1 << 20, ctypes.byref(plan), None) == ARG   # tile height
+    assert L.moe_grouped_gemm_plan(P, 0, 100, 0, P, 1 << 20, ctypes.byref(plan), None) == SHAPE
+    assert L.moe_grouped_gemm_plan(P, 4, 100, 0, P, 8, ctypes.byref(plan), None) == WS
+    assert L.moe_grouped_gemm_plan(P, 4, 100, 0, P, 1 << 20, None, None) == NULL
+    assert L.moe_grouped_gemm_plan(P, 4, 0, 0, None, 0, ctypes.byref(plan), None) == OK          # nothing to plan
+    assert plan.tile_rows == 32 and plan.groups == 4 and plan.max_rows == 0
+    # automatic tile height: the smallest of 32/48/64/128 holding twice the average group
+    for rows, groups, tr in ((100, 8, 32), (1536, 64, 48), (2000, 64, 64), (147456, 257, 128)):
+        L.moe_grouped_gemm_plan(P, groups, rows, 0, None, 0, ctypes.byref(plan), None)
+        assert plan.tile_rows == tr, (rows, groups, plan.tile_rows)
+    planned = lambda N=256, K=256, epi=0, od=1, bl=0, pl=True: (
+        ctypes.byref(plan) if pl else None, P, P, P, P, bl, P, N, K, epi, P, od, None, None)
+    plan.tile_rows, plan.groups, plan.max_rows, plan.workspace = 32, 4, 100, 256
+    assert L.moe_grouped_gemm_fp8_planned(*planned(pl=False)) == NULL
+    assert L.moe_grouped_gemm_fp8_planned(*planned(N=200)) == SHAPE
+    assert L.moe_grouped_gemm_fp8_planned(*planned(od=2)) == DTYPE
+    assert L.moe_grouped_gemm_fp8_planned(*planned(bl=3)) == ARG
+    assert L.moe_grouped_gemm_fp8_planned(*planned(epi=1, od=2)) == NULL   # out_scales missing
+    plan.tile_rows = 40
+    assert L.moe_grouped_gemm_fp8_planned(*planned()) == ARG
+
+
 def test_pack_validation(L):
     P = ctypes.c_void_p(256)
     assert L.moe_pack_weights_fp8(P, 4, 256, 256, 7, P, None) == ARG

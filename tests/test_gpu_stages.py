@@ -376,6 +376,31 @@ def test_grouped_gemm_packed_equals_rowmajor(name, tile):
         _cleanup()
 
 
+@pytest.mark.parametrize("name", ["tiny", "decode", "longctx"])
+def test_grouped_gemm_plan_shared_by_two_gemms(name):
+    """One plan, two GEMMs (SwiGLU over W1, then store over W2), bitwise equal to the one-call path
+    for the automatic and every explicit tile height."""
+    cfg = synth.CONFIGS[name]
+    offsets, a, as_, b1, bs1, N1, K1 = _gemm_case(cfg, "w1", 13)
+    goff = torch.from_numpy(offsets).to(DEV)
+    rows = int(offsets[-1])
+    G = cfg.groups
+    b2 = synth.random_codes((G, K1, N1 // 2), cfg.seed, 60, device=DEV)
+    bs2 = synth.random_scales((G, K1 // 128, N1 // 256), cfg.seed, 61, device=DEV, lo=2.0 ** -10, hi=2.0 ** -6)
+    p1, p2 = M.moe_pack_weights_fp8(b1, M.MOE_EPI_SWIGLU_QUANT), M.moe_pack_weights_fp8(b2, M.MOE_EPI_STORE)
+    ws = torch.empty(M.workspace_bytes(M.MOE_OP_GROUPED_GEMM, rows, 0, G), dtype=torch.uint8, device=DEV)
+    for tile in [0] + TILES:
+        plan = M.moe_grouped_gemm_plan(goff, rows, ws, tile_rows=tile)
+        hq, hs = M.moe_grouped_gemm_fp8(a, as_, goff, p1, bs1, M.MOE_EPI_SWIGLU_QUANT, plan=plan)
+        y = M.moe_grouped_gemm_fp8(hq, hs, goff, p2, bs2, M.MOE_EPI_STORE, torch.bfloat16, plan=plan)
+        hq0, hs0 = M.moe_grouped_gemm_fp8(a, as_, goff, p1, bs1, M.MOE_EPI_SWIGLU_QUANT, tile_rows=plan.tile_rows)
+        y0 = M.moe_grouped_gemm_fp8(hq0, hs0, goff, p2, bs2, M.MOE_EPI_STORE, torch.bfloat16, tile_rows=plan.tile_rows)
+        assert torch.equal(hq[:rows], hq0[:rows]) and torch.equal(hs[:rows], hs0[:rows]), (name, tile)
+        assert torch.equal(y[:rows].view(torch.int16), y0[:rows].view(torch.int16)), (name, tile)
+    del a, as_, b1, b2, p1, p2
+    _cleanup()
+
+
 @pytest.mark.parametrize("name", NAMES)
 @pytest.mark.parametrize("tile", TILES)
 def test_grouped_gemm_swiglu_quant(name, tile):
