@@ -197,8 +197,10 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(dm["bytes"] / dt / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
-    roof["kernel"] = dom
+    kname = stage_kernel(dom, layer)
+    roof["traffic"] = measured_traffic(kname, cfg.name)
+    roof["kernel"] = kname
+    roof["stage"] = dom
 
     if a.copy_probe_mb:
         n = a.copy_probe_mb * (1 << 20)
@@ -239,6 +241,39 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
+
+
+GEMM_SRC = os.path.join(ROOT, "block_scaled_fp8_top_amd", "csrc", "grouped_gemm.hip")
+
+
+def stage_kernel(stage, layer):
+    """The kernel a stage launches (the GEMM stages are one kernel each; the tile plan is part of
+    the dispatch stage)."""
+    import torch
+    if stage == "gemm1_swiglu":
+        return f"grouped_gemm_kernel<{layer.plan.tile_rows}, swiglu_quant, packed>"
+    if stage == "gemm2":
+        out = "bf16" if layer.act == torch.bfloat16 else "f32"
+        return f"grouped_gemm_kernel<{layer.plan.tile_rows}, store_{out}, packed>"
+    return stage
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's readings), or None when they were taken
+    on a different kernel source than the one built here."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(GEMM_SRC, "rb") as f:
+        src = hashlib.sha256(f.read()).hexdigest()
+    for r in rec.get("kernels", []):
+        if r["kernel"] == kernel and r["workload"] == workload and r["source_sha256"] == src:
+            return r["bytes_per_launch"]
+    return None
 
 
 def cpu_baseline(cfg, x, dev):

@@ -108,6 +108,7 @@ class MoELayer:
         self.gemm_ws = torch.empty(M.workspace_bytes(M.MOE_OP_GROUPED_GEMM, self.max_rows, 0, G, 0, 0),
                                    dtype=torch.uint8, device=d)
         self.bad = torch.zeros(1, dtype=torch.int32, device=d)
+        self.plan = None   # tile plan of the last forward's expert GEMMs
 
     def forward(self, x: torch.Tensor, replay: Optional[torch.Tensor] = None, record: Optional[torch.Tensor] = None,
                 stream=None, events=None) -> torch.Tensor:
@@ -137,7 +138,7 @@ class MoELayer:
         M.moe_dispatch(self.idx, w.E, w.shared, self.xq, self.xs, workspace=self.workspace, out=self.disp,
                        stream=stream)
         # one tile plan for both expert GEMMs (same groups); it lives in the GEMM workspace
-        plan = M.moe_grouped_gemm_plan(self.disp.offsets, self.max_rows, self.gemm_ws, stream=stream)
+        plan = self.plan = M.moe_grouped_gemm_plan(self.disp.offsets, self.max_rows, self.gemm_ws, stream=stream)
         mark(4)
         M.moe_grouped_gemm_fp8(self.disp.aq, self.disp.as_, self.disp.offsets, w.w1p or w.w1q, w.w1s,
                                epilogue=M.MOE_EPI_SWIGLU_QUANT, out=self.hq, out_scales=self.hs, plan=plan,
