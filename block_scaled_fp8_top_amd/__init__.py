@@ -27,7 +27,8 @@ MOE_EPI_STORE, MOE_EPI_SWIGLU_QUANT = 0, 1
 MOE_OP_DISPATCH, MOE_OP_GROUPED_GEMM = 1, 2
 MOE_B_ROWMAJOR, MOE_B_PACKED = 0, 1
 
-EXPORTED = ("moe_gate_logits", "moe_route", "moe_replay_route", "moe_router_score_eval", "moe_quant_fp8_block",
+EXPORTED = ("moe_gate_logits", "moe_route", "moe_replay_route", "moe_replay_gate", "moe_router_score_eval",
+            "moe_quant_fp8_block",
             "moe_dispatch", "moe_pack_weights_fp8", "moe_packed_weight_bytes", "moe_grouped_gemm_plan",
             "moe_grouped_gemm_fp8_planned", "moe_grouped_gemm_fp8", "moe_combine", "moe_workspace_bytes",
             "moe_status_str", "moe_version")
@@ -72,6 +73,7 @@ def lib():
         "moe_gate_logits": [P, ctypes.c_int, P, P, I64, I32, I32, P, P],
         "moe_route": [P, I64, cfgp, P, P, P, I64, P],
         "moe_replay_route": [P, I64, cfgp, P, I64, P, P, P, P],
+        "moe_replay_gate": [P, ctypes.c_int, P, P, I64, I32, cfgp, P, I64, P, P, P, P],
         "moe_router_score_eval": [P, I64, ctypes.c_int, P, P],
         "moe_quant_fp8_block": [P, ctypes.c_int, I64, I64, I32, I32, P, P, P],
         "moe_dispatch": [P, I64, I32, I32, I32, P, P, I32, P, P, P, P, P, P, P, SZ, P],
@@ -210,6 +212,31 @@ def moe_replay_route(logits: torch.Tensor, cfg: RouterCfg, replay: torch.Tensor,
     w = torch.empty((T, k), dtype=torch.float32, device=logits.device) if topk_w is None else _dev(topk_w, "topk_w", torch.float32, (T, k))
     _check(lib().moe_replay_route(_p(logits), T, ctypes.byref(cfg), _p(replay), replay.stride(0), _p(idx), _p(w),
                                   _p(bad_count), _stream(stream)), "moe_replay_route")
+    return idx, w
+
+
+def moe_replay_gate(x: torch.Tensor, wg: torch.Tensor, bias: Optional[torch.Tensor], cfg: RouterCfg,
+                    replay: torch.Tensor, bad_count: Optional[torch.Tensor] = None, topk_idx=None, topk_w=None,
+                    stream=None):
+    """Sigmoid routers: replay fused with the gate projection (only the k recorded logits per
+    token).  Same (topk_idx, topk_w) as moe_gate_logits + moe_replay_route, bit for bit."""
+    T, H = x.shape
+    E = wg.shape[0]
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    _dev(wg, "wg", torch.float32, (E, H))
+    if bias is not None:
+        _dev(bias, "bias", torch.float32, (E,))
+    k = cfg.top_k
+    if replay.device.type != "cuda" or replay.dtype != torch.int32 or replay.dim() != 2 or replay.shape[0] != k \
+            or replay.stride(1) != 1 or replay.shape[1] < T:
+        raise ValueError("replay must be a cuda int32 [k, seq_len>=T] view with unit column stride")
+    if bad_count is not None:
+        _dev(bad_count, "bad_count", torch.int32, (1,))
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device) if topk_idx is None else _dev(topk_idx, "topk_idx", torch.int32, (T, k))
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device) if topk_w is None else _dev(topk_w, "topk_w", torch.float32, (T, k))
+    code = MOE_BF16 if x.dtype == torch.bfloat16 else MOE_F32
+    _check(lib().moe_replay_gate(_p(x), code, _p(wg), _p(bias), T, H, ctypes.byref(cfg), _p(replay), replay.stride(0),
+                                 _p(idx), _p(w), _p(bad_count), _stream(stream)), "moe_replay_gate")
     return idx, w
 
 

@@ -229,6 +229,84 @@ __global__ __launch_bounds__(64 * WAVES) void replay_kernel(const float* __restr
   }
 }
 
+// Replay fused with the gate projection, for sigmoid routers: a token's weights depend only on the
+// logits of its k recorded experts, so only those k dot products are computed (k/E of the gate
+// work).  Lane (token, slot) walks its own chain: x[t,h] * wg[e,h] fma'd in ascending h from +0,
+// then + bias[e] -- the chain of the gate projection, so each logit equals that kernel's output
+// bit for bit.  Validation, weights and renormalisation follow the replay kernel.
+template <bool BF16>
+__global__ __launch_bounds__(256) void replay_gate_kernel(const void* __restrict__ xv, const float* __restrict__ wg,
+                                                          const float* __restrict__ bias, int64_t T, int H,
+                                                          moe_router_cfg cfg, const int32_t* __restrict__ replay,
+                                                          int64_t replay_ld, int32_t* __restrict__ topk_idx,
+                                                          float* __restrict__ topk_w, int32_t* __restrict__ bad) {
+  const int E = cfg.num_experts, k = cfg.top_k;
+  const int tpw = 64 / k;   // tokens per wavefront
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int tt = lane / k, j = lane - tt * k;
+  const int64_t t = ((int64_t)blockIdx.x * 4 + wv) * tpw + tt;
+  const bool live = tt < tpw && t < T;
+  const int e = live ? replay[j * replay_ld + t] : 0;
+  bool ok = e >= 0 && e < E;
+  const int base = tt * k;
+  for (int q = 0; q < k; ++q) {
+    const int oe = __shfl(e, (base + q) & 63, 64);
+    if (q < j && oe == e) ok = false;
+  }
+  const uint64_t badm = __ballot(live && !ok);
+  const uint64_t mine = k == 64 ? ~0ull : (((1ull << k) - 1ull) << (base & 63));
+  const bool tok_ok = (badm & mine) == 0;
+  float z = 0.0f;
+  if (live && tok_ok) {
+    const float* wr = wg + (int64_t)e * H;
+    if (BF16) {
+      const uint16_t* xr = reinterpret_cast<const uint16_t*>(xv) + t * H;
+#pragma unroll 4
+      for (int h = 0; h < H; h += 8) {
+        const uint4 u = *reinterpret_cast<const uint4*>(xr + h);
+        const float4 w0 = *reinterpret_cast<const float4*>(wr + h);
+        const float4 w1 = *reinterpret_cast<const float4*>(wr + h + 4);
+        z = __builtin_fmaf(__uint_as_float(u.x << 16), w0.x, z);
+        z = __builtin_fmaf(__uint_as_float(u.x & 0xFFFF0000u), w0.y, z);
+        z = __builtin_fmaf(__uint_as_float(u.y << 16), w0.z, z);
+        z = __builtin_fmaf(__uint_as_float(u.y & 0xFFFF0000u), w0.w, z);
+        z = __builtin_fmaf(__uint_as_float(u.z << 16), w1.x, z);
+        z = __builtin_fmaf(__uint_as_float(u.z & 0xFFFF0000u), w1.y, z);
+        z = __builtin_fmaf(__uint_as_float(u.w << 16), w1.z, z);
+        z = __builtin_fmaf(__uint_as_float(u.w & 0xFFFF0000u), w1.w, z);
+      }
+    } else {
+      const float* xr = reinterpret_cast<const float*>(xv) + t * H;
+#pragma unroll 4
+      for (int h = 0; h < H; h += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(xr + h);
+        const float4 w = *reinterpret_cast<const float4*>(wr + h);
+        z = __builtin_fmaf(a.x, w.x, z);
+        z = __builtin_fmaf(a.y, w.y, z);
+        z = __builtin_fmaf(a.z, w.z, z);
+        z = __builtin_fmaf(a.w, w.w, z);
+      }
+    }
+    if (bias) z = z + bias[e];
+  }
+  const float my_s = live && tok_ok ? router_sigmoid(z) : 0.0f;
+  float w = my_s;
+  if (cfg.renormalize) {
+    float d = 0.0f;
+    for (int q = 0; q < k; ++q) d = d + __shfl(my_s, (base + q) & 63, 64);
+    w = my_s / d;
+  }
+  if (!live) return;
+  if (tok_ok) {
+    topk_idx[t * k + j] = e;
+    topk_w[t * k + j] = w;
+  } else {
+    topk_idx[t * k + j] = -1;
+    topk_w[t * k + j] = 0.0f;
+    if (j == 0 && bad) atomicAdd(bad, 1);
+  }
+}
+
 __global__ __launch_bounds__(256) void score_eval_kernel(const float* __restrict__ x, int64_t n, int score_fn,
                                                         float* __restrict__ y) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -306,6 +384,31 @@ extern "C" int moe_replay_route(const float* logits, int64_t T, const moe_router
   hipStream_t st = as_stream(stream);
   DISPATCH_EPL(c.num_experts, (replay_kernel<EPL><<<grid, 64 * WAVES, 0, st>>>(logits, T, c, replay, replay_ld,
                                                                                 topk_idx, topk_w, bad_count)));
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+extern "C" int moe_replay_gate(const void* x, int x_dtype, const float* wg, const float* bias, int64_t T, int32_t H,
+                               const moe_router_cfg* cfg, const int32_t* replay, int64_t replay_ld, int32_t* topk_idx,
+                               float* topk_w, int32_t* bad_count, void* stream) {
+  const int rc = check_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  if (cfg->score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_ARG;   // softmax weights need every logit
+  if (T < 0 || H < 8 || H % 8 != 0 || T > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (T == 0) return MOE_OK;
+  if (replay_ld < T) return MOE_ERR_ARG;
+  if (!x || !wg || !replay || !topk_idx || !topk_w) return MOE_ERR_NULL;
+  const int tpw = 64 / cfg->top_k;
+  const int64_t grid = ceil_div64(T, 4 * tpw);
+  if (grid > INT32_MAX) return MOE_ERR_SHAPE;
+  hipStream_t st = as_stream(stream);
+  if (x_dtype == MOE_BF16)
+    replay_gate_kernel<true><<<(unsigned)grid, 256, 0, st>>>(x, wg, bias, T, H, *cfg, replay, replay_ld, topk_idx,
+                                                            topk_w, bad_count);
+  else
+    replay_gate_kernel<false><<<(unsigned)grid, 256, 0, st>>>(x, wg, bias, T, H, *cfg, replay, replay_ld, topk_idx,
+                                                             topk_w, bad_count);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

@@ -111,9 +111,11 @@ class MoELayer:
         self.plan = None   # tile plan of the last forward's expert GEMMs
 
     def forward(self, x: torch.Tensor, replay: Optional[torch.Tensor] = None, record: Optional[torch.Tensor] = None,
-                stream=None, events=None) -> torch.Tensor:
+                stream=None, events=None, fused_replay: bool = True) -> torch.Tensor:
         """``events``: optional list of 8 timing events (torch.cuda.Event), recorded on the launch
-        stream before the first stage and after each of the seven stages."""
+        stream before the first stage and after each of the seven stages.  With ``replay`` and a
+        sigmoid router the gate projection and the replay run fused (``fused_replay``), and
+        ``self.logits`` is not written."""
         T = x.shape[0]
         if T != self.T_max:
             raise ValueError(f"layer buffers are sized for T={self.T_max}, got {T}")
@@ -125,9 +127,15 @@ class MoELayer:
                 events[i].record(st)
 
         mark(0)
-        M.moe_gate_logits(x, w.wg, w.bias, out=self.logits, stream=stream)
+        fused = replay is not None and int(w.cfg.score_fn) == M.MOE_SCORE_SIGMOID and fused_replay
+        if not fused:
+            M.moe_gate_logits(x, w.wg, w.bias, out=self.logits, stream=stream)
         mark(1)
-        if replay is not None:
+        if fused:
+            # sigmoid replay: only the k recorded logits per token are needed (logits is not written)
+            M.moe_replay_gate(x, w.wg, w.bias, w.cfg, replay, bad_count=self.bad, topk_idx=self.idx, topk_w=self.wts,
+                              stream=stream)
+        elif replay is not None:
             M.moe_replay_route(self.logits, w.cfg, replay, bad_count=self.bad, topk_idx=self.idx, topk_w=self.wts,
                                stream=stream)
         else:

@@ -120,6 +120,19 @@ int moe_route(const float* logits, int64_t T, const moe_router_cfg* cfg, int32_t
 int moe_replay_route(const float* logits, int64_t T, const moe_router_cfg* cfg, const int32_t* replay,
                      int64_t replay_ld, int32_t* topk_idx, float* topk_w, int32_t* bad_count, void* stream);
 
+/* Router replay fused with the gate projection, for sigmoid routers (blog section "Router replay";
+ * the trainer replays recorded decisions, and with sigmoid scores a token's weights depend only on
+ * the logits of its k recorded experts).  Equivalent, bit for bit, to moe_gate_logits followed by
+ * moe_replay_route, but only the k recorded logits of each token are computed (k/E of the gate
+ * projection's work): each is the same fp32 chain over h ascending from +0, plus bias[e].
+ *   x [T,H] in x_dtype (MOE_F32 or MOE_BF16); wg [E,H] fp32; bias [E] fp32 or NULL;
+ *   replay, replay_ld, topk_idx, topk_w, bad_count as in moe_replay_route.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (H % 8), MOE_ERR_DTYPE, MOE_ERR_ARG (invalid cfg, a softmax cfg,
+ *         replay_ld < T), MOE_ERR_HIP. */
+int moe_replay_gate(const void* x, int x_dtype, const float* wg, const float* bias, int64_t T, int32_t H,
+                    const moe_router_cfg* cfg, const int32_t* replay, int64_t replay_ld, int32_t* topk_idx,
+                    float* topk_w, int32_t* bad_count, void* stream);
+
 /* The router's fixed score function, elementwise, for validating the bit-exact routing contract:
  * y[i] = exp(x[i]) as used in the softmax scores (score_fn MOE_SCORE_SOFTMAX), or
  * y[i] = 1 / (1 + exp(-x[i])) (MOE_SCORE_SIGMOID); exp is the Cody-Waite + degree-6 polynomial fp32

@@ -130,6 +130,19 @@ def test_gemm_validation(L):
     assert L.moe_grouped_gemm_fp8(*g(bl=2)) == ARG                    # unknown weight layout
 
 
+def test_replay_gate_validation(L):
+    P = ctypes.c_void_p(256)
+    sig = M.router_cfg(256, 8, 1, 1, 8, 4, 2)
+    soft = M.router_cfg(64, 6, 0, 0)
+    f = lambda cfg=sig, T=100, H=512, dt=1, ld=100, x=P: (x, dt, P, None, T, H, ctypes.byref(cfg), P, ld, P, P, None, None)
+    assert L.moe_replay_gate(*f(cfg=soft)) == ARG          # softmax weights need every logit
+    assert L.moe_replay_gate(*f(H=100)) == SHAPE
+    assert L.moe_replay_gate(*f(dt=2)) == DTYPE
+    assert L.moe_replay_gate(*f(ld=50)) == ARG
+    assert L.moe_replay_gate(*f(x=None)) == NULL
+    assert L.moe_replay_gate(*f(T=0)) == OK
+
+
 def test_gemm_plan_validation(L):
     P = ctypes.c_void_p(256)
     plan = M.GemmPlan()

@@ -156,6 +156,45 @@ def test_replay(name):
     assert_equal("replay3 w", host(rw3), ow3)
 
 
+@pytest.mark.parametrize("name,renorm,act,k", [("prefill", 1, "bf16", None), ("r3", 1, "bf16", None),
+                                               ("prefill", 0, "f32", None), ("tiny", 1, "f32", 6),
+                                               ("prefill", 1, "bf16", 7)])
+def test_replay_gate_fused(name, renorm, act, k):
+    """Sigmoid replay fused with the gate projection == moe_gate_logits + moe_replay_route, bit for
+    bit, with and without renormalisation, bf16 and fp32 x, a k that does not divide 64, bias, and
+    planted bad entries; and against the oracle's logits + replay on sampled tokens."""
+    cfg = synth.CONFIGS[name]
+    E, H = cfg.E, cfg.H
+    k = k or cfg.k
+    T = min(cfg.T, 8192)
+    gcfg = M.router_cfg(E, k, 1, renorm)
+    ocfg = O.router_cfg(E, k, 1, renorm)
+    x = synth.make_x(cfg, DEV)[:T]
+    x = x.float() if act == "f32" else x.to(torch.bfloat16)
+    wg, b = synth.make_gate(cfg, 0, DEV)
+    bias = synth.randn((E,), cfg.seed, 90, 0, 0, device=DEV) * 0.5
+    rng = np.random.default_rng(cfg.seed + k)
+    pay = np.stack([rng.permutation(E)[:k] for _ in range(T)], 1).astype(np.int32)   # [k, T], distinct per token
+    pay[0, 5] = E
+    pay[k - 1, T // 3] = -1
+    pay[1, T - 1] = pay[0, T - 1]
+    gpay = torch.from_numpy(pay).to(DEV)
+    for bb in (None, bias):
+        bad1 = torch.zeros(1, dtype=torch.int32, device=DEV)
+        bad2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+        z = M.moe_gate_logits(x, wg, bb)
+        ridx, rw = M.moe_replay_route(z, gcfg, gpay, bad_count=bad1)
+        fidx, fw = M.moe_replay_gate(x, wg, bb, gcfg, gpay, bad_count=bad2)
+        assert_equal("fused idx", host(fidx), host(ridx))
+        assert_equal("fused w", host(fw), host(rw))
+        assert int(bad1.item()) == int(bad2.item()) == 3
+        toks = synth.sample_tokens(T, 64, cfg.seed + 5)
+        oz = O.moe_gate_logits(host(x)[toks], host(wg), None if bb is None else host(bb))
+        oidx, ow, _ = O.moe_replay_route(oz, ocfg, np.ascontiguousarray(pay[:, toks]))
+        assert_equal("fused idx vs oracle", rows_host(fidx, toks), oidx)
+        assert_equal("fused w vs oracle", rows_host(fw, toks), ow)
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill"])
 def test_route_ties(name):
     """Logits on a coarse grid: many exact ties, broken toward the lower expert index."""
