@@ -20,9 +20,12 @@
 // straight from global memory into the LDS ring with global_load_lds (no registers in between),
 // issued NSTAGE-1 K steps ahead; each wavefront waits for its own loads with an explicit vmcnt and
 // a bare s_barrier publishes the stage (a __syncthreads fence would drain every load in flight).
-// Rows are stored with a 16-byte-chunk XOR swizzle (chunk c of row r at slot c ^ ((r >> 1) & 7):
-// the 16 rows one MFMA operand read touches then hit 16 distinct bank groups), applied on the
-// global side: lane L of a DMA instruction writes LDS slot L, so it fetches the chunk that belongs
+// LDS holds each 16-row block of a K slice (2 KB) in the order the MFMA operand reads it: lane l
+// of an operand needs row l%16 and K bytes 32(l/16) .. +32, so the block stores every lane's first
+// 16 bytes in lane order (1 KB), then every lane's second 16 bytes.  Both operand reads of a
+// fragment are then 64 consecutive 16-byte words, the conflict-free LDS pattern (row-major rows
+// with any 16-byte XOR swizzle measured 1.5x slower).  The layout is made on the global side:
+// lane L of a DMA instruction writes LDS word L, so it fetches the row and 16 bytes that belong
 // there.  Weights may come pre-packed (moe_pack_weights_fp8): each K step of a 256-row panel is
 // then one contiguous 32 KB block holding exactly that LDS image, and every DMA instruction reads
 // 1 KB of consecutive bytes instead of eight 128-byte row pieces K bytes apart, which keeps HBM
@@ -81,6 +84,12 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
+// DMA instruction i (1 KB of a stage) and lane L: the row of the K slice and the 16-byte chunk of
+// its 128 bytes that land at LDS word 64 i + L (16-row block i/2, operand half i%2)
+__device__ __forceinline__ int dma_row(int i, int L) { return 16 * (i >> 1) + (L & 15); }
+__device__ __forceinline__ int dma_chunk(int i, int L) { return ((L >> 4) << 1) | (i & 1); }
+// A (row-major activations) keeps whole 128-byte rows per DMA instruction: instruction i holds rows
+// 8i .. 8i+7, lane L row 8i + L/8 with its 16-byte chunk L%8 stored at slot (L%8) ^ ((row >> 1) & 7)
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 typedef uint32_t uint32x2 __attribute__((ext_vector_type(2)));
@@ -115,8 +124,8 @@ __device__ __forceinline__ int panel_row(int epi, int nt, int r, int F) {
 
 // ------------------------------------------------------------------------------------------------
 // Packed weights: packed[g][nt][kb] is the 32 KB LDS image of K step kb of panel nt: 16-byte unit
-// u = 64 i + L (DMA instruction i, lane L) holds chunk (L % 8) ^ ((r >> 1) & 7) of virtual row
-// r = 8 i + L / 8.  One thread per 16-byte unit; rows past N (STORE panels) are zero.
+// u = 64 i + L (DMA instruction i, lane L) holds chunk dma_chunk(i, L) of virtual row dma_row(i, L).
+// One thread per 16-byte unit; rows past N (STORE panels) are zero.
 __global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __restrict__ b, int N, int K, int ny, int epi,
                                                            int64_t units, uint8_t* __restrict__ packed) {
   const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -128,8 +137,8 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __rest
   const int64_t gnt = blk / KB;
   const int nt = (int)(gnt % ny);
   const int64_t g = gnt / ny;
-  const int r = (w >> 6) * 8 + ((w & 63) >> 3);
-  const int chunk = (w & 7) ^ ((r >> 1) & 7);
+  const int r = dma_row(w >> 6, w & 63);
+  const int chunk = dma_chunk(w >> 6, w & 63);
   const int n = panel_row(epi, nt, r, N / 2);
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
   if (n < N) v = *reinterpret_cast<const uint4*>(b + ((size_t)g * N + n) * K + (size_t)kb * BK + chunk * 16);
@@ -238,11 +247,10 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   const int wm = wave / WN, wn = wave % WN;
   const size_t gstride = (PACKED ? (size_t)ny * BN : (size_t)N) * K;   // bytes of one group's weights
 
-  // ---- DMA roles.  A slice: instruction i covers rows 8i .. 8i+7; wave w issues instructions
-  // w*A_PW + j (or just w, for slices of fewer than 8 instructions).  B slice: instructions
-  // 4w .. 4w+3.  Lane: row 8i + lane/8, 16-byte chunk lane%8 (swizzled); for packed weights the
-  // lane's 16 bytes sit at 1024 i + 16 lane of the K step's block.
-  const int drow = lane >> 3, dslot = lane & 7;
+  // ---- DMA roles.  A slice: instruction i covers half of the 16-row block i/2; wave w issues
+  // instructions w*A_PW + j (or just w, for slices of fewer than 8 instructions).  B slice:
+  // instructions 4w .. 4w+3.  Lane L fetches chunk dma_chunk(i, L) of row dma_row(i, L); for packed
+  // weights its 16 bytes sit at 1024 i + 16 L of the K step's block.
   const bool has_a = T::A_INSTR >= 8 || wave < T::A_INSTR;
   const int a_i0 = T::A_INSTR >= 8 ? wave * T::A_PW : wave;
   const bool scale_loader = wave >= 8 - T::S_INSTR;   // the last S_INSTR waves bring 64 rows' scales each
@@ -263,16 +271,16 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   do {                                                                                              \
     const Unit un_ = unit_at(me + (I) * G, ny, tiles, offsets, BM);                                 \
     _Pragma("unroll") for (int j_ = 0; j_ < T::A_PW; ++j_) {                                        \
-      const int r_ = (a_i0 + j_) * 8 + drow;                                                        \
-      aoff[j_] = (uint32_t)min(un_.row0 + r_, un_.row_end - 1) * (uint32_t)K + ((dslot ^ ((r_ >> 1) & 7)) << 4); \
+      const int r_ = (a_i0 + j_) * 8 + (lane >> 3);                                                \
+      aoff[j_] = (uint32_t)min(un_.row0 + r_, un_.row_end - 1) * (uint32_t)K + (((lane & 7) ^ ((r_ >> 1) & 7)) << 4); \
     }                                                                                               \
     _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                              \
       if (PACKED) {                                                                                 \
         boff[i_] = (uint32_t)un_.nt * (uint32_t)(BN * K) + (uint32_t)((4 * wave + i_) * 1024 + lane * 16); \
       } else {                                                                                      \
-        const int r_ = (4 * wave + i_) * 8 + drow;                                                  \
+        const int r_ = dma_row(4 * wave + i_, lane);                                                \
         const int n_ = min(panel_row(EPI, un_.nt, r_, F), N - 1);                                   \
-        boff[i_] = (uint32_t)n_ * (uint32_t)K + ((dslot ^ ((r_ >> 1) & 7)) << 4);                   \
+        boff[i_] = (uint32_t)n_ * (uint32_t)K + (dma_chunk(4 * wave + i_, lane) << 4);              \
       }                                                                                             \
     }                                                                                               \
     bg = b + (size_t)un_.g * gstride;                                                               \
@@ -327,21 +335,21 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     for (int j = 0; j < NS; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int lr = lane & 15;         // row within a 16-row operand tile
-  const int kc = (lane >> 4) * 2;   // first of the two 16-byte K chunks this lane supplies
-  // operand fragments of one K step, read from LDS stage ST
+  // operand fragments of one K step, read from LDS stage ST: the 16-row block starting at row R
+  // is 2 KB at 128 R; lane l's 32 bytes are words l and 64 + l of it
   intx8 af[MS], bf[NS];
 #define GEMM_READ(ST)                                                                                   \
   do {                                                                                                  \
     _Pragma("unroll") for (int ms = 0; ms < MS; ++ms) {                                                 \
       const int r_ = wm * WROWS + ms * 16 + lr;                                                         \
-      const intx4 lo_ = *reinterpret_cast<const intx4*>(&a_lds[ST][swz(r_, kc)]);                       \
-      const intx4 hi_ = *reinterpret_cast<const intx4*>(&a_lds[ST][swz(r_, kc + 1)]);                   \
+      const intx4 lo_ = *reinterpret_cast<const intx4*>(&a_lds[ST][swz(r_, (lane >> 4) * 2)]);          \
+      const intx4 hi_ = *reinterpret_cast<const intx4*>(&a_lds[ST][swz(r_, (lane >> 4) * 2 + 1)]);      \
       af[ms] = intx8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};                   \
     }                                                                                                   \
     _Pragma("unroll") for (int ns = 0; ns < NS; ++ns) {                                                 \
-      const int r_ = b_lrow[ns] + lr;                                                                   \
-      const intx4 lo_ = *reinterpret_cast<const intx4*>(&b_lds[ST][swz(r_, kc)]);                       \
-      const intx4 hi_ = *reinterpret_cast<const intx4*>(&b_lds[ST][swz(r_, kc + 1)]);                   \
+      const int o_ = b_lrow[ns] * BK + lane * 16;                                                       \
+      const intx4 lo_ = *reinterpret_cast<const intx4*>(&b_lds[ST][o_]);                                \
+      const intx4 hi_ = *reinterpret_cast<const intx4*>(&b_lds[ST][o_ + 1024]);                         \
       bf[ns] = intx8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};                   \
     }                                                                                                   \
   } while (0)

@@ -367,13 +367,14 @@ def test_grouped_gemm_exact_integers():
 
 def _expected_pack(b: np.ndarray, epi: int) -> np.ndarray:
     """The packed layout written out: block (g, panel, K step) = 2048 units of 16 bytes; unit
-    64 i + L holds chunk (L % 8) ^ ((r >> 1) & 7) of panel row r = 8 i + L / 8."""
+    64 i + L holds 16-byte chunk 2 (L // 16) + i % 2 of panel row r = 16 (i // 2) + L % 16."""
     G, N, K = b.shape
     KB, F = K // 128, N // 2
     ny = N // 256 if epi == M.MOE_EPI_SWIGLU_QUANT else -(-N // 256)
     u = np.arange(2048)
-    r = (u >> 6) * 8 + ((u & 63) >> 3)
-    chunk = (u & 7) ^ ((r >> 1) & 7)
+    i, lane = u >> 6, u & 63
+    r = 16 * (i >> 1) + (lane & 15)
+    chunk = 2 * (lane >> 4) + (i & 1)
     out = np.zeros((G, ny, KB, 2048, 16), np.uint8)
     for nt in range(ny):
         if epi == M.MOE_EPI_SWIGLU_QUANT:
