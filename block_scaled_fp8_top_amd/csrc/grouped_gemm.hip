@@ -20,13 +20,14 @@
 // straight from global memory into the LDS ring with global_load_lds (no registers in between),
 // issued NSTAGE-1 K steps ahead; each wavefront waits for its own loads with an explicit vmcnt and
 // a bare s_barrier publishes the stage (a __syncthreads fence would drain every load in flight).
-// LDS holds each 16-row block of a K slice (2 KB) in the order the MFMA operand reads it: lane l
-// of an operand needs row l%16 and K bytes 32(l/16) .. +32, so the block stores every lane's first
-// 16 bytes in lane order (1 KB), then every lane's second 16 bytes.  Both operand reads of a
-// fragment are then 64 consecutive 16-byte words, the conflict-free LDS pattern (row-major rows
-// with any 16-byte XOR swizzle measured 1.5x slower).  The layout is made on the global side:
-// lane L of a DMA instruction writes LDS word L, so it fetches the row and 16 bytes that belong
-// there.  Weights may come pre-packed (moe_pack_weights_fp8): each K step of a 256-row panel is
+// Packed weights sit in LDS in the order the MFMA operand reads them: lane l of an operand needs
+// row l%16 and K bytes 32(l/16) .. +32, so each 16-row block (2 KB) stores every lane's first 16
+// bytes in lane order, then every lane's second 16 bytes; both reads of a fragment are 64
+// consecutive 16-byte words, the conflict-free pattern, and each DMA instruction copies 1 KB of
+// consecutive packed bytes.  Row-major operands (activations, unpacked weights) are stored as
+// swizzled 128-byte rows instead (swz below), which keeps their global reads to whole cache lines.
+// Either way the layout is made on the global side: lane L of a DMA instruction writes LDS word L,
+// so it fetches the bytes that belong there.  Weights may come pre-packed (moe_pack_weights_fp8): each K step of a 256-row panel is
 // then one contiguous 32 KB block holding exactly that LDS image, and every DMA instruction reads
 // 1 KB of consecutive bytes instead of eight 128-byte row pieces K bytes apart, which keeps HBM
 // streaming near its peak.  Weight scales travel through scalar loads in a ring as deep as the DMA
@@ -88,9 +89,14 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
 // its 128 bytes that land at LDS word 64 i + L (16-row block i/2, operand half i%2)
 __device__ __forceinline__ int dma_row(int i, int L) { return 16 * (i >> 1) + (L & 15); }
 __device__ __forceinline__ int dma_chunk(int i, int L) { return ((L >> 4) << 1) | (i & 1); }
-// A (row-major activations) keeps whole 128-byte rows per DMA instruction: instruction i holds rows
-// 8i .. 8i+7, lane L row 8i + L/8 with its 16-byte chunk L%8 stored at slot (L%8) ^ ((row >> 1) & 7)
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 4); }
+// Row-major operands (activations; weights that are not packed) keep whole 128-byte rows per DMA
+// instruction, which keeps the global reads to one full cache line per 8 lanes: instruction i holds
+// rows 8i .. 8i+7, lane L row 8i + L/8, its 16-byte chunk L%8 stored at slot (L%8) ^ f(row) with
+// f(row) = (row & 7) ^ ((row >> 3) & 1).  Of the XOR swizzles measured on gfx950 for the operand
+// read pattern this one is the fastest (175 B/clk/CU against 180 for linear reads; (row & 7) or
+// ((row >> 1) & 7) alone reach 123).
+__device__ __forceinline__ int swz_mask(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ swz_mask(row)) << 4); }
 
 typedef uint32_t uint32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t uint32x4 __attribute__((ext_vector_type(4)));
@@ -247,10 +253,10 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   const int wm = wave / WN, wn = wave % WN;
   const size_t gstride = (PACKED ? (size_t)ny * BN : (size_t)N) * K;   // bytes of one group's weights
 
-  // ---- DMA roles.  A slice: instruction i covers half of the 16-row block i/2; wave w issues
-  // instructions w*A_PW + j (or just w, for slices of fewer than 8 instructions).  B slice:
-  // instructions 4w .. 4w+3.  Lane L fetches chunk dma_chunk(i, L) of row dma_row(i, L); for packed
-  // weights its 16 bytes sit at 1024 i + 16 L of the K step's block.
+  // ---- DMA roles.  A slice: wave w issues instructions w*A_PW + j (or just w, for slices of fewer
+  // than 8 instructions); B slice: instructions 4w .. 4w+3.  Row-major operands: instruction i
+  // holds rows 8i .. 8i+7, lane L row 8i + L/8 and chunk L%8 (stored at its swizzled slot); packed
+  // weights: lane L's 16 bytes sit at 1024 i + 16 L of the K step's block.
   const bool has_a = T::A_INSTR >= 8 || wave < T::A_INSTR;
   const int a_i0 = T::A_INSTR >= 8 ? wave * T::A_PW : wave;
   const bool scale_loader = wave >= 8 - T::S_INSTR;   // the last S_INSTR waves bring 64 rows' scales each
@@ -272,15 +278,15 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     const Unit un_ = unit_at(me + (I) * G, ny, tiles, offsets, BM);                                 \
     _Pragma("unroll") for (int j_ = 0; j_ < T::A_PW; ++j_) {                                        \
       const int r_ = (a_i0 + j_) * 8 + (lane >> 3);                                                \
-      aoff[j_] = (uint32_t)min(un_.row0 + r_, un_.row_end - 1) * (uint32_t)K + (((lane & 7) ^ ((r_ >> 1) & 7)) << 4); \
+      aoff[j_] = (uint32_t)min(un_.row0 + r_, un_.row_end - 1) * (uint32_t)K + (((lane & 7) ^ swz_mask(r_)) << 4); \
     }                                                                                               \
     _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                              \
       if (PACKED) {                                                                                 \
         boff[i_] = (uint32_t)un_.nt * (uint32_t)(BN * K) + (uint32_t)((4 * wave + i_) * 1024 + lane * 16); \
       } else {                                                                                      \
-        const int r_ = dma_row(4 * wave + i_, lane);                                                \
+        const int r_ = (4 * wave + i_) * 8 + (lane >> 3);                                           \
         const int n_ = min(panel_row(EPI, un_.nt, r_, F), N - 1);                                   \
-        boff[i_] = (uint32_t)n_ * (uint32_t)K + (dma_chunk(4 * wave + i_, lane) << 4);              \
+        boff[i_] = (uint32_t)n_ * (uint32_t)K + (((lane & 7) ^ swz_mask(r_)) << 4);                 \
       }                                                                                             \
     }                                                                                               \
     bg = b + (size_t)un_.g * gstride;                                                               \
@@ -347,9 +353,12 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
       af[ms] = intx8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};                   \
     }                                                                                                   \
     _Pragma("unroll") for (int ns = 0; ns < NS; ++ns) {                                                 \
-      const int o_ = b_lrow[ns] * BK + lane * 16;                                                       \
+      /* packed weights: operand order; row-major weights: swizzled rows */                             \
+      const int r_ = b_lrow[ns] + lr;                                                                   \
+      const int o_ = PACKED ? b_lrow[ns] * BK + lane * 16 : swz(r_, (lane >> 4) * 2);                   \
+      const int o2_ = PACKED ? o_ + 1024 : swz(r_, (lane >> 4) * 2 + 1);                                \
       const intx4 lo_ = *reinterpret_cast<const intx4*>(&b_lds[ST][o_]);                                \
-      const intx4 hi_ = *reinterpret_cast<const intx4*>(&b_lds[ST][o_ + 1024]);                         \
+      const intx4 hi_ = *reinterpret_cast<const intx4*>(&b_lds[ST][o2_]);                               \
       bf[ns] = intx8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};                   \
     }                                                                                                   \
   } while (0)
