@@ -4,7 +4,11 @@
 //
 // One K block of 128 is exactly one v_mfma_f32_16x16x128_f8f6f4 (e4m3 x e4m3, fp32 result), so
 // every MFMA produces a fresh 128-wide partial P that is promoted into the fp32 accumulator with
-// its scale product: acc = fma(P, as * bs, acc).
+// its scale product: acc = fma(P, as * bs, acc).  The weight slice is the instruction's first
+// operand and the activations its second, so a lane's four results are four consecutive output
+// columns of one row: one scale product per lane and tile, and no transpose before the stores.
+// (fp32 VALU work does not overlap with the fp8 MFMAs on gfx950, so every VALU instruction in the
+// K loop costs MFMA time; the loop keeps only the promotion FMAs and scalar address arithmetic.)
 //
 // Workgroup tile: BM rows x BN = 256 (virtual) columns, 8 wavefronts.  Row-tile heights:
 //   BM = 128: waves in a 2 x 4 grid, each 64 x 64 (4 x 4 MFMA tiles of 16 x 16), 3-stage LDS ring
@@ -27,11 +31,11 @@
 // consecutive packed bytes.  Row-major operands (activations, unpacked weights) are stored as
 // swizzled 128-byte rows instead (swz below), which keeps their global reads to whole cache lines.
 // Either way the layout is made on the global side: lane L of a DMA instruction writes LDS word L,
-// so it fetches the bytes that belong there.  Weights may come pre-packed (moe_pack_weights_fp8): each K step of a 256-row panel is
-// then one contiguous 32 KB block holding exactly that LDS image, and every DMA instruction reads
-// 1 KB of consecutive bytes instead of eight 128-byte row pieces K bytes apart, which keeps HBM
-// streaming near its peak.  Weight scales travel through scalar loads in a ring as deep as the DMA
-// lookahead.
+// so it fetches the bytes that belong there.  Weights may come pre-packed
+// (moe_pack_weights_fp8): each K step of a 256-row panel is then one contiguous 32 KB block holding
+// exactly that LDS image, and every DMA instruction reads 1 KB of consecutive bytes instead of
+// eight 128-byte row pieces K bytes apart, which keeps HBM streaming near its peak.  The weight
+// scales of each step travel by DMA too, through a small LDS ring beside the operand ring.
 //
 // Tile order: a one-workgroup kernel turns `offsets` into the list of BM-row tiles (never
 // straddling a group); a unit is one (tile, 256-column panel) pair, logical units run expert by
@@ -75,8 +79,13 @@ struct Tile {
 // Issued through inline assembly so that the compiler's conservative wait insertion (it cannot tell
 // which LDS stage an in-flight DMA targets) does not drain the pipeline; every wait on these loads
 // is explicit.  M0 holds the wave-uniform LDS address and has no other user in these kernels.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(g) : "memory", "m0");
+// dma16s: wave-uniform 64-bit base in SGPRs (so the per-step K advance is scalar work), 32-bit
+// per-lane offset and an immediate offset IMM, which the hardware adds to both the global and the
+// LDS address (lane L's bytes land at lds_addr + IMM + 16 L).
+template <int IMM>
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3" ::"s"(lds_addr), "v"(voff), "s"(base),
+               "i"(IMM) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr), "v"(g) : "memory", "m0");
@@ -100,27 +109,6 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chu
 
 typedef uint32_t uint32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t uint32x4 __attribute__((ext_vector_type(4)));
-
-// 4 x 4 transpose inside each quad of lanes (DPP quad permutations, no LDS): on entry lane q of
-// the quad holds v[i] = M[i][q], on exit v[i] = M[q][i].  Two butterfly steps: across lane pairs
-// q ^ 1 the elements whose index bit 0 differs from q's are exchanged, then across q ^ 2 bit 1.
-__device__ __forceinline__ float dpp_xor1(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float dpp_xor2(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-}
-__device__ __forceinline__ void quad_transpose(float (&v)[4], int q) {
-  float t[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) t[i] = dpp_xor1(v[i ^ 1]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = ((i ^ q) & 1) ? t[i] : v[i];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) t[i] = dpp_xor2(v[i ^ 2]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = ((i ^ q) & 2) ? t[i] : v[i];
-}
 
 // Weight row held by virtual row r (0..255) of panel nt: SwiGLU panels pair gate rows
 // [128 nt, 128 nt + 128) with up rows [F + 128 nt, ...); STORE panels are rows [256 nt, 256 nt + 256).
@@ -309,13 +297,20 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     if (has_a) {                                                                          \
       const uint32_t ao_ = a_dst + (uint32_t)(ST) * A_BYTES;                              \
       _Pragma("unroll") for (int j_ = 0; j_ < T::A_PW; ++j_)                               \
-        dma16(a + (aoff[j_] + ko_), ao_ + 1024 * j_);                                     \
+        dma16s<0>(a + ko_, aoff[j_], ao_ + 1024 * j_);                                    \
     }                                                                                     \
     const uint32_t bo_ = b_dst + (uint32_t)(ST) * B_BYTES;                                \
-    dma16(bg + (boff[0] + kob_), bo_);                                                    \
-    dma16(bg + (boff[1] + kob_), bo_ + 1024);                                             \
-    dma16(bg + (boff[2] + kob_), bo_ + 2048);                                             \
-    dma16(bg + (boff[3] + kob_), bo_ + 3072);                                             \
+    if (PACKED) {                                                                         \
+      dma16s<0>(bg + kob_, boff[0], bo_);                                                 \
+      dma16s<1024>(bg + kob_, boff[0], bo_);                                              \
+      dma16s<2048>(bg + kob_, boff[0], bo_);                                              \
+      dma16s<3072>(bg + kob_, boff[0], bo_);                                              \
+    } else {                                                                              \
+      dma16s<0>(bg + kob_, boff[0], bo_);                                                 \
+      dma16s<0>(bg + kob_, boff[1], bo_ + 1024);                                          \
+      dma16s<0>(bg + kob_, boff[2], bo_ + 2048);                                          \
+      dma16s<0>(bg + kob_, boff[3], bo_ + 3072);                                          \
+    }                                                                                     \
     if (scale_loader) dma4(ssrc + ik, s_dst + (uint32_t)((SV) & 3) * AS_W * 4);           \
     if (bscale_loader) dma4(bsrc + ik, bsc_dst + (uint32_t)((SV) & 3) * 256);             \
     if (++ik == KB) {                                                                     \
@@ -392,7 +387,7 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     const bool wave_active = EPI == 1 ? true : (cu.nt * BN + wn * NS * 16 < N);
     if (wave_active) {
       GEMM_READ(st);
-      const float* srow = &as_lds[s & 3][wm * WROWS + (lane >> 4) * 4];
+      const float* srow = &as_lds[s & 3][wm * WROWS + lr];
       // weight scales of this step: SwiGLU gate columns use the low block and up columns the high
       // one; a STORE wave's 16*NS columns lie in block (wn * NS * 16) / 128 of the panel
       const float sb_lo = bsc_lds[s & 3][EPI == 1 ? 0 : (wn * NS * 16) / 128];
@@ -402,23 +397,18 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
       for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns)
-          p[ms][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[ms], bf[ns], floatx4{0.f, 0.f, 0.f, 0.f},
+          p[ms][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[ns], af[ms], floatx4{0.f, 0.f, 0.f, 0.f},
                                                                        0, 0, 0, 0, 0, 0);
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms) {
-        const floatx4 sa = *reinterpret_cast<const floatx4*>(srow + ms * 16);
-        floatx4 c_lo, c_hi;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          c_lo[i] = sa[i] * sb_lo;
-          c_hi[i] = sa[i] * sb_hi;
-        }
+        const float sa = srow[ms * 16];
+        const float c_lo = sa * sb_lo, c_hi = EPI == 1 ? sa * sb_hi : c_lo;
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
           const bool hi = EPI == 1 && ns >= HS;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            acc[ms][ns][i] = __builtin_fmaf(p[ms][ns][i], hi ? c_hi[i] : c_lo[i], acc[ms][ns][i]);
+            acc[ms][ns][i] = __builtin_fmaf(p[ms][ns][i], hi ? c_hi : c_lo, acc[ms][ns][i]);
         }
       }
     }
@@ -428,14 +418,13 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     recent[D - 1] = 0;
 
     if (++ck < KB) continue;
-    // ---- epilogue of unit ci, then move on.  Each 16 x 16 result tile is transposed within lane
-    // quads (lane 4j+q then holds row 4(lane/16)+q, columns 4j..4j+3) so every lane writes one
-    // contiguous piece per tile; stores go through a buffer resource bounded by the unit's valid
+    // ---- epilogue of unit ci, then move on.  Lane l holds row l%16 and columns 4(l/16) .. +3 of
+    // each 16 x 16 result tile, so every lane writes one contiguous piece per tile; stores go through a buffer resource bounded by the unit's valid
     // rows, so rows past the group end are dropped by the hardware instead of by a branch, and
     // every wave issues a fixed number of stores.
     const int row0 = cu.row0, nrows = cu.row_end - cu.row0;
-    const int q4 = lane & 3, tr = (lane >> 4) * 4 + q4;   // row within a 16-row tile after the transpose
-    const int tc = lr & ~3;                                // first of the lane's 4 columns
+    const int tr = lr;                 // this lane's row within a 16-row tile
+    const int tc = (lane >> 4) * 4;    // first of the lane's 4 consecutive columns
     if (EPI == 0) {
       if (wave_active) {
         constexpr int EB = OUT_BF16 ? 2 : 4;
@@ -447,7 +436,6 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
 #pragma unroll
           for (int ns = 0; ns < NS; ++ns) {
             float v[4] = {acc[ms][ns][0], acc[ms][ns][1], acc[ms][ns][2], acc[ms][ns][3]};
-            quad_transpose(v, q4);
             const int off = ((wm * WROWS + ms * 16 + tr) * N + c0 + ns * 16) * EB;
             if (OUT_BF16) {
               uint32x2 w;
@@ -467,10 +455,10 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
       // h for this lane: rows (ms, i), columns wn*HS*16 + hs*16 + lr (hs < HS) of the 128-wide block
       float h[MS][HS][4];
 #pragma unroll
-      for (int ms = 0; ms < MS; ++ms)
+      for (int ms = 0; ms < MS; ++ms) {
+        float mx = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float mx = 0.0f;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int hs = 0; hs < HS; ++hs) {
             const float gt = acc[ms][hs][i], up = acc[ms][hs + HS][i];
@@ -478,10 +466,10 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
             h[ms][hs][i] = v;
             mx = fmaxf(mx, fabsf(v));
           }
-#pragma unroll
-          for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-          if (lr == 0) red[wm][wn][ms * 16 + (lane >> 4) * 4 + i] = mx;
-        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (lane < 16) red[wm][wn][ms * 16 + lr] = mx;
+      }
       // publish the row maxima (LDS only: a __syncthreads fence would also drain the DMA in flight)
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
@@ -494,7 +482,7 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
       const int f0 = cu.nt * 128 + wn * HS * 16 + tc;
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms) {
-        const int lrow = ms * 16 + tr;   // this lane's row (after the transpose) within the wave's rows
+        const int lrow = ms * 16 + tr;   // this lane's row within the wave's rows
         float amax = red[wm][0][lrow];
 #pragma unroll
         for (int w = 1; w < WN; ++w) amax = fmaxf(amax, red[wm][w][lrow]);
@@ -503,7 +491,6 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
 #pragma unroll
         for (int hs = 0; hs < HS; ++hs) {
           float v[4] = {h[ms][hs][0], h[ms][hs][1], h[ms][hs][2], h[ms][hs][3]};
-          quad_transpose(v, q4);
           const uint32_t codes = e4m3_pack4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
           __builtin_amdgcn_raw_buffer_store_b32(codes, rq, row * F + f0 + hs * 16, 0, 0);
         }
@@ -511,7 +498,7 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
         // the buffer's end, which the hardware drops
         if (wn == 0)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc,
-                                                (lr >> 2) == 0 ? (row * FB + cu.nt) * 4 : 0x7FFFFFF0, 0, 0);
+                                                (lane >> 4) == 0 ? (row * FB + cu.nt) * 4 : 0x7FFFFFF0, 0, 0);
       }
       recent[D - 1] = MS * HS + (wn == 0 ? MS : 0);
     }
