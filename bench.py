@@ -94,6 +94,9 @@ def main():
         sys.exit(1)
     M.lib()  # fail loudly if the HIP library is missing
     dev = "cuda"
+    if a.workload == "payload":
+        payload_bench(a)
+        return
     cfg = synth.CONFIGS[a.workload]
     sf = 0 if cfg.score_fn == "softmax" else 1
     rcfg = M.router_cfg(cfg.E, cfg.k, sf, cfg.renorm, cfg.n_group, cfg.topk_group, cfg.group_score_topk)
@@ -274,6 +277,89 @@ def measured_traffic(kernel, workload):
         if r["kernel"] == kernel and r["workload"] == workload and r["source_sha256"] == src:
             return r["bytes_per_launch"]
     return None
+
+
+PAYLOAD_SHAPE = (60, 8, 131072)   # [num_layers, top_k, seq_len]: a long-context rollout of a 60-layer model
+PAYLOAD_EXPERTS = 256
+
+
+def payload_bench(a):
+    """Router-replay payload codec: pack (int32 -> ceil(log2 E) bits) and unpack on the device, and
+    the pack + copy to pinned host / copy from host + unpack transport, on a synthetic uniform
+    payload resident in HBM.  One JSON line; `value` is the pack kernel's algorithmic GB/s."""
+    import numpy as np
+    import torch
+
+    import block_scaled_fp8_top_amd as M
+
+    L, k, T = PAYLOAD_SHAPE
+    E = PAYLOAD_EXPERTS
+    n = L * k * T
+    g = torch.Generator(device="cuda").manual_seed(11)
+    idx = torch.randint(0, E, (L, k, T), dtype=torch.int32, device="cuda", generator=g)
+    nb = M.payload_bytes(n, E)
+    packed = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    staging = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    back = torch.empty_like(idx)
+    hostbuf = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
+    st = torch.cuda.current_stream()
+
+    def timed(fn, steps):
+        for _ in range(max(a.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(steps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    steps = a.steps
+    t_pack = timed(lambda: M.moe_payload_pack(idx, E, out=packed), steps)
+    t_unpack = timed(lambda: M.moe_payload_unpack(packed, (L, k, T), E, out=back), steps)
+    t_d2h = timed(lambda: M.moe_payload_to_host(idx, E, staging, hostbuf), max(steps // 5, 2))
+    t_h2d = timed(lambda: M.moe_payload_from_host(hostbuf, (L, k, T), E, staging, out=back), max(steps // 5, 2))
+    torch.cuda.synchronize()
+    ok = bool(torch.equal(back, idx))
+    # the raw int32 payload copied to pinned host, for comparison with the packed transport
+    rawhost = torch.empty(n, dtype=torch.int32, pin_memory=True)
+    t_raw = timed(lambda: rawhost.copy_(idx.view(-1), non_blocking=True), max(steps // 5, 2))
+    algo = n * 4 + nb
+    gbs = algo / (t_pack * 1e-3) / 1e9
+
+    # CPU baseline: the oracle's pack on one layer of the payload
+    import oracle.payload as OP
+    sample = idx[0].cpu().numpy()
+    t0 = time.perf_counter()
+    OP.payload_pack(sample, E)
+    dt = time.perf_counter() - t0
+    line = {
+        "metric": "R3 router-replay payload pack, 1 GPU",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": a.warmup,
+        "ms_per_step": round(t_pack, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int32 -> packed bits", "data": "synthetic (seeded uniform expert indices)",
+        "config": {"workload": "payload", "shape": list(PAYLOAD_SHAPE), "experts": E,
+                   "bits": nb * 8 // (((n + 31) // 32) * 32), "int32_bytes": n * 4, "packed_bytes": nb},
+        "round_trip_exact": ok,
+        "stages": {
+            "pack": {"ms": round(t_pack, 4), "GB_s": round(gbs, 1), "bound": "hbm", "frac": round(gbs / 8000, 4)},
+            "unpack": {"ms": round(t_unpack, 4), "GB_s": round(algo / (t_unpack * 1e-3) / 1e9, 1), "bound": "hbm",
+                       "frac": round(algo / (t_unpack * 1e-3) / 1e9 / 8000, 4)},
+            "pack_to_pinned_host": {"ms": round(t_d2h, 4), "payload_GB_s": round(n * 4 / (t_d2h * 1e-3) / 1e9, 1),
+                                    "wire_GB_s": round(nb / (t_d2h * 1e-3) / 1e9, 1)},
+            "pinned_host_to_unpack": {"ms": round(t_h2d, 4), "payload_GB_s": round(n * 4 / (t_h2d * 1e-3) / 1e9, 1)},
+            "raw_int32_to_pinned_host": {"ms": round(t_raw, 4), "payload_GB_s": round(n * 4 / (t_raw * 1e-3) / 1e9, 1)},
+        },
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbs / 8000, 4), "traffic": None, "kernel": "payload_pack_kernel<8>",
+                     "stage": "pack"},
+        "cpu_baseline": {"value": round(sample.size * 4 / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                         "kind": "oracle", "sample": f"one layer ({k} x {T} indices) of the payload",
+                         "seconds": round(dt, 3)},
+    }
+    print(json.dumps(line), flush=True)
 
 
 def cpu_baseline(cfg, x, dev):

@@ -30,8 +30,9 @@ MOE_B_ROWMAJOR, MOE_B_PACKED = 0, 1
 EXPORTED = ("moe_gate_logits", "moe_route", "moe_replay_route", "moe_replay_gate", "moe_router_score_eval",
             "moe_quant_fp8_block",
             "moe_dispatch", "moe_pack_weights_fp8", "moe_packed_weight_bytes", "moe_grouped_gemm_plan",
-            "moe_grouped_gemm_fp8_planned", "moe_grouped_gemm_fp8", "moe_combine", "moe_workspace_bytes",
-            "moe_status_str", "moe_version")
+            "moe_grouped_gemm_fp8_planned", "moe_grouped_gemm_fp8", "moe_combine", "moe_payload_bytes",
+            "moe_payload_pack", "moe_payload_unpack", "moe_payload_to_host", "moe_payload_from_host",
+            "moe_workspace_bytes", "moe_status_str", "moe_version")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -84,6 +85,11 @@ def lib():
         "moe_grouped_gemm_fp8_planned": [ctypes.POINTER(GemmPlan), P, P, P, P, I32, P, I32, I32, I32, P, ctypes.c_int,
                                          P, P],
         "moe_combine": [P, ctypes.c_int, P, P, I64, I32, I32, P, P, ctypes.c_int, P],
+        "moe_payload_bytes": [I64, I32],
+        "moe_payload_pack": [P, I64, I32, P, P, P],
+        "moe_payload_unpack": [P, I64, I32, P, P],
+        "moe_payload_to_host": [P, I64, I32, P, P, P, P],
+        "moe_payload_from_host": [P, I64, I32, P, P, P],
         "moe_workspace_bytes": [ctypes.c_int, I64, I32, I32, I32, I32],
         "moe_status_str": [ctypes.c_int],
         "moe_version": [],
@@ -94,6 +100,7 @@ def lib():
         fn.restype = ctypes.c_int
     L.moe_workspace_bytes.restype = ctypes.c_size_t
     L.moe_packed_weight_bytes.restype = ctypes.c_size_t
+    L.moe_payload_bytes.restype = ctypes.c_size_t
     L.moe_status_str.restype = ctypes.c_char_p
     L.moe_version.restype = ctypes.c_char_p
     _lib = L
@@ -426,6 +433,87 @@ def moe_combine(y: torch.Tensor, dest_row: torch.Tensor, topk_w: torch.Tensor, s
     out = torch.empty((T, H), dtype=od, device=y.device) if out is None else _dev(out, "out", od, (T, H))
     _check(lib().moe_combine(_p(y), _act_code(y), _p(dest_row), _p(topk_w), T, k, H, _p(shared_first_row), _p(out),
                              _act_code(out), _stream(stream)), "moe_combine")
+    return out
+
+
+def payload_bytes(n: int, num_experts: int) -> int:
+    """Bytes of a packed router-replay payload of n indices (0 for an invalid size)."""
+    return int(lib().moe_payload_bytes(n, num_experts))
+
+
+def _payload_out(n: int, num_experts: int, out, device):
+    nb = payload_bytes(n, num_experts)
+    if nb == 0 and n != 0:
+        raise MoeError(MOE_ERR_SHAPE, "moe_payload_bytes")
+    if out is None:
+        return torch.empty(nb, dtype=torch.uint8, device=device)
+    if out.dtype != torch.uint8 or out.numel() < nb or not out.is_contiguous():
+        raise ValueError(f"packed buffer must be contiguous uint8 with >= {nb} bytes")
+    return out
+
+
+def moe_payload_pack(payload: torch.Tensor, num_experts: int, out: Optional[torch.Tensor] = None,
+                     bad_count: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Bit-pack a router-replay payload (any shape of int32 indices, e.g. [num_layers, top_k, seq_len])
+    to ceil(log2 E) bits per index; returns the packed uint8 device buffer."""
+    _dev(payload, "payload", torch.int32)
+    if bad_count is not None:
+        _dev(bad_count, "bad_count", torch.int32, (1,))
+    n = payload.numel()
+    out = _payload_out(n, num_experts, out, payload.device)
+    if out.device.type != "cuda":
+        raise ValueError("packed buffer must be on the GPU")
+    _check(lib().moe_payload_pack(_p(payload), n, num_experts, _p(out), _p(bad_count), _stream(stream)),
+           "moe_payload_pack")
+    return out
+
+
+def moe_payload_unpack(packed: torch.Tensor, shape, num_experts: int, out: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Inverse of moe_payload_pack: int32 indices of the given shape."""
+    _dev(packed, "packed", torch.uint8)
+    n = 1
+    for d in shape:
+        n *= int(d)
+    if packed.numel() < payload_bytes(n, num_experts):
+        raise ValueError("packed buffer smaller than moe_payload_bytes")
+    out = torch.empty(tuple(shape), dtype=torch.int32, device=packed.device) if out is None else \
+        _dev(out, "out", torch.int32, tuple(shape))
+    _check(lib().moe_payload_unpack(_p(packed), n, num_experts, _p(out), _stream(stream)), "moe_payload_unpack")
+    return out
+
+
+def moe_payload_to_host(payload: torch.Tensor, num_experts: int, staging: torch.Tensor, host: torch.Tensor,
+                        bad_count: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Pack on the device into `staging` and copy the packed bytes into `host` (a pinned uint8 CPU
+    tensor) asynchronously on the stream; returns `host`."""
+    _dev(payload, "payload", torch.int32)
+    n = payload.numel()
+    nb = payload_bytes(n, num_experts)
+    _payload_out(n, num_experts, staging, payload.device)
+    if host.device.type != "cpu" or host.dtype != torch.uint8 or host.numel() < nb or not host.is_contiguous():
+        raise ValueError(f"host buffer must be a contiguous uint8 CPU tensor with >= {nb} bytes")
+    _check(lib().moe_payload_to_host(_p(payload), n, num_experts, _p(staging), _p(host), _p(bad_count),
+                                     _stream(stream)), "moe_payload_to_host")
+    return host
+
+
+def moe_payload_from_host(host: torch.Tensor, shape, num_experts: int, staging: torch.Tensor,
+                          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Copy packed bytes from `host` (pinned uint8 CPU tensor) to `staging` and unpack them on the
+    device, asynchronously on the stream."""
+    n = 1
+    for d in shape:
+        n *= int(d)
+    nb = payload_bytes(n, num_experts)
+    if host.device.type != "cpu" or host.dtype != torch.uint8 or host.numel() < nb or not host.is_contiguous():
+        raise ValueError(f"host buffer must be a contiguous uint8 CPU tensor with >= {nb} bytes")
+    _dev(staging, "staging", torch.uint8)
+    _payload_out(n, num_experts, staging, staging.device)
+    out = torch.empty(tuple(shape), dtype=torch.int32, device=staging.device) if out is None else \
+        _dev(out, "out", torch.int32, tuple(shape))
+    _check(lib().moe_payload_from_host(_p(host), n, num_experts, _p(staging), _p(out), _stream(stream)),
+           "moe_payload_from_host")
     return out
 
 

@@ -245,6 +245,38 @@ int moe_grouped_gemm_fp8_planned(const moe_gemm_plan* plan, const uint8_t* a, co
 int moe_combine(const void* y, int y_dtype, const int32_t* dest_row, const float* topk_w, int64_t T, int32_t k,
                 int32_t H, const int32_t* shared_first_row, void* out, int out_dtype, void* stream);
 
+/* Router-replay payload codec (blog section "Router replay": the routing decisions recorded at
+ * inference, a [num_layers, top_k, seq_len] integer payload, reach tens of Gbps and hundreds of GB
+ * and are handled as an opaque tensor by tensor operations only).  The pages fix no storage format;
+ * this one is a lossless fixed-width code.
+ * Format: b = max(1, ceil(log2 E)) bits per index; index i of the flattened payload occupies bits
+ * [i*b, (i+1)*b) of a little-endian bit stream, least significant bit first (stream bit j is bit j%8
+ * of byte j/8), zero-padded to whole groups of 32 indices: moe_payload_bytes(n, E) =
+ * ceil(n/32) * 4 * b bytes (E <= 256: one byte per index, 4x smaller than int32).
+ *   n: indices (any shape, flattened; 0 <= n <= 2^40), E: experts (1 <= E <= 65536).
+ * moe_payload_bytes returns 0 for an invalid (n, E). */
+size_t moe_payload_bytes(int64_t n, int32_t E);
+
+/* Pack n int32 indices (device) into `packed` (device, moe_payload_bytes(n, E) bytes).  Indices
+ * outside [0, E) are not representable: their low b bits are stored and, if bad_count is not NULL,
+ * their number is added to *bad_count (device int32).  idx and packed must be 16-byte aligned.
+ * Errors: MOE_ERR_SHAPE (n, E), MOE_ERR_NULL, MOE_ERR_ARG (alignment), MOE_ERR_HIP. */
+int moe_payload_pack(const int32_t* idx, int64_t n, int32_t E, uint8_t* packed, int32_t* bad_count, void* stream);
+
+/* Unpack n indices from `packed` (device) into idx (device int32).  16-byte alignment as above.
+ * Errors: as moe_payload_pack. */
+int moe_payload_unpack(const uint8_t* packed, int64_t n, int32_t E, int32_t* idx, void* stream);
+
+/* Pack on the device into `staging` (device, moe_payload_bytes(n, E) bytes) and copy the packed
+ * bytes to `host` asynchronously on `stream` (host should be pinned memory, else the copy is not
+ * asynchronous); the host bytes are valid once the stream reaches this point. */
+int moe_payload_to_host(const int32_t* idx, int64_t n, int32_t E, uint8_t* staging, void* host, int32_t* bad_count,
+                        void* stream);
+
+/* Copy packed bytes from `host` into `staging` (device) and unpack them into idx (device int32),
+ * asynchronously on `stream`; host must stay unchanged until the stream reaches this point. */
+int moe_payload_from_host(const void* host, int64_t n, int32_t E, uint8_t* staging, int32_t* idx, void* stream);
+
 /* Workspace bytes needed by moe_dispatch (op MOE_OP_DISPATCH: rows_or_T = T, k, E) or
  * moe_grouped_gemm_fp8 (op MOE_OP_GROUPED_GEMM: rows_or_T = max_rows, E = groups, N, K). */
 size_t moe_workspace_bytes(int op, int64_t rows_or_T, int32_t k, int32_t E, int32_t N, int32_t K);

@@ -186,6 +186,28 @@ def test_packed_weight_bytes(L):
     assert M.packed_weight_bytes(4, 256, 100, M.MOE_EPI_STORE) == 0
 
 
+def test_payload_validation_and_size(L):
+    """Sizes follow the format (the oracle's formula); bad sizes, NULLs and misaligned pointers are
+    rejected on the host."""
+    import oracle.payload as OP
+    for n, E in ((0, 8), (1, 1), (31, 5), (32, 256), (33, 257), (4 * 8 * 32768, 256), (10 ** 9, 1024), (7, 65536)):
+        assert M.payload_bytes(n, E) == OP.payload_bytes(n, E)
+    assert M.payload_bytes(-1, 8) == 0 and M.payload_bytes(5, 0) == 0 and M.payload_bytes(5, 65537) == 0
+    P = ctypes.c_void_p(256)
+    assert L.moe_payload_pack(P, -1, 8, P, None, None) == SHAPE
+    assert L.moe_payload_pack(P, 5, 0, P, None, None) == SHAPE
+    assert L.moe_payload_pack(P, 5, 65537, P, None, None) == SHAPE
+    assert L.moe_payload_pack(None, 5, 8, P, None, None) == NULL
+    assert L.moe_payload_pack(P, 5, 8, None, None, None) == NULL
+    assert L.moe_payload_pack(ctypes.c_void_p(260), 5, 8, P, None, None) == ARG
+    assert L.moe_payload_pack(None, 0, 8, None, None, None) == OK
+    assert L.moe_payload_unpack(P, 5, 8, ctypes.c_void_p(264), None) == ARG
+    assert L.moe_payload_unpack(None, 5, 8, P, None) == NULL
+    assert L.moe_payload_to_host(P, 5, 8, P, None, None, None) == NULL
+    assert L.moe_payload_from_host(None, 5, 8, P, P, None) == NULL
+    assert L.moe_payload_from_host(P, 5, 8, None, P, None) == NULL
+
+
 def test_combine_validation(L):
     P = ctypes.c_void_p(256)
     assert L.moe_combine(P, 1, P, P, 4, 2, 100, None, P, 1, None) == SHAPE

@@ -279,6 +279,25 @@ def test_dispatch_small_and_chunked_paths(T, k, E):
         assert_equal("src_token", host(d.src_token)[:oo[-1]], osrc)
 
 
+@pytest.mark.parametrize("H", [128, 1152, 8192, 8320])
+def test_dispatch_permute_widths(H):
+    """Row permutation at several widths: a row shorter than one wavefront's 16-byte pieces, a
+    partial last round of pieces, 8 KB and a wider row; with a shared expert and dropped slots,
+    every row compared."""
+    T, k, E = 300, 3, 5
+    rng = np.random.default_rng(H)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    idx[rng.random((T, k)) < 0.05] = -1
+    xq = synth.random_codes((T, H), 7, 42, device=DEV)
+    xs = synth.random_scales((T, H // 128), 7, 43, device=DEV)
+    for shared in (False, True):
+        d = M.moe_dispatch(torch.from_numpy(idx).to(DEV), E, shared, xq, xs)
+        _, oo, _, osrc = O.moe_dispatch(idx, E, shared)
+        n = int(oo[-1])
+        assert_equal(f"aq H={H}", host(d.aq)[:n], O.permute_rows(host(xq), osrc))
+        assert_equal(f"as H={H}", host(d.as_)[:n], O.permute_rows(host(xs), osrc))
+
+
 # ----------------------------------------------------------------------------- grouped GEMM
 def _gemm_case(cfg, which, part):
     """Random codes/scales with the workload's group sizes; offsets from the oracle dispatch of

@@ -419,3 +419,52 @@ def test_combine_gather_and_weighted_sum():
     d1 = np.array([[4], [0], [7], [7]], np.int32)
     g = O.moe_combine(y, d1, np.ones((T, 1), np.float32), y_shared=y[:T])
     assert np.array_equal(g, y[d1[:, 0]].astype(np.float64) + y[:T].astype(np.float64))
+
+
+# ----------------------------------------------------------------------------- R3 payload codec
+import oracle.payload as OP  # noqa: E402
+
+
+def _payload_golden():
+    cases = []
+    with open(os.path.join(GOLD, "payload_pack.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            kv = dict(tok.split("=", 1) for tok in line.split())
+            cases.append((int(kv["E"]), [int(v) for v in kv["idx"].split(",")],
+                          [int(v) for v in kv["bytes"].split(",")]))
+    return cases
+
+
+@pytest.mark.parametrize("case", _payload_golden(), ids=lambda c: f"E{c[0]}")
+def test_payload_pack_golden(case):
+    E, idx, expect = case
+    packed, bad = OP.payload_pack(np.array(idx, np.int32), E)
+    assert bad == 0 and packed.tolist() == expect and OP.payload_pack_slow(idx, E) == expect
+    assert len(expect) == OP.payload_bytes(len(idx), E)
+    assert OP.payload_unpack(packed, len(idx), E).tolist() == idx
+
+
+def test_payload_bits_closed_form():
+    for E in list(range(1, 300)) + [1023, 1024, 1025, 65535, 65536]:
+        b = OP.payload_bits(E)
+        assert (1 << b) >= E and (b == 1 or (1 << (b - 1)) < E)
+        assert b == max(1, math.ceil(math.log2(E)))
+
+
+def test_payload_brute_force_and_round_trip():
+    """Random payloads of every width up to 16 bits against the bit-by-bit construction; the 8-bit
+    code of E <= 256 is the plain uint8 array; out-of-range indices are counted."""
+    rng = np.random.default_rng(5)
+    for E in (2, 3, 5, 8, 9, 31, 64, 100, 256, 257, 1000, 4097, 65536):
+        for n in (1, 31, 32, 33, 95):
+            idx = rng.integers(0, E, size=n).astype(np.int32)
+            packed, bad = OP.payload_pack(idx, E)
+            assert bad == 0 and packed.tolist() == OP.payload_pack_slow(idx, E)
+            assert np.array_equal(OP.payload_unpack(packed, n, E), idx)
+            if OP.payload_bits(E) == 8:
+                assert np.array_equal(packed[:n], idx.astype(np.uint8)) and not packed[n:].any()
+    idx = np.array([3, -1, 7, 8, 2], np.int32)
+    _, bad = OP.payload_pack(idx, 8)
+    assert bad == 2
