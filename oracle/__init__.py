@@ -71,7 +71,9 @@ def _load():
         lib.orc_route.argtypes = [P, I64, P, P, P, P, I64]
         lib.orc_replay_route.restype = I64
         lib.orc_replay_route.argtypes = [P, I64, P, P, I64, P, P]
-        lib.orc_quant_block.argtypes = [P, I64, I64, I32, I32, P, P]
+        lib.orc_quant_block.argtypes = [P, I64, I64, I32, I32, I32, P, P]
+        lib.orc_pow2_scale.restype = ctypes.c_float
+        lib.orc_pow2_scale.argtypes = [ctypes.c_float]
         lib.orc_dispatch.argtypes = [P, I64, I32, I32, I32, P, P, P, P]
         lib.orc_permute_rows.argtypes = [P, P, I64, I64, P]
         lib.orc_dequant_act.argtypes = [P, P, I64, I32, P]
@@ -203,8 +205,14 @@ def moe_replay_route(z: np.ndarray, cfg: RouterCfg, replay: np.ndarray):
     return idx, w, int(bad)
 
 
-def moe_quant_fp8_block(x_f32: np.ndarray, block_rows: int):
-    """Block quantisation of x ([rows, cols] or [batch, rows, cols], fp32).
+def pow2_scale(amax: float) -> float:
+    """Power-of-two block scale of a block whose largest magnitude is amax (see the C file)."""
+    return float(_load().orc_pow2_scale(float(amax)))
+
+
+def moe_quant_fp8_block(x_f32: np.ndarray, block_rows: int, pow2: bool = False):
+    """Block quantisation of x ([rows, cols] or [batch, rows, cols], fp32); with pow2 the scales are
+    powers of two (the smallest at or above amax / 448).
     Returns (codes uint8 same shape, scales fp32 [..., rows/block_rows, cols/128])."""
     x = _c(x_f32, np.float32)
     squeeze = x.ndim == 2
@@ -214,7 +222,7 @@ def moe_quant_fp8_block(x_f32: np.ndarray, block_rows: int):
     assert C % 128 == 0 and R % block_rows == 0 and block_rows in (1, 128)
     q = np.empty(x.shape, np.uint8)
     s = np.empty((B, R // block_rows, C // 128), np.float32)
-    _load().orc_quant_block(_ptr(x), B, R, C, block_rows, _ptr(q), _ptr(s))
+    _load().orc_quant_block(_ptr(x), B, R, C, block_rows, 1 if pow2 else 0, _ptr(q), _ptr(s))
     if squeeze:
         return q[0], s[0]
     return q, s

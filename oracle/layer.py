@@ -38,10 +38,10 @@ class ExpertWeights:
     w2s: np.ndarray
 
 
-def quantize_expert(w1: np.ndarray, w2: np.ndarray) -> ExpertWeights:
-    """128x128 block quantisation of one expert's fp32 masters."""
-    w1q, w1s = O.moe_quant_fp8_block(w1, 128)
-    w2q, w2s = O.moe_quant_fp8_block(w2, 128)
+def quantize_expert(w1: np.ndarray, w2: np.ndarray, pow2: bool = False) -> ExpertWeights:
+    """128x128 block quantisation of one expert's fp32 masters (power-of-two scales with pow2)."""
+    w1q, w1s = O.moe_quant_fp8_block(w1, 128, pow2)
+    w2q, w2s = O.moe_quant_fp8_block(w2, 128, pow2)
     return ExpertWeights(w1q, w1s, w2q, w2s)
 
 
@@ -58,6 +58,8 @@ class OracleLayer:
     act: str                             # "f32" or "bf16"
     F: int
     expert: Callable[[int], ExpertWeights]
+    pow2: bool = False                   # power-of-two block scales for activations and h (the
+                                         # expert weights come from ``expert`` as they are)
     _cache: dict = field(default_factory=dict)
 
     def get(self, e: int) -> ExpertWeights:
@@ -94,7 +96,7 @@ def forward_dispatch(layer: OracleLayer, x: np.ndarray, replay=None, record=None
     E, F = layer.E, layer.F
     z = O.moe_gate_logits(x, layer.wg, layer.bias)
     idx, w, bad = route_or_replay(layer, z, replay, record)
-    xq, xs = O.moe_quant_fp8_block(x, 1)
+    xq, xs = O.moe_quant_fp8_block(x, 1, layer.pow2)
     counts, offsets, dest, src = O.moe_dispatch(idx, E, layer.shared)
     aq, as_ = O.permute_rows(xq, src), O.permute_rows(xs, src)
     G = layer.groups
@@ -104,7 +106,7 @@ def forward_dispatch(layer: OracleLayer, x: np.ndarray, replay=None, record=None
     w2s = np.stack([layer.get(g).w2s for g in range(G)])
     g1 = O.moe_grouped_gemm_fp8(aq, as_, offsets, w1q, w1s)
     h = O.swiglu(g1, F)
-    hq, hs = O.moe_quant_fp8_block(h, 1)
+    hq, hs = O.moe_quant_fp8_block(h, 1, layer.pow2)
     y = O.moe_grouped_gemm_fp8(hq, hs, offsets, w2q, w2s)
     y_act = to_act(y, layer.act)
     T = x.shape[0]
@@ -114,11 +116,11 @@ def forward_dispatch(layer: OracleLayer, x: np.ndarray, replay=None, record=None
                 src=src, aq=aq, as_=as_, g1=g1, h=h, hq=hq, hs=hs, y=y, y_act=y_act, out=out)
 
 
-def expert_ffn(ew: ExpertWeights, xq: np.ndarray, xs: np.ndarray, F: int, act: str):
+def expert_ffn(ew: ExpertWeights, xq: np.ndarray, xs: np.ndarray, F: int, act: str, pow2: bool = False):
     """FFN_e on already-quantised activation rows: returns (g1, h, hq, hs, y, y_act)."""
     g1 = O.dequant_act(xq, xs) @ O.dequant_weight(ew.w1q, ew.w1s).T
     h = O.swiglu(g1, F)
-    hq, hs = O.moe_quant_fp8_block(h, 1)
+    hq, hs = O.moe_quant_fp8_block(h, 1, pow2)
     y = O.dequant_act(hq, hs) @ O.dequant_weight(ew.w2q, ew.w2s).T
     return g1, h, hq, hs, y, to_act(y, act)
 
@@ -130,7 +132,7 @@ def forward_token(layer: OracleLayer, x_rows: np.ndarray, replay_rows: Optional[
     E, F = layer.E, layer.F
     z = O.moe_gate_logits(x_rows, layer.wg, layer.bias)
     idx, w, bad = route_or_replay(layer, z, replay_rows)
-    xq, xs = O.moe_quant_fp8_block(x_rows, 1)
+    xq, xs = O.moe_quant_fp8_block(x_rows, 1, layer.pow2)
     n, H = x_rows.shape
     out = np.zeros((n, H), np.float64)
     for t in range(n):
@@ -140,17 +142,17 @@ def forward_token(layer: OracleLayer, x_rows: np.ndarray, replay_rows: Optional[
                 if idx[t, j] >= 0:
                     gate[idx[t, j]] = w[t, j]
             for e in range(E):
-                y_act = expert_ffn(layer.get(e), xq[t:t + 1], xs[t:t + 1], F, layer.act)[5]
+                y_act = expert_ffn(layer.get(e), xq[t:t + 1], xs[t:t + 1], F, layer.act, layer.pow2)[5]
                 out[t] += gate[e] * y_act[0].astype(np.float64)
         else:
             for j in range(idx.shape[1]):
                 e = int(idx[t, j])
                 if e < 0:
                     continue
-                y_act = expert_ffn(layer.get(e), xq[t:t + 1], xs[t:t + 1], F, layer.act)[5]
+                y_act = expert_ffn(layer.get(e), xq[t:t + 1], xs[t:t + 1], F, layer.act, layer.pow2)[5]
                 out[t] += float(w[t, j]) * y_act[0].astype(np.float64)
         if layer.shared:
-            y_act = expert_ffn(layer.get(E), xq[t:t + 1], xs[t:t + 1], F, layer.act)[5]
+            y_act = expert_ffn(layer.get(E), xq[t:t + 1], xs[t:t + 1], F, layer.act, layer.pow2)[5]
             out[t] += y_act[0].astype(np.float64)
     return dict(z=z, idx=idx, w=w, bad=bad, xq=xq, xs=xs, out=out)
 
@@ -192,7 +194,7 @@ def forward_sampled(layer: OracleLayer, x_rows: np.ndarray, replay_rows: Optiona
     E, F = layer.E, layer.F
     z = O.moe_gate_logits(x_rows, layer.wg, layer.bias)
     idx, w, bad = route_or_replay(layer, z, replay_rows)
-    xq, xs = O.moe_quant_fp8_block(x_rows, 1)
+    xq, xs = O.moe_quant_fp8_block(x_rows, 1, layer.pow2)
     n, H = x_rows.shape
     ys = {}
     users = {}
@@ -202,7 +204,7 @@ def forward_sampled(layer: OracleLayer, x_rows: np.ndarray, replay_rows: Optiona
                 users.setdefault(int(idx[t, j]), []).append((t, j))
     for e, lst in users.items():
         rows = np.array([t for t, _ in lst])
-        y_act = expert_ffn(layer.get(e), xq[rows], xs[rows], F, layer.act)[5]
+        y_act = expert_ffn(layer.get(e), xq[rows], xs[rows], F, layer.act, layer.pow2)[5]
         for (t, j), yr in zip(lst, y_act):
             ys[(t, j)] = yr
     out = np.zeros((n, H), np.float64)
@@ -211,6 +213,6 @@ def forward_sampled(layer: OracleLayer, x_rows: np.ndarray, replay_rows: Optiona
             if idx[t, j] >= 0:
                 out[t] += float(w[t, j]) * ys[(t, j)].astype(np.float64)
     if layer.shared:
-        y_act = expert_ffn(layer.get(E), xq, xs, F, layer.act)[5]
+        y_act = expert_ffn(layer.get(E), xq, xs, F, layer.act, layer.pow2)[5]
         out += y_act.astype(np.float64)
     return dict(z=z, idx=idx, w=w, bad=bad, xq=xq, xs=xs, out=out, experts=sorted(users))

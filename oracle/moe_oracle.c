@@ -288,11 +288,26 @@ int64_t orc_replay_route(const float* z, int64_t T, const orc_router_cfg* c, con
 /* ---------------------------------------------------------------------------------------
  * Block quantisation (DeepSeek-V3-style fine-grained scaling): x is [batch][rows][cols] fp32;
  * blocks are block_rows x 128 (1x128 for activations, 128x128 for weights).  Per block:
- * amax = max |x| (exact), s = amax / 448 (IEEE fp32 division; s = 1 for an all-zero block),
- * q = e4m3(x / s) with x / s an IEEE fp32 division.  scales: [batch][rows/block_rows][cols/128].
+ * amax = max |x| (exact), s = amax / 448 (IEEE fp32 division; s = 1 for an all-zero block) or, with
+ * pow2, orc_pow2_scale(amax); q = e4m3(x / s) with x / s an IEEE fp32 division.
+ * scales: [batch][rows/block_rows][cols/128].
  * ------------------------------------------------------------------------------------- */
+/* Power-of-two scale (for the hardware-scaled MFMA, whose E8M0 block scales are powers of two):
+ * the smallest power of two at or above t = amax / 448 (IEEE fp32 division), and at least 2^-127
+ * (the smallest E8M0 value; also the result when t underflows to 0); 1 for an all-zero block.  frexpf writes t = m * 2^e with m in
+ * [0.5, 1): t is itself a power of two exactly when m == 0.5. */
+float orc_pow2_scale(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  float t = amax / 448.0f;
+  int e;
+  float m = frexpf(t, &e);
+  float s = m == 0.5f ? t : m == 0.0f ? 0.0f : ldexpf(1.0f, e);   /* t == 0 when amax/448 underflows */
+  float lo = ldexpf(1.0f, -127);
+  return s < lo ? lo : s;
+}
+
 void orc_quant_block(const float* x, int64_t batch, int64_t rows, int32_t cols, int32_t block_rows,
-                     uint8_t* q, float* scales) {
+                     int32_t pow2, uint8_t* q, float* scales) {
   int64_t rb_n = rows / block_rows, cb_n = cols / 128;
   int64_t nblocks = batch * rb_n * cb_n;
 #pragma omp parallel for schedule(static)
@@ -306,7 +321,7 @@ void orc_quant_block(const float* x, int64_t batch, int64_t rows, int32_t cols, 
         float a = fabsf(base[r * cols + c]);
         if (a > amax) amax = a;
       }
-    float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+    float s = pow2 ? orc_pow2_scale(amax) : (amax == 0.0f ? 1.0f : amax / 448.0f);
     for (int64_t r = rb * block_rows; r < (rb + 1) * block_rows; ++r)
       for (int64_t c = cb * 128; c < cb * 128 + 128; ++c)
         qbase[r * cols + c] = orc_e4m3_encode(base[r * cols + c] / s);

@@ -468,3 +468,54 @@ def test_payload_brute_force_and_round_trip():
     idx = np.array([3, -1, 7, 8, 2], np.int32)
     _, bad = OP.payload_pack(idx, 8)
     assert bad == 2
+
+
+# ----------------------------------------------------------------------------- power-of-two scales
+def _is_pow2_f32(v: np.ndarray) -> np.ndarray:
+    bits = np.asarray(v, np.float32).view(np.uint32)
+    e, m = (bits >> 23) & 0xFF, bits & 0x7FFFFF
+    return np.where(e == 0, (m != 0) & ((m & (m - 1)) == 0), m == 0)
+
+
+def test_pow2_scale_definition():
+    """s is a power of two, s >= t = fl32(amax / 448) and s / 2 < t (unless clamped at 2^-127);
+    amax = 0 gives 1.  Checked on powers of two, their fp32 neighbours, subnormals and a wide sweep."""
+    rng = np.random.default_rng(3)
+    amax = [0.0, 448.0, 449.0, 224.0, 1.0, 2.0 ** -140, 2.0 ** -120, 3.4e38, 1e-45]
+    for k in range(-140, 120, 7):
+        p = np.float32(2.0 ** k)
+        amax += [float(p), float(np.nextafter(p, np.float32(np.inf))), float(np.nextafter(p, np.float32(0)))]
+    amax += list((10.0 ** rng.uniform(-44, 38, 2000)).astype(np.float32).astype(float))
+    lo = np.float32(2.0 ** -127)
+    for a in amax:
+        s = np.float32(O.pow2_scale(a))
+        if a == 0.0:
+            assert s == 1.0
+            continue
+        t = np.float32(a) / np.float32(448.0)
+        assert _is_pow2_f32(s), (a, s)
+        assert s >= t and (s == lo or s / 2 < t), (a, s, t)
+        assert s >= lo
+
+
+def test_quant_pow2_codes_and_range():
+    """Codes equal the library route (torch fp32 division, float8 cast) with the oracle's scales;
+    every scale is a power of two; every non-zero block reaches the upper half of the e4m3 range
+    (amax / s > 224, so its largest code is at least 224: the scale was rounded up to the next power
+    of two, not down, which would saturate)."""
+    x = synth.randn((2, 256, 384), 31, synth.STAGE, part=20).numpy() * np.float32(3.0)
+    x[0, 0, :128] = 0.0
+    x[1, 5, 128:256] *= np.float32(1e-30)
+    for br in (1, 128):
+        q, s = O.moe_quant_fp8_block(x, br, pow2=True)
+        assert _is_pow2_f32(s).all()
+        se = np.repeat(np.repeat(s, br, axis=1), 128, axis=2)
+        lib = (torch.from_numpy(x) / torch.from_numpy(se)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(q, lib)
+        vals = torch.from_numpy(q).view(torch.float8_e4m3fn).float().abs().numpy()
+        bmax = vals.reshape(2, 256 // br, br, 3, 128).max(axis=(2, 4))
+        nz = np.abs(x).reshape(2, 256 // br, br, 3, 128).max(axis=(2, 4)) > 0
+        amax = np.abs(x).reshape(2, 256 // br, br, 3, 128).max(axis=(2, 4))
+        assert (amax[nz] / s[nz] > 224).all() and (amax[nz] / s[nz] <= 448).all()
+        assert (bmax[nz] >= 224).all() and (bmax[~nz] == 0).all()
+        assert np.array_equal(s[~nz], np.ones(int((~nz).sum()), np.float32))
