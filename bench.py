@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
     ap.add_argument("--copies", type=int, default=0,
                     help="layer copies cycled through by consecutive steps (0: enough for 2 GiB of weights, >= 2)")
+    ap.add_argument("--scales", choices=("amax", "pow2"), default="amax",
+                    help="block-scale form: amax/448 fp32 scales (default) or power-of-two scales applied by "
+                         "the matrix cores")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -101,10 +104,11 @@ def main():
     sf = 0 if cfg.score_fn == "softmax" else 1
     rcfg = M.router_cfg(cfg.E, cfg.k, sf, cfg.renorm, cfg.n_group, cfg.topk_group, cfg.group_score_topk)
     wg, b = synth.make_gate(cfg, 0, dev)
+    pow2 = a.scales == "pow2"
     w1q, w1s, w2q, w2s = quantize_expert_weights(cfg.groups, cfg.H, cfg.F,
-                                                 lambda g: synth.make_expert(cfg, g, 0, dev), device=dev)
+                                                 lambda g: synth.make_expert(cfg, g, 0, dev), device=dev, pow2=pow2)
     weights = pack_expert_weights(MoELayerWeights(wg=wg, bias=b, w1q=w1q, w1s=w1s, w2q=w2q, w2s=w2s, cfg=rcfg,
-                                                  shared=cfg.shared), keep_rowmajor=False)
+                                                  shared=cfg.shared, pow2=pow2), keep_rowmajor=False)
     del w1q, w2q
     wbytes = weights.w1p.data.numel() + weights.w2p.data.numel()
     copies = a.copies if a.copies > 0 else max(2, math.ceil((2 << 30) / wbytes))
@@ -215,7 +219,7 @@ def main():
 
     cpu = None
     if not a.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, x, dev)
+        cpu = cpu_baseline(cfg, x, dev, pow2)
 
     tokens_per_s = cfg.T / (ms_per_step * 1e-3)
     line = {
@@ -236,7 +240,8 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
                    "shared_experts": int(cfg.shared), "ffn": cfg.F, "top_k": cfg.k, "score": cfg.score_fn,
                    "rows": model["_rows"], "active_experts": n_active, "layer_copies": copies,
-                   "weight_layout": "packed", "parallelism": "none (1 GPU)"},
+                   "weight_layout": "packed", "block_scales": "power of two" if pow2 else "amax/448 fp32",
+                   "parallelism": "none (1 GPU)"},
         "gemm_tflops": round(gemm_tflops, 2),
         "gemm_frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
         "stages": stages,
@@ -253,11 +258,12 @@ def stage_kernel(stage, layer):
     """The kernel a stage launches (the GEMM stages are one kernel each; the tile plan is part of
     the dispatch stage)."""
     import torch
+    p2 = ", pow2" if layer.w.pow2 else ""
     if stage == "gemm1_swiglu":
-        return f"grouped_gemm_kernel<{layer.plan.tile_rows}, swiglu_quant, packed>"
+        return f"grouped_gemm_kernel<{layer.plan.tile_rows}, swiglu_quant, packed{p2}>"
     if stage == "gemm2":
         out = "bf16" if layer.act == torch.bfloat16 else "f32"
-        return f"grouped_gemm_kernel<{layer.plan.tile_rows}, store_{out}, packed>"
+        return f"grouped_gemm_kernel<{layer.plan.tile_rows}, store_{out}, packed{p2}>"
     return stage
 
 
@@ -362,7 +368,7 @@ def payload_bench(a):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(cfg, x, dev):
+def cpu_baseline(cfg, x, dev, pow2=False):
     """The CPU oracle on a bounded sample of the same workload, timed on this host: the whole
     batch for small layers, else a seeded token sample evaluated per token."""
     import numpy as np
@@ -377,10 +383,10 @@ def cpu_baseline(cfg, x, dev):
 
     def expert(e):
         w1, w2 = synth.make_expert(cfg, e, 0, dev)
-        return L.quantize_expert(w1.cpu().numpy(), w2.cpu().numpy())
+        return L.quantize_expert(w1.cpu().numpy(), w2.cpu().numpy(), pow2)
 
     ol = L.OracleLayer(wg=wg.cpu().numpy(), bias=None if b is None else b.cpu().numpy(), cfg=rc, shared=cfg.shared,
-                       act=cfg.act, F=cfg.F, expert=expert)
+                       act=cfg.act, F=cfg.F, expert=expert, pow2=pow2)
     xh = x.float().cpu().numpy()
     if cfg.T <= 256:
         toks = np.arange(cfg.T)

@@ -26,6 +26,7 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_EPI_STORE, MOE_EPI_SWIGLU_QUANT = 0, 1
 MOE_OP_DISPATCH, MOE_OP_GROUPED_GEMM = 1, 2
 MOE_B_ROWMAJOR, MOE_B_PACKED = 0, 1
+MOE_SCALE_AMAX, MOE_SCALE_POW2 = 0, 1
 
 EXPORTED = ("moe_gate_logits", "moe_route", "moe_replay_route", "moe_replay_gate", "moe_router_score_eval",
             "moe_quant_fp8_block",
@@ -76,14 +77,14 @@ def lib():
         "moe_replay_route": [P, I64, cfgp, P, I64, P, P, P, P],
         "moe_replay_gate": [P, ctypes.c_int, P, P, I64, I32, cfgp, P, I64, P, P, P, P],
         "moe_router_score_eval": [P, I64, ctypes.c_int, P, P],
-        "moe_quant_fp8_block": [P, ctypes.c_int, I64, I64, I32, I32, P, P, P],
+        "moe_quant_fp8_block": [P, ctypes.c_int, I64, I64, I32, I32, I32, P, P, P],
         "moe_dispatch": [P, I64, I32, I32, I32, P, P, I32, P, P, P, P, P, P, P, SZ, P],
         "moe_pack_weights_fp8": [P, I32, I32, I32, I32, P, P],
         "moe_packed_weight_bytes": [I32, I32, I32, I32],
-        "moe_grouped_gemm_fp8": [P, P, P, I32, I64, P, I32, P, I32, I32, I32, I32, P, ctypes.c_int, P, P, SZ, P],
+        "moe_grouped_gemm_fp8": [P, P, P, I32, I64, P, I32, P, I32, I32, I32, I32, I32, P, ctypes.c_int, P, P, SZ, P],
         "moe_grouped_gemm_plan": [P, I32, I64, I32, P, SZ, ctypes.POINTER(GemmPlan), P],
-        "moe_grouped_gemm_fp8_planned": [ctypes.POINTER(GemmPlan), P, P, P, P, I32, P, I32, I32, I32, P, ctypes.c_int,
-                                         P, P],
+        "moe_grouped_gemm_fp8_planned": [ctypes.POINTER(GemmPlan), P, P, P, P, I32, P, I32, I32, I32, I32, P,
+                                         ctypes.c_int, P, P],
         "moe_combine": [P, ctypes.c_int, P, P, I64, I32, I32, P, P, ctypes.c_int, P],
         "moe_payload_bytes": [I64, I32],
         "moe_payload_pack": [P, I64, I32, P, P, P],
@@ -256,8 +257,9 @@ def moe_router_score_eval(x: torch.Tensor, score_fn, out=None, stream=None) -> t
     return out
 
 
-def moe_quant_fp8_block(x: torch.Tensor, block_rows: int, q=None, scales=None, stream=None):
-    """x: [rows, cols] or [batch, rows, cols] fp32/bf16 -> (codes uint8 same shape, scales fp32)."""
+def moe_quant_fp8_block(x: torch.Tensor, block_rows: int, q=None, scales=None, stream=None, pow2: bool = False):
+    """x: [rows, cols] or [batch, rows, cols] fp32/bf16 -> (codes uint8 same shape, scales fp32);
+    pow2: power-of-two scales (the form the GEMM applies in the matrix cores)."""
     _dev(x, "x", (torch.float32, torch.bfloat16))
     xx = x if x.dim() == 3 else x.unsqueeze(0)
     B, R, C = xx.shape
@@ -266,8 +268,9 @@ def moe_quant_fp8_block(x: torch.Tensor, block_rows: int, q=None, scales=None, s
     sshape = (B, R // block_rows, C // 128) if x.dim() == 3 else (R // block_rows, C // 128)
     q = torch.empty(x.shape, dtype=FP8, device=x.device) if q is None else _dev(q, "q", FP8, x.shape)
     scales = torch.empty(sshape, dtype=torch.float32, device=x.device) if scales is None else _dev(scales, "scales", torch.float32, sshape)
-    _check(lib().moe_quant_fp8_block(_p(x), _act_code(x), B, R, C, block_rows, _p(q), _p(scales), _stream(stream)),
-           "moe_quant_fp8_block")
+    mode = MOE_SCALE_POW2 if pow2 else MOE_SCALE_AMAX
+    _check(lib().moe_quant_fp8_block(_p(x), _act_code(x), B, R, C, block_rows, mode, _p(q), _p(scales),
+                                     _stream(stream)), "moe_quant_fp8_block")
     return q, scales
 
 
@@ -363,13 +366,14 @@ def moe_grouped_gemm_plan(offsets: torch.Tensor, max_rows: int, workspace: torch
 def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tensor, b, bs: torch.Tensor,
                          epilogue: int = MOE_EPI_STORE, out_dtype=torch.bfloat16, out=None, out_scales=None,
                          workspace: Optional[torch.Tensor] = None, stream=None, tile_rows: int = 0,
-                         plan: Optional[GemmPlan] = None):
+                         plan: Optional[GemmPlan] = None, pow2: bool = False):
     """a [max_rows,K] uint8, as_ [max_rows,K/128], offsets [G+1] (device), b [G,N,K] uint8 or a
     PackedWeight packed for this epilogue, bs [G,N/128,K/128].
     STORE -> out [max_rows,N] (bf16/fp32); SWIGLU_QUANT -> (h codes [max_rows,N/2] uint8, scales [max_rows,N/256]).
     tile_rows: 32, 48, 64 or 128 rows per workgroup tile, 0 = chosen from the average group size.
     plan: a plan from moe_grouped_gemm_plan for these offsets and max_rows (then no workspace is
-    needed and tile_rows is the plan's)."""
+    needed and tile_rows is the plan's).  pow2: every scale in as_ and bs is a power of two (the
+    matrix cores apply them; the SwiGLU epilogue writes power-of-two scales for h)."""
     max_rows, K = a.shape
     if isinstance(b, PackedWeight):
         if b.epilogue != epilogue:
@@ -406,13 +410,15 @@ def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tens
         out = torch.empty((max_rows, F), dtype=FP8, device=dev) if out is None else _dev(out, "out", FP8, (max_rows, F))
         osc = torch.empty((max_rows, F // 128), dtype=torch.float32, device=dev) if out_scales is None else \
             _dev(out_scales, "out_scales", torch.float32, (max_rows, F // 128))
+    mode = MOE_SCALE_POW2 if pow2 else MOE_SCALE_AMAX
     if plan is not None:
         _check(lib().moe_grouped_gemm_fp8_planned(ctypes.byref(plan), _p(a), _p(as_), _p(offsets), _p(b_t), b_layout,
-                                                  _p(bs), N, K, epilogue, _p(out), code, _p(osc), _stream(stream)),
+                                                  _p(bs), N, K, epilogue, mode, _p(out), code, _p(osc),
+                                                  _stream(stream)),
                "moe_grouped_gemm_fp8_planned")
         return out if epilogue == MOE_EPI_STORE else (out, osc)
     _check(lib().moe_grouped_gemm_fp8(_p(a), _p(as_), _p(offsets), G, max_rows, _p(b_t), b_layout, _p(bs), N, K,
-                                      epilogue, tile_rows, _p(out),
+                                      epilogue, mode, tile_rows, _p(out),
                                       code, _p(osc), _p(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream)), "moe_grouped_gemm_fp8")
     return out if epilogue == MOE_EPI_STORE else (out, osc)

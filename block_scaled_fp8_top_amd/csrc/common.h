@@ -29,6 +29,24 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // ------------------------------------------------------------------------------------------
+// Block scale of a block whose largest magnitude is amax.  Default: amax / 448 (IEEE fp32 division;
+// 1 for an all-zero block).  Power of two (the scale the hardware-scaled MFMA takes as an E8M0
+// exponent): the smallest power of two at or above t = amax / 448, at least 2^-127 (the smallest
+// E8M0 value), 1 for an all-zero block.  From t's bits: a normal t with a zero mantissa is a power
+// of two, otherwise the next one has the exponent field plus one; a subnormal t (or t flushed to 0
+// by the division) rounds up to 2^-127 or 2^-126.
+__device__ __forceinline__ float block_scale(float amax, bool pow2) {
+  if (amax == 0.0f) return 1.0f;
+  const float t = amax / 448.0f;
+  if (!pow2) return t;
+  const uint32_t u = __float_as_uint(t), ex = u >> 23, man = u & 0x7FFFFFu;
+  const uint32_t s = ex == 0 ? (u <= 0x00400000u ? 0x00400000u : 0x00800000u) : (man == 0 ? u : (ex + 1) << 23);
+  return __uint_as_float(s);
+}
+// E8M0 code of a power-of-two scale (its fp32 exponent field; 2^-127, an fp32 subnormal, is code 0)
+__device__ __forceinline__ uint32_t e8m0_code(float pow2_scale) { return (__float_as_uint(pow2_scale) >> 23) & 0xFFu; }
+
+// ------------------------------------------------------------------------------------------
 // OCP FP8 E4M3 encode: round to nearest even, saturating to +-448, sign of zero kept.
 // gfx950's v_cvt_pk_fp8_f32 rounds to nearest even on [-448, 448] but returns NaN beyond 464,
 // so the value is clamped to the largest finite magnitude first (clamping commutes with

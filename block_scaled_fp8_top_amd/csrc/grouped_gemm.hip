@@ -207,7 +207,7 @@ __device__ __forceinline__ Unit unit_at(int u, int ny, const int4* __restrict__ 
 // Persistent workgroups: workgroup w takes units me(w), me(w) + G, me(w) + 2G, ... (G = grid size),
 // and its K steps over all of them form one stream: the DMA lookahead runs into the next unit while
 // the current unit's last steps and epilogue execute, so no unit pays the pipeline fill again.
-template <int BM, int EPI, bool OUT_BF16, bool PACKED>
+template <int BM, int EPI, bool OUT_BF16, bool PACKED, bool POW2>
 __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const int32_t* __restrict__ offsets,
     const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles, int ny, const uint8_t* __restrict__ b,
@@ -392,23 +392,38 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
       // one; a STORE wave's 16*NS columns lie in block (wn * NS * 16) / 128 of the panel
       const float sb_lo = bsc_lds[s & 3][EPI == 1 ? 0 : (wn * NS * 16) / 128];
       const float sb_hi = bsc_lds[s & 3][1];
-      floatx4 p[MS][NS];
+      if (POW2) {
+        // power-of-two scales: the matrix cores apply them (E8M0 exponents; each lane gives the
+        // scale of its operand row for its 32-wide K piece, here the same for the whole 128-wide
+        // step) and accumulate straight into acc - no promotion
+        const uint32_t eb_lo = e8m0_code(sb_lo), eb_hi = e8m0_code(sb_hi);
 #pragma unroll
-      for (int ms = 0; ms < MS; ++ms)
+        for (int ms = 0; ms < MS; ++ms) {
+          const uint32_t ea = e8m0_code(srow[ms * 16]);
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns)
-          p[ms][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[ns], af[ms], floatx4{0.f, 0.f, 0.f, 0.f},
-                                                                       0, 0, 0, 0, 0, 0);
+          for (int ns = 0; ns < NS; ++ns)
+            acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                bf[ns], af[ms], acc[ms][ns], 0, 0, 0, (EPI == 1 && ns >= HS) ? eb_hi : eb_lo, 0, ea);
+        }
+      } else {
+        floatx4 p[MS][NS];
 #pragma unroll
-      for (int ms = 0; ms < MS; ++ms) {
-        const float sa = srow[ms * 16];
-        const float c_lo = sa * sb_lo, c_hi = EPI == 1 ? sa * sb_hi : c_lo;
+        for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns) {
-          const bool hi = EPI == 1 && ns >= HS;
+          for (int ns = 0; ns < NS; ++ns)
+            p[ms][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[ns], af[ms], floatx4{0.f, 0.f, 0.f, 0.f},
+                                                                         0, 0, 0, 0, 0, 0);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[ms][ns][i] = __builtin_fmaf(p[ms][ns][i], hi ? c_hi : c_lo, acc[ms][ns][i]);
+        for (int ms = 0; ms < MS; ++ms) {
+          const float sa = srow[ms * 16];
+          const float c_lo = sa * sb_lo, c_hi = EPI == 1 ? sa * sb_hi : c_lo;
+#pragma unroll
+          for (int ns = 0; ns < NS; ++ns) {
+            const bool hi = EPI == 1 && ns >= HS;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[ms][ns][i] = __builtin_fmaf(p[ms][ns][i], hi ? c_hi : c_lo, acc[ms][ns][i]);
+          }
         }
       }
     }
@@ -486,7 +501,7 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
         float amax = red[wm][0][lrow];
 #pragma unroll
         for (int w = 1; w < WN; ++w) amax = fmaxf(amax, red[wm][w][lrow]);
-        const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+        const float sc = block_scale(amax, POW2);
         const int row = wm * WROWS + lrow;
 #pragma unroll
         for (int hs = 0; hs < HS; ++hs) {
@@ -524,21 +539,33 @@ int auto_tile_rows(int64_t max_rows, int groups) {
   return avg2 <= 32 ? 32 : avg2 <= 48 ? 48 : avg2 <= 64 ? 64 : 128;
 }
 
-template <int BM, bool PACKED>
-void launch(unsigned grid, hipStream_t st, int epilogue, int out_dtype, const uint8_t* a, const float* as,
-            const int32_t* offsets, const int4* tiles, const int32_t* ntiles, int ny, const uint8_t* b, const float* bs,
-            int N, int K, void* out, float* out_scales) {
+template <int BM, bool PACKED, bool POW2>
+void launch3(unsigned grid, hipStream_t st, int epilogue, int out_dtype, const uint8_t* a, const float* as,
+             const int32_t* offsets, const int4* tiles, const int32_t* ntiles, int ny, const uint8_t* b,
+             const float* bs, int N, int K, void* out, float* out_scales) {
   if (epilogue == MOE_EPI_STORE) {
     if (out_dtype == MOE_BF16)
-      grouped_gemm_kernel<BM, 0, true, PACKED><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b, bs, N,
-                                                                          K, out, nullptr);
+      grouped_gemm_kernel<BM, 0, true, PACKED, POW2><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b,
+                                                                                bs, N, K, out, nullptr);
     else
-      grouped_gemm_kernel<BM, 0, false, PACKED><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b, bs, N,
-                                                                           K, out, nullptr);
+      grouped_gemm_kernel<BM, 0, false, PACKED, POW2><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b,
+                                                                                 bs, N, K, out, nullptr);
   } else {
-    grouped_gemm_kernel<BM, 1, false, PACKED><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b, bs, N,
-                                                                         K, out, out_scales);
+    grouped_gemm_kernel<BM, 1, false, PACKED, POW2><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b,
+                                                                               bs, N, K, out, out_scales);
   }
+}
+
+template <int BM, bool PACKED>
+void launch(unsigned grid, hipStream_t st, int epilogue, int scale_mode, int out_dtype, const uint8_t* a,
+            const float* as, const int32_t* offsets, const int4* tiles, const int32_t* ntiles, int ny,
+            const uint8_t* b, const float* bs, int N, int K, void* out, float* out_scales) {
+  if (scale_mode == MOE_SCALE_POW2)
+    launch3<BM, PACKED, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+                              out_scales);
+  else
+    launch3<BM, PACKED, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+                               out_scales);
 }
 
 // compute units of the current device, queried once per device
@@ -588,8 +615,9 @@ extern "C" int moe_pack_weights_fp8(const uint8_t* b, int32_t groups, int32_t N,
 namespace {
 
 // argument checks shared by the one-call and the planned entry points
-int check_gemm_args(int64_t max_rows, int32_t groups, int32_t N, int32_t K, int32_t epilogue, int out_dtype,
-                    int32_t b_layout) {
+int check_gemm_args(int64_t max_rows, int32_t groups, int32_t N, int32_t K, int32_t epilogue, int32_t scale_mode,
+                    int out_dtype, int32_t b_layout) {
+  if (scale_mode != MOE_SCALE_AMAX && scale_mode != MOE_SCALE_POW2) return MOE_ERR_ARG;
   if (groups < 1 || groups > 4096 || max_rows < 0 || max_rows > INT32_MAX - 256) return MOE_ERR_SHAPE;
   if (N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return MOE_ERR_SHAPE;
   if (epilogue == MOE_EPI_STORE) {
@@ -632,13 +660,14 @@ extern "C" int moe_grouped_gemm_plan(const int32_t* offsets, int32_t groups, int
 
 extern "C" int moe_grouped_gemm_fp8_planned(const moe_gemm_plan* plan, const uint8_t* a, const float* as,
                                             const int32_t* offsets, const uint8_t* b, int32_t b_layout,
-                                            const float* bs, int32_t N, int32_t K, int32_t epilogue, void* out,
-                                            int out_dtype, float* out_scales, void* stream) {
+                                            const float* bs, int32_t N, int32_t K, int32_t epilogue,
+                                            int32_t scale_mode, void* out, int out_dtype, float* out_scales,
+                                            void* stream) {
   if (!plan) return MOE_ERR_NULL;
   const int64_t max_rows = plan->max_rows;
   const int32_t groups = plan->groups;
   const int bm = plan->tile_rows;
-  int rc = check_gemm_args(max_rows, groups, N, K, epilogue, out_dtype, b_layout);
+  int rc = check_gemm_args(max_rows, groups, N, K, epilogue, scale_mode, out_dtype, b_layout);
   if (rc != MOE_OK) return rc;
   if (bm != 32 && bm != 48 && bm != 64 && bm != 128) return MOE_ERR_ARG;
   if (max_rows == 0) return MOE_OK;
@@ -658,30 +687,39 @@ extern "C" int moe_grouped_gemm_fp8_planned(const moe_gemm_plan* plan, const uin
   const unsigned grid = (unsigned)std::min<int64_t>(nwg, cus);
   const bool pk = b_layout == MOE_B_PACKED;
   if (bm == 32 && pk)
-    launch<32, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
+    launch<32, true>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+                      out_scales);
   else if (bm == 32)
-    launch<32, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
+    launch<32, false>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+                      out_scales);
   else if (bm == 48 && pk)
-    launch<48, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
+    launch<48, true>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+                      out_scales);
   else if (bm == 48)
-    launch<48, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
+    launch<48, false>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+                      out_scales);
   else if (bm == 64 && pk)
-    launch<64, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
+    launch<64, true>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+                      out_scales);
   else if (bm == 64)
-    launch<64, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
+    launch<64, false>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+                      out_scales);
   else if (pk)
-    launch<128, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
+    launch<128, true>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+                      out_scales);
   else
-    launch<128, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales);
+    launch<128, false>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+                      out_scales);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
 
 extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int32_t* offsets, int32_t groups,
                                     int64_t max_rows, const uint8_t* b, int32_t b_layout, const float* bs, int32_t N,
-                                    int32_t K, int32_t epilogue, int32_t tile_rows, void* out, int out_dtype,
-                                    float* out_scales, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_gemm_args(max_rows, groups, N, K, epilogue, out_dtype, b_layout);
+                                    int32_t K, int32_t epilogue, int32_t scale_mode, int32_t tile_rows, void* out,
+                                    int out_dtype, float* out_scales, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  int rc = check_gemm_args(max_rows, groups, N, K, epilogue, scale_mode, out_dtype, b_layout);
   if (rc != MOE_OK) return rc;
   if (tile_rows != 0 && tile_rows != 32 && tile_rows != 48 && tile_rows != 64 && tile_rows != 128) return MOE_ERR_ARG;
   if (max_rows == 0) return MOE_OK;
@@ -692,6 +730,6 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int
   moe_gemm_plan plan;
   rc = moe_grouped_gemm_plan(offsets, groups, max_rows, tile_rows, workspace, workspace_bytes, &plan, stream);
   if (rc != MOE_OK) return rc;
-  return moe_grouped_gemm_fp8_planned(&plan, a, as, offsets, b, b_layout, bs, N, K, epilogue, out, out_dtype,
-                                      out_scales, stream);
+  return moe_grouped_gemm_fp8_planned(&plan, a, as, offsets, b, b_layout, bs, N, K, epilogue, scale_mode, out,
+                                      out_dtype, out_scales, stream);
 }

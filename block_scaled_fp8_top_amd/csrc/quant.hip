@@ -1,6 +1,7 @@
 // Block-scaled FP8 e4m3 quantisation (1x128 activation blocks, 128x128 weight blocks).
 //
-// Per block: amax = max |x|; s = amax / 448 (IEEE fp32 division; 1 for an all-zero block);
+// Per block: amax = max |x|; s = amax / 448 (IEEE fp32 division; 1 for an all-zero block), or the
+// power-of-two scale of common.h's block_scale;
 // q = e4m3(x / s) with x / s an IEEE fp32 division (hipcc emits correctly rounded fp32 division by
 // default), rounded to nearest even and saturated at 448 by the clamp-then-convert in common.h.
 // HBM-bound: every input byte is read once and every code written once.
@@ -35,7 +36,7 @@ __device__ __forceinline__ uint2 encode8(const float (&v)[8], float s) {
 // 1x128: 16 lanes per block, 8 consecutive values per lane.  Blocks are contiguous in memory
 // (rows are contiguous and cols % 128 == 0), so block b covers x[128 b, 128 b + 128) and its
 // scale is scales[b].
-template <bool BF16>
+template <bool BF16, bool POW2>
 __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict__ x, int64_t nblocks,
                                                           uint8_t* __restrict__ q, float* __restrict__ scales) {
   const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -50,14 +51,14 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict
   for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  const float s = m == 0.0f ? 1.0f : m / 448.0f;
+  const float s = block_scale(m, POW2);
   *reinterpret_cast<uint2*>(q + b * 128 + sub * 8) = encode8(v, s);
   if (sub == 0) scales[b] = s;
 }
 
 // 128x128: one workgroup of 256 threads per block; thread (r16 = tid / 16, c = tid % 16) handles
 // rows r16 + 16 p (p < 8), columns 8c .. 8c+7.
-template <bool BF16>
+template <bool BF16, bool POW2>
 __global__ __launch_bounds__(256) void quant_128x128_kernel(const void* __restrict__ x, int64_t rows, int cols,
                                                             uint8_t* __restrict__ q, float* __restrict__ scales) {
   __shared__ float red[4];
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const void* __restri
   if ((tid & 63) == 0) red[tid / 64] = m;
   __syncthreads();
   m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = m == 0.0f ? 1.0f : m / 448.0f;
+  const float s = block_scale(m, POW2);
 #pragma unroll
   for (int p = 0; p < 8; ++p)
     *reinterpret_cast<uint2*>(q + base + (int64_t)(r16 + 16 * p) * cols) = encode8(v[p], s);
@@ -91,29 +92,28 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const void* __restri
 }  // namespace
 
 extern "C" int moe_quant_fp8_block(const void* x, int x_dtype, int64_t batch, int64_t rows, int32_t cols,
-                                   int32_t block_rows, uint8_t* q, float* scales, void* stream) {
+                                   int32_t block_rows, int32_t scale_mode, uint8_t* q, float* scales, void* stream) {
   if (block_rows != 1 && block_rows != 128) return MOE_ERR_ARG;
+  if (scale_mode != MOE_SCALE_AMAX && scale_mode != MOE_SCALE_POW2) return MOE_ERR_ARG;
   if (batch < 0 || rows < 0 || cols < 0 || cols % 128 != 0 || rows % block_rows != 0) return MOE_ERR_SHAPE;
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
   const int64_t nblocks = batch * (rows / block_rows) * (cols / 128);
   if (nblocks == 0) return MOE_OK;
   if (!x || !q || !scales) return MOE_ERR_NULL;
   hipStream_t st = as_stream(stream);
-  const bool bf16 = x_dtype == MOE_BF16;
+  const bool bf16 = x_dtype == MOE_BF16, pow2 = scale_mode == MOE_SCALE_POW2;
   if (block_rows == 1) {
     const int64_t threads = nblocks * 16;
     const int64_t grid = ceil_div64(threads, 256);
     if (grid > INT32_MAX) return MOE_ERR_SHAPE;
-    if (bf16)
-      quant_1x128_kernel<true><<<(unsigned)grid, 256, 0, st>>>(x, nblocks, q, scales);
-    else
-      quant_1x128_kernel<false><<<(unsigned)grid, 256, 0, st>>>(x, nblocks, q, scales);
+    auto k = bf16 ? (pow2 ? quant_1x128_kernel<true, true> : quant_1x128_kernel<true, false>)
+                  : (pow2 ? quant_1x128_kernel<false, true> : quant_1x128_kernel<false, false>);
+    k<<<(unsigned)grid, 256, 0, st>>>(x, nblocks, q, scales);
   } else {
     if (nblocks > INT32_MAX) return MOE_ERR_SHAPE;
-    if (bf16)
-      quant_128x128_kernel<true><<<(unsigned)nblocks, 256, 0, st>>>(x, rows, cols, q, scales);
-    else
-      quant_128x128_kernel<false><<<(unsigned)nblocks, 256, 0, st>>>(x, rows, cols, q, scales);
+    auto k = bf16 ? (pow2 ? quant_128x128_kernel<true, true> : quant_128x128_kernel<true, false>)
+                  : (pow2 ? quant_128x128_kernel<false, true> : quant_128x128_kernel<false, false>);
+    k<<<(unsigned)nblocks, 256, 0, st>>>(x, rows, cols, q, scales);
   }
   MOE_CHECK_LAUNCH();
   return MOE_OK;

@@ -34,6 +34,8 @@ class MoELayerWeights:
     shared: bool
     w1p: Optional[M.PackedWeight] = None   # w1q packed for the SwiGLU epilogue
     w2p: Optional[M.PackedWeight] = None   # w2q packed for the store epilogue
+    pow2: bool = False                     # power-of-two block scales: the weights were quantised so,
+                                           # and the forward quantises x and h the same way
 
     @property
     def E(self) -> int:
@@ -62,17 +64,18 @@ def pack_expert_weights(weights: MoELayerWeights, keep_rowmajor: bool = True, st
     return replace(weights, w1q=None, w2q=None, w1p=w1p, w2p=w2p)
 
 
-def quantize_expert_weights(groups: int, H: int, F: int, master, device="cuda", stream=None):
+def quantize_expert_weights(groups: int, H: int, F: int, master, device="cuda", stream=None, pow2: bool = False):
     """Allocate the quantised weight tensors and fill expert g from ``master(g) -> (w1 [2F,H], w2 [H,F])``
-    (fp32 or bf16 device tensors), one expert at a time so the fp32 masters never coexist."""
+    (fp32 or bf16 device tensors), one expert at a time so the fp32 masters never coexist; pow2:
+    power-of-two block scales."""
     w1q = torch.empty((groups, 2 * F, H), dtype=torch.uint8, device=device)
     w1s = torch.empty((groups, 2 * F // 128, H // 128), dtype=torch.float32, device=device)
     w2q = torch.empty((groups, H, F), dtype=torch.uint8, device=device)
     w2s = torch.empty((groups, H // 128, F // 128), dtype=torch.float32, device=device)
     for g in range(groups):
         w1, w2 = master(g)
-        M.moe_quant_fp8_block(w1, 128, q=w1q[g], scales=w1s[g], stream=stream)
-        M.moe_quant_fp8_block(w2, 128, q=w2q[g], scales=w2s[g], stream=stream)
+        M.moe_quant_fp8_block(w1, 128, q=w1q[g], scales=w1s[g], stream=stream, pow2=pow2)
+        M.moe_quant_fp8_block(w2, 128, q=w2q[g], scales=w2s[g], stream=stream, pow2=pow2)
     return w1q, w1s, w2q, w2s
 
 
@@ -141,7 +144,7 @@ class MoELayer:
         else:
             M.moe_route(self.logits, w.cfg, record=record, topk_idx=self.idx, topk_w=self.wts, stream=stream)
         mark(2)
-        M.moe_quant_fp8_block(x, 1, q=self.xq, scales=self.xs, stream=stream)
+        M.moe_quant_fp8_block(x, 1, q=self.xq, scales=self.xs, stream=stream, pow2=w.pow2)
         mark(3)
         M.moe_dispatch(self.idx, w.E, w.shared, self.xq, self.xs, workspace=self.workspace, out=self.disp,
                        stream=stream)
@@ -150,10 +153,10 @@ class MoELayer:
         mark(4)
         M.moe_grouped_gemm_fp8(self.disp.aq, self.disp.as_, self.disp.offsets, w.w1p or w.w1q, w.w1s,
                                epilogue=M.MOE_EPI_SWIGLU_QUANT, out=self.hq, out_scales=self.hs, plan=plan,
-                               stream=stream)
+                               stream=stream, pow2=w.pow2)
         mark(5)
         M.moe_grouped_gemm_fp8(self.hq, self.hs, self.disp.offsets, w.w2p or w.w2q, w.w2s, epilogue=M.MOE_EPI_STORE,
-                               out_dtype=self.act, out=self.y, plan=plan, stream=stream)
+                               out_dtype=self.act, out=self.y, plan=plan, stream=stream, pow2=w.pow2)
         mark(6)
         shared_row = self.disp.offsets[w.E:w.E + 1] if w.shared else None
         M.moe_combine(self.y, self.disp.dest_row, self.wts, shared_row, out=self.out, stream=stream)

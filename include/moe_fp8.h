@@ -66,6 +66,10 @@ extern "C" {
 #define MOE_EPI_STORE 0        /* out = A * W^T in out_dtype (bf16 or fp32)                   */
 #define MOE_EPI_SWIGLU_QUANT 1 /* h = silu(gate) * up, then 1x128 FP8 quantisation of h     */
 
+/* block-scale forms (moe_quant_fp8_block, moe_grouped_gemm_fp8) */
+#define MOE_SCALE_AMAX 0       /* s = amax / 448, any positive fp32                            */
+#define MOE_SCALE_POW2 1       /* s a power of two in [2^-127, 2^127] (an E8M0 exponent)       */
+
 /* weight layouts accepted by moe_grouped_gemm_fp8 */
 #define MOE_B_ROWMAJOR 0       /* b [groups, N, K] e4m3, row-major                             */
 #define MOE_B_PACKED 1         /* b rearranged by moe_pack_weights_fp8 for the same epilogue    */
@@ -143,14 +147,16 @@ int moe_router_score_eval(const float* x, int64_t n, int score_fn, float* y, voi
 /* Block-scaled FP8 quantisation (blog section "FP8 training": block-scaled FP8 as in DeepSeek V3).
  * x is [batch, rows, cols] in x_dtype (MOE_F32 or MOE_BF16); blocks are block_rows x 128 with
  * block_rows = 1 (activations) or 128 (weights).  Per block: amax = max |x|; s = amax / 448 (IEEE
- * fp32 division; s = 1 if amax == 0); q = e4m3(x / s), x / s an IEEE fp32 division, rounded to
- * nearest even, magnitudes above 448 saturated to 448, sign of zero kept.
+ * fp32 division; s = 1 if amax == 0) with scale_mode MOE_SCALE_AMAX, or with MOE_SCALE_POW2 the
+ * smallest power of two at or above that quotient, at least 2^-127 (s = 1 if amax == 0), the form
+ * the grouped GEMM applies in the matrix cores; q = e4m3(x / s), x / s an IEEE fp32 division,
+ * rounded to nearest even, magnitudes above 448 saturated to 448, sign of zero kept.
  *   q       [batch, rows, cols] e4m3 bytes (out)
  *   scales  [batch, rows/block_rows, cols/128] fp32 (out)
- * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (cols % 128, rows % block_rows), MOE_ERR_ARG (block_rows),
- *         MOE_ERR_DTYPE, MOE_ERR_HIP. */
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (cols % 128, rows % block_rows), MOE_ERR_ARG (block_rows,
+ *         scale_mode), MOE_ERR_DTYPE, MOE_ERR_HIP. */
 int moe_quant_fp8_block(const void* x, int x_dtype, int64_t batch, int64_t rows, int32_t cols, int32_t block_rows,
-                        uint8_t* q, float* scales, void* stream);
+                        int32_t scale_mode, uint8_t* q, float* scales, void* stream);
 
 /* Dispatch (blog sections "Wide EP" / "Parallelism / EP": tokens are sent to their experts).
  * A stable counting sort of the [T,k] expert ids: group e holds the rows of every (t,j) with
@@ -199,18 +205,25 @@ size_t moe_packed_weight_bytes(int32_t groups, int32_t N, int32_t K, int32_t epi
  *   epilogue MOE_EPI_SWIGLU_QUANT: N = 2F; h[r,f] = silu(acc[r,f]) * acc[r,F+f] in fp32, quantised
  *            1x128 as in moe_quant_fp8_block: out [max_rows, F] e4m3 (out_dtype MOE_FP8_E4M3),
  *            out_scales [max_rows, F/128] fp32
+ *   scale_mode: MOE_SCALE_AMAX (any positive fp32 scales: each 128-wide K block's fp32 partial is
+ *            promoted into the accumulator with the product of its two scales) or MOE_SCALE_POW2
+ *            (every scale in as and bs a power of two in [2^-127, 2^127], as moe_quant_fp8_block
+ *            writes them in that mode: the matrix cores apply them as E8M0 exponents and accumulate
+ *            directly; only the exponent field of each scale is read; the SwiGLU epilogue then
+ *            quantises h with power-of-two scales too)
  *   tile_rows: rows per workgroup tile, 32, 48, 64 or 128, or 0 to choose from the average group size
  *            (the smallest height >= 2 * ceil(max_rows / groups)).  The result is the same for every
  *            height.
  *   Rows beyond offsets[groups] are not written.  workspace >= moe_workspace_bytes(MOE_OP_GROUPED_GEMM,
  *   max_rows, 0, groups, N, K).
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (N, K % 128; F % 128 for SwiGLU; (max_rows+1)*K or one group's
- *         weight bytes at or above 2^32), MOE_ERR_DTYPE, MOE_ERR_ARG (epilogue, tile_rows, b_layout),
+ *         weight bytes at or above 2^32), MOE_ERR_DTYPE, MOE_ERR_ARG (epilogue, scale_mode, tile_rows,
+ *         b_layout),
  *         MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
 int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int32_t* offsets, int32_t groups, int64_t max_rows,
                          const uint8_t* b, int32_t b_layout, const float* bs, int32_t N, int32_t K, int32_t epilogue,
-                         int32_t tile_rows, void* out, int out_dtype, float* out_scales, void* workspace,
-                         size_t workspace_bytes, void* stream);
+                         int32_t scale_mode, int32_t tile_rows, void* out, int out_dtype, float* out_scales,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Grouped GEMM in two steps, so that one tile plan serves several GEMMs over the same groups
  * (the layer's W1 and W2 GEMMs) and the GEMM launch itself is a single kernel.
@@ -233,7 +246,8 @@ int moe_grouped_gemm_plan(const int32_t* offsets, int32_t groups, int64_t max_ro
 
 int moe_grouped_gemm_fp8_planned(const moe_gemm_plan* plan, const uint8_t* a, const float* as, const int32_t* offsets,
                                  const uint8_t* b, int32_t b_layout, const float* bs, int32_t N, int32_t K,
-                                 int32_t epilogue, void* out, int out_dtype, float* out_scales, void* stream);
+                                 int32_t epilogue, int32_t scale_mode, void* out, int out_dtype, float* out_scales,
+                                 void* stream);
 
 /* Combine (blog sections "Wide EP" / "Parallelism / EP": expert outputs return to token order).
  *   out[t,:] = sum_{j<k, dest_row[t,j] >= 0} topk_w[t,j] * y[dest_row[t,j],:]  (+ y[*shared_first_row + t,:])

@@ -25,26 +25,27 @@ def cfgs_for(cfg: synth.LayerConfig):
     return M.router_cfg(*args), O.router_cfg(*args)
 
 
-def gpu_weights(cfg: synth.LayerConfig, layer: int = 0, perturbed: bool = False) -> MoELayerWeights:
+def gpu_weights(cfg: synth.LayerConfig, layer: int = 0, perturbed: bool = False, pow2: bool = False) -> MoELayerWeights:
     wg, b = synth.make_gate(cfg, layer, DEV, perturbed=perturbed)
     w1q, w1s, w2q, w2s = quantize_expert_weights(
-        cfg.groups, cfg.H, cfg.F, lambda g: synth.make_expert(cfg, g, layer, DEV, perturbed=perturbed), device=DEV)
+        cfg.groups, cfg.H, cfg.F, lambda g: synth.make_expert(cfg, g, layer, DEV, perturbed=perturbed), device=DEV,
+        pow2=pow2)
     # the layer streams the packed copies; the row-major codes stay for the weight checks
     return pack_expert_weights(MoELayerWeights(wg=wg, bias=b, w1q=w1q, w1s=w1s, w2q=w2q, w2s=w2s,
-                                               cfg=cfgs_for(cfg)[0], shared=cfg.shared))
+                                               cfg=cfgs_for(cfg)[0], shared=cfg.shared, pow2=pow2))
 
 
-def oracle_layer(cfg: synth.LayerConfig, layer: int = 0, perturbed: bool = False) -> L.OracleLayer:
+def oracle_layer(cfg: synth.LayerConfig, layer: int = 0, perturbed: bool = False, pow2: bool = False) -> L.OracleLayer:
     """Oracle view of the same layer: gate and masters re-drawn from the same GPU streams and
     copied to the host; the oracle quantises each expert it needs."""
     wg, b = synth.make_gate(cfg, layer, DEV, perturbed=perturbed)
 
     def expert(e):
         w1, w2 = synth.make_expert(cfg, e, layer, DEV, perturbed=perturbed)
-        return L.quantize_expert(w1.cpu().numpy(), w2.cpu().numpy())
+        return L.quantize_expert(w1.cpu().numpy(), w2.cpu().numpy(), pow2)
 
     return L.OracleLayer(wg=wg.cpu().numpy(), bias=None if b is None else b.cpu().numpy(), cfg=cfgs_for(cfg)[1],
-                         shared=cfg.shared, act=cfg.act, F=cfg.F, expert=expert)
+                         shared=cfg.shared, act=cfg.act, F=cfg.F, expert=expert, pow2=pow2)
 
 
 def host(t: torch.Tensor) -> np.ndarray:

@@ -92,12 +92,13 @@ def test_gate_logits_validation(L):
 
 
 def test_quant_validation(L):
-    assert L.moe_quant_fp8_block(None, 0, 1, 4, 100, 1, None, None, None) == SHAPE     # cols % 128
-    assert L.moe_quant_fp8_block(None, 0, 1, 100, 128, 128, None, None, None) == SHAPE # rows % 128
-    assert L.moe_quant_fp8_block(None, 0, 1, 128, 128, 64, None, None, None) == ARG
-    assert L.moe_quant_fp8_block(None, 2, 1, 128, 128, 1, None, None, None) == DTYPE
-    assert L.moe_quant_fp8_block(None, 0, 1, 128, 128, 1, None, None, None) == NULL
-    assert L.moe_quant_fp8_block(None, 0, 0, 128, 128, 1, None, None, None) == OK
+    assert L.moe_quant_fp8_block(None, 0, 1, 4, 100, 1, 0, None, None, None) == SHAPE     # cols % 128
+    assert L.moe_quant_fp8_block(None, 0, 1, 100, 128, 128, 0, None, None, None) == SHAPE # rows % 128
+    assert L.moe_quant_fp8_block(None, 0, 1, 128, 128, 64, 0, None, None, None) == ARG
+    assert L.moe_quant_fp8_block(None, 0, 1, 128, 128, 1, 2, None, None, None) == ARG     # scale mode
+    assert L.moe_quant_fp8_block(None, 2, 1, 128, 128, 1, 0, None, None, None) == DTYPE
+    assert L.moe_quant_fp8_block(None, 0, 1, 128, 128, 1, 1, None, None, None) == NULL
+    assert L.moe_quant_fp8_block(None, 0, 0, 128, 128, 1, 1, None, None, None) == OK
 
 
 def test_dispatch_validation(L):
@@ -113,8 +114,8 @@ def test_dispatch_validation(L):
 
 def test_gemm_validation(L):
     P = ctypes.c_void_p(256)
-    g = lambda N=256, K=256, epi=0, od=1, ws=P, wsb=1 << 20, osc=None, groups=4, tr=0, rows=100, bl=0: (
-        P, P, P, groups, rows, P, bl, P, N, K, epi, tr, P, od, osc, ws, wsb, None)
+    g = lambda N=256, K=256, epi=0, od=1, ws=P, wsb=1 << 20, osc=None, groups=4, tr=0, rows=100, bl=0, sm=0: (
+        P, P, P, groups, rows, P, bl, P, N, K, epi, sm, tr, P, od, osc, ws, wsb, None)
     assert L.moe_grouped_gemm_fp8(*g(N=200)) == SHAPE
     assert L.moe_grouped_gemm_fp8(*g(K=100)) == SHAPE
     assert L.moe_grouped_gemm_fp8(*g(od=2)) == DTYPE
@@ -128,6 +129,8 @@ def test_gemm_validation(L):
     assert L.moe_grouped_gemm_fp8(*g(rows=1 << 20, K=4096)) == SHAPE   # 2^32 bytes of activations
     assert L.moe_grouped_gemm_fp8(*g(N=1 << 17, K=1 << 15)) == SHAPE   # 2^32 bytes of one group's weights
     assert L.moe_grouped_gemm_fp8(*g(bl=2)) == ARG                    # unknown weight layout
+    assert L.moe_grouped_gemm_fp8(*g(sm=2)) == ARG                    # unknown scale mode
+    assert L.moe_grouped_gemm_fp8(*g(sm=1, wsb=8)) == WS
 
 
 def test_replay_gate_validation(L):
@@ -156,13 +159,14 @@ def test_gemm_plan_validation(L):
     for rows, groups, tr in ((100, 8, 32), (1536, 64, 48), (2000, 64, 64), (147456, 257, 128)):
         L.moe_grouped_gemm_plan(P, groups, rows, 0, None, 0, ctypes.byref(plan), None)
         assert plan.tile_rows == tr, (rows, groups, plan.tile_rows)
-    planned = lambda N=256, K=256, epi=0, od=1, bl=0, pl=True: (
-        ctypes.byref(plan) if pl else None, P, P, P, P, bl, P, N, K, epi, P, od, None, None)
+    planned = lambda N=256, K=256, epi=0, od=1, bl=0, pl=True, sm=0: (
+        ctypes.byref(plan) if pl else None, P, P, P, P, bl, P, N, K, epi, sm, P, od, None, None)
     plan.tile_rows, plan.groups, plan.max_rows, plan.workspace = 32, 4, 100, 256
     assert L.moe_grouped_gemm_fp8_planned(*planned(pl=False)) == NULL
     assert L.moe_grouped_gemm_fp8_planned(*planned(N=200)) == SHAPE
     assert L.moe_grouped_gemm_fp8_planned(*planned(od=2)) == DTYPE
     assert L.moe_grouped_gemm_fp8_planned(*planned(bl=3)) == ARG
+    assert L.moe_grouped_gemm_fp8_planned(*planned(sm=5)) == ARG
     assert L.moe_grouped_gemm_fp8_planned(*planned(epi=1, od=2)) == NULL   # out_scales missing
     plan.tile_rows = 40
     assert L.moe_grouped_gemm_fp8_planned(*planned()) == ARG
