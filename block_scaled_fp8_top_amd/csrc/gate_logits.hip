@@ -2,8 +2,9 @@
 //
 // The chain order is part of the contract (it makes routing reproducible bit for bit), so the
 // contraction cannot use matrix cores or split K: it is fp32 VALU work.  Each thread owns a
-// TT x TE register tile of outputs and walks h in order; x and Wg are staged through LDS in
-// chunks of HC columns (x converted to fp32 on the way), padded so that the 16-byte LDS reads of
+// TT x TE register tile of outputs and walks h in order; x and Wg are staged through two LDS
+// buffers in chunks of HC columns (x converted to fp32 on the way; the next chunk's global loads
+// are in flight during the current chunk's chain), padded so that the 16-byte LDS reads of
 // different rows fall in different banks.
 #include "common.h"
 
@@ -18,8 +19,11 @@ __global__ __launch_bounds__(NT) void gate_logits_kernel(const void* __restrict_
                                                          const float* __restrict__ bias, int64_t T, int H, int E,
                                                          float* __restrict__ z) {
   constexpr int BT = 16 * TT, BE = 16 * TE;
-  __shared__ __attribute__((aligned(16))) float xs[BT * PAD];
-  __shared__ __attribute__((aligned(16))) float ws[BE * PAD];
+  constexpr int XI = BT * (HC / 8), WI = BE * (HC / 8);   // 8-column staging items per chunk
+  constexpr int XPT = (XI + NT - 1) / NT, WPT = (WI + NT - 1) / NT;
+  // two LDS buffers: chunk c is read from buffer c & 1 while chunk c + 1 is written to the other
+  __shared__ __attribute__((aligned(16))) float xs[2][BT * PAD];
+  __shared__ __attribute__((aligned(16))) float ws[2][BE * PAD];
   const int tid = threadIdx.x;
   const int tx = tid % 16, ty = tid / 16;
   const int64_t t0 = (int64_t)blockIdx.x * BT;
@@ -31,57 +35,83 @@ __global__ __launch_bounds__(NT) void gate_logits_kernel(const void* __restrict_
 #pragma unroll
     for (int j = 0; j < TE; ++j) acc[i][j] = 0.0f;
 
-  for (int h0 = 0; h0 < H; h0 += HC) {
-    const int hc = min(HC, H - h0);  // multiple of 8
-    // ---- stage x[t0 .. t0+BT) x [h0 .. h0+HC) as fp32, 8 values per item
-    for (int it = tid; it < BT * (HC / 8); it += NT) {
+  // this thread's staging items of one chunk, held in registers between the global loads (issued
+  // before the previous chunk's chain) and the LDS stores (after it)
+  uint4 rxb[XPT];          // bf16 x: 8 values
+  float4 rxf[XPT][2];      // fp32 x
+  float4 rw[WPT][2];
+  auto load = [&](int h0) {
+    const int hc = min(HC, H - h0);
+#pragma unroll
+    for (int q = 0; q < XPT; ++q) {
+      const int it = tid + q * NT;
       const int r = it / (HC / 8), c8 = (it % (HC / 8)) * 8;
       const int64_t t = t0 + r;
-      float v[8];
-      if (t < T && c8 < hc) {
-        if (BF16) {
-          const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(xv) + t * H + h0 + c8);
-          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v[2 * q] = __uint_as_float(w4[q] << 16);
-            v[2 * q + 1] = __uint_as_float(w4[q] & 0xFFFF0000u);
-          }
-        } else {
-          const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(xv) + t * H + h0 + c8);
-          const float4 a = p[0], b = p[1];
-          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-        }
+      const bool ok = it < XI && t < T && c8 < hc;
+      if (BF16) {
+        rxb[q] = ok ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(xv) + t * H + h0 + c8)
+                    : make_uint4(0u, 0u, 0u, 0u);
       } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = 0.0f;
+        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(xv) + t * H + h0 + c8);
+        rxf[q][0] = ok ? p[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+        rxf[q][1] = ok ? p[1] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
-      float4* d = reinterpret_cast<float4*>(&xs[r * PAD + c8]);
-      d[0] = make_float4(v[0], v[1], v[2], v[3]);
-      d[1] = make_float4(v[4], v[5], v[6], v[7]);
     }
-    // ---- stage Wg[e0 .. e0+BE) x [h0 .. h0+HC)
-    for (int it = tid; it < BE * (HC / 8); it += NT) {
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+      const int it = tid + q * NT;
       const int r = it / (HC / 8), c8 = (it % (HC / 8)) * 8;
       const int e = e0 + r;
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-      if (e < E && c8 < hc) {
-        const float4* p = reinterpret_cast<const float4*>(wg + (int64_t)e * H + h0 + c8);
-        a = p[0];
-        b = p[1];
-      }
-      float4* d = reinterpret_cast<float4*>(&ws[r * PAD + c8]);
-      d[0] = a;
-      d[1] = b;
+      const bool ok = it < WI && e < E && c8 < hc;
+      const float4* p = reinterpret_cast<const float4*>(wg + (int64_t)e * H + h0 + c8);
+      rw[q][0] = ok ? p[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+      rw[q][1] = ok ? p[1] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    __syncthreads();
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < XPT; ++q) {
+      const int it = tid + q * NT;
+      if (it >= XI) continue;
+      const int r = it / (HC / 8), c8 = (it % (HC / 8)) * 8;
+      float4* d = reinterpret_cast<float4*>(&xs[buf][r * PAD + c8]);
+      if (BF16) {
+        const uint4 u = rxb[q];
+        d[0] = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
+                           __uint_as_float(u.y & 0xFFFF0000u));
+        d[1] = make_float4(__uint_as_float(u.z << 16), __uint_as_float(u.z & 0xFFFF0000u), __uint_as_float(u.w << 16),
+                           __uint_as_float(u.w & 0xFFFF0000u));
+      } else {
+        d[0] = rxf[q][0];
+        d[1] = rxf[q][1];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+      const int it = tid + q * NT;
+      if (it >= WI) continue;
+      const int r = it / (HC / 8), c8 = (it % (HC / 8)) * 8;
+      float4* d = reinterpret_cast<float4*>(&ws[buf][r * PAD + c8]);
+      d[0] = rw[q][0];
+      d[1] = rw[q][1];
+    }
+  };
+
+  const int nchunk = (H + HC - 1) / HC;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int c = 0; c < nchunk; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nchunk) load((c + 1) * HC);   // in flight during this chunk's chain
+    const int hc = min(HC, H - c * HC);        // a multiple of 8
     // ---- the chain, 4 h at a time, strictly ascending
     for (int hh = 0; hh < hc; hh += 4) {
       float4 xr[TT], wr[TE];
 #pragma unroll
-      for (int i = 0; i < TT; ++i) xr[i] = *reinterpret_cast<const float4*>(&xs[(ty * TT + i) * PAD + hh]);
+      for (int i = 0; i < TT; ++i) xr[i] = *reinterpret_cast<const float4*>(&xs[buf][(ty * TT + i) * PAD + hh]);
 #pragma unroll
-      for (int j = 0; j < TE; ++j) wr[j] = *reinterpret_cast<const float4*>(&ws[(tx * TE + j) * PAD + hh]);
+      for (int j = 0; j < TE; ++j) wr[j] = *reinterpret_cast<const float4*>(&ws[buf][(tx * TE + j) * PAD + hh]);
 #pragma unroll
       for (int i = 0; i < TT; ++i)
 #pragma unroll
@@ -94,6 +124,8 @@ __global__ __launch_bounds__(NT) void gate_logits_kernel(const void* __restrict_
           acc[i][j] = a;
         }
     }
+    // the other buffer was last read during chunk c - 1, before the barrier that ended it
+    if (c + 1 < nchunk) store(buf ^ 1);
     __syncthreads();
   }
 #pragma unroll
@@ -304,8 +336,10 @@ extern "C" int moe_gate_logits(const void* x, int x_dtype, const float* wg, cons
   }
   // Larger register tiles amortise LDS reads; use them only when they still give >= 512
   // workgroups (two per CU), because each output is one long dependent chain.
+  const int64_t wg84 = ceil_div64(T, 128) * ceil_div64(E, 64);
   const int64_t wg44 = ceil_div64(T, 64) * ceil_div64(E, 64);
   const int64_t wg22 = ceil_div64(T, 32) * ceil_div64(E, 32);
+  if (wg84 >= 512) return launch<8, 4>(x, bf16, wg, bias, T, H, E, logits, st);
   if (wg44 >= 512) return launch<4, 4>(x, bf16, wg, bias, T, H, E, logits, st);
   if (wg22 >= 512) return launch<2, 2>(x, bf16, wg, bias, T, H, E, logits, st);
   return launch<1, 1>(x, bf16, wg, bias, T, H, E, logits, st);

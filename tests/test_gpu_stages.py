@@ -90,7 +90,9 @@ def test_gate_logits(name):
 @pytest.mark.parametrize("T,H,E", [(77, 136, 13),       # direct (one output per thread)
                                     (700, 264, 256),     # LDS-staged 1x1 tiles
                                     (5000, 136, 200),    # 2x2 tiles, ragged
-                                    (9000, 520, 130)])   # 4x4 tiles, ragged
+                                    (9000, 520, 130),    # 2x2 tiles, ragged, 17 chunks
+                                    (8200, 136, 200),    # 4x4 tiles, ragged
+                                    (16383, 136, 260)])  # 8x4 tiles, ragged T, E and last chunk
 def test_gate_logits_ragged_all_paths(T, H, E):
     """T and E not multiples of the register tiles, H not a multiple of the LDS chunk; fp32 and bf16."""
     x = synth.randn((T, H), 6, synth.STAGE, part=31, device=DEV)
