@@ -21,6 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_fp8.so")
 
 MOE_OK = 0
+MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ARG, MOE_ERR_HIP, MOE_ERR_WORKSPACE = -1, -2, -3, -4, -5, -6
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_EPI_STORE, MOE_EPI_SWIGLU_QUANT = 0, 1
@@ -33,6 +34,8 @@ EXPORTED = ("moe_gate_logits", "moe_route", "moe_replay_route", "moe_replay_gate
             "moe_dispatch", "moe_pack_weights_fp8", "moe_packed_weight_bytes", "moe_grouped_gemm_plan",
             "moe_grouped_gemm_fp8_planned", "moe_grouped_gemm_fp8", "moe_combine", "moe_payload_bytes",
             "moe_payload_pack", "moe_payload_unpack", "moe_payload_to_host", "moe_payload_from_host",
+            "moe_combine_backward", "moe_swiglu_backward_quant", "moe_route_backward", "moe_gate_backward",
+            "moe_gate_backward_workspace", "moe_transpose_fp8_blocks",
             "moe_workspace_bytes", "moe_status_str", "moe_version")
 
 
@@ -91,6 +94,12 @@ def lib():
         "moe_payload_unpack": [P, I64, I32, P, P],
         "moe_payload_to_host": [P, I64, I32, P, P, P, P],
         "moe_payload_from_host": [P, I64, I32, P, P, P],
+        "moe_combine_backward": [P, ctypes.c_int, P, ctypes.c_int, P, P, I64, I32, I32, P, I32, P, P, P, P],
+        "moe_swiglu_backward_quant": [P, P, I64, I32, I32, P, P, P],
+        "moe_route_backward": [P, P, P, I64, cfgp, P, P],
+        "moe_gate_backward": [P, P, ctypes.c_int, P, I64, I32, I32, P, P, ctypes.c_int, P, P, P, SZ, P],
+        "moe_gate_backward_workspace": [I64, I32, I32],
+        "moe_transpose_fp8_blocks": [P, P, I32, I32, I32, P, P, P],
         "moe_workspace_bytes": [ctypes.c_int, I64, I32, I32, I32, I32],
         "moe_status_str": [ctypes.c_int],
         "moe_version": [],
@@ -102,6 +111,7 @@ def lib():
     L.moe_workspace_bytes.restype = ctypes.c_size_t
     L.moe_packed_weight_bytes.restype = ctypes.c_size_t
     L.moe_payload_bytes.restype = ctypes.c_size_t
+    L.moe_gate_backward_workspace.restype = ctypes.c_size_t
     L.moe_status_str.restype = ctypes.c_char_p
     L.moe_version.restype = ctypes.c_char_p
     _lib = L
@@ -523,4 +533,111 @@ def moe_payload_from_host(host: torch.Tensor, shape, num_experts: int, staging: 
     return out
 
 
-from .layer import MoELayerWeights, MoELayer, pack_expert_weights, quantize_expert_weights  # noqa: E402,F401
+
+# ----------------------------------------------------------------------------- backward
+def moe_combine_backward(dout: torch.Tensor, y: torch.Tensor, dest_row: torch.Tensor, topk_w: torch.Tensor,
+                         shared_first_row: Optional[torch.Tensor] = None, pow2: bool = False, dyq=None, dys=None,
+                         dw=None, stream=None):
+    """dY = w * dout per slot row (dout for the shared row), 1x128-quantised into (dyq [rows,H] uint8,
+    dys [rows,H/128] fp32) with rows = y.shape[0], and dw[t,j] = <dout[t], y[dest_row[t,j]]> (fp32 [T,k])."""
+    _dev(dout, "dout", (torch.float32, torch.bfloat16))
+    _dev(y, "y", (torch.float32, torch.bfloat16))
+    T, k = dest_row.shape
+    rows, H = y.shape
+    _dev(dout, "dout", shape=(T, H))
+    _dev(dest_row, "dest_row", torch.int32)
+    _dev(topk_w, "topk_w", torch.float32, (T, k))
+    if shared_first_row is not None:
+        _dev(shared_first_row, "shared_first_row", torch.int32, (1,))
+    dev = y.device
+    dyq = torch.empty((rows, H), dtype=FP8, device=dev) if dyq is None else _dev(dyq, "dyq", FP8, (rows, H))
+    dys = torch.empty((rows, H // 128), dtype=torch.float32, device=dev) if dys is None else \
+        _dev(dys, "dys", torch.float32, (rows, H // 128))
+    dw = torch.empty((T, k), dtype=torch.float32, device=dev) if dw is None else _dev(dw, "dw", torch.float32, (T, k))
+    mode = MOE_SCALE_POW2 if pow2 else MOE_SCALE_AMAX
+    _check(lib().moe_combine_backward(_p(dout), _act_code(dout), _p(y), _act_code(y), _p(dest_row), _p(topk_w), T, k, H,
+                                      _p(shared_first_row), mode, _p(dyq), _p(dys), _p(dw), _stream(stream)),
+           "moe_combine_backward")
+    return dyq, dys, dw
+
+
+def moe_swiglu_backward_quant(dh: torch.Tensor, g: torch.Tensor, pow2: bool = False, dgq=None, dgs=None, stream=None):
+    """dG = [dgate | dup] of h = silu(gate) * up (g = [gate | up] [rows,2F] fp32, dh [rows,F] fp32),
+    1x128-quantised: (dgq [rows,2F] uint8, dgs [rows,2F/128] fp32)."""
+    rows, F = dh.shape
+    _dev(dh, "dh", torch.float32)
+    _dev(g, "g", torch.float32, (rows, 2 * F))
+    dgq = torch.empty((rows, 2 * F), dtype=FP8, device=dh.device) if dgq is None else _dev(dgq, "dgq", FP8, (rows, 2 * F))
+    dgs = torch.empty((rows, 2 * F // 128), dtype=torch.float32, device=dh.device) if dgs is None else \
+        _dev(dgs, "dgs", torch.float32, (rows, 2 * F // 128))
+    mode = MOE_SCALE_POW2 if pow2 else MOE_SCALE_AMAX
+    _check(lib().moe_swiglu_backward_quant(_p(dh), _p(g), rows, F, mode, _p(dgq), _p(dgs), _stream(stream)),
+           "moe_swiglu_backward_quant")
+    return dgq, dgs
+
+
+def moe_route_backward(logits: torch.Tensor, topk_idx: torch.Tensor, dw: torch.Tensor, cfg: RouterCfg, dz=None,
+                       stream=None) -> torch.Tensor:
+    """dz [T,E] fp32: gradient of the logits from the routing-weight gradient dw, selection fixed."""
+    T, E = logits.shape
+    k = cfg.top_k
+    _dev(logits, "logits", torch.float32)
+    _dev(topk_idx, "topk_idx", torch.int32, (T, k))
+    _dev(dw, "dw", torch.float32, (T, k))
+    if E != cfg.num_experts:
+        raise ValueError("logits width != num_experts")
+    dz = torch.empty((T, E), dtype=torch.float32, device=logits.device) if dz is None else \
+        _dev(dz, "dz", torch.float32, (T, E))
+    _check(lib().moe_route_backward(_p(logits), _p(topk_idx), _p(dw), T, ctypes.byref(cfg), _p(dz), _stream(stream)),
+           "moe_route_backward")
+    return dz
+
+
+def gate_backward_workspace(T: int, E: int, H: int) -> int:
+    return int(lib().moe_gate_backward_workspace(T, E, H))
+
+
+def moe_gate_backward(dz: torch.Tensor, x: torch.Tensor, wg: torch.Tensor, dx_in: Optional[torch.Tensor] = None,
+                      dx_dtype=None, dx=None, dwg=None, db=None, want_db: bool = True, workspace=None, stream=None):
+    """dx = dx_in + dz Wg (rounded once to dx_dtype), dWg = dz^T x, db = column sums of dz (fp32).
+    Returns (dx, dwg, db or None)."""
+    T, H = x.shape
+    E = wg.shape[0]
+    _dev(dz, "dz", torch.float32, (T, E))
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    _dev(wg, "wg", torch.float32, (E, H))
+    if dx_in is not None:
+        _dev(dx_in, "dx_in", torch.float32, (T, H))
+    dev = x.device
+    od = x.dtype if dx_dtype is None else dx_dtype
+    dx = torch.empty((T, H), dtype=od, device=dev) if dx is None else _dev(dx, "dx", od, (T, H))
+    dwg = torch.empty((E, H), dtype=torch.float32, device=dev) if dwg is None else _dev(dwg, "dwg", torch.float32, (E, H))
+    if want_db:
+        db = torch.empty(E, dtype=torch.float32, device=dev) if db is None else _dev(db, "db", torch.float32, (E,))
+    else:
+        db = None
+    need = gate_backward_workspace(T, E, H)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace too small")
+    _check(lib().moe_gate_backward(_p(dz), _p(x), _act_code(x), _p(wg), T, H, E, _p(dx_in), _p(dx), _act_code(dx),
+                                   _p(dwg), _p(db), _p(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "moe_gate_backward")
+    return dx, dwg, db
+
+
+def moe_transpose_fp8_blocks(q: torch.Tensor, scales: torch.Tensor, qt=None, scales_t=None, stream=None):
+    """[G,N,K] 128x128-block codes and [G,N/128,K/128] scales -> ([G,K,N], [G,K/128,N/128])."""
+    _dev(q, "q", FP8)
+    G, N, K = q.shape
+    _dev(scales, "scales", torch.float32, (G, N // 128, K // 128))
+    qt = torch.empty((G, K, N), dtype=FP8, device=q.device) if qt is None else _dev(qt, "qt", FP8, (G, K, N))
+    scales_t = torch.empty((G, K // 128, N // 128), dtype=torch.float32, device=q.device) if scales_t is None else \
+        _dev(scales_t, "scales_t", torch.float32, (G, K // 128, N // 128))
+    _check(lib().moe_transpose_fp8_blocks(_p(q), _p(scales), G, N, K, _p(qt), _p(scales_t), _stream(stream)),
+           "moe_transpose_fp8_blocks")
+    return qt, scales_t
+
+from .layer import (MoELayerWeights, MoELayer, BackwardWeights, pack_expert_weights,  # noqa: E402,F401
+                    prepare_backward_weights, quantize_expert_weights)

@@ -6,6 +6,12 @@ forward(x) enqueues, on the current stream and without any host synchronisation:
   moe_grouped_gemm_fp8_planned (W1, SwiGLU + 1x128 quantisation of h) -> moe_grouped_gemm_fp8_planned
   (W2) -> moe_combine.
 
+backward(x, dout, bw) enqueues the gradients of the last forward (its buffers must still hold its
+results): moe_combine_backward (dY codes, dw) -> moe_grouped_gemm_fp8 (dY, W2^T: dh) ->
+moe_grouped_gemm_fp8 (A, W1: the GEMM1 output recomputed) -> moe_swiglu_backward_quant (dG codes)
+-> moe_grouped_gemm_fp8 (dG, W1^T: dA) -> moe_combine (dA, weights 1: expert part of dx) ->
+moe_route_backward (dz) -> moe_gate_backward (dx, dWg, db).
+
 This is the layer that "RL at 1T Scale: prime-rl Performance Deep Dive" runs in FP8 at inference
 (section "FP8 inference") and in block-scaled FP8 in the trainer (section "FP8 training"), with
 router replay (section "Router replay") as a mode of the same forward.
@@ -64,6 +70,32 @@ def pack_expert_weights(weights: MoELayerWeights, keep_rowmajor: bool = True, st
     return replace(weights, w1q=None, w2q=None, w1p=w1p, w2p=w2p)
 
 
+@dataclass
+class BackwardWeights:
+    """The expert-weight copies the backward streams, all packed for the store epilogue: W1 as is
+    (the GEMM1 output is recomputed rather than kept), and W1^T, W2^T (128x128 blocks transposed
+    together with their scales, so no re-quantisation)."""
+    w1_store: M.PackedWeight   # W1 [G,2F,H]
+    w1t: M.PackedWeight        # W1^T [G,H,2F]
+    w1ts: torch.Tensor         # [G,H/128,2F/128]
+    w2t: M.PackedWeight        # W2^T [G,F,H]
+    w2ts: torch.Tensor         # [G,F/128,H/128]
+
+
+def prepare_backward_weights(weights: MoELayerWeights, stream=None) -> BackwardWeights:
+    """Transposed and store-packed copies of the expert weights (from the row-major codes)."""
+    if weights.w1q is None or weights.w2q is None:
+        raise ValueError("prepare_backward_weights needs the row-major codes (pack with keep_rowmajor=True)")
+    w1t, w1ts = M.moe_transpose_fp8_blocks(weights.w1q, weights.w1s, stream=stream)
+    w1t_p = M.moe_pack_weights_fp8(w1t, M.MOE_EPI_STORE, stream=stream)
+    del w1t
+    w2t, w2ts = M.moe_transpose_fp8_blocks(weights.w2q, weights.w2s, stream=stream)
+    w2t_p = M.moe_pack_weights_fp8(w2t, M.MOE_EPI_STORE, stream=stream)
+    del w2t
+    w1_store = M.moe_pack_weights_fp8(weights.w1q, M.MOE_EPI_STORE, stream=stream)
+    return BackwardWeights(w1_store, w1t_p, w1ts, w2t_p, w2ts)
+
+
 def quantize_expert_weights(groups: int, H: int, F: int, master, device="cuda", stream=None, pow2: bool = False):
     """Allocate the quantised weight tensors and fill expert g from ``master(g) -> (w1 [2F,H], w2 [H,F])``
     (fp32 or bf16 device tensors), one expert at a time so the fp32 masters never coexist; pow2:
@@ -112,6 +144,9 @@ class MoELayer:
                                    dtype=torch.uint8, device=d)
         self.bad = torch.zeros(1, dtype=torch.int32, device=d)
         self.plan = None   # tile plan of the last forward's expert GEMMs
+        self.logits_valid = False   # the last forward wrote self.logits (not the fused sigmoid replay)
+        self.device = d
+        self.bwd = None    # backward buffers, allocated by the first backward
 
     def forward(self, x: torch.Tensor, replay: Optional[torch.Tensor] = None, record: Optional[torch.Tensor] = None,
                 stream=None, events=None, fused_replay: bool = True) -> torch.Tensor:
@@ -131,6 +166,7 @@ class MoELayer:
 
         mark(0)
         fused = replay is not None and int(w.cfg.score_fn) == M.MOE_SCORE_SIGMOID and fused_replay
+        self.logits_valid = not fused
         if not fused:
             M.moe_gate_logits(x, w.wg, w.bias, out=self.logits, stream=stream)
         mark(1)
@@ -162,3 +198,68 @@ class MoELayer:
         M.moe_combine(self.y, self.disp.dest_row, self.wts, shared_row, out=self.out, stream=stream)
         mark(7)
         return self.out
+
+    def _backward_buffers(self):
+        if self.bwd is not None:
+            return self.bwd
+        w, d, R, T = self.w, self.device, self.max_rows, self.T_max
+        E, H, F, k = w.E, w.H, w.F, int(w.cfg.top_k)
+        f32 = torch.float32
+        self.bwd = dict(
+            dyq=torch.empty((R, H), dtype=torch.uint8, device=d), dys=torch.empty((R, H // 128), dtype=f32, device=d),
+            dw=torch.empty((T, k), dtype=f32, device=d), dh=torch.empty((R, F), dtype=f32, device=d),
+            g=torch.empty((R, 2 * F), dtype=f32, device=d), dgq=torch.empty((R, 2 * F), dtype=torch.uint8, device=d),
+            dgs=torch.empty((R, 2 * F // 128), dtype=f32, device=d), dA=torch.empty((R, H), dtype=f32, device=d),
+            ones=torch.ones((T, k), dtype=f32, device=d), dx_exp=torch.empty((T, H), dtype=f32, device=d),
+            dz=torch.empty((T, E), dtype=f32, device=d), dx=torch.empty((T, H), dtype=self.act, device=d),
+            dwg=torch.empty((E, H), dtype=f32, device=d), db=torch.empty(E, dtype=f32, device=d),
+            gws=torch.empty(max(M.gate_backward_workspace(T, E, H), 1), dtype=torch.uint8, device=d))
+        return self.bwd
+
+    def backward(self, x: torch.Tensor, dout: torch.Tensor, bw: BackwardWeights, stream=None, events=None) -> dict:
+        """Gradients of the last forward (x is that forward's input) for the output gradient dout [T,H]
+        (activation dtype): dx [T,H] (activation dtype), dwg [E,H] and db [E] (None without a bias)
+        in fp32, plus the routing-weight gradient dw [T,k] and the logit gradient dz [T,E].  The
+        returned tensors are views of buffers reused by the next backward.  ``events``: optional
+        list of 9 timing events recorded before the first and after each of the 8 stages."""
+        if self.plan is None:
+            raise RuntimeError("backward needs a forward first")
+        if x.shape[0] != self.T_max or tuple(dout.shape) != (self.T_max, self.w.H):
+            raise ValueError("x / dout do not match the layer's buffers")
+        w = self.w
+        b = self._backward_buffers()
+        st = torch.cuda.current_stream() if stream is None else stream
+
+        def mark(i):
+            if events is not None:
+                events[i].record(st)
+
+        off = self.disp.offsets
+        shared_row = off[w.E:w.E + 1] if w.shared else None
+        mark(0)
+        M.moe_combine_backward(dout, self.y, self.disp.dest_row, self.wts, shared_row, pow2=w.pow2, dyq=b["dyq"],
+                               dys=b["dys"], dw=b["dw"], stream=stream)
+        mark(1)
+        M.moe_grouped_gemm_fp8(b["dyq"], b["dys"], off, bw.w2t, bw.w2ts, epilogue=M.MOE_EPI_STORE,
+                               out_dtype=torch.float32, out=b["dh"], plan=self.plan, stream=stream, pow2=w.pow2)
+        mark(2)
+        M.moe_grouped_gemm_fp8(self.disp.aq, self.disp.as_, off, bw.w1_store, w.w1s, epilogue=M.MOE_EPI_STORE,
+                               out_dtype=torch.float32, out=b["g"], plan=self.plan, stream=stream, pow2=w.pow2)
+        mark(3)
+        M.moe_swiglu_backward_quant(b["dh"], b["g"], pow2=w.pow2, dgq=b["dgq"], dgs=b["dgs"], stream=stream)
+        mark(4)
+        M.moe_grouped_gemm_fp8(b["dgq"], b["dgs"], off, bw.w1t, bw.w1ts, epilogue=M.MOE_EPI_STORE,
+                               out_dtype=torch.float32, out=b["dA"], plan=self.plan, stream=stream, pow2=w.pow2)
+        mark(5)
+        M.moe_combine(b["dA"], self.disp.dest_row, b["ones"], shared_row, out_dtype=torch.float32, out=b["dx_exp"],
+                      stream=stream)
+        mark(6)
+        if not self.logits_valid:
+            M.moe_gate_logits(x, w.wg, w.bias, out=self.logits, stream=stream)
+            self.logits_valid = True
+        M.moe_route_backward(self.logits, self.idx, b["dw"], w.cfg, dz=b["dz"], stream=stream)
+        mark(7)
+        M.moe_gate_backward(b["dz"], x, w.wg, dx_in=b["dx_exp"], dx_dtype=self.act, dx=b["dx"], dwg=b["dwg"],
+                            db=b["db"], want_db=w.bias is not None, workspace=b["gws"], stream=stream)
+        mark(8)
+        return dict(dx=b["dx"], dwg=b["dwg"], db=b["db"] if w.bias is not None else None, dw=b["dw"], dz=b["dz"])

@@ -291,6 +291,74 @@ int moe_payload_to_host(const int32_t* idx, int64_t n, int32_t E, uint8_t* stagi
  * asynchronously on `stream`; host must stay unchanged until the stream reaches this point. */
 int moe_payload_from_host(const void* host, int64_t n, int32_t E, uint8_t* staging, int32_t* idx, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * Backward of the layer (blog section "FP8 training": the trainer runs the same block-scaled FP8
+ * recipe as inference, so the backward contracts in FP8 too; section "Router replay": the routing
+ * selection is replayed, so it is a fixed input of the backward and only the routing weights carry
+ * gradient).  Calling order, after a forward whose buffers are still live (dispatch, logits,
+ * topk_idx/topk_w, expert rows y):
+ *   moe_combine_backward (dY codes, dw) -> moe_grouped_gemm_fp8 (dY x W2^T packed, STORE fp32: dh)
+ *   -> moe_grouped_gemm_fp8 (A x W1 packed for STORE, fp32: G, the GEMM1 output recomputed)
+ *   -> moe_swiglu_backward_quant (dG codes) -> moe_grouped_gemm_fp8 (dG x W1^T packed, fp32: dA)
+ *   -> moe_combine (dA, weights 1, fp32: expert part of dx) -> moe_route_backward (dz)
+ *   -> moe_gate_backward (dx = expert part + dz Wg, dWg, db).
+ * The transposed weights come from moe_transpose_fp8_blocks (a 128x128 block keeps its scale under
+ * transposition, so the data-gradient GEMMs need no re-quantisation).
+ * ------------------------------------------------------------------------------------------- */
+
+/* Combine backward.  For out[t] = sum_j w[t,j] y[dest_row[t,j]] (+ y[shared_first_row + t]):
+ *   dY[dest_row[t,j],:] = w[t,j] * dout[t,:]   (one fp32 product; dY = dout for the shared row)
+ * stored 1x128-quantised (codes dyq [rows,H] e4m3, scales dys [rows,H/128] fp32, scale_mode as in
+ * moe_quant_fp8_block), and dw[t,j] = sum_h dout[t,h] * y[dest_row[t,j],h] in fp32 (a fixed-order
+ * tree reduction; 0 for a slot with dest_row -1, whose dY row is not written).
+ *   dout [T,H] in dout_dtype, y [rows,H] in y_dtype (MOE_F32 or MOE_BF16: the forward's expert rows
+ *   as the combine read them); dest_row, topk_w [T,k] from the forward; shared_first_row NULL or a
+ *   device int32 (&offsets[E]); dw [T,k] fp32 (out).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (H % 128, k > 16), MOE_ERR_DTYPE, MOE_ERR_ARG (scale_mode),
+ * MOE_ERR_HIP.  T == 0 is a no-op. */
+int moe_combine_backward(const void* dout, int dout_dtype, const void* y, int y_dtype, const int32_t* dest_row,
+                         const float* topk_w, int64_t T, int32_t k, int32_t H, const int32_t* shared_first_row,
+                         int32_t scale_mode, uint8_t* dyq, float* dys, float* dw, void* stream);
+
+/* SwiGLU backward and 1x128 quantisation of the result.  With G = [gate | up] the GEMM1 output
+ * [rows, 2F] fp32 and dh [rows, F] fp32:  s = sigmoid(gate), dgate = dh * up * s * (1 + gate * (1 - s)),
+ * dup = dh * gate * s (fp32), dG = [dgate | dup] quantised in 1x128 blocks along 2F:
+ * dgq [rows, 2F] e4m3, dgs [rows, 2F/128] fp32.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (F % 128), MOE_ERR_ARG (scale_mode), MOE_ERR_HIP. */
+int moe_swiglu_backward_quant(const float* dh, const float* g, int64_t rows, int32_t F, int32_t scale_mode,
+                              uint8_t* dgq, float* dgs, void* stream);
+
+/* Router backward with the selection held fixed: dz[t,e] = d(loss)/d(logit[t,e]) from
+ * dw[t,j] = d(loss)/d(topk_w[t,j]), with the scores recomputed from the logits by the router's own
+ * fixed exp.  Renormalised (w_j = score_j / sum_l score_l):  sigmoid dz_{i_j} = s_j (1 - s_j)
+ * (dw_j - sum_l w_l dw_l) / sum_l s_l;  softmax dz_{i_j} = w_j (dw_j - sum_l w_l dw_l).  Not
+ * renormalised:  sigmoid dz_{i_j} = dw_j s_j (1 - s_j);  softmax (full softmax p over E)
+ * dz_e = [e selected] w_e dw_e - p_e sum_l w_l dw_l.  Every other dz element is 0; slots with index
+ * -1 carry nothing.  logits [T,E], topk_idx [T,k], dw [T,k], dz [T,E] (out, every element written).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ARG (score_fn), MOE_ERR_HIP. */
+int moe_route_backward(const float* logits, const int32_t* topk_idx, const float* dw, int64_t T,
+                       const moe_router_cfg* cfg, float* dz, void* stream);
+
+/* Gate-projection backward (fp32, like the forward's logits):
+ *   dx[t,h] = dx_in[t,h] + sum_e dz[t,e] wg[e,h]   (dx_in [T,H] fp32 or NULL; one rounding to dx_dtype)
+ *   dwg[e,h] = sum_t dz[t,e] x[t,h]                 (fp32; the token range is split into fixed slices
+ *                                                    whose partials are summed in slice order)
+ *   db[e] = sum_t dz[t,e]                           (fp32, or db NULL to skip)
+ * x [T,H] in x_dtype; wg [E,H] fp32; workspace >= moe_gate_backward_workspace(T, E, H) bytes.
+ * Deterministic.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (H % 8), MOE_ERR_DTYPE, MOE_ERR_WORKSPACE,
+ * MOE_ERR_HIP. */
+int moe_gate_backward(const float* dz, const void* x, int x_dtype, const float* wg, int64_t T, int32_t H, int32_t E,
+                      const float* dx_in, void* dx, int dx_dtype, float* dwg, float* db, void* workspace,
+                      size_t workspace_bytes, void* stream);
+size_t moe_gate_backward_workspace(int64_t T, int32_t E, int32_t H);
+
+/* Transpose of 128x128-block FP8 weights with their scales: qt[g][c][r] = q[g][r][c],
+ * scales_t[g][cb][rb] = scales[g][rb][cb]; q [groups,N,K] -> qt [groups,K,N] (N, K multiples of 128).
+ * Exact (the codes are moved, not re-encoded).  qt must not alias q.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ARG (qt == q), MOE_ERR_HIP. */
+int moe_transpose_fp8_blocks(const uint8_t* q, const float* scales, int32_t groups, int32_t N, int32_t K,
+                             uint8_t* qt, float* scales_t, void* stream);
+
 /* Workspace bytes needed by moe_dispatch (op MOE_OP_DISPATCH: rows_or_T = T, k, E) or
  * moe_grouped_gemm_fp8 (op MOE_OP_GROUPED_GEMM: rows_or_T = max_rows, E = groups, N, K). */
 size_t moe_workspace_bytes(int op, int64_t rows_or_T, int32_t k, int32_t E, int32_t N, int32_t K);

@@ -26,7 +26,7 @@ import numpy as np
 import torch
 
 # tensor ids of the per-tensor streams
-X, WG, BIAS, W1, W2, SW1, SW2, PERTURB, ZIPF, STAGE = range(10)
+X, WG, BIAS, W1, W2, SW1, SW2, PERTURB, ZIPF, STAGE, DOUT = range(11)
 
 
 @dataclass(frozen=True)
@@ -123,6 +123,11 @@ def make_x(cfg: LayerConfig, device="cpu", chunk: int = 0, tokens: Optional[int]
     """Activations [T,H] in the activation dtype (chunk c of a chunked workload)."""
     T = cfg.T if tokens is None else tokens
     return to_act(randn((T, cfg.H), cfg.seed, X, 0, chunk, device=device), cfg.act)
+
+
+def make_dout(cfg: LayerConfig, device="cpu", chunk: int = 0) -> torch.Tensor:
+    """Output gradient [T,H] for the backward, N(0,1) in the activation dtype."""
+    return to_act(randn((cfg.T, cfg.H), cfg.seed, DOUT, 0, chunk, device=device), cfg.act)
 
 
 def zipf_bias(cfg: LayerConfig) -> np.ndarray:

@@ -236,3 +236,39 @@ def test_product_package_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in src and "from oracle" not in src and "moe_oracle" not in src, f
+
+
+def test_backward_validation(L):
+    P = ctypes.c_void_p(16)   # never dereferenced: every case fails (or is empty) before a launch
+    cfgp = ctypes.byref(_cfg())
+    # combine backward: (dout, dt, y, yt, dest, w, T, k, H, shared, mode, dyq, dys, dw, stream)
+    assert L.moe_combine_backward(P, 1, P, 1, P, P, 4, 17, 256, None, 0, P, P, P, None) == SHAPE   # k > 16
+    assert L.moe_combine_backward(P, 1, P, 1, P, P, 4, 8, 200, None, 0, P, P, P, None) == SHAPE    # H % 128
+    assert L.moe_combine_backward(P, 2, P, 1, P, P, 4, 8, 256, None, 0, P, P, P, None) == DTYPE
+    assert L.moe_combine_backward(P, 1, P, 1, P, P, 4, 8, 256, None, 2, P, P, P, None) == ARG
+    assert L.moe_combine_backward(None, 1, P, 1, P, P, 4, 8, 256, None, 0, P, P, P, None) == NULL
+    assert L.moe_combine_backward(None, 1, None, 1, None, None, 0, 8, 256, None, 0, None, None, None, None) == OK
+    # SwiGLU backward: (dh, g, rows, F, mode, dgq, dgs, stream)
+    assert L.moe_swiglu_backward_quant(P, P, 4, 100, 0, P, P, None) == SHAPE
+    assert L.moe_swiglu_backward_quant(P, P, 4, 128, 3, P, P, None) == ARG
+    assert L.moe_swiglu_backward_quant(P, None, 4, 128, 0, P, P, None) == NULL
+    assert L.moe_swiglu_backward_quant(None, None, 0, 128, 0, None, None, None) == OK
+    # router backward: (logits, idx, dw, T, cfg, dz, stream)
+    assert L.moe_route_backward(P, P, P, 4, None, P, None) == NULL
+    assert L.moe_route_backward(P, P, P, 4, ctypes.byref(_cfg(top_k=300)), P, None) == SHAPE
+    assert L.moe_route_backward(P, P, P, 4, ctypes.byref(_cfg(score_fn=5)), P, None) == ARG
+    assert L.moe_route_backward(P, None, P, 4, cfgp, P, None) == NULL
+    assert L.moe_route_backward(None, None, None, 0, cfgp, None, None) == OK
+    # gate backward: (dz, x, xt, wg, T, H, E, dx_in, dx, dxt, dwg, db, ws, ws_bytes, stream)
+    need = L.moe_gate_backward_workspace(16384, 256, 6144)
+    assert need == 16 * (256 * 6144 + 256) * 4 and L.moe_gate_backward_workspace(256, 64, 4096) == 64 * 4096 * 4 + 256
+    assert L.moe_gate_backward(P, P, 1, P, 4, 100, 8, None, P, 1, P, None, P, 1 << 20, None) == SHAPE
+    assert L.moe_gate_backward(P, P, 2, P, 4, 128, 8, None, P, 1, P, None, P, 1 << 20, None) == DTYPE
+    assert L.moe_gate_backward(P, P, 1, P, 16384, 6144, 256, None, P, 1, P, None, P, need - 1, None) == WS
+    assert L.moe_gate_backward(P, None, 1, P, 4, 128, 8, None, P, 1, P, None, P, 1 << 20, None) == NULL
+    assert L.moe_gate_backward(None, None, 1, None, 0, 128, 8, None, None, 1, None, None, None, 0, None) == OK
+    # transpose: (q, s, G, N, K, qt, st, stream)
+    assert L.moe_transpose_fp8_blocks(P, P, 2, 200, 256, ctypes.c_void_p(32), P, None) == SHAPE
+    assert L.moe_transpose_fp8_blocks(P, P, 2, 256, 256, P, P, None) == ARG          # in place
+    assert L.moe_transpose_fp8_blocks(P, None, 2, 256, 256, ctypes.c_void_p(32), P, None) == NULL
+    assert L.moe_transpose_fp8_blocks(None, None, 0, 256, 256, None, None, None) == OK
