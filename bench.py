@@ -1,6 +1,7 @@
 """Benchmark of the block-scaled FP8 MoE layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|longctx|r3|tiny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|longctx|r3|tiny|payload]
+                    [--scales amax|pow2] [--backward]
 
 A step is one full layer forward (gate logits, routing, activation quantisation, dispatch,
 grouped GEMM1 + SwiGLU + h quantisation, grouped GEMM2, combine) over one batch of synthetic
@@ -12,7 +13,9 @@ weights in the 256 MB Infinity Cache left behind by the step before.  The report
 replays of a HIP graph holding the whole layer forward (--no-graph: eager launches); a second
 pass of eager steps with HIP events between the stages gives the per-stage times.  Prints one JSON
 line: layer tokens/s, per-stage times, the grouped GEMM's TFLOP/s, the roofline of the dominant
-kernel, and the CPU oracle timed on a bounded sample.
+kernel, and the CPU oracle timed on a bounded sample.  With --backward a step is the layer's training
+forward (GEMM1 also keeps its fp32 output) followed by its backward (output gradient -> dx, dWg,
+db), and the line reports the backward's stages too.
 """
 from __future__ import annotations
 
@@ -32,6 +35,8 @@ PEAK_FP32_TFLOPS = 157.3       # published fp32 vector peak (a non-packed fma lo
 RIDGE_FP8 = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 
 STAGES = ["gate_logits", "route", "quant_x", "dispatch", "gemm1_swiglu", "gemm2", "combine"]
+BWD_STAGES = ["bwd_combine", "bwd_gemm_dh", "bwd_gemm_g", "bwd_swiglu", "bwd_gemm_da", "bwd_combine_dx", "bwd_route",
+              "bwd_gate"]
 
 
 def parse():
@@ -47,6 +52,8 @@ def parse():
     ap.add_argument("--scales", choices=("amax", "pow2"), default="amax",
                     help="block-scale form: amax/448 fp32 scales (default) or power-of-two scales applied by "
                          "the matrix cores")
+    ap.add_argument("--backward", action="store_true",
+                    help="time forward + backward of the layer (gradients of x, the gate and its bias)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -72,6 +79,17 @@ def stage_model(cfg, counts, n_active1):
                              bound=None),
         "gemm2": dict(bytes=rows * F * (1 + sig) + w2 + rows * H * ab, flops=2.0 * H * F * rows, bound=None),
         "combine": dict(bytes=rows * H * ab + T * k * 8 + T * H * ab, flops=0.0, bound="hbm"),
+        # backward (dY, dG quantised 1x128; dh, G, dA fp32; the router and gate in fp32)
+        "bwd_combine": dict(bytes=T * H * ab + rows * H * ab + rows * H * (1 + sig) + T * k * 12, flops=0.0,
+                            bound="hbm"),
+        "bwd_gemm_dh": dict(bytes=rows * H * (1 + sig) + w2 + rows * F * 4, flops=2.0 * H * F * rows, bound=None),
+        "bwd_gemm_g": dict(bytes=rows * H * (1 + sig) + w1 + rows * 2 * F * 4, flops=4.0 * H * F * rows, bound=None),
+        "bwd_swiglu": dict(bytes=rows * F * 4 + rows * 2 * F * 4 + rows * 2 * F * (1 + sig), flops=0.0, bound="hbm"),
+        "bwd_gemm_da": dict(bytes=rows * 2 * F * (1 + sig) + w1 + rows * H * 4, flops=4.0 * H * F * rows, bound=None),
+        "bwd_combine_dx": dict(bytes=rows * H * 4 + T * k * 8 + T * H * 4, flops=0.0, bound="hbm"),
+        "bwd_route": dict(bytes=T * E * 8 + T * k * 8, flops=0.0, bound="hbm"),
+        "bwd_gate": dict(bytes=T * E * 4 + T * H * ab + E * H * 4 + T * H * 4 + T * H * ab + E * H * 4,
+                         flops=4.0 * T * H * E, bound="alu"),
         "_rows": rows, "_groups": G,
     }
 
@@ -108,7 +126,12 @@ def main():
     w1q, w1s, w2q, w2s = quantize_expert_weights(cfg.groups, cfg.H, cfg.F,
                                                  lambda g: synth.make_expert(cfg, g, 0, dev), device=dev, pow2=pow2)
     weights = pack_expert_weights(MoELayerWeights(wg=wg, bias=b, w1q=w1q, w1s=w1s, w2q=w2q, w2s=w2s, cfg=rcfg,
-                                                  shared=cfg.shared, pow2=pow2), keep_rowmajor=False)
+                                                  shared=cfg.shared, pow2=pow2), keep_rowmajor=a.backward)
+    bwd_weights = None
+    if a.backward:
+        from block_scaled_fp8_top_amd.layer import prepare_backward_weights
+        bwd_weights = prepare_backward_weights(weights)
+        weights = replace(weights, w1q=None, w2q=None)
     del w1q, w2q
     wbytes = weights.w1p.data.numel() + weights.w2p.data.numel()
     copies = a.copies if a.copies > 0 else max(2, math.ceil((2 << 30) / wbytes))
@@ -122,6 +145,9 @@ def main():
     layer = layers[0]
     x = synth.make_x(cfg, dev)
     torch.cuda.synchronize()
+    if a.backward:
+        backward_bench(a, cfg, layers, bwd_weights, x, copies, pow2)
+        return
 
     for s in range(a.warmup):
         layers[s % copies].forward(x)
@@ -252,6 +278,155 @@ def main():
 
 
 GEMM_SRC = os.path.join(ROOT, "block_scaled_fp8_top_amd", "csrc", "grouped_gemm.hip")
+
+
+def stage_entry(name, model, ms):
+    """Achieved rates of one stage and its roofline fraction."""
+    m = model[name]
+    t = ms * 1e-3
+    d = {"ms": round(ms, 4), "GB_s": round(m["bytes"] / t / 1e9, 1)}
+    if m["flops"]:
+        d["TFLOP_s"] = round(m["flops"] / t / 1e12, 2)
+    if m["bound"] is None:
+        d["bound"] = "mfma" if m["flops"] / m["bytes"] >= RIDGE_FP8 else "hbm"
+    else:
+        d["bound"] = m["bound"]
+    if d["bound"] == "mfma":
+        d["frac"] = round(m["flops"] / t / 1e12 / PEAK_FP8_TFLOPS, 4)
+    elif d["bound"] == "alu":
+        d["frac"] = round(m["flops"] / t / 1e12 / PEAK_FP32_TFLOPS, 4)
+    else:
+        d["frac"] = round(m["bytes"] / t / 1e9 / PEAK_HBM_GBS, 4)
+    return d
+
+
+def backward_bench(a, cfg, layers, bw, x, copies, pow2):
+    """Forward + backward steps: HIP-graph replays of both for the rate, then eager steps with
+    events between every stage of each pass."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    dev = "cuda"
+    dout = synth.make_dout(cfg, dev)
+    for s in range(a.warmup):
+        layers[s % copies].forward(x, training=True)
+        layers[s % copies].backward(x, dout, bw)
+    torch.cuda.synchronize()
+    K = a.steps
+    graphs = None
+    if not a.no_graph:
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in range(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    layers[c].forward(x, training=True)
+                    layers[c].backward(x, dout, bw)
+                graphs.append(g)
+        torch.cuda.current_stream().wait_stream(side)
+        for s in range(a.warmup):
+            graphs[s % copies].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(K):
+            graphs[s % copies].replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / K
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(K)]
+    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(len(BWD_STAGES) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        layers[s % copies].forward(x, events=evf[s], training=True)
+        layers[s % copies].backward(x, dout, bw, events=evb[s])
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / K
+    ms_per_step = eager_ms if graphs is None else graph_ms
+    stage_ms = {name: float(np.mean([evf[s][i].elapsed_time(evf[s][i + 1]) for s in range(K)]))
+                for i, name in enumerate(STAGES)}
+    stage_ms.update({name: float(np.mean([evb[s][i].elapsed_time(evb[s][i + 1]) for s in range(K)]))
+                     for i, name in enumerate(BWD_STAGES)})
+    layer = layers[0]
+    counts = layer.disp.counts.cpu().numpy()
+    n_active = int((counts > 0).sum())
+    model = stage_model(cfg, counts, n_active)
+    # the training forward's GEMM1 also writes G (fp32); the backward then has no recompute
+    g1 = model["gemm1_swiglu"]
+    model["gemm1_swiglu"] = dict(g1, bytes=g1["bytes"] + model["_rows"] * 2 * cfg.F * 4)
+    timed = [n for n in STAGES + BWD_STAGES if n != "bwd_gemm_g"]   # no recompute after a training forward
+    stages = {name: stage_entry(name, model, stage_ms[name]) for name in timed}
+    fwd_ms = sum(stage_ms[n] for n in STAGES)
+    bwd_ms = sum(stage_ms[n] for n in BWD_STAGES)
+    gemm_names = [n for n in ("bwd_gemm_dh", "bwd_gemm_g", "bwd_gemm_da") if n in stages]
+    bgemm_ms = sum(stage_ms[n] for n in gemm_names)
+    bgemm_tflops = sum(model[n]["flops"] for n in gemm_names) / (bgemm_ms * 1e-3) / 1e12
+    dom = max((n for n in BWD_STAGES if n in stages), key=lambda n: stage_ms[n])
+    e = stages[dom]
+    if e["bound"] == "hbm":
+        roof = {"bound": "hbm", "achieved": e["GB_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": e["bound"], "achieved": e["TFLOP_s"],
+                "peak": PEAK_FP8_TFLOPS if e["bound"] == "mfma" else PEAK_FP32_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    p2 = ", pow2" if pow2 else ""
+    roof["kernel"] = f"grouped_gemm_kernel<{layer.plan.tile_rows}, store_f32, packed{p2}>" if "gemm" in dom else dom
+    roof["stage"] = dom
+    cpu = None if a.no_cpu_baseline else cpu_baseline_backward(cfg, x, dout, dev, pow2)
+    line = {
+        "metric": "MoE layer forward+backward tokens/s + backward grouped FP8 GEMM TFLOP/s, 1 GPU",
+        "value": round(cfg.T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4),
+        "launch": "eager" if graphs is None else "hip-graph replay", "eager_ms_per_step": round(eager_ms, 4),
+        "forward_ms": round(fwd_ms, 4), "backward_ms": round(bwd_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3 x fp8-e4m3 -> fp32 (GEMMs, forward and backward); fp32 router and gate; "
+                 + ("bf16" if cfg.act == "bf16" else "fp32") + " activations and gradients",
+        "data": "synthetic (seeded N(0,1) activations and output gradient, N(0,1/sqrt(fan_in)) weights)",
+        "config": {"workload": cfg.name, "pass": "forward+backward", "tokens": cfg.T, "hidden": cfg.H,
+                   "experts": cfg.E, "shared_experts": int(cfg.shared), "ffn": cfg.F, "top_k": cfg.k,
+                   "score": cfg.score_fn, "rows": model["_rows"], "active_experts": n_active,
+                   "layer_copies": copies, "weight_layout": "packed",
+                   "block_scales": "power of two" if pow2 else "amax/448 fp32", "parallelism": "none (1 GPU)"},
+        "backward_gemm_tflops": round(bgemm_tflops, 2),
+        "backward_gemm_frac_fp8_peak": round(bgemm_tflops / PEAK_FP8_TFLOPS, 4),
+        "stages": stages, "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+def cpu_baseline_backward(cfg, x, dout, dev, pow2=False):
+    """The backward oracle, per token with no dispatch, on a seeded sample of tokens."""
+    import oracle as O
+    import oracle.backward as B
+    import oracle.layer as L
+    import synth
+
+    wg, b = synth.make_gate(cfg, 0, dev)
+    rc = O.router_cfg(cfg.E, cfg.k, 0 if cfg.score_fn == "softmax" else 1, cfg.renorm, cfg.n_group,
+                      cfg.topk_group, cfg.group_score_topk)
+
+    def expert(e):
+        w1, w2 = synth.make_expert(cfg, e, 0, dev)
+        return L.quantize_expert(w1.cpu().numpy(), w2.cpu().numpy(), pow2)
+
+    ol = L.OracleLayer(wg=wg.cpu().numpy(), bias=None if b is None else b.cpu().numpy(), cfg=rc, shared=cfg.shared,
+                       act=cfg.act, F=cfg.F, expert=expert, pow2=pow2)
+    toks = synth.sample_tokens(cfg.T, 4, cfg.seed + 98)
+    xh, dh = x.float().cpu().numpy()[toks], dout.float().cpu().numpy()[toks]
+    r0 = O.moe_route(O.moe_gate_logits(xh, ol.wg, ol.bias), rc)[0]
+    for e in set(r0.reshape(-1).tolist()) | ({cfg.E} if cfg.shared else set()):
+        ol.get(e)                              # weight quantisation is offline on the GPU side too
+    t0 = time.perf_counter()
+    B.backward_token(ol, xh, dh)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(toks) / dt, 3), "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"{len(toks)} seeded tokens of {cfg.T}, per-token backward (with its forward), "
+                      "expert weights pre-quantised", "seconds": round(dt, 2)}
 
 
 def stage_kernel(stage, layer):

@@ -32,7 +32,7 @@ MOE_SCALE_AMAX, MOE_SCALE_POW2 = 0, 1
 EXPORTED = ("moe_gate_logits", "moe_route", "moe_replay_route", "moe_replay_gate", "moe_router_score_eval",
             "moe_quant_fp8_block",
             "moe_dispatch", "moe_pack_weights_fp8", "moe_packed_weight_bytes", "moe_grouped_gemm_plan",
-            "moe_grouped_gemm_fp8_planned", "moe_grouped_gemm_fp8", "moe_combine", "moe_payload_bytes",
+            "moe_grouped_gemm_fp8_planned", "moe_grouped_gemm_fp8_swiglu_save", "moe_grouped_gemm_fp8", "moe_combine", "moe_payload_bytes",
             "moe_payload_pack", "moe_payload_unpack", "moe_payload_to_host", "moe_payload_from_host",
             "moe_combine_backward", "moe_swiglu_backward_quant", "moe_route_backward", "moe_gate_backward",
             "moe_gate_backward_workspace", "moe_transpose_fp8_blocks",
@@ -88,6 +88,8 @@ def lib():
         "moe_grouped_gemm_plan": [P, I32, I64, I32, P, SZ, ctypes.POINTER(GemmPlan), P],
         "moe_grouped_gemm_fp8_planned": [ctypes.POINTER(GemmPlan), P, P, P, P, I32, P, I32, I32, I32, I32, P,
                                          ctypes.c_int, P, P],
+        "moe_grouped_gemm_fp8_swiglu_save": [ctypes.POINTER(GemmPlan), P, P, P, P, I32, P, I32, I32, I32, P, P, P,
+                                             P],
         "moe_combine": [P, ctypes.c_int, P, P, I64, I32, I32, P, P, ctypes.c_int, P],
         "moe_payload_bytes": [I64, I32],
         "moe_payload_pack": [P, I64, I32, P, P, P],
@@ -376,14 +378,15 @@ def moe_grouped_gemm_plan(offsets: torch.Tensor, max_rows: int, workspace: torch
 def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tensor, b, bs: torch.Tensor,
                          epilogue: int = MOE_EPI_STORE, out_dtype=torch.bfloat16, out=None, out_scales=None,
                          workspace: Optional[torch.Tensor] = None, stream=None, tile_rows: int = 0,
-                         plan: Optional[GemmPlan] = None, pow2: bool = False):
+                         plan: Optional[GemmPlan] = None, pow2: bool = False, save_g: Optional[torch.Tensor] = None):
     """a [max_rows,K] uint8, as_ [max_rows,K/128], offsets [G+1] (device), b [G,N,K] uint8 or a
     PackedWeight packed for this epilogue, bs [G,N/128,K/128].
     STORE -> out [max_rows,N] (bf16/fp32); SWIGLU_QUANT -> (h codes [max_rows,N/2] uint8, scales [max_rows,N/256]).
     tile_rows: 32, 48, 64 or 128 rows per workgroup tile, 0 = chosen from the average group size.
     plan: a plan from moe_grouped_gemm_plan for these offsets and max_rows (then no workspace is
     needed and tile_rows is the plan's).  pow2: every scale in as_ and bs is a power of two (the
-    matrix cores apply them; the SwiGLU epilogue writes power-of-two scales for h)."""
+    matrix cores apply them; the SwiGLU epilogue writes power-of-two scales for h).
+    save_g (SwiGLU with a plan only): fp32 [max_rows, N] that also receives the GEMM output G."""
     max_rows, K = a.shape
     if isinstance(b, PackedWeight):
         if b.epilogue != epilogue:
@@ -421,6 +424,14 @@ def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tens
         osc = torch.empty((max_rows, F // 128), dtype=torch.float32, device=dev) if out_scales is None else \
             _dev(out_scales, "out_scales", torch.float32, (max_rows, F // 128))
     mode = MOE_SCALE_POW2 if pow2 else MOE_SCALE_AMAX
+    if save_g is not None:
+        if plan is None or epilogue != MOE_EPI_SWIGLU_QUANT:
+            raise ValueError("save_g needs a plan and the SwiGLU epilogue")
+        _dev(save_g, "save_g", torch.float32, (max_rows, N))
+        _check(lib().moe_grouped_gemm_fp8_swiglu_save(ctypes.byref(plan), _p(a), _p(as_), _p(offsets), _p(b_t),
+                                                      b_layout, _p(bs), N, K, mode, _p(out), _p(osc), _p(save_g),
+                                                      _stream(stream)), "moe_grouped_gemm_fp8_swiglu_save")
+        return out, osc
     if plan is not None:
         _check(lib().moe_grouped_gemm_fp8_planned(ctypes.byref(plan), _p(a), _p(as_), _p(offsets), _p(b_t), b_layout,
                                                   _p(bs), N, K, epilogue, mode, _p(out), code, _p(osc),

@@ -163,7 +163,9 @@ __global__ __launch_bounds__(256) void reduce_slices_kernel(const float* __restr
   }
 }
 
-int gate_bwd_slices(int64_t T) { return (int)std::max<int64_t>(1, std::min<int64_t>(16, T / 512)); }
+// token slices of dWg: about 64 tokens each for short batches (enough workgroups to fill the
+// chip), at most 16 (the partials are re-read once by the reduction)
+int gate_bwd_slices(int64_t T) { return (int)std::max<int64_t>(1, std::min<int64_t>(16, ceil_div64(T, 64))); }
 
 }  // namespace
 

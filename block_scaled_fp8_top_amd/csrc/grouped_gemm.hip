@@ -211,7 +211,8 @@ template <int BM, int EPI, bool OUT_BF16, bool PACKED, bool POW2>
 __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const int32_t* __restrict__ offsets,
     const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles, int ny, const uint8_t* __restrict__ b,
-    const float* __restrict__ bs, int N, int K, void* __restrict__ out, float* __restrict__ out_scales) {
+    const float* __restrict__ bs, int N, int K, void* __restrict__ out, float* __restrict__ out_scales,
+    float* __restrict__ g_out) {
   using T = Tile<BM>;
   constexpr int WM = T::WM, WN = T::WN, MS = T::MS, NS = T::NS, HS = NS / 2, NSTAGE = T::NSTAGE;
   constexpr int A_BYTES = T::A_BYTES, B_BYTES = T::B_BYTES, AS_W = T::AS_W;
@@ -467,6 +468,22 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
         recent[D - 1] = MS * NS;
       }
     } else {
+      // training forward: also store the fp32 GEMM output G = [gate | up] ([rows, N], N = 2F), which
+      // the backward's SwiGLU derivative needs (uniform branch; rows past the group are dropped)
+      if (g_out) {
+        const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+            g_out + (size_t)row0 * N, 0, nrows * N * 4, 0x00020000);
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+          for (int ns = 0; ns < NS; ++ns) {
+            const int col = (ns < HS ? 0 : F) + cu.nt * 128 + wn * HS * 16 + (ns % HS) * 16 + tc;
+            uint32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(acc[ms][ns][i]);
+            __builtin_amdgcn_raw_buffer_store_b128(v, rg, ((wm * WROWS + ms * 16 + tr) * N + col) * 4, 0, 0);
+          }
+      }
       // h for this lane: rows (ms, i), columns wn*HS*16 + hs*16 + lr (hs < HS) of the 128-wide block
       float h[MS][HS][4];
 #pragma unroll
@@ -515,7 +532,7 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc,
                                                 (lane >> 4) == 0 ? (row * FB + cu.nt) * 4 : 0x7FFFFFF0, 0, 0);
       }
-      recent[D - 1] = MS * HS + (wn == 0 ? MS : 0);
+      recent[D - 1] = MS * HS + (wn == 0 ? MS : 0) + (g_out ? MS * NS : 0);
     }
 #pragma unroll
     for (int i = 0; i < MS; ++i)
@@ -542,30 +559,30 @@ int auto_tile_rows(int64_t max_rows, int groups) {
 template <int BM, bool PACKED, bool POW2>
 void launch3(unsigned grid, hipStream_t st, int epilogue, int out_dtype, const uint8_t* a, const float* as,
              const int32_t* offsets, const int4* tiles, const int32_t* ntiles, int ny, const uint8_t* b,
-             const float* bs, int N, int K, void* out, float* out_scales) {
+             const float* bs, int N, int K, void* out, float* out_scales, float* g_out) {
   if (epilogue == MOE_EPI_STORE) {
     if (out_dtype == MOE_BF16)
       grouped_gemm_kernel<BM, 0, true, PACKED, POW2><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b,
-                                                                                bs, N, K, out, nullptr);
+                                                                                bs, N, K, out, nullptr, nullptr);
     else
       grouped_gemm_kernel<BM, 0, false, PACKED, POW2><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b,
-                                                                                 bs, N, K, out, nullptr);
+                                                                                 bs, N, K, out, nullptr, nullptr);
   } else {
     grouped_gemm_kernel<BM, 1, false, PACKED, POW2><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b,
-                                                                               bs, N, K, out, out_scales);
+                                                                               bs, N, K, out, out_scales, g_out);
   }
 }
 
 template <int BM, bool PACKED>
 void launch(unsigned grid, hipStream_t st, int epilogue, int scale_mode, int out_dtype, const uint8_t* a,
             const float* as, const int32_t* offsets, const int4* tiles, const int32_t* ntiles, int ny,
-            const uint8_t* b, const float* bs, int N, int K, void* out, float* out_scales) {
+            const uint8_t* b, const float* bs, int N, int K, void* out, float* out_scales, float* g_out) {
   if (scale_mode == MOE_SCALE_POW2)
     launch3<BM, PACKED, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                              out_scales);
+                              out_scales, g_out);
   else
     launch3<BM, PACKED, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                               out_scales);
+                               out_scales, g_out);
 }
 
 // compute units of the current device, queried once per device
@@ -658,11 +675,10 @@ extern "C" int moe_grouped_gemm_plan(const int32_t* offsets, int32_t groups, int
   return MOE_OK;
 }
 
-extern "C" int moe_grouped_gemm_fp8_planned(const moe_gemm_plan* plan, const uint8_t* a, const float* as,
-                                            const int32_t* offsets, const uint8_t* b, int32_t b_layout,
-                                            const float* bs, int32_t N, int32_t K, int32_t epilogue,
-                                            int32_t scale_mode, void* out, int out_dtype, float* out_scales,
-                                            void* stream) {
+namespace {
+int run_planned(const moe_gemm_plan* plan, const uint8_t* a, const float* as, const int32_t* offsets,
+                const uint8_t* b, int32_t b_layout, const float* bs, int32_t N, int32_t K, int32_t epilogue,
+                int32_t scale_mode, void* out, int out_dtype, float* out_scales, float* g_out, void* stream) {
   if (!plan) return MOE_ERR_NULL;
   const int64_t max_rows = plan->max_rows;
   const int32_t groups = plan->groups;
@@ -688,30 +704,49 @@ extern "C" int moe_grouped_gemm_fp8_planned(const moe_gemm_plan* plan, const uin
   const bool pk = b_layout == MOE_B_PACKED;
   if (bm == 32 && pk)
     launch<32, true>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                      out_scales);
+                      out_scales, g_out);
   else if (bm == 32)
     launch<32, false>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                      out_scales);
+                      out_scales, g_out);
   else if (bm == 48 && pk)
     launch<48, true>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                      out_scales);
+                      out_scales, g_out);
   else if (bm == 48)
     launch<48, false>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                      out_scales);
+                      out_scales, g_out);
   else if (bm == 64 && pk)
     launch<64, true>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                      out_scales);
+                      out_scales, g_out);
   else if (bm == 64)
     launch<64, false>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                      out_scales);
+                      out_scales, g_out);
   else if (pk)
     launch<128, true>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                      out_scales);
+                      out_scales, g_out);
   else
     launch<128, false>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                      out_scales);
+                      out_scales, g_out);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
+}
+}  // namespace
+
+extern "C" int moe_grouped_gemm_fp8_planned(const moe_gemm_plan* plan, const uint8_t* a, const float* as,
+                                            const int32_t* offsets, const uint8_t* b, int32_t b_layout,
+                                            const float* bs, int32_t N, int32_t K, int32_t epilogue,
+                                            int32_t scale_mode, void* out, int out_dtype, float* out_scales,
+                                            void* stream) {
+  return run_planned(plan, a, as, offsets, b, b_layout, bs, N, K, epilogue, scale_mode, out, out_dtype, out_scales,
+                     nullptr, stream);
+}
+
+extern "C" int moe_grouped_gemm_fp8_swiglu_save(const moe_gemm_plan* plan, const uint8_t* a, const float* as,
+                                                const int32_t* offsets, const uint8_t* b, int32_t b_layout,
+                                                const float* bs, int32_t N, int32_t K, int32_t scale_mode,
+                                                uint8_t* h, float* h_scales, float* g_out, void* stream) {
+  if (!g_out && plan && plan->max_rows > 0) return MOE_ERR_NULL;
+  return run_planned(plan, a, as, offsets, b, b_layout, bs, N, K, MOE_EPI_SWIGLU_QUANT, scale_mode, h, MOE_FP8_E4M3,
+                     h_scales, g_out, stream);
 }
 
 extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int32_t* offsets, int32_t groups,

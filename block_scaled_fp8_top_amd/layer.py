@@ -8,7 +8,8 @@ forward(x) enqueues, on the current stream and without any host synchronisation:
 
 backward(x, dout, bw) enqueues the gradients of the last forward (its buffers must still hold its
 results): moe_combine_backward (dY codes, dw) -> moe_grouped_gemm_fp8 (dY, W2^T: dh) ->
-moe_grouped_gemm_fp8 (A, W1: the GEMM1 output recomputed) -> moe_swiglu_backward_quant (dG codes)
+moe_grouped_gemm_fp8 (A, W1: the GEMM1 output recomputed, unless a training forward kept it) ->
+moe_swiglu_backward_quant (dG codes)
 -> moe_grouped_gemm_fp8 (dG, W1^T: dA) -> moe_combine (dA, weights 1: expert part of dx) ->
 moe_route_backward (dz) -> moe_gate_backward (dx, dWg, db).
 
@@ -146,14 +147,16 @@ class MoELayer:
         self.plan = None   # tile plan of the last forward's expert GEMMs
         self.logits_valid = False   # the last forward wrote self.logits (not the fused sigmoid replay)
         self.device = d
-        self.bwd = None    # backward buffers, allocated by the first backward
+        self.bwd = None    # backward buffers, allocated by the first backward (or training forward)
+        self.g_saved = False   # the last forward kept GEMM1's output in self.bwd["g"]
 
     def forward(self, x: torch.Tensor, replay: Optional[torch.Tensor] = None, record: Optional[torch.Tensor] = None,
-                stream=None, events=None, fused_replay: bool = True) -> torch.Tensor:
+                stream=None, events=None, fused_replay: bool = True, training: bool = False) -> torch.Tensor:
         """``events``: optional list of 8 timing events (torch.cuda.Event), recorded on the launch
         stream before the first stage and after each of the seven stages.  With ``replay`` and a
         sigmoid router the gate projection and the replay run fused (``fused_replay``), and
-        ``self.logits`` is not written."""
+        ``self.logits`` is not written.  ``training``: GEMM1 also keeps its fp32 output for the
+        backward (which then does not recompute it)."""
         T = x.shape[0]
         if T != self.T_max:
             raise ValueError(f"layer buffers are sized for T={self.T_max}, got {T}")
@@ -189,7 +192,9 @@ class MoELayer:
         mark(4)
         M.moe_grouped_gemm_fp8(self.disp.aq, self.disp.as_, self.disp.offsets, w.w1p or w.w1q, w.w1s,
                                epilogue=M.MOE_EPI_SWIGLU_QUANT, out=self.hq, out_scales=self.hs, plan=plan,
-                               stream=stream, pow2=w.pow2)
+                               stream=stream, pow2=w.pow2,
+                               save_g=self._backward_buffers()["g"] if training else None)
+        self.g_saved = training
         mark(5)
         M.moe_grouped_gemm_fp8(self.hq, self.hs, self.disp.offsets, w.w2p or w.w2q, w.w2s, epilogue=M.MOE_EPI_STORE,
                                out_dtype=self.act, out=self.y, plan=plan, stream=stream, pow2=w.pow2)
@@ -243,8 +248,9 @@ class MoELayer:
         M.moe_grouped_gemm_fp8(b["dyq"], b["dys"], off, bw.w2t, bw.w2ts, epilogue=M.MOE_EPI_STORE,
                                out_dtype=torch.float32, out=b["dh"], plan=self.plan, stream=stream, pow2=w.pow2)
         mark(2)
-        M.moe_grouped_gemm_fp8(self.disp.aq, self.disp.as_, off, bw.w1_store, w.w1s, epilogue=M.MOE_EPI_STORE,
-                               out_dtype=torch.float32, out=b["g"], plan=self.plan, stream=stream, pow2=w.pow2)
+        if not self.g_saved:
+            M.moe_grouped_gemm_fp8(self.disp.aq, self.disp.as_, off, bw.w1_store, w.w1s, epilogue=M.MOE_EPI_STORE,
+                                   out_dtype=torch.float32, out=b["g"], plan=self.plan, stream=stream, pow2=w.pow2)
         mark(3)
         M.moe_swiglu_backward_quant(b["dh"], b["g"], pow2=w.pow2, dgq=b["dgq"], dgs=b["dgs"], stream=stream)
         mark(4)

@@ -249,6 +249,17 @@ int moe_grouped_gemm_fp8_planned(const moe_gemm_plan* plan, const uint8_t* a, co
                                  int32_t epilogue, int32_t scale_mode, void* out, int out_dtype, float* out_scales,
                                  void* stream);
 
+/* Training forward of GEMM1 (blog section "FP8 training": the trainer runs this layer and then its
+ * backward, whose SwiGLU derivative needs the GEMM1 output): moe_grouped_gemm_fp8_planned with
+ * epilogue MOE_EPI_SWIGLU_QUANT (h codes into h [max_rows, N/2], scales into h_scales), which in
+ * the same pass also stores the fp32 accumulators G = [gate | up] into g_out [max_rows, N] (rows
+ * past offsets[groups] are not written).  h and h_scales are bitwise those of the plain call.
+ * Errors: as moe_grouped_gemm_fp8_planned (MOE_ERR_NULL for a NULL g_out). */
+int moe_grouped_gemm_fp8_swiglu_save(const moe_gemm_plan* plan, const uint8_t* a, const float* as,
+                                     const int32_t* offsets, const uint8_t* b, int32_t b_layout, const float* bs,
+                                     int32_t N, int32_t K, int32_t scale_mode, uint8_t* h, float* h_scales,
+                                     float* g_out, void* stream);
+
 /* Combine (blog sections "Wide EP" / "Parallelism / EP": expert outputs return to token order).
  *   out[t,:] = sum_{j<k, dest_row[t,j] >= 0} topk_w[t,j] * y[dest_row[t,j],:]  (+ y[*shared_first_row + t,:])
  * accumulated in fp32 in slot order, the shared row last, then rounded to out_dtype.
@@ -298,7 +309,8 @@ int moe_payload_from_host(const void* host, int64_t n, int32_t E, uint8_t* stagi
  * gradient).  Calling order, after a forward whose buffers are still live (dispatch, logits,
  * topk_idx/topk_w, expert rows y):
  *   moe_combine_backward (dY codes, dw) -> moe_grouped_gemm_fp8 (dY x W2^T packed, STORE fp32: dh)
- *   -> moe_grouped_gemm_fp8 (A x W1 packed for STORE, fp32: G, the GEMM1 output recomputed)
+ *   -> [the GEMM1 output G: kept by a forward that ran moe_grouped_gemm_fp8_swiglu_save, else
+ *      recomputed by moe_grouped_gemm_fp8 (A x W1 packed for STORE, fp32)]
  *   -> moe_swiglu_backward_quant (dG codes) -> moe_grouped_gemm_fp8 (dG x W1^T packed, fp32: dA)
  *   -> moe_combine (dA, weights 1, fp32: expert part of dx) -> moe_route_backward (dz)
  *   -> moe_gate_backward (dx = expert part + dz Wg, dWg, db).

@@ -261,7 +261,7 @@ def test_backward_validation(L):
     assert L.moe_route_backward(None, None, None, 0, cfgp, None, None) == OK
     # gate backward: (dz, x, xt, wg, T, H, E, dx_in, dx, dxt, dwg, db, ws, ws_bytes, stream)
     need = L.moe_gate_backward_workspace(16384, 256, 6144)
-    assert need == 16 * (256 * 6144 + 256) * 4 and L.moe_gate_backward_workspace(256, 64, 4096) == 64 * 4096 * 4 + 256
+    assert need == 16 * (256 * 6144 + 256) * 4 and L.moe_gate_backward_workspace(256, 64, 4096) == 4 * (64 * 4096 + 64) * 4
     assert L.moe_gate_backward(P, P, 1, P, 4, 100, 8, None, P, 1, P, None, P, 1 << 20, None) == SHAPE
     assert L.moe_gate_backward(P, P, 2, P, 4, 128, 8, None, P, 1, P, None, P, 1 << 20, None) == DTYPE
     assert L.moe_gate_backward(P, P, 1, P, 16384, 6144, 256, None, P, 1, P, None, P, need - 1, None) == WS
@@ -272,3 +272,13 @@ def test_backward_validation(L):
     assert L.moe_transpose_fp8_blocks(P, P, 2, 256, 256, P, P, None) == ARG          # in place
     assert L.moe_transpose_fp8_blocks(P, None, 2, 256, 256, ctypes.c_void_p(32), P, None) == NULL
     assert L.moe_transpose_fp8_blocks(None, None, 0, 256, 256, None, None, None) == OK
+
+
+def test_swiglu_save_validation(L):
+    P = ctypes.c_void_p(16)
+    plan = M.GemmPlan(128, 4, 1000, P)
+    args = lambda g: (ctypes.byref(plan), P, P, P, P, 1, P, 512, 256, 0, P, P, g, None)
+    assert L.moe_grouped_gemm_fp8_swiglu_save(*args(None)) == NULL
+    assert L.moe_grouped_gemm_fp8_swiglu_save(None, P, P, P, P, 1, P, 512, 256, 0, P, P, P, None) == NULL
+    bad = (ctypes.byref(plan), P, P, P, P, 1, P, 384, 256, 0, P, P, P, None)   # SwiGLU needs N % 256
+    assert L.moe_grouped_gemm_fp8_swiglu_save(*bad) == SHAPE

@@ -216,3 +216,27 @@ def test_layer_backward_full_size_sampled(name, n):
         assert rel_err(host(g["db"]), db_r) < 1e-4
     del lay, gw, bw
     _free()
+
+
+@pytest.mark.parametrize("name,pow2", [("tiny", False), ("prefill_small", False), ("prefill_small", True)])
+def test_training_forward_keeps_g(name, pow2):
+    """GEMM1 of a training forward also stores its fp32 output: h codes and scales unchanged, G
+    bitwise the store-epilogue recompute, and the backward's gradients bitwise unchanged."""
+    cfg = SMALL[name]
+    gw, bw, _ = _layer_pair(cfg, pow2)
+    lay = MoELayer(gw, cfg.T, _act(cfg))
+    x = synth.make_x(cfg, DEV)
+    dout = synth.make_dout(cfg, DEV)
+    lay.forward(x)
+    hq, hs, out = lay.hq.clone(), lay.hs.clone(), lay.out.clone()
+    ref = {k: (v.clone() if v is not None else None) for k, v in lay.backward(x, dout, bw).items()}
+    g_re = lay.bwd["g"].clone()
+    lay.bwd["g"].fill_(float("nan"))
+    lay.forward(x, training=True)
+    n = int(host(lay.disp.offsets)[-1])
+    assert torch.equal(lay.hq[:n], hq[:n]) and torch.equal(lay.hs[:n], hs[:n]) and torch.equal(lay.out, out)
+    assert torch.equal(lay.bwd["g"][:n], g_re[:n])
+    got = lay.backward(x, dout, bw)
+    torch.cuda.synchronize()
+    for key in ("dx", "dwg", "dw", "dz"):
+        assert torch.equal(got[key], ref[key]), key
