@@ -23,6 +23,12 @@ pages give no formula for any of it; the readings used here:
   fp32, then quantised.
 * dx = sum_j dA[dest(t,j)] + dA_shared[t] + dz[t] Wg: the expert part in slot order, the shared
   row last, then the router part.
+* Expert-weight gradients: dW2[e] = sum over e's rows r of dY[r]^T h[r] ([H,F]) and
+  dW1[e] = sum over e's rows of dG[r]^T x[r] ([2F,H]), with h = silu(gate) up in fp32 from the
+  GEMM1 output and x the layer input row (activation dtype) of the row's token.  Both operands of
+  these products contract over rows, so they are quantised in 128x1 blocks: 128 consecutive rows of
+  one expert by one column (the expert's rows zero-padded to a multiple of 128), i.e. 1x128 blocks
+  of the transposed segment; fp32 accumulation, fp32 result.
 * Router backward (selection fixed): sigmoid scores s = 1 / (1 + exp(-z)); softmax scores are
   the full softmax over E.  Renormalised weights w_j = score_j / sum_l score_l:
       sigmoid:  dz_{i_j} = s_j (1 - s_j) (dw_j - sum_l w_l dw_l) / sum_l s_l
@@ -103,6 +109,36 @@ def route_backward(z: np.ndarray, idx: np.ndarray, dw: np.ndarray, cfg: O.Router
     return dz
 
 
+def colwise_segments(a32: np.ndarray, offsets, quant: bool = True, pow2: bool = False):
+    """Per group g: rows offsets[g]..offsets[g+1] of a [rows, C], zero-padded to a multiple of 128
+    rows and transposed to [C, Kg]; with quant, 1x128-quantised along Kg (= 128x1 blocks of a).
+    Returns a list of (codes, scales) or, without quant, of fp64 [C, Kg] values."""
+    out = []
+    a32 = np.asarray(a32, np.float32)
+    C = a32.shape[1]
+    for g in range(len(offsets) - 1):
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        kg = -(-(r1 - r0) // 128) * 128
+        seg = np.zeros((kg, C), np.float32)
+        seg[:r1 - r0] = a32[r0:r1]
+        segT = np.ascontiguousarray(seg.T)
+        out.append(O.moe_quant_fp8_block(segT, 1, pow2) if quant else segT.astype(np.float64))
+    return out
+
+
+def wgrad(dY: np.ndarray, h: np.ndarray, dG: np.ndarray, xrows: np.ndarray, offsets, quant: bool = True,
+          pow2: bool = False):
+    """dW2[g] = dY_g^T h_g ([H,F]) and dW1[g] = dG_g^T x_g ([2F,H]) over each group's rows, in fp64
+    from the 128x1-quantised operands (or the fp32 values without quant)."""
+    def val(seg):
+        return O.dequant_act(*seg) if quant else seg
+    sY, sh = colwise_segments(dY, offsets, quant, pow2), colwise_segments(h, offsets, quant, pow2)
+    sG, sx = colwise_segments(dG, offsets, quant, pow2), colwise_segments(xrows, offsets, quant, pow2)
+    dW2 = np.stack([val(a) @ val(b).T for a, b in zip(sY, sh)])
+    dW1 = np.stack([val(a) @ val(b).T for a, b in zip(sG, sx)])
+    return dW1, dW2
+
+
 def gate_backward(dz: np.ndarray, x: np.ndarray, wg: np.ndarray):
     """dx_router = dz Wg [T,H], dWg = dz^T x [E,H], db = column sums of dz [E] (fp64)."""
     dz = np.asarray(dz, np.float64)
@@ -119,7 +155,7 @@ def _deq_or_keep(a32: np.ndarray, quant: bool, pow2: bool):
 
 def backward_core(dout, x, z, idx, w, dest, offsets, y_act, g1, cfg: O.RouterCfg, wg,
                   w1: Sequence[np.ndarray], w2: Sequence[np.ndarray], F: int, shared: bool,
-                  act: str = "f32", quant: bool = True, pow2: bool = False) -> dict:
+                  act: str = "f32", quant: bool = True, pow2: bool = False, src=None) -> dict:
     """The whole backward over all tokens, in the dispatch (expert-grouped) layout.
 
     w1[g], w2[g]: fp64 values of group g's weights ([2F,H], [H,F]: dequantised codes, or the
@@ -149,8 +185,14 @@ def backward_core(dout, x, z, idx, w, dest, offsets, y_act, g1, cfg: O.RouterCfg
                            dA[int(offsets[E]):int(offsets[E]) + T] if shared else None)
     dz = route_backward(z, idx, dw, cfg)
     dx_r, dwg, db = gate_backward(dz, x, wg)
-    return dict(dY=dY, dYq=dYq, dYs=dYs, dw=dw, dh=dh, dG=dG, dGq=dGq, dGs=dGs, dA=dA,
-                dx_experts=dx_exp, dz=dz, dx_router=dx_r, dx=dx_exp + dx_r, dwg=dwg, db=db)
+    res = dict(dY=dY, dYq=dYq, dYs=dYs, dw=dw, dh=dh, dG=dG, dGq=dGq, dGs=dGs, dA=dA,
+               dx_experts=dx_exp, dz=dz, dx_router=dx_r, dx=dx_exp + dx_r, dwg=dwg, db=db)
+    if src is not None:
+        h = np.asarray(g1, np.float64)
+        h = (h[:, :F] / (1.0 + np.exp(-h[:, :F])) * h[:, F:2 * F]).astype(np.float32)
+        xrows = np.asarray(x, np.float32)[np.asarray(src)[:rows]]
+        res["dW1"], res["dW2"] = wgrad(dY, h, dG, xrows, offsets, quant, pow2)
+    return res
 
 
 def backward_dispatch(layer, fwd: dict, x: np.ndarray, dout: np.ndarray) -> dict:
@@ -160,7 +202,7 @@ def backward_dispatch(layer, fwd: dict, x: np.ndarray, dout: np.ndarray) -> dict
     w2 = [O.dequant_weight(layer.get(g).w2q, layer.get(g).w2s) for g in range(G)]
     return backward_core(dout, x, fwd["z"], fwd["idx"], fwd["w"], fwd["dest"], fwd["offsets"], fwd["y_act"],
                          fwd["g1"], layer.cfg, layer.wg, w1, w2, layer.F, layer.shared, layer.act,
-                         quant=True, pow2=layer.pow2)
+                         quant=True, pow2=layer.pow2, src=fwd["src"])
 
 
 def backward_token(layer, x_rows: np.ndarray, dout_rows: np.ndarray, replay_rows=None) -> dict:

@@ -64,6 +64,8 @@ def torch_reference(cfg, x, wg, b, W1, W2, idx, dout):
     F = cfg.F
     xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
     wgt = torch.tensor(wg, dtype=torch.float64, requires_grad=True)
+    W1t = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in W1]
+    W2t = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in W2]
     bt = torch.tensor(b, dtype=torch.float64, requires_grad=True) if b is not None else None
     z = xt @ wgt.T + (bt if bt is not None else 0.0)
     z.retain_grad()
@@ -74,9 +76,9 @@ def torch_reference(cfg, x, wg, b, W1, W2, idx, dout):
     w.retain_grad()
 
     def ffn(rows, g):
-        a = rows @ torch.tensor(W1[g]).T
+        a = rows @ W1t[g].T
         h = torch.nn.functional.silu(a[:, :F]) * a[:, F:]
-        return h @ torch.tensor(W2[g]).T
+        return h @ W2t[g].T
 
     out = torch.zeros_like(xt)
     for e in range(cfg.E):
@@ -87,8 +89,10 @@ def torch_reference(cfg, x, wg, b, W1, W2, idx, dout):
     if cfg.shared:
         out = out + ffn(xt, cfg.E)
     (out * torch.tensor(dout, dtype=torch.float64)).sum().backward()
+    zero = lambda t, a: t.grad.numpy() if t.grad is not None else np.zeros_like(a)
     return dict(dx=xt.grad.numpy(), dwg=wgt.grad.numpy(), db=None if bt is None else bt.grad.numpy(),
-                dw=w.grad.numpy(), dz=z.grad.numpy(), w=w.detach().numpy(), out=out.detach().numpy())
+                dw=w.grad.numpy(), dz=z.grad.numpy(), w=w.detach().numpy(), out=out.detach().numpy(),
+                dW1=np.stack([zero(t, a) for t, a in zip(W1t, W1)]), dW2=np.stack([zero(t, a) for t, a in zip(W2t, W2)]))
 
 
 def real_forward_rows(cfg, x, idx, W1, W2):
@@ -104,7 +108,7 @@ def real_forward_rows(cfg, x, idx, W1, W2):
             g1[r0:r1] = a
             h = a[:, :cfg.F] / (1 + np.exp(-a[:, :cfg.F])) * a[:, cfg.F:]
             y[r0:r1] = h @ W2[g].T
-    return offsets, dest, g1, y
+    return offsets, dest, g1, y, src
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -118,11 +122,12 @@ def test_unquantised_backward_equals_autograd(name, with_bias):
     idx, _ = O.moe_route(z.astype(np.float32), rcfg(cfg))
     dout = dout_for(cfg)
     ref = torch_reference(cfg, x, wg, b, W1, W2, idx, dout)
-    offsets, dest, g1, y = real_forward_rows(cfg, x, idx, W1, W2)
+    offsets, dest, g1, y, src = real_forward_rows(cfg, x, idx, W1, W2)
     got = B.backward_core(dout, x, z, idx, ref["w"], dest, offsets, y, g1, rcfg(cfg), wg, W1, W2, cfg.F,
-                          cfg.shared, quant=False)
-    # the only rounding on the oracle side: dY = fp32(w) * fp32(dout), i.e. 2^-24 relative
-    for key in ("dw", "dz", "dx", "dwg"):
+                          cfg.shared, quant=False, src=src)
+    # the oracle's own roundings: dY = fp32(w) * fp32(dout), and h, dG rounded to fp32 (the
+    # weight gradients' operands), i.e. ~2^-24 relative
+    for key in ("dw", "dz", "dx", "dwg", "dW1", "dW2"):
         assert L.rel_err(got[key], ref[key]) < 1e-6, (key, L.rel_err(got[key], ref[key]))
     if b is not None:
         assert L.rel_err(got["db"], ref["db"]) < 1e-6
@@ -170,12 +175,23 @@ def test_quantised_backward_codes_and_error(name, pow2):
     w1 = [O.dequant_weight(lay.get(g).w1q, lay.get(g).w1s) for g in range(G)]
     w2 = [O.dequant_weight(lay.get(g).w2q, lay.get(g).w2s) for g in range(G)]
     real = B.backward_core(dout, x, fwd["z"], fwd["idx"], fwd["w"], fwd["dest"], fwd["offsets"], fwd["y_act"],
-                           fwd["g1"], lay.cfg, lay.wg, w1, w2, cfg.F, cfg.shared, quant=False)
-    for key in ("dh", "dA", "dx"):
+                           fwd["g1"], lay.cfg, lay.wg, w1, w2, cfg.F, cfg.shared, quant=False, src=fwd["src"])
+    for key in ("dh", "dA", "dx", "dW1", "dW2"):
         e = L.rel_err(got[key], real[key])
-        assert e < 6e-2, (key, e)
+        # one FP8 rounding per operand (2^-4 relative, coarser in the subnormal range); the weight
+        # gradients sum few rows per expert here, so their max error is less averaged
+        assert e < (1e-1 if key.startswith("dW") else 6e-2), (key, e)
     # quantisation changed something (the two paths are not the same computation)
-    assert L.rel_err(got["dA"], real["dA"]) > 1e-4
+    assert L.rel_err(got["dA"], real["dA"]) > 1e-4 and L.rel_err(got["dW1"], real["dW1"]) > 1e-4
+    # the 128x1 operand codes of dW2 are the pinned 1x128 rule applied to the transposed,
+    # zero-padded segments of the fp32 dY (bitwise reproducible: one product per element)
+    seg = B.colwise_segments(dY, fwd["offsets"], True, pow2)
+    g0 = next(g for g in range(len(fwd["offsets"]) - 1) if fwd["offsets"][g + 1] > fwd["offsets"][g])
+    r0, r1 = int(fwd["offsets"][g0]), int(fwd["offsets"][g0 + 1])
+    pad = np.zeros((-(-(r1 - r0) // 128) * 128, cfg.H), np.float32)
+    pad[:r1 - r0] = dY[r0:r1]
+    q0, s0 = O.moe_quant_fp8_block(np.ascontiguousarray(pad.T), 1, pow2)
+    assert np.array_equal(seg[g0][0], q0) and np.array_equal(seg[g0][1], s0)
     assert np.array_equal(got["dw"], real["dw"]) and np.array_equal(got["dz"], real["dz"])
 
 
