@@ -35,7 +35,8 @@ EXPORTED = ("moe_gate_logits", "moe_route", "moe_replay_route", "moe_replay_gate
             "moe_grouped_gemm_fp8_planned", "moe_grouped_gemm_fp8_swiglu_save", "moe_grouped_gemm_fp8", "moe_combine", "moe_payload_bytes",
             "moe_payload_pack", "moe_payload_unpack", "moe_payload_to_host", "moe_payload_from_host",
             "moe_combine_backward", "moe_swiglu_backward_quant", "moe_route_backward", "moe_gate_backward",
-            "moe_gate_backward_workspace", "moe_transpose_fp8_blocks",
+            "moe_gate_backward_workspace", "moe_transpose_fp8_blocks", "moe_wgrad_max_tiles", "moe_wgrad_tiles",
+            "moe_colwise_quant_rows", "moe_colwise_quant_swiglu", "moe_grouped_gemm_wgrad",
             "moe_workspace_bytes", "moe_status_str", "moe_version")
 
 
@@ -96,7 +97,12 @@ def lib():
         "moe_payload_unpack": [P, I64, I32, P, P],
         "moe_payload_to_host": [P, I64, I32, P, P, P, P],
         "moe_payload_from_host": [P, I64, I32, P, P, P],
-        "moe_combine_backward": [P, ctypes.c_int, P, ctypes.c_int, P, P, I64, I32, I32, P, I32, P, P, P, P],
+        "moe_combine_backward": [P, ctypes.c_int, P, ctypes.c_int, P, P, I64, I32, I32, P, I32, P, P, P, P, P],
+        "moe_wgrad_max_tiles": [I64, I32],
+        "moe_wgrad_tiles": [P, I32, P, P],
+        "moe_colwise_quant_rows": [P, ctypes.c_int, P, P, P, P, I32, I64, I32, I32, P, P, P],
+        "moe_colwise_quant_swiglu": [P, P, I32, P, P, I32, I64, I32, P, P, P],
+        "moe_grouped_gemm_wgrad": [P, P, I32, P, P, I32, P, I32, I64, I32, P, P],
         "moe_swiglu_backward_quant": [P, P, I64, I32, I32, P, P, P],
         "moe_route_backward": [P, P, P, I64, cfgp, P, P],
         "moe_gate_backward": [P, P, ctypes.c_int, P, I64, I32, I32, P, P, ctypes.c_int, P, P, P, SZ, P],
@@ -114,6 +120,7 @@ def lib():
     L.moe_packed_weight_bytes.restype = ctypes.c_size_t
     L.moe_payload_bytes.restype = ctypes.c_size_t
     L.moe_gate_backward_workspace.restype = ctypes.c_size_t
+    L.moe_wgrad_max_tiles.restype = ctypes.c_int64
     L.moe_status_str.restype = ctypes.c_char_p
     L.moe_version.restype = ctypes.c_char_p
     _lib = L
@@ -548,9 +555,10 @@ def moe_payload_from_host(host: torch.Tensor, shape, num_experts: int, staging: 
 # ----------------------------------------------------------------------------- backward
 def moe_combine_backward(dout: torch.Tensor, y: torch.Tensor, dest_row: torch.Tensor, topk_w: torch.Tensor,
                          shared_first_row: Optional[torch.Tensor] = None, pow2: bool = False, dyq=None, dys=None,
-                         dw=None, stream=None):
+                         dw=None, row_w: Optional[torch.Tensor] = None, stream=None):
     """dY = w * dout per slot row (dout for the shared row), 1x128-quantised into (dyq [rows,H] uint8,
-    dys [rows,H/128] fp32) with rows = y.shape[0], and dw[t,j] = <dout[t], y[dest_row[t,j]]> (fp32 [T,k])."""
+    dys [rows,H/128] fp32) with rows = y.shape[0], and dw[t,j] = <dout[t], y[dest_row[t,j]]> (fp32 [T,k]).
+    row_w: optional fp32 [rows] that receives each written row's factor."""
     _dev(dout, "dout", (torch.float32, torch.bfloat16))
     _dev(y, "y", (torch.float32, torch.bfloat16))
     T, k = dest_row.shape
@@ -565,10 +573,12 @@ def moe_combine_backward(dout: torch.Tensor, y: torch.Tensor, dest_row: torch.Te
     dys = torch.empty((rows, H // 128), dtype=torch.float32, device=dev) if dys is None else \
         _dev(dys, "dys", torch.float32, (rows, H // 128))
     dw = torch.empty((T, k), dtype=torch.float32, device=dev) if dw is None else _dev(dw, "dw", torch.float32, (T, k))
+    if row_w is not None:
+        _dev(row_w, "row_w", torch.float32, (rows,))
     mode = MOE_SCALE_POW2 if pow2 else MOE_SCALE_AMAX
     _check(lib().moe_combine_backward(_p(dout), _act_code(dout), _p(y), _act_code(y), _p(dest_row), _p(topk_w), T, k, H,
-                                      _p(shared_first_row), mode, _p(dyq), _p(dys), _p(dw), _stream(stream)),
-           "moe_combine_backward")
+                                      _p(shared_first_row), mode, _p(dyq), _p(dys), _p(dw), _p(row_w),
+                                      _stream(stream)), "moe_combine_backward")
     return dyq, dys, dw
 
 
@@ -636,6 +646,89 @@ def moe_gate_backward(dz: torch.Tensor, x: torch.Tensor, wg: torch.Tensor, dx_in
                                    _p(dwg), _p(db), _p(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream)), "moe_gate_backward")
     return dx, dwg, db
+
+
+def wgrad_max_tiles(max_rows: int, groups: int) -> int:
+    """128-row tiles the weight-gradient operands are sized for."""
+    return int(lib().moe_wgrad_max_tiles(max_rows, groups))
+
+
+def moe_wgrad_tiles(offsets: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """tile_first [G+1] int32: each group's first 128-row tile of the weight-gradient operands."""
+    G = offsets.shape[0] - 1
+    _dev(offsets, "offsets", torch.int32, (G + 1,))
+    out = torch.empty(G + 1, dtype=torch.int32, device=offsets.device) if out is None else \
+        _dev(out, "tile_first", torch.int32, (G + 1,))
+    _check(lib().moe_wgrad_tiles(_p(offsets), G, _p(out), _stream(stream)), "moe_wgrad_tiles")
+    return out
+
+
+def _colwise_out(C, max_tiles, qt, st, dev):
+    qt = torch.empty((C, max_tiles * 128), dtype=FP8, device=dev) if qt is None else \
+        _dev(qt, "qt", FP8, (C, max_tiles * 128))
+    st = torch.empty((C, max_tiles), dtype=torch.float32, device=dev) if st is None else \
+        _dev(st, "st", torch.float32, (C, max_tiles))
+    return qt, st
+
+
+def moe_colwise_quant_rows(x: torch.Tensor, offsets: torch.Tensor, tile_first: torch.Tensor, max_tiles: int,
+                           src_row: Optional[torch.Tensor] = None, row_scale: Optional[torch.Tensor] = None,
+                           pow2: bool = False, qt=None, st=None, stream=None):
+    """128x1-quantised transposed operand: column c, row r = row_scale[r] * x[src_row[r], c], each
+    group's rows in whole 128-row tiles.  Returns (codes [C, max_tiles*128], scales [C, max_tiles])."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    C = x.shape[1]
+    G = offsets.shape[0] - 1
+    _dev(offsets, "offsets", torch.int32, (G + 1,))
+    _dev(tile_first, "tile_first", torch.int32, (G + 1,))
+    if src_row is not None:
+        _dev(src_row, "src_row", torch.int32)
+    if row_scale is not None:
+        _dev(row_scale, "row_scale", torch.float32)
+    qt, st = _colwise_out(C, max_tiles, qt, st, x.device)
+    mode = MOE_SCALE_POW2 if pow2 else MOE_SCALE_AMAX
+    _check(lib().moe_colwise_quant_rows(_p(x), _act_code(x), _p(src_row), _p(row_scale), _p(offsets), _p(tile_first),
+                                        G, max_tiles, C, mode, _p(qt), _p(st), _stream(stream)),
+           "moe_colwise_quant_rows")
+    return qt, st
+
+
+def moe_colwise_quant_swiglu(g: torch.Tensor, offsets: torch.Tensor, tile_first: torch.Tensor, max_tiles: int,
+                             dh: Optional[torch.Tensor] = None, pow2: bool = False, qt=None, st=None, stream=None):
+    """128x1-quantised transposed h = silu(gate) * up (dh None; C = F) or dG = [dgate | dup] (C = 2F)
+    from the GEMM1 output g [rows, 2F] fp32."""
+    rows, F2 = g.shape
+    F = F2 // 2
+    _dev(g, "g", torch.float32)
+    if dh is not None:
+        _dev(dh, "dh", torch.float32, (rows, F))
+    G = offsets.shape[0] - 1
+    _dev(offsets, "offsets", torch.int32, (G + 1,))
+    _dev(tile_first, "tile_first", torch.int32, (G + 1,))
+    qt, st = _colwise_out(F2 if dh is not None else F, max_tiles, qt, st, g.device)
+    mode = MOE_SCALE_POW2 if pow2 else MOE_SCALE_AMAX
+    _check(lib().moe_colwise_quant_swiglu(_p(g), _p(dh), F, _p(offsets), _p(tile_first), G, max_tiles, mode, _p(qt),
+                                          _p(st), _stream(stream)), "moe_colwise_quant_swiglu")
+    return qt, st
+
+
+def moe_grouped_gemm_wgrad(a: torch.Tensor, as_: torch.Tensor, b: torch.Tensor, bs: torch.Tensor,
+                           tile_first: torch.Tensor, max_tiles: int, pow2: bool = False, out=None, stream=None):
+    """out[g] = A_g B_g^T over group g's tiles: a [M, max_tiles*128], b [N, max_tiles*128] codes with
+    scales [M, max_tiles], [N, max_tiles] -> fp32 [G, M, N]."""
+    M, N = a.shape[0], b.shape[0]
+    G = tile_first.shape[0] - 1
+    _dev(a, "a", FP8, (M, max_tiles * 128))
+    _dev(b, "b", FP8, (N, max_tiles * 128))
+    _dev(as_, "as", torch.float32, (M, max_tiles))
+    _dev(bs, "bs", torch.float32, (N, max_tiles))
+    _dev(tile_first, "tile_first", torch.int32, (G + 1,))
+    out = torch.empty((G, M, N), dtype=torch.float32, device=a.device) if out is None else \
+        _dev(out, "out", torch.float32, (G, M, N))
+    mode = MOE_SCALE_POW2 if pow2 else MOE_SCALE_AMAX
+    _check(lib().moe_grouped_gemm_wgrad(_p(a), _p(as_), M, _p(b), _p(bs), N, _p(tile_first), G, max_tiles, mode,
+                                        _p(out), _stream(stream)), "moe_grouped_gemm_wgrad")
+    return out
 
 
 def moe_transpose_fp8_blocks(q: torch.Tensor, scales: torch.Tensor, qt=None, scales_t=None, stream=None):

@@ -67,7 +67,7 @@ template <bool DBF16, bool YBF16, bool POW2>
 __global__ __launch_bounds__(CB_THREADS) void combine_backward_kernel(
     const void* __restrict__ dout, const void* __restrict__ y, const int32_t* __restrict__ dest,
     const float* __restrict__ w, int k, int H, const int32_t* __restrict__ shared_first_row,
-    uint8_t* __restrict__ dyq, float* __restrict__ dys, float* __restrict__ dw) {
+    uint8_t* __restrict__ dyq, float* __restrict__ dys, float* __restrict__ dw, float* __restrict__ row_w) {
   __shared__ float red[CB_THREADS / 64][CB_KMAX];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x, sub = tid & 15;
@@ -81,6 +81,9 @@ __global__ __launch_bounds__(CB_THREADS) void combine_backward_kernel(
     acc[j] = 0.0f;
   }
   const int64_t srow = shared_first_row ? (int64_t)(*shared_first_row) + t : -1;
+  // each written row's factor, for the weight gradients' dY operand
+  if (row_w && tid < k && dest[t * k + tid] >= 0) row_w[dest[t * k + tid]] = w[t * k + tid];
+  if (row_w && tid == 64 && srow >= 0) row_w[srow] = 1.0f;
   for (int c = tid * 8; c < H; c += CB_THREADS * 8) {
     // 16-lane groups are whole blocks (H % 128 == 0), so a group is entirely in or out of range
     float d[8];
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(256) void transpose_blocks_kernel(const uint8_t* __
 extern "C" int moe_combine_backward(const void* dout, int dout_dtype, const void* y, int y_dtype,
                                     const int32_t* dest_row, const float* topk_w, int64_t T, int32_t k, int32_t H,
                                     const int32_t* shared_first_row, int32_t scale_mode, uint8_t* dyq, float* dys,
-                                    float* dw, void* stream) {
+                                    float* dw, float* row_w, void* stream) {
   if (T < 0 || k < 1 || k > CB_KMAX || H < 128 || H % 128 != 0) return MOE_ERR_SHAPE;
   if ((dout_dtype != MOE_BF16 && dout_dtype != MOE_F32) || (y_dtype != MOE_BF16 && y_dtype != MOE_F32))
     return MOE_ERR_DTYPE;
@@ -279,7 +282,7 @@ extern "C" int moe_combine_backward(const void* dout, int dout_dtype, const void
   const bool db = dout_dtype == MOE_BF16, yb = y_dtype == MOE_BF16, p2 = scale_mode == MOE_SCALE_POW2;
 #define CB_LAUNCH(A, B, C)                                                                                    \
   combine_backward_kernel<A, B, C><<<(unsigned)T, CB_THREADS, 0, st>>>(dout, y, dest_row, topk_w, k, H,     \
-                                                                      shared_first_row, dyq, dys, dw)
+                                                                      shared_first_row, dyq, dys, dw, row_w)
   if (db && yb) { if (p2) CB_LAUNCH(true, true, true); else CB_LAUNCH(true, true, false); }
   else if (db) { if (p2) CB_LAUNCH(true, false, true); else CB_LAUNCH(true, false, false); }
   else if (yb) { if (p2) CB_LAUNCH(false, true, true); else CB_LAUNCH(false, true, false); }

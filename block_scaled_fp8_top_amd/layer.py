@@ -218,21 +218,40 @@ class MoELayer:
             ones=torch.ones((T, k), dtype=f32, device=d), dx_exp=torch.empty((T, H), dtype=f32, device=d),
             dz=torch.empty((T, E), dtype=f32, device=d), dx=torch.empty((T, H), dtype=self.act, device=d),
             dwg=torch.empty((E, H), dtype=f32, device=d), db=torch.empty(E, dtype=f32, device=d),
-            gws=torch.empty(max(M.gate_backward_workspace(T, E, H), 1), dtype=torch.uint8, device=d))
+            gws=torch.empty(max(M.gate_backward_workspace(T, E, H), 1), dtype=torch.uint8, device=d),
+            row_w=torch.empty(R, dtype=f32, device=d))
         return self.bwd
 
-    def backward(self, x: torch.Tensor, dout: torch.Tensor, bw: BackwardWeights, stream=None, events=None) -> dict:
+    def _wgrad_buffers(self):
+        b = self._backward_buffers()
+        if "dW1" in b:
+            return b
+        w, d = self.w, self.device
+        H, F, G = w.H, w.F, w.groups
+        mt = M.wgrad_max_tiles(self.max_rows, G)
+        kp, f32, u8 = mt * 128, torch.float32, torch.uint8
+        b.update(max_tiles=mt, tile_first=torch.empty(G + 1, dtype=torch.int32, device=d),
+                 dYt=torch.empty((H, kp), dtype=u8, device=d), dYts=torch.empty((H, mt), dtype=f32, device=d),
+                 ht=torch.empty((F, kp), dtype=u8, device=d), hts=torch.empty((F, mt), dtype=f32, device=d),
+                 dGt=torch.empty((2 * F, kp), dtype=u8, device=d), dGts=torch.empty((2 * F, mt), dtype=f32, device=d),
+                 xt=torch.empty((H, kp), dtype=u8, device=d), xts=torch.empty((H, mt), dtype=f32, device=d),
+                 dW1=torch.empty((G, 2 * F, H), dtype=f32, device=d), dW2=torch.empty((G, H, F), dtype=f32, device=d))
+        return b
+
+    def backward(self, x: torch.Tensor, dout: torch.Tensor, bw: BackwardWeights, stream=None, events=None,
+                 weight_grads: bool = False) -> dict:
         """Gradients of the last forward (x is that forward's input) for the output gradient dout [T,H]
         (activation dtype): dx [T,H] (activation dtype), dwg [E,H] and db [E] (None without a bias)
-        in fp32, plus the routing-weight gradient dw [T,k] and the logit gradient dz [T,E].  The
+        in fp32, plus the routing-weight gradient dw [T,k] and the logit gradient dz [T,E]; with
+        ``weight_grads`` also the expert-weight gradients dW1 [G,2F,H] and dW2 [G,H,F] (fp32).  The
         returned tensors are views of buffers reused by the next backward.  ``events``: optional
-        list of 9 timing events recorded before the first and after each of the 8 stages."""
+        list of 9 timing events (11 with weight_grads) recorded before the first and after each stage."""
         if self.plan is None:
             raise RuntimeError("backward needs a forward first")
         if x.shape[0] != self.T_max or tuple(dout.shape) != (self.T_max, self.w.H):
             raise ValueError("x / dout do not match the layer's buffers")
         w = self.w
-        b = self._backward_buffers()
+        b = self._wgrad_buffers() if weight_grads else self._backward_buffers()
         st = torch.cuda.current_stream() if stream is None else stream
 
         def mark(i):
@@ -243,7 +262,7 @@ class MoELayer:
         shared_row = off[w.E:w.E + 1] if w.shared else None
         mark(0)
         M.moe_combine_backward(dout, self.y, self.disp.dest_row, self.wts, shared_row, pow2=w.pow2, dyq=b["dyq"],
-                               dys=b["dys"], dw=b["dw"], stream=stream)
+                               dys=b["dys"], dw=b["dw"], row_w=b["row_w"] if weight_grads else None, stream=stream)
         mark(1)
         M.moe_grouped_gemm_fp8(b["dyq"], b["dys"], off, bw.w2t, bw.w2ts, epilogue=M.MOE_EPI_STORE,
                                out_dtype=torch.float32, out=b["dh"], plan=self.plan, stream=stream, pow2=w.pow2)
@@ -268,4 +287,22 @@ class MoELayer:
         M.moe_gate_backward(b["dz"], x, w.wg, dx_in=b["dx_exp"], dx_dtype=self.act, dx=b["dx"], dwg=b["dwg"],
                             db=b["db"], want_db=w.bias is not None, workspace=b["gws"], stream=stream)
         mark(8)
-        return dict(dx=b["dx"], dwg=b["dwg"], db=b["db"] if w.bias is not None else None, dw=b["dw"], dz=b["dz"])
+        res = dict(dx=b["dx"], dwg=b["dwg"], db=b["db"] if w.bias is not None else None, dw=b["dw"], dz=b["dz"])
+        if weight_grads:
+            # 128x1 operands over each expert's rows, then one fp32 matrix per expert
+            mt, tf, src = b["max_tiles"], b["tile_first"], self.disp.src_token
+            M.moe_wgrad_tiles(off, out=tf, stream=stream)
+            M.moe_colwise_quant_rows(dout, off, tf, mt, src_row=src, row_scale=b["row_w"], pow2=w.pow2, qt=b["dYt"],
+                                     st=b["dYts"], stream=stream)
+            M.moe_colwise_quant_swiglu(b["g"], off, tf, mt, pow2=w.pow2, qt=b["ht"], st=b["hts"], stream=stream)
+            M.moe_colwise_quant_swiglu(b["g"], off, tf, mt, dh=b["dh"], pow2=w.pow2, qt=b["dGt"], st=b["dGts"],
+                                       stream=stream)
+            M.moe_colwise_quant_rows(x, off, tf, mt, src_row=src, pow2=w.pow2, qt=b["xt"], st=b["xts"], stream=stream)
+            mark(9)
+            M.moe_grouped_gemm_wgrad(b["dYt"], b["dYts"], b["ht"], b["hts"], tf, mt, pow2=w.pow2, out=b["dW2"],
+                                     stream=stream)
+            M.moe_grouped_gemm_wgrad(b["dGt"], b["dGts"], b["xt"], b["xts"], tf, mt, pow2=w.pow2, out=b["dW1"],
+                                     stream=stream)
+            mark(10)
+            res.update(dW1=b["dW1"], dW2=b["dW2"])
+        return res

@@ -325,12 +325,13 @@ int moe_payload_from_host(const void* host, int64_t n, int32_t E, uint8_t* stagi
  * tree reduction; 0 for a slot with dest_row -1, whose dY row is not written).
  *   dout [T,H] in dout_dtype, y [rows,H] in y_dtype (MOE_F32 or MOE_BF16: the forward's expert rows
  *   as the combine read them); dest_row, topk_w [T,k] from the forward; shared_first_row NULL or a
- *   device int32 (&offsets[E]); dw [T,k] fp32 (out).
+ *   device int32 (&offsets[E]); dw [T,k] fp32 (out); row_w NULL or [rows] fp32 (out): each written
+ *   row's factor (topk_w of its slot, 1 for a shared row), for the weight gradients.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (H % 128, k > 16), MOE_ERR_DTYPE, MOE_ERR_ARG (scale_mode),
  * MOE_ERR_HIP.  T == 0 is a no-op. */
 int moe_combine_backward(const void* dout, int dout_dtype, const void* y, int y_dtype, const int32_t* dest_row,
                          const float* topk_w, int64_t T, int32_t k, int32_t H, const int32_t* shared_first_row,
-                         int32_t scale_mode, uint8_t* dyq, float* dys, float* dw, void* stream);
+                         int32_t scale_mode, uint8_t* dyq, float* dys, float* dw, float* row_w, void* stream);
 
 /* SwiGLU backward and 1x128 quantisation of the result.  With G = [gate | up] the GEMM1 output
  * [rows, 2F] fp32 and dh [rows, F] fp32:  s = sigmoid(gate), dgate = dh * up * s * (1 + gate * (1 - s)),
@@ -363,6 +364,37 @@ int moe_gate_backward(const float* dz, const void* x, int x_dtype, const float* 
                       const float* dx_in, void* dx, int dx_dtype, float* dwg, float* db, void* workspace,
                       size_t workspace_bytes, void* stream);
 size_t moe_gate_backward_workspace(int64_t T, int32_t E, int32_t H);
+
+/* Expert-weight gradients (blog section "FP8 training"): dW2[e] = sum over e's rows of dY^T h
+ * ([H,F]) and dW1[e] = sum over e's rows of dG^T x ([2F,H]).  Both operands contract over an expert's
+ * rows, so they are quantised in 128x1 blocks (128 consecutive rows of one expert x one column) and
+ * stored transposed, operand[c][k] with k a padded row: expert e's rows fill whole 128-row tiles
+ * tile_first[e] .. tile_first[e+1]-1 (zero-padded), k = tile * 128 + row within the tile.  Buffers
+ * are sized for max_tiles = moe_wgrad_max_tiles(max_rows, groups) tiles: codes [C, max_tiles*128]
+ * e4m3, scales [C, max_tiles] fp32 (tiles past tile_first[groups] are not written).
+ *   moe_wgrad_tiles: tile_first [groups+1] int32 (device, out) from the dispatch offsets [groups+1].
+ *   moe_colwise_quant_rows: column c, row r of the operand = row_scale[r] * x[src_row[r], c]
+ *     (x [*, C] in x_dtype; src_row NULL = identity; row_scale NULL = 1): dY from dout with the
+ *     dispatch's src_token and moe_combine_backward's row_w, or x itself with src_token.
+ *   moe_colwise_quant_swiglu: from the GEMM1 output g [rows, 2F] fp32, h = silu(gate) * up (C = F,
+ *     dh NULL) or, with dh [rows, F] fp32, dG = [dgate | dup] as in moe_swiglu_backward_quant (C = 2F).
+ *   moe_grouped_gemm_wgrad: c[e] = A_e B_e^T ([groups, M, N] fp32, every expert written; zeros for an
+ *     expert with no rows), A [M, max_tiles*128] and B [N, max_tiles*128] codes with scales
+ *     [M or N, max_tiles]; amax scales promoted per 128-row step, power-of-two scales applied by
+ *     the matrix cores.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (C, M, N % 128; groups), MOE_ERR_DTYPE, MOE_ERR_ARG
+ * (scale_mode), MOE_ERR_HIP.  moe_wgrad_max_tiles returns 0 for invalid sizes. */
+int64_t moe_wgrad_max_tiles(int64_t max_rows, int32_t groups);
+int moe_wgrad_tiles(const int32_t* offsets, int32_t groups, int32_t* tile_first, void* stream);
+int moe_colwise_quant_rows(const void* x, int x_dtype, const int32_t* src_row, const float* row_scale,
+                           const int32_t* offsets, const int32_t* tile_first, int32_t groups, int64_t max_tiles,
+                           int32_t C, int32_t scale_mode, uint8_t* qt, float* st, void* stream);
+int moe_colwise_quant_swiglu(const float* g, const float* dh, int32_t F, const int32_t* offsets,
+                             const int32_t* tile_first, int32_t groups, int64_t max_tiles, int32_t scale_mode,
+                             uint8_t* qt, float* st, void* stream);
+int moe_grouped_gemm_wgrad(const uint8_t* a, const float* as, int32_t M, const uint8_t* b, const float* bs, int32_t N,
+                           const int32_t* tile_first, int32_t groups, int64_t max_tiles, int32_t scale_mode, float* c,
+                           void* stream);
 
 /* Transpose of 128x128-block FP8 weights with their scales: qt[g][c][r] = q[g][r][c],
  * scales_t[g][cb][rb] = scales[g][rb][cb]; q [groups,N,K] -> qt [groups,K,N] (N, K multiples of 128).

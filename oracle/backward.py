@@ -237,3 +237,32 @@ def backward_token(layer, x_rows: np.ndarray, dout_rows: np.ndarray, replay_rows
     dz = route_backward(z, idx, dw, layer.cfg)
     dx_r = dz @ np.asarray(layer.wg, np.float64)
     return dict(z=z, idx=idx, w=w, dw=dw, dz=dz, dx_experts=dx_exp, dx_router=dx_r, dx=dx_exp + dx_r)
+
+
+def wgrad_expert(layer, x: np.ndarray, dout: np.ndarray, e: int, replay=None):
+    """dW1 and dW2 of expert e alone over a whole batch (x, dout [T,H]): the batch is routed, e's rows
+    are formed in dispatch order (ascending token) and evaluated row by row (each row depends on its
+    own token only), then contracted as in ``wgrad``.  Returns (dW1 [2F,H], dW2 [H,F]) fp64."""
+    import oracle.layer as OL
+    E, F = layer.E, layer.F
+    z = O.moe_gate_logits(x, layer.wg, layer.bias)
+    idx, w, _ = OL.route_or_replay(layer, z, replay)
+    dout32 = np.asarray(dout, np.float32)
+    if e == E:
+        toks = np.arange(x.shape[0])
+        fac = np.ones(len(toks), np.float32)
+    else:
+        t_, j_ = np.nonzero(idx == e)
+        order = np.argsort(t_, kind="stable")
+        toks, fac = t_[order], np.asarray(w, np.float32)[t_[order], j_[order]]
+    ew = layer.get(e)
+    xr = np.asarray(x, np.float32)[toks]
+    xq, xs = O.moe_quant_fp8_block(xr, 1, layer.pow2)
+    g1 = O.dequant_act(xq, xs) @ O.dequant_weight(ew.w1q, ew.w1s).T
+    h = O.swiglu(g1, F)
+    dY = (fac[:, None] * dout32[toks]).astype(np.float32)
+    dYq, dYs = O.moe_quant_fp8_block(dY, 1, layer.pow2)
+    dh = O.dequant_act(dYq, dYs) @ O.dequant_weight(ew.w2q, ew.w2s)
+    dG = swiglu_backward(dh, g1, F)
+    dW1, dW2 = wgrad(dY, h, dG, xr, [0, len(toks)], True, layer.pow2)
+    return dW1[0], dW2[0]

@@ -241,13 +241,13 @@ def test_product_package_does_not_touch_the_oracle():
 def test_backward_validation(L):
     P = ctypes.c_void_p(16)   # never dereferenced: every case fails (or is empty) before a launch
     cfgp = ctypes.byref(_cfg())
-    # combine backward: (dout, dt, y, yt, dest, w, T, k, H, shared, mode, dyq, dys, dw, stream)
-    assert L.moe_combine_backward(P, 1, P, 1, P, P, 4, 17, 256, None, 0, P, P, P, None) == SHAPE   # k > 16
-    assert L.moe_combine_backward(P, 1, P, 1, P, P, 4, 8, 200, None, 0, P, P, P, None) == SHAPE    # H % 128
-    assert L.moe_combine_backward(P, 2, P, 1, P, P, 4, 8, 256, None, 0, P, P, P, None) == DTYPE
-    assert L.moe_combine_backward(P, 1, P, 1, P, P, 4, 8, 256, None, 2, P, P, P, None) == ARG
-    assert L.moe_combine_backward(None, 1, P, 1, P, P, 4, 8, 256, None, 0, P, P, P, None) == NULL
-    assert L.moe_combine_backward(None, 1, None, 1, None, None, 0, 8, 256, None, 0, None, None, None, None) == OK
+    # combine backward: (dout, dt, y, yt, dest, w, T, k, H, shared, mode, dyq, dys, dw, row_w, stream)
+    assert L.moe_combine_backward(P, 1, P, 1, P, P, 4, 17, 256, None, 0, P, P, P, None, None) == SHAPE   # k > 16
+    assert L.moe_combine_backward(P, 1, P, 1, P, P, 4, 8, 200, None, 0, P, P, P, None, None) == SHAPE    # H % 128
+    assert L.moe_combine_backward(P, 2, P, 1, P, P, 4, 8, 256, None, 0, P, P, P, None, None) == DTYPE
+    assert L.moe_combine_backward(P, 1, P, 1, P, P, 4, 8, 256, None, 2, P, P, P, None, None) == ARG
+    assert L.moe_combine_backward(None, 1, P, 1, P, P, 4, 8, 256, None, 0, P, P, P, None, None) == NULL
+    assert L.moe_combine_backward(None, 1, None, 1, None, None, 0, 8, 256, None, 0, None, None, None, None, None) == OK
     # SwiGLU backward: (dh, g, rows, F, mode, dgq, dgs, stream)
     assert L.moe_swiglu_backward_quant(P, P, 4, 100, 0, P, P, None) == SHAPE
     assert L.moe_swiglu_backward_quant(P, P, 4, 128, 3, P, P, None) == ARG
@@ -282,3 +282,24 @@ def test_swiglu_save_validation(L):
     assert L.moe_grouped_gemm_fp8_swiglu_save(None, P, P, P, P, 1, P, 512, 256, 0, P, P, P, None) == NULL
     bad = (ctypes.byref(plan), P, P, P, P, 1, P, 384, 256, 0, P, P, P, None)   # SwiGLU needs N % 256
     assert L.moe_grouped_gemm_fp8_swiglu_save(*bad) == SHAPE
+
+
+def test_wgrad_validation(L):
+    P = ctypes.c_void_p(16)
+    assert L.moe_wgrad_max_tiles(147456, 257) == 1152 + 257 and L.moe_wgrad_max_tiles(-1, 4) == 0
+    assert L.moe_wgrad_tiles(P, 0, P, None) == SHAPE and L.moe_wgrad_tiles(None, 4, P, None) == NULL
+    # colwise rows: (x, xt, src, scale, offsets, tile_first, G, max_tiles, C, mode, qt, st, stream)
+    assert L.moe_colwise_quant_rows(P, 1, None, None, P, P, 4, 10, 200, 0, P, P, None) == SHAPE
+    assert L.moe_colwise_quant_rows(P, 2, None, None, P, P, 4, 10, 256, 0, P, P, None) == DTYPE
+    assert L.moe_colwise_quant_rows(P, 1, None, None, P, P, 4, 10, 256, 7, P, P, None) == ARG
+    assert L.moe_colwise_quant_rows(P, 1, None, None, None, P, 4, 10, 256, 0, P, P, None) == NULL
+    assert L.moe_colwise_quant_rows(None, 1, None, None, None, None, 4, 0, 256, 0, None, None, None) == OK
+    # colwise swiglu: (g, dh, F, offsets, tile_first, G, max_tiles, mode, qt, st, stream)
+    assert L.moe_colwise_quant_swiglu(P, None, 100, P, P, 4, 10, 0, P, P, None) == SHAPE
+    assert L.moe_colwise_quant_swiglu(P, None, 128, P, P, 4, 10, 9, P, P, None) == ARG
+    assert L.moe_colwise_quant_swiglu(None, None, 128, P, P, 4, 10, 0, P, P, None) == NULL
+    # wgrad GEMM: (a, as, M, b, bs, N, tile_first, G, max_tiles, mode, c, stream)
+    assert L.moe_grouped_gemm_wgrad(P, P, 200, P, P, 256, P, 4, 10, 0, P, None) == SHAPE
+    assert L.moe_grouped_gemm_wgrad(P, P, 256, P, P, 256, P, 0, 10, 0, P, None) == SHAPE
+    assert L.moe_grouped_gemm_wgrad(P, P, 256, P, P, 256, P, 4, 10, 3, P, None) == ARG
+    assert L.moe_grouped_gemm_wgrad(P, P, 256, P, None, 256, P, 4, 10, 0, P, None) == NULL

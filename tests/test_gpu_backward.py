@@ -240,3 +240,150 @@ def test_training_forward_keeps_g(name, pow2):
     torch.cuda.synchronize()
     for key in ("dx", "dwg", "dw", "dz"):
         assert torch.equal(got[key], ref[key]), key
+
+
+
+def _segments(G, sizes_seed):
+    """Group offsets with an empty group, a multiple of 128 and ragged sizes."""
+    rng = np.random.default_rng(sizes_seed)
+    counts = rng.integers(1, 300, G).astype(np.int32)
+    counts[1] = 0
+    counts[2] = 256
+    counts[-1] = 129
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("xdt,pow2", [("bf16", False), ("f32", False), ("bf16", True)])
+def test_colwise_quant_rows(xdt, pow2):
+    G, C, T = 7, 384, 900
+    offsets = _segments(G, 3)
+    rows = int(offsets[-1])
+    x = synth.to_act(synth.randn((T, C), 21, synth.STAGE, 0, 0, 71, device=DEV), xdt)
+    src = torch.from_numpy(np.random.default_rng(4).integers(0, T, rows).astype(np.int32)).to(DEV)
+    scale = synth.random_scales((rows,), 21, 72, device=DEV, lo=0.01, hi=1.0)
+    off_d = torch.from_numpy(offsets).to(DEV)
+    tf = M.moe_wgrad_tiles(off_d)
+    mt = M.wgrad_max_tiles(rows, G)
+    qt, st = M.moe_colwise_quant_rows(x, off_d, tf, mt, src_row=src, row_scale=scale, pow2=pow2)
+    vals = (host(scale)[:, None] * host(x)[host(src)]).astype(np.float32)
+    segs = B.colwise_segments(vals, offsets, True, pow2)
+    tfh = host(tf)
+    assert tfh[-1] == sum(-(-int(c) // 128) for c in np.diff(offsets))
+    q, sc = host(qt), host(st)
+    for g in range(G):
+        k0, k1 = int(tfh[g]) * 128, int(tfh[g + 1]) * 128
+        assert_equal(f"codes g{g}", q[:, k0:k1], segs[g][0])
+        assert_equal(f"scales g{g}", sc[:, k0 // 128:k1 // 128], segs[g][1])
+    # without a row map / factor: the rows themselves
+    qi, si = M.moe_colwise_quant_rows(x[:rows] if rows <= T else x, off_d[:1 + 3], M.moe_wgrad_tiles(off_d[:4]),
+                                      M.wgrad_max_tiles(int(offsets[3]), 3), pow2=pow2)
+    seg0 = B.colwise_segments(host(x)[:int(offsets[3])], offsets[:4], True, pow2)
+    assert_equal("identity rows", host(qi)[:, :seg0[0][0].shape[1]], seg0[0][0])
+
+
+@pytest.mark.parametrize("dg,pow2", [(False, False), (True, False), (True, True)])
+def test_colwise_quant_swiglu(dg, pow2):
+    G, F = 5, 256
+    offsets = _segments(G, 5)
+    rows = int(offsets[-1])
+    g = synth.randn((rows, 2 * F), 23, synth.STAGE, 0, 0, 73, device=DEV, std=2.0)
+    dh = synth.randn((rows, F), 23, synth.STAGE, 0, 0, 74, device=DEV, std=0.5) if dg else None
+    off_d = torch.from_numpy(offsets).to(DEV)
+    tf = M.moe_wgrad_tiles(off_d)
+    mt = M.wgrad_max_tiles(rows, G)
+    qt, st = M.moe_colwise_quant_swiglu(g, off_d, tf, mt, dh=dh, pow2=pow2)
+    gh = host(g)
+    vals = B.swiglu_backward(host(dh), gh, F) if dg else O.swiglu(gh, F)
+    segs = B.colwise_segments(vals, offsets, True, pow2)
+    tfh, q, sc = host(tf), host(qt), host(st)
+    tab = O.e4m3_table()
+    for gi in range(G):
+        k0, k1 = int(tfh[gi]) * 128, int(tfh[gi + 1]) * 128
+        if k1 == k0:
+            continue                          # the empty group: no tiles
+        gq, gs = q[:, k0:k1], sc[:, k0 // 128:k1 // 128]
+        rq, rs = segs[gi]
+        assert np.max(np.abs(gs - rs) / rs) < 1e-5
+        diff = gq != rq
+        assert diff.mean() < 1e-3
+        if diff.any():
+            assert np.all(np.abs(tab[gq[diff]] - tab[rq[diff]]) <= np.maximum(np.abs(tab[rq[diff]]) / 8, 2.0 ** -9))
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_wgrad_gemm(pow2):
+    G, M_, N_ = 6, 256, 384
+    offsets = _segments(G, 7)
+    rows = int(offsets[-1])
+    off_d = torch.from_numpy(offsets).to(DEV)
+    tf = M.moe_wgrad_tiles(off_d)
+    mt = M.wgrad_max_tiles(rows, G)
+    a32 = synth.randn((rows, M_), 25, synth.STAGE, 0, 0, 75, device=DEV)
+    b32 = synth.randn((rows, N_), 25, synth.STAGE, 0, 0, 76, device=DEV)
+    aq, as_ = M.moe_colwise_quant_rows(a32, off_d, tf, mt, pow2=pow2)
+    bq, bs = M.moe_colwise_quant_rows(b32, off_d, tf, mt, pow2=pow2)
+    c = M.moe_grouped_gemm_wgrad(aq, as_, bq, bs, tf, mt, pow2=pow2)
+    tfh = host(tf)
+    ref = np.zeros((G, M_, N_))
+    for g in range(G):
+        k0, k1 = int(tfh[g]) * 128, int(tfh[g + 1]) * 128
+        if k1 > k0:
+            A = O.dequant_act(host(aq)[:, k0:k1], host(as_)[:, k0 // 128:k1 // 128])
+            Bm = O.dequant_act(host(bq)[:, k0:k1], host(bs)[:, k0 // 128:k1 // 128])
+            ref[g] = A @ Bm.T
+    assert np.all(host(c)[1] == 0)            # the empty group
+    # fp32 accumulation over up to 3 steps of 128 products: error <= ~K u sum|a b|, and with random
+    # signs sum|a b| / max|C| is ~sqrt(K), so ~1e-4 of max|C| at K = 384 (1.9e-5 observed)
+    assert rel_err(host(c), ref) < 1e-4
+
+
+# weight gradients sum an expert's rows, so a one-step FP8 code difference (where the two sides'
+# fp32 and fp64 values straddle a rounding boundary) moves them by ~1/(16 sqrt(rows)) of their
+# largest entry: these layers give every expert a few hundred rows
+WG_CASES = {
+    "tiny": replace(synth.CONFIGS["tiny"], name="tiny_wg", T=512),
+    "prefill_wg": replace(synth.CONFIGS["prefill"], name="prefill_wg", T=512, H=256, E=16, F=256, k=8),
+}
+
+
+@pytest.mark.parametrize("name,pow2", [("tiny", False), ("prefill_wg", False), ("prefill_wg", True)])
+def test_layer_weight_gradients(name, pow2):
+    cfg = WG_CASES[name]
+    gw, bw, ol = _layer_pair(cfg, pow2)
+    lay = MoELayer(gw, cfg.T, _act(cfg))
+    x = synth.make_x(cfg, DEV)
+    dout = synth.make_dout(cfg, DEV)
+    lay.forward(x, training=True)
+    g = lay.backward(x, dout, bw, weight_grads=True)
+    torch.cuda.synchronize()
+    r = L.forward_dispatch(ol, host(x))
+    rb = B.backward_dispatch(ol, r, host(x), host(dout))
+    for key in ("dW1", "dW2"):
+        e = rel_err(host(g[key]), rb[key])
+        print(f"{name} pow2={pow2} {key} err {e:.2e}")
+        assert e < TOL, key
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_layer_weight_gradients_full_size_sampled(name):
+    """Full-size layers: the busiest routed expert of the oracle's own routing, and the shared
+    expert (all tokens) where there is one."""
+    cfg = synth.CONFIGS[name]
+    gw, bw, ol = _layer_pair(cfg)
+    lay = MoELayer(gw, cfg.T, _act(cfg))
+    x = synth.make_x(cfg, DEV)
+    dout = synth.make_dout(cfg, DEV)
+    lay.forward(x, training=True)
+    g = lay.backward(x, dout, bw, weight_grads=True)
+    torch.cuda.synchronize()
+    xh, dh = host(x), host(dout)
+    idx, _ = O.moe_route(O.moe_gate_logits(xh, ol.wg, ol.bias), ol.cfg)
+    busiest = int(np.argmax(np.bincount(idx[idx >= 0].ravel(), minlength=cfg.E)))
+    experts = (busiest, cfg.E) if cfg.shared else (busiest,)
+    for e in experts:
+        dW1, dW2 = B.wgrad_expert(ol, xh, dh, e)
+        e1, e2 = rel_err(host(g["dW1"][e]), dW1), rel_err(host(g["dW2"][e]), dW2)
+        print(f"{name} expert {e} dW1 err {e1:.2e} dW2 err {e2:.2e}")
+        assert e1 < TOL and e2 < TOL
+    del lay, gw, bw, g
+    _free()
