@@ -37,6 +37,7 @@ RIDGE_FP8 = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 STAGES = ["gate_logits", "route", "quant_x", "dispatch", "gemm1_swiglu", "gemm2", "combine"]
 BWD_STAGES = ["bwd_combine", "bwd_gemm_dh", "bwd_gemm_g", "bwd_swiglu", "bwd_gemm_da", "bwd_combine_dx", "bwd_route",
               "bwd_gate"]
+WGRAD_STAGES = ["bwd_wgrad_quant", "bwd_wgrad_gemm"]
 
 
 def parse():
@@ -54,6 +55,8 @@ def parse():
                          "the matrix cores")
     ap.add_argument("--backward", action="store_true",
                     help="time forward + backward of the layer (gradients of x, the gate and its bias)")
+    ap.add_argument("--weight-grads", action="store_true",
+                    help="with --backward: also the expert-weight gradients dW1, dW2 (fp32)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -90,6 +93,11 @@ def stage_model(cfg, counts, n_active1):
         "bwd_route": dict(bytes=T * E * 8 + T * k * 8, flops=0.0, bound="hbm"),
         "bwd_gate": dict(bytes=T * E * 4 + T * H * ab + E * H * 4 + T * H * 4 + T * H * ab + E * H * 4,
                          flops=4.0 * T * H * E, bound="alu"),
+        # weight gradients: 128x1 operands (dY, x gathered; h, dG from G and dh), then fp32 dW1, dW2
+        "bwd_wgrad_quant": dict(bytes=rows * (2 * H * ab + 2 * 8 * F + 4 * F) + rows * (2 * H + 3 * F) * (1 + sig),
+                                flops=0.0, bound="hbm"),
+        "bwd_wgrad_gemm": dict(bytes=rows * (2 * H + 3 * F) + act_groups * 3 * H * F * 4, flops=6.0 * H * F * rows,
+                               bound=None),
         "_rows": rows, "_groups": G,
     }
 
@@ -312,7 +320,7 @@ def backward_bench(a, cfg, layers, bw, x, copies, pow2):
     dout = synth.make_dout(cfg, dev)
     for s in range(a.warmup):
         layers[s % copies].forward(x, training=True)
-        layers[s % copies].backward(x, dout, bw)
+        layers[s % copies].backward(x, dout, bw, weight_grads=a.weight_grads)
     torch.cuda.synchronize()
     K = a.steps
     graphs = None
@@ -325,7 +333,7 @@ def backward_bench(a, cfg, layers, bw, x, copies, pow2):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=side):
                     layers[c].forward(x, training=True)
-                    layers[c].backward(x, dout, bw)
+                    layers[c].backward(x, dout, bw, weight_grads=a.weight_grads)
                 graphs.append(g)
         torch.cuda.current_stream().wait_stream(side)
         for s in range(a.warmup):
@@ -337,19 +345,20 @@ def backward_bench(a, cfg, layers, bw, x, copies, pow2):
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t0) * 1e3 / K
     evf = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(K)]
-    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(len(BWD_STAGES) + 1)] for _ in range(K)]
+    bst = BWD_STAGES + (WGRAD_STAGES if a.weight_grads else [])
+    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(len(bst) + 1)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
         layers[s % copies].forward(x, events=evf[s], training=True)
-        layers[s % copies].backward(x, dout, bw, events=evb[s])
+        layers[s % copies].backward(x, dout, bw, events=evb[s], weight_grads=a.weight_grads)
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / K
     ms_per_step = eager_ms if graphs is None else graph_ms
     stage_ms = {name: float(np.mean([evf[s][i].elapsed_time(evf[s][i + 1]) for s in range(K)]))
                 for i, name in enumerate(STAGES)}
     stage_ms.update({name: float(np.mean([evb[s][i].elapsed_time(evb[s][i + 1]) for s in range(K)]))
-                     for i, name in enumerate(BWD_STAGES)})
+                     for i, name in enumerate(bst)})
     layer = layers[0]
     counts = layer.disp.counts.cpu().numpy()
     n_active = int((counts > 0).sum())
@@ -357,14 +366,14 @@ def backward_bench(a, cfg, layers, bw, x, copies, pow2):
     # the training forward's GEMM1 also writes G (fp32); the backward then has no recompute
     g1 = model["gemm1_swiglu"]
     model["gemm1_swiglu"] = dict(g1, bytes=g1["bytes"] + model["_rows"] * 2 * cfg.F * 4)
-    timed = [n for n in STAGES + BWD_STAGES if n != "bwd_gemm_g"]   # no recompute after a training forward
+    timed = [n for n in STAGES + bst if n != "bwd_gemm_g"]   # no recompute after a training forward
     stages = {name: stage_entry(name, model, stage_ms[name]) for name in timed}
     fwd_ms = sum(stage_ms[n] for n in STAGES)
-    bwd_ms = sum(stage_ms[n] for n in BWD_STAGES)
+    bwd_ms = sum(stage_ms[n] for n in bst)
     gemm_names = [n for n in ("bwd_gemm_dh", "bwd_gemm_g", "bwd_gemm_da") if n in stages]
     bgemm_ms = sum(stage_ms[n] for n in gemm_names)
     bgemm_tflops = sum(model[n]["flops"] for n in gemm_names) / (bgemm_ms * 1e-3) / 1e12
-    dom = max((n for n in BWD_STAGES if n in stages), key=lambda n: stage_ms[n])
+    dom = max((n for n in bst if n in stages), key=lambda n: stage_ms[n])
     e = stages[dom]
     if e["bound"] == "hbm":
         roof = {"bound": "hbm", "achieved": e["GB_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s"}
@@ -374,7 +383,10 @@ def backward_bench(a, cfg, layers, bw, x, copies, pow2):
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = None
     p2 = ", pow2" if pow2 else ""
-    roof["kernel"] = f"grouped_gemm_kernel<{layer.plan.tile_rows}, store_f32, packed{p2}>" if "gemm" in dom else dom
+    if dom == "bwd_wgrad_gemm":
+        roof["kernel"] = f"wgrad_gemm_kernel<{'pow2' if pow2 else 'amax'}>"
+    else:
+        roof["kernel"] = f"grouped_gemm_kernel<{layer.plan.tile_rows}, store_f32, packed{p2}>" if "gemm" in dom else dom
     roof["stage"] = dom
     cpu = None if a.no_cpu_baseline else cpu_baseline_backward(cfg, x, dout, dev, pow2)
     line = {
@@ -387,7 +399,9 @@ def backward_bench(a, cfg, layers, bw, x, copies, pow2):
         "dtype": "fp8-e4m3 x fp8-e4m3 -> fp32 (GEMMs, forward and backward); fp32 router and gate; "
                  + ("bf16" if cfg.act == "bf16" else "fp32") + " activations and gradients",
         "data": "synthetic (seeded N(0,1) activations and output gradient, N(0,1/sqrt(fan_in)) weights)",
-        "config": {"workload": cfg.name, "pass": "forward+backward", "tokens": cfg.T, "hidden": cfg.H,
+        "config": {"workload": cfg.name, "pass": "forward+backward" + (" (with expert-weight gradients)"
+                                                                       if a.weight_grads else ""),
+                   "tokens": cfg.T, "hidden": cfg.H,
                    "experts": cfg.E, "shared_experts": int(cfg.shared), "ffn": cfg.F, "top_k": cfg.k,
                    "score": cfg.score_fn, "rows": model["_rows"], "active_experts": n_active,
                    "layer_copies": copies, "weight_layout": "packed",

@@ -675,7 +675,10 @@ def moe_colwise_quant_rows(x: torch.Tensor, offsets: torch.Tensor, tile_first: t
                            src_row: Optional[torch.Tensor] = None, row_scale: Optional[torch.Tensor] = None,
                            pow2: bool = False, qt=None, st=None, stream=None):
     """128x1-quantised transposed operand: column c, row r = row_scale[r] * x[src_row[r], c], each
-    group's rows in whole 128-row tiles.  Returns (codes [C, max_tiles*128], scales [C, max_tiles])."""
+    group's rows in whole 128-row tiles.  Returns (codes, scales) buffers of C * max_tiles * 128 bytes
+    and C * max_tiles floats (shaped [C, max_tiles*128] / [C, max_tiles] for storage only): group g's
+    codes are the row-major [C, 128 n_g] block at flat offset tile_first[g] * 128 * C, its scales the
+    [C, n_g] block at tile_first[g] * C (``colwise_block``)."""
     _dev(x, "x", (torch.float32, torch.bfloat16))
     C = x.shape[1]
     G = offsets.shape[0] - 1
@@ -691,6 +694,16 @@ def moe_colwise_quant_rows(x: torch.Tensor, offsets: torch.Tensor, tile_first: t
                                         G, max_tiles, C, mode, _p(qt), _p(st), _stream(stream)),
            "moe_colwise_quant_rows")
     return qt, st
+
+
+def colwise_block(qt: torch.Tensor, st: torch.Tensor, tile_first, g: int):
+    """Views of group g's codes [C, 128 n_g] and scales [C, n_g] in a column-wise operand buffer
+    (tile_first: host sequence of int)."""
+    C = qt.shape[0]
+    t0, t1 = int(tile_first[g]), int(tile_first[g + 1])
+    q = qt.reshape(-1)[t0 * 128 * C:t1 * 128 * C].view(C, (t1 - t0) * 128)
+    s = st.reshape(-1)[t0 * C:t1 * C].view(C, t1 - t0)
+    return q, s
 
 
 def moe_colwise_quant_swiglu(g: torch.Tensor, offsets: torch.Tensor, tile_first: torch.Tensor, max_tiles: int,

@@ -5,9 +5,11 @@
 //   dW2[e] = sum over e's rows r of dY[r]^T h[r]      [H, F]
 //   dW1[e] = sum over e's rows r of dG[r]^T x[r]      [2F, H]
 // Both operands contract over an expert's rows, so they are quantised in 128x1 blocks (128
-// consecutive rows of one expert by one column) and stored transposed: operand[c][k] for column c
-// and padded row k, each expert's rows a segment of whole 128-row tiles (zero-padded).  Expert e's
-// segment starts at tile_first[e] * 128, tile_first = exclusive prefix sum of ceil(rows_e / 128).
+// consecutive rows of one expert by one column) and stored transposed, one contiguous block per
+// expert: expert e's rows fill K_e = 128 * ntiles_e padded rows (zero-padded), and its block
+// [C, K_e] (codes; scales [C, ntiles_e]) starts at tile_first[e] * 128 * C bytes (scales at
+// tile_first[e] * C), tile_first = exclusive prefix sum of ntiles_e = ceil(rows_e / 128).  A block
+// is contiguous so that the GEMM's reads of one expert stay within a few MB.
 //
 //   moe_wgrad_tiles            tile_first [G+1] from the group offsets
 //   moe_colwise_quant_rows     dY = w * dout gathered per row (or x gathered per row), 128x1 codes
@@ -65,8 +67,8 @@ __device__ __forceinline__ int group_of_tile(const int32_t* __restrict__ tile_fi
 constexpr int CQ_COLS = 64;
 
 template <bool POW2>
-__device__ __forceinline__ void colwise_store(float (&v)[8][4], int tile, int c0, int64_t kpad, uint8_t* __restrict__ qt,
-                                              float* __restrict__ st) {
+__device__ __forceinline__ void colwise_store(float (&v)[8][4], int tile, int tf0, int ntiles, int C, int c0,
+                                              uint8_t* __restrict__ qt, float* __restrict__ st) {
   __shared__ float red[4][CQ_COLS];
   const int tid = threadIdx.x, rr = tid >> 4, cc = tid & 15, lane = tid & 63, wave = tid >> 6;
   float m[4];
@@ -84,7 +86,11 @@ __device__ __forceinline__ void colwise_store(float (&v)[8][4], int tile, int c0
     for (int j = 0; j < 4; ++j) red[wave][cc * 4 + j] = m[j];
   }
   __syncthreads();
-  const int64_t kb = kpad / 128;
+  // the expert's block: codes [C, 128 ntiles] at 128 C tf0, scales [C, ntiles] at C tf0
+  const int64_t kg = (int64_t)ntiles * 128;
+  uint8_t* qb = qt + (int64_t)tf0 * 128 * C;
+  float* sb = st + (int64_t)tf0 * C;
+  const int lt = tile - tf0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int c = cc * 4 + j;
@@ -92,8 +98,8 @@ __device__ __forceinline__ void colwise_store(float (&v)[8][4], int tile, int c0
     const float s = block_scale(amax, POW2);
     const uint32_t lo = e4m3_pack4(v[0][j] / s, v[1][j] / s, v[2][j] / s, v[3][j] / s);
     const uint32_t hi = e4m3_pack4(v[4][j] / s, v[5][j] / s, v[6][j] / s, v[7][j] / s);
-    *reinterpret_cast<uint2*>(qt + (int64_t)(c0 + c) * kpad + (int64_t)tile * 128 + rr * 8) = make_uint2(lo, hi);
-    if (rr == 0) st[(int64_t)(c0 + c) * kb + tile] = s;
+    *reinterpret_cast<uint2*>(qb + (int64_t)(c0 + c) * kg + lt * 128 + rr * 8) = make_uint2(lo, hi);
+    if (rr == 0) sb[(int64_t)(c0 + c) * ntiles + lt] = s;
   }
 }
 
@@ -103,8 +109,7 @@ __global__ __launch_bounds__(256) void colquant_rows_kernel(const void* __restri
                                                             const float* __restrict__ rowf,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ tile_first, int groups, int C,
-                                                            int64_t kpad, uint8_t* __restrict__ qt,
-                                                            float* __restrict__ st) {
+                                                            uint8_t* __restrict__ qt, float* __restrict__ st) {
   const int tile = blockIdx.x;
   const int g = group_of_tile(tile_first, groups, tile);
   if (g < 0) return;
@@ -135,7 +140,7 @@ __global__ __launch_bounds__(256) void colquant_rows_kernel(const void* __restri
       }
     }
   }
-  colwise_store<POW2>(v, tile, c0, kpad, qt, st);
+  colwise_store<POW2>(v, tile, tile_first[g], tile_first[g + 1] - tile_first[g], C, c0, qt, st);
 }
 
 // from the GEMM1 output G = [gate | up] ([rows, 2F] fp32): h = silu(gate) up (C = F), or with dh
@@ -144,8 +149,7 @@ template <bool DG, bool POW2>
 __global__ __launch_bounds__(256) void colquant_swiglu_kernel(const float* __restrict__ gm, const float* __restrict__ dh,
                                                               int F, const int32_t* __restrict__ offsets,
                                                               const int32_t* __restrict__ tile_first, int groups,
-                                                              int64_t kpad, uint8_t* __restrict__ qt,
-                                                              float* __restrict__ st) {
+                                                              uint8_t* __restrict__ qt, float* __restrict__ st) {
   const int tile = blockIdx.x;
   const int g = group_of_tile(tile_first, groups, tile);
   if (g < 0) return;
@@ -180,12 +184,12 @@ __global__ __launch_bounds__(256) void colquant_swiglu_kernel(const float* __res
       }
     }
   }
-  colwise_store<POW2>(v, tile, c0, kpad, qt, st);
+  colwise_store<POW2>(v, tile, tile_first[g], tile_first[g + 1] - tile_first[g], DG ? 2 * F : F, c0, qt, st);
 }
 
 // ------------------------------------------------------------------------------------------------
-// C_e [M, N] = A_e B_e^T over expert e's segment of k (tiles tile_first[e] .. tile_first[e+1]),
-// A [M, kpad] and B [N, kpad] 128x1-quantised codes with scales [M or N, kpad/128].  One workgroup
+// C_e [M, N] = A_e B_e^T over expert e's K_e padded rows, A_e [M, K_e] and B_e [N, K_e] the experts'
+// blocks of 128x1-quantised codes (scales [M or N, K_e/128]).  One workgroup
 // per 128 x 128 output tile of one expert (grid N/128, M/128, G); four waves of 64 x 64 each
 // (4 x 4 MFMA 16x16x128 tiles); k in 128-wide steps, the next step's operands loaded into registers
 // during the current step's MFMAs, LDS double-buffered.  An expert with no rows gets zeros.
@@ -202,7 +206,7 @@ template <bool POW2>
 __global__ __launch_bounds__(256) void wgrad_gemm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ as,
                                                          const uint8_t* __restrict__ b, const float* __restrict__ bs,
                                                          int M, int N, const int32_t* __restrict__ tile_first,
-                                                         int64_t kpad, float* __restrict__ c) {
+                                                         float* __restrict__ c) {
   __shared__ __attribute__((aligned(16))) uint8_t la[2][WG_T * 128];
   __shared__ __attribute__((aligned(16))) uint8_t lb[2][WG_T * 128];
   __shared__ __attribute__((aligned(16))) float lsa[2][WG_T];
@@ -211,20 +215,22 @@ __global__ __launch_bounds__(256) void wgrad_gemm_kernel(const uint8_t* __restri
   const int t0 = tile_first[g], t1 = tile_first[g + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t kb = kpad / 128;
+  const int kt = t1 - t0;                     // the expert's 128-row tiles
+  const int64_t kg = (int64_t)kt * 128;        // row length of its blocks
   // staging: 1024 16-byte pieces per operand per step; thread takes pieces tid + 256 p
   uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
   float rsv = 0.0f;   // this thread's scale: A rows for tid < 128, B rows above
   const int srow_ = tid & 127;
-  const float* sp_ = tid < 128 ? as + (int64_t)(m0 + srow_) * kb : bs + (int64_t)(n0 + srow_) * kb;
+  const float* sp_ = tid < 128 ? as + (int64_t)t0 * M + (int64_t)(m0 + srow_) * kt
+                                : bs + (int64_t)t0 * N + (int64_t)(n0 + srow_) * kt;
   // piece p of a thread: row (tid + 256 p) / 8 = tid / 8 + 32 p, 16-byte chunk tid % 8
   const int prow = tid >> 3, pch = tid & 7;
-  const uint8_t* pa_ = a + (int64_t)(m0 + prow) * kpad + pch * 16;
-  const uint8_t* pb_ = b + (int64_t)(n0 + prow) * kpad + pch * 16;
-  const int64_t pstep = 32 * kpad;
+  const uint8_t* pa_ = a + (int64_t)t0 * 128 * M + (int64_t)(m0 + prow) * kg + pch * 16;
+  const uint8_t* pb_ = b + (int64_t)t0 * 128 * N + (int64_t)(n0 + prow) * kg + pch * 16;
+  const int64_t pstep = 32 * kg;
 #define WG_LOAD(TILE)                                                                       \
   do {                                                                                      \
-    const int64_t k0_ = (int64_t)(TILE) * 128;                                              \
+    const int64_t k0_ = (int64_t)((TILE) - t0) * 128;                                       \
     ra0 = *reinterpret_cast<const uint4*>(pa_ + k0_);                                       \
     ra1 = *reinterpret_cast<const uint4*>(pa_ + pstep + k0_);                               \
     ra2 = *reinterpret_cast<const uint4*>(pa_ + 2 * pstep + k0_);                           \
@@ -233,7 +239,7 @@ __global__ __launch_bounds__(256) void wgrad_gemm_kernel(const uint8_t* __restri
     rb1 = *reinterpret_cast<const uint4*>(pb_ + pstep + k0_);                               \
     rb2 = *reinterpret_cast<const uint4*>(pb_ + 2 * pstep + k0_);                           \
     rb3 = *reinterpret_cast<const uint4*>(pb_ + 3 * pstep + k0_);                           \
-    rsv = sp_[(TILE)];                                                                      \
+    rsv = sp_[(TILE) - t0];                                                                 \
   } while (0)
 #define WG_STORE(BUF)                                                                       \
   do {                                                                                      \
@@ -353,13 +359,12 @@ extern "C" int moe_colwise_quant_rows(const void* x, int x_dtype, const int32_t*
   if (scale_mode != MOE_SCALE_AMAX && scale_mode != MOE_SCALE_POW2) return MOE_ERR_ARG;
   if (max_tiles == 0) return MOE_OK;
   if (!x || !offsets || !tile_first || !qt || !st) return MOE_ERR_NULL;
-  const int64_t kpad = max_tiles * 128;
   const dim3 grid((unsigned)max_tiles, (unsigned)(C / CQ_COLS));
   hipStream_t s = as_stream(stream);
   const bool bf = x_dtype == MOE_BF16, p2 = scale_mode == MOE_SCALE_POW2;
   auto k = bf ? (p2 ? colquant_rows_kernel<true, true> : colquant_rows_kernel<true, false>)
               : (p2 ? colquant_rows_kernel<false, true> : colquant_rows_kernel<false, false>);
-  k<<<grid, 256, 0, s>>>(x, src_row, row_scale, offsets, tile_first, groups, C, kpad, qt, st);
+  k<<<grid, 256, 0, s>>>(x, src_row, row_scale, offsets, tile_first, groups, C, qt, st);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -373,16 +378,15 @@ extern "C" int moe_colwise_quant_swiglu(const float* g, const float* dh, int32_t
   if (scale_mode != MOE_SCALE_AMAX && scale_mode != MOE_SCALE_POW2) return MOE_ERR_ARG;
   if (max_tiles == 0) return MOE_OK;
   if (!g || !offsets || !tile_first || !qt || !st) return MOE_ERR_NULL;
-  const int64_t kpad = max_tiles * 128;
   const dim3 grid((unsigned)max_tiles, (unsigned)(C / CQ_COLS));
   hipStream_t s = as_stream(stream);
   const bool p2 = scale_mode == MOE_SCALE_POW2;
   if (dh) {
     auto k = p2 ? colquant_swiglu_kernel<true, true> : colquant_swiglu_kernel<true, false>;
-    k<<<grid, 256, 0, s>>>(g, dh, F, offsets, tile_first, groups, kpad, qt, st);
+    k<<<grid, 256, 0, s>>>(g, dh, F, offsets, tile_first, groups, qt, st);
   } else {
     auto k = p2 ? colquant_swiglu_kernel<false, true> : colquant_swiglu_kernel<false, false>;
-    k<<<grid, 256, 0, s>>>(g, dh, F, offsets, tile_first, groups, kpad, qt, st);
+    k<<<grid, 256, 0, s>>>(g, dh, F, offsets, tile_first, groups, qt, st);
   }
   MOE_CHECK_LAUNCH();
   return MOE_OK;
@@ -395,12 +399,11 @@ extern "C" int moe_grouped_gemm_wgrad(const uint8_t* a, const float* as, int32_t
   if (M < 128 || N < 128 || M % 128 != 0 || N % 128 != 0 || M / 128 > 65535) return MOE_ERR_SHAPE;
   if (scale_mode != MOE_SCALE_AMAX && scale_mode != MOE_SCALE_POW2) return MOE_ERR_ARG;
   if (!a || !as || !b || !bs || !tile_first || !c) return MOE_ERR_NULL;
-  const int64_t kpad = max_tiles * 128;
   const dim3 grid((unsigned)(N / WG_T), (unsigned)(M / WG_T), (unsigned)groups);
   if (scale_mode == MOE_SCALE_POW2)
-    wgrad_gemm_kernel<true><<<grid, 256, 0, as_stream(stream)>>>(a, as, b, bs, M, N, tile_first, kpad, c);
+    wgrad_gemm_kernel<true><<<grid, 256, 0, as_stream(stream)>>>(a, as, b, bs, M, N, tile_first, c);
   else
-    wgrad_gemm_kernel<false><<<grid, 256, 0, as_stream(stream)>>>(a, as, b, bs, M, N, tile_first, kpad, c);
+    wgrad_gemm_kernel<false><<<grid, 256, 0, as_stream(stream)>>>(a, as, b, bs, M, N, tile_first, c);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

@@ -368,10 +368,11 @@ size_t moe_gate_backward_workspace(int64_t T, int32_t E, int32_t H);
 /* Expert-weight gradients (blog section "FP8 training"): dW2[e] = sum over e's rows of dY^T h
  * ([H,F]) and dW1[e] = sum over e's rows of dG^T x ([2F,H]).  Both operands contract over an expert's
  * rows, so they are quantised in 128x1 blocks (128 consecutive rows of one expert x one column) and
- * stored transposed, operand[c][k] with k a padded row: expert e's rows fill whole 128-row tiles
- * tile_first[e] .. tile_first[e+1]-1 (zero-padded), k = tile * 128 + row within the tile.  Buffers
- * are sized for max_tiles = moe_wgrad_max_tiles(max_rows, groups) tiles: codes [C, max_tiles*128]
- * e4m3, scales [C, max_tiles] fp32 (tiles past tile_first[groups] are not written).
+ * stored transposed, one contiguous block per expert: expert e's rows fill n_e = tile_first[e+1] -
+ * tile_first[e] whole 128-row tiles (zero-padded), its codes are a row-major [C, 128 n_e] block at
+ * byte tile_first[e] * 128 * C and its scales a [C, n_e] block at element tile_first[e] * C.
+ * Buffers hold max_tiles = moe_wgrad_max_tiles(max_rows, groups) tiles: codes C * max_tiles * 128
+ * bytes, scales C * max_tiles fp32 (past tile_first[groups] * 128 * C nothing is written).
  *   moe_wgrad_tiles: tile_first [groups+1] int32 (device, out) from the dispatch offsets [groups+1].
  *   moe_colwise_quant_rows: column c, row r of the operand = row_scale[r] * x[src_row[r], c]
  *     (x [*, C] in x_dtype; src_row NULL = identity; row_scale NULL = 1): dY from dout with the
@@ -379,9 +380,9 @@ size_t moe_gate_backward_workspace(int64_t T, int32_t E, int32_t H);
  *   moe_colwise_quant_swiglu: from the GEMM1 output g [rows, 2F] fp32, h = silu(gate) * up (C = F,
  *     dh NULL) or, with dh [rows, F] fp32, dG = [dgate | dup] as in moe_swiglu_backward_quant (C = 2F).
  *   moe_grouped_gemm_wgrad: c[e] = A_e B_e^T ([groups, M, N] fp32, every expert written; zeros for an
- *     expert with no rows), A [M, max_tiles*128] and B [N, max_tiles*128] codes with scales
- *     [M or N, max_tiles]; amax scales promoted per 128-row step, power-of-two scales applied by
- *     the matrix cores.
+ *     expert with no rows), A_e [M, 128 n_e] and B_e [N, 128 n_e] the experts' blocks of two operands
+ *     in the layout above (C = M and C = N); amax scales promoted per 128-row step, power-of-two
+ *     scales applied by the matrix cores.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (C, M, N % 128; groups), MOE_ERR_DTYPE, MOE_ERR_ARG
  * (scale_mode), MOE_ERR_HIP.  moe_wgrad_max_tiles returns 0 for invalid sizes. */
 int64_t moe_wgrad_max_tiles(int64_t max_rows, int32_t groups);

@@ -269,16 +269,15 @@ def test_colwise_quant_rows(xdt, pow2):
     segs = B.colwise_segments(vals, offsets, True, pow2)
     tfh = host(tf)
     assert tfh[-1] == sum(-(-int(c) // 128) for c in np.diff(offsets))
-    q, sc = host(qt), host(st)
     for g in range(G):
-        k0, k1 = int(tfh[g]) * 128, int(tfh[g + 1]) * 128
-        assert_equal(f"codes g{g}", q[:, k0:k1], segs[g][0])
-        assert_equal(f"scales g{g}", sc[:, k0 // 128:k1 // 128], segs[g][1])
+        qg, sg = M.colwise_block(qt, st, tfh, g)
+        assert_equal(f"codes g{g}", host(qg), segs[g][0])
+        assert_equal(f"scales g{g}", host(sg), segs[g][1])
     # without a row map / factor: the rows themselves
     qi, si = M.moe_colwise_quant_rows(x[:rows] if rows <= T else x, off_d[:1 + 3], M.moe_wgrad_tiles(off_d[:4]),
                                       M.wgrad_max_tiles(int(offsets[3]), 3), pow2=pow2)
     seg0 = B.colwise_segments(host(x)[:int(offsets[3])], offsets[:4], True, pow2)
-    assert_equal("identity rows", host(qi)[:, :seg0[0][0].shape[1]], seg0[0][0])
+    assert_equal("identity rows", host(M.colwise_block(qi, si, [0, seg0[0][0].shape[1] // 128], 0)[0]), seg0[0][0])
 
 
 @pytest.mark.parametrize("dg,pow2", [(False, False), (True, False), (True, True)])
@@ -295,13 +294,12 @@ def test_colwise_quant_swiglu(dg, pow2):
     gh = host(g)
     vals = B.swiglu_backward(host(dh), gh, F) if dg else O.swiglu(gh, F)
     segs = B.colwise_segments(vals, offsets, True, pow2)
-    tfh, q, sc = host(tf), host(qt), host(st)
+    tfh = host(tf)
     tab = O.e4m3_table()
     for gi in range(G):
-        k0, k1 = int(tfh[gi]) * 128, int(tfh[gi + 1]) * 128
-        if k1 == k0:
+        if tfh[gi + 1] == tfh[gi]:
             continue                          # the empty group: no tiles
-        gq, gs = q[:, k0:k1], sc[:, k0 // 128:k1 // 128]
+        gq, gs = (host(t) for t in M.colwise_block(qt, st, tfh, gi))
         rq, rs = segs[gi]
         assert np.max(np.abs(gs - rs) / rs) < 1e-5
         diff = gq != rq
@@ -326,10 +324,9 @@ def test_wgrad_gemm(pow2):
     tfh = host(tf)
     ref = np.zeros((G, M_, N_))
     for g in range(G):
-        k0, k1 = int(tfh[g]) * 128, int(tfh[g + 1]) * 128
-        if k1 > k0:
-            A = O.dequant_act(host(aq)[:, k0:k1], host(as_)[:, k0 // 128:k1 // 128])
-            Bm = O.dequant_act(host(bq)[:, k0:k1], host(bs)[:, k0 // 128:k1 // 128])
+        if tfh[g + 1] > tfh[g]:
+            A = O.dequant_act(*(host(t) for t in M.colwise_block(aq, as_, tfh, g)))
+            Bm = O.dequant_act(*(host(t) for t in M.colwise_block(bq, bs, tfh, g)))
             ref[g] = A @ Bm.T
     assert np.all(host(c)[1] == 0)            # the empty group
     # fp32 accumulation over up to 3 steps of 128 products: error <= ~K u sum|a b|, and with random
