@@ -269,43 +269,41 @@ __global__ __launch_bounds__(256) void wgrad_gemm_kernel(const uint8_t* __restri
   for (int tile = t0; tile < t1; ++tile) {
     const bool more = tile + 1 < t1;
     if (more) WG_LOAD(tile + 1);
-    intx8 af[4], bf[4];
+    // B fragments of the step stay in registers; A fragments and the amax path's products are
+    // taken one 16-row block at a time, which keeps the kernel at two waves per SIMD
+    intx8 bf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ra_ = wm * 64 + i * 16 + lr, rb_ = wn * 64 + i * 16 + lr;
-      const intx4 alo = *reinterpret_cast<const intx4*>(&la[buf][wswz(ra_, 2 * lq)]);
-      const intx4 ahi = *reinterpret_cast<const intx4*>(&la[buf][wswz(ra_, 2 * lq + 1)]);
+      const int rb_ = wn * 64 + i * 16 + lr;
       const intx4 blo = *reinterpret_cast<const intx4*>(&lb[buf][wswz(rb_, 2 * lq)]);
       const intx4 bhi = *reinterpret_cast<const intx4*>(&lb[buf][wswz(rb_, 2 * lq + 1)]);
-      af[i] = intx8{alo[0], alo[1], alo[2], alo[3], ahi[0], ahi[1], ahi[2], ahi[3]};
       bf[i] = intx8{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
     }
-    if (POW2) {
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms) {
-        const uint32_t ea = e8m0_code(lsa[buf][wm * 64 + ms * 16 + lr]);
+    for (int ms = 0; ms < 4; ++ms) {
+      const int ra_ = wm * 64 + ms * 16 + lr;
+      const intx4 alo = *reinterpret_cast<const intx4*>(&la[buf][wswz(ra_, 2 * lq)]);
+      const intx4 ahi = *reinterpret_cast<const intx4*>(&la[buf][wswz(ra_, 2 * lq + 1)]);
+      const intx8 af = intx8{alo[0], alo[1], alo[2], alo[3], ahi[0], ahi[1], ahi[2], ahi[3]};
+      if (POW2) {
+        const uint32_t ea = e8m0_code(lsa[buf][ra_]);
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns)
           acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              bf[ns], af[ms], acc[ms][ns], 0, 0, 0, e8m0_code(lsb[buf][wn * 64 + ns * 16 + lr]), 0, ea);
-      }
-    } else {
-      floatx4 p[4][4];
-#pragma unroll
-      for (int ms = 0; ms < 4; ++ms)
+              bf[ns], af, acc[ms][ns], 0, 0, 0, e8m0_code(lsb[buf][wn * 64 + ns * 16 + lr]), 0, ea);
+      } else {
+        floatx4 p[4];
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns)
-          p[ms][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[ns], af[ms], floatx4{0.f, 0.f, 0.f, 0.f},
-                                                                       0, 0, 0, 0, 0, 0);
-#pragma unroll
-      for (int ms = 0; ms < 4; ++ms) {
-        const float sa = lsa[buf][wm * 64 + ms * 16 + lr];
+          p[ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[ns], af, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                                   0, 0, 0);
+        const float sa = lsa[buf][ra_];
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns) {
           const float4 sb = *reinterpret_cast<const float4*>(&lsb[buf][wn * 64 + ns * 16 + 4 * lq]);
           const float sbv[4] = {sb.x, sb.y, sb.z, sb.w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[ms][ns][r] = __builtin_fmaf(p[ms][ns][r], sa * sbv[r], acc[ms][ns][r]);
+          for (int r = 0; r < 4; ++r) acc[ms][ns][r] = __builtin_fmaf(p[ns][r], sa * sbv[r], acc[ms][ns][r]);
         }
       }
     }
