@@ -71,6 +71,7 @@ __device__ __forceinline__ void colwise_store(float (&v)[8][4], int tile, int tf
                                               uint8_t* __restrict__ qt, float* __restrict__ st) {
   __shared__ float red[4][CQ_COLS];
   const int tid = threadIdx.x, rr = tid >> 4, cc = tid & 15, lane = tid & 63, wave = tid >> 6;
+  __syncthreads();   // a previous call's reads of red are done
   float m[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -144,7 +145,9 @@ __global__ __launch_bounds__(256) void colquant_rows_kernel(const void* __restri
 }
 
 // from the GEMM1 output G = [gate | up] ([rows, 2F] fp32): h = silu(gate) up (C = F), or with dh
-// ([rows, F] fp32) dG = [dgate | dup] (C = 2F) in exactly the SwiGLU backward's operations
+// ([rows, F] fp32) dG = [dgate | dup] (C = 2F) in exactly the SwiGLU backward's operations.  A
+// workgroup covers features f0 .. f0 + 63; for dG it writes both halves (columns f and F + f) from
+// one read of gate, up and dh.
 template <bool DG, bool POW2>
 __global__ __launch_bounds__(256) void colquant_swiglu_kernel(const float* __restrict__ gm, const float* __restrict__ dh,
                                                               int F, const int32_t* __restrict__ offsets,
@@ -154,18 +157,15 @@ __global__ __launch_bounds__(256) void colquant_swiglu_kernel(const float* __res
   const int g = group_of_tile(tile_first, groups, tile);
   if (g < 0) return;
   const int r0 = offsets[g] + (tile - tile_first[g]) * 128, r1 = offsets[g + 1];
-  const int c0 = blockIdx.y * CQ_COLS;
+  const int f0 = blockIdx.y * CQ_COLS;
   const int tid = threadIdx.x, rr = tid >> 4, cc = tid & 15;
-  // column c of the operand: h or dgate for c < F (feature f = c), dup for c >= F (f = c - F)
-  const int c = c0 + cc * 4;
-  const bool up_half = DG && c >= F;
-  const int f = up_half ? c - F : c;
-  float v[8][4];
+  const int f = f0 + cc * 4;
+  float v[8][4], u[8][4];   // h or dgate; dup
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = r0 + rr * 8 + i;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[i][j] = 0.0f;
+    for (int j = 0; j < 4; ++j) v[i][j] = u[i][j] = 0.0f;
     if (r < r1) {
       const float4 ga = *reinterpret_cast<const float4*>(gm + (int64_t)r * 2 * F + f);
       const float4 ua = *reinterpret_cast<const float4*>(gm + (int64_t)r * 2 * F + F + f);
@@ -179,12 +179,15 @@ __global__ __launch_bounds__(256) void colquant_swiglu_kernel(const float* __res
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float s = 1.0f / (1.0f + __expf(-gv[j]));
-          v[i][j] = up_half ? dv[j] * gv[j] * s : dv[j] * uv[j] * s * (1.0f + gv[j] * (1.0f - s));
+          v[i][j] = dv[j] * uv[j] * s * (1.0f + gv[j] * (1.0f - s));
+          u[i][j] = dv[j] * gv[j] * s;
         }
       }
     }
   }
-  colwise_store<POW2>(v, tile, tile_first[g], tile_first[g + 1] - tile_first[g], DG ? 2 * F : F, c0, qt, st);
+  const int nt = tile_first[g + 1] - tile_first[g];
+  colwise_store<POW2>(v, tile, tile_first[g], nt, DG ? 2 * F : F, f0, qt, st);
+  if (DG) colwise_store<POW2>(u, tile, tile_first[g], nt, 2 * F, F + f0, qt, st);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -370,13 +373,12 @@ extern "C" int moe_colwise_quant_rows(const void* x, int x_dtype, const int32_t*
 extern "C" int moe_colwise_quant_swiglu(const float* g, const float* dh, int32_t F, const int32_t* offsets,
                                         const int32_t* tile_first, int32_t groups, int64_t max_tiles,
                                         int32_t scale_mode, uint8_t* qt, float* st, void* stream) {
-  const int32_t C = dh ? 2 * F : F;
   int rc = check_seg(groups, max_tiles, F);
   if (rc != MOE_OK) return rc;
   if (scale_mode != MOE_SCALE_AMAX && scale_mode != MOE_SCALE_POW2) return MOE_ERR_ARG;
   if (max_tiles == 0) return MOE_OK;
   if (!g || !offsets || !tile_first || !qt || !st) return MOE_ERR_NULL;
-  const dim3 grid((unsigned)max_tiles, (unsigned)(C / CQ_COLS));
+  const dim3 grid((unsigned)max_tiles, (unsigned)(F / CQ_COLS));
   hipStream_t s = as_stream(stream);
   const bool p2 = scale_mode == MOE_SCALE_POW2;
   if (dh) {
