@@ -79,6 +79,15 @@ def _load():
         lib.orc_dequant_act.argtypes = [P, P, I64, I32, P]
         lib.orc_dequant_weight.argtypes = [P, P, I32, I32, P]
         lib.orc_gemm_block_form.argtypes = [P, P, I64, P, P, I32, I32, P]
+        lib.orc_e2m1_value.restype = ctypes.c_double
+        lib.orc_e2m1_value.argtypes = [ctypes.c_uint8]
+        lib.orc_e2m1_encode.restype = ctypes.c_uint8
+        lib.orc_e2m1_encode.argtypes = [ctypes.c_float]
+        lib.orc_e2m1_encode_array.argtypes = [P, I64, P]
+        lib.orc_fp4_scale.restype = ctypes.c_float
+        lib.orc_fp4_scale.argtypes = [ctypes.c_float]
+        lib.orc_quant_mxfp4.argtypes = [P, I64, I32, P, P]
+        lib.orc_dequant_mxfp4.argtypes = [P, P, I64, I32, P]
         _lib = lib
         return lib
 
@@ -320,4 +329,57 @@ def moe_combine(y: np.ndarray, dest_row: np.ndarray, w: np.ndarray, y_shared: np
         out[ok] += w[ok, j].astype(np.float64)[:, None] * y[d[ok]]
     if y_shared is not None:
         out += np.asarray(y_shared, np.float64)
+    return out
+
+
+# ------------------------------------------------------------------ FP4 weights (see the C file)
+def e2m1_table() -> np.ndarray:
+    """fp64 value of each of the 16 FP4 E2M1 codes."""
+    return np.array([_load().orc_e2m1_value(c) for c in range(16)])
+
+
+def e2m1_encode(v) -> np.ndarray:
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    _load().orc_e2m1_encode_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def fp4_scale(amax: float) -> float:
+    return float(_load().orc_fp4_scale(float(amax)))
+
+
+def quant_mxfp4(x_f32: np.ndarray):
+    """[..., rows, cols] fp32 -> (packed codes [..., rows, cols/2] uint8, E8M0 scale codes
+    [..., rows, cols/32] uint8); 1x32 blocks along cols."""
+    x = _c(x_f32, np.float32)
+    cols = x.shape[-1]
+    assert cols % 32 == 0
+    rows = x.size // cols
+    q = np.empty(x.shape[:-1] + (cols // 2,), np.uint8)
+    e8 = np.empty(x.shape[:-1] + (cols // 32,), np.uint8)
+    _load().orc_quant_mxfp4(_ptr(x), rows, cols, _ptr(q), _ptr(e8))
+    return q, e8
+
+
+def dequant_mxfp4(q: np.ndarray, e8: np.ndarray) -> np.ndarray:
+    """fp64 value of packed FP4 weights [N, K/2] with E8M0 scales [N, K/32]."""
+    q, e8 = _c(q, np.uint8), _c(e8, np.uint8)
+    N, K = q.shape[0], q.shape[1] * 2
+    assert e8.shape == (N, K // 32)
+    out = np.empty((N, K), np.float64)
+    _load().orc_dequant_mxfp4(_ptr(q), _ptr(e8), N, K, _ptr(out))
+    return out
+
+
+def moe_grouped_gemm_fp4w(aq, as_, offsets, wq, we8) -> np.ndarray:
+    """Grouped GEMM with FP4 weights in fp64: rows of group g times deq_fp4(w[g])^T.
+    aq [rows,K] e4m3 codes with 1x128 scales; wq [G,N,K/2]; we8 [G,N,K/32]."""
+    offsets = np.asarray(offsets)
+    G, N = wq.shape[0], wq.shape[1]
+    out = np.zeros((aq.shape[0], N), np.float64)
+    for g in range(G):
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        if r1 > r0:
+            out[r0:r1] = dequant_act(aq[r0:r1], as_[r0:r1]) @ dequant_mxfp4(wq[g], we8[g]).T
     return out

@@ -407,3 +407,81 @@ void orc_gemm_block_form(const uint8_t* a, const float* as, int64_t M, const uin
       out[m * N + n] = acc;
     }
 }
+
+/* ---------------------------------------------------------------------------------------
+ * FP4 weights (the 4-bit analogue of the block-scaled recipe; the pages name NVFP4 only as
+ * future work, so the format here is the OCP microscaling one the MI355X matrix cores take):
+ * OCP FP4 E2M1 elements -- 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit; magnitudes
+ * 0, 0.5 (subnormal), 1, 1.5, 2, 3, 4, 6 for codes 0..7; no infinities or NaN -- in 1x32
+ * blocks along K, each with a power-of-two scale s = the smallest power of two at or above
+ * fl32(amax / 6), at least 2^-127 (1 for an all-zero block), stored as its E8M0 exponent code
+ * (the fp32 exponent field; 2^-127 is code 0).  q = e2m1(x / s), round to nearest with ties to
+ * the even code, saturating at 6, sign of zero kept.  Two codes per byte, element 2i in the low
+ * nibble.
+ * ------------------------------------------------------------------------------------- */
+double orc_e2m1_value(uint8_t code) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  double v = mag[code & 7];
+  return (code & 8) ? -v : v;
+}
+
+/* nearest magnitude, ties to the even code (the midpoints 0.25, 0.75, ... go to codes 0, 2, 2, 4, 4, 6, 6) */
+uint8_t orc_e2m1_encode(float v) {
+  uint8_t sign = signbit(v) ? 8 : 0;
+  double a = fabs((double)v);
+  uint8_t c;
+  if (a <= 0.25) c = 0;
+  else if (a < 0.75) c = 1;
+  else if (a <= 1.25) c = 2;
+  else if (a < 1.75) c = 3;
+  else if (a <= 2.5) c = 4;
+  else if (a < 3.5) c = 5;
+  else if (a <= 5.0) c = 6;
+  else c = 7;
+  return sign | c;
+}
+
+void orc_e2m1_encode_array(const float* v, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e2m1_encode(v[i]);
+}
+
+/* the block scale of a 1x32 FP4 block with largest magnitude amax */
+float orc_fp4_scale(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  float t = amax / 6.0f;
+  int e;
+  float m = frexpf(t, &e);
+  float s = m == 0.5f ? t : m == 0.0f ? 0.0f : ldexpf(1.0f, e);
+  float lo = ldexpf(1.0f, -127);
+  return s < lo ? lo : s;
+}
+
+/* x [rows][cols] fp32 -> q [rows][cols/2] packed codes, e8 [rows][cols/32] E8M0 scale codes */
+void orc_quant_mxfp4(const float* x, int64_t rows, int32_t cols, uint8_t* q, uint8_t* e8) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int32_t b = 0; b < cols / 32; ++b) {
+      const float* v = x + r * cols + b * 32;
+      float amax = 0.0f;
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      float s = orc_fp4_scale(amax);
+      int e;
+      frexpf(s, &e);                       /* s = 0.5 * 2^e, i.e. 2^(e-1) */
+      e8[r * (cols / 32) + b] = (uint8_t)(e - 1 + 127);
+      for (int i = 0; i < 32; i += 2) {
+        uint8_t lo = orc_e2m1_encode(v[i] / s), hi = orc_e2m1_encode(v[i + 1] / s);
+        q[r * (cols / 2) + b * 16 + i / 2] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+}
+
+/* fp64 value of packed FP4 weights [N][K/2] with E8M0 scales [N][K/32] */
+void orc_dequant_mxfp4(const uint8_t* q, const uint8_t* e8, int64_t N, int32_t K, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int32_t k = 0; k < K; ++k) {
+      uint8_t byte = q[n * (K / 2) + k / 2];
+      uint8_t code = (k & 1) ? (byte >> 4) : (byte & 15);
+      out[n * K + k] = orc_e2m1_value(code) * ldexp(1.0, (int)e8[n * (K / 32) + k / 32] - 127);
+    }
+}
