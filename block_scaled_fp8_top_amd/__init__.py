@@ -26,7 +26,7 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_EPI_STORE, MOE_EPI_SWIGLU_QUANT = 0, 1
 MOE_OP_DISPATCH, MOE_OP_GROUPED_GEMM = 1, 2
-MOE_B_ROWMAJOR, MOE_B_PACKED = 0, 1
+MOE_B_ROWMAJOR, MOE_B_PACKED, MOE_B_PACKED_FP4 = 0, 1, 2
 MOE_SCALE_AMAX, MOE_SCALE_POW2 = 0, 1
 
 EXPORTED = ("moe_gate_logits", "moe_route", "moe_replay_route", "moe_replay_gate", "moe_router_score_eval",
@@ -36,7 +36,8 @@ EXPORTED = ("moe_gate_logits", "moe_route", "moe_replay_route", "moe_replay_gate
             "moe_payload_pack", "moe_payload_unpack", "moe_payload_to_host", "moe_payload_from_host",
             "moe_combine_backward", "moe_swiglu_backward_quant", "moe_route_backward", "moe_gate_backward",
             "moe_gate_backward_workspace", "moe_transpose_fp8_blocks", "moe_wgrad_max_tiles", "moe_wgrad_tiles",
-            "moe_colwise_quant_rows", "moe_colwise_quant_swiglu", "moe_grouped_gemm_wgrad",
+            "moe_colwise_quant_rows", "moe_colwise_quant_swiglu", "moe_grouped_gemm_wgrad", "moe_quant_mxfp4",
+            "moe_packed_fp4_bytes", "moe_pack_weights_fp4",
             "moe_workspace_bytes", "moe_status_str", "moe_version")
 
 
@@ -99,6 +100,9 @@ def lib():
         "moe_payload_from_host": [P, I64, I32, P, P, P],
         "moe_combine_backward": [P, ctypes.c_int, P, ctypes.c_int, P, P, I64, I32, I32, P, I32, P, P, P, P, P],
         "moe_wgrad_max_tiles": [I64, I32],
+        "moe_quant_mxfp4": [P, ctypes.c_int, I64, I32, P, P, P],
+        "moe_packed_fp4_bytes": [I32, I32, I32, I32, P],
+        "moe_pack_weights_fp4": [P, P, I32, I32, I32, I32, P, P, P],
         "moe_wgrad_tiles": [P, I32, P, P],
         "moe_colwise_quant_rows": [P, ctypes.c_int, P, P, P, P, I32, I64, I32, I32, P, P, P],
         "moe_colwise_quant_swiglu": [P, P, I32, P, P, I32, I64, I32, P, P, P],
@@ -121,6 +125,7 @@ def lib():
     L.moe_payload_bytes.restype = ctypes.c_size_t
     L.moe_gate_backward_workspace.restype = ctypes.c_size_t
     L.moe_wgrad_max_tiles.restype = ctypes.c_int64
+    L.moe_packed_fp4_bytes.restype = ctypes.c_size_t
     L.moe_status_str.restype = ctypes.c_char_p
     L.moe_version.restype = ctypes.c_char_p
     _lib = L
@@ -367,6 +372,50 @@ def moe_pack_weights_fp8(b: torch.Tensor, epilogue: int, out: Optional[torch.Ten
     return PackedWeight(out, G, N, K, epilogue)
 
 
+@dataclass
+class PackedWeightFP4:
+    """A [G,N,K] FP4 weight (two codes per byte) with its E8M0 scales, packed by
+    moe_pack_weights_fp4 for one GEMM epilogue."""
+    data: torch.Tensor     # [G, code bytes per group] uint8
+    scales: torch.Tensor   # [G, scale-image bytes per group] uint8
+    G: int
+    N: int
+    K: int
+    epilogue: int
+
+
+def moe_quant_mxfp4(w: torch.Tensor, q=None, e8=None, stream=None):
+    """w [..., rows, cols] fp32/bf16 -> (codes [..., rows, cols/2] uint8, E8M0 scale codes
+    [..., rows, cols/32] uint8): FP4 E2M1 in 1x32 blocks with power-of-two scales."""
+    _dev(w, "w", (torch.float32, torch.bfloat16))
+    cols = w.shape[-1]
+    rows = w.numel() // cols if cols else 0
+    if cols % 32:
+        raise ValueError("cols must be a multiple of 32")
+    qs, es = tuple(w.shape[:-1]) + (cols // 2,), tuple(w.shape[:-1]) + (cols // 32,)
+    q = torch.empty(qs, dtype=torch.uint8, device=w.device) if q is None else _dev(q, "q", torch.uint8, qs)
+    e8 = torch.empty(es, dtype=torch.uint8, device=w.device) if e8 is None else _dev(e8, "e8", torch.uint8, es)
+    _check(lib().moe_quant_mxfp4(_p(w), _act_code(w), rows, cols, _p(q), _p(e8), _stream(stream)), "moe_quant_mxfp4")
+    return q, e8
+
+
+def moe_pack_weights_fp4(q: torch.Tensor, e8: torch.Tensor, epilogue: int, stream=None) -> PackedWeightFP4:
+    """q [G,N,K/2], e8 [G,N,K/32] (from moe_quant_mxfp4) -> the packed FP4 layout of ``epilogue``."""
+    _dev(q, "q", torch.uint8)
+    G, N, K2 = q.shape
+    K = 2 * K2
+    _dev(e8, "e8", torch.uint8, (G, N, K // 32))
+    sb = ctypes.c_size_t(0)
+    nbytes = int(lib().moe_packed_fp4_bytes(G, N, K, epilogue, ctypes.byref(sb)))
+    if nbytes == 0:
+        raise MoeError(MOE_ERR_SHAPE, f"moe_pack_weights_fp4: unsupported shape {(G, N, K)} / epilogue {epilogue}")
+    data = torch.empty((G, nbytes // G), dtype=torch.uint8, device=q.device)
+    scales = torch.empty((G, sb.value // G), dtype=torch.uint8, device=q.device)
+    _check(lib().moe_pack_weights_fp4(_p(q), _p(e8), G, N, K, epilogue, _p(data), _p(scales), _stream(stream)),
+           "moe_pack_weights_fp4")
+    return PackedWeightFP4(data, scales, G, N, K, epilogue)
+
+
 def moe_grouped_gemm_plan(offsets: torch.Tensor, max_rows: int, workspace: torch.Tensor, tile_rows: int = 0,
                           stream=None):
     """Tile plan of the groups in ``offsets`` [G+1] (device) for up to max_rows rows, written into
@@ -395,7 +444,14 @@ def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tens
     matrix cores apply them; the SwiGLU epilogue writes power-of-two scales for h).
     save_g (SwiGLU with a plan only): fp32 [max_rows, N] that also receives the GEMM output G."""
     max_rows, K = a.shape
-    if isinstance(b, PackedWeight):
+    if isinstance(b, PackedWeightFP4):
+        if b.epilogue != epilogue:
+            raise ValueError("weight was packed for another epilogue")
+        if not pow2:
+            raise ValueError("FP4 weights need power-of-two activation scales (pow2=True)")
+        G, N, Kb, b_layout, b_t = b.G, b.N, b.K, MOE_B_PACKED_FP4, b.data
+        bs = b.scales
+    elif isinstance(b, PackedWeight):
         if b.epilogue != epilogue:
             raise ValueError("weight was packed for another epilogue")
         G, N, Kb, b_layout, b_t = b.G, b.N, b.K, MOE_B_PACKED, b.data
@@ -409,7 +465,10 @@ def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tens
     _dev(a, "a", FP8)
     _dev(as_, "as", torch.float32, (max_rows, K // 128))
     _dev(offsets, "offsets", torch.int32, (G + 1,))
-    _dev(bs, "bs", torch.float32, (G, N // 128, K // 128))
+    if b_layout == MOE_B_PACKED_FP4:
+        _dev(bs, "bs", torch.uint8)
+    else:
+        _dev(bs, "bs", torch.float32, (G, N // 128, K // 128))
     dev = a.device
     if plan is not None:
         if plan.groups != G or plan.max_rows != max_rows:

@@ -58,14 +58,14 @@ constexpr int BN = 256, BK = 128;
 constexpr int NTHREADS = 512;
 constexpr int MIN_BM = 32;
 
-template <int BM_>
+template <int BM_, bool FP4 = false>
 struct Tile {
   static constexpr int BM = BM_;
   static constexpr int WM = BM_ >= 128 ? 2 : 1;             // wave grid WM x WN
   static constexpr int WN = 8 / WM;
   static constexpr int MS = BM_ / WM / 16;                   // 16 x 16 MFMA tiles per wave along M
   static constexpr int NS = BN / WN / 16;                    // ... along N
-  static constexpr int A_BYTES = BM_ * BK, B_BYTES = BN * BK;
+  static constexpr int A_BYTES = BM_ * BK, B_BYTES = FP4 ? BN * BK / 2 : BN * BK;   // FP4: two codes per byte
   static constexpr int NSTAGE = 4 * (A_BYTES + B_BYTES) <= 155 * 1024 ? 4 : 3;   // ring within 160 KB of LDS
   static constexpr int A_INSTR = BM_ / 8;                    // 1 KB DMA instructions per A slice
   static constexpr int A_PW = A_INSTR >= 8 ? A_INSTR / 8 : 1;
@@ -207,14 +207,16 @@ __device__ __forceinline__ Unit unit_at(int u, int ny, const int4* __restrict__ 
 // Persistent workgroups: workgroup w takes units me(w), me(w) + G, me(w) + 2G, ... (G = grid size),
 // and its K steps over all of them form one stream: the DMA lookahead runs into the next unit while
 // the current unit's last steps and epilogue execute, so no unit pays the pipeline fill again.
-template <int BM, int EPI, bool OUT_BF16, bool PACKED, bool POW2>
+template <int BM, int EPI, bool OUT_BF16, bool PACKED, bool POW2, bool FP4 = false>
 __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const int32_t* __restrict__ offsets,
     const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles, int ny, const uint8_t* __restrict__ b,
     const float* __restrict__ bs, int N, int K, void* __restrict__ out, float* __restrict__ out_scales,
     float* __restrict__ g_out) {
-  using T = Tile<BM>;
+  static_assert(!FP4 || (PACKED && POW2), "FP4 weights come packed, with power-of-two activation scales");
+  using T = Tile<BM, FP4>;
   constexpr int WM = T::WM, WN = T::WN, MS = T::MS, NS = T::NS, HS = NS / 2, NSTAGE = T::NSTAGE;
+  constexpr int B_PW = FP4 ? 2 : 4;   // B DMA instructions per wave and step
   constexpr int A_BYTES = T::A_BYTES, B_BYTES = T::B_BYTES, AS_W = T::AS_W;
   constexpr int WROWS = MS * 16;   // rows per wave
   constexpr int D = NSTAGE - 1;    // DMA lookahead in K steps
@@ -222,6 +224,8 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t b_lds[NSTAGE][B_BYTES];
   __shared__ __attribute__((aligned(16))) float as_lds[4][AS_W];   // activation-scale ring: slot (step & 3)
   __shared__ __attribute__((aligned(16))) float bsc_lds[4][64];    // weight-scale ring: [0] low, [1] high block
+  // FP4 weights: E8M0 scale codes of each step, [panel row][32-wide K chunk] (ring slot step & 3)
+  __shared__ __attribute__((aligned(16))) uint8_t bsc4_lds[4][FP4 ? 1024 : 16];
   __shared__ float red[WM][WN][WROWS];
 
   // ---- this workgroup's units: each round of G consecutive logical units is split into
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
-  const size_t gstride = (PACKED ? (size_t)ny * BN : (size_t)N) * K;   // bytes of one group's weights
+  const size_t gstride = (PACKED ? (size_t)ny * BN : (size_t)N) * K / (FP4 ? 2 : 1);   // bytes of one group's weights
 
   // ---- DMA roles.  A slice: wave w issues instructions w*A_PW + j (or just w, for slices of fewer
   // than 8 instructions); B slice: instructions 4w .. 4w+3.  Row-major operands: instruction i
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   const int sidx = max(wave - (8 - T::S_INSTR), 0);
   // wave 0 also brings the step's two weight scales (lane 0: low 128-column block, lane 1: high)
   const bool bscale_loader = wave == 0;
-  const int per_stage = (has_a ? T::A_PW : 0) + 4 + (scale_loader ? 1 : 0) + (bscale_loader ? 1 : 0);
+  const int per_stage = (has_a ? T::A_PW : 0) + B_PW + (scale_loader ? 1 : 0) + (bscale_loader ? 1 : 0);
 
   // issue-side context of the unit whose steps are being issued: 32-bit byte offsets from a and
   // from the unit's group weights (both < 2^32 for every accepted shape); rows past the tile's end
@@ -261,6 +265,7 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   const uint8_t* bg = b;
   const float* ssrc = as;
   const float* bsrc = bs;   // this lane's weight-scale row (low block for lane != 1)
+  const uint8_t* bsrc4 = reinterpret_cast<const uint8_t*>(bs);   // FP4: the unit's panel scale images
   int ii = 0, ik = 0;   // unit index and K step of the next step to issue
 #define GEMM_ISSUE_CTX(I)                                                                           \
   do {                                                                                              \
@@ -271,7 +276,8 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     }                                                                                               \
     _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                              \
       if (PACKED) {                                                                                 \
-        boff[i_] = (uint32_t)un_.nt * (uint32_t)(BN * K) + (uint32_t)((4 * wave + i_) * 1024 + lane * 16); \
+        boff[i_] = (uint32_t)un_.nt * (uint32_t)(BN * K / (FP4 ? 2 : 1)) +                           \
+                   (uint32_t)((B_PW * wave + i_) * 1024 + lane * 16);                               \
       } else {                                                                                      \
         const int r_ = (4 * wave + i_) * 8 + (lane >> 3);                                           \
         const int n_ = min(panel_row(EPI, un_.nt, r_, F), N - 1);                                   \
@@ -283,11 +289,13 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     const int nlo_ = EPI == 1 ? un_.nt : min(un_.nt * BN, N - 1) / 128;                             \
     const int nhi_ = EPI == 1 ? (F / 128) + un_.nt : min(un_.nt * BN + 128, N - 1) / 128;           \
     bsrc = bs + ((size_t)un_.g * (N / 128) + (lane == 1 ? nhi_ : nlo_)) * KB;                       \
+    bsrc4 = reinterpret_cast<const uint8_t*>(bs) + ((size_t)un_.g * ny + un_.nt) * (size_t)KB * 1024; \
   } while (0)
 
   // wave-uniform LDS destinations of this wave's DMA instructions, stage 0; stage s adds s * stride
   const uint32_t a_dst = lds_u32(&a_lds[0][a_i0 * 1024]);
-  const uint32_t b_dst = lds_u32(&b_lds[0][(4 * wave) * 1024]);
+  const uint32_t b_dst = lds_u32(&b_lds[0][(B_PW * wave) * 1024]);
+  const uint32_t bsc4_dst = lds_u32(&bsc4_lds[0][0]);
   const uint32_t s_dst = lds_u32(&as_lds[0][sidx * 64]);
   const uint32_t bsc_dst = lds_u32(&bsc_lds[0][0]);
   // issue K step ik of unit ii (global step SV) into LDS stage ST, then advance (ii, ik)
@@ -301,7 +309,10 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
         dma16s<0>(a + ko_, aoff[j_], ao_ + 1024 * j_);                                    \
     }                                                                                     \
     const uint32_t bo_ = b_dst + (uint32_t)(ST) * B_BYTES;                                \
-    if (PACKED) {                                                                         \
+    if (FP4) {                                                                            \
+      dma16s<0>(bg + kob_, boff[0], bo_);                                                 \
+      dma16s<1024>(bg + kob_, boff[0], bo_);                                              \
+    } else if (PACKED) {                                                                  \
       dma16s<0>(bg + kob_, boff[0], bo_);                                                 \
       dma16s<1024>(bg + kob_, boff[0], bo_);                                              \
       dma16s<2048>(bg + kob_, boff[0], bo_);                                              \
@@ -313,7 +324,13 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
       dma16s<0>(bg + kob_, boff[3], bo_ + 3072);                                          \
     }                                                                                     \
     if (scale_loader) dma4(ssrc + ik, s_dst + (uint32_t)((SV) & 3) * AS_W * 4);           \
-    if (bscale_loader) dma4(bsrc + ik, bsc_dst + (uint32_t)((SV) & 3) * 256);             \
+    if (FP4) {                                                                            \
+      if (bscale_loader)                                                                  \
+        dma16s<0>(bsrc4 + (size_t)ik * 1024, (uint32_t)(lane * 16),                       \
+                  bsc4_dst + (uint32_t)((SV) & 3) * 1024);                                \
+    } else if (bscale_loader) {                                                           \
+      dma4(bsrc + ik, bsc_dst + (uint32_t)((SV) & 3) * 256);                              \
+    }                                                                                     \
     if (++ik == KB) {                                                                     \
       ik = 0;                                                                             \
       if (++ii < nunits) GEMM_ISSUE_CTX(ii);                                              \
@@ -338,19 +355,30 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
 
   const int lr = lane & 15;         // row within a 16-row operand tile
   // operand fragments of one K step, read from LDS stage ST: the 16-row block starting at row R
-  // is 2 KB at 128 R; lane l's 32 bytes are words l and 64 + l of it
+  // is 2 KB at 128 R; lane l's 32 bytes are words l and 64 + l of it.  With FP8 on both sides the
+  // K order inside a lane is immaterial as long as both operands share it, so lane group c takes
+  // the 16-byte chunks 2c, 2c + 1.  An FP4 operand holds K 32c .. 32c + 31 in lane group c while an
+  // FP8 operand holds K 16c .. 16c + 15 in its low and 64 + 16c .. 64 + 16c + 15 in its high 16
+  // bytes, so against FP4 weights the activation fragment takes chunks c and 4 + c.
   intx8 af[MS], bf[NS];
+  const int a_c0 = FP4 ? (lane >> 4) : (lane >> 4) * 2, a_c1 = FP4 ? 4 + (lane >> 4) : (lane >> 4) * 2 + 1;
 #define GEMM_READ(ST)                                                                                   \
   do {                                                                                                  \
     _Pragma("unroll") for (int ms = 0; ms < MS; ++ms) {                                                 \
       const int r_ = wm * WROWS + ms * 16 + lr;                                                         \
-      const intx4 lo_ = *reinterpret_cast<const intx4*>(&a_lds[ST][swz(r_, (lane >> 4) * 2)]);          \
-      const intx4 hi_ = *reinterpret_cast<const intx4*>(&a_lds[ST][swz(r_, (lane >> 4) * 2 + 1)]);      \
+      const intx4 lo_ = *reinterpret_cast<const intx4*>(&a_lds[ST][swz(r_, a_c0)]);                     \
+      const intx4 hi_ = *reinterpret_cast<const intx4*>(&a_lds[ST][swz(r_, a_c1)]);                     \
       af[ms] = intx8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};                   \
     }                                                                                                   \
     _Pragma("unroll") for (int ns = 0; ns < NS; ++ns) {                                                 \
-      /* packed weights: operand order; row-major weights: swizzled rows */                             \
+      /* packed weights: operand order; row-major weights: swizzled rows; FP4: one 1 KB */              \
+      /* block per 16 rows, lane l's 16 bytes at 16 l */                                                \
       const int r_ = b_lrow[ns] + lr;                                                                   \
+      if (FP4) {                                                                                        \
+        const intx4 q_ = *reinterpret_cast<const intx4*>(&b_lds[ST][b_lrow[ns] * 64 + lane * 16]);      \
+        bf[ns] = intx8{q_[0], q_[1], q_[2], q_[3], 0, 0, 0, 0};                                         \
+        continue;                                                                                       \
+      }                                                                                                 \
       const int o_ = PACKED ? b_lrow[ns] * BK + lane * 16 : swz(r_, (lane >> 4) * 2);                   \
       const int o2_ = PACKED ? o_ + 1024 : swz(r_, (lane >> 4) * 2 + 1);                                \
       const intx4 lo_ = *reinterpret_cast<const intx4*>(&b_lds[ST][o_]);                                \
@@ -398,13 +426,19 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
         // scale of its operand row for its 32-wide K piece, here the same for the whole 128-wide
         // step) and accumulate straight into acc - no promotion
         const uint32_t eb_lo = e8m0_code(sb_lo), eb_hi = e8m0_code(sb_hi);
+        // FP4 weights: each lane's operand row has its own scale per 32-wide K chunk (lane / 16)
+        uint32_t eb4[NS];
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns)
+          eb4[ns] = FP4 ? (uint32_t)bsc4_lds[s & 3][(b_lrow[ns] + lr) * 4 + (lane >> 4)] : 0u;
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms) {
           const uint32_t ea = e8m0_code(srow[ms * 16]);
 #pragma unroll
           for (int ns = 0; ns < NS; ++ns)
             acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                bf[ns], af[ms], acc[ms][ns], 0, 0, 0, (EPI == 1 && ns >= HS) ? eb_hi : eb_lo, 0, ea);
+                bf[ns], af[ms], acc[ms][ns], FP4 ? 4 : 0, 0, 0,
+                FP4 ? eb4[ns] : ((EPI == 1 && ns >= HS) ? eb_hi : eb_lo), 0, ea);
         }
       } else {
         floatx4 p[MS][NS];
@@ -556,33 +590,44 @@ int auto_tile_rows(int64_t max_rows, int groups) {
   return avg2 <= 32 ? 32 : avg2 <= 48 ? 48 : avg2 <= 64 ? 64 : 128;
 }
 
-template <int BM, bool PACKED, bool POW2>
+template <int BM, bool PACKED, bool POW2, bool FP4 = false>
 void launch3(unsigned grid, hipStream_t st, int epilogue, int out_dtype, const uint8_t* a, const float* as,
              const int32_t* offsets, const int4* tiles, const int32_t* ntiles, int ny, const uint8_t* b,
              const float* bs, int N, int K, void* out, float* out_scales, float* g_out) {
   if (epilogue == MOE_EPI_STORE) {
     if (out_dtype == MOE_BF16)
-      grouped_gemm_kernel<BM, 0, true, PACKED, POW2><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b,
-                                                                                bs, N, K, out, nullptr, nullptr);
+      grouped_gemm_kernel<BM, 0, true, PACKED, POW2, FP4><<<grid, NTHREADS, 0, st>>>(
+          a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, nullptr, nullptr);
     else
-      grouped_gemm_kernel<BM, 0, false, PACKED, POW2><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b,
-                                                                                 bs, N, K, out, nullptr, nullptr);
+      grouped_gemm_kernel<BM, 0, false, PACKED, POW2, FP4><<<grid, NTHREADS, 0, st>>>(
+          a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, nullptr, nullptr);
   } else {
-    grouped_gemm_kernel<BM, 1, false, PACKED, POW2><<<grid, NTHREADS, 0, st>>>(a, as, offsets, tiles, ntiles, ny, b,
-                                                                               bs, N, K, out, out_scales, g_out);
+    grouped_gemm_kernel<BM, 1, false, PACKED, POW2, FP4><<<grid, NTHREADS, 0, st>>>(
+        a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales, g_out);
   }
 }
 
-template <int BM, bool PACKED>
-void launch(unsigned grid, hipStream_t st, int epilogue, int scale_mode, int out_dtype, const uint8_t* a,
-            const float* as, const int32_t* offsets, const int4* tiles, const int32_t* ntiles, int ny,
-            const uint8_t* b, const float* bs, int N, int K, void* out, float* out_scales, float* g_out) {
-  if (scale_mode == MOE_SCALE_POW2)
-    launch3<BM, PACKED, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                              out_scales, g_out);
+// b_layout: 0 row-major, 1 packed FP8, 2 packed FP4 (power-of-two scales only)
+template <int BM>
+void launch(unsigned grid, hipStream_t st, int b_layout, int epilogue, int scale_mode, int out_dtype,
+            const uint8_t* a, const float* as, const int32_t* offsets, const int4* tiles, const int32_t* ntiles,
+            int ny, const uint8_t* b, const float* bs, int N, int K, void* out, float* out_scales, float* g_out) {
+  const bool p2 = scale_mode == MOE_SCALE_POW2;
+  if (b_layout == MOE_B_PACKED_FP4)
+    launch3<BM, true, true, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+                                  out_scales, g_out);
+  else if (b_layout == MOE_B_PACKED && p2)
+    launch3<BM, true, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+                            out_scales, g_out);
+  else if (b_layout == MOE_B_PACKED)
+    launch3<BM, true, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+                             out_scales, g_out);
+  else if (p2)
+    launch3<BM, false, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+                             out_scales, g_out);
   else
-    launch3<BM, PACKED, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                               out_scales, g_out);
+    launch3<BM, false, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+                              out_scales, g_out);
 }
 
 // compute units of the current device, queried once per device
@@ -648,7 +693,8 @@ int check_gemm_args(int64_t max_rows, int32_t groups, int32_t N, int32_t K, int3
   // byte offsets inside a and inside one group's weights are 32-bit in the kernel
   if ((max_rows + 1) * (int64_t)K > (int64_t)UINT32_MAX || panels(N, epilogue) * BN * (int64_t)K > (int64_t)UINT32_MAX)
     return MOE_ERR_SHAPE;
-  if (b_layout != MOE_B_ROWMAJOR && b_layout != MOE_B_PACKED) return MOE_ERR_ARG;
+  if (b_layout != MOE_B_ROWMAJOR && b_layout != MOE_B_PACKED && b_layout != MOE_B_PACKED_FP4) return MOE_ERR_ARG;
+  if (b_layout == MOE_B_PACKED_FP4 && scale_mode != MOE_SCALE_POW2) return MOE_ERR_ARG;
   return MOE_OK;
 }
 
@@ -701,31 +747,18 @@ int run_planned(const moe_gemm_plan* plan, const uint8_t* a, const float* as, co
   // one persistent workgroup per compute unit (the LDS ring admits one per CU), never more than
   // the worst-case number of units
   const unsigned grid = (unsigned)std::min<int64_t>(nwg, cus);
-  const bool pk = b_layout == MOE_B_PACKED;
-  if (bm == 32 && pk)
-    launch<32, true>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                      out_scales, g_out);
-  else if (bm == 32)
-    launch<32, false>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                      out_scales, g_out);
-  else if (bm == 48 && pk)
-    launch<48, true>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                      out_scales, g_out);
+  if (bm == 32)
+    launch<32>(grid, st, b_layout, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+               out_scales, g_out);
   else if (bm == 48)
-    launch<48, false>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                      out_scales, g_out);
-  else if (bm == 64 && pk)
-    launch<64, true>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                      out_scales, g_out);
+    launch<48>(grid, st, b_layout, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+               out_scales, g_out);
   else if (bm == 64)
-    launch<64, false>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                      out_scales, g_out);
-  else if (pk)
-    launch<128, true>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                      out_scales, g_out);
+    launch<64>(grid, st, b_layout, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+               out_scales, g_out);
   else
-    launch<128, false>(grid, st, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                      out_scales, g_out);
+    launch<128>(grid, st, b_layout, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K,
+                out, out_scales, g_out);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

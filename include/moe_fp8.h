@@ -73,6 +73,7 @@ extern "C" {
 /* weight layouts accepted by moe_grouped_gemm_fp8 */
 #define MOE_B_ROWMAJOR 0       /* b [groups, N, K] e4m3, row-major                             */
 #define MOE_B_PACKED 1         /* b rearranged by moe_pack_weights_fp8 for the same epilogue    */
+#define MOE_B_PACKED_FP4 2     /* FP4 weights from moe_pack_weights_fp4 (bs: its scale image)   */
 
 /* workspace query op codes */
 #define MOE_OP_DISPATCH 1
@@ -200,7 +201,9 @@ size_t moe_packed_weight_bytes(int32_t groups, int32_t N, int32_t K, int32_t epi
  * with fp32 accumulation (e4m3 products accumulated exactly inside each 128-block, then promoted).
  *   a  [max_rows, K] e4m3, as [max_rows, K/128] fp32; offsets [groups+1] device int32, offsets[groups] <= max_rows
  *   b  [groups, N, K] e4m3 (b_layout MOE_B_ROWMAJOR) or the same weight after moe_pack_weights_fp8
- *      with this call's epilogue (b_layout MOE_B_PACKED); bs [groups, N/128, K/128] fp32
+ *      with this call's epilogue (b_layout MOE_B_PACKED), or FP4 weights packed by moe_pack_weights_fp4
+ *      (b_layout MOE_B_PACKED_FP4, bs its scale image, power-of-two scale_mode only);
+ *      bs [groups, N/128, K/128] fp32
  *   epilogue MOE_EPI_STORE:        out [max_rows, N] in out_dtype (MOE_BF16 or MOE_F32)
  *   epilogue MOE_EPI_SWIGLU_QUANT: N = 2F; h[r,f] = silu(acc[r,f]) * acc[r,F+f] in fp32, quantised
  *            1x128 as in moe_quant_fp8_block: out [max_rows, F] e4m3 (out_dtype MOE_FP8_E4M3),
@@ -396,6 +399,27 @@ int moe_colwise_quant_swiglu(const float* g, const float* dh, int32_t F, const i
 int moe_grouped_gemm_wgrad(const uint8_t* a, const float* as, int32_t M, const uint8_t* b, const float* bs, int32_t N,
                            const int32_t* tile_first, int32_t groups, int64_t max_tiles, int32_t scale_mode, float* c,
                            void* stream);
+
+/* FP4 expert weights: the 4-bit variant of the block-scaled recipe (the blog names NVFP4 as future
+ * work; the MI355X matrix cores take OCP microscaling FP4).  Elements are FP4 E2M1 (magnitudes 0,
+ * 0.5, 1, 1.5, 2, 3, 4, 6) in 1x32 blocks along K; a block's scale is the smallest power of two at
+ * or above fl32(amax / 6), at least 2^-127 (1 for an all-zero block), stored as its E8M0 code (the
+ * fp32 exponent field); q = e2m1(x / s), round to nearest with ties to the even code, saturating at
+ * 6, sign of zero kept.  Activations stay FP8 with power-of-two 1x128 scales.
+ *   moe_quant_mxfp4: w [rows, cols] in w_dtype (MOE_F32 / MOE_BF16; cols % 32 == 0) -> q [rows, cols/2]
+ *     (two codes per byte, element 2i in the low nibble), e8 [rows, cols/32] uint8.
+ *   moe_packed_fp4_bytes: bytes of the packed codes for moe_pack_weights_fp4 (0 if unsupported);
+ *     *scale_bytes (if not NULL) receives the bytes of the packed scale image.
+ *   moe_pack_weights_fp4: q [groups, N, K/2], e8 [groups, N, K/32] -> packed_q, packed_e8 in the
+ *     order the grouped GEMM streams for `epilogue` (per 256-row panel and 128-wide K step: 16 KB of
+ *     codes in MFMA fragment order, 1 KB of scale codes [row][32-wide chunk]).  The GEMM then takes
+ *     b = packed_q, b_layout = MOE_B_PACKED_FP4, bs = (const float*)packed_e8, scale_mode
+ *     MOE_SCALE_POW2 (activation scales must be powers of two).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ARG (epilogue), MOE_ERR_HIP. */
+int moe_quant_mxfp4(const void* w, int w_dtype, int64_t rows, int32_t cols, uint8_t* q, uint8_t* e8, void* stream);
+size_t moe_packed_fp4_bytes(int32_t groups, int32_t N, int32_t K, int32_t epilogue, size_t* scale_bytes);
+int moe_pack_weights_fp4(const uint8_t* q, const uint8_t* e8, int32_t groups, int32_t N, int32_t K, int32_t epilogue,
+                         uint8_t* packed_q, uint8_t* packed_e8, void* stream);
 
 /* Transpose of 128x128-block FP8 weights with their scales: qt[g][c][r] = q[g][r][c],
  * scales_t[g][cb][rb] = scales[g][rb][cb]; q [groups,N,K] -> qt [groups,K,N] (N, K multiples of 128).

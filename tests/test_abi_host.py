@@ -128,7 +128,8 @@ def test_gemm_validation(L):
     assert L.moe_grouped_gemm_fp8(*g(tr=40)) == ARG                   # tile height not 32, 48, 64 or 128
     assert L.moe_grouped_gemm_fp8(*g(rows=1 << 20, K=4096)) == SHAPE   # 2^32 bytes of activations
     assert L.moe_grouped_gemm_fp8(*g(N=1 << 17, K=1 << 15)) == SHAPE   # 2^32 bytes of one group's weights
-    assert L.moe_grouped_gemm_fp8(*g(bl=2)) == ARG                    # unknown weight layout
+    assert L.moe_grouped_gemm_fp8(*g(bl=3)) == ARG                    # unknown weight layout
+    assert L.moe_grouped_gemm_fp8(*g(bl=2)) == ARG                    # FP4 weights need power-of-two scales
     assert L.moe_grouped_gemm_fp8(*g(sm=2)) == ARG                    # unknown scale mode
     assert L.moe_grouped_gemm_fp8(*g(sm=1, wsb=8)) == WS
 
@@ -303,3 +304,24 @@ def test_wgrad_validation(L):
     assert L.moe_grouped_gemm_wgrad(P, P, 256, P, P, 256, P, 0, 10, 0, P, None) == SHAPE
     assert L.moe_grouped_gemm_wgrad(P, P, 256, P, P, 256, P, 4, 10, 3, P, None) == ARG
     assert L.moe_grouped_gemm_wgrad(P, P, 256, P, None, 256, P, 4, 10, 0, P, None) == NULL
+
+
+def test_fp4_validation(L):
+    P = ctypes.c_void_p(256)
+    # quant: (w, w_dtype, rows, cols, q, e8, stream)
+    assert L.moe_quant_mxfp4(P, 1, 4, 48, P, P, None) == SHAPE        # cols not a multiple of 32
+    assert L.moe_quant_mxfp4(P, 1, -1, 64, P, P, None) == SHAPE
+    assert L.moe_quant_mxfp4(P, 2, 4, 64, P, P, None) == DTYPE        # FP8 input
+    assert L.moe_quant_mxfp4(P, 1, 4, 64, None, P, None) == NULL
+    assert L.moe_quant_mxfp4(None, 1, 0, 64, None, None, None) == OK  # empty
+    sb = ctypes.c_size_t(0)
+    assert M.lib().moe_packed_fp4_bytes(4, 512, 1024, 0, ctypes.byref(sb)) == 4 * 2 * 8 * 16384
+    assert sb.value == 4 * 2 * 8 * 1024
+    assert M.lib().moe_packed_fp4_bytes(4, 384, 1024, 0, None) == 4 * 2 * 8 * 16384   # padded to 2 panels
+    assert M.lib().moe_packed_fp4_bytes(4, 384, 1024, 1, None) == 0                   # SwiGLU: N % 256
+    assert M.lib().moe_packed_fp4_bytes(4, 512, 100, 0, None) == 0
+    # pack: (q, e8, groups, N, K, epilogue, packed_q, packed_e8, stream)
+    assert L.moe_pack_weights_fp4(P, P, 4, 512, 100, 0, P, P, None) == SHAPE
+    assert L.moe_pack_weights_fp4(P, P, 0, 512, 128, 0, P, P, None) == SHAPE
+    assert L.moe_pack_weights_fp4(P, P, 4, 512, 128, 5, P, P, None) == ARG
+    assert L.moe_pack_weights_fp4(P, None, 4, 512, 128, 0, P, P, None) == NULL
