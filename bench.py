@@ -1,7 +1,7 @@
 """Benchmark of the block-scaled FP8 MoE layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|longctx|r3|tiny|payload]
-                    [--scales amax|pow2] [--backward]
+                    [--scales amax|pow2] [--weights fp8|fp4] [--backward]
 
 A step is one full layer forward (gate logits, routing, activation quantisation, dispatch,
 grouped GEMM1 + SwiGLU + h quantisation, grouped GEMM2, combine) over one batch of synthetic
@@ -15,7 +15,8 @@ pass of eager steps with HIP events between the stages gives the per-stage times
 line: layer tokens/s, per-stage times, the grouped GEMM's TFLOP/s, the roofline of the dominant
 kernel, and the CPU oracle timed on a bounded sample.  With --backward a step is the layer's training
 forward (GEMM1 also keeps its fp32 output) followed by its backward (output gradient -> dx, dWg,
-db), and the line reports the backward's stages too.
+db), and the line reports the backward's stages too.  --weights fp4 runs the same forward with FP4
+expert weights (E2M1 in 1x32 blocks with E8M0 scales; activations stay FP8 with power-of-two scales).
 """
 from __future__ import annotations
 
@@ -53,6 +54,9 @@ def parse():
     ap.add_argument("--scales", choices=("amax", "pow2"), default="amax",
                     help="block-scale form: amax/448 fp32 scales (default) or power-of-two scales applied by "
                          "the matrix cores")
+    ap.add_argument("--weights", choices=("fp8", "fp4"), default="fp8",
+                    help="expert weight format: fp8 e4m3 in 128x128 blocks, or fp4 e2m1 in 1x32 blocks with E8M0 "
+                         "scales (forward only; implies power-of-two activation scales)")
     ap.add_argument("--backward", action="store_true",
                     help="time forward + backward of the layer (gradients of x, the gate and its bias)")
     ap.add_argument("--weight-grads", action="store_true",
@@ -62,16 +66,19 @@ def parse():
     return ap.parse_args()
 
 
-def stage_model(cfg, counts, n_active1):
-    """Algorithmic bytes and flops of each stage (inputs read once, outputs written once)."""
+def stage_model(cfg, counts, n_active1, fp4=False):
+    """Algorithmic bytes and flops of each stage (inputs read once, outputs written once).  Expert
+    weight bytes per element: 1 + 4/128^2 for e4m3 with 128x128 fp32 scales, 1/2 + 1/32 for FP4
+    with one E8M0 byte per 1x32 block."""
     T, H, E, F, k = cfg.T, cfg.H, cfg.E, cfg.F, cfg.k
     ab = 4 if cfg.act == "f32" else 2
     sig = 4.0 / 128
     rows = int(sum(counts))
     G = cfg.groups
     act_groups = n_active1
-    w1 = act_groups * (2 * F * H) * (1 + 4.0 / (128 * 128))
-    w2 = act_groups * (H * F) * (1 + 4.0 / (128 * 128))
+    wb = (0.5 + 1.0 / 32) if fp4 else (1 + 4.0 / (128 * 128))
+    w1 = act_groups * (2 * F * H) * wb
+    w2 = act_groups * (H * F) * wb
     return {
         "gate_logits": dict(bytes=T * H * ab + E * H * 4 + T * E * 4, flops=2.0 * T * H * E, bound="alu"),
         "route": dict(bytes=T * E * 4 + T * k * 8, flops=0.0, bound="hbm"),
@@ -116,7 +123,8 @@ def main():
     import synth
     from dataclasses import replace
 
-    from block_scaled_fp8_top_amd.layer import MoELayer, MoELayerWeights, pack_expert_weights, quantize_expert_weights
+    from block_scaled_fp8_top_amd.layer import (MoELayer, MoELayerWeights, pack_expert_weights, quantize_expert_weights,
+                                                quantize_expert_weights_fp4)
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -130,25 +138,41 @@ def main():
     sf = 0 if cfg.score_fn == "softmax" else 1
     rcfg = M.router_cfg(cfg.E, cfg.k, sf, cfg.renorm, cfg.n_group, cfg.topk_group, cfg.group_score_topk)
     wg, b = synth.make_gate(cfg, 0, dev)
-    pow2 = a.scales == "pow2"
-    w1q, w1s, w2q, w2s = quantize_expert_weights(cfg.groups, cfg.H, cfg.F,
-                                                 lambda g: synth.make_expert(cfg, g, 0, dev), device=dev, pow2=pow2)
-    weights = pack_expert_weights(MoELayerWeights(wg=wg, bias=b, w1q=w1q, w1s=w1s, w2q=w2q, w2s=w2s, cfg=rcfg,
-                                                  shared=cfg.shared, pow2=pow2), keep_rowmajor=a.backward)
+    fp4 = a.weights == "fp4"
+    if fp4 and a.backward:
+        print("--weights fp4 is a forward-only format (no backward)", file=sys.stderr)
+        sys.exit(2)
+    pow2 = a.scales == "pow2" or fp4
     bwd_weights = None
-    if a.backward:
-        from block_scaled_fp8_top_amd.layer import prepare_backward_weights
-        bwd_weights = prepare_backward_weights(weights)
-        weights = replace(weights, w1q=None, w2q=None)
-    del w1q, w2q
+    if fp4:
+        w1p, w2p = quantize_expert_weights_fp4(cfg.groups, cfg.H, cfg.F, lambda g: synth.make_expert(cfg, g, 0, dev),
+                                               device=dev)
+        weights = MoELayerWeights(wg=wg, bias=b, w1q=None, w1s=None, w2q=None, w2s=None, cfg=rcfg, shared=cfg.shared,
+                                  w1p=w1p, w2p=w2p, pow2=True)
+        del w1p, w2p
+    else:
+        w1q, w1s, w2q, w2s = quantize_expert_weights(cfg.groups, cfg.H, cfg.F,
+                                                     lambda g: synth.make_expert(cfg, g, 0, dev), device=dev, pow2=pow2)
+        weights = pack_expert_weights(MoELayerWeights(wg=wg, bias=b, w1q=w1q, w1s=w1s, w2q=w2q, w2s=w2s, cfg=rcfg,
+                                                      shared=cfg.shared, pow2=pow2), keep_rowmajor=a.backward)
+        if a.backward:
+            from block_scaled_fp8_top_amd.layer import prepare_backward_weights
+            bwd_weights = prepare_backward_weights(weights)
+            weights = replace(weights, w1q=None, w2q=None)
+        del w1q, w2q
     wbytes = weights.w1p.data.numel() + weights.w2p.data.numel()
     copies = a.copies if a.copies > 0 else max(2, math.ceil((2 << 30) / wbytes))
     act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
     layers = [MoELayer(weights, cfg.T, act, dev)]
     for _ in range(1, copies):
-        wc = replace(weights, w1p=replace(weights.w1p, data=weights.w1p.data.clone()),
-                     w2p=replace(weights.w2p, data=weights.w2p.data.clone()), w1s=weights.w1s.clone(),
-                     w2s=weights.w2s.clone())
+        if fp4:
+            wc = replace(weights, w1p=replace(weights.w1p, data=weights.w1p.data.clone(),
+                                              scales=weights.w1p.scales.clone()),
+                         w2p=replace(weights.w2p, data=weights.w2p.data.clone(), scales=weights.w2p.scales.clone()))
+        else:
+            wc = replace(weights, w1p=replace(weights.w1p, data=weights.w1p.data.clone()),
+                         w2p=replace(weights.w2p, data=weights.w2p.data.clone()), w1s=weights.w1s.clone(),
+                         w2s=weights.w2s.clone())
         layers.append(MoELayer(wc, cfg.T, act, dev))
     layer = layers[0]
     x = synth.make_x(cfg, dev)
@@ -201,7 +225,7 @@ def main():
 
     counts = layer.disp.counts.cpu().numpy()
     n_active = int((counts > 0).sum())
-    model = stage_model(cfg, counts, n_active)
+    model = stage_model(cfg, counts, n_active, fp4)
     stages = {}
     for name in STAGES:
         m = model[name]
@@ -253,7 +277,7 @@ def main():
 
     cpu = None
     if not a.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, x, dev, pow2)
+        cpu = cpu_baseline(cfg, x, dev, pow2, fp4)
 
     tokens_per_s = cfg.T / (ms_per_step * 1e-3)
     line = {
@@ -269,12 +293,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 x fp8-e4m3 -> fp32 (GEMM); fp32 router; " + ("bf16" if cfg.act == "bf16" else "fp32") + " activations",
+        "dtype": ("fp4-e2m1 weights x fp8-e4m3" if fp4 else "fp8-e4m3 x fp8-e4m3") + " -> fp32 (GEMM); fp32 router; "
+                 + ("bf16" if cfg.act == "bf16" else "fp32") + " activations",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) weights, random-init)",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
                    "shared_experts": int(cfg.shared), "ffn": cfg.F, "top_k": cfg.k, "score": cfg.score_fn,
                    "rows": model["_rows"], "active_experts": n_active, "layer_copies": copies,
                    "weight_layout": "packed", "block_scales": "power of two" if pow2 else "amax/448 fp32",
+                   "expert_weights": "fp4 e2m1, 1x32 e8m0 scales" if fp4 else "fp8 e4m3, 128x128 scales",
                    "parallelism": "none (1 GPU)"},
         "gemm_tflops": round(gemm_tflops, 2),
         "gemm_frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
@@ -447,7 +473,7 @@ def stage_kernel(stage, layer):
     """The kernel a stage launches (the GEMM stages are one kernel each; the tile plan is part of
     the dispatch stage)."""
     import torch
-    p2 = ", pow2" if layer.w.pow2 else ""
+    p2 = ", fp4" if layer.w.fp4 else ", pow2" if layer.w.pow2 else ""
     if stage == "gemm1_swiglu":
         return f"grouped_gemm_kernel<{layer.plan.tile_rows}, swiglu_quant, packed{p2}>"
     if stage == "gemm2":
@@ -557,7 +583,7 @@ def payload_bench(a):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(cfg, x, dev, pow2=False):
+def cpu_baseline(cfg, x, dev, pow2=False, fp4=False):
     """The CPU oracle on a bounded sample of the same workload, timed on this host: the whole
     batch for small layers, else a seeded token sample evaluated per token."""
     import numpy as np
@@ -572,6 +598,8 @@ def cpu_baseline(cfg, x, dev, pow2=False):
 
     def expert(e):
         w1, w2 = synth.make_expert(cfg, e, 0, dev)
+        if fp4:
+            return L.quantize_expert_fp4(w1.cpu().numpy(), w2.cpu().numpy())
         return L.quantize_expert(w1.cpu().numpy(), w2.cpu().numpy(), pow2)
 
     ol = L.OracleLayer(wg=wg.cpu().numpy(), bias=None if b is None else b.cpu().numpy(), cfg=rc, shared=cfg.shared,

@@ -15,7 +15,9 @@ moe_route_backward (dz) -> moe_gate_backward (dx, dWg, db).
 
 This is the layer that "RL at 1T Scale: prime-rl Performance Deep Dive" runs in FP8 at inference
 (section "FP8 inference") and in block-scaled FP8 in the trainer (section "FP8 training"), with
-router replay (section "Router replay") as a mode of the same forward.
+router replay (section "Router replay") as a mode of the same forward.  Its forward also takes FP4
+expert weights (E2M1 in 1x32 blocks with E8M0 scales, the activations staying FP8 with power-of-two
+1x128 scales): the 4-bit variant the page lists as future work (section "Future work").
 """
 from __future__ import annotations
 
@@ -30,17 +32,19 @@ import block_scaled_fp8_top_amd as M
 @dataclass
 class MoELayerWeights:
     """Router gate and 128x128-block-quantised expert weights (group E is the shared expert).
-    The forward streams the packed copies (w1p, w2p) when present, else the row-major codes."""
+    The forward streams the packed copies (w1p, w2p) when present, else the row-major codes.
+    FP4 experts (see quantize_expert_weights_fp4) come only packed, as PackedWeightFP4 in w1p and
+    w2p with their own scales, and need pow2 (the activations' scales are then powers of two)."""
     wg: torch.Tensor                 # [E,H] fp32
     bias: Optional[torch.Tensor]     # [E] fp32
     w1q: Optional[torch.Tensor]      # [G,2F,H] e4m3 bytes (None once packed without a row-major copy)
-    w1s: torch.Tensor                # [G,2F/128,H/128] fp32
+    w1s: Optional[torch.Tensor]      # [G,2F/128,H/128] fp32 (None for FP4 experts)
     w2q: Optional[torch.Tensor]      # [G,H,F] e4m3 bytes
-    w2s: torch.Tensor                # [G,H/128,F/128] fp32
+    w2s: Optional[torch.Tensor]      # [G,H/128,F/128] fp32 (None for FP4 experts)
     cfg: M.RouterCfg
     shared: bool
-    w1p: Optional[M.PackedWeight] = None   # w1q packed for the SwiGLU epilogue
-    w2p: Optional[M.PackedWeight] = None   # w2q packed for the store epilogue
+    w1p: Optional[M.PackedWeight | M.PackedWeightFP4] = None   # w1 packed for the SwiGLU epilogue
+    w2p: Optional[M.PackedWeight | M.PackedWeightFP4] = None   # w2 packed for the store epilogue
     pow2: bool = False                     # power-of-two block scales: the weights were quantised so,
                                            # and the forward quantises x and h the same way
 
@@ -53,12 +57,16 @@ class MoELayerWeights:
         return int(self.wg.shape[1])
 
     @property
+    def fp4(self) -> bool:
+        return isinstance(self.w1p, M.PackedWeightFP4)
+
+    @property
     def F(self) -> int:
-        return int(self.w2s.shape[2]) * 128
+        return int(self.w2p.K) if self.fp4 else int(self.w2s.shape[2]) * 128
 
     @property
     def groups(self) -> int:
-        return int(self.w1s.shape[0])
+        return int(self.w1p.G) if self.fp4 else int(self.w1s.shape[0])
 
 
 def pack_expert_weights(weights: MoELayerWeights, keep_rowmajor: bool = True, stream=None) -> MoELayerWeights:
@@ -112,10 +120,31 @@ def quantize_expert_weights(groups: int, H: int, F: int, master, device="cuda", 
     return w1q, w1s, w2q, w2s
 
 
+def quantize_expert_weights_fp4(groups: int, H: int, F: int, master, device="cuda", stream=None):
+    """FP4 expert weights, the 4-bit variant: expert g from ``master(g) -> (w1 [2F,H], w2 [H,F])``
+    (fp32 or bf16 device tensors) is quantised to FP4 E2M1 in 1x32 blocks along the input
+    dimension with E8M0 scales (moe_quant_mxfp4), one expert at a time, and the codes are packed
+    for the two GEMM epilogues.  Returns (w1p, w2p) as PackedWeightFP4, for MoELayerWeights with
+    w1q = w1s = w2q = w2s = None and pow2=True."""
+    w1q = torch.empty((groups, 2 * F, H // 2), dtype=torch.uint8, device=device)
+    w1e = torch.empty((groups, 2 * F, H // 32), dtype=torch.uint8, device=device)
+    w2q = torch.empty((groups, H, F // 2), dtype=torch.uint8, device=device)
+    w2e = torch.empty((groups, H, F // 32), dtype=torch.uint8, device=device)
+    for g in range(groups):
+        w1, w2 = master(g)
+        M.moe_quant_mxfp4(w1, q=w1q[g], e8=w1e[g], stream=stream)
+        M.moe_quant_mxfp4(w2, q=w2q[g], e8=w2e[g], stream=stream)
+    w1p = M.moe_pack_weights_fp4(w1q, w1e, M.MOE_EPI_SWIGLU_QUANT, stream=stream)
+    w2p = M.moe_pack_weights_fp4(w2q, w2e, M.MOE_EPI_STORE, stream=stream)
+    return w1p, w2p
+
+
 class MoELayer:
     """Preallocated buffers for up to ``T_max`` tokens; ``forward`` returns a view of the output."""
 
     def __init__(self, weights: MoELayerWeights, T_max: int, act_dtype=torch.bfloat16, device="cuda"):
+        if weights.fp4 and not weights.pow2:
+            raise ValueError("FP4 expert weights need power-of-two activation scales (pow2=True)")
         self.w = weights
         self.T_max = T_max
         self.act = act_dtype
@@ -161,6 +190,8 @@ class MoELayer:
         if T != self.T_max:
             raise ValueError(f"layer buffers are sized for T={self.T_max}, got {T}")
         w = self.w
+        if training and w.fp4:
+            raise ValueError("FP4 expert weights are an inference format here: no training forward or backward")
         st = torch.cuda.current_stream() if stream is None else stream
 
         def mark(i):
@@ -248,6 +279,8 @@ class MoELayer:
         list of 9 timing events (11 with weight_grads) recorded before the first and after each stage."""
         if self.plan is None:
             raise RuntimeError("backward needs a forward first")
+        if self.w.fp4:
+            raise ValueError("FP4 expert weights are an inference format here: no backward")
         if x.shape[0] != self.T_max or tuple(dout.shape) != (self.T_max, self.w.H):
             raise ValueError("x / dout do not match the layer's buffers")
         w = self.w

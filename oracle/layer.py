@@ -31,11 +31,21 @@ import oracle as O
 
 @dataclass
 class ExpertWeights:
-    """One expert's quantised FFN: W1 [2F,H] (rows [0,F) gate, [F,2F) up), W2 [H,F]."""
+    """One expert's quantised FFN: W1 [2F,H] (rows [0,F) gate, [F,2F) up), W2 [H,F].  FP8: e4m3
+    codes with 128x128 fp32 block scales; fp4: FP4 E2M1 codes two per byte ([rows, cols/2]) with
+    1x32 E8M0 scale codes ([rows, cols/32]) in the scale fields."""
     w1q: np.ndarray
     w1s: np.ndarray
     w2q: np.ndarray
     w2s: np.ndarray
+    fp4: bool = False
+
+    def w1(self) -> np.ndarray:
+        """fp64 value of the quantised W1."""
+        return O.dequant_mxfp4(self.w1q, self.w1s) if self.fp4 else O.dequant_weight(self.w1q, self.w1s)
+
+    def w2(self) -> np.ndarray:
+        return O.dequant_mxfp4(self.w2q, self.w2s) if self.fp4 else O.dequant_weight(self.w2q, self.w2s)
 
 
 def quantize_expert(w1: np.ndarray, w2: np.ndarray, pow2: bool = False) -> ExpertWeights:
@@ -43,6 +53,15 @@ def quantize_expert(w1: np.ndarray, w2: np.ndarray, pow2: bool = False) -> Exper
     w1q, w1s = O.moe_quant_fp8_block(w1, 128, pow2)
     w2q, w2s = O.moe_quant_fp8_block(w2, 128, pow2)
     return ExpertWeights(w1q, w1s, w2q, w2s)
+
+
+def quantize_expert_fp4(w1: np.ndarray, w2: np.ndarray) -> ExpertWeights:
+    """FP4 (E2M1 in 1x32 blocks along the input dimension, E8M0 scales) quantisation of one
+    expert's fp32 masters: the 4-bit variant of the expert weights, with the activations kept in
+    FP8 (power-of-two 1x128 scales)."""
+    w1q, w1e = O.quant_mxfp4(np.asarray(w1, np.float32))
+    w2q, w2e = O.quant_mxfp4(np.asarray(w2, np.float32))
+    return ExpertWeights(w1q, w1e, w2q, w2e, fp4=True)
 
 
 @dataclass
@@ -104,10 +123,11 @@ def forward_dispatch(layer: OracleLayer, x: np.ndarray, replay=None, record=None
     w1s = np.stack([layer.get(g).w1s for g in range(G)])
     w2q = np.stack([layer.get(g).w2q for g in range(G)])
     w2s = np.stack([layer.get(g).w2s for g in range(G)])
-    g1 = O.moe_grouped_gemm_fp8(aq, as_, offsets, w1q, w1s)
+    gemm = O.moe_grouped_gemm_fp4w if layer.get(0).fp4 else O.moe_grouped_gemm_fp8
+    g1 = gemm(aq, as_, offsets, w1q, w1s)
     h = O.swiglu(g1, F)
     hq, hs = O.moe_quant_fp8_block(h, 1, layer.pow2)
-    y = O.moe_grouped_gemm_fp8(hq, hs, offsets, w2q, w2s)
+    y = gemm(hq, hs, offsets, w2q, w2s)
     y_act = to_act(y, layer.act)
     T = x.shape[0]
     y_sh = y_act[offsets[E]:offsets[E] + T] if layer.shared else None
@@ -118,10 +138,10 @@ def forward_dispatch(layer: OracleLayer, x: np.ndarray, replay=None, record=None
 
 def expert_ffn(ew: ExpertWeights, xq: np.ndarray, xs: np.ndarray, F: int, act: str, pow2: bool = False):
     """FFN_e on already-quantised activation rows: returns (g1, h, hq, hs, y, y_act)."""
-    g1 = O.dequant_act(xq, xs) @ O.dequant_weight(ew.w1q, ew.w1s).T
+    g1 = O.dequant_act(xq, xs) @ ew.w1().T
     h = O.swiglu(g1, F)
     hq, hs = O.moe_quant_fp8_block(h, 1, pow2)
-    y = O.dequant_act(hq, hs) @ O.dequant_weight(ew.w2q, ew.w2s).T
+    y = O.dequant_act(hq, hs) @ ew.w2().T
     return g1, h, hq, hs, y, to_act(y, act)
 
 

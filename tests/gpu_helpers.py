@@ -12,7 +12,8 @@ import block_scaled_fp8_top_amd as M
 import oracle as O
 import oracle.layer as L
 import synth
-from block_scaled_fp8_top_amd.layer import MoELayer, MoELayerWeights, pack_expert_weights, quantize_expert_weights
+from block_scaled_fp8_top_amd.layer import (MoELayer, MoELayerWeights, pack_expert_weights, quantize_expert_weights,
+                                            quantize_expert_weights_fp4)
 
 DEV = "cuda"
 TOL = 2e-2          # max |gpu - ref| / max |ref| for GEMM and combine outputs
@@ -25,8 +26,15 @@ def cfgs_for(cfg: synth.LayerConfig):
     return M.router_cfg(*args), O.router_cfg(*args)
 
 
-def gpu_weights(cfg: synth.LayerConfig, layer: int = 0, perturbed: bool = False, pow2: bool = False) -> MoELayerWeights:
+def gpu_weights(cfg: synth.LayerConfig, layer: int = 0, perturbed: bool = False, pow2: bool = False,
+                fp4: bool = False) -> MoELayerWeights:
+    """fp4: FP4 experts (packed only), with power-of-two activation scales."""
     wg, b = synth.make_gate(cfg, layer, DEV, perturbed=perturbed)
+    if fp4:
+        w1p, w2p = quantize_expert_weights_fp4(
+            cfg.groups, cfg.H, cfg.F, lambda g: synth.make_expert(cfg, g, layer, DEV, perturbed=perturbed), device=DEV)
+        return MoELayerWeights(wg=wg, bias=b, w1q=None, w1s=None, w2q=None, w2s=None, cfg=cfgs_for(cfg)[0],
+                               shared=cfg.shared, w1p=w1p, w2p=w2p, pow2=True)
     w1q, w1s, w2q, w2s = quantize_expert_weights(
         cfg.groups, cfg.H, cfg.F, lambda g: synth.make_expert(cfg, g, layer, DEV, perturbed=perturbed), device=DEV,
         pow2=pow2)
@@ -35,17 +43,20 @@ def gpu_weights(cfg: synth.LayerConfig, layer: int = 0, perturbed: bool = False,
                                                cfg=cfgs_for(cfg)[0], shared=cfg.shared, pow2=pow2))
 
 
-def oracle_layer(cfg: synth.LayerConfig, layer: int = 0, perturbed: bool = False, pow2: bool = False) -> L.OracleLayer:
+def oracle_layer(cfg: synth.LayerConfig, layer: int = 0, perturbed: bool = False, pow2: bool = False,
+                 fp4: bool = False) -> L.OracleLayer:
     """Oracle view of the same layer: gate and masters re-drawn from the same GPU streams and
-    copied to the host; the oracle quantises each expert it needs."""
+    copied to the host; the oracle quantises each expert it needs (fp4: FP4 experts, pow2 scales)."""
     wg, b = synth.make_gate(cfg, layer, DEV, perturbed=perturbed)
 
     def expert(e):
         w1, w2 = synth.make_expert(cfg, e, layer, DEV, perturbed=perturbed)
+        if fp4:
+            return L.quantize_expert_fp4(w1.cpu().numpy(), w2.cpu().numpy())
         return L.quantize_expert(w1.cpu().numpy(), w2.cpu().numpy(), pow2)
 
     return L.OracleLayer(wg=wg.cpu().numpy(), bias=None if b is None else b.cpu().numpy(), cfg=cfgs_for(cfg)[1],
-                         shared=cfg.shared, act=cfg.act, F=cfg.F, expert=expert, pow2=pow2)
+                         shared=cfg.shared, act=cfg.act, F=cfg.F, expert=expert, pow2=pow2 or fp4)
 
 
 def host(t: torch.Tensor) -> np.ndarray:

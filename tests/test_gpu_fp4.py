@@ -1,7 +1,8 @@
 """FP4 expert weights on the GPU against the oracle, through the C ABI: the MX quantisation bit for
 bit (codes and E8M0 scales), the grouped GEMM with packed FP4 weights exactly on integer cases for
 every tile height (every product and partial sum is exact), against the oracle's fp64 product on
-random weights, and the SwiGLU epilogue's h codes."""
+random weights, the SwiGLU epilogue's h codes, and the MoE layer forward with FP4 experts (the tiny
+layer's every intermediate, sampled tokens of the full-size decode and prefill layers)."""
 import itertools
 
 import numpy as np
@@ -10,8 +11,10 @@ import torch
 
 import block_scaled_fp8_top_amd as M
 import oracle as O
+import oracle.layer as L
 import synth
-from gpu_helpers import DEV, assert_equal, host, rel_err
+from block_scaled_fp8_top_amd.layer import MoELayer
+from gpu_helpers import DEV, TOL, assert_equal, gpu_weights, host, oracle_layer, rel_err, rows_host
 
 pytestmark = pytest.mark.gpu
 TILES = [32, 48, 64, 128]
@@ -94,5 +97,48 @@ def test_fp4_gemm_random(name, tile):
     dg, dr = tab[gq] * np.repeat(gs, 128, 1), tab[rq] * np.repeat(rs, 128, 1)
     step = np.abs(dr) / 8 + np.repeat(rs, 128, 1) * (2.0 ** -9 + 448 * 1e-3)
     assert np.all(np.abs(dg - dr)[same] <= step[same] * 1.0001)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_fp4_layer_tiny_every_intermediate():
+    cfg = synth.CONFIGS["tiny"]
+    gw = gpu_weights(cfg, fp4=True)
+    lay = MoELayer(gw, cfg.T, torch.float32)
+    x = synth.make_x(cfg, DEV)
+    out = lay.forward(x)
+    ol = oracle_layer(cfg, fp4=True)
+    r = L.forward_dispatch(ol, host(x))
+    assert_equal("idx", host(lay.idx), r["idx"])
+    assert_equal("xq", host(lay.xq), r["xq"])
+    assert_equal("xs", host(lay.xs), r["xs"])
+    n = int(r["offsets"][-1])
+    assert_equal("aq", host(lay.disp.aq)[:n], r["aq"])
+    assert rel_err(host(lay.y)[:n], r["y_act"]) < TOL
+    err = rel_err(host(out), r["out"])
+    print(f"tiny fp4 layer output err {err:.3e}")
+    assert err < TOL
+    with pytest.raises(ValueError):
+        lay.forward(x, training=True)
+
+
+@pytest.mark.parametrize("name,samples", [("decode", 32), ("prefill", 4)])
+def test_fp4_layer_sampled(name, samples):
+    cfg = synth.CONFIGS[name]
+    gw = gpu_weights(cfg, fp4=True)
+    act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
+    lay = MoELayer(gw, cfg.T, act)
+    x = synth.make_x(cfg, DEV)
+    out = lay.forward(x)
+    torch.cuda.synchronize()
+    toks = synth.sample_tokens(cfg.T, samples, cfg.seed)
+    ol = oracle_layer(cfg, fp4=True)
+    r = L.forward_sampled(ol, rows_host(x, toks))
+    assert_equal("idx", rows_host(lay.idx, toks), r["idx"])
+    assert_equal("xq", rows_host(lay.xq, toks), r["xq"])
+    err = rel_err(rows_host(out, toks), r["out"])
+    print(f"{name} fp4 layer output err {err:.3e}")
+    assert err < TOL
+    del lay, gw, x, out
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

@@ -110,3 +110,80 @@ def test_grouped_gemm_fp4_weights_exact_integers():
         assert np.array_equal(got[r0:r1], ref)
         assert np.array_equal(O.dequant_mxfp4(wq[g], we8[g]), wv[g].astype(np.float64))   # exactly representable
         assert np.array_equal(got[r0:r1], av[r0:r1].astype(np.float64) @ wv[g].astype(np.float64).T)
+
+
+def _fp4_layer_pair(cfg, int_weights: bool):
+    """The same small layer with FP4 experts and, for int_weights, with power-of-two FP8 experts
+    too.  int_weights: masters are 2^-5 times integers in {0, +-1, +-2, +-3, +-4, +-6}, which
+    both formats hold exactly (FP4 with a 1x32 scale of 2^-5 or 2^-6; e4m3 with a 128x128 scale)."""
+    import oracle.layer as L
+    import synth
+    wg, b = synth.make_gate(cfg, 0, "cpu")
+    rc = O.router_cfg(cfg.E, cfg.k, O.SOFTMAX if cfg.score_fn == "softmax" else O.SIGMOID, cfg.renorm,
+                      cfg.n_group, cfg.topk_group, cfg.group_score_topk)
+
+    def master(e):
+        if not int_weights:
+            w1, w2 = synth.make_expert(cfg, e, 0, "cpu")
+            return w1.numpy(), w2.numpy()
+        rng = np.random.default_rng(100 + e)
+        vals = [-6, -4, -3, -2, -1, 0, 1, 2, 3, 4, 6]
+        w1 = rng.choice(vals, size=(2 * cfg.F, cfg.H)).astype(np.float32) * 2.0 ** -5
+        w2 = rng.choice(vals, size=(cfg.H, cfg.F)).astype(np.float32) * 2.0 ** -5
+        return w1, w2
+
+    def mk(expert):
+        return L.OracleLayer(wg=wg.numpy(), bias=None if b is None else b.numpy(), cfg=rc, shared=cfg.shared,
+                             act=cfg.act, F=cfg.F, expert=expert, pow2=True)
+
+    fp4 = mk(lambda e: L.quantize_expert_fp4(*master(e)))
+    fp8 = mk(lambda e: L.quantize_expert(*master(e), pow2=True))
+    return fp4, fp8, master
+
+
+@pytest.mark.parametrize("name", ["tiny", "prefill_small"])
+def test_fp4_layer_dispatch_equals_per_token(name):
+    """The FP4-expert layer's dispatch path equals per-token evaluation with no dispatch (the same
+    composition pin as for FP8 experts: the grouped FP4 GEMM and the per-expert products agree)."""
+    import oracle.layer as L
+    from test_oracle_layer import SMALL, x_f32
+    cfg = SMALL[name]
+    lay, _, _ = _fp4_layer_pair(cfg, False)
+    x = x_f32(cfg)
+    full = L.forward_dispatch(lay, x)
+    tok = L.forward_token(lay, x)
+    assert np.array_equal(full["idx"], tok["idx"])
+    assert L.rel_err(full["out"], tok["out"]) < 1e-13
+
+
+def test_fp4_layer_equals_fp8_layer_on_shared_values():
+    """On weights both formats represent exactly, the FP4-expert layer and the power-of-two FP8
+    layer hold the same expert values, so the two layers agree to fp64 rounding; a wrong E2M1
+    value, nibble order, scale exponent or GEMM operand in the FP4 side would break this."""
+    import oracle.layer as L
+    from test_oracle_layer import SMALL, x_f32
+    cfg = SMALL["decode_small"]
+    l4, l8, master = _fp4_layer_pair(cfg, True)
+    for e in range(3):
+        w1, w2 = master(e)
+        assert np.array_equal(l4.get(e).w1(), w1.astype(np.float64))
+        assert np.array_equal(l8.get(e).w2(), w2.astype(np.float64))
+    x = x_f32(cfg)
+    a, c = L.forward_dispatch(l4, x), L.forward_dispatch(l8, x)
+    assert np.array_equal(a["hq"], c["hq"]) and np.array_equal(a["hs"], c["hs"])
+    assert L.rel_err(a["out"], c["out"]) < 1e-13
+
+
+def test_fp4_quantisation_error_is_moderate_context_only():
+    """Context, not parity: FP4 experts move the tiny layer more than FP8 experts do, but stay
+    within tens of percent of the unquantised layer."""
+    import oracle.layer as L
+    from test_oracle_layer import SMALL, x_f32
+    cfg = SMALL["tiny"]
+    l4, l8, master = _fp4_layer_pair(cfg, False)
+    x = x_f32(cfg)
+    u = L.forward_unquantized(l4, x, master)
+    e4 = L.rel_err(L.forward_dispatch(l4, x)["out"], u)
+    e8 = L.rel_err(L.forward_dispatch(l8, x)["out"], u)
+    print(f"fp4 layer err {e4:.3e}, fp8 pow2 layer err {e8:.3e}")
+    assert e8 < e4 < 0.4
