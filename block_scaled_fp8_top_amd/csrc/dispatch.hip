@@ -45,13 +45,19 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
   __shared__ int part[1024];
   const int e = threadIdx.x;
+  // expert e's total over the chunks: 16 independent loads in flight per step (a load-add chain
+  // over 128 chunks would cost 128 memory round trips)
   int total = 0;
   if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = chunk_counts[(int64_t)c * E + e];
-      chunk_base[(int64_t)c * E + e] = total;
-      total += v;
+    int c = 0;
+    for (; c + 16 <= nchunks; c += 16) {
+      int v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = chunk_counts[(int64_t)(c + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) total += v[i];
     }
+    for (; c < nchunks; ++c) total += chunk_counts[(int64_t)c * E + e];
   }
   // inclusive block scan of totals over e (Hillis-Steele; integers, so order does not matter)
   part[e] = total;
@@ -66,7 +72,23 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   if (e < E) {
     counts[e] = total;
     offsets[e] = excl;
-    for (int c = 0; c < nchunks; ++c) chunk_base[(int64_t)c * E + e] += excl;
+    // each chunk's base row for expert e: the expert's offset plus its counts in earlier chunks
+    int run = excl, c = 0;
+    for (; c + 16 <= nchunks; c += 16) {
+      int v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = chunk_counts[(int64_t)(c + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        chunk_base[(int64_t)(c + i) * E + e] = run;
+        run += v[i];
+      }
+    }
+    for (; c < nchunks; ++c) {
+      const int v = chunk_counts[(int64_t)c * E + e];
+      chunk_base[(int64_t)c * E + e] = run;
+      run += v;
+    }
   }
   if (e == 0) {
     const int routed = part[E - 1];

@@ -140,11 +140,15 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __rest
 }
 
 // ------------------------------------------------------------------------------------------------
-// tiles[i] = {group, first row, index of the group's first tile, number of tiles of the group}
+// tiles[i] = {group, first row, index of the group's first tile, number of tiles of the group}.
+// A block scan gives each group's first tile; then every thread writes tiles (each finds its group
+// by binary search over the first tiles), so a long group's tiles are not written by one thread.
+constexpr int TILE_MAP_MAXG = 4096;
 __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restrict__ offsets, int groups, int bm,
                                                         int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
                                                         int max_tiles) {
   __shared__ int part[1024];
+  __shared__ int first[TILE_MAP_MAXG + 1];   // first[g] = tiles before group g; first[groups] = all
   __shared__ int carry;
   if (threadIdx.x == 0) carry = 0;
   __syncthreads();
@@ -160,14 +164,27 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
       part[threadIdx.x] += v;
       __syncthreads();
     }
-    const int start = carry + part[threadIdx.x] - nt;
-    if (g < groups)
-      for (int i = 0; i < nt && start + i < max_tiles; ++i) tiles[start + i] = make_int4(g, offsets[g] + i * bm, start, nt);
+    if (g < groups) first[g] = carry + part[threadIdx.x] - nt;
     __syncthreads();
     if (threadIdx.x == 1023) carry += part[1023];
     __syncthreads();
   }
-  if (threadIdx.x == 0) *ntiles = min(carry, max_tiles);
+  if (threadIdx.x == 0) first[groups] = carry;
+  __syncthreads();
+  const int total = min(carry, max_tiles);
+  for (int t = threadIdx.x; t < total; t += 1024) {
+    // the last group whose first tile is at or before t (empty groups share their first tile
+    // with the next group, so the last such group is the one that owns t)
+    int lo = 0, hi = groups - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (first[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    const int i = t - first[lo];
+    tiles[t] = make_int4(lo, offsets[lo] + i * bm, first[lo], first[lo + 1] - first[lo]);
+  }
+  if (threadIdx.x == 0) *ntiles = total;
 }
 
 // wait until at most n of this wave's vector memory instructions are outstanding (n is
