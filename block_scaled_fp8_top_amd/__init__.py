@@ -32,7 +32,8 @@ MOE_SCALE_AMAX, MOE_SCALE_POW2 = 0, 1
 EXPORTED = ("moe_gate_logits", "moe_route", "moe_replay_route", "moe_replay_gate", "moe_router_score_eval",
             "moe_quant_fp8_block",
             "moe_dispatch", "moe_pack_weights_fp8", "moe_packed_weight_bytes", "moe_grouped_gemm_plan",
-            "moe_grouped_gemm_fp8_planned", "moe_grouped_gemm_fp8_swiglu_save", "moe_grouped_gemm_fp8", "moe_combine", "moe_payload_bytes",
+            "moe_grouped_gemm_fp8_planned", "moe_grouped_gemm_fp8_swiglu_save", "moe_grouped_gemm_fp8_gather",
+            "moe_grouped_gemm_fp8", "moe_combine", "moe_payload_bytes",
             "moe_payload_pack", "moe_payload_unpack", "moe_payload_to_host", "moe_payload_from_host",
             "moe_combine_backward", "moe_swiglu_backward_quant", "moe_route_backward", "moe_gate_backward",
             "moe_gate_backward_workspace", "moe_transpose_fp8_blocks", "moe_wgrad_max_tiles", "moe_wgrad_tiles",
@@ -92,6 +93,8 @@ def lib():
                                          ctypes.c_int, P, P],
         "moe_grouped_gemm_fp8_swiglu_save": [ctypes.POINTER(GemmPlan), P, P, P, P, I32, P, I32, I32, I32, P, P, P,
                                              P],
+        "moe_grouped_gemm_fp8_gather": [ctypes.POINTER(GemmPlan), P, I64, P, P, P, P, I32, P, I32, I32, I32, I32, P,
+                                        ctypes.c_int, P, P, P],
         "moe_combine": [P, ctypes.c_int, P, P, I64, I32, I32, P, P, ctypes.c_int, P],
         "moe_payload_bytes": [I64, I32],
         "moe_payload_pack": [P, I64, I32, P, P, P],
@@ -311,7 +314,9 @@ class Dispatched:
 
 def moe_dispatch(topk_idx: torch.Tensor, num_experts: int, append_shared: bool, xq: Optional[torch.Tensor] = None,
                  xs: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                 out: Optional[Dispatched] = None, stream=None) -> Dispatched:
+                 out: Optional[Dispatched] = None, stream=None, copy_codes: bool = True) -> Dispatched:
+    """copy_codes=False: only the scales are permuted (aq is None); the grouped GEMM then gathers
+    the codes from xq through src_token (moe_grouped_gemm_fp8 with a_rows)."""
     T, k = topk_idx.shape
     _dev(topk_idx, "topk_idx", torch.int32)
     dev = topk_idx.device
@@ -333,7 +338,7 @@ def moe_dispatch(topk_idx: torch.Tensor, num_experts: int, append_shared: bool, 
             offsets=torch.empty(G + 1, dtype=torch.int32, device=dev),
             dest_row=torch.empty((T, k), dtype=torch.int32, device=dev),
             src_token=torch.empty(max(max_rows, 1), dtype=torch.int32, device=dev),
-            aq=torch.empty((max_rows, H), dtype=FP8, device=dev) if xq is not None else None,
+            aq=torch.empty((max_rows, H), dtype=FP8, device=dev) if xq is not None and copy_codes else None,
             as_=torch.empty((max_rows, H // 128), dtype=torch.float32, device=dev) if xq is not None else None,
             max_rows=max_rows)
     _check(lib().moe_dispatch(_p(topk_idx), T, k, num_experts, int(bool(append_shared)), _p(xq), _p(xs), H,
@@ -434,7 +439,8 @@ def moe_grouped_gemm_plan(offsets: torch.Tensor, max_rows: int, workspace: torch
 def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tensor, b, bs: torch.Tensor,
                          epilogue: int = MOE_EPI_STORE, out_dtype=torch.bfloat16, out=None, out_scales=None,
                          workspace: Optional[torch.Tensor] = None, stream=None, tile_rows: int = 0,
-                         plan: Optional[GemmPlan] = None, pow2: bool = False, save_g: Optional[torch.Tensor] = None):
+                         plan: Optional[GemmPlan] = None, pow2: bool = False, save_g: Optional[torch.Tensor] = None,
+                         a_rows: Optional[torch.Tensor] = None):
     """a [max_rows,K] uint8, as_ [max_rows,K/128], offsets [G+1] (device), b [G,N,K] uint8 or a
     PackedWeight packed for this epilogue, bs [G,N/128,K/128].
     STORE -> out [max_rows,N] (bf16/fp32); SWIGLU_QUANT -> (h codes [max_rows,N/2] uint8, scales [max_rows,N/256]).
@@ -442,8 +448,11 @@ def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tens
     plan: a plan from moe_grouped_gemm_plan for these offsets and max_rows (then no workspace is
     needed and tile_rows is the plan's).  pow2: every scale in as_ and bs is a power of two (the
     matrix cores apply them; the SwiGLU epilogue writes power-of-two scales for h).
-    save_g (SwiGLU with a plan only): fp32 [max_rows, N] that also receives the GEMM output G."""
-    max_rows, K = a.shape
+    save_g (SwiGLU with a plan only): fp32 [max_rows, N] that also receives the GEMM output G.
+    a_rows (with a plan only): int32 [max_rows] (the dispatch's src_token); group row r then reads
+    the codes of row a_rows[r] of a [a_count, K], while as_ [max_rows, K/128] stays in group order."""
+    a_count, K = a.shape
+    max_rows = as_.shape[0] if a_rows is not None else a_count
     if isinstance(b, PackedWeightFP4):
         if b.epilogue != epilogue:
             raise ValueError("weight was packed for another epilogue")
@@ -464,6 +473,10 @@ def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tens
         raise ValueError("K mismatch")
     _dev(a, "a", FP8)
     _dev(as_, "as", torch.float32, (max_rows, K // 128))
+    if a_rows is not None:
+        _dev(a_rows, "a_rows", torch.int32)
+        if a_rows.shape[0] < max_rows or plan is None:
+            raise ValueError("a_rows needs a plan and one entry per group row")
     _dev(offsets, "offsets", torch.int32, (G + 1,))
     if b_layout == MOE_B_PACKED_FP4:
         _dev(bs, "bs", torch.uint8)
@@ -490,10 +503,16 @@ def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tens
         osc = torch.empty((max_rows, F // 128), dtype=torch.float32, device=dev) if out_scales is None else \
             _dev(out_scales, "out_scales", torch.float32, (max_rows, F // 128))
     mode = MOE_SCALE_POW2 if pow2 else MOE_SCALE_AMAX
+    if save_g is not None and (plan is None or epilogue != MOE_EPI_SWIGLU_QUANT):
+        raise ValueError("save_g needs a plan and the SwiGLU epilogue")
     if save_g is not None:
-        if plan is None or epilogue != MOE_EPI_SWIGLU_QUANT:
-            raise ValueError("save_g needs a plan and the SwiGLU epilogue")
         _dev(save_g, "save_g", torch.float32, (max_rows, N))
+    if a_rows is not None:
+        _check(lib().moe_grouped_gemm_fp8_gather(ctypes.byref(plan), _p(a), a_count, _p(a_rows), _p(as_), _p(offsets),
+                                                 _p(b_t), b_layout, _p(bs), N, K, epilogue, mode, _p(out), code,
+                                                 _p(osc), _p(save_g), _stream(stream)), "moe_grouped_gemm_fp8_gather")
+        return out if epilogue == MOE_EPI_STORE else (out, osc)
+    if save_g is not None:
         _check(lib().moe_grouped_gemm_fp8_swiglu_save(ctypes.byref(plan), _p(a), _p(as_), _p(offsets), _p(b_t),
                                                       b_layout, _p(bs), N, K, mode, _p(out), _p(osc), _p(save_g),
                                                       _stream(stream)), "moe_grouped_gemm_fp8_swiglu_save")

@@ -155,9 +155,11 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint8_t* __restrict_
   for (int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64; row < rows && row < max_rows;
        row += (int64_t)gridDim.x * 4) {
     const int64_t t = src_token[row];
-    const uint4* src = reinterpret_cast<const uint4*>(xq + t * H);
-    uint4* dst = reinterpret_cast<uint4*>(aq + row * H);
-    for (int c = lane; c < H / 16; c += 64) dst[c] = src[c];
+    if (aq) {   // codes too (without them a grouped GEMM gathers the rows through src_token)
+      const uint4* src = reinterpret_cast<const uint4*>(xq + t * H);
+      uint4* dst = reinterpret_cast<uint4*>(aq + row * H);
+      for (int c = lane; c < H / 16; c += 64) dst[c] = src[c];
+    }
     const int nsc = H / 128;
     for (int c = lane; c < nsc; c += 64) as[row * nsc + c] = xs[t * nsc + c];
   }
@@ -263,11 +265,12 @@ extern "C" int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32
                             size_t workspace_bytes, void* stream) {
   if (T < 0 || k < 1 || k > 64 || E < 1 || E > MAXE) return MOE_ERR_SHAPE;
   if (T * (int64_t)k + T > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
-  const bool copy_rows = xq || aq;
+  // rows: aq given -> codes and scales are permuted; only as given -> only the scales
+  const bool copy_rows = aq || as;
   if (copy_rows && (H < 128 || H % 128 != 0)) return MOE_ERR_SHAPE;
   if (!counts || !offsets) return MOE_ERR_NULL;
   if (T > 0 && (!topk_idx || !dest_row || !src_token)) return MOE_ERR_NULL;
-  if (copy_rows && (!xq || !xs || !aq || !as)) return MOE_ERR_NULL;
+  if (copy_rows && (!xs || !as || (aq && !xq))) return MOE_ERR_NULL;
   const int64_t nch = nchunks_for(T, k);
   if (!workspace || workspace_bytes < moe_dispatch_workspace(T, k, E)) return MOE_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);

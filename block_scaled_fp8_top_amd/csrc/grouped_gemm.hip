@@ -226,7 +226,8 @@ __device__ __forceinline__ Unit unit_at(int u, int ny, const int4* __restrict__ 
 // the current unit's last steps and epilogue execute, so no unit pays the pipeline fill again.
 template <int BM, int EPI, bool OUT_BF16, bool PACKED, bool POW2, bool FP4 = false>
 __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
-    const uint8_t* __restrict__ a, const float* __restrict__ as, const int32_t* __restrict__ offsets,
+    const uint8_t* __restrict__ a, const int32_t* __restrict__ a_rows, int a_count, const float* __restrict__ as,
+    const int32_t* __restrict__ offsets,
     const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles, int ny, const uint8_t* __restrict__ b,
     const float* __restrict__ bs, int N, int K, void* __restrict__ out, float* __restrict__ out_scales,
     float* __restrict__ g_out) {
@@ -289,7 +290,19 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     const Unit un_ = unit_at(me + (I) * G, ny, tiles, offsets, BM);                                 \
     _Pragma("unroll") for (int j_ = 0; j_ < T::A_PW; ++j_) {                                        \
       const int r_ = (a_i0 + j_) * 8 + (lane >> 3);                                                \
-      aoff[j_] = (uint32_t)min(un_.row0 + r_, un_.row_end - 1) * (uint32_t)K + (((lane & 7) ^ swz_mask(r_)) << 4); \
+      int src_ = min(un_.row0 + r_, un_.row_end - 1);                                               \
+      if (a_rows) {                                                                                 \
+        /* gathered rows: the 8 rows of instruction j_ are wave-uniform, so their row ids come */  \
+        /* through the scalar cache (a vector load here would make the compiler drain the DMA */   \
+        /* in flight before using it); each lane then selects its own, clamped to a's rows */      \
+        int g8_[8];                                                                                 \
+        _Pragma("unroll") for (int q_ = 0; q_ < 8; ++q_)                                            \
+          g8_[q_] = a_rows[min(un_.row0 + (a_i0 + j_) * 8 + q_, un_.row_end - 1)];                  \
+        int t_ = g8_[0];                                                                            \
+        _Pragma("unroll") for (int q_ = 1; q_ < 8; ++q_) t_ = (lane >> 3) == q_ ? g8_[q_] : t_;     \
+        src_ = min(max(t_, 0), a_count - 1);                                                        \
+      }                                                                                             \
+      aoff[j_] = (uint32_t)src_ * (uint32_t)K + (((lane & 7) ^ swz_mask(r_)) << 4);                 \
     }                                                                                               \
     _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                              \
       if (PACKED) {                                                                                 \
@@ -608,42 +621,43 @@ int auto_tile_rows(int64_t max_rows, int groups) {
 }
 
 template <int BM, bool PACKED, bool POW2, bool FP4 = false>
-void launch3(unsigned grid, hipStream_t st, int epilogue, int out_dtype, const uint8_t* a, const float* as,
+void launch3(unsigned grid, hipStream_t st, int epilogue, int out_dtype, const uint8_t* a, const int32_t* a_rows,
+             int a_count, const float* as,
              const int32_t* offsets, const int4* tiles, const int32_t* ntiles, int ny, const uint8_t* b,
              const float* bs, int N, int K, void* out, float* out_scales, float* g_out) {
   if (epilogue == MOE_EPI_STORE) {
     if (out_dtype == MOE_BF16)
       grouped_gemm_kernel<BM, 0, true, PACKED, POW2, FP4><<<grid, NTHREADS, 0, st>>>(
-          a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, nullptr, nullptr);
+          a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, nullptr, nullptr);
     else
       grouped_gemm_kernel<BM, 0, false, PACKED, POW2, FP4><<<grid, NTHREADS, 0, st>>>(
-          a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, nullptr, nullptr);
+          a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, nullptr, nullptr);
   } else {
     grouped_gemm_kernel<BM, 1, false, PACKED, POW2, FP4><<<grid, NTHREADS, 0, st>>>(
-        a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales, g_out);
+        a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales, g_out);
   }
 }
 
 // b_layout: 0 row-major, 1 packed FP8, 2 packed FP4 (power-of-two scales only)
 template <int BM>
 void launch(unsigned grid, hipStream_t st, int b_layout, int epilogue, int scale_mode, int out_dtype,
-            const uint8_t* a, const float* as, const int32_t* offsets, const int4* tiles, const int32_t* ntiles,
+            const uint8_t* a, const int32_t* a_rows, int a_count, const float* as, const int32_t* offsets, const int4* tiles, const int32_t* ntiles,
             int ny, const uint8_t* b, const float* bs, int N, int K, void* out, float* out_scales, float* g_out) {
   const bool p2 = scale_mode == MOE_SCALE_POW2;
   if (b_layout == MOE_B_PACKED_FP4)
-    launch3<BM, true, true, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+    launch3<BM, true, true, true>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
                                   out_scales, g_out);
   else if (b_layout == MOE_B_PACKED && p2)
-    launch3<BM, true, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+    launch3<BM, true, true>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
                             out_scales, g_out);
   else if (b_layout == MOE_B_PACKED)
-    launch3<BM, true, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+    launch3<BM, true, false>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
                              out_scales, g_out);
   else if (p2)
-    launch3<BM, false, true>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+    launch3<BM, false, true>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
                              out_scales, g_out);
   else
-    launch3<BM, false, false>(grid, st, epilogue, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+    launch3<BM, false, false>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
                               out_scales, g_out);
 }
 
@@ -739,7 +753,8 @@ extern "C" int moe_grouped_gemm_plan(const int32_t* offsets, int32_t groups, int
 }
 
 namespace {
-int run_planned(const moe_gemm_plan* plan, const uint8_t* a, const float* as, const int32_t* offsets,
+int run_planned(const moe_gemm_plan* plan, const uint8_t* a, const int32_t* a_rows, int64_t a_count, const float* as,
+                const int32_t* offsets,
                 const uint8_t* b, int32_t b_layout, const float* bs, int32_t N, int32_t K, int32_t epilogue,
                 int32_t scale_mode, void* out, int out_dtype, float* out_scales, float* g_out, void* stream) {
   if (!plan) return MOE_ERR_NULL;
@@ -750,6 +765,8 @@ int run_planned(const moe_gemm_plan* plan, const uint8_t* a, const float* as, co
   if (rc != MOE_OK) return rc;
   if (bm != 32 && bm != 48 && bm != 64 && bm != 128) return MOE_ERR_ARG;
   if (max_rows == 0) return MOE_OK;
+  // gathered rows: a holds a_count rows; every byte offset into it must fit 32 bits like a's own
+  if (a_rows && (a_count < 1 || (a_count + 1) * (int64_t)K >= ((int64_t)1 << 32))) return MOE_ERR_SHAPE;
   if (!a || !as || !offsets || !b || !bs || !out || !plan->workspace) return MOE_ERR_NULL;
   if (epilogue == MOE_EPI_SWIGLU_QUANT && !out_scales) return MOE_ERR_NULL;
   hipStream_t st = as_stream(stream);
@@ -765,16 +782,16 @@ int run_planned(const moe_gemm_plan* plan, const uint8_t* a, const float* as, co
   // the worst-case number of units
   const unsigned grid = (unsigned)std::min<int64_t>(nwg, cus);
   if (bm == 32)
-    launch<32>(grid, st, b_layout, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+    launch<32>(grid, st, b_layout, epilogue, scale_mode, out_dtype, a, a_rows, (int)a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
                out_scales, g_out);
   else if (bm == 48)
-    launch<48>(grid, st, b_layout, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+    launch<48>(grid, st, b_layout, epilogue, scale_mode, out_dtype, a, a_rows, (int)a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
                out_scales, g_out);
   else if (bm == 64)
-    launch<64>(grid, st, b_layout, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
+    launch<64>(grid, st, b_layout, epilogue, scale_mode, out_dtype, a, a_rows, (int)a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
                out_scales, g_out);
   else
-    launch<128>(grid, st, b_layout, epilogue, scale_mode, out_dtype, a, as, offsets, tiles, ntiles, ny, b, bs, N, K,
+    launch<128>(grid, st, b_layout, epilogue, scale_mode, out_dtype, a, a_rows, (int)a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K,
                 out, out_scales, g_out);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
@@ -786,8 +803,19 @@ extern "C" int moe_grouped_gemm_fp8_planned(const moe_gemm_plan* plan, const uin
                                             const float* bs, int32_t N, int32_t K, int32_t epilogue,
                                             int32_t scale_mode, void* out, int out_dtype, float* out_scales,
                                             void* stream) {
-  return run_planned(plan, a, as, offsets, b, b_layout, bs, N, K, epilogue, scale_mode, out, out_dtype, out_scales,
-                     nullptr, stream);
+  return run_planned(plan, a, nullptr, 0, as, offsets, b, b_layout, bs, N, K, epilogue, scale_mode, out, out_dtype,
+                     out_scales, nullptr, stream);
+}
+
+extern "C" int moe_grouped_gemm_fp8_gather(const moe_gemm_plan* plan, const uint8_t* a, int64_t a_count,
+                                           const int32_t* a_rows, const float* as, const int32_t* offsets,
+                                           const uint8_t* b, int32_t b_layout, const float* bs, int32_t N, int32_t K,
+                                           int32_t epilogue, int32_t scale_mode, void* out, int out_dtype,
+                                           float* out_scales, float* g_out, void* stream) {
+  if (!a_rows && plan && plan->max_rows > 0) return MOE_ERR_NULL;
+  if (g_out && epilogue != MOE_EPI_SWIGLU_QUANT) return MOE_ERR_ARG;
+  return run_planned(plan, a, a_rows, a_count, as, offsets, b, b_layout, bs, N, K, epilogue, scale_mode, out,
+                     out_dtype, out_scales, g_out, stream);
 }
 
 extern "C" int moe_grouped_gemm_fp8_swiglu_save(const moe_gemm_plan* plan, const uint8_t* a, const float* as,
@@ -795,7 +823,7 @@ extern "C" int moe_grouped_gemm_fp8_swiglu_save(const moe_gemm_plan* plan, const
                                                 const float* bs, int32_t N, int32_t K, int32_t scale_mode,
                                                 uint8_t* h, float* h_scales, float* g_out, void* stream) {
   if (!g_out && plan && plan->max_rows > 0) return MOE_ERR_NULL;
-  return run_planned(plan, a, as, offsets, b, b_layout, bs, N, K, MOE_EPI_SWIGLU_QUANT, scale_mode, h, MOE_FP8_E4M3,
+  return run_planned(plan, a, nullptr, 0, as, offsets, b, b_layout, bs, N, K, MOE_EPI_SWIGLU_QUANT, scale_mode, h, MOE_FP8_E4M3,
                      h_scales, g_out, stream);
 }
 

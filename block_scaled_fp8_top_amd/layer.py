@@ -142,7 +142,11 @@ def quantize_expert_weights_fp4(groups: int, H: int, F: int, master, device="cud
 class MoELayer:
     """Preallocated buffers for up to ``T_max`` tokens; ``forward`` returns a view of the output."""
 
-    def __init__(self, weights: MoELayerWeights, T_max: int, act_dtype=torch.bfloat16, device="cuda"):
+    def __init__(self, weights: MoELayerWeights, T_max: int, act_dtype=torch.bfloat16, device="cuda",
+                 gather_rows: bool = True):
+        """gather_rows: GEMM1 reads each group row's codes straight from the token-order xq through
+        the dispatch's src_token (only the scales are permuted); False: the dispatch also writes the
+        permuted codes (disp.aq) and GEMM1 reads those.  Both give bitwise the same results."""
         if weights.fp4 and not weights.pow2:
             raise ValueError("FP4 expert weights need power-of-two activation scales (pow2=True)")
         self.w = weights
@@ -162,7 +166,7 @@ class MoELayer:
             offsets=torch.empty(G + 1, dtype=torch.int32, device=d),
             dest_row=torch.empty((T_max, k), dtype=torch.int32, device=d),
             src_token=torch.empty(self.max_rows, dtype=torch.int32, device=d),
-            aq=torch.empty((self.max_rows, H), dtype=torch.uint8, device=d),
+            aq=None if gather_rows else torch.empty((self.max_rows, H), dtype=torch.uint8, device=d),
             as_=torch.empty((self.max_rows, H // 128), dtype=torch.float32, device=d),
             max_rows=self.max_rows)
         self.hq = torch.empty((self.max_rows, F), dtype=torch.uint8, device=d)
@@ -176,8 +180,16 @@ class MoELayer:
         self.plan = None   # tile plan of the last forward's expert GEMMs
         self.logits_valid = False   # the last forward wrote self.logits (not the fused sigmoid replay)
         self.device = d
+        self.gather_rows = gather_rows
         self.bwd = None    # backward buffers, allocated by the first backward (or training forward)
         self.g_saved = False   # the last forward kept GEMM1's output in self.bwd["g"]
+
+    def _gemm1_a(self):
+        """GEMM1's A operand: (codes, group-order scales)."""
+        return (self.xq if self.gather_rows else self.disp.aq), self.disp.as_
+
+    def _a_rows(self):
+        return self.disp.src_token if self.gather_rows else None
 
     def forward(self, x: torch.Tensor, replay: Optional[torch.Tensor] = None, record: Optional[torch.Tensor] = None,
                 stream=None, events=None, fused_replay: bool = True, training: bool = False) -> torch.Tensor:
@@ -217,14 +229,14 @@ class MoELayer:
         M.moe_quant_fp8_block(x, 1, q=self.xq, scales=self.xs, stream=stream, pow2=w.pow2)
         mark(3)
         M.moe_dispatch(self.idx, w.E, w.shared, self.xq, self.xs, workspace=self.workspace, out=self.disp,
-                       stream=stream)
+                       stream=stream, copy_codes=not self.gather_rows)
         # one tile plan for both expert GEMMs (same groups); it lives in the GEMM workspace
         plan = self.plan = M.moe_grouped_gemm_plan(self.disp.offsets, self.max_rows, self.gemm_ws, stream=stream)
         mark(4)
-        M.moe_grouped_gemm_fp8(self.disp.aq, self.disp.as_, self.disp.offsets, w.w1p or w.w1q, w.w1s,
+        M.moe_grouped_gemm_fp8(*self._gemm1_a(), self.disp.offsets, w.w1p or w.w1q, w.w1s,
                                epilogue=M.MOE_EPI_SWIGLU_QUANT, out=self.hq, out_scales=self.hs, plan=plan,
                                stream=stream, pow2=w.pow2,
-                               save_g=self._backward_buffers()["g"] if training else None)
+                               save_g=self._backward_buffers()["g"] if training else None, a_rows=self._a_rows())
         self.g_saved = training
         mark(5)
         M.moe_grouped_gemm_fp8(self.hq, self.hs, self.disp.offsets, w.w2p or w.w2q, w.w2s, epilogue=M.MOE_EPI_STORE,
@@ -301,8 +313,9 @@ class MoELayer:
                                out_dtype=torch.float32, out=b["dh"], plan=self.plan, stream=stream, pow2=w.pow2)
         mark(2)
         if not self.g_saved:
-            M.moe_grouped_gemm_fp8(self.disp.aq, self.disp.as_, off, bw.w1_store, w.w1s, epilogue=M.MOE_EPI_STORE,
-                                   out_dtype=torch.float32, out=b["g"], plan=self.plan, stream=stream, pow2=w.pow2)
+            M.moe_grouped_gemm_fp8(*self._gemm1_a(), off, bw.w1_store, w.w1s, epilogue=M.MOE_EPI_STORE,
+                                   out_dtype=torch.float32, out=b["g"], plan=self.plan, stream=stream, pow2=w.pow2,
+                                   a_rows=self._a_rows())
         mark(3)
         M.moe_swiglu_backward_quant(b["dh"], b["g"], pow2=w.pow2, dgq=b["dgq"], dgs=b["dgs"], stream=stream)
         mark(4)

@@ -168,8 +168,10 @@ int moe_quant_fp8_block(const void* x, int x_dtype, int64_t batch, int64_t rows,
  *   src_token [T*k + (append_shared ? T : 0)] int32: token of each row; entries beyond offsets[G]
  *             are left untouched (out)
  *   xq, xs    the 1x128-quantised activations [T,H] and scales [T,H/128]; aq, as receive the
- *             permuted copies [rows,H] and [rows,H/128] (rows = offsets[G]).  If xq and aq are both
- *             NULL only the index outputs are produced.
+ *             permuted copies [rows,H] and [rows,H/128] (rows = offsets[G]).  With aq NULL and as
+ *             given only the scales are permuted (moe_grouped_gemm_fp8_gather then reads the codes
+ *             from xq through src_token); with aq and as both NULL only the index outputs are
+ *             produced.
  *   workspace >= moe_workspace_bytes(MOE_OP_DISPATCH, T, k, E, 0, 0) bytes.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (H % 128, E > 1024), MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
 int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_t append_shared,
@@ -251,6 +253,22 @@ int moe_grouped_gemm_fp8_planned(const moe_gemm_plan* plan, const uint8_t* a, co
                                  const uint8_t* b, int32_t b_layout, const float* bs, int32_t N, int32_t K,
                                  int32_t epilogue, int32_t scale_mode, void* out, int out_dtype, float* out_scales,
                                  void* stream);
+
+/* moe_grouped_gemm_fp8_planned with the rows of A gathered instead of stored in group order (blog
+ * sections "Wide EP" / "Parallelism / EP": the dispatch permutation, here folded into the GEMM's
+ * loads): group row r (r < offsets[groups]) multiplies the codes of row a_rows[r] of
+ * a [a_count, K] (the token-order quantised activations, a_rows the dispatch's src_token), with the
+ * scales of group row r in as [max_rows, K/128] (permuted by moe_dispatch with aq NULL).  The
+ * result is bitwise that of moe_grouped_gemm_fp8_planned on the permuted copy.  a_rows entries
+ * must lie in [0, a_count); the kernel clamps them into that range, so a bad entry cannot read
+ * outside a.  g_out: as in moe_grouped_gemm_fp8_swiglu_save (NULL unless epilogue is
+ * MOE_EPI_SWIGLU_QUANT).
+ * Errors: as moe_grouped_gemm_fp8_planned; MOE_ERR_NULL (a_rows NULL), MOE_ERR_SHAPE (a_count < 1
+ * or (a_count + 1) * K at or above 2^32), MOE_ERR_ARG (g_out with the store epilogue). */
+int moe_grouped_gemm_fp8_gather(const moe_gemm_plan* plan, const uint8_t* a, int64_t a_count, const int32_t* a_rows,
+                                const float* as, const int32_t* offsets, const uint8_t* b, int32_t b_layout,
+                                const float* bs, int32_t N, int32_t K, int32_t epilogue, int32_t scale_mode, void* out,
+                                int out_dtype, float* out_scales, float* g_out, void* stream);
 
 /* Training forward of GEMM1 (blog section "FP8 training": the trainer runs this layer and then its
  * backward, whose SwiGLU derivative needs the GEMM1 output): moe_grouped_gemm_fp8_planned with

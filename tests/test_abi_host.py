@@ -325,3 +325,22 @@ def test_fp4_validation(L):
     assert L.moe_pack_weights_fp4(P, P, 0, 512, 128, 0, P, P, None) == SHAPE
     assert L.moe_pack_weights_fp4(P, P, 4, 512, 128, 5, P, P, None) == ARG
     assert L.moe_pack_weights_fp4(P, None, 4, 512, 128, 0, P, P, None) == NULL
+
+
+def test_gather_validation(L):
+    P = ctypes.c_void_p(16)
+    plan = M.GemmPlan(128, 4, 1000, P)
+    # (plan, a, a_count, a_rows, as, offsets, b, b_layout, bs, N, K, epilogue, scale_mode, out, out_dtype,
+    #  out_scales, g_out, stream)
+    g = lambda a_count=100, a_rows=P, g_out=None, K=256: (ctypes.byref(plan), P, a_count, a_rows, P, P, P, 1, P, 512,
+                                                          K, 0, 0, P, 1, None, g_out, None)
+    assert L.moe_grouped_gemm_fp8_gather(*g(a_rows=None)) == NULL
+    assert L.moe_grouped_gemm_fp8_gather(*g(g_out=P)) == ARG          # G is kept only by the SwiGLU epilogue
+    assert L.moe_grouped_gemm_fp8_gather(*g(a_count=0)) == SHAPE
+    assert L.moe_grouped_gemm_fp8_gather(*g(a_count=1 << 24, K=512)) == SHAPE   # 2^33 bytes of gathered rows
+    empty = M.GemmPlan(128, 4, 0, P)
+    assert L.moe_grouped_gemm_fp8_gather(ctypes.byref(empty), None, 0, None, None, None, None, 1, None, 512, 256, 0, 0,
+                                         None, 1, None, None, None) == OK
+    # dispatch: scales only (aq NULL) needs xs and as; codes need xq
+    assert L.moe_dispatch(P, 10, 2, 8, 0, None, None, 256, P, P, P, P, None, P, P, 1 << 20, None) == NULL
+    assert L.moe_dispatch(P, 10, 2, 8, 0, None, P, 256, P, P, P, P, P, P, P, 1 << 20, None) == NULL

@@ -52,7 +52,8 @@ def test_layer_tiny_every_intermediate():
     assert_equal("dest", host(lay.disp.dest_row), r["dest"])
     n = int(r["offsets"][-1])
     assert_equal("src", host(lay.disp.src_token)[:n], r["src"])
-    assert_equal("aq", host(lay.disp.aq)[:n], r["aq"])
+    # the rows GEMM1 reads: xq gathered through src_token (the layer keeps no permuted copy)
+    assert_equal("gathered rows", host(lay.xq)[host(lay.disp.src_token)[:n]], r["aq"])
     assert_equal("as", host(lay.disp.as_)[:n], r["as_"])
     assert rel_err(host(lay.y)[:n], r["y_act"]) < TOL
     err = rel_err(host(out), r["out"])
@@ -111,6 +112,36 @@ def test_layer_deterministic_and_chunk_concatenation():
     both = l2.forward(x)
     assert torch.equal(a0.view(torch.int16), a0b.view(torch.int16))
     assert torch.equal(torch.cat([a0, a1]).view(torch.int16), both.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill"])
+def test_layer_gathered_rows_equal_permuted_copy(name):
+    """GEMM1 reading its rows from xq through src_token gives bitwise the forward (and, for the
+    small layers, the training backward's dx) of GEMM1 reading the dispatch's permuted copy."""
+    cfg = synth.CONFIGS[name]
+    gw = gpu_weights(cfg)
+    outs = {}
+    for gather in (True, False):
+        lay = MoELayer(gw, cfg.T, _act(cfg), gather_rows=gather)
+        assert (lay.disp.aq is None) == gather
+        x = synth.make_x(cfg, DEV)
+        o = lay.forward(x).clone()
+        hq = lay.hq.clone()
+        dx = None
+        if name != "prefill":
+            from block_scaled_fp8_top_amd.layer import prepare_backward_weights
+            dx = lay.backward(x, synth.make_dout(cfg, DEV), prepare_backward_weights(gw))["dx"].clone()
+        outs[gather] = (o, hq, dx)
+        del lay
+    torch.cuda.synchronize()
+    (o1, h1, d1), (o0, h0, d0) = outs[True], outs[False]
+    assert torch.equal(h1, h0)
+    iv = torch.int16 if o1.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(o1.view(iv), o0.view(iv))
+    if d1 is not None:
+        assert torch.equal(d1.view(iv), d0.view(iv))
+    del outs, gw
+    _free()
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode"])

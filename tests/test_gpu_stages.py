@@ -437,6 +437,49 @@ def test_grouped_gemm_packed_equals_rowmajor(name, tile):
         _cleanup()
 
 
+@pytest.mark.parametrize("tile", [32, 48, 64, 128])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_grouped_gemm_gathered_rows(tile, pow2):
+    """A rows gathered from a token-order matrix through a row-id list (repeats, any order) give
+    bitwise the GEMM of the explicitly permuted copy: store (bf16, fp32) and SwiGLU epilogues, and
+    FP4 weights with power-of-two scales."""
+    rng = np.random.default_rng(tile + 7 * pow2)
+    G, N, K, T = 5, 512, 768, 300
+    counts = np.array([0, 130, 1, 257, 77])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = int(offsets[-1]) + 9                               # a few rows past the last group
+    src = torch.from_numpy(rng.integers(0, T, rows).astype(np.int32)).to(DEV)
+    x = synth.randn((T, K), 41, synth.STAGE, part=tile, device=DEV)
+    xq, xs = M.moe_quant_fp8_block(x, 1, pow2=pow2)
+    aq = xq[src.long()].contiguous()
+    as_ = xs[src.long()].contiguous()
+    w = synth.randn((G, N, K), 41, synth.STAGE, part=100 + tile, device=DEV, std=K ** -0.5)
+    bq, bsc = M.moe_quant_fp8_block(w, 128, pow2=pow2)
+    goff = torch.from_numpy(offsets).to(DEV)
+    ws = torch.empty(M.workspace_bytes(M.MOE_OP_GROUPED_GEMM, rows, 0, G, 0, 0), dtype=torch.uint8, device=DEV)
+    plan = M.moe_grouped_gemm_plan(goff, rows, ws, tile_rows=tile)
+    n = int(offsets[-1])
+    for epi in (M.MOE_EPI_STORE, M.MOE_EPI_SWIGLU_QUANT):
+        pk = M.moe_pack_weights_fp8(bq, epi)
+        for od in ((torch.bfloat16, torch.float32) if epi == M.MOE_EPI_STORE else (None,)):
+            kw = dict(out_dtype=od) if od is not None else {}
+            ref = M.moe_grouped_gemm_fp8(aq, as_, goff, pk, bsc, epi, plan=plan, pow2=pow2, **kw)
+            got = M.moe_grouped_gemm_fp8(xq, as_, goff, pk, bsc, epi, plan=plan, pow2=pow2, a_rows=src, **kw)
+            if epi == M.MOE_EPI_STORE:
+                assert_equal(f"store {od}", host(got)[:n], host(ref)[:n])
+            else:
+                assert_equal("h codes", host(got[0])[:n], host(ref[0])[:n])
+                assert_equal("h scales", host(got[1])[:n], host(ref[1])[:n])
+    if pow2:
+        q4, e8 = M.moe_quant_mxfp4(w)
+        pk4 = M.moe_pack_weights_fp4(q4, e8, M.MOE_EPI_STORE)
+        ref = M.moe_grouped_gemm_fp8(aq, as_, goff, pk4, None, M.MOE_EPI_STORE, torch.float32, plan=plan, pow2=True)
+        got = M.moe_grouped_gemm_fp8(xq, as_, goff, pk4, None, M.MOE_EPI_STORE, torch.float32, plan=plan, pow2=True,
+                                     a_rows=src)
+        assert_equal("fp4 store", host(got)[:n], host(ref)[:n])
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode", "longctx"])
 def test_grouped_gemm_plan_shared_by_two_gemms(name):
     """One plan, two GEMMs (SwiGLU over W1, then store over W2), bitwise equal to the one-call path
