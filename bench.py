@@ -83,7 +83,8 @@ def stage_model(cfg, counts, n_active1, fp4=False):
         "gate_logits": dict(bytes=T * H * ab + E * H * 4 + T * E * 4, flops=2.0 * T * H * E, bound="alu"),
         "route": dict(bytes=T * E * 4 + T * k * 8, flops=0.0, bound="hbm"),
         "quant_x": dict(bytes=T * H * (ab + 1 + sig), flops=0.0, bound="hbm"),
-        "dispatch": dict(bytes=T * k * 4 + T * H * (1 + sig) + rows * H * (1 + sig) + T * k * 4 + rows * 4,
+        # ids in, dest_row and src_token out, the 1x128 scales permuted (GEMM1 gathers the codes)
+        "dispatch": dict(bytes=T * k * 4 + T * k * 4 + rows * 4 + T * H * sig + rows * H * sig,
                          flops=0.0, bound="hbm"),
         "gemm1_swiglu": dict(bytes=rows * H * (1 + sig) + w1 + rows * F * (1 + sig), flops=4.0 * H * F * rows,
                              bound=None),
