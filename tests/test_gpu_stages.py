@@ -298,6 +298,12 @@ def test_dispatch_permute_widths(H):
         n = int(oo[-1])
         assert_equal(f"aq H={H}", host(d.aq)[:n], O.permute_rows(host(xq), osrc))
         assert_equal(f"as H={H}", host(d.as_)[:n], O.permute_rows(host(xs), osrc))
+        # scales only (the codes are then gathered by the grouped GEMM): same indices and scales,
+        # no code copy
+        ds = M.moe_dispatch(torch.from_numpy(idx).to(DEV), E, shared, xq, xs, copy_codes=False)
+        assert ds.aq is None
+        assert_equal(f"src H={H}", host(ds.src_token)[:n], osrc)
+        assert_equal(f"as only H={H}", host(ds.as_)[:n], O.permute_rows(host(xs), osrc))
 
 
 # ----------------------------------------------------------------------------- grouped GEMM
