@@ -49,6 +49,7 @@
 // fp32, and the tile's 128 h columns are one 1x128 quantisation block (amax across the waves of a
 // row through LDS).
 #include <algorithm>
+#include <atomic>
 
 #include "common.h"
 
@@ -661,15 +662,19 @@ void launch(unsigned grid, hipStream_t st, int b_layout, int epilogue, int scale
                               out_scales, g_out);
 }
 
-// compute units of the current device, queried once per device
+// compute units of the current device, queried once per device (atomics: calls may come from
+// several host threads at once)
 int compute_units() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-  if (dev < 64) cached[dev] = n;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
