@@ -31,7 +31,7 @@ MOE_SCALE_AMAX, MOE_SCALE_POW2 = 0, 1
 
 EXPORTED = ("moe_gate_logits", "moe_route", "moe_replay_route", "moe_replay_gate", "moe_router_score_eval",
             "moe_quant_fp8_block",
-            "moe_dispatch", "moe_pack_weights_fp8", "moe_packed_weight_bytes", "moe_grouped_gemm_plan",
+            "moe_dispatch", "moe_dispatch_plan", "moe_pack_weights_fp8", "moe_packed_weight_bytes", "moe_grouped_gemm_plan",
             "moe_grouped_gemm_fp8_planned", "moe_grouped_gemm_fp8_swiglu_save", "moe_grouped_gemm_fp8_gather",
             "moe_grouped_gemm_fp8", "moe_combine", "moe_payload_bytes",
             "moe_payload_pack", "moe_payload_unpack", "moe_payload_to_host", "moe_payload_from_host",
@@ -85,6 +85,8 @@ def lib():
         "moe_router_score_eval": [P, I64, ctypes.c_int, P, P],
         "moe_quant_fp8_block": [P, ctypes.c_int, I64, I64, I32, I32, I32, P, P, P],
         "moe_dispatch": [P, I64, I32, I32, I32, P, P, I32, P, P, P, P, P, P, P, SZ, P],
+        "moe_dispatch_plan": [P, I64, I32, I32, I32, P, P, I32, P, P, P, P, P, P, P, SZ, I32, P, SZ,
+                              ctypes.POINTER(GemmPlan), P],
         "moe_pack_weights_fp8": [P, I32, I32, I32, I32, P, P],
         "moe_packed_weight_bytes": [I32, I32, I32, I32],
         "moe_grouped_gemm_fp8": [P, P, P, I32, I64, P, I32, P, I32, I32, I32, I32, I32, P, ctypes.c_int, P, P, SZ, P],
@@ -346,6 +348,29 @@ def moe_dispatch(topk_idx: torch.Tensor, num_experts: int, append_shared: bool, 
                               _p(out.as_), _p(workspace), workspace.numel() * workspace.element_size(),
                               _stream(stream)), "moe_dispatch")
     return out
+
+
+def moe_dispatch_plan(topk_idx: torch.Tensor, num_experts: int, append_shared: bool, xq: Optional[torch.Tensor],
+                      xs: Optional[torch.Tensor], workspace: torch.Tensor, out: Dispatched, gemm_workspace: torch.Tensor,
+                      tile_rows: int = 0, stream=None):
+    """moe_dispatch into ``out`` followed by the grouped GEMM's tile plan of its groups (held in
+    ``gemm_workspace``); for one-workgroup batches the dispatch kernel writes the plan itself.
+    Returns the GemmPlan to pass as ``plan=`` to moe_grouped_gemm_fp8."""
+    T, k = topk_idx.shape
+    _dev(topk_idx, "topk_idx", torch.int32)
+    H = 0
+    if xq is not None:
+        H = xq.shape[1]
+        _dev(xq, "xq", FP8, (T, H))
+        _dev(xs, "xs", torch.float32, (T, H // 128))
+    plan = GemmPlan()
+    _check(lib().moe_dispatch_plan(_p(topk_idx), T, k, num_experts, int(bool(append_shared)), _p(xq), _p(xs), H,
+                                   _p(out.counts), _p(out.offsets), _p(out.dest_row), _p(out.src_token), _p(out.aq),
+                                   _p(out.as_), _p(workspace), workspace.numel() * workspace.element_size(),
+                                   tile_rows, _p(gemm_workspace), gemm_workspace.numel() * gemm_workspace.element_size(),
+                                   ctypes.byref(plan), _stream(stream)), "moe_dispatch_plan")
+    plan._keep = gemm_workspace
+    return plan
 
 
 def packed_weight_bytes(groups: int, N: int, K: int, epilogue: int) -> int:

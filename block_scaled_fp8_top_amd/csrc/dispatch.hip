@@ -174,16 +174,23 @@ constexpr int SMALL_CNT = 16384;      // (64-slot pieces) x experts counters in 
 // leader records the piece's count for the expert.  Thread e then turns its expert's piece counts
 // into running bases (pieces in order), a block scan gives the expert offsets, and every slot's
 // row is offset + piece base + rank: the stable order.
+// With tiles != NULL the same workgroup also writes the grouped GEMM's tile list for row tiles of
+// bm (the entries the plan kernel of the grouped GEMM writes: {group, first row, the group's first
+// tile, the group's tile count}, at most max_tiles of them, and their number into *ntiles).
 template <int BITS>
 __global__ __launch_bounds__(1024) void small_dispatch_kernel(const int32_t* __restrict__ idx, int nslots, int k, int E,
                                                               int T, int append_shared, int32_t* __restrict__ counts,
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ dest_row,
-                                                              int32_t* __restrict__ src_token) {
+                                                              int32_t* __restrict__ src_token, int bm,
+                                                              int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                                              int max_tiles) {
   __shared__ int sidx[SMALL_MAX];
   __shared__ uint8_t srank[SMALL_MAX];
   __shared__ int cnt[SMALL_CNT];      // [piece][e]
   __shared__ int part[1024];
+  __shared__ int tpart[1024];
+  __shared__ int first[1025];         // tile plan: the groups' first tiles, first[G] = all tiles
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int npiece = (nslots + 63) / 64;
   for (int i = tid; i < npiece * E; i += 1024) cnt[i] = 0;
@@ -249,6 +256,35 @@ __global__ __launch_bounds__(1024) void small_dispatch_kernel(const int32_t* __r
   }
   if (append_shared)
     for (int t = tid; t < T; t += 1024) src_token[routed + t] = t;
+  if (!tiles) return;
+  // tile plan: group g has ceil(rows / bm) tiles; a block scan gives each group's first tile, then
+  // every thread writes tiles, finding a tile's group by binary search over the first tiles
+  const int G = E + (append_shared ? 1 : 0);
+  const int rows_g = tid < E ? total : (tid == E && append_shared ? T : 0);
+  const int nt = (rows_g + bm - 1) / bm;
+  tpart[tid] = nt;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? tpart[tid - o] : 0;
+    __syncthreads();
+    tpart[tid] += v;
+    __syncthreads();
+  }
+  if (tid < G) first[tid] = tpart[tid] - nt;
+  if (tid == 0) first[G] = tpart[G - 1];
+  __syncthreads();
+  const int ntot = min(first[G], max_tiles);
+  for (int t = tid; t < ntot; t += 1024) {
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (first[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    const int off = lo < E ? (lo == 0 ? 0 : part[lo - 1]) : routed;
+    tiles[t] = make_int4(lo, off + (t - first[lo]) * bm, first[lo], first[lo + 1] - first[lo]);
+  }
+  if (tid == 0) *ntiles = ntot;
 }
 
 int64_t nchunks_for(int64_t T, int k) { return ceil_div64(T * k, CHUNK); }
@@ -259,10 +295,19 @@ size_t moe_dispatch_workspace(int64_t T, int32_t k, int32_t E) {
   return (size_t)(2 * nchunks_for(T, k) * (int64_t)E * 4 + 256);
 }
 
-extern "C" int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_t append_shared,
-                            const uint8_t* xq, const float* xs, int32_t H, int32_t* counts, int32_t* offsets,
-                            int32_t* dest_row, int32_t* src_token, uint8_t* aq, float* as, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+int moe_plan_host(int32_t groups, int64_t max_rows, int32_t tile_rows, void* workspace, size_t workspace_bytes,
+                  moe_gemm_plan* plan, int64_t* max_tiles);
+
+namespace {
+
+// The dispatch; with plan_ws != NULL and the one-workgroup path taken, that workgroup also writes
+// the tile list of plan_bm-row tiles into plan_ws (*planned is then set).
+int dispatch_impl(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_t append_shared,
+                  const uint8_t* xq, const float* xs, int32_t H, int32_t* counts, int32_t* offsets,
+                  int32_t* dest_row, int32_t* src_token, uint8_t* aq, float* as, void* workspace,
+                  size_t workspace_bytes, void* stream, int plan_bm, void* plan_ws, int64_t plan_max_tiles,
+                  bool* planned) {
+  *planned = false;
   if (T < 0 || k < 1 || k > 64 || E < 1 || E > MAXE) return MOE_ERR_SHAPE;
   if (T * (int64_t)k + T > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
   // rows: aq given -> codes and scales are permuted; only as given -> only the scales
@@ -280,11 +325,15 @@ extern "C" int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32
   int bits = 1;
   while ((1 << bits) < E) ++bits;
   if (nslots <= SMALL_MAX && ceil_div64(nslots, 64) * E <= SMALL_CNT) {
+    const bool plan_here = plan_ws && E + (append_shared ? 1 : 0) <= 1024 && plan_max_tiles <= INT32_MAX;
+    int4* ptiles = plan_here ? reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan_ws) + 256) : nullptr;
+    int32_t* pntiles = plan_here ? reinterpret_cast<int32_t*>(plan_ws) : nullptr;
     switch (bits) {
 #define CASE_SMALL(B)                                                                                   \
   case B:                                                                                               \
     small_dispatch_kernel<B><<<1, 1024, 0, st>>>(topk_idx, (int)nslots, k, E, (int)T, append_shared, counts, \
-                                                 offsets, dest_row, src_token);                          \
+                                                 offsets, dest_row, src_token, plan_bm, ptiles, pntiles, \
+                                                 (int)plan_max_tiles);                                   \
     break;
       CASE_SMALL(1) CASE_SMALL(2) CASE_SMALL(3) CASE_SMALL(4) CASE_SMALL(5)
       CASE_SMALL(6) CASE_SMALL(7) CASE_SMALL(8) CASE_SMALL(9) CASE_SMALL(10)
@@ -293,6 +342,7 @@ extern "C" int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32
         return MOE_ERR_SHAPE;
     }
     MOE_CHECK_LAUNCH();
+    *planned = plan_here;
   } else {
   if (nch > 0) {
     count_kernel<<<(unsigned)nch, 256, 0, st>>>(topk_idx, nslots, E, chunk_counts);
@@ -325,4 +375,36 @@ extern "C" int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32
     MOE_CHECK_LAUNCH();
   }
   return MOE_OK;
+}
+}  // namespace
+
+extern "C" int moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_t append_shared,
+                            const uint8_t* xq, const float* xs, int32_t H, int32_t* counts, int32_t* offsets,
+                            int32_t* dest_row, int32_t* src_token, uint8_t* aq, float* as, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  bool planned = false;
+  return dispatch_impl(topk_idx, T, k, E, append_shared, xq, xs, H, counts, offsets, dest_row, src_token, aq, as,
+                       workspace, workspace_bytes, stream, 0, nullptr, 0, &planned);
+}
+
+extern "C" int moe_dispatch_plan(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_t append_shared,
+                                 const uint8_t* xq, const float* xs, int32_t H, int32_t* counts, int32_t* offsets,
+                                 int32_t* dest_row, int32_t* src_token, uint8_t* aq, float* as, void* workspace,
+                                 size_t workspace_bytes, int32_t tile_rows, void* gemm_workspace,
+                                 size_t gemm_workspace_bytes, moe_gemm_plan* plan, void* stream) {
+  if (T < 0 || k < 1 || k > 64 || E < 1 || E > MAXE) return MOE_ERR_SHAPE;
+  if (T * (int64_t)k + T > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
+  const int32_t G = E + (append_shared ? 1 : 0);
+  const int64_t max_rows = T * (int64_t)k + (append_shared ? T : 0);
+  int64_t mt = 0;
+  int rc = moe_plan_host(G, max_rows, tile_rows, gemm_workspace, gemm_workspace_bytes, plan, &mt);
+  if (rc != MOE_OK) return rc;
+  bool planned = false;
+  rc = dispatch_impl(topk_idx, T, k, E, append_shared, xq, xs, H, counts, offsets, dest_row, src_token, aq, as,
+                     workspace, workspace_bytes, stream, plan->tile_rows, max_rows > 0 ? gemm_workspace : nullptr, mt,
+                     &planned);
+  if (rc != MOE_OK || planned || max_rows == 0) return rc;
+  // the multi-kernel dispatch path: the plan kernel of the grouped GEMM
+  return moe_grouped_gemm_plan(offsets, G, max_rows, plan->tile_rows, gemm_workspace, gemm_workspace_bytes, plan,
+                               stream);
 }

@@ -736,8 +736,11 @@ int check_gemm_args(int64_t max_rows, int32_t groups, int32_t N, int32_t K, int3
 
 }  // namespace
 
-extern "C" int moe_grouped_gemm_plan(const int32_t* offsets, int32_t groups, int64_t max_rows, int32_t tile_rows,
-                                     void* workspace, size_t workspace_bytes, moe_gemm_plan* plan, void* stream) {
+// The host half of a plan: checks, tile height, sizes (no launch).  *max_tiles receives the length
+// of the tile list the workspace holds (0 when max_rows is 0).  Shared with the dispatch, whose
+// one-workgroup path writes the tile list itself.
+int moe_plan_host(int32_t groups, int64_t max_rows, int32_t tile_rows, void* workspace, size_t workspace_bytes,
+                  moe_gemm_plan* plan, int64_t* max_tiles) {
   if (!plan) return MOE_ERR_NULL;
   if (groups < 1 || groups > 4096 || max_rows < 0 || max_rows > INT32_MAX - 256) return MOE_ERR_SHAPE;
   if (tile_rows != 0 && tile_rows != 32 && tile_rows != 48 && tile_rows != 64 && tile_rows != 128) return MOE_ERR_ARG;
@@ -746,10 +749,21 @@ extern "C" int moe_grouped_gemm_plan(const int32_t* offsets, int32_t groups, int
   plan->groups = groups;
   plan->max_rows = max_rows;
   plan->workspace = workspace;
+  *max_tiles = 0;
   if (max_rows == 0) return MOE_OK;
-  if (!offsets) return MOE_ERR_NULL;
   if (!workspace || workspace_bytes < moe_gemm_workspace(max_rows, groups)) return MOE_ERR_WORKSPACE;
-  const int64_t mt = max_tiles_for(max_rows, groups, bm);
+  *max_tiles = max_tiles_for(max_rows, groups, bm);
+  return MOE_OK;
+}
+
+extern "C" int moe_grouped_gemm_plan(const int32_t* offsets, int32_t groups, int64_t max_rows, int32_t tile_rows,
+                                     void* workspace, size_t workspace_bytes, moe_gemm_plan* plan, void* stream) {
+  if (!plan) return MOE_ERR_NULL;
+  if (max_rows > 0 && !offsets) return MOE_ERR_NULL;
+  int64_t mt = 0;
+  const int rc = moe_plan_host(groups, max_rows, tile_rows, workspace, workspace_bytes, plan, &mt);
+  if (rc != MOE_OK || max_rows == 0) return rc;
+  const int bm = plan->tile_rows;
   int4* tiles = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(workspace) + 256);
   int32_t* ntiles = reinterpret_cast<int32_t*>(workspace);
   tile_map_kernel<<<1, 1024, 0, as_stream(stream)>>>(offsets, groups, bm, tiles, ntiles, (int)mt);

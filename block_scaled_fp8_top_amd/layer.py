@@ -2,8 +2,9 @@
 
 forward(x) enqueues, on the current stream and without any host synchronisation:
   moe_gate_logits -> moe_route (optionally recording into the routing payload) or
-  moe_replay_route -> moe_quant_fp8_block (x, 1x128) -> moe_dispatch -> moe_grouped_gemm_plan ->
-  moe_grouped_gemm_fp8_planned (W1, SwiGLU + 1x128 quantisation of h) -> moe_grouped_gemm_fp8_planned
+  moe_replay_route -> moe_quant_fp8_block (x, 1x128) -> moe_dispatch_plan (permutation indices and
+  scales, and the tile plan of both expert GEMMs) -> moe_grouped_gemm_fp8_gather (W1 on the rows of
+  xq gathered through src_token, SwiGLU + 1x128 quantisation of h) -> moe_grouped_gemm_fp8_planned
   (W2) -> moe_combine.
 
 backward(x, dout, bw) enqueues the gradients of the last forward (its buffers must still hold its
@@ -228,10 +229,10 @@ class MoELayer:
         mark(2)
         M.moe_quant_fp8_block(x, 1, q=self.xq, scales=self.xs, stream=stream, pow2=w.pow2)
         mark(3)
-        M.moe_dispatch(self.idx, w.E, w.shared, self.xq, self.xs, workspace=self.workspace, out=self.disp,
-                       stream=stream, copy_codes=not self.gather_rows)
-        # one tile plan for both expert GEMMs (same groups); it lives in the GEMM workspace
-        plan = self.plan = M.moe_grouped_gemm_plan(self.disp.offsets, self.max_rows, self.gemm_ws, stream=stream)
+        # dispatch, and one tile plan for both expert GEMMs (same groups), living in the GEMM workspace
+        # (for decode-sized batches the dispatch workgroup writes it)
+        plan = self.plan = M.moe_dispatch_plan(self.idx, w.E, w.shared, self.xq, self.xs, self.workspace, self.disp,
+                                               self.gemm_ws, stream=stream)
         mark(4)
         M.moe_grouped_gemm_fp8(*self._gemm1_a(), self.disp.offsets, w.w1p or w.w1q, w.w1s,
                                epilogue=M.MOE_EPI_SWIGLU_QUANT, out=self.hq, out_scales=self.hs, plan=plan,

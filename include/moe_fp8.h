@@ -254,6 +254,19 @@ int moe_grouped_gemm_fp8_planned(const moe_gemm_plan* plan, const uint8_t* a, co
                                  int32_t epilogue, int32_t scale_mode, void* out, int out_dtype, float* out_scales,
                                  void* stream);
 
+/* Dispatch and tile plan in one call: moe_dispatch (same arguments and outputs) followed by
+ * moe_grouped_gemm_plan(offsets, G, max_rows = T*k + (append_shared ? T : 0), tile_rows,
+ * gemm_workspace, ...) for the G = E + (append_shared ? 1 : 0) groups it produces.  When the batch is
+ * small enough for the one-workgroup dispatch (decode) and G <= 1024, that workgroup also writes the
+ * tile list, which saves the plan's own launch; otherwise the plan kernel runs after the dispatch.
+ * The plan is the same either way.
+ * Errors: as moe_dispatch and moe_grouped_gemm_plan. */
+int moe_dispatch_plan(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_t append_shared,
+                      const uint8_t* xq, const float* xs, int32_t H, int32_t* counts, int32_t* offsets,
+                      int32_t* dest_row, int32_t* src_token, uint8_t* aq, float* as, void* workspace,
+                      size_t workspace_bytes, int32_t tile_rows, void* gemm_workspace, size_t gemm_workspace_bytes,
+                      moe_gemm_plan* plan, void* stream);
+
 /* moe_grouped_gemm_fp8_planned with the rows of A gathered instead of stored in group order (blog
  * sections "Wide EP" / "Parallelism / EP": the dispatch permutation, here folded into the GEMM's
  * loads): group row r (r < offsets[groups]) multiplies the codes of row a_rows[r] of

@@ -344,3 +344,16 @@ def test_gather_validation(L):
     # dispatch: scales only (aq NULL) needs xs and as; codes need xq
     assert L.moe_dispatch(P, 10, 2, 8, 0, None, None, 256, P, P, P, P, None, P, P, 1 << 20, None) == NULL
     assert L.moe_dispatch(P, 10, 2, 8, 0, None, P, 256, P, P, P, P, P, P, P, 1 << 20, None) == NULL
+
+
+def test_dispatch_plan_validation(L):
+    P = ctypes.c_void_p(256)
+    plan = M.GemmPlan()
+    # (idx, T, k, E, shared, xq, xs, H, counts, offsets, dest, src, aq, as, ws, ws_bytes, tile_rows, gws,
+    #  gws_bytes, plan, stream)
+    a = lambda tr=0, gwsb=1 << 20, pl=ctypes.byref(plan), E=8: (P, 10, 2, E, 0, None, None, 0, P, P, P, P, None, None,
+                                                               P, 1 << 20, tr, P, gwsb, pl, None)
+    assert L.moe_dispatch_plan(*a(pl=None)) == NULL
+    assert L.moe_dispatch_plan(*a(tr=40)) == ARG
+    assert L.moe_dispatch_plan(*a(gwsb=8)) == WS
+    assert L.moe_dispatch_plan(*a(E=2000)) == SHAPE

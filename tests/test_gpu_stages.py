@@ -281,6 +281,44 @@ def test_dispatch_small_and_chunked_paths(T, k, E):
         assert_equal("src_token", host(d.src_token)[:oo[-1]], osrc)
 
 
+@pytest.mark.parametrize("T,k,E,shared", [(256, 6, 64, False), (96, 8, 32, True), (1, 8, 256, True),
+                                           (0, 6, 64, False), (2048, 8, 256, True)])
+def test_dispatch_plan_equals_separate_plan(T, k, E, shared):
+    """moe_dispatch_plan: the same dispatch outputs as moe_dispatch and the same tile list (every
+    entry and the count) as moe_grouped_gemm_plan, for each tile height; the one-workgroup path
+    writes the plan itself, the chunked path (16384 slots) falls back to the plan kernel."""
+    rng = np.random.default_rng(T + E)
+    idx = torch.from_numpy(rng.integers(0, E, size=(T, k)).astype(np.int32)).to(DEV)
+    H = 256
+    xq = synth.random_codes((T, H), 8, 44, device=DEV)
+    xs = synth.random_scales((T, H // 128), 8, 45, device=DEV)
+    G = E + (1 if shared else 0)
+    max_rows = T * k + (T if shared else 0)
+    ref = M.moe_dispatch(idx, E, shared, xq, xs, copy_codes=False)
+    for tile in (0, 32, 48, 64, 128):
+        out = M.moe_dispatch(idx, E, shared, xq, xs, copy_codes=False)   # fresh buffers of the same shape
+        for t_ in (out.counts, out.offsets, out.dest_row, out.src_token, out.as_):
+            t_.fill_(-9)
+        ws = torch.empty(M.workspace_bytes(M.MOE_OP_DISPATCH, T, k, E), dtype=torch.uint8, device=DEV)
+        gws = torch.full((max(M.workspace_bytes(M.MOE_OP_GROUPED_GEMM, max_rows, 0, G, 0, 0), 256),), 0xEE,
+                         dtype=torch.uint8, device=DEV)
+        gws2 = gws.clone()
+        plan = M.moe_dispatch_plan(idx, E, shared, xq, xs, ws, out, gws, tile_rows=tile)
+        plan2 = M.moe_grouped_gemm_plan(ref.offsets, max_rows, gws2, tile_rows=tile)
+        torch.cuda.synchronize()
+        assert (plan.tile_rows, plan.groups, plan.max_rows) == (plan2.tile_rows, plan2.groups, plan2.max_rows)
+        for name in ("counts", "offsets", "dest_row"):
+            assert_equal(f"{name} tile {tile}", host(getattr(out, name)), host(getattr(ref, name)))
+        n = int(host(ref.offsets)[-1])
+        assert_equal(f"src tile {tile}", host(out.src_token)[:n], host(ref.src_token)[:n])
+        assert_equal(f"as tile {tile}", host(out.as_)[:n], host(ref.as_)[:n])
+        if max_rows == 0:
+            continue
+        nt = int(host(gws2[:4].view(torch.int32))[0])
+        assert int(host(gws[:4].view(torch.int32))[0]) == nt
+        assert_equal(f"tiles tile {tile}", host(gws[256:256 + 16 * nt]), host(gws2[256:256 + 16 * nt]))
+
+
 @pytest.mark.parametrize("H", [128, 1152, 8192, 8320])
 def test_dispatch_permute_widths(H):
     """Row permutation at several widths: a row shorter than one wavefront's 16-byte pieces, a
