@@ -481,6 +481,35 @@ def test_grouped_gemm_packed_equals_rowmajor(name, tile):
         _cleanup()
 
 
+def test_grouped_gemm_gathered_rows_clamped():
+    """Row ids outside [0, a_count) are clamped into it (the documented safety net): the group rows
+    that name -5 and a_count + 7 get exactly the results of rows 0 and a_count - 1."""
+    G, N, K, T = 2, 256, 256, 40
+    offsets = np.array([0, 20, 33], np.int32)
+    rows = 33
+    rng = np.random.default_rng(9)
+    src = rng.integers(0, T, rows).astype(np.int32)
+    bad = src.copy()
+    bad[3], bad[25] = -5, T + 7
+    want = src.copy()
+    want[3], want[25] = 0, T - 1
+    x = synth.randn((T, K), 42, synth.STAGE, part=1, device=DEV)
+    xq, xs = M.moe_quant_fp8_block(x, 1)
+    w = synth.randn((G, N, K), 42, synth.STAGE, part=2, device=DEV, std=K ** -0.5)
+    bq, bsc = M.moe_quant_fp8_block(w, 128)
+    goff = torch.from_numpy(offsets).to(DEV)
+    ws = torch.empty(M.workspace_bytes(M.MOE_OP_GROUPED_GEMM, rows, 0, G, 0, 0), dtype=torch.uint8, device=DEV)
+    plan = M.moe_grouped_gemm_plan(goff, rows, ws)
+    pk = M.moe_pack_weights_fp8(bq, M.MOE_EPI_STORE)
+    as_ = xs[torch.from_numpy(want).long().to(DEV)].contiguous()
+    got = M.moe_grouped_gemm_fp8(xq, as_, goff, pk, bsc, M.MOE_EPI_STORE, torch.float32, plan=plan,
+                                 a_rows=torch.from_numpy(bad).to(DEV))
+    ref = M.moe_grouped_gemm_fp8(xq, as_, goff, pk, bsc, M.MOE_EPI_STORE, torch.float32, plan=plan,
+                                 a_rows=torch.from_numpy(want).to(DEV))
+    torch.cuda.synchronize()
+    assert_equal("clamped rows", host(got), host(ref))
+
+
 @pytest.mark.parametrize("tile", [32, 48, 64, 128])
 @pytest.mark.parametrize("pow2", [False, True])
 def test_grouped_gemm_gathered_rows(tile, pow2):
