@@ -282,7 +282,8 @@ def test_dispatch_small_and_chunked_paths(T, k, E):
 
 
 @pytest.mark.parametrize("T,k,E,shared", [(256, 6, 64, False), (96, 8, 32, True), (1, 8, 256, True),
-                                           (0, 6, 64, False), (2048, 8, 256, True)])
+                                           (0, 6, 64, False), (2048, 8, 256, True),
+                                           (3, 2, 1023, True), (4, 2, 1024, True)])   # G = 1024, 1025
 def test_dispatch_plan_equals_separate_plan(T, k, E, shared):
     """moe_dispatch_plan: the same dispatch outputs as moe_dispatch and the same tile list (every
     entry and the count) as moe_grouped_gemm_plan, for each tile height; the one-workgroup path
