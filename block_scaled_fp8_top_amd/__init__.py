@@ -314,6 +314,20 @@ class Dispatched:
     max_rows: int
 
 
+def _check_dispatched(out: Dispatched, T: int, k: int, G: int, max_rows: int, H: int):
+    """Caller-provided dispatch outputs: the kernels write exactly these extents."""
+    _dev(out.counts, "counts", torch.int32, (G,))
+    _dev(out.offsets, "offsets", torch.int32, (G + 1,))
+    _dev(out.dest_row, "dest_row", torch.int32, (T, k))
+    _dev(out.src_token, "src_token", torch.int32)
+    if out.src_token.numel() < max_rows:
+        raise ValueError("src_token holds fewer than T*k (+T) rows")
+    if out.aq is not None:
+        _dev(out.aq, "aq", FP8, (max_rows, H))
+    if out.as_ is not None:
+        _dev(out.as_, "as", torch.float32, (max_rows, H // 128))
+
+
 def moe_dispatch(topk_idx: torch.Tensor, num_experts: int, append_shared: bool, xq: Optional[torch.Tensor] = None,
                  xs: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                  out: Optional[Dispatched] = None, stream=None, copy_codes: bool = True) -> Dispatched:
@@ -343,6 +357,8 @@ def moe_dispatch(topk_idx: torch.Tensor, num_experts: int, append_shared: bool, 
             aq=torch.empty((max_rows, H), dtype=FP8, device=dev) if xq is not None and copy_codes else None,
             as_=torch.empty((max_rows, H // 128), dtype=torch.float32, device=dev) if xq is not None else None,
             max_rows=max_rows)
+    else:
+        _check_dispatched(out, T, k, G, max_rows, H)
     _check(lib().moe_dispatch(_p(topk_idx), T, k, num_experts, int(bool(append_shared)), _p(xq), _p(xs), H,
                               _p(out.counts), _p(out.offsets), _p(out.dest_row), _p(out.src_token), _p(out.aq),
                               _p(out.as_), _p(workspace), workspace.numel() * workspace.element_size(),
@@ -363,6 +379,9 @@ def moe_dispatch_plan(topk_idx: torch.Tensor, num_experts: int, append_shared: b
         H = xq.shape[1]
         _dev(xq, "xq", FP8, (T, H))
         _dev(xs, "xs", torch.float32, (T, H // 128))
+    _check_dispatched(out, T, k, num_experts + (1 if append_shared else 0), T * k + (T if append_shared else 0), H)
+    if workspace.numel() * workspace.element_size() < workspace_bytes(MOE_OP_DISPATCH, T, k, num_experts):
+        raise ValueError("workspace too small")
     plan = GemmPlan()
     _check(lib().moe_dispatch_plan(_p(topk_idx), T, k, num_experts, int(bool(append_shared)), _p(xq), _p(xs), H,
                                    _p(out.counts), _p(out.offsets), _p(out.dest_row), _p(out.src_token), _p(out.aq),

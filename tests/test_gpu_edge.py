@@ -141,3 +141,23 @@ def test_layer_replay_with_bad_ids(name):
     if not cfg.shared:
         for t in (1, cfg.T // 2, cfg.T - 1):
             assert np.all(host(out)[t] == 0)
+
+
+def test_dispatch_rejects_missized_outputs():
+    """Caller-provided dispatch outputs are checked against the extents the kernels write, before
+    any launch (a short src_token or a wrong counts length would otherwise be written past)."""
+    T, k, E, H = 16, 2, 8, 256
+    idx = torch.randint(0, E, (T, k), dtype=torch.int32, device=DEV)
+    xq = torch.zeros((T, H), dtype=torch.uint8, device=DEV)
+    xs = torch.ones((T, H // 128), dtype=torch.float32, device=DEV)
+    good = M.moe_dispatch(idx, E, False, xq, xs)
+    ws = torch.empty(M.workspace_bytes(M.MOE_OP_DISPATCH, T, k, E), dtype=torch.uint8, device=DEV)
+    gws = torch.empty(M.workspace_bytes(M.MOE_OP_GROUPED_GEMM, T * k, 0, E, 0, 0), dtype=torch.uint8, device=DEV)
+    for field, bad in (("counts", torch.empty(E - 1, dtype=torch.int32, device=DEV)),
+                       ("src_token", torch.empty(T * k - 1, dtype=torch.int32, device=DEV)),
+                       ("as_", torch.empty((T * k, 1), dtype=torch.float32, device=DEV))):
+        out = replace(good, **{field: bad})
+        with pytest.raises(ValueError):
+            M.moe_dispatch(idx, E, False, xq, xs, out=out)
+        with pytest.raises(ValueError):
+            M.moe_dispatch_plan(idx, E, False, xq, xs, ws, out, gws)
