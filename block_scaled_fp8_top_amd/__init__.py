@@ -29,7 +29,7 @@ MOE_OP_DISPATCH, MOE_OP_GROUPED_GEMM = 1, 2
 MOE_B_ROWMAJOR, MOE_B_PACKED, MOE_B_PACKED_FP4 = 0, 1, 2
 MOE_SCALE_AMAX, MOE_SCALE_POW2 = 0, 1
 
-EXPORTED = ("moe_gate_logits", "moe_route", "moe_replay_route", "moe_replay_gate", "moe_router_score_eval",
+EXPORTED = ("moe_gate_logits", "moe_route", "moe_route_quant", "moe_replay_route", "moe_replay_gate", "moe_router_score_eval",
             "moe_quant_fp8_block",
             "moe_dispatch", "moe_dispatch_plan", "moe_pack_weights_fp8", "moe_packed_weight_bytes", "moe_grouped_gemm_plan",
             "moe_grouped_gemm_fp8_planned", "moe_grouped_gemm_fp8_swiglu_save", "moe_grouped_gemm_fp8_gather",
@@ -84,6 +84,7 @@ def lib():
         "moe_replay_gate": [P, ctypes.c_int, P, P, I64, I32, cfgp, P, I64, P, P, P, P],
         "moe_router_score_eval": [P, I64, ctypes.c_int, P, P],
         "moe_quant_fp8_block": [P, ctypes.c_int, I64, I64, I32, I32, I32, P, P, P],
+        "moe_route_quant": [P, I64, ctypes.POINTER(RouterCfg), P, P, P, I64, P, ctypes.c_int, I32, I32, P, P, P],
         "moe_dispatch": [P, I64, I32, I32, I32, P, P, I32, P, P, P, P, P, P, P, SZ, P],
         "moe_dispatch_plan": [P, I64, I32, I32, I32, P, P, I32, P, P, P, P, P, P, P, SZ, I32, P, SZ,
                               ctypes.POINTER(GemmPlan), P],
@@ -231,6 +232,36 @@ def moe_route(logits: torch.Tensor, cfg: RouterCfg, record: Optional[torch.Tenso
     _check(lib().moe_route(_p(logits), T, ctypes.byref(cfg), _p(idx), _p(w), rec_ptr, rec_ld, _stream(stream)),
            "moe_route")
     return idx, w
+
+
+def moe_route_quant(logits: torch.Tensor, cfg: RouterCfg, x: torch.Tensor, record: Optional[torch.Tensor] = None,
+                    topk_idx=None, topk_w=None, q=None, scales=None, stream=None, pow2: bool = False):
+    """moe_route and the 1x128 quantisation of x [T,H] in one launch; returns (topk_idx, topk_w, q, scales)."""
+    T, E = logits.shape
+    _dev(logits, "logits", torch.float32)
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    if x.dim() != 2 or x.shape[0] != T or x.shape[1] % 128:
+        raise ValueError("x must be [T, H] with H % 128 == 0")
+    H = x.shape[1]
+    if E != cfg.num_experts:
+        raise ValueError("logits width != num_experts")
+    k = cfg.top_k
+    dev = logits.device
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_idx is None else _dev(topk_idx, "topk_idx", torch.int32, (T, k))
+    w = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_w is None else _dev(topk_w, "topk_w", torch.float32, (T, k))
+    q = torch.empty((T, H), dtype=FP8, device=dev) if q is None else _dev(q, "q", FP8, (T, H))
+    scales = torch.empty((T, H // 128), dtype=torch.float32, device=dev) if scales is None else \
+        _dev(scales, "scales", torch.float32, (T, H // 128))
+    rec_ptr, rec_ld = None, 0
+    if record is not None:
+        if record.device.type != "cuda" or record.dtype != torch.int32 or record.dim() != 2 or record.shape[0] != k \
+                or record.stride(1) != 1 or record.shape[1] < T:
+            raise ValueError("record must be a cuda int32 [k, seq_len>=T] view with unit column stride")
+        rec_ptr, rec_ld = _p(record), record.stride(0)
+    _check(lib().moe_route_quant(_p(logits), T, ctypes.byref(cfg), _p(idx), _p(w), rec_ptr, rec_ld, _p(x), _act_code(x),
+                                 H, MOE_SCALE_POW2 if pow2 else MOE_SCALE_AMAX, _p(q), _p(scales), _stream(stream)),
+           "moe_route_quant")
+    return idx, w, q, scales
 
 
 def moe_replay_route(logits: torch.Tensor, cfg: RouterCfg, replay: torch.Tensor, bad_count: Optional[torch.Tensor] = None,

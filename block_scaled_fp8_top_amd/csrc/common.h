@@ -99,3 +99,46 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
 static inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* x, int64_t i, float (&v)[8]) {
+  if (BF16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + i);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(w[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + i);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+__device__ __forceinline__ uint2 encode8(const float (&v)[8], float s) {
+  float r[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) r[q] = v[q] / s;
+  return make_uint2(e4m3_pack4(r[0], r[1], r[2], r[3]), e4m3_pack4(r[4], r[5], r[6], r[7]));
+}
+
+
+// 1x128 activation block b (x[128 b, 128 b + 128), rows contiguous and cols % 128 == 0): 16 lanes
+// per block, lane `sub` holding 8 consecutive values; amax across the 16 lanes, the block scale,
+// e4m3 codes (x / s an IEEE division) and, from lane 0, the scale.
+template <bool BF16, bool POW2>
+__device__ __forceinline__ void quant_1x128_piece(const void* __restrict__ x, int64_t b, int sub,
+                                                  uint8_t* __restrict__ q, float* __restrict__ scales) {
+  float v[8];
+  load8<BF16>(x, b * 128 + sub * 8, v);
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  const float s = block_scale(m, POW2);
+  *reinterpret_cast<uint2*>(q + b * 128 + sub * 8) = encode8(v, s);
+  if (sub == 0) scales[b] = s;
+}

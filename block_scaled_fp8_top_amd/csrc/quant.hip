@@ -9,30 +9,6 @@
 
 namespace {
 
-template <bool BF16>
-__device__ __forceinline__ void load8(const void* x, int64_t i, float (&v)[8]) {
-  if (BF16) {
-    const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + i);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[2 * q] = __uint_as_float(w[q] << 16);
-      v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + i);
-    const float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-}
-
-__device__ __forceinline__ uint2 encode8(const float (&v)[8], float s) {
-  float r[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) r[q] = v[q] / s;
-  return make_uint2(e4m3_pack4(r[0], r[1], r[2], r[3]), e4m3_pack4(r[4], r[5], r[6], r[7]));
-}
-
 // 1x128: 16 lanes per block, 8 consecutive values per lane.  Blocks are contiguous in memory
 // (rows are contiguous and cols % 128 == 0), so block b covers x[128 b, 128 b + 128) and its
 // scale is scales[b].
@@ -41,19 +17,9 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict
                                                           uint8_t* __restrict__ q, float* __restrict__ scales) {
   const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t b = gt >> 4;
-  const int sub = threadIdx.x & 15;
   // every lane of a 16-lane group shares b; whole groups are in or out of range
   if (b >= nblocks) return;
-  float v[8];
-  load8<BF16>(x, b * 128 + sub * 8, v);
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  const float s = block_scale(m, POW2);
-  *reinterpret_cast<uint2*>(q + b * 128 + sub * 8) = encode8(v, s);
-  if (sub == 0) scales[b] = s;
+  quant_1x128_piece<BF16, POW2>(x, b, threadIdx.x & 15, q, scales);
 }
 
 // 128x128: one workgroup of 256 threads per block; thread (r16 = tid / 16, c = tid % 16) handles

@@ -83,18 +83,11 @@ __device__ __forceinline__ void token_scores(const float* __restrict__ zrow, int
 }
 
 template <int EPL>
-__global__ __launch_bounds__(64 * WAVES) void route_kernel(const float* __restrict__ logits, int64_t T,
-                                                           moe_router_cfg cfg, int32_t* __restrict__ topk_idx,
-                                                           float* __restrict__ topk_w, int32_t* __restrict__ record,
-                                                           int64_t record_ld) {
-  __shared__ float key_s[WAVES][64 * EPL];
-  __shared__ float sc_s[WAVES][64 * EPL];
-  const int lane = threadIdx.x % 64, wv = threadIdx.x / 64;
-  const int64_t t = (int64_t)blockIdx.x * WAVES + wv;
-  if (t >= T) return;
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int64_t t, const moe_router_cfg& cfg,
+                                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                            int32_t* __restrict__ record, int64_t record_ld, int lane, float* key,
+                                            float* sc) {
   const int E = cfg.num_experts, k = cfg.top_k;
-  float* key = key_s[wv];
-  float* sc = sc_s[wv];
   float z[EPL];
   token_scores<EPL>(logits + t * E, E, cfg.score_fn, lane, z, key, sc);
 
@@ -181,6 +174,45 @@ __global__ __launch_bounds__(64 * WAVES) void route_kernel(const float* __restri
     topk_w[t * k + lane] = w;
     if (record) record[lane * record_ld + t] = my_e;
   }
+}
+
+// one wavefront per token
+template <int EPL>
+__global__ __launch_bounds__(64 * WAVES) void route_kernel(const float* __restrict__ logits, int64_t T,
+                                                           moe_router_cfg cfg, int32_t* __restrict__ topk_idx,
+                                                           float* __restrict__ topk_w, int32_t* __restrict__ record,
+                                                           int64_t record_ld) {
+  __shared__ float key_s[WAVES][64 * EPL];
+  __shared__ float sc_s[WAVES][64 * EPL];
+  const int lane = threadIdx.x % 64, wv = threadIdx.x / 64;
+  const int64_t t = (int64_t)blockIdx.x * WAVES + wv;
+  if (t >= T) return;
+  route_token<EPL>(logits, t, cfg, topk_idx, topk_w, record, record_ld, lane, key_s[wv], sc_s[wv]);
+}
+
+// The router and the 1x128 quantisation of x in one launch (the quantisation does not depend on
+// the routing): workgroups [0, nroute) route 4 tokens each as route_kernel does; the others
+// quantise 16 blocks of 128 values each, as the 1x128 quantisation kernel does.
+template <int EPL, bool BF16, bool POW2>
+__global__ __launch_bounds__(64 * WAVES) void route_quant_kernel(const float* __restrict__ logits, int64_t T,
+                                                                 moe_router_cfg cfg, int32_t* __restrict__ topk_idx,
+                                                                 float* __restrict__ topk_w,
+                                                                 int32_t* __restrict__ record, int64_t record_ld,
+                                                                 int64_t nroute, const void* __restrict__ x,
+                                                                 int64_t nblocks, uint8_t* __restrict__ xq,
+                                                                 float* __restrict__ xs) {
+  __shared__ float key_s[WAVES][64 * EPL];
+  __shared__ float sc_s[WAVES][64 * EPL];
+  if ((int64_t)blockIdx.x < nroute) {
+    const int lane = threadIdx.x % 64, wv = threadIdx.x / 64;
+    const int64_t t = (int64_t)blockIdx.x * WAVES + wv;
+    if (t >= T) return;
+    route_token<EPL>(logits, t, cfg, topk_idx, topk_w, record, record_ld, lane, key_s[wv], sc_s[wv]);
+    return;
+  }
+  const int64_t b = ((int64_t)blockIdx.x - nroute) * 16 + threadIdx.x / 16;
+  if (b >= nblocks) return;   // whole 16-lane groups are in or out of range
+  quant_1x128_piece<BF16, POW2>(x, b, threadIdx.x & 15, xq, xs);
 }
 
 template <int EPL>
@@ -366,6 +398,37 @@ extern "C" int moe_route(const float* logits, int64_t T, const moe_router_cfg* c
   hipStream_t st = as_stream(stream);
   DISPATCH_EPL(c.num_experts, (route_kernel<EPL><<<grid, 64 * WAVES, 0, st>>>(logits, T, c, topk_idx, topk_w,
                                                                                record, record_ld)));
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+extern "C" int moe_route_quant(const float* logits, int64_t T, const moe_router_cfg* cfg, int32_t* topk_idx,
+                               float* topk_w, int32_t* record, int64_t record_ld, const void* x, int x_dtype,
+                               int32_t H, int32_t scale_mode, uint8_t* xq, float* xs, void* stream) {
+  const int rc = check_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  if (T < 0 || T > (int64_t)INT32_MAX * WAVES) return MOE_ERR_SHAPE;
+  if (H < 128 || H % 128 != 0) return MOE_ERR_SHAPE;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (scale_mode != MOE_SCALE_AMAX && scale_mode != MOE_SCALE_POW2) return MOE_ERR_ARG;
+  if (record && record_ld < T) return MOE_ERR_ARG;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !topk_w || !x || !xq || !xs) return MOE_ERR_NULL;
+  const moe_router_cfg c = *cfg;
+  const int64_t nroute = ceil_div64(T, WAVES);
+  const int64_t nblocks = T * (H / 128);
+  const int64_t grid = nroute + ceil_div64(nblocks, 16);
+  if (grid > INT32_MAX) return MOE_ERR_SHAPE;
+  hipStream_t st = as_stream(stream);
+  const bool bf16 = x_dtype == MOE_BF16, pow2 = scale_mode == MOE_SCALE_POW2;
+#define RQ_LAUNCH(B, P)                                                                                          \
+  DISPATCH_EPL(c.num_experts, (route_quant_kernel<EPL, B, P><<<(unsigned)grid, 64 * WAVES, 0, st>>>(             \
+                                  logits, T, c, topk_idx, topk_w, record, record_ld, nroute, x, nblocks, xq, xs)))
+  if (bf16 && pow2) RQ_LAUNCH(true, true);
+  else if (bf16) RQ_LAUNCH(true, false);
+  else if (pow2) RQ_LAUNCH(false, true);
+  else RQ_LAUNCH(false, false);
+#undef RQ_LAUNCH
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

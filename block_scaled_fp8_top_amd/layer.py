@@ -1,8 +1,9 @@
 """One MoE layer forward composed from the C-ABI calls, with buffers allocated once.
 
 forward(x) enqueues, on the current stream and without any host synchronisation:
-  moe_gate_logits -> moe_route (optionally recording into the routing payload) or
-  moe_replay_route -> moe_quant_fp8_block (x, 1x128) -> moe_dispatch_plan (permutation indices and
+  moe_gate_logits -> moe_route_quant (the router, optionally recording into the routing payload, and
+  the 1x128 quantisation of x in one launch) or moe_replay_route / moe_replay_gate ->
+  moe_quant_fp8_block (x, 1x128) -> moe_dispatch_plan (permutation indices and
   scales, and the tile plan of both expert GEMMs) -> moe_grouped_gemm_fp8_gather (W1 on the rows of
   xq gathered through src_token, SwiGLU + 1x128 quantisation of h) -> moe_grouped_gemm_fp8_planned
   (W2) -> moe_combine.
@@ -225,9 +226,12 @@ class MoELayer:
             M.moe_replay_route(self.logits, w.cfg, replay, bad_count=self.bad, topk_idx=self.idx, topk_w=self.wts,
                                stream=stream)
         else:
-            M.moe_route(self.logits, w.cfg, record=record, topk_idx=self.idx, topk_w=self.wts, stream=stream)
+            # the router and x's 1x128 quantisation in one launch
+            M.moe_route_quant(self.logits, w.cfg, x, record=record, topk_idx=self.idx, topk_w=self.wts, q=self.xq,
+                              scales=self.xs, stream=stream, pow2=w.pow2)
         mark(2)
-        M.moe_quant_fp8_block(x, 1, q=self.xq, scales=self.xs, stream=stream, pow2=w.pow2)
+        if replay is not None:
+            M.moe_quant_fp8_block(x, 1, q=self.xq, scales=self.xs, stream=stream, pow2=w.pow2)
         mark(3)
         # dispatch, and one tile plan for both expert GEMMs (same groups), living in the GEMM workspace
         # (for decode-sized batches the dispatch workgroup writes it)

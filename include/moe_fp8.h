@@ -116,6 +116,15 @@ int moe_gate_logits(const void* x, int x_dtype, const float* wg, const float* bi
 int moe_route(const float* logits, int64_t T, const moe_router_cfg* cfg, int32_t* topk_idx, float* topk_w,
               int32_t* record, int64_t record_ld, void* stream);
 
+/* moe_route and the 1x128 quantisation of x (moe_quant_fp8_block with block_rows 1, scale_mode)
+ * in one launch: the quantisation does not depend on the routing, so its workgroups run beside the
+ * router's.  Outputs bitwise those of the two separate calls.
+ *   x [T, H] in x_dtype (MOE_F32 / MOE_BF16; H % 128 == 0) -> xq [T, H] e4m3, xs [T, H/128] fp32.
+ * Errors: as moe_route and moe_quant_fp8_block. */
+int moe_route_quant(const float* logits, int64_t T, const moe_router_cfg* cfg, int32_t* topk_idx, float* topk_w,
+                    int32_t* record, int64_t record_ld, const void* x, int x_dtype, int32_t H, int32_t scale_mode,
+                    uint8_t* xq, float* xs, void* stream);
+
 /* Router replay (blog section "Router replay": recorded decisions replayed on the trainer in place
  * of the router).  topk_idx[t,j] = replay[j*replay_ld + t] unchanged; weights recomputed from the
  * current logits with cfg's score function and normalisation (group limits do not apply).  A token

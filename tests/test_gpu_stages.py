@@ -122,6 +122,27 @@ def test_route_and_record(name):
     assert np.all(host(payload[0]) == -5)
 
 
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill"])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_route_quant_equals_separate_calls(name, pow2):
+    """moe_route_quant: the router's indices, weights and recorded payload and the 1x128 codes and
+    scales of x, bitwise those of moe_route and moe_quant_fp8_block called separately."""
+    cfg = synth.CONFIGS[name]
+    gcfg, _ = cfgs_for(cfg)
+    T, k = min(cfg.T, 2048), cfg.k
+    z = synth.make_logits(cfg, device=DEV)[:T].contiguous()
+    x = synth.make_x(cfg, DEV)[:T].contiguous()
+    p1 = torch.full((k, T), -3, dtype=torch.int32, device=DEV)
+    p2 = p1.clone()
+    i1, w1 = M.moe_route(z, gcfg, record=p1)
+    q1, s1 = M.moe_quant_fp8_block(x, 1, pow2=pow2)
+    i2, w2, q2, s2 = M.moe_route_quant(z, gcfg, x, record=p2, pow2=pow2)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(w1.view(torch.int32), w2.view(torch.int32))
+    assert torch.equal(p1, p2)
+    assert torch.equal(q1, q2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+
+
 @pytest.mark.parametrize("name", NAMES)
 def test_replay(name):
     cfg = synth.CONFIGS[name]
