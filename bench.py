@@ -1,22 +1,29 @@
 """Benchmark of the block-scaled FP8 MoE layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|longctx|r3|tiny|payload]
-                    [--scales amax|pow2] [--weights fp8|fp4] [--backward]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload longctx|prefill|decode|r3|tiny|payload]
+                    [--scales amax|pow2] [--weights fp8|fp4] [--backward] [--no-extras]
 
-A step is one full layer forward (gate logits, routing, activation quantisation, dispatch,
-grouped GEMM1 + SwiGLU + h quantisation, grouped GEMM2, combine) over one batch of synthetic
-tokens whose inputs and quantised weights are already resident in HBM.  The default workload is
-the decode-shaped layer (256 tokens, hidden 4096, 64 experts, FFN 1408, top-6).  Consecutive steps
-cycle through several copies of the layer (weights packed for the grouped GEMM, plus buffers), at
-least 2 GiB of weights in all, as consecutive layers of a model would: a step never finds its
-weights in the 256 MB Infinity Cache left behind by the step before.  The reported rate times
-replays of a HIP graph holding the whole layer forward (--no-graph: eager launches); a second
-pass of eager steps with HIP events between the stages gives the per-stage times.  Prints one JSON
-line: layer tokens/s, per-stage times, the grouped GEMM's TFLOP/s, the roofline of the dominant
-kernel, and the CPU oracle timed on a bounded sample.  With --backward a step is the layer's training
-forward (GEMM1 also keeps its fp32 output) followed by its backward (output gradient -> dx, dWg,
-db), and the line reports the backward's stages too.  --weights fp4 runs the same forward with FP4
-expert weights (E2M1 in 1x32 blocks with E8M0 scales; activations stay FP8 with power-of-two scales).
+A step is one pass of the layer forward (gate logits, routing with the 1x128 quantisation of x,
+dispatch, grouped GEMM1 + SwiGLU + h quantisation, grouped GEMM2, combine) over one batch of
+synthetic tokens whose inputs and quantised weights are already resident in HBM.  The default
+workload is the long-context layer: 131072 tokens streamed through one layer (hidden 6144, 256
+experts, FFN 2048, top-8 sigmoid routing in 8 groups keeping 4, with a Zipf(1.2) expert-popularity
+bias) as 16 chunks of 8192 tokens, each chunk's output written to its rows of the [131072, 6144]
+output; a step is the whole stream.  Consecutive steps cycle through several copies of the layer
+(weights packed for the grouped GEMM, plus buffers), at least 2 GiB of weights in all, so a step
+never finds its weights in the 256 MB Infinity Cache left behind by the step before.  The reported
+rate times replays of a HIP graph holding the whole step (--no-graph: eager launches); a second
+pass of eager steps with HIP events between the stages gives the per-stage times (on the launch
+stream).  Prints one JSON line: tokens/s, per-stage times and roofline fractions, the grouped
+GEMM's TFLOP/s, the roofline of the dominant kernel, the CPU oracle timed on a bounded sample and,
+unless --no-extras, the prefill layer (16384 tokens, 256 routed + 1 shared expert), the four-layer
+router-replay stack (32768 tokens: pass A routes and records, pass B replays on perturbed weights,
+pass C recomputes the routing on them) and the 128x128 quantisation of one layer's expert weights
+(the per-step cost of block-scaled FP8 training) as extra keys.
+With --backward a step is the layer's training forward (GEMM1 also keeps its fp32 output)
+followed by its backward (output gradient -> dx, dWg, db), and the line reports the backward's
+stages too.  --weights fp4 runs the same forward with FP4 expert weights (E2M1 in 1x32 blocks with
+E8M0 scales; activations stay FP8 with power-of-two scales).
 """
 from __future__ import annotations
 
@@ -32,10 +39,25 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0       # dense fp8 MFMA (published, no sparsity)
-PEAK_FP32_TFLOPS = 157.3       # published fp32 vector peak (a non-packed fma loop reaches 110 on the box)
+# fp32 vector peak this build can issue: the published 157.3 TFLOP/s needs packed fp32 FMAs, which
+# the build turns off, so one fma per lane per clock: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz
+PEAK_FP32_TFLOPS = 78.6
 RIDGE_FP8 = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+PEAKS = {"hbm": "8.0 TB/s HBM3E (published)", "mfma": "5.0 PFLOP/s dense fp8 (published)",
+         "alu": "78.6 TFLOP/s fp32 vector without packed FMA (published 157.3 needs packed fp32 FMA, "
+                "which the build turns off)"}
+# achievable peaks measured on MI355X with in-bounds microbenchmarks built here (a register-only fp8
+# MFMA loop, 16 independent accumulators, 2 waves per SIMD; streaming reads of contiguous 32 KB
+# blocks by 256-1024 workgroups); reported beside the published ones
+MEASURED_FP8_TFLOPS = 4680.0
+MEASURED_HBM_READ_GBS = 6300.0
 
-STAGES = ["gate_logits", "route", "quant_x", "dispatch", "gemm1_swiglu", "gemm2", "combine"]
+def log(msg):
+    """Progress line on stderr (the JSON result is the only line on stdout)."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+STAGES = ["gate_logits", "route_quant", "dispatch", "gemm1_swiglu", "gemm2", "combine"]
 BWD_STAGES = ["bwd_combine", "bwd_gemm_dh", "bwd_gemm_g", "bwd_swiglu", "bwd_gemm_da", "bwd_combine_dx", "bwd_route",
               "bwd_gate"]
 WGRAD_STAGES = ["bwd_wgrad_quant", "bwd_wgrad_gemm"]
@@ -44,10 +66,12 @@ WGRAD_STAGES = ["bwd_wgrad_quant", "bwd_wgrad_gemm"]
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="longctx")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the prefill layer, the replay stack and the weight quantisation after the headline")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
     ap.add_argument("--copies", type=int, default=0,
                     help="layer copies cycled through by consecutive steps (0: enough for 2 GiB of weights, >= 2)")
@@ -66,10 +90,11 @@ def parse():
     return ap.parse_args()
 
 
-def stage_model(cfg, counts, n_active1, fp4=False):
+def stage_model(cfg, counts, n_active1, fp4=False, record=False):
     """Algorithmic bytes and flops of each stage (inputs read once, outputs written once).  Expert
     weight bytes per element: 1 + 4/128^2 for e4m3 with 128x128 fp32 scales, 1/2 + 1/32 for FP4
-    with one E8M0 byte per 1x32 block."""
+    with one E8M0 byte per 1x32 block.  route_quant is one launch: the router (logits in, indices
+    and weights out, the payload record) and x's 1x128 quantisation."""
     T, H, E, F, k = cfg.T, cfg.H, cfg.E, cfg.F, cfg.k
     ab = 4 if cfg.act == "f32" else 2
     sig = 4.0 / 128
@@ -81,8 +106,8 @@ def stage_model(cfg, counts, n_active1, fp4=False):
     w2 = act_groups * (H * F) * wb
     return {
         "gate_logits": dict(bytes=T * H * ab + E * H * 4 + T * E * 4, flops=2.0 * T * H * E, bound="alu"),
-        "route": dict(bytes=T * E * 4 + T * k * 8, flops=0.0, bound="hbm"),
-        "quant_x": dict(bytes=T * H * (ab + 1 + sig), flops=0.0, bound="hbm"),
+        "route_quant": dict(bytes=T * E * 4 + T * k * 8 + (T * k * 4 if record else 0) + T * H * (ab + 1 + sig),
+                            flops=0.0, bound="hbm"),
         # ids in, dest_row and src_token out, the 1x128 scales permuted (GEMM1 gathers the codes)
         "dispatch": dict(bytes=T * k * 4 + T * k * 4 + rows * 4 + T * H * sig + rows * H * sig,
                          flops=0.0, bound="hbm"),
@@ -110,6 +135,392 @@ def stage_model(cfg, counts, n_active1, fp4=False):
     }
 
 
+def rates(m, ms):
+    """Achieved rates of work m (bytes, flops, bound) done in ms, and its roofline fraction.  A
+    GEMM's bound is the larger of its MFMA time (flops / fp8 peak) and its HBM time (algorithmic
+    bytes / HBM peak); both fractions are reported."""
+    t = ms * 1e-3
+    d = {"ms": round(ms, 4), "GB_s": round(m["bytes"] / t / 1e9, 1)}
+    if m["flops"]:
+        d["TFLOP_s"] = round(m["flops"] / t / 1e12, 2)
+    if m["bound"] is None:
+        t_mfma = m["flops"] / (PEAK_FP8_TFLOPS * 1e12)
+        t_hbm = m["bytes"] / (PEAK_HBM_GBS * 1e9)
+        d["bound"] = "mfma" if t_mfma >= t_hbm else "hbm"
+        d["frac"] = round(max(t_mfma, t_hbm) / t, 4)
+        d["frac_mfma"] = round(t_mfma / t, 4)
+        d["frac_hbm"] = round(t_hbm / t, 4)
+    else:
+        d["bound"] = m["bound"]
+        if d["bound"] == "alu":
+            d["frac"] = round(m["flops"] / t / 1e12 / PEAK_FP32_TFLOPS, 4)
+        else:
+            d["frac"] = round(m["bytes"] / t / 1e9 / PEAK_HBM_GBS, 4)
+    return d
+
+
+def sum_models(models, names):
+    """Stage models of several launches (chunks) added up."""
+    out = {}
+    for n in names:
+        out[n] = dict(bytes=sum(m[n]["bytes"] for m in models), flops=sum(m[n]["flops"] for m in models),
+                      bound=models[0][n]["bound"])
+    return out
+
+
+def build_weights(cfg, dev, pow2=False, fp4=False, layer=0, perturbed=False, keep_rowmajor=False):
+    """One layer's router gate and expert weights (quantised and packed on the GPU from the seeded
+    fp32 masters, one expert at a time)."""
+    import synth
+    import block_scaled_fp8_top_amd as M
+    from block_scaled_fp8_top_amd.layer import (MoELayerWeights, pack_expert_weights, quantize_expert_weights,
+                                                quantize_expert_weights_fp4)
+    sf = 0 if cfg.score_fn == "softmax" else 1
+    rcfg = M.router_cfg(cfg.E, cfg.k, sf, cfg.renorm, cfg.n_group, cfg.topk_group, cfg.group_score_topk)
+    wg, b = synth.make_gate(cfg, layer, dev, perturbed=perturbed)
+    master = lambda g: synth.make_expert(cfg, g, layer, dev, perturbed=perturbed)  # noqa: E731
+    if fp4:
+        w1p, w2p = quantize_expert_weights_fp4(cfg.groups, cfg.H, cfg.F, master, device=dev)
+        return MoELayerWeights(wg=wg, bias=b, w1q=None, w1s=None, w2q=None, w2s=None, cfg=rcfg, shared=cfg.shared,
+                               w1p=w1p, w2p=w2p, pow2=True)
+    w1q, w1s, w2q, w2s = quantize_expert_weights(cfg.groups, cfg.H, cfg.F, master, device=dev, pow2=pow2)
+    return pack_expert_weights(MoELayerWeights(wg=wg, bias=b, w1q=w1q, w1s=w1s, w2q=w2q, w2s=w2s, cfg=rcfg,
+                                               shared=cfg.shared, pow2=pow2), keep_rowmajor=keep_rowmajor)
+
+
+def clone_weights(weights):
+    """A second copy of a layer's packed expert weights (same values, other memory)."""
+    from dataclasses import replace
+    if weights.fp4:
+        return replace(weights, w1p=replace(weights.w1p, data=weights.w1p.data.clone(),
+                                            scales=weights.w1p.scales.clone()),
+                       w2p=replace(weights.w2p, data=weights.w2p.data.clone(), scales=weights.w2p.scales.clone()))
+    return replace(weights, w1p=replace(weights.w1p, data=weights.w1p.data.clone()),
+                   w2p=replace(weights.w2p, data=weights.w2p.data.clone()), w1s=weights.w1s.clone(),
+                   w2s=weights.w2s.clone())
+
+
+def free_gpu():
+    import gc
+    import torch
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def stage_kernel(stage, layer):
+    """The kernel a stage launches (the GEMM stages are one kernel each; the tile plan is part of
+    the dispatch stage)."""
+    import torch
+    p2 = ", fp4" if layer.w.fp4 else ", pow2" if layer.w.pow2 else ""
+    if stage == "gemm1_swiglu":
+        return f"grouped_gemm_kernel<{layer.plan.tile_rows}, swiglu_quant, packed{p2}>"
+    if stage == "gemm2":
+        out = "bf16" if layer.act == torch.bfloat16 else "f32"
+        return f"grouped_gemm_kernel<{layer.plan.tile_rows}, store_{out}, packed{p2}>"
+    if stage == "route_quant":
+        return "route_quant_kernel"
+    if stage == "gate_logits":
+        return "gate_logits_kernel"
+    if stage == "combine":
+        return "combine_kernel"
+    return stage
+
+
+def run_forward_workload(a, cfg, dev, steps, warmup, pow2=False, fp4=False, cpu=True):
+    """Time the layer forward on workload cfg; a step covers all of cfg's chunks.  Returns the
+    result dict (the JSON line's body for the headline, an extra key otherwise)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from block_scaled_fp8_top_amd.layer import MoELayer
+
+    log(f"{cfg.name}: building weights")
+    weights = build_weights(cfg, dev, pow2, fp4)
+    wbytes = weights.w1p.data.numel() + weights.w2p.data.numel()
+    copies = a.copies if a.copies > 0 else max(2, math.ceil((2 << 30) / wbytes))
+    act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
+    layers = [MoELayer(weights, cfg.T, act, dev)]
+    for _ in range(1, copies):
+        layers.append(MoELayer(clone_weights(weights), cfg.T, act, dev))
+    C, T = cfg.chunks, cfg.T
+    if C > 1:
+        x_all = torch.empty((C * T, cfg.H), dtype=act, device=dev)
+        for c in range(C):
+            x_all[c * T:(c + 1) * T] = synth.make_x(cfg, dev, chunk=c)
+    else:
+        x_all = synth.make_x(cfg, dev)
+    out_all = torch.empty_like(x_all)
+    xs = [x_all[c * T:(c + 1) * T] for c in range(C)]
+    outs = [out_all[c * T:(c + 1) * T] for c in range(C)]
+
+    def step(copy, evs=None):
+        lay = layers[copy]
+        for c in range(C):
+            lay.forward(xs[c], out=outs[c], events=None if evs is None else evs[c])
+
+    # census of the realised routing of every chunk (untimed): each chunk's group sizes
+    counts = []
+    for c in range(C):
+        layers[0].forward(xs[c], out=outs[c])
+        counts.append(layers[0].disp.counts.cpu().numpy())
+    for s in range(warmup):
+        step(s % copies)
+    torch.cuda.synchronize()
+    log(f"{cfg.name}: {copies} layer copies, {C} chunk(s) per step; timing {steps} steps")
+
+    graphs = None
+    if not a.no_graph:
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in range(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    step(c)
+                graphs.append(g)
+        torch.cuda.current_stream().wait_stream(side)
+        for s in range(warmup):
+            graphs[s % copies].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            graphs[s % copies].replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / steps
+
+    ns = len(STAGES)
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)] for _ in range(C)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(s % copies, ev[s])
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms_per_step = eager_ms if graphs is None else graph_ms
+    # stage time of chunk c, averaged over the steps (events on the launch stream)
+    chunk_ms = [{name: float(np.mean([ev[s][c][i].elapsed_time(ev[s][c][i + 1]) for s in range(steps)]))
+                 for i, name in enumerate(STAGES)} for c in range(C)]
+    models = [stage_model(cfg, counts[c], int((counts[c] > 0).sum()), fp4) for c in range(C)]
+    total = sum_models(models, STAGES)
+    stage_ms = {n: sum(chunk_ms[c][n] for c in range(C)) for n in STAGES}
+    stages = {n: rates(total[n], stage_ms[n]) for n in STAGES}
+    gemm_ms = stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]
+    gemm_flops = total["gemm1_swiglu"]["flops"] + total["gemm2"]["flops"]
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
+
+    # dominant kernel: the slowest stage; per launch = per chunk (same rows in every chunk, the
+    # active experts vary), so achieved = mean algorithmic work per launch / mean launch time
+    dom = max(STAGES, key=lambda n: stage_ms[n])
+    e = stages[dom]
+    launch_ms = stage_ms[dom] / C
+    if e["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": round(total[dom]["flops"] / C / (launch_ms * 1e-3) / 1e12, 2),
+                "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s"}
+    elif e["bound"] == "alu":
+        roof = {"bound": "alu", "achieved": round(total[dom]["flops"] / C / (launch_ms * 1e-3) / 1e12, 2),
+                "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(total[dom]["bytes"] / C / (launch_ms * 1e-3) / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    if roof["bound"] == "mfma":
+        roof["frac_of_measured_mfma_loop"] = round(roof["achieved"] / MEASURED_FP8_TFLOPS, 4)
+    elif roof["bound"] == "hbm":
+        roof["frac_of_measured_stream_read"] = round(roof["achieved"] / MEASURED_HBM_READ_GBS, 4)
+    kname = stage_kernel(dom, layers[0])
+    roof["traffic"] = measured_traffic(kname, cfg.name)
+    roof["kernel"] = kname
+    roof["stage"] = dom
+    roof["launch_ms"] = round(launch_ms, 4)
+    roof["launches_per_step"] = C
+
+    res = {
+        "value": round(C * T / (ms_per_step * 1e-3), 1),
+        "ms_per_step": round(ms_per_step, 4),
+        "launch": "eager" if graphs is None else "hip-graph replay",
+        "eager_ms_per_step": round(eager_ms, 4),
+        "config": {"workload": cfg.name, "tokens": C * T, "chunk_tokens": T, "chunks": C, "hidden": cfg.H,
+                   "experts": cfg.E, "shared_experts": int(cfg.shared), "ffn": cfg.F, "top_k": cfg.k,
+                   "score": cfg.score_fn, "group_limit": f"{cfg.n_group} groups keep {cfg.topk_group}"
+                   if cfg.n_group > 1 else None, "expert_bias": cfg.bias,
+                   "rows_per_chunk": models[0]["_rows"],
+                   "active_experts_per_chunk": [int((cc > 0).sum()) for cc in counts],
+                   "layer_copies": copies, "weight_layout": "packed",
+                   "block_scales": "power of two" if pow2 else "amax/448 fp32",
+                   "expert_weights": "fp4 e2m1, 1x32 e8m0 scales" if fp4 else "fp8 e4m3, 128x128 scales",
+                   "parallelism": "none (1 GPU)"},
+        "gemm_tflops": round(gemm_tflops, 2),
+        "gemm_frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+        "stages": stages,
+        "roofline": roof,
+    }
+    if C > 1:
+        # per chunk: GEMM1's bound and fraction from that chunk's realised group sizes
+        res["per_chunk"] = [{"active_experts": int((counts[c] > 0).sum()),
+                             "max_group_rows": int(counts[c].max()),
+                             "gemm1_swiglu": {k2: v for k2, v in rates(models[c]["gemm1_swiglu"],
+                                                                       chunk_ms[c]["gemm1_swiglu"]).items()
+                                              if k2 in ("ms", "bound", "frac", "frac_mfma", "frac_hbm")},
+                             "gemm2_frac": rates(models[c]["gemm2"], chunk_ms[c]["gemm2"])["frac"]}
+                            for c in range(C)]
+    if a.copy_probe_mb:
+        n = a.copy_probe_mb * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    x0 = xs[0].clone()
+    del layers, graphs, weights, x_all, out_all, xs, outs
+    free_gpu()
+    log(f"{cfg.name}: {res['value']:.0f} tokens/s, {res['ms_per_step']:.3f} ms per step")
+    if cpu:
+        log(f"{cfg.name}: CPU oracle baseline")
+        res["cpu_baseline"] = cpu_baseline(cfg, x0, dev, pow2, fp4)
+    return res
+
+
+def run_r3_stack(a, cfg, dev, steps, warmup):
+    """The four-layer replay stack (residual x_{l+1} = act(x_l + out_l)): pass A routes on W and
+    records the [layers, top_k, seq_len] payload, pass B replays it on W' = W + N(0, 1e-3), pass C
+    recomputes the routing on W'.  Each pass is one HIP graph replayed `steps` times; an untimed
+    eager run checks replay exactness and measures the drift that replay removes."""
+    import torch
+
+    import synth
+    from block_scaled_fp8_top_amd.layer import MoELayer
+
+    Lyr, T, k = cfg.layers, cfg.T, cfg.k
+    act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
+    W, Wp = [], []
+    for l in range(Lyr):
+        log(f"r3: building weights of layer {l} (W and W')")
+        W.append(build_weights(cfg, dev, layer=l))
+        Wp.append(build_weights(cfg, dev, layer=l, perturbed=True))
+    lay = MoELayer(W[0], T, act, dev)
+    payload = torch.full((Lyr, k, T), -1, dtype=torch.int32, device=dev)
+    x0 = synth.make_x(cfg, dev)
+    xbuf = {p: torch.empty_like(x0) for p in "ABC"}
+
+    def run_pass(p, keep=None):
+        x = xbuf[p]
+        x.copy_(x0)
+        for l in range(Lyr):
+            lay.w = W[l] if p == "A" else Wp[l]
+            if p == "A":
+                lay.forward(x, record=payload[l], residual_out=x)
+            elif p == "B":
+                lay.forward(x, replay=payload[l], residual_out=x)
+            else:
+                lay.forward(x, residual_out=x)
+            if keep is not None:
+                keep[(p, l)] = (lay.idx.clone(), lay.disp.counts.clone(), lay.disp.dest_row.clone(),
+                                int(lay.bad.item()))
+        return x
+
+    lay.bad.zero_()
+    keep = {}
+    for p in "ABC":
+        run_pass(p, keep)
+    torch.cuda.synchronize()
+    mismatch = sum(int((keep[("B", l)][0] != payload[l].t()).sum().item()) for l in range(Lyr))
+    perm_equal = all(torch.equal(keep[("B", l)][1], keep[("A", l)][1]) and
+                     torch.equal(keep[("B", l)][2], keep[("A", l)][2]) for l in range(Lyr))
+    drift = []
+    for l in range(Lyr):
+        ia, ic = keep[("A", l)][0], keep[("C", l)][0]
+        slot = (ic != ia).float().mean().item()
+        setd = 1.0 - (ic[:, :, None] == ia[:, None, :]).any(-1).float().mean().item()
+        drift.append({"layer": l, "slot_drift": round(slot, 4), "expert_set_drift": round(setd, 4)})
+
+    def rel(u, v):
+        u, v = u.float(), v.float()
+        return float((u - v).abs().max() / v.abs().max())
+
+    dB, dC = rel(xbuf["B"], xbuf["A"]), rel(xbuf["C"], xbuf["A"])
+    log(f"r3: checked passes (replay mismatch {mismatch}); timing")
+    passes = {}
+    for p in "ABC":
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                run_pass(p)
+        torch.cuda.current_stream().wait_stream(side)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        passes[p] = {"ms_per_pass": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                     "layer_tokens_per_s": round(Lyr * T / (ms * 1e-3), 1)}
+        del g
+    passes["A"]["what"] = "route on W, record the payload"
+    passes["B"]["what"] = "replay the payload on W' (gate projection fused with the replay: k logits per token)"
+    passes["C"]["what"] = "route again on W'"
+    res = {"workload": "r3", "layers": Lyr, "tokens": T, "passes": passes, "replay_index_mismatch": mismatch,
+           "replay_bad_ids": int(lay.bad.item()), "replay_permutation_equal": perm_equal,
+           "recompute_drift_per_layer": drift, "out_rel_diff_B_vs_A": round(dB, 4),
+           "out_rel_diff_C_vs_A": round(dC, 4), "steps": steps}
+    del W, Wp, lay, payload, xbuf, keep
+    free_gpu()
+    return res
+
+
+def run_weight_quant(cfg, dev, steps, pow2=False):
+    """128x128 block quantisation of one layer's expert weights (fp32 masters -> e4m3 codes + fp32
+    scales; all routed and shared experts, W1 and W2, one batched call each): the per-step weight
+    cast of block-scaled FP8 training, which inference does once offline."""
+    import torch
+
+    import block_scaled_fp8_top_amd as M
+    import synth
+
+    G, H, F = cfg.groups, cfg.H, cfg.F
+    log(f"weight quantisation: drawing {G} experts' fp32 masters")
+    w1 = torch.empty((G, 2 * F, H), dtype=torch.float32, device=dev)
+    w2 = torch.empty((G, H, F), dtype=torch.float32, device=dev)
+    for g in range(G):
+        a1, a2 = synth.make_expert(cfg, g, 0, dev)
+        w1[g].copy_(a1)
+        w2[g].copy_(a2)
+        del a1, a2
+    q1 = torch.empty(w1.shape, dtype=torch.uint8, device=dev)
+    q2 = torch.empty(w2.shape, dtype=torch.uint8, device=dev)
+    s1 = torch.empty((G, 2 * F // 128, H // 128), dtype=torch.float32, device=dev)
+    s2 = torch.empty((G, H // 128, F // 128), dtype=torch.float32, device=dev)
+
+    def once():
+        M.moe_quant_fp8_block(w1, 128, q=q1, scales=s1, pow2=pow2)
+        M.moe_quant_fp8_block(w2, 128, q=q2, scales=s2, pow2=pow2)
+
+    once()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        once()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    n = w1.numel() + w2.numel()
+    nbytes = n * (4 + 1) + (s1.numel() + s2.numel()) * 4
+    del w1, w2, q1, q2, s1, s2
+    free_gpu()
+    d = rates(dict(bytes=nbytes, flops=0.0, bound="hbm"), ms)
+    d.update({"kernel": "quant_128x128_kernel", "experts": G, "elements": n,
+              "what": "one layer's expert weights, fp32 masters -> e4m3 + 128x128 fp32 scales"})
+    return d
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -117,15 +528,10 @@ def main():
               "parallel dispatch/combine over xGMI) is not part of this build.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import block_scaled_fp8_top_amd as M
     import synth
-    from dataclasses import replace
-
-    from block_scaled_fp8_top_amd.layer import (MoELayer, MoELayerWeights, pack_expert_weights, quantize_expert_weights,
-                                                quantize_expert_weights_fp4)
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -136,203 +542,89 @@ def main():
         payload_bench(a)
         return
     cfg = synth.CONFIGS[a.workload]
-    sf = 0 if cfg.score_fn == "softmax" else 1
-    rcfg = M.router_cfg(cfg.E, cfg.k, sf, cfg.renorm, cfg.n_group, cfg.topk_group, cfg.group_score_topk)
-    wg, b = synth.make_gate(cfg, 0, dev)
     fp4 = a.weights == "fp4"
     if fp4 and a.backward:
         print("--weights fp4 is a forward-only format (no backward)", file=sys.stderr)
         sys.exit(2)
     pow2 = a.scales == "pow2" or fp4
-    bwd_weights = None
-    if fp4:
-        w1p, w2p = quantize_expert_weights_fp4(cfg.groups, cfg.H, cfg.F, lambda g: synth.make_expert(cfg, g, 0, dev),
-                                               device=dev)
-        weights = MoELayerWeights(wg=wg, bias=b, w1q=None, w1s=None, w2q=None, w2s=None, cfg=rcfg, shared=cfg.shared,
-                                  w1p=w1p, w2p=w2p, pow2=True)
-        del w1p, w2p
-    else:
-        w1q, w1s, w2q, w2s = quantize_expert_weights(cfg.groups, cfg.H, cfg.F,
-                                                     lambda g: synth.make_expert(cfg, g, 0, dev), device=dev, pow2=pow2)
-        weights = pack_expert_weights(MoELayerWeights(wg=wg, bias=b, w1q=w1q, w1s=w1s, w2q=w2q, w2s=w2s, cfg=rcfg,
-                                                      shared=cfg.shared, pow2=pow2), keep_rowmajor=a.backward)
-        if a.backward:
-            from block_scaled_fp8_top_amd.layer import prepare_backward_weights
-            bwd_weights = prepare_backward_weights(weights)
-            weights = replace(weights, w1q=None, w2q=None)
-        del w1q, w2q
-    wbytes = weights.w1p.data.numel() + weights.w2p.data.numel()
-    copies = a.copies if a.copies > 0 else max(2, math.ceil((2 << 30) / wbytes))
-    act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
-    layers = [MoELayer(weights, cfg.T, act, dev)]
-    for _ in range(1, copies):
-        if fp4:
-            wc = replace(weights, w1p=replace(weights.w1p, data=weights.w1p.data.clone(),
-                                              scales=weights.w1p.scales.clone()),
-                         w2p=replace(weights.w2p, data=weights.w2p.data.clone(), scales=weights.w2p.scales.clone()))
-        else:
-            wc = replace(weights, w1p=replace(weights.w1p, data=weights.w1p.data.clone()),
-                         w2p=replace(weights.w2p, data=weights.w2p.data.clone()), w1s=weights.w1s.clone(),
-                         w2s=weights.w2s.clone())
-        layers.append(MoELayer(wc, cfg.T, act, dev))
-    layer = layers[0]
-    x = synth.make_x(cfg, dev)
-    torch.cuda.synchronize()
     if a.backward:
-        backward_bench(a, cfg, layers, bwd_weights, x, copies, pow2)
+        backward_main(a, cfg, dev, pow2)
         return
-
-    for s in range(a.warmup):
-        layers[s % copies].forward(x)
-    torch.cuda.synchronize()
-    K = a.steps
-
-    # ---- timed region 1 (the reported rate): K steps, each one replay of a HIP graph holding the
-    # whole layer forward (the launch sequence of a decode loop, without per-kernel launch gaps)
-    graphs = None
-    if not a.no_graph:
-        graphs = []
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for c in range(copies):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=side):
-                    layers[c].forward(x)
-                graphs.append(g)
-        torch.cuda.current_stream().wait_stream(side)
-        for s in range(a.warmup):
-            graphs[s % copies].replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for s in range(K):
-            graphs[s % copies].replay()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        graph_ms = (t1 - t0) * 1e3 / K
-
-    # ---- timed region 2: K eager steps with HIP events between the stages on the launch stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(K):
-        layers[s % copies].forward(x, events=ev[s])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    eager_ms = (t1 - t0) * 1e3 / K
-    ms_per_step = eager_ms if graphs is None else graph_ms
-    stage_ms = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)]))
-                for i, name in enumerate(STAGES)}
-
-    counts = layer.disp.counts.cpu().numpy()
-    n_active = int((counts > 0).sum())
-    model = stage_model(cfg, counts, n_active, fp4)
-    stages = {}
-    for name in STAGES:
-        m = model[name]
-        t = stage_ms[name] * 1e-3
-        d = {"ms": round(stage_ms[name], 4), "GB_s": round(m["bytes"] / t / 1e9, 1)}
-        if m["flops"]:
-            d["TFLOP_s"] = round(m["flops"] / t / 1e12, 2)
-        if name.startswith("gemm"):
-            intensity = m["flops"] / m["bytes"]
-            d["bound"] = "mfma" if intensity >= RIDGE_FP8 else "hbm"
-            d["frac"] = round((m["flops"] / t / 1e12 / PEAK_FP8_TFLOPS) if d["bound"] == "mfma"
-                              else (m["bytes"] / t / 1e9 / PEAK_HBM_GBS), 4)
-        elif m["bound"] == "alu":
-            d["bound"] = "alu"
-            d["frac"] = round(m["flops"] / t / 1e12 / PEAK_FP32_TFLOPS, 4)
-        else:
-            d["bound"] = "hbm"
-            d["frac"] = round(m["bytes"] / t / 1e9 / PEAK_HBM_GBS, 4)
-        stages[name] = d
-
-    gemm_ms = stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]
-    gemm_flops = model["gemm1_swiglu"]["flops"] + model["gemm2"]["flops"]
-    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
-    dom = max(STAGES, key=lambda n: stage_ms[n])
-    dm = model[dom]
-    dt = stage_ms[dom] * 1e-3
-    bound = stages[dom]["bound"]
-    if bound == "mfma":
-        roof = {"bound": "mfma", "achieved": round(dm["flops"] / dt / 1e12, 2), "peak": PEAK_FP8_TFLOPS,
-                "unit": "TFLOP/s"}
-    elif bound == "alu":
-        roof = {"bound": "alu", "achieved": round(dm["flops"] / dt / 1e12, 2), "peak": PEAK_FP32_TFLOPS,
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": round(dm["bytes"] / dt / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    kname = stage_kernel(dom, layer)
-    roof["traffic"] = measured_traffic(kname, cfg.name)
-    roof["kernel"] = kname
-    roof["stage"] = dom
-
-    if a.copy_probe_mb:
-        n = a.copy_probe_mb * (1 << 20)
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-
-    cpu = None
-    if not a.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, x, dev, pow2, fp4)
-
-    tokens_per_s = cfg.T / (ms_per_step * 1e-3)
+    if a.workload == "r3":
+        r = run_r3_stack(a, cfg, dev, a.steps, a.warmup)
+        pa = r["passes"]["A"]
+        line = {"metric": "MoE layer tokens/s + grouped FP8 GEMM TFLOP/s (% of fp8 MFMA peak), 1 GPU",
+                "value": pa["layer_tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+                "warmup": a.warmup, "ms_per_step": pa["ms_per_pass"], "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3 x fp8-e4m3 -> fp32 (GEMM); fp32 router",
+                "data": "synthetic", "config": {"workload": "r3", "layers": cfg.layers, "tokens": cfg.T},
+                "r3": r}
+        print(json.dumps(line), flush=True)
+        return
+    steps, warm = a.steps, a.warmup
+    head = run_forward_workload(a, cfg, dev, steps, warm, pow2, fp4, cpu=not a.no_cpu_baseline)
     line = {
         "metric": "MoE layer tokens/s + grouped FP8 GEMM TFLOP/s (% of fp8 MFMA peak), 1 GPU",
-        "value": round(tokens_per_s, 1),
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
-        "warmup": a.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "launch": "eager" if graphs is None else "hip-graph replay",
-        "eager_ms_per_step": round(eager_ms, 4),
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": head["ms_per_step"],
+        "launch": head["launch"],
+        "eager_ms_per_step": head["eager_ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("fp4-e2m1 weights x fp8-e4m3" if fp4 else "fp8-e4m3 x fp8-e4m3") + " -> fp32 (GEMM); fp32 router; "
                  + ("bf16" if cfg.act == "bf16" else "fp32") + " activations",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) weights, random-init)",
-        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
-                   "shared_experts": int(cfg.shared), "ffn": cfg.F, "top_k": cfg.k, "score": cfg.score_fn,
-                   "rows": model["_rows"], "active_experts": n_active, "layer_copies": copies,
-                   "weight_layout": "packed", "block_scales": "power of two" if pow2 else "amax/448 fp32",
-                   "expert_weights": "fp4 e2m1, 1x32 e8m0 scales" if fp4 else "fp8 e4m3, 128x128 scales",
-                   "parallelism": "none (1 GPU)"},
-        "gemm_tflops": round(gemm_tflops, 2),
-        "gemm_frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
-        "stages": stages,
-        "roofline": roof,
-        "cpu_baseline": cpu,
+        "config": head["config"],
+        "gemm_tflops": head["gemm_tflops"],
+        "gemm_frac_fp8_peak": head["gemm_frac_fp8_peak"],
+        "stages": head["stages"],
+        "roofline": head["roofline"],
+        "cpu_baseline": head.get("cpu_baseline"),
+        "peaks": PEAKS,
     }
-    print(json.dumps(line))
+    if "per_chunk" in head:
+        line["per_chunk"] = head["per_chunk"]
+    if not a.no_extras and a.workload == "longctx" and not fp4:
+        xs = min(steps, 10)
+        pre = run_forward_workload(a, synth.CONFIGS["prefill"], dev, xs, 2, pow2, False, cpu=False)
+        line["prefill"] = {k2: pre[k2] for k2 in ("value", "ms_per_step", "gemm_tflops", "gemm_frac_fp8_peak",
+                                                 "stages", "roofline")}
+        line["prefill"]["unit"] = "tokens/s"
+        line["prefill"]["config"] = {k2: pre["config"][k2] for k2 in ("workload", "tokens", "experts",
+                                                                      "shared_experts", "block_scales")}
+        line["r3"] = run_r3_stack(a, synth.CONFIGS["r3"], dev, min(steps, 5), 1)
+        line["weight_quant"] = run_weight_quant(synth.CONFIGS["prefill"], dev, 3, pow2)
+    print(json.dumps(line), flush=True)
 
 
 GEMM_SRC = os.path.join(ROOT, "block_scaled_fp8_top_amd", "csrc", "grouped_gemm.hip")
 
 
-def stage_entry(name, model, ms):
-    """Achieved rates of one stage and its roofline fraction."""
-    m = model[name]
-    t = ms * 1e-3
-    d = {"ms": round(ms, 4), "GB_s": round(m["bytes"] / t / 1e9, 1)}
-    if m["flops"]:
-        d["TFLOP_s"] = round(m["flops"] / t / 1e12, 2)
-    if m["bound"] is None:
-        d["bound"] = "mfma" if m["flops"] / m["bytes"] >= RIDGE_FP8 else "hbm"
-    else:
-        d["bound"] = m["bound"]
-    if d["bound"] == "mfma":
-        d["frac"] = round(m["flops"] / t / 1e12 / PEAK_FP8_TFLOPS, 4)
-    elif d["bound"] == "alu":
-        d["frac"] = round(m["flops"] / t / 1e12 / PEAK_FP32_TFLOPS, 4)
-    else:
-        d["frac"] = round(m["bytes"] / t / 1e9 / PEAK_HBM_GBS, 4)
-    return d
+def backward_main(a, cfg, dev, pow2):
+    """Layer copies with the backward's weight copies, then the forward + backward bench."""
+    import torch
+
+    import synth
+    from block_scaled_fp8_top_amd.layer import MoELayer, prepare_backward_weights
+    from dataclasses import replace
+
+    weights = build_weights(cfg, dev, pow2, keep_rowmajor=True)
+    bwd_weights = prepare_backward_weights(weights)
+    weights = replace(weights, w1q=None, w2q=None)
+    wbytes = weights.w1p.data.numel() + weights.w2p.data.numel()
+    copies = a.copies if a.copies > 0 else max(2, math.ceil((2 << 30) / wbytes))
+    act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
+    layers = [MoELayer(weights, cfg.T, act, dev)]
+    for _ in range(1, copies):
+        layers.append(MoELayer(clone_weights(weights), cfg.T, act, dev))
+    x = synth.make_x(cfg, dev)
+    torch.cuda.synchronize()
+    backward_bench(a, cfg, layers, bwd_weights, x, copies, pow2)
 
 
 def backward_bench(a, cfg, layers, bw, x, copies, pow2):
@@ -394,7 +686,7 @@ def backward_bench(a, cfg, layers, bw, x, copies, pow2):
     g1 = model["gemm1_swiglu"]
     model["gemm1_swiglu"] = dict(g1, bytes=g1["bytes"] + model["_rows"] * 2 * cfg.F * 4)
     timed = [n for n in STAGES + bst if n != "bwd_gemm_g"]   # no recompute after a training forward
-    stages = {name: stage_entry(name, model, stage_ms[name]) for name in timed}
+    stages = {name: rates(model[name], stage_ms[name]) for name in timed}
     fwd_ms = sum(stage_ms[n] for n in STAGES)
     bwd_ms = sum(stage_ms[n] for n in bst)
     gemm_names = [n for n in ("bwd_gemm_dh", "bwd_gemm_g", "bwd_gemm_da") if n in stages]
@@ -468,19 +760,6 @@ def cpu_baseline_backward(cfg, x, dout, dev, pow2=False):
     return {"value": round(len(toks) / dt, 3), "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
             "sample": f"{len(toks)} seeded tokens of {cfg.T}, per-token backward (with its forward), "
                       "expert weights pre-quantised", "seconds": round(dt, 2)}
-
-
-def stage_kernel(stage, layer):
-    """The kernel a stage launches (the GEMM stages are one kernel each; the tile plan is part of
-    the dispatch stage)."""
-    import torch
-    p2 = ", fp4" if layer.w.fp4 else ", pow2" if layer.w.pow2 else ""
-    if stage == "gemm1_swiglu":
-        return f"grouped_gemm_kernel<{layer.plan.tile_rows}, swiglu_quant, packed{p2}>"
-    if stage == "gemm2":
-        out = "bf16" if layer.act == torch.bfloat16 else "f32"
-        return f"grouped_gemm_kernel<{layer.plan.tile_rows}, store_{out}, packed{p2}>"
-    return stage
 
 
 def measured_traffic(kernel, workload):

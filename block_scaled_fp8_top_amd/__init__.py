@@ -33,7 +33,7 @@ EXPORTED = ("moe_gate_logits", "moe_route", "moe_route_quant", "moe_replay_route
             "moe_quant_fp8_block",
             "moe_dispatch", "moe_dispatch_plan", "moe_pack_weights_fp8", "moe_packed_weight_bytes", "moe_grouped_gemm_plan",
             "moe_grouped_gemm_fp8_planned", "moe_grouped_gemm_fp8_swiglu_save", "moe_grouped_gemm_fp8_gather",
-            "moe_grouped_gemm_fp8", "moe_combine", "moe_payload_bytes",
+            "moe_grouped_gemm_fp8", "moe_combine", "moe_combine_residual", "moe_payload_bytes",
             "moe_payload_pack", "moe_payload_unpack", "moe_payload_to_host", "moe_payload_from_host",
             "moe_combine_backward", "moe_swiglu_backward_quant", "moe_route_backward", "moe_gate_backward",
             "moe_gate_backward_workspace", "moe_transpose_fp8_blocks", "moe_wgrad_max_tiles", "moe_wgrad_tiles",
@@ -99,6 +99,7 @@ def lib():
         "moe_grouped_gemm_fp8_gather": [ctypes.POINTER(GemmPlan), P, I64, P, P, P, P, I32, P, I32, I32, I32, I32, P,
                                         ctypes.c_int, P, P, P],
         "moe_combine": [P, ctypes.c_int, P, P, I64, I32, I32, P, P, ctypes.c_int, P],
+        "moe_combine_residual": [P, ctypes.c_int, P, P, I64, I32, I32, P, P, P, P, ctypes.c_int, P],
         "moe_payload_bytes": [I64, I32],
         "moe_payload_pack": [P, I64, I32, P, P, P],
         "moe_payload_unpack": [P, I64, I32, P, P],
@@ -377,7 +378,7 @@ def moe_dispatch(topk_idx: torch.Tensor, num_experts: int, append_shared: bool, 
     ws_need = workspace_bytes(MOE_OP_DISPATCH, T, k, num_experts)
     if workspace is None:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
-    elif workspace.numel() * workspace.element_size() < ws_need:
+    elif _dev(workspace, "workspace", torch.uint8).numel() < ws_need:
         raise ValueError("workspace too small")
     if out is None:
         out = Dispatched(
@@ -411,6 +412,8 @@ def moe_dispatch_plan(topk_idx: torch.Tensor, num_experts: int, append_shared: b
         _dev(xq, "xq", FP8, (T, H))
         _dev(xs, "xs", torch.float32, (T, H // 128))
     _check_dispatched(out, T, k, num_experts + (1 if append_shared else 0), T * k + (T if append_shared else 0), H)
+    _dev(workspace, "workspace", torch.uint8)
+    _dev(gemm_workspace, "gemm_workspace", torch.uint8)
     if workspace.numel() * workspace.element_size() < workspace_bytes(MOE_OP_DISPATCH, T, k, num_experts):
         raise ValueError("workspace too small")
     plan = GemmPlan()
@@ -623,6 +626,33 @@ def moe_combine(y: torch.Tensor, dest_row: torch.Tensor, topk_w: torch.Tensor, s
     return out
 
 
+def moe_combine_residual(y: torch.Tensor, dest_row: torch.Tensor, topk_w: torch.Tensor,
+                         shared_first_row: Optional[torch.Tensor], residual: torch.Tensor, x_next=None, out=None,
+                         write_out: bool = False, stream=None):
+    """The combine on a residual branch: o = act(sum_j w[t,j] y[dest_row[t,j]] (+ shared row)) and
+    x_next = act(residual + o), act = residual's dtype.  Returns x_next, or (x_next, o) when
+    ``write_out`` (o then goes to ``out``, bitwise what moe_combine writes).  x_next may be
+    ``residual`` itself (in-place update of the stack's activations)."""
+    _dev(y, "y", (torch.float32, torch.bfloat16))
+    T, k = dest_row.shape
+    H = y.shape[1]
+    _dev(dest_row, "dest_row", torch.int32)
+    _dev(topk_w, "topk_w", torch.float32, (T, k))
+    if shared_first_row is not None:
+        _dev(shared_first_row, "shared_first_row", torch.int32, (1,))
+    _dev(residual, "residual", (torch.float32, torch.bfloat16), (T, H))
+    ad = residual.dtype
+    x_next = torch.empty_like(residual) if x_next is None else _dev(x_next, "x_next", ad, (T, H))
+    if write_out:
+        out = torch.empty((T, H), dtype=ad, device=y.device) if out is None else _dev(out, "out", ad, (T, H))
+    else:
+        out = None
+    _check(lib().moe_combine_residual(_p(y), _act_code(y), _p(dest_row), _p(topk_w), T, k, H, _p(shared_first_row),
+                                      _p(residual), _p(out), _p(x_next), _act_code(residual), _stream(stream)),
+           "moe_combine_residual")
+    return (x_next, out) if write_out else x_next
+
+
 def payload_bytes(n: int, num_experts: int) -> int:
     """Bytes of a packed router-replay payload of n indices (0 for an invalid size)."""
     return int(lib().moe_payload_bytes(n, num_experts))
@@ -680,6 +710,8 @@ def moe_payload_to_host(payload: torch.Tensor, num_experts: int, staging: torch.
     _payload_out(n, num_experts, staging, payload.device)
     if host.device.type != "cpu" or host.dtype != torch.uint8 or host.numel() < nb or not host.is_contiguous():
         raise ValueError(f"host buffer must be a contiguous uint8 CPU tensor with >= {nb} bytes")
+    if not host.is_pinned():
+        raise ValueError("host buffer must be pinned (torch.empty(..., pin_memory=True)): the copy is asynchronous")
     _check(lib().moe_payload_to_host(_p(payload), n, num_experts, _p(staging), _p(host), _p(bad_count),
                                      _stream(stream)), "moe_payload_to_host")
     return host
@@ -695,6 +727,8 @@ def moe_payload_from_host(host: torch.Tensor, shape, num_experts: int, staging: 
     nb = payload_bytes(n, num_experts)
     if host.device.type != "cpu" or host.dtype != torch.uint8 or host.numel() < nb or not host.is_contiguous():
         raise ValueError(f"host buffer must be a contiguous uint8 CPU tensor with >= {nb} bytes")
+    if not host.is_pinned():
+        raise ValueError("host buffer must be pinned (torch.empty(..., pin_memory=True)): the copy is asynchronous")
     _dev(staging, "staging", torch.uint8)
     _payload_out(n, num_experts, staging, staging.device)
     out = torch.empty(tuple(shape), dtype=torch.int32, device=staging.device) if out is None else \

@@ -4,7 +4,9 @@
 // bf16 or 2 x 16-byte fp32 loads).  The rows of up to 8 slots are loaded together (all loads in
 // flight before the first use), then accumulated in fp32 with fused multiply-adds in slot order,
 // the shared row added last, one rounding to the output dtype.  No atomics: each output element
-// has one owner.
+// has one owner.  The residual form (a MoE layer on a residual branch, stacked) also adds the layer
+// input: x_next = act(residual + act(sum)), the sum rounded to the activation dtype first, exactly
+// as if the layer output were stored and then added in fp32 and rounded again.
 #include "common.h"
 
 namespace {
@@ -26,11 +28,33 @@ __device__ __forceinline__ void load8y(const void* y, int64_t off, float (&v)[8]
   }
 }
 
-template <bool YBF16, bool OBF16>
+template <bool OBF16>
+__device__ __forceinline__ void store8(void* __restrict__ out, int64_t off, const float (&v)[8]) {
+  if (OBF16) {
+    uint32_t p[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) p[q] = (uint32_t)f32_to_bf16(v[2 * q]) | ((uint32_t)f32_to_bf16(v[2 * q + 1]) << 16);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + off) = make_uint4(p[0], p[1], p[2], p[3]);
+  } else {
+    float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + off);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+// the value a float takes once stored in the output dtype
+template <bool OBF16>
+__device__ __forceinline__ float as_stored(float v) {
+  return OBF16 ? bf16_to_f32(f32_to_bf16(v)) : v;
+}
+
+// RES: residual form (out may be NULL; x_next = act(residual + act(sum)), all in the output dtype)
+template <bool YBF16, bool OBF16, bool RES = false>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y, const int32_t* __restrict__ dest,
                                                       const float* __restrict__ w, int k, int H,
                                                       const int32_t* __restrict__ shared_first_row,
-                                                      void* __restrict__ out) {
+                                                      void* __restrict__ out, const void* residual = nullptr,
+                                                      void* x_next = nullptr) {
   const int64_t t = blockIdx.x;
   const int32_t* d = dest + t * k;
   const float* wt = w + t * k;
@@ -60,15 +84,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] = acc[q] + v[q];
     }
-    if (OBF16) {
-      uint32_t p[4];
+    if (!RES || out) store8<OBF16>(out, t * H + c, acc);
+    if (RES) {
+      float r[8];
+      load8y<OBF16>(residual, t * H + c, r);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) p[q] = (uint32_t)f32_to_bf16(acc[2 * q]) | ((uint32_t)f32_to_bf16(acc[2 * q + 1]) << 16);
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + t * H + c) = make_uint4(p[0], p[1], p[2], p[3]);
-    } else {
-      float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + t * H + c);
-      o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      for (int q = 0; q < 8; ++q) r[q] = r[q] + as_stored<OBF16>(acc[q]);
+      store8<OBF16>(x_next, t * H + c, r);
     }
   }
 }
@@ -95,6 +117,34 @@ extern "C" int moe_combine(const void* y, int y_dtype, const int32_t* dest_row, 
     combine_kernel<false, true><<<grid, 256, 0, st>>>(y, dest_row, topk_w, k, H, shared_first_row, out);
   else
     combine_kernel<false, false><<<grid, 256, 0, st>>>(y, dest_row, topk_w, k, H, shared_first_row, out);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+extern "C" int moe_combine_residual(const void* y, int y_dtype, const int32_t* dest_row, const float* topk_w, int64_t T,
+                                    int32_t k, int32_t H, const int32_t* shared_first_row, const void* residual,
+                                    void* out, void* x_next, int act_dtype, void* stream) {
+  if (T < 0 || k < 1 || k > 64 || H < 8 || H % 8 != 0) return MOE_ERR_SHAPE;
+  if ((y_dtype != MOE_BF16 && y_dtype != MOE_F32) || (act_dtype != MOE_BF16 && act_dtype != MOE_F32))
+    return MOE_ERR_DTYPE;
+  if (T == 0) return MOE_OK;
+  if (!y || !dest_row || !topk_w || !residual || !x_next) return MOE_ERR_NULL;
+  if (T > INT32_MAX) return MOE_ERR_SHAPE;
+  hipStream_t st = as_stream(stream);
+  const dim3 grid((unsigned)T, (unsigned)ceil_div64(H, 256 * 8));
+  const bool yb = y_dtype == MOE_BF16, ob = act_dtype == MOE_BF16;
+  if (yb && ob)
+    combine_kernel<true, true, true><<<grid, 256, 0, st>>>(y, dest_row, topk_w, k, H, shared_first_row, out, residual,
+                                                           x_next);
+  else if (yb)
+    combine_kernel<true, false, true><<<grid, 256, 0, st>>>(y, dest_row, topk_w, k, H, shared_first_row, out,
+                                                            residual, x_next);
+  else if (ob)
+    combine_kernel<false, true, true><<<grid, 256, 0, st>>>(y, dest_row, topk_w, k, H, shared_first_row, out,
+                                                            residual, x_next);
+  else
+    combine_kernel<false, false, true><<<grid, 256, 0, st>>>(y, dest_row, topk_w, k, H, shared_first_row, out,
+                                                             residual, x_next);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

@@ -5,7 +5,11 @@
 // weights follow the router contract in moe_fp8.h step for step, so that indices and weights are
 // reproducible bit for bit.  Sequential sums (the softmax denominator over experts, the
 // renormalisation over slots) are taken in the stated order by a single lane or redundantly by
-// every lane, never as a tree.
+// every lane, never as a tree.  Logits may be -inf (a masked expert): such an expert still ranks
+// by the same rule (below every finite logit, ties to the lower index), so a token with fewer than
+// k finite allowed logits takes its remaining slots from the lowest-index allowed -inf experts.
+// The "no candidate" placeholder of a lane is (-inf, INT_MAX), which every real expert ranks
+// before.  NaN logits are outside the contract.
 #include <float.h>
 
 #include "common.h"
@@ -14,6 +18,9 @@ namespace {
 
 constexpr int WAVES = 4;  // tokens per workgroup
 constexpr int MAX_GROUPS = 64;
+// 1x128 blocks quantised by one workgroup of the fused router + quantisation launch (16 lanes per block)
+constexpr int QBLK = 64 * WAVES / 16;
+static_assert(QBLK * 16 == 64 * WAVES, "whole 16-lane groups per workgroup");
 
 struct Cand {
   float z;
@@ -48,7 +55,7 @@ __device__ __forceinline__ void token_scores(const float* __restrict__ zrow, int
     if (e < E) key[e] = z[j];
   }
   if (score_fn == MOE_SCORE_SOFTMAX) {
-    float m = -FLT_MAX;
+    float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < EPL; ++j)
       if (lane + 64 * j < E) m = fmaxf(m, z[j]);
@@ -146,7 +153,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
   int my_e = -1;
 #pragma unroll 1
   for (int r = 0; r < k; ++r) {
-    Cand c{-FLT_MAX, 0x7FFFFFFF};
+    Cand c{-INFINITY, 0x7FFFFFFF};
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const int e = lane + 64 * j;
@@ -210,7 +217,7 @@ __global__ __launch_bounds__(64 * WAVES) void route_quant_kernel(const float* __
     route_token<EPL>(logits, t, cfg, topk_idx, topk_w, record, record_ld, lane, key_s[wv], sc_s[wv]);
     return;
   }
-  const int64_t b = ((int64_t)blockIdx.x - nroute) * 16 + threadIdx.x / 16;
+  const int64_t b = ((int64_t)blockIdx.x - nroute) * QBLK + threadIdx.x / 16;
   if (b >= nblocks) return;   // whole 16-lane groups are in or out of range
   quant_1x128_piece<BF16, POW2>(x, b, threadIdx.x & 15, xq, xs);
 }
@@ -417,7 +424,7 @@ extern "C" int moe_route_quant(const float* logits, int64_t T, const moe_router_
   const moe_router_cfg c = *cfg;
   const int64_t nroute = ceil_div64(T, WAVES);
   const int64_t nblocks = T * (H / 128);
-  const int64_t grid = nroute + ceil_div64(nblocks, 16);
+  const int64_t grid = nroute + ceil_div64(nblocks, QBLK);
   if (grid > INT32_MAX) return MOE_ERR_SHAPE;
   hipStream_t st = as_stream(stream);
   const bool bf16 = x_dtype == MOE_BF16, pow2 = scale_mode == MOE_SCALE_POW2;

@@ -194,12 +194,18 @@ class MoELayer:
         return self.disp.src_token if self.gather_rows else None
 
     def forward(self, x: torch.Tensor, replay: Optional[torch.Tensor] = None, record: Optional[torch.Tensor] = None,
-                stream=None, events=None, fused_replay: bool = True, training: bool = False) -> torch.Tensor:
-        """``events``: optional list of 8 timing events (torch.cuda.Event), recorded on the launch
-        stream before the first stage and after each of the seven stages.  With ``replay`` and a
+                stream=None, events=None, fused_replay: bool = True, training: bool = False,
+                out: Optional[torch.Tensor] = None, residual_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """``events``: optional list of 7 timing events (torch.cuda.Event), recorded on the launch
+        stream before the first stage and after each of the six stages (gate logits, routing with
+        x's quantisation, dispatch, GEMM1, GEMM2, combine).  With ``replay`` and a
         sigmoid router the gate projection and the replay run fused (``fused_replay``), and
         ``self.logits`` is not written.  ``training``: GEMM1 also keeps its fp32 output for the
-        backward (which then does not recompute it)."""
+        backward (which then does not recompute it).  ``out``: where the combine writes the layer
+        output (default: the layer's own buffer), e.g. a chunk's rows of a longer sequence.
+        ``residual_out``: the layer sits on a residual branch; the combine then writes
+        act(x + output) there (it may be x itself) and returns it, and the layer output itself is
+        written only if ``out`` is given."""
         T = x.shape[0]
         if T != self.T_max:
             raise ValueError(f"layer buffers are sized for T={self.T_max}, got {T}")
@@ -218,6 +224,7 @@ class MoELayer:
         if not fused:
             M.moe_gate_logits(x, w.wg, w.bias, out=self.logits, stream=stream)
         mark(1)
+        # routing stage: the routing decisions and x's 1x128 quantisation
         if fused:
             # sigmoid replay: only the k recorded logits per token are needed (logits is not written)
             M.moe_replay_gate(x, w.wg, w.bias, w.cfg, replay, bad_count=self.bad, topk_idx=self.idx, topk_w=self.wts,
@@ -229,28 +236,33 @@ class MoELayer:
             # the router and x's 1x128 quantisation in one launch
             M.moe_route_quant(self.logits, w.cfg, x, record=record, topk_idx=self.idx, topk_w=self.wts, q=self.xq,
                               scales=self.xs, stream=stream, pow2=w.pow2)
-        mark(2)
         if replay is not None:
             M.moe_quant_fp8_block(x, 1, q=self.xq, scales=self.xs, stream=stream, pow2=w.pow2)
-        mark(3)
+        mark(2)
         # dispatch, and one tile plan for both expert GEMMs (same groups), living in the GEMM workspace
         # (for decode-sized batches the dispatch workgroup writes it)
         plan = self.plan = M.moe_dispatch_plan(self.idx, w.E, w.shared, self.xq, self.xs, self.workspace, self.disp,
                                                self.gemm_ws, stream=stream)
-        mark(4)
+        mark(3)
         M.moe_grouped_gemm_fp8(*self._gemm1_a(), self.disp.offsets, w.w1p or w.w1q, w.w1s,
                                epilogue=M.MOE_EPI_SWIGLU_QUANT, out=self.hq, out_scales=self.hs, plan=plan,
                                stream=stream, pow2=w.pow2,
                                save_g=self._backward_buffers()["g"] if training else None, a_rows=self._a_rows())
         self.g_saved = training
-        mark(5)
+        mark(4)
         M.moe_grouped_gemm_fp8(self.hq, self.hs, self.disp.offsets, w.w2p or w.w2q, w.w2s, epilogue=M.MOE_EPI_STORE,
                                out_dtype=self.act, out=self.y, plan=plan, stream=stream, pow2=w.pow2)
-        mark(6)
+        mark(5)
         shared_row = self.disp.offsets[w.E:w.E + 1] if w.shared else None
-        M.moe_combine(self.y, self.disp.dest_row, self.wts, shared_row, out=self.out, stream=stream)
-        mark(7)
-        return self.out
+        if residual_out is not None:
+            res = M.moe_combine_residual(self.y, self.disp.dest_row, self.wts, shared_row, x, x_next=residual_out,
+                                         out=out, write_out=out is not None, stream=stream)
+            mark(6)
+            return res[0] if out is not None else res
+        o = self.out if out is None else out
+        M.moe_combine(self.y, self.disp.dest_row, self.wts, shared_row, out=o, stream=stream)
+        mark(6)
+        return o
 
     def _backward_buffers(self):
         if self.bwd is not None:

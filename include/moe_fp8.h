@@ -112,6 +112,10 @@ int moe_gate_logits(const void* x, int x_dtype, const float* wg, const float* bi
  *   logits    [T,E] fp32          topk_idx [T,top_k] int32 (out)     topk_w [T,top_k] fp32 (out)
  *   record    NULL, or one layer of the routing payload [top_k, record_ld] int32 (record_ld >= T):
  *             record[j*record_ld + t] = topk_idx[t,j]
+ * Logits may be -inf (a masked expert): it ranks below every finite logit by the same rule, so a
+ * token with fewer than top_k finite allowed logits fills its last slots with the lowest-index
+ * allowed -inf experts.  A softmax router needs at least one finite logit per token (the maximum
+ * is subtracted); NaN logits are outside the contract.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ARG (invalid cfg, record_ld < T), MOE_ERR_HIP. */
 int moe_route(const float* logits, int64_t T, const moe_router_cfg* cfg, int32_t* topk_idx, float* topk_w,
               int32_t* record, int64_t record_ld, void* stream);
@@ -312,6 +316,19 @@ int moe_grouped_gemm_fp8_swiglu_save(const moe_gemm_plan* plan, const uint8_t* a
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (H % 8), MOE_ERR_DTYPE, MOE_ERR_HIP. */
 int moe_combine(const void* y, int y_dtype, const int32_t* dest_row, const float* topk_w, int64_t T, int32_t k,
                 int32_t H, const int32_t* shared_first_row, void* out, int out_dtype, void* stream);
+
+/* Combine on a residual branch (the replay stack of the blog's "Router replay" section runs the same
+ * MoE layer several layers deep; each layer's output is added to its input).
+ *   o[t,:]      = act(sum_j topk_w[t,j] * y[dest_row[t,j],:] (+ shared row))   -- as moe_combine
+ *   x_next[t,:] = act(residual[t,:] + o[t,:])     (fp32 add of the two stored values, one rounding)
+ * act = act_dtype (MOE_BF16 or MOE_F32) for residual, out and x_next.  out may be NULL (then only
+ * x_next is written); otherwise out receives o, bitwise what moe_combine writes.  x_next may alias
+ * residual (each element is read before it is written, by the same thread).
+ * Errors: MOE_ERR_NULL (y, dest_row, topk_w, residual or x_next NULL), MOE_ERR_SHAPE, MOE_ERR_DTYPE,
+ * MOE_ERR_HIP. */
+int moe_combine_residual(const void* y, int y_dtype, const int32_t* dest_row, const float* topk_w, int64_t T,
+                         int32_t k, int32_t H, const int32_t* shared_first_row, const void* residual, void* out,
+                         void* x_next, int act_dtype, void* stream);
 
 /* Router-replay payload codec (blog section "Router replay": the routing decisions recorded at
  * inference, a [num_layers, top_k, seq_len] integer payload, reach tens of Gbps and hundreds of GB

@@ -101,6 +101,16 @@ def to_act(y: np.ndarray, act: str) -> np.ndarray:
     return O.round_to_bf16(y32) if act == "bf16" else y32
 
 
+def residual_add(x: np.ndarray, out: np.ndarray, act: str) -> np.ndarray:
+    """A MoE layer on a residual branch, stacked: the next layer's input is the fp32 sum of the
+    layer input and the layer output as stored in the activation dtype, rounded once more to the
+    activation dtype (reading R23 of the replay stack: "the config-3 layer stacked 4 deep" says
+    nothing of what lies between the layers; a residual connection with no attention or norm is the
+    plainest reading)."""
+    s32 = np.asarray(x, np.float32) + to_act(out, act).astype(np.float32)   # one IEEE fp32 add
+    return to_act(s32, act)
+
+
 def route_or_replay(layer: OracleLayer, z: np.ndarray, replay: Optional[np.ndarray] = None,
                     record: Optional[np.ndarray] = None):
     if replay is not None:

@@ -143,6 +143,28 @@ def test_route_quant_equals_separate_calls(name, pow2):
     assert torch.equal(q1, q2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
 
 
+@pytest.mark.parametrize("T", [1, 5, 67])
+@pytest.mark.parametrize("H", [128, 384])
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_route_quant_ragged_equals_separate_calls(T, H, act, pow2):
+    """The fused launch's ragged ends (a last routing workgroup with fewer than 4 tokens, a last
+    quantisation workgroup with fewer blocks than it holds) give bitwise the separate calls."""
+    cfg = synth.CONFIGS["prefill"]
+    gcfg, _ = cfgs_for(cfg)
+    z = synth.make_logits(cfg, T=T, device=DEV, part=5)
+    x = synth.to_act(synth.randn((T, H), 23, synth.STAGE, part=78, device=DEV), act)
+    p1 = torch.full((cfg.k, T), -3, dtype=torch.int32, device=DEV)
+    p2 = p1.clone()
+    i1, w1 = M.moe_route(z, gcfg, record=p1)
+    q1, s1 = M.moe_quant_fp8_block(x, 1, pow2=pow2)
+    i2, w2, q2, s2 = M.moe_route_quant(z, gcfg, x, record=p2, pow2=pow2)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(w1.view(torch.int32), w2.view(torch.int32))
+    assert torch.equal(p1, p2)
+    assert torch.equal(q1, q2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+
+
 @pytest.mark.parametrize("name", NAMES)
 def test_replay(name):
     cfg = synth.CONFIGS[name]
@@ -228,6 +250,26 @@ def test_route_ties(name):
     oidx, ow = O.moe_route(host(z), ocfg)
     assert_equal("idx", host(idx), oidx)
     assert_equal("w", host(w), ow)
+
+
+@pytest.mark.parametrize("score,ng", [(0, 1), (1, 1), (1, 4)])
+def test_route_masked_experts(score, ng):
+    """-inf logits (masked experts), including tokens with fewer finite logits than k: indices
+    and weights bit for bit the oracle's (no placeholder index escapes)."""
+    from test_oracle_pins import masked_logits
+    T, E, k = 512, 64, 6
+    z = masked_logits(T, E, 22, [1, 2, 5, 6, 7, 40] if score == 0 else [0, 1, 2, 5, 6, 7, 40])
+    gcfg = M.router_cfg(E, k, score, True, ng, 2 if ng > 1 else 1, 2)
+    ocfg = O.router_cfg(E, k, score, True, ng, 2 if ng > 1 else 1, 2)
+    zd = torch.from_numpy(z).to(DEV)
+    idx, w = M.moe_route(zd, gcfg)
+    oidx, ow = O.moe_route(z, ocfg)
+    assert_equal("idx", host(idx), oidx)
+    assert_equal("w", host(w), ow)
+    x = synth.randn((T, 256), 22, synth.STAGE, part=77, device=DEV)
+    fidx, fw, _, _ = M.moe_route_quant(zd, gcfg, x)
+    assert_equal("fused idx", host(fidx), oidx)
+    assert_equal("fused w", host(fw), ow)
 
 
 @pytest.mark.parametrize("E,k,score,ng,tg,gt", [(1024, 64, 0, 1, 1, 2), (1024, 8, 1, 64, 7, 3), (96, 5, 1, 3, 2, 1),
@@ -676,3 +718,34 @@ def test_combine_pure_gather_is_exact():
     out = M.moe_combine(y, perm[:, None].contiguous().to(DEV), torch.ones((T, 1), device=DEV), None,
                         out_dtype=torch.float32)
     assert_equal("gather", host(out), host(y)[perm.numpy()])
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+@pytest.mark.parametrize("shared", [False, True])
+def test_combine_residual(act, shared):
+    """The combine on a residual branch: its layer output is bitwise moe_combine's, and
+    x_next = act(residual + output) bitwise the oracle's residual rule on those same values;
+    in place (x_next is the residual) gives the same bits."""
+    import oracle.layer as OL
+    cfg = synth.CONFIGS["prefill"]
+    T, k, E, H = 777, cfg.k, cfg.E, 384
+    idx = synth.routing_indices(cfg, T, seed_part=9).numpy()
+    idx[3, 2] = -1
+    _, offsets, dest, _ = O.moe_dispatch(idx, E, shared)
+    rows = int(offsets[-1])
+    dt = torch.bfloat16 if act == "bf16" else torch.float32
+    y = synth.randn((rows, H), 31, synth.STAGE, part=72, device=DEV).to(dt)
+    w = torch.rand((T, k), generator=torch.Generator().manual_seed(31), dtype=torch.float32).to(DEV)
+    res = synth.to_act(synth.randn((T, H), 31, synth.STAGE, part=73, device=DEV) * 4, act)
+    gdest = torch.from_numpy(dest).to(DEV)
+    goff = torch.from_numpy(offsets).to(DEV)
+    sh = goff[E:E + 1] if shared else None
+    ref_out = M.moe_combine(y, gdest, w, sh)
+    x_next, out = M.moe_combine_residual(y, gdest, w, sh, res, write_out=True)
+    iv = torch.int16 if act == "bf16" else torch.int32
+    assert torch.equal(out.view(iv), ref_out.view(iv))
+    want = OL.residual_add(host(res), host(ref_out), act)
+    assert_equal("x_next", host(x_next), want)
+    inplace = res.clone()
+    M.moe_combine_residual(y, gdest, w, sh, inplace, x_next=inplace)
+    assert torch.equal(inplace.view(iv), x_next.view(iv))

@@ -229,3 +229,38 @@ def test_router_backward_shift_invariance(name):
         mask = np.zeros_like(dz, bool)
         np.put_along_axis(mask, idx.astype(np.int64), True, axis=1)
         assert np.all(dz[~mask] == 0)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_small", "prefill_small"])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_wgrad_expert_equals_grouped_weight_gradients(name, pow2):
+    """The one-expert weight gradient (the reference of the full-size GPU weight-gradient tests)
+    equals the grouped backward's dW1[e], dW2[e] for every expert, the shared one included; an
+    expert that no token selected has zero gradients."""
+    cfg, lay, x = quantised_case(name, pow2)
+    fwd = L.forward_dispatch(lay, x)
+    dout = dout_for(cfg)
+    full = B.backward_dispatch(lay, fwd, x, dout)
+    for e in range(lay.groups):
+        if fwd["counts"][e] == 0:
+            assert not full["dW1"][e].any() and not full["dW2"][e].any()
+            continue
+        dW1, dW2 = B.wgrad_expert(lay, x, dout, e)
+        assert L.rel_err(dW1, full["dW1"][e]) < 1e-12, ("dW1", e)
+        assert L.rel_err(dW2, full["dW2"][e]) < 1e-12, ("dW2", e)
+
+
+def test_wgrad_expert_follows_replayed_routing():
+    cfg, lay, x = quantised_case("prefill_small")
+    payload = np.zeros((cfg.k, cfg.T), np.int32)
+    L.forward_dispatch(lay, x, record=payload)
+    # replay a rotated routing (every token's experts shifted by one), so the rows differ from routing
+    rot = np.ascontiguousarray((payload + 1) % cfg.E)
+    fwd = L.forward_dispatch(lay, x, replay=rot)
+    dout = dout_for(cfg)
+    full = B.backward_dispatch(lay, fwd, x, dout)
+    for e in sorted(set(int(v) for v in rot[:, :3].reshape(-1)))[:4]:
+        dW1, dW2 = B.wgrad_expert(lay, x, dout, e, replay=rot)
+        assert L.rel_err(dW1, full["dW1"][e]) < 1e-12 and L.rel_err(dW2, full["dW2"][e]) < 1e-12
+        d_routed = B.wgrad_expert(lay, x, dout, e)
+        assert L.rel_err(d_routed[1], full["dW2"][e]) > 1e-6

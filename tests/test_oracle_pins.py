@@ -210,6 +210,38 @@ def test_router_ties_go_to_lower_index_and_full_sort():
     assert np.array_equal(idx4, np.argsort(-z, axis=1, kind="stable")[:, :4])
 
 
+def masked_logits(T, E, seed, finite_per_token):
+    """Logits where each token keeps only a few finite entries and the rest are -inf (experts
+    masked out, e.g. by a -inf bias)."""
+    rng = np.random.default_rng(seed)
+    z = np.full((T, E), -np.inf, np.float32)
+    for t in range(T):
+        keep = rng.choice(E, size=finite_per_token[t % len(finite_per_token)], replace=False)
+        z[t, keep] = rng.standard_normal(len(keep)).astype(np.float32)
+    return z
+
+
+@pytest.mark.parametrize("score", [O.SOFTMAX, O.SIGMOID])
+def test_router_masked_experts_take_lowest_index(score):
+    """A token with fewer than k finite logits fills its remaining slots with the lowest-index
+    allowed experts of -inf logit (the same key order: -inf below every finite value, ties to the
+    lower index), never with an invalid index; checked against an exhaustive sort."""
+    T, E, k = 64, 32, 6
+    # a softmax over a token with no finite logit is undefined (its maximum is -inf), so softmax
+    # tokens keep at least one; sigmoid scores of -inf are fine (the exp input is clamped)
+    z = masked_logits(T, E, 21, [1, 3, 5, 6, 9] if score == O.SOFTMAX else [0, 1, 3, 5, 6, 9])
+    idx, w = O.moe_route(z, O.router_cfg(E, k, score, True))
+    for t in range(T):
+        ref = sorted(range(E), key=lambda e: (-float(z[t, e]), e))[:k]   # -(-inf) = inf sorts last
+        assert idx[t].tolist() == ref
+    assert np.all(idx >= 0) and np.all(idx < E) and np.all(np.isfinite(w))
+    # group-limited: the same rule inside the kept groups
+    cfg = O.router_cfg(E, 4, O.SIGMOID, True, n_group=4, topk_group=2, group_score_topk=2)
+    gidx, _ = O.moe_route(z, cfg)
+    assert np.all(gidx >= 0) and np.all(gidx < E)
+    assert all(len(set(r)) == 4 for r in gidx.tolist())
+
+
 def test_router_degenerate_cases():
     T, E = 64, 32
     z = synth.randn((T, E), 13, synth.STAGE, part=9).numpy()
