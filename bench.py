@@ -85,6 +85,8 @@ def parse():
                     help="time forward + backward of the layer (gradients of x, the gate and its bias)")
     ap.add_argument("--weight-grads", action="store_true",
                     help="with --backward: also the expert-weight gradients dW1, dW2 (fp32)")
+    ap.add_argument("--tile-rows", type=int, default=0,
+                    help="row-tile height of the expert GEMMs (0: chosen from the group sizes)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -241,9 +243,9 @@ def run_forward_workload(a, cfg, dev, steps, warmup, pow2=False, fp4=False, cpu=
     wbytes = weights.w1p.data.numel() + weights.w2p.data.numel()
     copies = a.copies if a.copies > 0 else max(2, math.ceil((2 << 30) / wbytes))
     act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
-    layers = [MoELayer(weights, cfg.T, act, dev)]
+    layers = [MoELayer(weights, cfg.T, act, dev, tile_rows=a.tile_rows)]
     for _ in range(1, copies):
-        layers.append(MoELayer(clone_weights(weights), cfg.T, act, dev))
+        layers.append(MoELayer(clone_weights(weights), cfg.T, act, dev, tile_rows=a.tile_rows))
     C, T = cfg.chunks, cfg.T
     if C > 1:
         x_all = torch.empty((C * T, cfg.H), dtype=act, device=dev)
@@ -401,7 +403,7 @@ def run_r3_stack(a, cfg, dev, steps, warmup):
         log(f"r3: building weights of layer {l} (W and W')")
         W.append(build_weights(cfg, dev, layer=l))
         Wp.append(build_weights(cfg, dev, layer=l, perturbed=True))
-    lay = MoELayer(W[0], T, act, dev)
+    lay = MoELayer(W[0], T, act, dev, tile_rows=a.tile_rows)
     payload = torch.full((Lyr, k, T), -1, dtype=torch.int32, device=dev)
     x0 = synth.make_x(cfg, dev)
     xbuf = {p: torch.empty_like(x0) for p in "ABC"}
@@ -900,7 +902,7 @@ def cpu_baseline(cfg, x, dev, pow2=False, fp4=False):
         sample = (f"whole batch ({cfg.T} tokens) x {passes} passes, dispatch path, expert weights "
                   "pre-quantised")
     else:
-        n = 12
+        n = 48                                # about 10-15 s of the oracle on 16 host threads
         toks = synth.sample_tokens(cfg.T, n, cfg.seed + 99)
         pre = L.forward_sampled(ol, xh[toks[:1]])   # warm the expert cache for token 0 only
         del pre

@@ -522,7 +522,8 @@ def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tens
     """a [max_rows,K] uint8, as_ [max_rows,K/128], offsets [G+1] (device), b [G,N,K] uint8 or a
     PackedWeight packed for this epilogue, bs [G,N/128,K/128].
     STORE -> out [max_rows,N] (bf16/fp32); SWIGLU_QUANT -> (h codes [max_rows,N/2] uint8, scales [max_rows,N/256]).
-    tile_rows: 32, 48, 64 or 128 rows per workgroup tile, 0 = chosen from the average group size.
+    tile_rows: 32, 48, 64, 128 or 256 (packed weights only) rows per workgroup tile, 0 = chosen from
+    the group sizes.
     plan: a plan from moe_grouped_gemm_plan for these offsets and max_rows (then no workspace is
     needed and tile_rows is the plan's).  pow2: every scale in as_ and bs is a power of two (the
     matrix cores apply them; the SwiGLU epilogue writes power-of-two scales for h).

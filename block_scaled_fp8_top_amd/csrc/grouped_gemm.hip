@@ -11,9 +11,12 @@
 // K loop costs MFMA time; the loop keeps only the promotion FMAs and scalar address arithmetic.)
 //
 // Workgroup tile: BM rows x BN = 256 (virtual) columns, 8 wavefronts.  Row-tile heights:
+//   BM = 256: waves in a 2 x 4 grid, each 128 x 64 (8 x 4 MFMA tiles), 2-stage LDS ring (64 KB per
+//             stage) - for groups of many hundreds of rows: per flop it moves half the global->LDS
+//             bytes of the 128-row tile and reads a quarter fewer LDS bytes, and the per-CU vector
+//             memory path, not the matrix cores, is what a narrower tile runs into;
 //   BM = 128: waves in a 2 x 4 grid, each 64 x 64 (4 x 4 MFMA tiles of 16 x 16), 3-stage LDS ring
-//             (48 KB per stage) - for groups of hundreds of rows, where the tile's operand bytes per
-//             flop decide the speed;
+//             (48 KB per stage) - for groups of a few hundred rows;
 //   BM = 32, 48, 64: waves in a 1 x 8 grid, each BM x 32 (BM/16 x 2 MFMA tiles), a 4-stage ring
 //             for 32 and 48 rows (36 / 38 KB per stage), 3 stages for 64 - for groups of a few
 //             dozen rows (decode), where the kernel streams the weights: a 128-row tile would spend
@@ -67,13 +70,23 @@ struct Tile {
   static constexpr int MS = BM_ / WM / 16;                   // 16 x 16 MFMA tiles per wave along M
   static constexpr int NS = BN / WN / 16;                    // ... along N
   static constexpr int A_BYTES = BM_ * BK, B_BYTES = FP4 ? BN * BK / 2 : BN * BK;   // FP4: two codes per byte
-  static constexpr int NSTAGE = 4 * (A_BYTES + B_BYTES) <= 155 * 1024 ? 4 : 3;   // ring within 160 KB of LDS
+  // ring within 160 KB of LDS
+  static constexpr int NSTAGE = 4 * (A_BYTES + B_BYTES) <= 155 * 1024 ? 4 : 3 * (A_BYTES + B_BYTES) <= 150 * 1024 ? 3 : 2;
+  // A fragments read AH 16-row blocks at a time (keeps a 128-row wave within its registers)
+  static constexpr int AH = MS > 4 ? MS / 4 : MS;
   static constexpr int A_INSTR = BM_ / 8;                    // 1 KB DMA instructions per A slice
-  static constexpr int A_PW = A_INSTR >= 8 ? A_INSTR / 8 : 1;
+  static constexpr int B_INSTR = B_BYTES / 1024;             // ... per B slice
+  // waves that issue the DMA: all 8.  (Leaving waves 0-3 free of DMA issue, so that each SIMD keeps
+  // one wave that never stalls on issuing global->LDS copies, measured slower: 5.28 against 5.18 ms
+  // for the prefill GEMM1 with 256-row tiles, 5.60 against 5.46 with 128-row tiles.)
+  static constexpr int DW = 8;
+  static constexpr int A_PW = A_INSTR >= DW ? A_INSTR / DW : 1;   // A instructions per DMA wave
+  static constexpr int B_PW = B_INSTR / DW;                        // B instructions per DMA wave
   static constexpr int S_INSTR = BM_ >= 64 ? BM_ / 64 : 1;   // 256-byte scale DMA instructions
   static constexpr int AS_W = BM_ >= 64 ? BM_ : 64;          // floats per scale-ring slot
   static_assert(WM * WN == 8 && MS >= 1 && NS >= 2 && NS % 2 == 0, "tile shape");
-  static_assert(A_INSTR % 8 == 0 || A_INSTR < 8, "A slice split");
+  static_assert(A_INSTR % DW == 0 || A_INSTR < DW, "A slice split");
+  static_assert(B_INSTR % DW == 0 && B_PW % 2 == 0 && S_INSTR <= DW, "B slice split");
 };
 
 // Global -> LDS DMA of 16 (or 4) bytes per lane: lane L's bytes land at lds_addr + 16 L (4 L).
@@ -235,7 +248,8 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   static_assert(!FP4 || (PACKED && POW2), "FP4 weights come packed, with power-of-two activation scales");
   using T = Tile<BM, FP4>;
   constexpr int WM = T::WM, WN = T::WN, MS = T::MS, NS = T::NS, HS = NS / 2, NSTAGE = T::NSTAGE;
-  constexpr int B_PW = FP4 ? 2 : 4;   // B DMA instructions per wave and step
+  constexpr int B_PW = T::B_PW;      // B DMA instructions per DMA wave and step
+  constexpr int BQ = PACKED ? (B_PW + 3) / 4 : B_PW;   // B offsets kept per DMA wave
   constexpr int A_BYTES = T::A_BYTES, B_BYTES = T::B_BYTES, AS_W = T::AS_W;
   constexpr int WROWS = MS * 16;   // rows per wave
   constexpr int D = NSTAGE - 1;    // DMA lookahead in K steps
@@ -265,22 +279,25 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   const int wm = wave / WN, wn = wave % WN;
   const size_t gstride = (PACKED ? (size_t)ny * BN : (size_t)N) * K / (FP4 ? 2 : 1);   // bytes of one group's weights
 
-  // ---- DMA roles.  A slice: wave w issues instructions w*A_PW + j (or just w, for slices of fewer
-  // than 8 instructions); B slice: instructions 4w .. 4w+3.  Row-major operands: instruction i
-  // holds rows 8i .. 8i+7, lane L row 8i + L/8 and chunk L%8 (stored at its swizzled slot); packed
-  // weights: lane L's 16 bytes sit at 1024 i + 16 L of the K step's block.
-  const bool has_a = T::A_INSTR >= 8 || wave < T::A_INSTR;
-  const int a_i0 = T::A_INSTR >= 8 ? wave * T::A_PW : wave;
+  // ---- DMA roles.  DMA wave d (wave 8 - DW + d) issues A instructions d*A_PW + j (or just d, for
+  // slices of fewer than DW instructions) and B instructions d*B_PW + j.  Row-major operands:
+  // instruction i holds rows 8i .. 8i+7, lane L row 8i + L/8 and chunk L%8 (stored at its swizzled
+  // slot); packed weights: lane L's 16 bytes sit at 1024 i + 16 L of the K step's block.
+  const bool dma_wave = wave >= 8 - T::DW;
+  const int dw = max(wave - (8 - T::DW), 0);
+  const bool has_a = dma_wave && (T::A_INSTR >= T::DW || dw < T::A_INSTR);
+  const int a_i0 = T::A_INSTR >= T::DW ? dw * T::A_PW : dw;
   const bool scale_loader = wave >= 8 - T::S_INSTR;   // the last S_INSTR waves bring 64 rows' scales each
   const int sidx = max(wave - (8 - T::S_INSTR), 0);
-  // wave 0 also brings the step's two weight scales (lane 0: low 128-column block, lane 1: high)
-  const bool bscale_loader = wave == 0;
-  const int per_stage = (has_a ? T::A_PW : 0) + B_PW + (scale_loader ? 1 : 0) + (bscale_loader ? 1 : 0);
+  // the first DMA wave also brings the step's two weight scales (lane 0: low 128-column block, lane 1: high)
+  const bool bscale_loader = wave == 8 - T::DW;
+  const int per_stage =
+      dma_wave ? (has_a ? T::A_PW : 0) + B_PW + (scale_loader ? 1 : 0) + (bscale_loader ? 1 : 0) : 0;
 
   // issue-side context of the unit whose steps are being issued: 32-bit byte offsets from a and
   // from the unit's group weights (both < 2^32 for every accepted shape); rows past the tile's end
   // read the tile's last row (any valid row would do)
-  uint32_t aoff[T::A_PW], boff[4];
+  uint32_t aoff[T::A_PW], boff[BQ];
   const uint8_t* bg = b;
   const float* ssrc = as;
   const float* bsrc = bs;   // this lane's weight-scale row (low block for lane != 1)
@@ -305,12 +322,13 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
       }                                                                                             \
       aoff[j_] = (uint32_t)src_ * (uint32_t)K + (((lane & 7) ^ swz_mask(r_)) << 4);                 \
     }                                                                                               \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                              \
+    _Pragma("unroll") for (int i_ = 0; i_ < BQ; ++i_) {                                             \
       if (PACKED) {                                                                                 \
+        /* one base per 4 instructions (the immediate offset reaches 4095) */                      \
         boff[i_] = (uint32_t)un_.nt * (uint32_t)(BN * K / (FP4 ? 2 : 1)) +                           \
-                   (uint32_t)((B_PW * wave + i_) * 1024 + lane * 16);                               \
+                   (uint32_t)((B_PW * dw + 4 * i_) * 1024 + lane * 16);                             \
       } else {                                                                                      \
-        const int r_ = (4 * wave + i_) * 8 + (lane >> 3);                                           \
+        const int r_ = (B_PW * dw + i_) * 8 + (lane >> 3);                                          \
         const int n_ = min(panel_row(EPI, un_.nt, r_, F), N - 1);                                   \
         boff[i_] = (uint32_t)n_ * (uint32_t)K + (((lane & 7) ^ swz_mask(r_)) << 4);                 \
       }                                                                                             \
@@ -325,7 +343,7 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
 
   // wave-uniform LDS destinations of this wave's DMA instructions, stage 0; stage s adds s * stride
   const uint32_t a_dst = lds_u32(&a_lds[0][a_i0 * 1024]);
-  const uint32_t b_dst = lds_u32(&b_lds[0][(B_PW * wave) * 1024]);
+  const uint32_t b_dst = lds_u32(&b_lds[0][(B_PW * dw) * 1024]);
   const uint32_t bsc4_dst = lds_u32(&bsc4_lds[0][0]);
   const uint32_t s_dst = lds_u32(&as_lds[0][sidx * 64]);
   const uint32_t bsc_dst = lds_u32(&bsc_lds[0][0]);
@@ -340,19 +358,20 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
         dma16s<0>(a + ko_, aoff[j_], ao_ + 1024 * j_);                                    \
     }                                                                                     \
     const uint32_t bo_ = b_dst + (uint32_t)(ST) * B_BYTES;                                \
-    if (FP4) {                                                                            \
-      dma16s<0>(bg + kob_, boff[0], bo_);                                                 \
-      dma16s<1024>(bg + kob_, boff[0], bo_);                                              \
-    } else if (PACKED) {                                                                  \
-      dma16s<0>(bg + kob_, boff[0], bo_);                                                 \
-      dma16s<1024>(bg + kob_, boff[0], bo_);                                              \
-      dma16s<2048>(bg + kob_, boff[0], bo_);                                              \
-      dma16s<3072>(bg + kob_, boff[0], bo_);                                              \
-    } else {                                                                              \
-      dma16s<0>(bg + kob_, boff[0], bo_);                                                 \
-      dma16s<0>(bg + kob_, boff[1], bo_ + 1024);                                          \
-      dma16s<0>(bg + kob_, boff[2], bo_ + 2048);                                          \
-      dma16s<0>(bg + kob_, boff[3], bo_ + 3072);                                          \
+    if (dma_wave) {                                                                       \
+      if (PACKED) {                                                                       \
+        _Pragma("unroll") for (int q_ = 0; q_ < BQ; ++q_) {                                \
+          dma16s<0>(bg + kob_, boff[q_], bo_ + 4096 * q_);                                \
+          dma16s<1024>(bg + kob_, boff[q_], bo_ + 4096 * q_);                             \
+          if (B_PW - 4 * q_ > 2) {                                                        \
+            dma16s<2048>(bg + kob_, boff[q_], bo_ + 4096 * q_);                           \
+            dma16s<3072>(bg + kob_, boff[q_], bo_ + 4096 * q_);                           \
+          }                                                                               \
+        }                                                                                 \
+      } else {                                                                            \
+        _Pragma("unroll") for (int q_ = 0; q_ < B_PW; ++q_)                                \
+          dma16s<0>(bg + kob_, boff[q_], bo_ + 1024 * q_);                                \
+      }                                                                                   \
     }                                                                                     \
     if (scale_loader) dma4(ssrc + ik, s_dst + (uint32_t)((SV) & 3) * AS_W * 4);           \
     if (FP4) {                                                                            \
@@ -391,16 +410,20 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   // the 16-byte chunks 2c, 2c + 1.  An FP4 operand holds K 32c .. 32c + 31 in lane group c while an
   // FP8 operand holds K 16c .. 16c + 15 in its low and 64 + 16c .. 64 + 16c + 15 in its high 16
   // bytes, so against FP4 weights the activation fragment takes chunks c and 4 + c.
-  intx8 af[MS], bf[NS];
+  intx8 af[T::AH], bf[NS];
   const int a_c0 = FP4 ? (lane >> 4) : (lane >> 4) * 2, a_c1 = FP4 ? 4 + (lane >> 4) : (lane >> 4) * 2 + 1;
-#define GEMM_READ(ST)                                                                                   \
+  // A fragments of 16-row blocks MS0 .. MS0 + AH - 1 (of this wave's rows) from LDS stage ST
+#define GEMM_READ_A(ST, MS0)                                                                            \
   do {                                                                                                  \
-    _Pragma("unroll") for (int ms = 0; ms < MS; ++ms) {                                                 \
-      const int r_ = wm * WROWS + ms * 16 + lr;                                                         \
+    _Pragma("unroll") for (int ms = 0; ms < T::AH; ++ms) {                                              \
+      const int r_ = wm * WROWS + ((MS0) + ms) * 16 + lr;                                               \
       const intx4 lo_ = *reinterpret_cast<const intx4*>(&a_lds[ST][swz(r_, a_c0)]);                     \
       const intx4 hi_ = *reinterpret_cast<const intx4*>(&a_lds[ST][swz(r_, a_c1)]);                     \
       af[ms] = intx8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};                   \
     }                                                                                                   \
+  } while (0)
+#define GEMM_READ_B(ST)                                                                                 \
+  do {                                                                                                  \
     _Pragma("unroll") for (int ns = 0; ns < NS; ++ns) {                                                 \
       /* packed weights: operand order; row-major weights: swizzled rows; FP4: one 1 KB */              \
       /* block per 16 rows, lane l's 16 bytes at 16 l */                                                \
@@ -444,51 +467,86 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
       const int ist = st == 0 ? NSTAGE - 1 : st - 1;   // (s + D) % NSTAGE: the stage read last step
       GEMM_ISSUE(s + D, ist);
     }
-    const bool wave_active = EPI == 1 ? true : (cu.nt * BN + wn * NS * 16 < N);
+    // a wave whose rows all lie past the unit's last row (a group's short last tile) or whose
+    // columns lie past N does no fragment reads and no MFMAs
+    const bool wave_active =
+        (EPI == 1 ? true : (cu.nt * BN + wn * NS * 16 < N)) && wm * WROWS < cu.row_end - cu.row0;
     if (wave_active) {
-      GEMM_READ(st);
+      GEMM_READ_B(st);
       const float* srow = &as_lds[s & 3][wm * WROWS + lr];
       // weight scales of this step: SwiGLU gate columns use the low block and up columns the high
       // one; a STORE wave's 16*NS columns lie in block (wn * NS * 16) / 128 of the panel
       const float sb_lo = bsc_lds[s & 3][EPI == 1 ? 0 : (wn * NS * 16) / 128];
       const float sb_hi = bsc_lds[s & 3][1];
-      if (POW2) {
-        // power-of-two scales: the matrix cores apply them (E8M0 exponents; each lane gives the
-        // scale of its operand row for its 32-wide K piece, here the same for the whole 128-wide
-        // step) and accumulate straight into acc - no promotion
-        const uint32_t eb_lo = e8m0_code(sb_lo), eb_hi = e8m0_code(sb_hi);
-        // FP4 weights: each lane's operand row has its own scale per 32-wide K chunk (lane / 16)
-        uint32_t eb4[NS];
+      // FP4 weights: each lane's operand row has its own scale per 32-wide K chunk (lane / 16)
+      uint32_t eb4[NS];
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns)
-          eb4[ns] = FP4 ? (uint32_t)bsc4_lds[s & 3][(b_lrow[ns] + lr) * 4 + (lane >> 4)] : 0u;
+      for (int ns = 0; ns < NS; ++ns)
+        eb4[ns] = FP4 ? (uint32_t)bsc4_lds[s & 3][(b_lrow[ns] + lr) * 4 + (lane >> 4)] : 0u;
 #pragma unroll
-        for (int ms = 0; ms < MS; ++ms) {
-          const uint32_t ea = e8m0_code(srow[ms * 16]);
+      for (int h = 0; h < MS / T::AH; ++h) {
+        GEMM_READ_A(st, h * T::AH);
+        if (POW2) {
+          // power-of-two scales: the matrix cores apply them (E8M0 exponents; each lane gives the
+          // scale of its operand row for its 32-wide K piece, here the same for the whole 128-wide
+          // step) and accumulate straight into acc - no promotion
+          const uint32_t eb_lo = e8m0_code(sb_lo), eb_hi = e8m0_code(sb_hi);
 #pragma unroll
-          for (int ns = 0; ns < NS; ++ns)
-            acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                bf[ns], af[ms], acc[ms][ns], FP4 ? 4 : 0, 0, 0,
-                FP4 ? eb4[ns] : ((EPI == 1 && ns >= HS) ? eb_hi : eb_lo), 0, ea);
-        }
-      } else {
-        floatx4 p[MS][NS];
+          for (int ms = 0; ms < T::AH; ++ms) {
+            const int m = h * T::AH + ms;
+            const uint32_t ea = e8m0_code(srow[m * 16]);
 #pragma unroll
-        for (int ms = 0; ms < MS; ++ms)
+            for (int ns = 0; ns < NS; ++ns)
+              acc[m][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  bf[ns], af[ms], acc[m][ns], FP4 ? 4 : 0, 0, 0,
+                  FP4 ? eb4[ns] : ((EPI == 1 && ns >= HS) ? eb_hi : eb_lo), 0, ea);
+          }
+        } else if (T::AH == MS) {
+          // every fresh partial of the step first, then the promotion
+          floatx4 p[T::AH][NS];
 #pragma unroll
-          for (int ns = 0; ns < NS; ++ns)
-            p[ms][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[ns], af[ms], floatx4{0.f, 0.f, 0.f, 0.f},
-                                                                         0, 0, 0, 0, 0, 0);
+          for (int ms = 0; ms < T::AH; ++ms)
 #pragma unroll
-        for (int ms = 0; ms < MS; ++ms) {
-          const float sa = srow[ms * 16];
-          const float c_lo = sa * sb_lo, c_hi = EPI == 1 ? sa * sb_hi : c_lo;
+            for (int ns = 0; ns < NS; ++ns)
+              p[ms][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[ns], af[ms],
+                                                                           floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0,
+                                                                           0, 0);
 #pragma unroll
-          for (int ns = 0; ns < NS; ++ns) {
-            const bool hi = EPI == 1 && ns >= HS;
+          for (int ms = 0; ms < T::AH; ++ms) {
+            const float sa = srow[ms * 16];
+            const float c_lo = sa * sb_lo, c_hi = EPI == 1 ? sa * sb_hi : c_lo;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[ms][ns][i] = __builtin_fmaf(p[ms][ns][i], hi ? c_hi : c_lo, acc[ms][ns][i]);
+            for (int ns = 0; ns < NS; ++ns) {
+              const bool hi = EPI == 1 && ns >= HS;
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                acc[ms][ns][i] = __builtin_fmaf(p[ms][ns][i], hi ? c_hi : c_lo, acc[ms][ns][i]);
+            }
+          }
+        } else {
+          // tall wave tile: fresh partials of two 16-row blocks at a time, block ms's MFMAs
+          // running while block ms - 1 is promoted (register budget)
+          floatx4 p[2][NS];
+#pragma unroll
+          for (int ms = 0; ms <= T::AH; ++ms) {
+            if (ms < T::AH) {
+#pragma unroll
+              for (int ns = 0; ns < NS; ++ns)
+                p[ms & 1][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    bf[ns], af[ms], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+            }
+            if (ms > 0) {
+              const int m = h * T::AH + ms - 1;
+              const float sa = srow[m * 16];
+              const float c_lo = sa * sb_lo, c_hi = EPI == 1 ? sa * sb_hi : c_lo;
+#pragma unroll
+              for (int ns = 0; ns < NS; ++ns) {
+                const bool hi = EPI == 1 && ns >= HS;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  acc[m][ns][i] = __builtin_fmaf(p[(ms - 1) & 1][ns][i], hi ? c_hi : c_lo, acc[m][ns][i]);
+              }
+            }
           }
         }
       }
@@ -549,8 +607,8 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
             __builtin_amdgcn_raw_buffer_store_b128(v, rg, ((wm * WROWS + ms * 16 + tr) * N + col) * 4, 0, 0);
           }
       }
-      // h for this lane: rows (ms, i), columns wn*HS*16 + hs*16 + lr (hs < HS) of the 128-wide block
-      float h[MS][HS][4];
+      // h for this lane, formed in place in acc[ms][hs < HS]: rows (ms, i), columns
+      // wn*HS*16 + hs*16 + tc + i of the 128-wide block
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms) {
         float mx = 0.0f;
@@ -560,7 +618,7 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
           for (int hs = 0; hs < HS; ++hs) {
             const float gt = acc[ms][hs][i], up = acc[ms][hs + HS][i];
             const float v = (gt * up) / (1.0f + __expf(-gt));
-            h[ms][hs][i] = v;
+            acc[ms][hs][i] = v;
             mx = fmaxf(mx, fabsf(v));
           }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -587,8 +645,8 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
         const int row = wm * WROWS + lrow;
 #pragma unroll
         for (int hs = 0; hs < HS; ++hs) {
-          float v[4] = {h[ms][hs][0], h[ms][hs][1], h[ms][hs][2], h[ms][hs][3]};
-          const uint32_t codes = e4m3_pack4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
+          const uint32_t codes = e4m3_pack4(acc[ms][hs][0] / sc, acc[ms][hs][1] / sc, acc[ms][hs][2] / sc,
+                                            acc[ms][hs][3] / sc);
           __builtin_amdgcn_raw_buffer_store_b32(codes, rq, row * F + f0 + hs * 16, 0, 0);
         }
         // the row's scale: one lane per row (column group 0) of wave column 0; other lanes aim past
@@ -606,7 +664,8 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     ck = 0;
     if (++ci < nunits) cu = unit_at(me + ci * G, ny, tiles, offsets, BM);
   }
-#undef GEMM_READ
+#undef GEMM_READ_A
+#undef GEMM_READ_B
 #undef GEMM_ISSUE
 #undef GEMM_ISSUE_CTX
 }
@@ -616,10 +675,13 @@ int64_t max_tiles_for(int64_t max_rows, int groups, int bm) { return ceil_div64(
 // Row-tile height when the caller leaves it open: the smallest height that holds twice the
 // average group, so that few groups need a second tile (which streams the same weight panel
 // again); short groups then stream weights through 32- or 64-row tiles, long ones use 128.
+// Groups averaging more than 256 rows take 256-row tiles (per flop, half the global->LDS bytes of
+// a 128-row tile; measured on the prefill layer: GEMM1 5.46 -> 5.18 ms, GEMM2 2.99 -> 2.73 ms).
 int auto_tile_rows(int64_t max_rows, int groups) {
   const int64_t avg2 = 2 * ceil_div64(max_rows, groups);
-  return avg2 <= 32 ? 32 : avg2 <= 48 ? 48 : avg2 <= 64 ? 64 : 128;
+  return avg2 <= 32 ? 32 : avg2 <= 48 ? 48 : avg2 <= 64 ? 64 : avg2 <= 512 ? 128 : 256;
 }
+bool valid_tile_rows(int bm) { return bm == 32 || bm == 48 || bm == 64 || bm == 128 || bm == 256; }
 
 template <int BM, bool PACKED, bool POW2, bool FP4 = false>
 void launch3(unsigned grid, hipStream_t st, int epilogue, int out_dtype, const uint8_t* a, const int32_t* a_rows,
@@ -645,21 +707,34 @@ void launch(unsigned grid, hipStream_t st, int b_layout, int epilogue, int scale
             const uint8_t* a, const int32_t* a_rows, int a_count, const float* as, const int32_t* offsets, const int4* tiles, const int32_t* ntiles,
             int ny, const uint8_t* b, const float* bs, int N, int K, void* out, float* out_scales, float* g_out) {
   const bool p2 = scale_mode == MOE_SCALE_POW2;
-  if (b_layout == MOE_B_PACKED_FP4)
-    launch3<BM, true, true, true>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                                  out_scales, g_out);
-  else if (b_layout == MOE_B_PACKED && p2)
-    launch3<BM, true, true>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                            out_scales, g_out);
-  else if (b_layout == MOE_B_PACKED)
-    launch3<BM, true, false>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                             out_scales, g_out);
-  else if (p2)
-    launch3<BM, false, true>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                             out_scales, g_out);
-  else
-    launch3<BM, false, false>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
-                              out_scales, g_out);
+  if constexpr (BM == 256) {
+    // 256-row tiles stream packed weights only (the host rejects row-major weights for them)
+    if (b_layout == MOE_B_PACKED_FP4)
+      launch3<BM, true, true, true>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs,
+                                    N, K, out, out_scales, g_out);
+    else if (p2)
+      launch3<BM, true, true>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K,
+                              out, out_scales, g_out);
+    else
+      launch3<BM, true, false>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N,
+                               K, out, out_scales, g_out);
+  } else {
+    if (b_layout == MOE_B_PACKED_FP4)
+      launch3<BM, true, true, true>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs,
+                                    N, K, out, out_scales, g_out);
+    else if (b_layout == MOE_B_PACKED && p2)
+      launch3<BM, true, true>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K,
+                              out, out_scales, g_out);
+    else if (b_layout == MOE_B_PACKED)
+      launch3<BM, true, false>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N,
+                               K, out, out_scales, g_out);
+    else if (p2)
+      launch3<BM, false, true>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N,
+                               K, out, out_scales, g_out);
+    else
+      launch3<BM, false, false>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N,
+                                K, out, out_scales, g_out);
+  }
 }
 
 // compute units of the current device, queried once per device (atomics: calls may come from
@@ -743,7 +818,7 @@ int moe_plan_host(int32_t groups, int64_t max_rows, int32_t tile_rows, void* wor
                   moe_gemm_plan* plan, int64_t* max_tiles) {
   if (!plan) return MOE_ERR_NULL;
   if (groups < 1 || groups > 4096 || max_rows < 0 || max_rows > INT32_MAX - 256) return MOE_ERR_SHAPE;
-  if (tile_rows != 0 && tile_rows != 32 && tile_rows != 48 && tile_rows != 64 && tile_rows != 128) return MOE_ERR_ARG;
+  if (tile_rows != 0 && !valid_tile_rows(tile_rows)) return MOE_ERR_ARG;
   const int bm = tile_rows != 0 ? tile_rows : auto_tile_rows(max_rows, groups);
   plan->tile_rows = bm;
   plan->groups = groups;
@@ -782,7 +857,8 @@ int run_planned(const moe_gemm_plan* plan, const uint8_t* a, const int32_t* a_ro
   const int bm = plan->tile_rows;
   int rc = check_gemm_args(max_rows, groups, N, K, epilogue, scale_mode, out_dtype, b_layout);
   if (rc != MOE_OK) return rc;
-  if (bm != 32 && bm != 48 && bm != 64 && bm != 128) return MOE_ERR_ARG;
+  if (!valid_tile_rows(bm)) return MOE_ERR_ARG;
+  if (bm == 256 && b_layout == MOE_B_ROWMAJOR) return MOE_ERR_ARG;   // 256-row tiles need packed weights
   if (max_rows == 0) return MOE_OK;
   // gathered rows: a holds a_count rows; every byte offset into it must fit 32 bits like a's own
   if (a_rows && (a_count < 1 || (a_count + 1) * (int64_t)K >= ((int64_t)1 << 32))) return MOE_ERR_SHAPE;
@@ -809,8 +885,11 @@ int run_planned(const moe_gemm_plan* plan, const uint8_t* a, const int32_t* a_ro
   else if (bm == 64)
     launch<64>(grid, st, b_layout, epilogue, scale_mode, out_dtype, a, a_rows, (int)a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out,
                out_scales, g_out);
-  else
+  else if (bm == 128)
     launch<128>(grid, st, b_layout, epilogue, scale_mode, out_dtype, a, a_rows, (int)a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K,
+                out, out_scales, g_out);
+  else
+    launch<256>(grid, st, b_layout, epilogue, scale_mode, out_dtype, a, a_rows, (int)a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K,
                 out, out_scales, g_out);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
@@ -853,12 +932,15 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int
                                     void* stream) {
   int rc = check_gemm_args(max_rows, groups, N, K, epilogue, scale_mode, out_dtype, b_layout);
   if (rc != MOE_OK) return rc;
-  if (tile_rows != 0 && tile_rows != 32 && tile_rows != 48 && tile_rows != 64 && tile_rows != 128) return MOE_ERR_ARG;
+  if (tile_rows != 0 && !valid_tile_rows(tile_rows)) return MOE_ERR_ARG;
+  if (tile_rows == 256 && b_layout == MOE_B_ROWMAJOR) return MOE_ERR_ARG;
   if (max_rows == 0) return MOE_OK;
   if (!a || !as || !offsets || !b || !bs || !out) return MOE_ERR_NULL;
   if (epilogue == MOE_EPI_SWIGLU_QUANT && !out_scales) return MOE_ERR_NULL;
   if (!workspace || workspace_bytes < moe_gemm_workspace(max_rows, groups)) return MOE_ERR_WORKSPACE;
   if (compute_units() <= 0) return MOE_ERR_HIP;
+  // the automatic height never picks 256-row tiles for row-major weights (packed weights only)
+  if (tile_rows == 0 && b_layout == MOE_B_ROWMAJOR) tile_rows = std::min(auto_tile_rows(max_rows, groups), 128);
   moe_gemm_plan plan;
   rc = moe_grouped_gemm_plan(offsets, groups, max_rows, tile_rows, workspace, workspace_bytes, &plan, stream);
   if (rc != MOE_OK) return rc;

@@ -145,10 +145,11 @@ class MoELayer:
     """Preallocated buffers for up to ``T_max`` tokens; ``forward`` returns a view of the output."""
 
     def __init__(self, weights: MoELayerWeights, T_max: int, act_dtype=torch.bfloat16, device="cuda",
-                 gather_rows: bool = True):
+                 gather_rows: bool = True, tile_rows: int = 0):
         """gather_rows: GEMM1 reads each group row's codes straight from the token-order xq through
         the dispatch's src_token (only the scales are permuted); False: the dispatch also writes the
-        permuted codes (disp.aq) and GEMM1 reads those.  Both give bitwise the same results."""
+        permuted codes (disp.aq) and GEMM1 reads those.  Both give bitwise the same results.
+        tile_rows: row-tile height of the expert GEMMs (0: chosen from the group sizes)."""
         if weights.fp4 and not weights.pow2:
             raise ValueError("FP4 expert weights need power-of-two activation scales (pow2=True)")
         self.w = weights
@@ -183,6 +184,7 @@ class MoELayer:
         self.logits_valid = False   # the last forward wrote self.logits (not the fused sigmoid replay)
         self.device = d
         self.gather_rows = gather_rows
+        self.tile_rows = tile_rows
         self.bwd = None    # backward buffers, allocated by the first backward (or training forward)
         self.g_saved = False   # the last forward kept GEMM1's output in self.bwd["g"]
 
@@ -242,7 +244,7 @@ class MoELayer:
         # dispatch, and one tile plan for both expert GEMMs (same groups), living in the GEMM workspace
         # (for decode-sized batches the dispatch workgroup writes it)
         plan = self.plan = M.moe_dispatch_plan(self.idx, w.E, w.shared, self.xq, self.xs, self.workspace, self.disp,
-                                               self.gemm_ws, stream=stream)
+                                               self.gemm_ws, tile_rows=self.tile_rows, stream=stream)
         mark(3)
         M.moe_grouped_gemm_fp8(*self._gemm1_a(), self.disp.offsets, w.w1p or w.w1q, w.w1s,
                                epilogue=M.MOE_EPI_SWIGLU_QUANT, out=self.hq, out_scales=self.hs, plan=plan,

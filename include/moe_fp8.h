@@ -229,7 +229,9 @@ size_t moe_packed_weight_bytes(int32_t groups, int32_t N, int32_t K, int32_t epi
  *            writes them in that mode: the matrix cores apply them as E8M0 exponents and accumulate
  *            directly; only the exponent field of each scale is read; the SwiGLU epilogue then
  *            quantises h with power-of-two scales too)
- *   tile_rows: rows per workgroup tile, 32, 48, 64 or 128, or 0 to choose from the average group size
+ *   tile_rows: rows per workgroup tile, 32, 48, 64, 128 or 256 (256: packed weights only), or 0 to
+ *              choose from the group sizes (256 when groups average more than 256 rows and the
+ *              weights are packed)
  *            (the smallest height >= 2 * ceil(max_rows / groups)).  The result is the same for every
  *            height.
  *   Rows beyond offsets[groups] are not written.  workspace >= moe_workspace_bytes(MOE_OP_GROUPED_GEMM,
@@ -250,7 +252,9 @@ int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int32_t* offse
  * holding the plan until the last GEMM that uses it has run) and fills `plan` (host) with the tile
  * height (tile_rows as in moe_grouped_gemm_fp8) and the sizes.  moe_grouped_gemm_fp8_planned then
  * computes exactly what moe_grouped_gemm_fp8 computes, for the groups, max_rows and tile height of
- * the plan, with the same `offsets` contents.
+ * the plan, with the same `offsets` contents.  A plan of 256-row tiles (chosen, or automatic for
+ * groups averaging more than 256 rows) serves packed weights only: a planned call with row-major
+ * weights on it returns MOE_ERR_ARG.
  * Errors: as moe_grouped_gemm_fp8 (MOE_ERR_NULL also for a NULL plan). */
 typedef struct moe_gemm_plan {
   int32_t tile_rows;   /* chosen row-tile height */

@@ -125,7 +125,8 @@ def test_gemm_validation(L):
     assert L.moe_grouped_gemm_fp8(*g(epi=7)) == ARG
     assert L.moe_grouped_gemm_fp8(*g(groups=0)) == SHAPE
     assert L.moe_grouped_gemm_fp8(*g(wsb=8)) == WS
-    assert L.moe_grouped_gemm_fp8(*g(tr=40)) == ARG                   # tile height not 32, 48, 64 or 128
+    assert L.moe_grouped_gemm_fp8(*g(tr=40)) == ARG                   # tile height not 32, 48, 64, 128 or 256
+    assert L.moe_grouped_gemm_fp8(*g(tr=256, bl=0)) == ARG            # 256-row tiles need packed weights
     assert L.moe_grouped_gemm_fp8(*g(rows=1 << 20, K=4096)) == SHAPE   # 2^32 bytes of activations
     assert L.moe_grouped_gemm_fp8(*g(N=1 << 17, K=1 << 15)) == SHAPE   # 2^32 bytes of one group's weights
     assert L.moe_grouped_gemm_fp8(*g(bl=3)) == ARG                    # unknown weight layout
@@ -156,8 +157,9 @@ def test_gemm_plan_validation(L):
     assert L.moe_grouped_gemm_plan(P, 4, 100, 0, P, 1 << 20, None, None) == NULL
     assert L.moe_grouped_gemm_plan(P, 4, 0, 0, None, 0, ctypes.byref(plan), None) == OK          # nothing to plan
     assert plan.tile_rows == 32 and plan.groups == 4 and plan.max_rows == 0
-    # automatic tile height: the smallest of 32/48/64/128 holding twice the average group
-    for rows, groups, tr in ((100, 8, 32), (1536, 64, 48), (2000, 64, 64), (147456, 257, 128)):
+    # automatic tile height: the smallest of 32/48/64/128 holding twice the average group, 256 for
+    # groups averaging more than 256 rows
+    for rows, groups, tr in ((100, 8, 32), (1536, 64, 48), (2000, 64, 64), (65536, 256, 128), (147456, 257, 256)):
         L.moe_grouped_gemm_plan(P, groups, rows, 0, None, 0, ctypes.byref(plan), None)
         assert plan.tile_rows == tr, (rows, groups, plan.tile_rows)
     planned = lambda N=256, K=256, epi=0, od=1, bl=0, pl=True, sm=0: (
@@ -169,6 +171,8 @@ def test_gemm_plan_validation(L):
     assert L.moe_grouped_gemm_fp8_planned(*planned(bl=3)) == ARG
     assert L.moe_grouped_gemm_fp8_planned(*planned(sm=5)) == ARG
     assert L.moe_grouped_gemm_fp8_planned(*planned(epi=1, od=2)) == NULL   # out_scales missing
+    plan.tile_rows = 256
+    assert L.moe_grouped_gemm_fp8_planned(*planned(bl=0)) == ARG           # 256-row plan, row-major weights
     plan.tile_rows = 40
     assert L.moe_grouped_gemm_fp8_planned(*planned()) == ARG
 

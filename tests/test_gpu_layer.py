@@ -114,6 +114,31 @@ def test_layer_deterministic_and_chunk_concatenation():
     assert torch.equal(torch.cat([a0, a1]).view(torch.int16), both.view(torch.int16))
 
 
+@pytest.mark.parametrize("name", ["prefill", "longctx"])
+def test_layer_tile_heights_bitwise(name):
+    """The expert GEMMs at 128- and 256-row tiles: the accumulation order of every output does not
+    depend on the tile height, so the layer forward (h codes, expert rows, output) is bitwise the
+    same, including groups whose last tile has a wave row of padding only."""
+    cfg = synth.CONFIGS[name]
+    gw = gpu_weights(cfg)
+    x = synth.make_x(cfg, DEV, chunk=3)
+    res = {}
+    for tile in (128, 256):
+        lay = MoELayer(gw, cfg.T, _act(cfg), tile_rows=tile)
+        out = lay.forward(x).clone()
+        assert lay.plan.tile_rows == tile
+        res[tile] = (out, lay.hq.clone(), lay.hs.clone(), lay.y.clone())
+        del lay
+    torch.cuda.synchronize()
+    n = cfg.rows
+    (o1, h1, s1, y1), (o2, h2, s2, y2) = res[128], res[256]
+    assert torch.equal(h1[:n], h2[:n]) and torch.equal(s1[:n].view(torch.int32), s2[:n].view(torch.int32))
+    assert torch.equal(y1[:n].view(torch.int16), y2[:n].view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    del res, gw
+    _free()
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill"])
 def test_layer_gathered_rows_equal_permuted_copy(name):
     """GEMM1 reading its rows from xq through src_token gives bitwise the forward (and, for the

@@ -18,7 +18,12 @@ from gpu_helpers import DEV, TOL, assert_equal, cfgs_for, host, rel_err, rows_ho
 
 pytestmark = pytest.mark.gpu
 NAMES = ["tiny", "decode", "prefill", "longctx", "r3"]
-TILES = [32, 48, 64, 128]   # every row-tile height of the grouped GEMM, whichever the shape would pick
+TILES = [32, 48, 64, 128, 256]   # every row-tile height of the grouped GEMM, whichever the shape would pick
+
+
+def _weights_for(b, epi, tile):
+    """256-row tiles stream packed weights only; other heights take the row-major codes."""
+    return M.moe_pack_weights_fp8(b, epi) if tile == 256 else b
 
 
 def _cleanup():
@@ -459,8 +464,9 @@ def test_grouped_gemm_store(name, which, tile):
     cfg = synth.CONFIGS[name]
     offsets, a, as_, b, bs, N, K = _gemm_case(cfg, which, 0 if which == "w1" else 5)
     goff = torch.from_numpy(offsets).to(DEV)
-    y32 = M.moe_grouped_gemm_fp8(a, as_, goff, b, bs, M.MOE_EPI_STORE, torch.float32, tile_rows=tile)
-    ybf = M.moe_grouped_gemm_fp8(a, as_, goff, b, bs, M.MOE_EPI_STORE, torch.bfloat16, tile_rows=tile)
+    bw = _weights_for(b, M.MOE_EPI_STORE, tile)
+    y32 = M.moe_grouped_gemm_fp8(a, as_, goff, bw, bs, M.MOE_EPI_STORE, torch.float32, tile_rows=tile)
+    ybf = M.moe_grouped_gemm_fp8(a, as_, goff, bw, bs, M.MOE_EPI_STORE, torch.bfloat16, tile_rows=tile)
     rows = _sample_rows(offsets, 24, cfg.seed)
     ref, _ = _oracle_rows(a, as_, offsets, b, bs, rows)
     e32 = rel_err(rows_host(y32, rows), ref)
@@ -487,6 +493,8 @@ def test_grouped_gemm_exact_integers():
         goff = torch.from_numpy(offsets.astype(np.int32)).to(DEV)
         ref = O.moe_grouped_gemm_fp8(host(a), host(as_), offsets, host(b), host(bs))
         for bw in (b, M.moe_pack_weights_fp8(b, M.MOE_EPI_STORE)):   # N = 384: a zero-padded packed panel
+            if tile == 256 and isinstance(bw, torch.Tensor):
+                continue                                              # 256-row tiles: packed weights only
             y = M.moe_grouped_gemm_fp8(a, as_, goff, bw, bs, M.MOE_EPI_STORE, torch.float32, tile_rows=tile)
             assert_equal(f"exact integer GEMM (scales {sa},{sb}, tile {tile}, {type(bw).__name__})", host(y),
                          ref.astype(np.float32))
@@ -534,7 +542,10 @@ def test_grouped_gemm_packed_equals_rowmajor(name, tile):
         offsets, a, as_, b, bs, N, K = _gemm_case(cfg, which, 11)
         goff = torch.from_numpy(offsets).to(DEV)
         pw = M.moe_pack_weights_fp8(b, epi)
-        r0 = M.moe_grouped_gemm_fp8(a, as_, goff, b, bs, epi, torch.float32, tile_rows=tile)
+        # 256-row tiles take packed weights only: their result is compared with the row-major
+        # weights at 128-row tiles (the accumulation order of an output does not depend on the
+        # tile height, so the two are bitwise equal)
+        r0 = M.moe_grouped_gemm_fp8(a, as_, goff, b, bs, epi, torch.float32, tile_rows=128 if tile == 256 else tile)
         r1 = M.moe_grouped_gemm_fp8(a, as_, goff, pw, bs, epi, torch.float32, tile_rows=tile)
         rows = int(offsets[-1])
         if epi == M.MOE_EPI_STORE:
@@ -574,7 +585,7 @@ def test_grouped_gemm_gathered_rows_clamped():
     assert_equal("clamped rows", host(got), host(ref))
 
 
-@pytest.mark.parametrize("tile", [32, 48, 64, 128])
+@pytest.mark.parametrize("tile", [32, 48, 64, 128, 256])
 @pytest.mark.parametrize("pow2", [False, True])
 def test_grouped_gemm_gathered_rows(tile, pow2):
     """A rows gathered from a token-order matrix through a row-id list (repeats, any order) give
@@ -649,7 +660,8 @@ def test_grouped_gemm_swiglu_quant(name, tile):
     offsets, a, as_, b, bs, N, K = _gemm_case(cfg, "w1", 9)
     F = N // 2
     goff = torch.from_numpy(offsets).to(DEV)
-    hq, hs = M.moe_grouped_gemm_fp8(a, as_, goff, b, bs, M.MOE_EPI_SWIGLU_QUANT, tile_rows=tile)
+    hq, hs = M.moe_grouped_gemm_fp8(a, as_, goff, _weights_for(b, M.MOE_EPI_SWIGLU_QUANT, tile), bs,
+                                    M.MOE_EPI_SWIGLU_QUANT, tile_rows=tile)
     rows = _sample_rows(offsets, 16, cfg.seed + 1)
     g1, _ = _oracle_rows(a, as_, offsets, b, bs, rows)
     h = O.swiglu(g1, F)
