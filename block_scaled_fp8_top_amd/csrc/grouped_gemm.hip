@@ -218,7 +218,13 @@ __device__ __forceinline__ void wait_vm(int n) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// Where unit u (a tile-row block x panel pair, in logical order) sits: group, rows, panel.
+// Where unit u (a tile-row block x panel pair, in logical order) sits: group, rows, panel.  A group's
+// w tiles x ny panels run in blocks of PB panels: every tile of the group on panels 0 .. PB-1, then
+// on panels PB .. 2PB-1, and so on (the last block takes the remaining ny % PB panels).  Consecutive
+// units, which run at the same time on one XCD, then share a few weight panels and a few activation
+// tiles, so a large group's activation rows are fetched once per PB panels rather than once per
+// panel (panel-major order) and each panel once per XCD's worth of tiles.
+constexpr int PB = 4;
 struct Unit {
   int g, row0, row_end, nt;
 };
@@ -226,13 +232,27 @@ __device__ __forceinline__ Unit unit_at(int u, int ny, const int4* __restrict__ 
                                         int bm) {
   const int q = u / ny;
   const int4 tq = tiles[q];
-  const int local = u - tq.z * ny;
-  Unit r;
-  r.nt = local / tq.w;
-  r.g = tq.x;
-  r.row0 = offsets[r.g] + (local - r.nt * tq.w) * bm;
-  r.row_end = min(r.row0 + bm, offsets[r.g + 1]);
-  return r;
+  const int local = u - tq.z * ny;   // unit within the group: [0, w * ny)
+  const int w = tq.w;
+  const int nfull = ny / PB;         // full panel blocks
+  const int pb = local / (w * PB);
+  int tile, nt;
+  if (pb < nfull) {
+    const int rem = local - pb * w * PB;
+    tile = rem / PB;
+    nt = pb * PB + (rem - tile * PB);
+  } else {
+    const int r = ny - nfull * PB;   // panels in the last block (>= 1 here)
+    const int rem = local - nfull * w * PB;
+    tile = rem / r;
+    nt = nfull * PB + (rem - tile * r);
+  }
+  Unit res;
+  res.nt = nt;
+  res.g = tq.x;
+  res.row0 = offsets[res.g] + tile * bm;
+  res.row_end = min(res.row0 + bm, offsets[res.g + 1]);
+  return res;
 }
 
 // Persistent workgroups: workgroup w takes units me(w), me(w) + G, me(w) + 2G, ... (G = grid size),
