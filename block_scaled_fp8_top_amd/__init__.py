@@ -33,7 +33,7 @@ EXPORTED = ("moe_gate_logits", "moe_route", "moe_route_quant", "moe_replay_route
             "moe_quant_fp8_block",
             "moe_dispatch", "moe_dispatch_plan", "moe_pack_weights_fp8", "moe_packed_weight_bytes", "moe_grouped_gemm_plan",
             "moe_grouped_gemm_fp8_planned", "moe_grouped_gemm_fp8_swiglu_save", "moe_grouped_gemm_fp8_gather",
-            "moe_grouped_gemm_fp8", "moe_combine", "moe_combine_residual", "moe_payload_bytes",
+            "moe_grouped_gemm_fp8", "moe_grouped_gemm_fp8_noalloc", "moe_combine", "moe_combine_residual", "moe_payload_bytes",
             "moe_payload_pack", "moe_payload_unpack", "moe_payload_to_host", "moe_payload_from_host",
             "moe_combine_backward", "moe_swiglu_backward_quant", "moe_route_backward", "moe_gate_backward",
             "moe_gate_backward_workspace", "moe_transpose_fp8_blocks", "moe_wgrad_max_tiles", "moe_wgrad_tiles",
@@ -91,6 +91,7 @@ def lib():
         "moe_pack_weights_fp8": [P, I32, I32, I32, I32, P, P],
         "moe_packed_weight_bytes": [I32, I32, I32, I32],
         "moe_grouped_gemm_fp8": [P, P, P, I32, I64, P, I32, P, I32, I32, I32, I32, I32, P, ctypes.c_int, P, P, SZ, P],
+        "moe_grouped_gemm_fp8_noalloc": [P, P, P, I32, I64, P, I32, P, I32, I32, I32, I32, I32, P, ctypes.c_int, P, P],
         "moe_grouped_gemm_plan": [P, I32, I64, I32, P, SZ, ctypes.POINTER(GemmPlan), P],
         "moe_grouped_gemm_fp8_planned": [ctypes.POINTER(GemmPlan), P, P, P, P, I32, P, I32, I32, I32, I32, P,
                                          ctypes.c_int, P, P],
@@ -607,6 +608,45 @@ def moe_grouped_gemm_fp8(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tens
                                       code, _p(osc), _p(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream)), "moe_grouped_gemm_fp8")
     return out if epilogue == MOE_EPI_STORE else (out, osc)
+
+
+NOALLOC_SCRATCH_BYTES = 1 << 20
+
+
+def moe_grouped_gemm_fp8_noalloc(a: torch.Tensor, as_: torch.Tensor, offsets: torch.Tensor, b, bs: torch.Tensor,
+                                 epilogue: int, out: torch.Tensor, out_scales: Optional[torch.Tensor] = None,
+                                 tile_rows: int = 0, pow2: bool = False, stream=None):
+    """moe_grouped_gemm_fp8 with the tile plan in the library's own device scratch (no workspace,
+    nothing allocated here either): ``out`` (and ``out_scales`` for the SwiGLU epilogue) must be given.
+    Results are bitwise those of moe_grouped_gemm_fp8."""
+    max_rows, K = a.shape
+    if isinstance(b, PackedWeight):
+        if b.epilogue != epilogue:
+            raise ValueError("weight was packed for another epilogue")
+        G, N, Kb, b_layout, b_t = b.G, b.N, b.K, MOE_B_PACKED, b.data
+    elif isinstance(b, PackedWeightFP4):
+        G, N, Kb, b_layout, b_t = b.G, b.N, b.K, MOE_B_PACKED_FP4, b.data
+        bs = b.scales
+    else:
+        G, N, Kb = b.shape
+        b_layout, b_t = MOE_B_ROWMAJOR, _dev(b, "b", FP8)
+    if Kb != K:
+        raise ValueError("K mismatch")
+    _dev(a, "a", FP8)
+    _dev(as_, "as", torch.float32, (max_rows, K // 128))
+    _dev(offsets, "offsets", torch.int32, (G + 1,))
+    if epilogue == MOE_EPI_STORE:
+        _dev(out, "out", (torch.float32, torch.bfloat16), (max_rows, N))
+        code = MOE_BF16 if out.dtype == torch.bfloat16 else MOE_F32
+    else:
+        _dev(out, "out", FP8, (max_rows, N // 2))
+        _dev(out_scales, "out_scales", torch.float32, (max_rows, N // 2 // 128))
+        code = MOE_FP8_E4M3
+    mode = MOE_SCALE_POW2 if pow2 else MOE_SCALE_AMAX
+    _check(lib().moe_grouped_gemm_fp8_noalloc(_p(a), _p(as_), _p(offsets), G, max_rows, _p(b_t), b_layout, _p(bs), N,
+                                              K, epilogue, mode, tile_rows, _p(out), code, _p(out_scales),
+                                              _stream(stream)), "moe_grouped_gemm_fp8_noalloc")
+    return out if epilogue == MOE_EPI_STORE else (out, out_scales)
 
 
 def moe_combine(y: torch.Tensor, dest_row: torch.Tensor, topk_w: torch.Tensor, shared_first_row: Optional[torch.Tensor] = None,

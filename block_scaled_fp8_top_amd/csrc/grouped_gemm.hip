@@ -967,3 +967,40 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int
   return moe_grouped_gemm_fp8_planned(&plan, a, as, offsets, b, b_layout, bs, N, K, epilogue, scale_mode, out,
                                       out_dtype, out_scales, stream);
 }
+
+// ------------------------------------------------------------------------------------------------
+// No-allocation variant: the tile plan lives in this file-scope device array (one copy per GPU).
+// Host code never passes `scratch` itself (its host-side name is not a device address): the
+// device address of each GPU's copy is looked up once, with that device current, and cached.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+// device address of this device's scratch (nullptr on a HIP error)
+void* scratch_address() {
+  static std::atomic<void*> cached[MAX_DEVICES];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  void* p = cached[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+  cached[dev].store(q, std::memory_order_release);   // concurrent first calls store the same value
+  return q;
+}
+}  // namespace
+
+extern "C" int moe_grouped_gemm_fp8_noalloc(const uint8_t* a, const float* as, const int32_t* offsets, int32_t groups,
+                                            int64_t max_rows, const uint8_t* b, int32_t b_layout, const float* bs,
+                                            int32_t N, int32_t K, int32_t epilogue, int32_t scale_mode,
+                                            int32_t tile_rows, void* out, int out_dtype, float* out_scales,
+                                            void* stream) {
+  int rc = check_gemm_args(max_rows, groups, N, K, epilogue, scale_mode, out_dtype, b_layout);
+  if (rc != MOE_OK) return rc;
+  if (max_rows == 0) return MOE_OK;
+  if (moe_gemm_workspace(max_rows, groups) > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = scratch_address();
+  if (!ws) return MOE_ERR_HIP;
+  return moe_grouped_gemm_fp8(a, as, offsets, groups, max_rows, b, b_layout, bs, N, K, epilogue, scale_mode, tile_rows,
+                              out, out_dtype, out_scales, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
+}

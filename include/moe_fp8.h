@@ -230,10 +230,9 @@ size_t moe_packed_weight_bytes(int32_t groups, int32_t N, int32_t K, int32_t epi
  *            directly; only the exponent field of each scale is read; the SwiGLU epilogue then
  *            quantises h with power-of-two scales too)
  *   tile_rows: rows per workgroup tile, 32, 48, 64, 128 or 256 (256: packed weights only), or 0 to
- *              choose from the group sizes (256 when groups average more than 256 rows and the
- *              weights are packed)
- *            (the smallest height >= 2 * ceil(max_rows / groups)).  The result is the same for every
- *            height.
+ *            choose from the group sizes: the smallest of 32, 48, 64, 128 at or above
+ *            2 * ceil(max_rows / groups), and 256 above 512 when the weights are packed.  The result
+ *            is the same for every height.
  *   Rows beyond offsets[groups] are not written.  workspace >= moe_workspace_bytes(MOE_OP_GROUPED_GEMM,
  *   max_rows, 0, groups, N, K).
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (N, K % 128; F % 128 for SwiGLU; (max_rows+1)*K or one group's
@@ -244,6 +243,24 @@ int moe_grouped_gemm_fp8(const uint8_t* a, const float* as, const int32_t* offse
                          const uint8_t* b, int32_t b_layout, const float* bs, int32_t N, int32_t K, int32_t epilogue,
                          int32_t scale_mode, int32_t tile_rows, void* out, int out_dtype, float* out_scales,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_grouped_gemm_fp8 for callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops, harnesses that forbid hipMalloc): the same computation and results
+ * (bitwise), with the tile plan kept in the library's own device scratch (MOE_NOALLOC_SCRATCH_BYTES,
+ * a static device array of each GPU the library runs on, held until the process ends) instead of a
+ * caller workspace.  The call allocates and frees nothing; the caller still passes every input and
+ * output.  Limit: moe_workspace_bytes(MOE_OP_GROUPED_GEMM, max_rows, 0, groups, N, K) must not
+ * exceed MOE_NOALLOC_SCRATCH_BYTES (about max_rows + 32 * groups <= 65000 * 32 rows), else
+ * MOE_ERR_WORKSPACE and nothing is enqueued.  Every call on one GPU shares that GPU's scratch, which
+ * keeps the last call's plan: calls that overlap on one GPU (several streams, or host threads without
+ * ordering) race and must be serialised by the caller.  The first call on a device looks up the
+ * scratch's device address (hipGetSymbolAddress) with that device current.
+ * Errors: as moe_grouped_gemm_fp8, with MOE_ERR_WORKSPACE for a plan larger than the scratch. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)1 << 20)
+int moe_grouped_gemm_fp8_noalloc(const uint8_t* a, const float* as, const int32_t* offsets, int32_t groups,
+                                 int64_t max_rows, const uint8_t* b, int32_t b_layout, const float* bs, int32_t N,
+                                 int32_t K, int32_t epilogue, int32_t scale_mode, int32_t tile_rows, void* out,
+                                 int out_dtype, float* out_scales, void* stream);
 
 /* Grouped GEMM in two steps, so that one tile plan serves several GEMMs over the same groups
  * (the layer's W1 and W2 GEMMs) and the GEMM launch itself is a single kernel.
