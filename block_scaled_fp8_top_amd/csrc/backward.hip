@@ -46,13 +46,9 @@ __device__ __forceinline__ uint2 quant8_block(const float (&v)[8], bool pow2, fl
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  m = row16_max(m);   // the 16 lanes are one aligned DPP row
   s = block_scale(m, pow2);
-  float r[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) r[q] = v[q] / s;
-  return make_uint2(e4m3_pack4(r[0], r[1], r[2], r[3]), e4m3_pack4(r[4], r[5], r[6], r[7]));
+  return encode8(v, s);
 }
 
 constexpr int CB_THREADS = 256;      // combine backward: one workgroup per token

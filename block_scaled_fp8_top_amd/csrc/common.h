@@ -117,11 +117,56 @@ __device__ __forceinline__ void load8(const void* x, int64_t i, float (&v)[8]) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// The quotients x / s of an encoder, s one block's scale.  With y = 1/s correctly rounded (one IEEE
+// division per block), q0 = x*y is within an ulp of x/s, the residual x - q0*s is exact in one FMA
+// while it does not underflow, and q0 + residual*y rounded once is then the correctly rounded x/s
+// (Markstein's theorem on division by a correctly rounded reciprocal; Markstein, IBM J. Res. Dev.
+// 34(1), 1990).  The residual can underflow only for |x| below about 2^-100, where |x/s| is far below
+// the smallest e4m3 step for every s >= 2^-60, so the e4m3 code (zero, sign of x) is the same;
+// the sign is copied from x so that -0 stays -0.  Scales below 2^-60 or not finite take IEEE
+// divisions.  Three VALU operations per value instead of a full division.
+__device__ __forceinline__ bool quot_by_recip(float s) { return s >= 0x1p-60f && s <= 0x1.fffffep+127f; }
+__device__ __forceinline__ float quot_recip_step(float x, float s, float y) {
+  const float q0 = x * y;
+  const float r = __builtin_fmaf(-q0, s, x);
+  return __builtin_copysignf(__builtin_fmaf(r, y, q0), x);
+}
+template <int N>
+__device__ __forceinline__ void quotients(const float* v, float s, float* r) {
+  if (quot_by_recip(s)) {
+    const float y = 1.0f / s;
+#pragma unroll
+    for (int q = 0; q < N; ++q) r[q] = quot_recip_step(v[q], s, y);
+  } else {
+#pragma unroll
+    for (int q = 0; q < N; ++q) r[q] = v[q] / s;
+  }
+}
+
 __device__ __forceinline__ uint2 encode8(const float (&v)[8], float s) {
   float r[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) r[q] = v[q] / s;
+  quotients<8>(v, s, r);
   return make_uint2(e4m3_pack4(r[0], r[1], r[2], r[3]), e4m3_pack4(r[4], r[5], r[6], r[7]));
+}
+
+// ------------------------------------------------------------------------------------------
+// Cross-lane moves within a 16-lane row by DPP (no LDS crossbar): lane i reads lane i^1 (quad
+// permutation 1,0,3,2), i^2 (2,3,0,1), 7-i within its 8 (half-row mirror) or 15-i within its 16
+// (row mirror).  Every source lane is inside the row, so rows are independent of one another.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) { return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v))); }
+// max over each aligned 16-lane row, in every lane of the row
+__device__ __forceinline__ float row16_max(float m) {
+  m = fmaxf(m, dpp_f32<DPP_XOR1>(m));
+  m = fmaxf(m, dpp_f32<DPP_XOR2>(m));
+  m = fmaxf(m, dpp_f32<DPP_HALF_MIRROR>(m));
+  return fmaxf(m, dpp_f32<DPP_MIRROR>(m));
 }
 
 
@@ -136,9 +181,32 @@ __device__ __forceinline__ void quant_1x128_piece(const void* __restrict__ x, in
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  m = row16_max(m);   // the block's 16 lanes are one aligned DPP row
   const float s = block_scale(m, POW2);
   *reinterpret_cast<uint2*>(q + b * 128 + sub * 8) = encode8(v, s);
   if (sub == 0) scales[b] = s;
+}
+
+// U blocks b0, b0 + step, ..., b0 + (U-1) step per 16-lane group (blocks >= nblocks skipped), every
+// load issued before the first block is encoded.
+template <bool BF16, bool POW2, int U>
+__device__ __forceinline__ void quant_1x128_pieces(const void* __restrict__ x, int64_t b0, int64_t step,
+                                                   int64_t nblocks, int sub, uint8_t* __restrict__ q,
+                                                   float* __restrict__ scales) {
+  float v[U][8];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (b0 + u * step < nblocks) load8<BF16>(x, (b0 + u * step) * 128 + sub * 8, v[u]);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t b = b0 + u * step;
+    if (b >= nblocks) break;
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[u][i]));
+    m = row16_max(m);
+    const float s = block_scale(m, POW2);
+    *reinterpret_cast<uint2*>(q + b * 128 + sub * 8) = encode8(v[u], s);
+    if (sub == 0) scales[b] = s;
+  }
 }

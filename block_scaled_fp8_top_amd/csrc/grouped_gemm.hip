@@ -688,8 +688,10 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
         const int row = wm * WROWS + lrow;
 #pragma unroll
         for (int hs = 0; hs < HS; ++hs) {
-          const uint32_t codes = e4m3_pack4(acc[ms][hs][0] / sc, acc[ms][hs][1] / sc, acc[ms][hs][2] / sc,
-                                            acc[ms][hs][3] / sc);
+          const float v[4] = {acc[ms][hs][0], acc[ms][hs][1], acc[ms][hs][2], acc[ms][hs][3]};
+          float r[4];
+          quotients<4>(v, sc, r);
+          const uint32_t codes = e4m3_pack4(r[0], r[1], r[2], r[3]);
           __builtin_amdgcn_raw_buffer_store_b32(codes, rq, row * F + f0 + hs * 16, 0, 0);
         }
         // the row's scale: one lane per row (column group 0) of wave column 0; other lanes aim past

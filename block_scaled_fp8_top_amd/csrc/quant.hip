@@ -11,15 +11,15 @@ namespace {
 
 // 1x128: 16 lanes per block, 8 consecutive values per lane.  Blocks are contiguous in memory
 // (rows are contiguous and cols % 128 == 0), so block b covers x[128 b, 128 b + 128) and its
-// scale is scales[b].
+// scale is scales[b].  A workgroup (16 lane groups) takes Q1_U * 16 consecutive blocks, group g
+// blocks 16 u + g of them, so each step u of the workgroup reads 16 adjacent blocks.
+constexpr int Q1_U = 4;
 template <bool BF16, bool POW2>
 __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict__ x, int64_t nblocks,
                                                           uint8_t* __restrict__ q, float* __restrict__ scales) {
-  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t b = gt >> 4;
-  // every lane of a 16-lane group shares b; whole groups are in or out of range
-  if (b >= nblocks) return;
-  quant_1x128_piece<BF16, POW2>(x, b, threadIdx.x & 15, q, scales);
+  const int64_t b0 = (int64_t)blockIdx.x * (16 * Q1_U) + threadIdx.x / 16;
+  // every lane of a 16-lane group shares its blocks; whole groups are in or out of range
+  quant_1x128_pieces<BF16, POW2, Q1_U>(x, b0, 16, nblocks, threadIdx.x & 15, q, scales);
 }
 
 // 128x128: one workgroup of 256 threads per block; thread (r16 = tid / 16, c = tid % 16) handles
@@ -69,8 +69,7 @@ extern "C" int moe_quant_fp8_block(const void* x, int x_dtype, int64_t batch, in
   hipStream_t st = as_stream(stream);
   const bool bf16 = x_dtype == MOE_BF16, pow2 = scale_mode == MOE_SCALE_POW2;
   if (block_rows == 1) {
-    const int64_t threads = nblocks * 16;
-    const int64_t grid = ceil_div64(threads, 256);
+    const int64_t grid = ceil_div64(nblocks, 16 * Q1_U);
     if (grid > INT32_MAX) return MOE_ERR_SHAPE;
     auto k = bf16 ? (pow2 ? quant_1x128_kernel<true, true> : quant_1x128_kernel<true, false>)
                   : (pow2 ? quant_1x128_kernel<false, true> : quant_1x128_kernel<false, false>);

@@ -222,6 +222,200 @@ __global__ __launch_bounds__(64 * WAVES) void route_quant_kernel(const float* __
   quant_1x128_piece<BF16, POW2>(x, b, threadIdx.x & 15, xq, xs);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Sixteen lanes per token (four tokens per wavefront, FTOK per workgroup), for E = 16 * EPT
+// experts: token-local lane tl holds experts tl*EPT .. tl*EPT + EPT - 1 in registers.  With a group
+// limit, a group (E / n_group experts, a multiple of EPT) is LPG = 16 / n_group adjacent lanes, an
+// aligned DPP segment.  Every expert carries a 64-bit rank key: the order-preserving bits of its
+// logit (-0 taken as +0, since the order compares values) above the complemented expert index,
+// so key order is (logit descending, expert ascending) and no real key is 0.  A selection round
+// takes the largest key below the previous round's winner: the next expert in that order.  The
+// results are those of route_token bit for bit: the same scores (the same fp32 operations on the
+// same logits), the same sums in the same order, the same orders.
+constexpr int FTOK = 16;
+
+__device__ __forceinline__ uint64_t rank_key(float z, int e) {
+  uint32_t u = __float_as_uint(z);
+  if (u == 0x80000000u) u = 0u;
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)e;
+}
+__device__ __forceinline__ int key_expert(uint64_t key) { return (int)~(uint32_t)key; }
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+// largest key of each aligned segment of n lanes (n = 1, 2, 4, 8 or 16, wave-uniform), in every
+// lane of the segment
+__device__ __forceinline__ uint64_t seg_max(uint64_t v, int n) {
+  if (n >= 2) v = umax64(v, dpp_u64<DPP_XOR1>(v));
+  if (n >= 4) v = umax64(v, dpp_u64<DPP_XOR2>(v));
+  if (n >= 8) v = umax64(v, dpp_u64<DPP_HALF_MIRROR>(v));
+  if (n >= 16) v = umax64(v, dpp_u64<DPP_MIRROR>(v));
+  return v;
+}
+// largest of this lane's keys below thr (0 if none)
+template <int EPT>
+__device__ __forceinline__ uint64_t lane_best_below(const uint64_t (&key)[EPT], uint64_t thr) {
+  uint64_t b = 0;
+#pragma unroll
+  for (int m = 0; m < EPT; ++m)
+    if (key[m] < thr && key[m] > b) b = key[m];
+  return b;
+}
+
+// token t (live: t < T; a dead token computes on placeholders and writes nothing).  psum: the
+// token's E floats of LDS (softmax only).
+template <int EPT, bool SOFTMAX>
+__device__ __forceinline__ void route_token16(const float* __restrict__ logits, int64_t t, bool live,
+                                              const moe_router_cfg& cfg, int32_t* __restrict__ topk_idx,
+                                              float* __restrict__ topk_w, int32_t* __restrict__ record,
+                                              int64_t record_ld, float* psum) {
+  constexpr int E = 16 * EPT;
+  const int k = cfg.top_k;
+  const int lane = threadIdx.x & 63, tl = lane & 15, tokbase = lane & 48;
+  const int e0 = tl * EPT;
+  float z[EPT];
+  if (live) {
+    const float4* src = reinterpret_cast<const float4*>(logits + t * E + e0);
+#pragma unroll
+    for (int m = 0; m < EPT / 4; ++m) {
+      const float4 v = src[m];
+      z[4 * m] = v.x; z[4 * m + 1] = v.y; z[4 * m + 2] = v.z; z[4 * m + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < EPT; ++m) z[m] = 0.0f;
+  }
+  uint64_t key[EPT];
+#pragma unroll
+  for (int m = 0; m < EPT; ++m) key[m] = rank_key(z[m], e0 + m);
+
+  // scores: softmax p_e / S with S summed over e ascending from +0, or the sigmoid
+  float mx = 0.0f, S = 1.0f;
+  if (SOFTMAX) {
+    mx = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < EPT; ++m) mx = fmaxf(mx, z[m]);
+    mx = row16_max(mx);
+#pragma unroll
+    for (int m = 0; m < EPT; ++m) psum[e0 + m] = router_exp(z[m] - mx);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    float acc = 0.0f;
+    if (tl == 0)
+      for (int e = 0; e < E; ++e) acc = acc + psum[e];
+    S = __shfl(acc, tokbase, 64);
+  }
+  auto score = [&](float zz) { return SOFTMAX ? router_exp(zz - mx) / S : router_sigmoid(zz); };
+
+  // group limit: each group's score is the sum of the scores of its group_score_topk first
+  // experts in key order; the topk_group groups first by (score descending, group ascending) stay
+  if (cfg.n_group > 1) {
+    const int lpg = 16 / cfg.n_group;
+    uint64_t thr = ~0ull;
+    float gsum = 0.0f;
+    for (int r = 0; r < cfg.group_score_topk; ++r) {
+      const uint64_t b = seg_max(lane_best_below<EPT>(key, thr), lpg);
+      gsum = gsum + score(key_logit(b));
+      thr = b;
+    }
+    const int G = tl / lpg;
+    int rank = 0;
+    for (int h = 0; h < cfg.n_group; ++h) {
+      const float sh = __shfl(gsum, tokbase + h * lpg, 64);
+      rank += (sh > gsum || (sh == gsum && h < G)) ? 1 : 0;
+    }
+    if (rank >= cfg.topk_group) {
+#pragma unroll
+      for (int m = 0; m < EPT; ++m) key[m] = 0;
+    }
+  }
+
+  // top-k: slot r is kept by lane r % 16 in entry r / 16
+  uint64_t slot[4] = {0, 0, 0, 0};
+  uint64_t thr = ~0ull;
+#pragma unroll 1
+  for (int r = 0; r < k; ++r) {
+    const uint64_t b = seg_max(lane_best_below<EPT>(key, thr), 16);
+    if ((r & 15) == tl) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if ((r >> 4) == q) slot[q] = b;
+    }
+    thr = b;
+  }
+  float sw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (16 * q < k && 16 * q + tl < k) sw[q] = score(key_logit(slot[q]));
+  float d = 1.0f;
+  if (cfg.renormalize) {
+    d = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      for (int i = 0; i < 16 && 16 * q + i < k; ++i) d = d + __shfl(sw[q], tokbase + i, 64);
+  }
+  if (!live) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 16 * q + tl;
+    if (r < k) {
+      const int e = key_expert(slot[q]);
+      topk_idx[t * k + r] = e;
+      topk_w[t * k + r] = cfg.renormalize ? sw[q] / d : sw[q];
+      if (record) record[r * record_ld + t] = e;
+    }
+  }
+}
+
+template <int EPT, bool SOFTMAX>
+__global__ __launch_bounds__(64 * WAVES) void route16_kernel(const float* __restrict__ logits, int64_t T,
+                                                             moe_router_cfg cfg, int32_t* __restrict__ topk_idx,
+                                                             float* __restrict__ topk_w, int32_t* __restrict__ record,
+                                                             int64_t record_ld) {
+  __shared__ float psum[SOFTMAX ? FTOK : 1][SOFTMAX ? 16 * EPT : 1];
+  const int tok = threadIdx.x / 16;
+  const int64_t t = (int64_t)blockIdx.x * FTOK + tok;
+  route_token16<EPT, SOFTMAX>(logits, t, t < T, cfg, topk_idx, topk_w, record, record_ld,
+                              psum[SOFTMAX ? tok : 0]);
+}
+
+// The router (16 tokens per workgroup, as route16_kernel) and the 1x128 quantisation of x (RQ_U * 16
+// blocks per workgroup) in one launch: the routing workgroups are spread through the grid, one at
+// every rstride-th position, so that the latency-bound routing runs beside the HBM-bound
+// quantisation instead of before it.
+constexpr int RQ_U = 4;
+template <int EPT, bool SOFTMAX, bool BF16, bool POW2>
+__global__ __launch_bounds__(64 * WAVES) void route16_quant_kernel(
+    const float* __restrict__ logits, int64_t T, moe_router_cfg cfg, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, int32_t* __restrict__ record, int64_t record_ld, int64_t nroute, int64_t rstride,
+    const void* __restrict__ x, int64_t nblocks, uint8_t* __restrict__ xq, float* __restrict__ xs) {
+  __shared__ float psum[SOFTMAX ? FTOK : 1][SOFTMAX ? 16 * EPT : 1];
+  const int64_t i = blockIdx.x;
+  int64_t qw;   // quantisation workgroup index, or -1 for a routing workgroup
+  if (i < nroute * rstride) {
+    if (i % rstride == 0) {
+      const int tok = threadIdx.x / 16;
+      const int64_t t = (i / rstride) * FTOK + tok;
+      route_token16<EPT, SOFTMAX>(logits, t, t < T, cfg, topk_idx, topk_w, record, record_ld,
+                                  psum[SOFTMAX ? tok : 0]);
+      return;
+    }
+    qw = i - i / rstride - 1;
+  } else {
+    qw = i - nroute;
+  }
+  quant_1x128_pieces<BF16, POW2, RQ_U>(x, qw * (16 * RQ_U) + threadIdx.x / 16, 16, nblocks, threadIdx.x & 15, xq,
+                                        xs);
+}
+
 template <int EPL>
 __global__ __launch_bounds__(64 * WAVES) void replay_kernel(const float* __restrict__ logits, int64_t T,
                                                             moe_router_cfg cfg, const int32_t* __restrict__ replay,
@@ -370,7 +564,34 @@ int check_cfg(const moe_router_cfg* c) {
   return MOE_OK;
 }
 
+// experts per lane of the 16-lane router for this call, or 0 where it does not apply: E of 64, 128,
+// 256 or 512, a group limit (if any) of 2, 4, 8 or 16 groups, 16-byte aligned logits
+int fast_ept(const moe_router_cfg& c, const float* logits) {
+  const int E = c.num_experts;
+  if (E != 64 && E != 128 && E != 256 && E != 512) return 0;
+  if (c.n_group > 1 && (c.n_group > 16 || 16 % c.n_group != 0)) return 0;
+  if ((reinterpret_cast<uintptr_t>(logits) & 15) != 0) return 0;
+  return E / 16;
+}
+
 }  // namespace
+
+#define DISPATCH_EPT(EPT_RT, SOFTMAX_RT, BODY)                   \
+  do {                                                           \
+    if (SOFTMAX_RT) {                                            \
+      constexpr bool SM = true;                                  \
+      if ((EPT_RT) == 4) { constexpr int EPT = 4; BODY; }        \
+      else if ((EPT_RT) == 8) { constexpr int EPT = 8; BODY; }   \
+      else if ((EPT_RT) == 16) { constexpr int EPT = 16; BODY; } \
+      else { constexpr int EPT = 32; BODY; }                     \
+    } else {                                                     \
+      constexpr bool SM = false;                                 \
+      if ((EPT_RT) == 4) { constexpr int EPT = 4; BODY; }        \
+      else if ((EPT_RT) == 8) { constexpr int EPT = 8; BODY; }   \
+      else if ((EPT_RT) == 16) { constexpr int EPT = 16; BODY; } \
+      else { constexpr int EPT = 32; BODY; }                     \
+    }                                                            \
+  } while (0)
 
 #define DISPATCH_EPL(E, BODY)                  \
   do {                                         \
@@ -401,10 +622,18 @@ extern "C" int moe_route(const float* logits, int64_t T, const moe_router_cfg* c
   if (T == 0) return MOE_OK;
   if (!logits || !topk_idx || !topk_w) return MOE_ERR_NULL;
   const moe_router_cfg c = *cfg;
-  const unsigned grid = (unsigned)ceil_div64(T, WAVES);
   hipStream_t st = as_stream(stream);
-  DISPATCH_EPL(c.num_experts, (route_kernel<EPL><<<grid, 64 * WAVES, 0, st>>>(logits, T, c, topk_idx, topk_w,
-                                                                               record, record_ld)));
+  const int ept = fast_ept(c, logits);
+  if (ept) {
+    const unsigned grid = (unsigned)ceil_div64(T, FTOK);
+    DISPATCH_EPT(ept, c.score_fn == MOE_SCORE_SOFTMAX,
+                 (route16_kernel<EPT, SM><<<grid, 64 * WAVES, 0, st>>>(logits, T, c, topk_idx, topk_w, record,
+                                                                       record_ld)));
+  } else {
+    const unsigned grid = (unsigned)ceil_div64(T, WAVES);
+    DISPATCH_EPL(c.num_experts, (route_kernel<EPL><<<grid, 64 * WAVES, 0, st>>>(logits, T, c, topk_idx, topk_w,
+                                                                                 record, record_ld)));
+  }
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -422,20 +651,37 @@ extern "C" int moe_route_quant(const float* logits, int64_t T, const moe_router_
   if (T == 0) return MOE_OK;
   if (!logits || !topk_idx || !topk_w || !x || !xq || !xs) return MOE_ERR_NULL;
   const moe_router_cfg c = *cfg;
-  const int64_t nroute = ceil_div64(T, WAVES);
   const int64_t nblocks = T * (H / 128);
-  const int64_t grid = nroute + ceil_div64(nblocks, QBLK);
-  if (grid > INT32_MAX) return MOE_ERR_SHAPE;
   hipStream_t st = as_stream(stream);
   const bool bf16 = x_dtype == MOE_BF16, pow2 = scale_mode == MOE_SCALE_POW2;
+  const int ept = fast_ept(c, logits);
+  if (ept) {
+    const int64_t nroute = ceil_div64(T, FTOK), nquant = ceil_div64(nblocks, 16 * RQ_U);
+    const int64_t grid = nroute + nquant;
+    if (grid > INT32_MAX) return MOE_ERR_SHAPE;
+    const int64_t rstride = grid / nroute;   // >= 1; routing workgroups at 0, rstride, 2 rstride, ...
+#define RQ16_LAUNCH(B, P)                                                                                       \
+  DISPATCH_EPT(ept, c.score_fn == MOE_SCORE_SOFTMAX,                                                            \
+               (route16_quant_kernel<EPT, SM, B, P><<<(unsigned)grid, 64 * WAVES, 0, st>>>(                     \
+                   logits, T, c, topk_idx, topk_w, record, record_ld, nroute, rstride, x, nblocks, xq, xs)))
+    if (bf16 && pow2) RQ16_LAUNCH(true, true);
+    else if (bf16) RQ16_LAUNCH(true, false);
+    else if (pow2) RQ16_LAUNCH(false, true);
+    else RQ16_LAUNCH(false, false);
+#undef RQ16_LAUNCH
+  } else {
+    const int64_t nroute = ceil_div64(T, WAVES);
+    const int64_t grid = nroute + ceil_div64(nblocks, QBLK);
+    if (grid > INT32_MAX) return MOE_ERR_SHAPE;
 #define RQ_LAUNCH(B, P)                                                                                          \
   DISPATCH_EPL(c.num_experts, (route_quant_kernel<EPL, B, P><<<(unsigned)grid, 64 * WAVES, 0, st>>>(             \
                                   logits, T, c, topk_idx, topk_w, record, record_ld, nroute, x, nblocks, xq, xs)))
-  if (bf16 && pow2) RQ_LAUNCH(true, true);
-  else if (bf16) RQ_LAUNCH(true, false);
-  else if (pow2) RQ_LAUNCH(false, true);
-  else RQ_LAUNCH(false, false);
+    if (bf16 && pow2) RQ_LAUNCH(true, true);
+    else if (bf16) RQ_LAUNCH(true, false);
+    else if (pow2) RQ_LAUNCH(false, true);
+    else RQ_LAUNCH(false, false);
 #undef RQ_LAUNCH
+  }
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

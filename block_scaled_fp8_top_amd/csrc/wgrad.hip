@@ -97,8 +97,11 @@ __device__ __forceinline__ void colwise_store(float (&v)[8][4], int tile, int tf
     const int c = cc * 4 + j;
     const float amax = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
     const float s = block_scale(amax, POW2);
-    const uint32_t lo = e4m3_pack4(v[0][j] / s, v[1][j] / s, v[2][j] / s, v[3][j] / s);
-    const uint32_t hi = e4m3_pack4(v[4][j] / s, v[5][j] / s, v[6][j] / s, v[7][j] / s);
+    const float col[8] = {v[0][j], v[1][j], v[2][j], v[3][j], v[4][j], v[5][j], v[6][j], v[7][j]};
+    float r[8];
+    quotients<8>(col, s, r);
+    const uint32_t lo = e4m3_pack4(r[0], r[1], r[2], r[3]);
+    const uint32_t hi = e4m3_pack4(r[4], r[5], r[6], r[7]);
     *reinterpret_cast<uint2*>(qb + (int64_t)(c0 + c) * kg + lt * 128 + rr * 8) = make_uint2(lo, hi);
     if (rr == 0) sb[(int64_t)(c0 + c) * ntiles + lt] = s;
   }

@@ -78,6 +78,48 @@ def test_quant_edge_values():
     assert_equal("scales", host(s), rs)
 
 
+def _quotient_edge_blocks(nblocks, seed, bf16_exact):
+    """Blocks of 128 whose amax A has an exponent anywhere from -133 to 127 (subnormal, tiny,
+    normal and huge scales, both sides of the 2^-60 scale below which the encoders divide in
+    full), filled with values spread over every bit pattern of magnitude <= A: subnormal and
+    signed-zero x included."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((nblocks, 128), np.float32)
+    for b in range(nblocks):
+        ex = int(rng.integers(-133, 128))
+        a = np.float32(np.ldexp(1.0 + rng.random(), ex)) if ex < 127 else np.float32(np.ldexp(1.0 + 0.99 * rng.random(), ex))
+        if bf16_exact:
+            a = (np.array([a], np.float32).view(np.uint32) & 0xFFFF0000).view(np.float32)[0]
+        if a == 0:
+            a = np.float32(np.ldexp(1.0, -133))
+        top = int(np.array([a], np.float32).view(np.uint32)[0])
+        bits = rng.integers(0, top + 1, size=127, dtype=np.int64).astype(np.uint32)
+        if bf16_exact:
+            bits &= np.uint32(0xFFFF0000)
+        bits |= rng.integers(0, 2, size=127).astype(np.uint32) << np.uint32(31)   # random signs
+        out[b, 0] = a if b % 2 else -a
+        out[b, 1:] = bits.view(np.float32)
+        rng.shuffle(out[b])
+    return out
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_quant_quotients_over_every_exponent(act, pow2):
+    """The encoders' x / s (one correctly rounded reciprocal and one FMA correction per value, or a
+    full division for scales below 2^-60): codes and scales bit for bit the oracle's (IEEE
+    division) for block scales across the whole fp32 exponent range, 1x128 and 128x128 blocks."""
+    x = _quotient_edge_blocks(4096, 41 + pow2, act == "bf16").reshape(512, 1024)
+    xt = torch.from_numpy(x).to(DEV)
+    if act == "bf16":
+        xt = xt.to(torch.bfloat16)
+    for br in (1, 128):
+        q, s = M.moe_quant_fp8_block(xt, br, pow2=pow2)
+        rq, rs = O.moe_quant_fp8_block(host(xt), br, pow2=pow2)
+        assert_equal(f"codes {br}", host(q), rq)
+        assert_equal(f"scales {br}", host(s), rs)
+
+
 # ----------------------------------------------------------------------------- gate logits
 @pytest.mark.parametrize("name", NAMES)
 def test_gate_logits(name):
@@ -761,3 +803,54 @@ def test_combine_residual(act, shared):
     inplace = res.clone()
     M.moe_combine_residual(y, gdest, w, sh, inplace, x_next=inplace)
     assert torch.equal(inplace.view(iv), x_next.view(iv))
+
+
+def _signed_zero_tie_logits(T, E, seed):
+    """Logits with exact ties, +0.0 / -0.0 mixtures (equal values, so ties by index) and a few -inf."""
+    rng = np.random.default_rng(seed)
+    z = rng.integers(-3, 4, size=(T, E)).astype(np.float32) * np.float32(0.5)
+    zero = z == 0
+    z[zero & (rng.random((T, E)) < 0.5)] = np.float32(-0.0)
+    z[rng.random((T, E)) < 0.01] = -np.inf
+    z[:, 0] = np.float32(7.0)   # at least one finite logit per token
+    return z
+
+
+@pytest.mark.parametrize("E", [64, 128, 256, 512])
+@pytest.mark.parametrize("score", [0, 1])
+@pytest.mark.parametrize("ng,tg,gt", [(1, 1, 2), (2, 1, 1), (4, 2, 3), (8, 4, 2), (16, 5, 2)])
+def test_route_sixteen_lane_path(E, score, ng, tg, gt):
+    """The 16-lanes-per-token router (E of 64..512, group limits of 2..16 groups): indices, weights
+    and record bit for bit the oracle's on random logits, on tie-heavy logits with signed zeros and
+    -inf, for k of 1, 8 and up to the groups' capacity; the fused launch gives the same; a
+    misaligned logits view (the general path) gives the same."""
+    gs = E // ng
+    for k in sorted({1, 8, min(17, tg * gs), min(40, tg * gs)}):
+        gcfg = M.router_cfg(E, k, score, k > 1, ng, tg, gt)
+        ocfg = O.router_cfg(E, k, score, k > 1, ng, tg, gt)
+        for T, kind in ((257, "rand"), (67, "ties")):
+            if kind == "rand":
+                z = (synth.randn((T, E), 11, synth.STAGE, part=E + k, device=DEV) * 2).cpu().numpy()
+            else:
+                z = _signed_zero_tie_logits(T, E, E * 100 + k)
+            zd = torch.from_numpy(z).to(DEV)
+            rec = torch.full((k, T + 1), -4, dtype=torch.int32, device=DEV)
+            idx, w = M.moe_route(zd, gcfg, record=rec)
+            orec = np.full((k, T + 1), -4, np.int32)
+            oidx, ow = O.moe_route(z, ocfg, record=orec)
+            tag = f"E={E} k={k} ng={ng} {kind}"
+            assert_equal(f"idx {tag}", host(idx), oidx)
+            assert_equal(f"w {tag}", host(w), ow)
+            assert_equal(f"record {tag}", host(rec), orec)
+            x = synth.randn((T, 256), 3, synth.STAGE, part=k, device=DEV).to(torch.bfloat16)
+            fidx, fw, fq, fs = M.moe_route_quant(zd, gcfg, x)
+            q1, s1 = M.moe_quant_fp8_block(x, 1)
+            assert_equal(f"fused idx {tag}", host(fidx), oidx)
+            assert_equal(f"fused w {tag}", host(fw), ow)
+            assert torch.equal(fq, q1) and torch.equal(fs.view(torch.int32), s1.view(torch.int32))
+            buf = torch.empty(T * E + 1, dtype=torch.float32, device=DEV)
+            zm = buf[1:].view(T, E)    # 4-byte aligned only: the general path
+            zm.copy_(zd)
+            midx, mw = M.moe_route(zm, gcfg)
+            assert_equal(f"misaligned idx {tag}", host(midx), oidx)
+            assert_equal(f"misaligned w {tag}", host(mw), ow)
