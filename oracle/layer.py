@@ -217,10 +217,13 @@ def rel_err(got, ref) -> float:
     return float(np.max(np.abs(got - ref))) / den
 
 
-def forward_sampled(layer: OracleLayer, x_rows: np.ndarray, replay_rows: Optional[np.ndarray] = None) -> dict:
+def forward_sampled(layer: OracleLayer, x_rows: np.ndarray, replay_rows: Optional[np.ndarray] = None,
+                    workers: int = 1) -> dict:
     """Per-token evaluation of sampled tokens, in matrix form: route each token, then apply each
     used expert once to all sampled rows that selected it (no dispatch permutation, no shared
-    state between tokens beyond the expert weights).  Same values as ``forward_token``."""
+    state between tokens beyond the expert weights).  Same values as ``forward_token``.
+    ``workers`` > 1 evaluates the experts on that many threads (each expert's arithmetic is
+    unchanged; only the wall time differs)."""
     E, F = layer.E, layer.F
     z = O.moe_gate_logits(x_rows, layer.wg, layer.bias)
     idx, w, bad = route_or_replay(layer, z, replay_rows)
@@ -232,9 +235,19 @@ def forward_sampled(layer: OracleLayer, x_rows: np.ndarray, replay_rows: Optiona
         for j in range(idx.shape[1]):
             if idx[t, j] >= 0:
                 users.setdefault(int(idx[t, j]), []).append((t, j))
-    for e, lst in users.items():
+    def one_expert(item):
+        e, lst = item
         rows = np.array([t for t, _ in lst])
-        y_act = expert_ffn(layer.get(e), xq[rows], xs[rows], F, layer.act, layer.pow2)[5]
+        return expert_ffn(layer.get(e), xq[rows], xs[rows], F, layer.act, layer.pow2)[5]
+
+    items = list(users.items())
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            results = list(ex.map(one_expert, items))
+    else:
+        results = [one_expert(it) for it in items]
+    for (e, lst), y_act in zip(items, results):
         for (t, j), yr in zip(lst, y_act):
             ys[(t, j)] = yr
     out = np.zeros((n, H), np.float64)

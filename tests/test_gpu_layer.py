@@ -114,6 +114,84 @@ def test_layer_deterministic_and_chunk_concatenation():
     assert torch.equal(torch.cat([a0, a1]).view(torch.int16), both.view(torch.int16))
 
 
+def test_layer_longctx_chunk_concatenation():
+    """The long-context layer: one 16384-token call is bitwise two 8192-token calls (every kernel
+    is row-local and the expert GEMMs' accumulation order does not depend on the group sizes)."""
+    cfg = synth.CONFIGS["longctx"]
+    gw = gpu_weights(cfg)
+    x = torch.cat([synth.make_x(cfg, DEV, chunk=0), synth.make_x(cfg, DEV, chunk=1)])
+    l1 = MoELayer(gw, cfg.T, _act(cfg))
+    a0 = l1.forward(x[:cfg.T]).clone()
+    a1 = l1.forward(x[cfg.T:]).clone()
+    del l1
+    l2 = MoELayer(gw, 2 * cfg.T, _act(cfg))
+    both = l2.forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([a0, a1]).view(torch.int16), both.view(torch.int16))
+    del l2, gw, x, both
+    _free()
+
+
+def _edge_payload(cfg, seed):
+    """A routing payload [k, T] for router replay: slot 0 is expert 0 for every token but 7, 8
+    and 9 (so group 0 has T - 3 rows and a ragged last tile), token 5 alone takes expert 1 (a
+    1-row group), nobody takes expert 2 (an empty group); the other slots are distinct random
+    experts from 3..E-1.  Returns (payload int32 [k, T], the 32 sampled tokens), the sampled
+    tokens' other slots drawn from experts 3..14 so that the oracle evaluates few experts."""
+    T, E, k = cfg.T, cfg.E, cfg.k
+    rng = np.random.default_rng(seed)
+    idx = np.empty((T, k), np.int32)
+    idx[:, 0] = 0
+    keys = rng.random((T, E - 3))
+    idx[:, 1:] = np.argsort(keys, axis=1)[:, :k - 1] + 3
+    fixed = [0, 1, 2, 3, 5, 7, 8, 9, T // 2, T // 2 + 1, T - 300, T - 3, T - 2, T - 1]
+    others = rng.choice(np.setdiff1d(np.arange(T), fixed), 32 - len(fixed), replace=False)
+    toks = np.array(sorted(set(fixed) | set(int(t) for t in others)))
+    pool = np.arange(3, 15)
+    for t in toks:
+        idx[t, 1:] = rng.choice(pool, k - 1, replace=False)
+    idx[5, 1] = 1
+    for t in (7, 8, 9):
+        idx[t, 0] = [e for e in pool if e not in idx[t, 1:]][0]
+    return np.ascontiguousarray(idx.T), toks
+
+
+@pytest.mark.parametrize("name", ["prefill", "longctx"])
+def test_layer_replayed_edge_groups_32_tokens(name):
+    """The full-size layer on a crafted replay payload (largest possible group with a ragged last
+    tile, a 1-row group, an empty group): 32 sampled tokens, among them the 1-row group's token and
+    rows in the first, a middle and the ragged last tile of the largest group, match the oracle:
+    indices, weights and activation codes bit for bit, outputs within the tolerance."""
+    cfg = synth.CONFIGS[name]
+    T, k = cfg.T, cfg.k
+    pay, toks = _edge_payload(cfg, cfg.seed + 99)
+    gw = gpu_weights(cfg)
+    lay = MoELayer(gw, T, _act(cfg))
+    x = synth.make_x(cfg, DEV, chunk=7)
+    out = lay.forward(x, replay=torch.from_numpy(pay).to(DEV))
+    torch.cuda.synchronize()
+    assert int(lay.bad.item()) == 0
+    counts = host(lay.disp.counts)
+    assert counts[0] == T - 3 and counts[1] == 1 and counts[2] == 0
+    tile = lay.plan.tile_rows
+    assert (T - 3) % tile != 0
+    dest = host(lay.disp.dest_row).reshape(T, k)
+    off0 = int(host(lay.disp.offsets)[0])
+    last_tile0 = ((T - 3) // tile) * tile
+    assert sum(1 for t in toks if t not in (7, 8, 9) and dest[t, 0] - off0 >= last_tile0) >= 3
+    ol = oracle_layer(cfg)
+    r = L.forward_sampled(ol, rows_host(x, toks), replay_rows=np.ascontiguousarray(pay[:, toks]), workers=8)
+    assert_equal("idx", rows_host(lay.idx, toks), r["idx"])
+    assert_equal("w", rows_host(lay.wts, toks), r["w"])
+    assert_equal("xq", rows_host(lay.xq, toks), r["xq"])
+    assert_equal("xs", rows_host(lay.xs, toks), r["xs"])
+    err = rel_err(rows_host(out, toks), r["out"])
+    print(f"{name}: 32 tokens over edge groups (tile {tile}): output err {err:.3e}")
+    assert err < TOL
+    del lay, gw, x, out
+    _free()
+
+
 @pytest.mark.parametrize("name", ["prefill", "longctx"])
 def test_layer_tile_heights_bitwise(name):
     """The expert GEMMs at 128- and 256-row tiles: the accumulation order of every output does not
@@ -203,18 +281,22 @@ def test_layer_graph_replay_matches_eager(name):
     _free()
 
 
-def test_r3_stack_record_replay():
+R3_TOKENS = 16
+
+
+@pytest.fixture(scope="module")
+def r3_stack():
     """The prefill layer 4 deep at 32768 tokens: pass A routes with W and records the
     [num_layers, top_k, seq_len] payload; pass B replays it on W' = W + N(0, 1e-3); pass C
-    recomputes the routing on W'.  Replayed indices equal the payload exactly, pass B's
-    counts / offsets / permutation equal pass A's, and layer 0 of passes A and B matches the
-    oracle on sampled tokens."""
+    recomputes the routing on W'.  Whole-batch facts are checked here; for 16 sampled tokens every
+    layer's input rows, indices, weights and output rows are kept for the oracle."""
     cfg = synth.CONFIGS["r3"]
     T, k, Lyr = cfg.T, cfg.k, cfg.layers
     act = _act(cfg)
+    toks = synth.sample_tokens(T, R3_TOKENS, cfg.seed)
     payload = torch.full((Lyr, k, T), -1, dtype=torch.int32, device=DEV)
     x0 = synth.make_x(cfg, DEV)
-    keep = {}
+    keep, rows = {}, {}
     stats = []
     for pas in ("A", "B", "C"):
         x = x0
@@ -242,33 +324,55 @@ def test_r3_stack_record_replay():
                 slot = (idx != ia).float().mean().item()
                 setd = 1.0 - (idx[:, :, None] == ia[:, None, :]).any(-1).float().mean().item()
                 stats.append((slot, setd))
-            if l == 0:
-                keep[(pas, "x0out")] = out.clone()
-                keep[(pas, "w0")] = lay.wts.clone()
+            if pas in ("A", "B"):
+                rows[(pas, l)] = dict(x=rows_host(x, toks), idx=rows_host(idx, toks), w=rows_host(lay.wts, toks),
+                                      out=rows_host(out, toks),
+                                      replay=np.ascontiguousarray(host(payload[l])[:, toks]))
             x = (x.float() + out.float()).to(act)
             del lay, gw
             _free()
         keep[(pas, "final")] = x
-    # recomputing the routing on W' moves slots (that is what replay prevents); report it
+    res = dict(cfg=cfg, toks=toks, rows=rows, stats=stats,
+               dB=rel_err(host(keep[("B", "final")]), host(keep[("A", "final")])),
+               dC=rel_err(host(keep[("C", "final")]), host(keep[("A", "final")])))
+    del keep, payload, x0
+    _free()
+    return res
+
+
+def test_r3_stack_record_replay(r3_stack):
+    """Replay reproduces the recorded routing and dispatch at every layer (checked while the
+    stack runs); recomputing the routing on W' moves slots, which is what replay prevents."""
+    stats = r3_stack["stats"]
     print("pass C vs pass A per layer (slot drift, expert-set drift):",
           [f"({a:.4f}, {b:.4f})" for a, b in stats])
+    assert len(stats) == r3_stack["cfg"].layers
     assert all(0.0 < b <= a < 1.0 for a, b in stats)
-    dB = rel_err(host(keep[("B", "final")]), host(keep[("A", "final")]))
-    dC = rel_err(host(keep[("C", "final")]), host(keep[("A", "final")]))
-    print(f"stack output rel diff: B vs A {dB:.3e}, C vs A {dC:.3e}")
-    # oracle: layer 0, pass A (route + record) and pass B (replay on W') on sampled tokens
-    toks = synth.sample_tokens(T, 2, cfg.seed)
-    xr = rows_host(x0, toks)
-    olA = oracle_layer(cfg, 0)
-    rA = L.forward_sampled(olA, xr)
-    assert_equal("pass A idx", rows_host(keep[("A", 0)][0], toks), rA["idx"])
-    assert_equal("pass A w", rows_host(keep[("A", "w0")], toks), rA["w"])
-    assert rel_err(rows_host(keep[("A", "x0out")], toks), rA["out"]) < TOL
-    olB = oracle_layer(cfg, 0, perturbed=True)
-    rB = L.forward_sampled(olB, xr, replay_rows=np.ascontiguousarray(rA["idx"].T))
-    assert_equal("pass B idx", rows_host(keep[("A", 0)][0], toks), rB["idx"])
-    assert_equal("pass B w", rows_host(keep[("B", "w0")], toks), rB["w"])
-    assert rel_err(rows_host(keep[("B", "x0out")], toks), rB["out"]) < TOL
+    print(f"stack output rel diff: B vs A {r3_stack['dB']:.3e}, C vs A {r3_stack['dC']:.3e}")
+    assert r3_stack["dB"] < r3_stack["dC"]
+
+
+@pytest.mark.parametrize("layer", [0, 1, 2, 3])
+def test_r3_stack_layer_parity(r3_stack, layer):
+    """Every layer of the stack on 16 sampled tokens, from the stack's own inputs at that layer:
+    pass A (route with W, record) and pass B (replay the record on W') against the oracle -
+    indices and weights bit for bit, outputs within the tolerance."""
+    cfg = r3_stack["cfg"]
+    a, b = r3_stack["rows"][("A", layer)], r3_stack["rows"][("B", layer)]
+    olA = oracle_layer(cfg, layer)
+    rA = L.forward_sampled(olA, a["x"], workers=8)
+    assert_equal(f"layer {layer} pass A idx", a["idx"], rA["idx"])
+    assert_equal(f"layer {layer} pass A w", a["w"], rA["w"])
+    assert_equal(f"layer {layer} record", a["replay"], np.ascontiguousarray(rA["idx"].T))
+    errA = rel_err(a["out"], rA["out"])
+    del olA
+    olB = oracle_layer(cfg, layer, perturbed=True)
+    rB = L.forward_sampled(olB, b["x"], replay_rows=a["replay"], workers=8)
+    assert_equal(f"layer {layer} pass B idx", b["idx"], rB["idx"])
+    assert_equal(f"layer {layer} pass B w", b["w"], rB["w"])
+    errB = rel_err(b["out"], rB["out"])
+    print(f"layer {layer}: {len(r3_stack['toks'])} tokens, output err pass A {errA:.3e} pass B {errB:.3e}")
+    assert errA < TOL and errB < TOL
 
 
 @pytest.mark.parametrize("layer", [1, 2, 3])

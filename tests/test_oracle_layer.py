@@ -207,6 +207,21 @@ def test_forward_sampled_equals_token_and_dispatch(name, pow2):
         assert L.rel_err(wrong["out"], full["out"][pick]) > 1e-6
 
 
+def test_forward_sampled_threaded_experts_same_bits():
+    """Evaluating the experts on several threads changes nothing: every output bit equals the
+    one-thread evaluation (routed and replayed)."""
+    cfg = SMALL["prefill_small"]
+    lay = oracle_layer(cfg)
+    x = x_f32(cfg)
+    pick = np.array([0, 3, 8, cfg.T // 2, cfg.T - 1])
+    one = L.forward_sampled(lay, x[pick])
+    many = L.forward_sampled(lay, x[pick], workers=4)
+    for key in ("idx", "w", "xq", "xs", "out"):
+        assert _same_bits(one[key], many[key]), key
+    rep = np.ascontiguousarray(one["idx"].T)
+    assert _same_bits(L.forward_sampled(lay, x[pick], replay_rows=rep, workers=3)["out"], one["out"])
+
+
 def test_forward_sampled_replayed_rows_on_perturbed_weights():
     cfg = SMALL["prefill_small"]
     lay = oracle_layer(cfg)
