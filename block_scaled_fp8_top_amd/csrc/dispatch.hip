@@ -9,7 +9,8 @@
 //               same expert find each other with ballots over the bits of the expert id, so each
 //               slot's row is (chunk base) + (earlier slots of the chunk with that expert) --
 //               exactly the stable order.  Also fills the shared expert's rows.
-//   4. permute: rows [0, offsets[G]) copy xq[src_token[row]] and xs[src_token[row]].
+//   4. permute: rows [0, offsets[G]) copy xq[src_token[row]] and xs[src_token[row]] (the scales
+//               alone when the codes are gathered by the GEMM).
 //
 // Small batches (decode: up to SMALL_MAX slots) run steps 1-3 in one workgroup instead
 // (small_dispatch_kernel), which gives the same stable order.
@@ -162,6 +163,32 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint8_t* __restrict_
     }
     const int nsc = H / 128;
     for (int c = lane; c < nsc; c += 64) as[row * nsc + c] = xs[t * nsc + c];
+  }
+}
+
+// Scales only (the grouped GEMM gathers the codes through src_token): 16 lanes per row, 16-byte
+// pieces (H % 512 == 0, so a row's H/128 scales are whole pieces), 4 rows per wavefront, and each
+// lane's source rows looked up before any copy, so several rows' loads are in flight at once.
+constexpr int PS_ROWS = 4;   // rows per 16-lane group
+__global__ __launch_bounds__(256) void permute_scales_kernel(const float* __restrict__ xs, int H,
+                                                             const int32_t* __restrict__ src_token,
+                                                             const int32_t* __restrict__ total_rows, int64_t max_rows,
+                                                             float* __restrict__ as) {
+  const int64_t rows = min((int64_t)*total_rows, max_rows);
+  const int sub = threadIdx.x & 15;
+  const int np = H / 512;   // 16-byte pieces per row
+  const int64_t r0 = ((int64_t)blockIdx.x * 16 + threadIdx.x / 16) * PS_ROWS;
+  int64_t t[PS_ROWS];
+#pragma unroll
+  for (int i = 0; i < PS_ROWS; ++i) t[i] = r0 + i < rows ? src_token[r0 + i] : -1;
+  for (int c = sub; c < np; c += 16) {
+    float4 v[PS_ROWS];
+#pragma unroll
+    for (int i = 0; i < PS_ROWS; ++i)
+      if (t[i] >= 0) v[i] = reinterpret_cast<const float4*>(xs + t[i] * (H / 128))[c];
+#pragma unroll
+    for (int i = 0; i < PS_ROWS; ++i)
+      if (t[i] >= 0) reinterpret_cast<float4*>(as + (r0 + i) * (H / 128))[c] = v[i];
   }
 }
 
@@ -370,8 +397,13 @@ int dispatch_impl(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int3
   if (copy_rows && T > 0) {
     const int G = E + (append_shared ? 1 : 0);
     const int64_t max_rows = nslots + (append_shared ? T : 0);
-    const int64_t grid = std::min<int64_t>(ceil_div64(max_rows, 4), 65536);
-    permute_kernel<<<(unsigned)grid, 256, 0, st>>>(xq, xs, H, src_token, offsets + G, max_rows, aq, as);
+    if (!aq && H % 512 == 0 && ceil_div64(max_rows, 16 * PS_ROWS) <= INT32_MAX) {
+      const int64_t grid = ceil_div64(max_rows, 16 * PS_ROWS);
+      permute_scales_kernel<<<(unsigned)grid, 256, 0, st>>>(xs, H, src_token, offsets + G, max_rows, as);
+    } else {
+      const int64_t grid = std::min<int64_t>(ceil_div64(max_rows, 4), 65536);
+      permute_kernel<<<(unsigned)grid, 256, 0, st>>>(xq, xs, H, src_token, offsets + G, max_rows, aq, as);
+    }
     MOE_CHECK_LAUNCH();
   }
   return MOE_OK;

@@ -358,8 +358,28 @@ def test_dispatch(name):
     # index-only mode
     d2 = M.moe_dispatch(torch.from_numpy(idx).to(DEV), E, cfg.shared)
     assert_equal("dest_row (index only)", host(d2.dest_row), od)
-    del xq, xs, d, d2
+    # scales-only mode (the GEMM gathers the codes): every row's scales
+    d3 = M.moe_dispatch(torch.from_numpy(idx).to(DEV), E, cfg.shared, xq, xs, copy_codes=False)
+    assert d3.aq is None
+    assert_equal("as rows (scales only)", host(d3.as_)[:nrows], O.permute_rows(xsh, osrc))
+    del xq, xs, d, d2, d3
     _cleanup()
+
+
+@pytest.mark.parametrize("H", [128, 384, 512, 1536, 6144])
+@pytest.mark.parametrize("T", [1, 61, 1000])
+def test_dispatch_scales_only_ragged(H, T):
+    """Scales-only permutation on row counts that are not multiples of a workgroup's rows and
+    scale rows of 1..48 floats (whole 16-byte pieces or not), with the shared expert appended."""
+    E, k = 64, 6
+    rng = np.random.default_rng(H + T)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    xs = synth.random_scales((T, H // 128), 7, 42, device=DEV)
+    xq = synth.random_codes((T, H), 7, 43, device=DEV)
+    d = M.moe_dispatch(torch.from_numpy(idx).to(DEV), E, True, xq, xs, copy_codes=False)
+    _, oo, _, osrc = O.moe_dispatch(idx, E, True)
+    nrows = int(oo[-1])
+    assert_equal("as rows", host(d.as_)[:nrows], O.permute_rows(host(xs), osrc))
 
 
 def test_dispatch_all_one_expert_and_tiny():
