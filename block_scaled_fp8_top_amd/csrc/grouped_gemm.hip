@@ -726,7 +726,7 @@ int64_t max_tiles_for(int64_t max_rows, int groups, int bm) { return ceil_div64(
 // a 128-row tile; measured on the prefill layer: GEMM1 5.46 -> 5.18 ms, GEMM2 2.99 -> 2.73 ms).
 int auto_tile_rows(int64_t max_rows, int groups) {
   const int64_t avg2 = 2 * ceil_div64(max_rows, groups);
-  return avg2 <= 32 ? 32 : avg2 <= 48 ? 48 : avg2 <= 64 ? 64 : avg2 <= 512 ? 128 : 256;
+  return avg2 <= 32 ? 32 : avg2 <= 48 ? 48 : avg2 <= 64 ? 64 : avg2 < 512 ? 128 : 256;
 }
 bool valid_tile_rows(int bm) { return bm == 32 || bm == 48 || bm == 64 || bm == 128 || bm == 256; }
 

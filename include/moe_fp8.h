@@ -231,7 +231,7 @@ size_t moe_packed_weight_bytes(int32_t groups, int32_t N, int32_t K, int32_t epi
  *            quantises h with power-of-two scales too)
  *   tile_rows: rows per workgroup tile, 32, 48, 64, 128 or 256 (256: packed weights only), or 0 to
  *            choose from the group sizes: the smallest of 32, 48, 64, 128 at or above
- *            2 * ceil(max_rows / groups), and 256 above 512 when the weights are packed.  The result
+ *            2 * ceil(max_rows / groups), and 256 from 512 on when the weights are packed.  The result
  *            is the same for every height.
  *   Rows beyond offsets[groups] are not written.  workspace >= moe_workspace_bytes(MOE_OP_GROUPED_GEMM,
  *   max_rows, 0, groups, N, K).

@@ -158,8 +158,9 @@ def test_gemm_plan_validation(L):
     assert L.moe_grouped_gemm_plan(P, 4, 0, 0, None, 0, ctypes.byref(plan), None) == OK          # nothing to plan
     assert plan.tile_rows == 32 and plan.groups == 4 and plan.max_rows == 0
     # automatic tile height: the smallest of 32/48/64/128 holding twice the average group, 256 for
-    # groups averaging more than 256 rows
-    for rows, groups, tr in ((100, 8, 32), (1536, 64, 48), (2000, 64, 64), (65536, 256, 128), (147456, 257, 256)):
+    # groups averaging 256 rows or more
+    for rows, groups, tr in ((100, 8, 32), (1536, 64, 48), (2000, 64, 64), (65280, 256, 128), (65536, 256, 256),
+                             (147456, 257, 256)):
         L.moe_grouped_gemm_plan(P, groups, rows, 0, None, 0, ctypes.byref(plan), None)
         assert plan.tile_rows == tr, (rows, groups, plan.tile_rows)
     planned = lambda N=256, K=256, epi=0, od=1, bl=0, pl=True, sm=0: (
