@@ -202,8 +202,10 @@ constexpr int SMALL_CNT = 16384;      // (64-slot pieces) x experts counters in 
 // into running bases (pieces in order), a block scan gives the expert offsets, and every slot's
 // row is offset + piece base + rank: the stable order.
 // With tiles != NULL the same workgroup also writes the grouped GEMM's tile list for row tiles of
-// bm (the entries the plan kernel of the grouped GEMM writes: {group, first row, the group's first
-// tile, the group's tile count}, at most max_tiles of them, and their number into *ntiles).
+// bm (the entries the plan kernel of the grouped GEMM writes: {group, first row, the block's first
+// tile, the block's tile count}, at most max_tiles of them, and their number into *ntiles), and
+// with second != 0 the second list at tiles + second (every group's full tiles first, then the
+// groups' short last tiles), as the plan kernel does.
 template <int BITS>
 __global__ __launch_bounds__(1024) void small_dispatch_kernel(const int32_t* __restrict__ idx, int nslots, int k, int E,
                                                               int T, int append_shared, int32_t* __restrict__ counts,
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(1024) void small_dispatch_kernel(const int32_t* __r
                                                               int32_t* __restrict__ dest_row,
                                                               int32_t* __restrict__ src_token, int bm,
                                                               int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
-                                                              int max_tiles) {
+                                                              int max_tiles, int second) {
   __shared__ int sidx[SMALL_MAX];
   __shared__ uint8_t srank[SMALL_MAX];
   __shared__ int cnt[SMALL_CNT];      // [piece][e]
@@ -288,30 +290,53 @@ __global__ __launch_bounds__(1024) void small_dispatch_kernel(const int32_t* __r
   // every thread writes tiles, finding a tile's group by binary search over the first tiles
   const int G = E + (append_shared ? 1 : 0);
   const int rows_g = tid < E ? total : (tid == E && append_shared ? T : 0);
-  const int nt = (rows_g + bm - 1) / bm;
-  tpart[tid] = nt;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int v = tid >= o ? tpart[tid - o] : 0;
+  // first[0 .. G]: exclusive block scan over the groups of v (this thread's group's count)
+  auto scan_first = [&](int v) {
+    tpart[tid] = v;
     __syncthreads();
-    tpart[tid] += v;
+    for (int o = 1; o < 1024; o <<= 1) {
+      const int u = tid >= o ? tpart[tid - o] : 0;
+      __syncthreads();
+      tpart[tid] += u;
+      __syncthreads();
+    }
+    if (tid < G) first[tid] = tpart[tid] - v;
+    if (tid == 0) first[G] = tpart[G - 1];
     __syncthreads();
-  }
-  if (tid < G) first[tid] = tpart[tid] - nt;
-  if (tid == 0) first[G] = tpart[G - 1];
-  __syncthreads();
-  const int ntot = min(first[G], max_tiles);
-  for (int t = tid; t < ntot; t += 1024) {
+  };
+  // the group owning position t: the last group whose first position is at or before t
+  auto owner = [&](int t) {
     int lo = 0, hi = G - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (first[mid] <= t) lo = mid;
       else hi = mid - 1;
     }
-    const int off = lo < E ? (lo == 0 ? 0 : part[lo - 1]) : routed;
-    tiles[t] = make_int4(lo, off + (t - first[lo]) * bm, first[lo], first[lo + 1] - first[lo]);
+    return lo;
+  };
+  auto row_of = [&](int g) { return g < E ? (g == 0 ? 0 : part[g - 1]) : routed; };
+  scan_first((rows_g + bm - 1) / bm);
+  const int ntot = min(first[G], max_tiles);
+  for (int t = tid; t < ntot; t += 1024) {
+    const int lo = owner(t);
+    tiles[t] = make_int4(lo, row_of(lo) + (t - first[lo]) * bm, first[lo], first[lo + 1] - first[lo]);
   }
   if (tid == 0) *ntiles = ntot;
+  if (!second) return;
+  __syncthreads();
+  scan_first(rows_g / bm);                       // full tiles first
+  const int nfull = first[G];
+  for (int t = tid; t < min(nfull, ntot); t += 1024) {
+    const int lo = owner(t);
+    tiles[second + t] = make_int4(lo, row_of(lo) + (t - first[lo]) * bm, first[lo], first[lo + 1] - first[lo]);
+  }
+  __syncthreads();
+  scan_first(rows_g % bm != 0 ? 1 : 0);          // then every group's short last tile
+  for (int t = nfull + tid; t < ntot; t += 1024) {
+    const int lo = owner(t - nfull);
+    const int g_rows = lo < E ? row_of(lo + 1) - row_of(lo) : T;
+    tiles[second + t] = make_int4(lo, row_of(lo) + (g_rows / bm) * bm, t, 1);
+  }
 }
 
 int64_t nchunks_for(int64_t T, int k) { return ceil_div64(T * k, CHUNK); }
@@ -322,6 +347,7 @@ size_t moe_dispatch_workspace(int64_t T, int32_t k, int32_t E) {
   return (size_t)(2 * nchunks_for(T, k) * (int64_t)E * 4 + 256);
 }
 
+int64_t moe_plan_second_list(int64_t max_rows, int groups, int bm);
 int moe_plan_host(int32_t groups, int64_t max_rows, int32_t tile_rows, void* workspace, size_t workspace_bytes,
                   moe_gemm_plan* plan, int64_t* max_tiles);
 
@@ -355,12 +381,14 @@ int dispatch_impl(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int3
     const bool plan_here = plan_ws && E + (append_shared ? 1 : 0) <= 1024 && plan_max_tiles <= INT32_MAX;
     int4* ptiles = plan_here ? reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan_ws) + 256) : nullptr;
     int32_t* pntiles = plan_here ? reinterpret_cast<int32_t*>(plan_ws) : nullptr;
+    const int64_t second = plan_here ? moe_plan_second_list(nslots + (append_shared ? T : 0),
+                                                            E + (append_shared ? 1 : 0), plan_bm) : 0;
     switch (bits) {
 #define CASE_SMALL(B)                                                                                   \
   case B:                                                                                               \
     small_dispatch_kernel<B><<<1, 1024, 0, st>>>(topk_idx, (int)nslots, k, E, (int)T, append_shared, counts, \
                                                  offsets, dest_row, src_token, plan_bm, ptiles, pntiles, \
-                                                 (int)plan_max_tiles);                                   \
+                                                 (int)plan_max_tiles, (int)second);                      \
     break;
       CASE_SMALL(1) CASE_SMALL(2) CASE_SMALL(3) CASE_SMALL(4) CASE_SMALL(5)
       CASE_SMALL(6) CASE_SMALL(7) CASE_SMALL(8) CASE_SMALL(9) CASE_SMALL(10)

@@ -158,19 +158,16 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __rest
 // A block scan gives each group's first tile; then every thread writes tiles (each finds its group
 // by binary search over the first tiles), so a long group's tiles are not written by one thread.
 constexpr int TILE_MAP_MAXG = 4096;
-__global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restrict__ offsets, int groups, int bm,
-                                                        int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
-                                                        int max_tiles) {
-  __shared__ int part[1024];
-  __shared__ int first[TILE_MAP_MAXG + 1];   // first[g] = tiles before group g; first[groups] = all
-  __shared__ int carry;
-  if (threadIdx.x == 0) carry = 0;
+// exclusive prefix over the groups of cnt(g) into dst[0 .. groups] (dst[groups] = total), in
+// chunks of 1024 groups; every thread of the workgroup calls it
+template <typename F>
+__device__ __forceinline__ void group_prefix(int groups, F cnt, int* dst, int* part, int* carry) {
+  if (threadIdx.x == 0) *carry = 0;
   __syncthreads();
   for (int g0 = 0; g0 < groups; g0 += 1024) {
     const int g = g0 + threadIdx.x;
-    int nt = 0;
-    if (g < groups) nt = (offsets[g + 1] - offsets[g] + bm - 1) / bm;
-    part[threadIdx.x] = nt;
+    const int n = g < groups ? cnt(g) : 0;
+    part[threadIdx.x] = n;
     __syncthreads();
     for (int o = 1; o < 1024; o <<= 1) {
       const int v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
@@ -178,27 +175,63 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
       part[threadIdx.x] += v;
       __syncthreads();
     }
-    if (g < groups) first[g] = carry + part[threadIdx.x] - nt;
+    if (g < groups) dst[g] = *carry + part[threadIdx.x] - n;
     __syncthreads();
-    if (threadIdx.x == 1023) carry += part[1023];
+    if (threadIdx.x == 1023) *carry += part[1023];
     __syncthreads();
   }
-  if (threadIdx.x == 0) first[groups] = carry;
+  if (threadIdx.x == 0) dst[groups] = *carry;
   __syncthreads();
-  const int total = min(carry, max_tiles);
+}
+
+// the group owning list position t: the last group whose first position is at or before t (a
+// group with no positions shares its first position with the next, so the last one owns t)
+__device__ __forceinline__ int owner(const int* first, int groups, int t) {
+  int lo = 0, hi = groups - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (first[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// The tile list: group g's ceil(rows_g / bm) tiles, groups in order; entry {group, first row, first
+// tile of the unit-order block, tiles in the block}, the block being the group's tiles.  With
+// second != 0 a second list at tiles + second holds the same tiles with every group's full tiles
+// first (block: the group's full tiles) and then each group's short last tile (a block of its
+// own): the SwiGLU GEMM runs in that order (see run_planned).
+__global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restrict__ offsets, int groups, int bm,
+                                                        int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                                        int max_tiles, int second) {
+  __shared__ int part[1024];
+  __shared__ int first[TILE_MAP_MAXG + 1];   // first[g] = tiles before group g; first[groups] = all
+  __shared__ int carry;
+  group_prefix(groups, [&](int g) { return (offsets[g + 1] - offsets[g] + bm - 1) / bm; }, first, part, &carry);
+  const int total = min(first[groups], max_tiles);
   for (int t = threadIdx.x; t < total; t += 1024) {
-    // the last group whose first tile is at or before t (empty groups share their first tile
-    // with the next group, so the last such group is the one that owns t)
-    int lo = 0, hi = groups - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (first[mid] <= t) lo = mid;
-      else hi = mid - 1;
-    }
+    const int lo = owner(first, groups, t);
     const int i = t - first[lo];
     tiles[t] = make_int4(lo, offsets[lo] + i * bm, first[lo], first[lo + 1] - first[lo]);
   }
   if (threadIdx.x == 0) *ntiles = total;
+  if (!second) return;
+  __syncthreads();
+  // full tiles: first[] becomes the full-tile prefix; short tiles follow all of them
+  group_prefix(groups, [&](int g) { return (offsets[g + 1] - offsets[g]) / bm; }, first, part, &carry);
+  const int nfull = first[groups];
+  for (int t = threadIdx.x; t < min(nfull, total); t += 1024) {
+    const int lo = owner(first, groups, t);
+    const int i = t - first[lo];
+    tiles[second + t] = make_int4(lo, offsets[lo] + i * bm, first[lo], first[lo + 1] - first[lo]);
+  }
+  __syncthreads();
+  group_prefix(groups, [&](int g) { return (offsets[g + 1] - offsets[g]) % bm != 0 ? 1 : 0; }, first, part, &carry);
+  for (int t = nfull + threadIdx.x; t < total; t += 1024) {
+    const int lo = owner(first, groups, t - nfull);
+    const int nf = (offsets[lo + 1] - offsets[lo]) / bm;
+    tiles[second + t] = make_int4(lo, offsets[lo] + nf * bm, t, 1);
+  }
 }
 
 // wait until at most n of this wave's vector memory instructions are outstanding (n is
@@ -250,7 +283,7 @@ __device__ __forceinline__ Unit unit_at(int u, int ny, const int4* __restrict__ 
   Unit res;
   res.nt = nt;
   res.g = tq.x;
-  res.row0 = offsets[res.g] + tile * bm;
+  res.row0 = tq.y + (tile - (q - tq.z)) * bm;   // tq.y: tile q's own first row
   res.row_end = min(res.row0 + bm, offsets[res.g + 1]);
   return res;
 }
@@ -719,6 +752,23 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
 
 int64_t max_tiles_for(int64_t max_rows, int groups, int bm) { return ceil_div64(max_rows, bm) + groups; }
 
+}  // namespace
+
+// Where the plan's second tile list (full tiles first) starts, in tiles from the first list, or 0
+// when there is none.  It is written for tiles of 128 and 256 rows, when it fits in the plan
+// workspace beside the first list.  A group's short last tile skips its padded wave rows and ends
+// early; in group order, the workgroups that share its weight panels then drift apart by more K
+// steps than an XCD's L2 holds, and the panels come again from beyond the L2.  With every full
+// tile first, the units of a round take equal time.  Measured on the SwiGLU GEMM: beyond-L2 fetch
+// at prefill 18.4 -> 14.4 GB, time -2% at prefill and -4% on the long-context chunk.  The store
+// GEMM (shorter K) measured 2-3% slower in that order and keeps the first list.
+int64_t moe_plan_second_list(int64_t max_rows, int groups, int bm) {
+  const int64_t mt = max_tiles_for(max_rows, groups, bm);
+  return bm >= 128 && 2 * mt <= max_tiles_for(max_rows, groups, MIN_BM) ? mt : 0;
+}
+
+namespace {
+
 // Row-tile height when the caller leaves it open: the smallest height that holds twice the
 // average group, so that few groups need a second tile (which streams the same weight panel
 // again); short groups then stream weights through 32- or 64-row tiles, long ones use 128.
@@ -888,7 +938,8 @@ extern "C" int moe_grouped_gemm_plan(const int32_t* offsets, int32_t groups, int
   const int bm = plan->tile_rows;
   int4* tiles = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(workspace) + 256);
   int32_t* ntiles = reinterpret_cast<int32_t*>(workspace);
-  tile_map_kernel<<<1, 1024, 0, as_stream(stream)>>>(offsets, groups, bm, tiles, ntiles, (int)mt);
+  tile_map_kernel<<<1, 1024, 0, as_stream(stream)>>>(offsets, groups, bm, tiles, ntiles, (int)mt,
+                                                    (int)moe_plan_second_list(max_rows, groups, bm));
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -917,6 +968,7 @@ int run_planned(const moe_gemm_plan* plan, const uint8_t* a, const int32_t* a_ro
   const int64_t nwg = mt * ny;
   if (nwg > INT32_MAX) return MOE_ERR_SHAPE;
   const int4* tiles = reinterpret_cast<const int4*>(reinterpret_cast<const uint8_t*>(plan->workspace) + 256);
+  if (epilogue == MOE_EPI_SWIGLU_QUANT) tiles += moe_plan_second_list(max_rows, groups, bm);   // full tiles first
   const int32_t* ntiles = reinterpret_cast<const int32_t*>(plan->workspace);
   const int cus = compute_units();
   if (cus <= 0) return MOE_ERR_HIP;

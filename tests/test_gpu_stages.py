@@ -413,7 +413,8 @@ def test_dispatch_small_and_chunked_paths(T, k, E):
 
 @pytest.mark.parametrize("T,k,E,shared", [(256, 6, 64, False), (96, 8, 32, True), (1, 8, 256, True),
                                            (0, 6, 64, False), (2048, 8, 256, True),
-                                           (3, 2, 1023, True), (4, 2, 1024, True)])   # G = 1024, 1025
+                                           (3, 2, 1023, True), (4, 2, 1024, True),    # G = 1024, 1025
+                                           (1024, 8, 16, True), (1000, 8, 24, False)])  # one workgroup, both lists
 def test_dispatch_plan_equals_separate_plan(T, k, E, shared):
     """moe_dispatch_plan: the same dispatch outputs as moe_dispatch and the same tile list (every
     entry and the count) as moe_grouped_gemm_plan, for each tile height; the one-workgroup path
@@ -426,7 +427,7 @@ def test_dispatch_plan_equals_separate_plan(T, k, E, shared):
     G = E + (1 if shared else 0)
     max_rows = T * k + (T if shared else 0)
     ref = M.moe_dispatch(idx, E, shared, xq, xs, copy_codes=False)
-    for tile in (0, 32, 48, 64, 128):
+    for tile in (0, 32, 48, 64, 128, 256):
         out = M.moe_dispatch(idx, E, shared, xq, xs, copy_codes=False)   # fresh buffers of the same shape
         for t_ in (out.counts, out.offsets, out.dest_row, out.src_token, out.as_):
             t_.fill_(-9)
@@ -448,6 +449,39 @@ def test_dispatch_plan_equals_separate_plan(T, k, E, shared):
         nt = int(host(gws2[:4].view(torch.int32))[0])
         assert int(host(gws[:4].view(torch.int32))[0]) == nt
         assert_equal(f"tiles tile {tile}", host(gws[256:256 + 16 * nt]), host(gws2[256:256 + 16 * nt]))
+        # both lists against their definition: group order, and (128- and 256-row tiles, when the
+        # workspace holds it) every group's full tiles first, then the groups' short last tiles
+        l1, l2, second = _expected_tile_lists(host(ref.offsets), plan.tile_rows, max_rows, G)
+        assert nt == len(l1)
+        got1 = host(gws[256:256 + 16 * nt].view(torch.int32)).reshape(-1, 4)
+        assert_equal(f"list 1 tile {tile}", got1, np.array(l1, np.int32).reshape(-1, 4))
+        if second:
+            for w in (gws, gws2):
+                got2 = host(w[256 + 16 * second:256 + 16 * (second + nt)].view(torch.int32)).reshape(-1, 4)
+                assert_equal(f"list 2 tile {tile}", got2, np.array(l2, np.int32).reshape(-1, 4))
+
+
+def _expected_tile_lists(offsets, bm, max_rows, G):
+    """The grouped GEMM's tile lists from their definition: entries {group, first row, first tile of
+    the entry's block, tiles in the block}."""
+    rows = np.diff(offsets[:G + 1])
+    l1 = []
+    for g in range(G):
+        n = -(-int(rows[g]) // bm)
+        f = len(l1)
+        l1 += [(g, int(offsets[g]) + i * bm, f, n) for i in range(n)]
+    mt = -(-max_rows // bm) + G
+    second = mt if bm >= 128 and 2 * mt <= -(-max_rows // 32) + G else 0
+    l2 = []
+    if second:
+        for g in range(G):
+            n = int(rows[g]) // bm
+            f = len(l2)
+            l2 += [(g, int(offsets[g]) + i * bm, f, n) for i in range(n)]
+        for g in range(G):
+            if rows[g] % bm:
+                l2.append((g, int(offsets[g]) + (int(rows[g]) // bm) * bm, len(l2), 1))
+    return l1, l2, second
 
 
 @pytest.mark.parametrize("H", [128, 1152, 8192, 8320])
