@@ -101,6 +101,18 @@ __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3" ::"s"(lds_addr), "v"(voff), "s"(base),
                "i"(IMM) : "memory", "m0");
 }
+// The weight operand's DMA: with NT the loads carry the non-temporal hint.  Short tiles (decode)
+// read each weight panel for about one tile, so the stream should not displace reusable lines;
+// measured on the decode layer: GEMM1 138 -> 128 us, GEMM2 82 -> 78 us.  Taller tiles reuse a panel
+// across a group's tiles through the L2, where the hint measured 1-4% slower.
+template <int IMM, bool NT>
+__device__ __forceinline__ void dma16s_w(const void* base, uint32_t voff, uint32_t lds_addr) {
+  if (NT)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3 nt" ::"s"(lds_addr), "v"(voff),
+                 "s"(base), "i"(IMM) : "memory", "m0");
+  else
+    dma16s<IMM>(base, voff, lds_addr);
+}
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr), "v"(g) : "memory", "m0");
 }
@@ -306,6 +318,7 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   constexpr int A_BYTES = T::A_BYTES, B_BYTES = T::B_BYTES, AS_W = T::AS_W;
   constexpr int WROWS = MS * 16;   // rows per wave
   constexpr int D = NSTAGE - 1;    // DMA lookahead in K steps
+  constexpr bool W_NT = BM <= 64;  // non-temporal weight loads for the short (weight-streaming) tiles
   __shared__ __attribute__((aligned(1024))) uint8_t a_lds[NSTAGE][A_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t b_lds[NSTAGE][B_BYTES];
   __shared__ __attribute__((aligned(16))) float as_lds[4][AS_W];   // activation-scale ring: slot (step & 3)
@@ -414,16 +427,16 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     if (dma_wave) {                                                                       \
       if (PACKED) {                                                                       \
         _Pragma("unroll") for (int q_ = 0; q_ < BQ; ++q_) {                                \
-          dma16s<0>(bg + kob_, boff[q_], bo_ + 4096 * q_);                                \
-          dma16s<1024>(bg + kob_, boff[q_], bo_ + 4096 * q_);                             \
+          dma16s_w<0, W_NT>(bg + kob_, boff[q_], bo_ + 4096 * q_);                        \
+          dma16s_w<1024, W_NT>(bg + kob_, boff[q_], bo_ + 4096 * q_);                     \
           if (B_PW - 4 * q_ > 2) {                                                        \
-            dma16s<2048>(bg + kob_, boff[q_], bo_ + 4096 * q_);                           \
-            dma16s<3072>(bg + kob_, boff[q_], bo_ + 4096 * q_);                           \
+            dma16s_w<2048, W_NT>(bg + kob_, boff[q_], bo_ + 4096 * q_);                   \
+            dma16s_w<3072, W_NT>(bg + kob_, boff[q_], bo_ + 4096 * q_);                   \
           }                                                                               \
         }                                                                                 \
       } else {                                                                            \
         _Pragma("unroll") for (int q_ = 0; q_ < B_PW; ++q_)                                \
-          dma16s<0>(bg + kob_, boff[q_], bo_ + 1024 * q_);                                \
+          dma16s_w<0, W_NT>(bg + kob_, boff[q_], bo_ + 1024 * q_);                        \
       }                                                                                   \
     }                                                                                     \
     if (scale_loader) dma4(ssrc + ik, s_dst + (uint32_t)((SV) & 3) * AS_W * 4);           \
