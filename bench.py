@@ -39,13 +39,14 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0       # dense fp8 MFMA (published, no sparsity)
-# fp32 vector peak this build can issue: the published 157.3 TFLOP/s needs packed fp32 FMAs, which
-# the build turns off, so one fma per lane per clock: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz
+# fp32 vector peak the library's kernels can issue: the published 157.3 TFLOP/s needs packed fp32 FMAs,
+# which the library's compile flags turn off, so one fma per lane per clock:
+# 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz
 PEAK_FP32_TFLOPS = 78.6
 RIDGE_FP8 = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 PEAKS = {"hbm": "8.0 TB/s HBM3E (published)", "mfma": "5.0 PFLOP/s dense fp8 (published)",
          "alu": "78.6 TFLOP/s fp32 vector without packed FMA (published 157.3 needs packed fp32 FMA, "
-                "which the build turns off)"}
+                "which the library's compile flags turn off)"}
 # achievable peaks measured on MI355X with in-bounds microbenchmarks built here (a register-only fp8
 # MFMA loop, 16 independent accumulators, 2 waves per SIMD; streaming reads of contiguous 32 KB
 # blocks by 256-1024 workgroups); reported beside the published ones
@@ -527,7 +528,7 @@ def main():
     a = parse()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}): the layer's multi-GPU form (expert "
-              "parallel dispatch/combine over xGMI) is not part of this build.", file=sys.stderr)
+              "parallel dispatch/combine over xGMI) is not implemented in this library.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -71,7 +71,7 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
 // x = n*ln2 + r with ln2 = hi + lo (hi has few enough bits that n*hi is exact for |n| <= 127),
 // degree-6 Taylor polynomial of e^r by Horner's rule with fused multiply-adds, exact scaling by
 // 2^n.  The input is clamped to [-86, 88] so the result is a normal, finite fp32 number.
-// Every step is one IEEE fp32 operation; the build uses -ffp-contract=off.
+// Every step is one IEEE fp32 operation; the library is compiled with -ffp-contract=off.
 __device__ __forceinline__ float router_exp(float x) {
   x = fminf(fmaxf(x, -86.0f), 88.0f);
   const float n = rintf(x * 0x1.715476p+0f);
