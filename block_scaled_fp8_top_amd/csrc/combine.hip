@@ -33,7 +33,7 @@ __device__ __forceinline__ void store8(void* __restrict__ out, int64_t off, cons
   if (OBF16) {
     uint32_t p[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) p[q] = (uint32_t)f32_to_bf16(v[2 * q]) | ((uint32_t)f32_to_bf16(v[2 * q + 1]) << 16);
+    for (int q = 0; q < 4; ++q) p[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
     *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + off) = make_uint4(p[0], p[1], p[2], p[3]);
   } else {
     float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + off);

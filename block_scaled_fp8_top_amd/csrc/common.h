@@ -19,14 +19,17 @@ static inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream
 
 // ------------------------------------------------------------------------------------------
 // bf16 <-> fp32.  bf16 is the upper half of an fp32 pattern, so widening is exact; narrowing
-// rounds to nearest even (finite inputs).
+// rounds to nearest even (NaN stays NaN) with gfx950's conversion instruction, v_cvt_pk_bf16_f32,
+// which converts two values at once.
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef float bf16_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16_x2 __attribute__((ext_vector_type(2)));
+// (lo, hi) -> one word, lo in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((bf16_f32x2){lo, hi}, bf16_x2));
 }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)pack_bf16x2(f, 0.0f); }
 
 // ------------------------------------------------------------------------------------------
 // Block scale of a block whose largest magnitude is amax.  Default: amax / 448 (IEEE fp32 division;

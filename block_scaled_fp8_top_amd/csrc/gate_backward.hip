@@ -134,7 +134,7 @@ __global__ __launch_bounds__(NTH) void gemm_kn_kernel(const float* __restrict__ 
       if (O_BF16) {
         uint32_t p[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) p[q] = (uint32_t)f32_to_bf16(v[2 * q]) | ((uint32_t)f32_to_bf16(v[2 * q + 1]) << 16);
+        for (int q = 0; q < 4; ++q) p[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
         *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(c) + m * N + nc) = make_uint4(p[0], p[1], p[2], p[3]);
       } else {
         float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(c) + m * N + nc);

@@ -667,8 +667,8 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
             const int off = ((wm * WROWS + ms * 16 + tr) * N + c0 + ns * 16) * EB;
             if (OUT_BF16) {
               uint32x2 w;
-              w[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-              w[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+              w[0] = pack_bf16x2(v[0], v[1]);
+              w[1] = pack_bf16x2(v[2], v[3]);
               __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, 0);
             } else {
               uint32x4 w;
