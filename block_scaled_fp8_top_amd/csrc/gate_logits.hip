@@ -1,11 +1,12 @@
 // Router gate projection: logits[t,e] = fp32 fma chain over h ascending (+ bias).
 //
 // The chain order is part of the contract (it makes routing reproducible bit for bit), so the
-// contraction cannot use matrix cores or split K: it is fp32 VALU work.  Each thread owns a
-// TT x TE register tile of outputs and walks h in order; x and Wg are staged through two LDS
-// buffers in chunks of HC columns (x converted to fp32 on the way; the next chunk's global loads
-// are in flight during the current chunk's chain), padded so that the 16-byte LDS reads of
-// different rows fall in different banks.
+// contraction cannot use matrix cores or split K: it is fp32 VALU work.  Three kernels, chosen by
+// size (moe_gate_logits): register tiles, the x-broadcast kernel and a one-logit-per-lane chain.
+// Tiles: each thread owns a TT x TE register tile of outputs and walks h in order; x and Wg are
+// staged through two LDS buffers in chunks of HC columns (x converted to fp32 on the way; the next
+// chunk's global loads are in flight during the current chunk's chain), padded so that the 16-byte
+// LDS reads of different rows fall in different banks.
 #include "common.h"
 
 namespace {
@@ -302,6 +303,181 @@ __global__ __launch_bounds__(64) void gate_logits_chain_kernel(const void* __res
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Many tokens, E of 64, 128 or 256, H a multiple of 32: x broadcast within 16-lane rows.
+// A wavefront owns TT tokens and every expert (lane l: experts l, l + 64, ..., TE = E / 64 of them),
+// so a Wg value read from LDS serves TT fmas (the tile kernel above reads an x value and a Wg value
+// from LDS for every TT x TE tile, twice the LDS bytes per fma at TT = TE = 4).  The x of a 32-column
+// chunk sits in two registers per token, lane 16 r + k holding columns 2k and 2k + 1, and the fma of
+// column h takes it from lane h / 2 of the lane's own row through a DPP row broadcast
+// (row_newbcast) fused into the fma, v_fmac_f32_dpp.  Chunks of Wg (E rows of 128 bytes, 16-byte
+// pieces XOR-swizzled by row so that eight rows' reads of one piece hit distinct banks) and of raw x
+// are copied global -> LDS by DMA (global_load_lds) into two buffers, one chunk ahead of the chain
+// (a deeper ring for x, which is read once from HBM, measured no faster).  Workgroup: NW wavefronts,
+// NW TT tokens.
+//
+// A DPP source register needs two wait states after a VALU instruction writes it, which the
+// compiler does not insert for inline assembly: the widened x registers pass through an s_nop 1
+// that takes them as operands, so every DPP read of them comes after it.
+constexpr int BC_HC = 32;   // h columns per chunk
+
+template <int K>
+__device__ __forceinline__ void fmac_row_bcast(float& acc, float x, float w) {
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(x), "v"(w), "i"(K));
+}
+
+__device__ __forceinline__ void bc_dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(g) : "memory", "m0");
+}
+
+// columns HL .. 31 of a chunk, four at a time: per expert of the lane one 16-byte LDS read (the
+// row's piece HL / 4, at its swizzled slot woff[HL / 4]) gives four columns; the reads of the next
+// piece are issued before the fmas of this one
+template <int TT, int TE>
+__device__ __forceinline__ void bc_read(float4 (&w4)[TE], const uint8_t* __restrict__ wbuf, int off) {
+#pragma unroll
+  for (int j = 0; j < TE; ++j) w4[j] = *reinterpret_cast<const float4*>(wbuf + j * 64 * 128 + off);
+}
+template <int HL, int TT, int TE>
+__device__ __forceinline__ void bcast_chunk(float (&acc)[TT][TE], const float (&xa)[TT], const float (&xb)[TT],
+                                            const uint8_t* __restrict__ wbuf, const int (&woff)[8],
+                                            const float4 (&w4)[TE]) {
+  float4 nx[TE];
+  if constexpr (HL + 4 < BC_HC) bc_read<TT, TE>(nx, wbuf, woff[HL / 4 + 1]);
+#define BC_COL(M, C)                                                                        \
+  _Pragma("unroll") for (int i = 0; i < TT; ++i)                                            \
+    _Pragma("unroll") for (int j = 0; j < TE; ++j)                                          \
+      fmac_row_bcast<(HL + M) / 2>(acc[i][j], (M) % 2 == 0 ? xa[i] : xb[i], w4[j].C);
+  BC_COL(0, x)
+  BC_COL(1, y)
+  BC_COL(2, z)
+  BC_COL(3, w)
+#undef BC_COL
+  if constexpr (HL + 4 < BC_HC) bcast_chunk<HL + 4, TT, TE>(acc, xa, xb, wbuf, woff, nx);
+}
+
+template <int TT, int TE, int NW, bool BF16>
+__global__ __launch_bounds__(NW * 64) void gate_logits_bcast_kernel(const void* __restrict__ xv,
+                                                                  const float* __restrict__ wg,
+                                                                  const float* __restrict__ bias, int64_t T, int H,
+                                                                  float* __restrict__ z) {
+  constexpr int E = 64 * TE, BT = NW * TT;
+  constexpr int XB = BF16 ? 2 : 4;                    // bytes per x value
+  constexpr int WBUF = E * BC_HC * 4;                 // bytes of a Wg chunk
+  constexpr int XBUF = BT * BC_HC * XB;               // bytes of an x chunk
+  constexpr int WI = WBUF / 1024 / NW;                // Wg DMA instructions per wavefront and chunk
+  constexpr int XI = XBUF / 1024;                     // x DMA instructions per chunk (waves 0 .. XI-1)
+  constexpr int XROWS = 1024 / (BC_HC * XB);          // tokens per x DMA instruction
+  static_assert(XI >= 1 && XI <= NW && WI >= 1 && WI * NW * 1024 == WBUF, "DMA split");
+  static_assert(2 * (WBUF + XBUF) <= 80 * 1024, "LDS: two workgroups per CU");
+  __shared__ __attribute__((aligned(1024))) uint8_t ws[2][WBUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[2][XBUF];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t tb = (int64_t)blockIdx.x * BT;
+  const int nchunk = H / BC_HC;
+
+  // DMA sources.  Wg instruction i = wave WI + q holds rows 8i .. 8i + 7: lane L writes LDS word L,
+  // row 8i + L / 8, slot L % 8, which holds the row's piece (L % 8) ^ (row % 8) = (L % 8) ^ (L / 8).
+  // x instruction wave (waves 0 .. XI-1): tokens XROWS wave .. + XROWS - 1, row-major (clamped to T-1).
+  const char* wsrc[WI];
+#pragma unroll
+  for (int q = 0; q < WI; ++q) {
+    const int row = 8 * (wave * WI + q) + (lane >> 3);
+    wsrc[q] = reinterpret_cast<const char*>(wg) + ((int64_t)row * H) * 4 + (((lane & 7) ^ (lane >> 3)) << 4);
+  }
+  const int xper = 64 / XROWS;   // lanes per token row
+  const int64_t xrow = min(tb + XROWS * min(wave, XI - 1) + lane / xper, T - 1);
+  const char* xsrc = reinterpret_cast<const char*>(xv) + xrow * H * XB + (lane % xper) * 16;
+  const uint32_t wdst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&ws[0][wave * WI * 1024]);
+  const uint32_t xdst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&xs[0][min(wave, XI - 1) * 1024]);
+  const bool x_dma = wave < XI;
+  auto issue = [&](int c) {   // chunk c into buffer c & 1
+    const int64_t h0 = (int64_t)c * BC_HC;
+#pragma unroll
+    for (int q = 0; q < WI; ++q) bc_dma16(wsrc[q] + h0 * 4, wdst + (c & 1) * WBUF + q * 1024);
+    if (x_dma) bc_dma16(xsrc + h0 * XB, xdst + (c & 1) * XBUF);
+  };
+
+  // this lane's swizzled slot of piece q in its rows (row % 8 = lane % 8 for every expert l + 64 j)
+  int woff[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) woff[q] = lane * 128 + ((q ^ (lane & 7)) << 4);
+
+  float acc[TT][TE];
+#pragma unroll
+  for (int i = 0; i < TT; ++i)
+#pragma unroll
+    for (int j = 0; j < TE; ++j) acc[i][j] = 0.0f;
+
+  issue(0);
+  for (int c = 0; c < nchunk; ++c) {
+    const int b = c & 1;
+    // this wave's DMA of chunk c has landed; after the barrier every wave's has, and every wave is
+    // done with chunk c - 1, whose buffers take chunk c + 1
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (c + 1 < nchunk) issue(c + 1);
+    // this wave's tokens: lane 16 r + k takes columns 2k and 2k + 1
+    float xa[TT], xb[TT];
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+      const uint8_t* row = &xs[b][(wave * TT + i) * BC_HC * XB];
+      if constexpr (BF16) {
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(row + (lane & 15) * 4);
+        xa[i] = __uint_as_float(u << 16);
+        xb[i] = __uint_as_float(u & 0xFFFF0000u);
+      } else {
+        const float2 p = *reinterpret_cast<const float2*>(row + (lane & 15) * 8);
+        xa[i] = p.x;
+        xb[i] = p.y;
+      }
+    }
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < TT; ++i) asm volatile("s_nop 1" : "+v"(xa[i]), "+v"(xb[i]));
+    }
+    float4 w4[TE];
+    bc_read<TT, TE>(w4, &ws[b][0], woff[0]);
+    bcast_chunk<0, TT, TE>(acc, xa, xb, &ws[b][0], woff, w4);
+  }
+#pragma unroll
+  for (int i = 0; i < TT; ++i) {
+    const int64_t t = tb + wave * TT + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < TE; ++j) {
+      const int e = lane + 64 * j;
+      float v = acc[i][j];
+      if (bias) v = v + bias[e];
+      z[t * E + e] = v;
+    }
+  }
+}
+
+template <int TT, int TE, int NW>
+int launch_bcast(const void* x, bool bf16, const float* wg, const float* bias, int64_t T, int H, float* z,
+                 hipStream_t st) {
+  const unsigned grid = (unsigned)ceil_div64(T, NW * TT);
+  if (bf16)
+    gate_logits_bcast_kernel<TT, TE, NW, true><<<grid, NW * 64, 0, st>>>(x, wg, bias, T, H, z);
+  else
+    gate_logits_bcast_kernel<TT, TE, NW, false><<<grid, NW * 64, 0, st>>>(x, wg, bias, T, H, z);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+template <int TT, int NW>
+int launch_bcast_e(const void* x, bool bf16, const float* wg, const float* bias, int64_t T, int H, int E, float* z,
+                   hipStream_t st) {
+  switch (E) {
+    case 64: return launch_bcast<TT, 1, NW>(x, bf16, wg, bias, T, H, z, st);
+    case 128: return launch_bcast<TT, 2, NW>(x, bf16, wg, bias, T, H, z, st);
+    default: return launch_bcast<TT, 4, NW>(x, bf16, wg, bias, T, H, z, st);
+  }
+}
+
 template <int TT, int TE>
 int launch(const void* x, bool bf16, const float* wg, const float* bias, int64_t T, int H, int E, float* z,
            hipStream_t st) {
@@ -340,6 +516,13 @@ extern "C" int moe_gate_logits(const void* x, int x_dtype, const float* wg, cons
   const int64_t wg44 = ceil_div64(T, 64) * ceil_div64(E, 64);
   const int64_t wg22 = ceil_div64(T, 32) * ceil_div64(E, 32);
   if (wg84 >= 512) return launch<8, 4>(x, bf16, wg, bias, T, H, E, logits, st);
+  // Below that, the x-broadcast kernel (4 tokens per wavefront, 4 wavefronts and a ring of two
+  // chunks per workgroup, so two workgroups share a CU) where its shape rules allow.  Measured at
+  // 8192 tokens, H 6144, 256 experts, bf16 x: 442 us against 483 us for the 4 x 4 tiles.  The 8 x 4
+  // tiles above stay ahead where they fill the chip (728 us against 804 us at 16384 tokens): their
+  // plain fmas issue faster than the DPP-fused ones, and 32 accumulators per thread hide more.
+  if (E % 64 == 0 && E <= 256 && H % BC_HC == 0 && T >= 8192)
+    return launch_bcast_e<4, 4>(x, bf16, wg, bias, T, H, E, logits, st);
   if (wg44 >= 512) return launch<4, 4>(x, bf16, wg, bias, T, H, E, logits, st);
   if (wg22 >= 512) return launch<2, 2>(x, bf16, wg, bias, T, H, E, logits, st);
   return launch<1, 1>(x, bf16, wg, bias, T, H, E, logits, st);
