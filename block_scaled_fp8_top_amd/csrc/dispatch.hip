@@ -203,9 +203,11 @@ constexpr int SMALL_CNT = 16384;      // (64-slot pieces) x experts counters in 
 // row is offset + piece base + rank: the stable order.
 // With tiles != NULL the same workgroup also writes the grouped GEMM's tile list for row tiles of
 // bm (the entries the plan kernel of the grouped GEMM writes: {group, first row, the block's first
-// tile, the block's tile count}, at most max_tiles of them, and their number into *ntiles), and
-// with second != 0 the second list at tiles + second (every group's full tiles first, then the
-// groups' short last tiles), as the plan kernel does.
+// tile, the block's tile count}, at most max_tiles of them, and their number into ntiles[0]), with
+// second != 0 the second list at tiles + second (every group's full tiles first, then the groups'
+// short last tiles; with third != 0 only those over 128 rows) into ntiles[1], and with third != 0
+// the third list at tiles + third (one 128-row tile per short remainder of 1 .. 128 rows) into
+// ntiles[2], as the plan kernel does.
 template <int BITS>
 __global__ __launch_bounds__(1024) void small_dispatch_kernel(const int32_t* __restrict__ idx, int nslots, int k, int E,
                                                               int T, int append_shared, int32_t* __restrict__ counts,
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(1024) void small_dispatch_kernel(const int32_t* __r
                                                               int32_t* __restrict__ dest_row,
                                                               int32_t* __restrict__ src_token, int bm,
                                                               int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
-                                                              int max_tiles, int second) {
+                                                              int max_tiles, int second, int third) {
   __shared__ int sidx[SMALL_MAX];
   __shared__ uint8_t srank[SMALL_MAX];
   __shared__ int cnt[SMALL_CNT];      // [piece][e]
@@ -331,12 +333,25 @@ __global__ __launch_bounds__(1024) void small_dispatch_kernel(const int32_t* __r
     tiles[second + t] = make_int4(lo, row_of(lo) + (t - first[lo]) * bm, first[lo], first[lo + 1] - first[lo]);
   }
   __syncthreads();
-  scan_first(rows_g % bm != 0 ? 1 : 0);          // then every group's short last tile
-  for (int t = nfull + tid; t < ntot; t += 1024) {
+  // then every group's short last tile (with a third list, only those over 128 rows)
+  scan_first(rows_g % bm > (third ? 128 : 0) ? 1 : 0);
+  const int n2 = min(nfull + first[G], ntot);
+  for (int t = nfull + tid; t < n2; t += 1024) {
     const int lo = owner(t - nfull);
     const int g_rows = lo < E ? row_of(lo + 1) - row_of(lo) : T;
     tiles[second + t] = make_int4(lo, row_of(lo) + (g_rows / bm) * bm, t, 1);
   }
+  if (tid == 0) ntiles[1] = n2;
+  if (!third) return;
+  __syncthreads();
+  scan_first(rows_g % bm > 0 && rows_g % bm <= 128 ? 1 : 0);   // the third list: short remainders
+  const int n3 = first[G];
+  for (int t = tid; t < n3; t += 1024) {
+    const int lo = owner(t);
+    const int g_rows = lo < E ? row_of(lo + 1) - row_of(lo) : T;
+    tiles[third + t] = make_int4(lo, row_of(lo) + (g_rows / bm) * bm, t, 1);
+  }
+  if (tid == 0) ntiles[2] = n3;
 }
 
 int64_t nchunks_for(int64_t T, int k) { return ceil_div64(T * k, CHUNK); }
@@ -348,6 +363,7 @@ size_t moe_dispatch_workspace(int64_t T, int32_t k, int32_t E) {
 }
 
 int64_t moe_plan_second_list(int64_t max_rows, int groups, int bm);
+int64_t moe_plan_third_list(int64_t max_rows, int groups, int bm);
 int moe_plan_host(int32_t groups, int64_t max_rows, int32_t tile_rows, void* workspace, size_t workspace_bytes,
                   moe_gemm_plan* plan, int64_t* max_tiles);
 
@@ -383,12 +399,14 @@ int dispatch_impl(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int3
     int32_t* pntiles = plan_here ? reinterpret_cast<int32_t*>(plan_ws) : nullptr;
     const int64_t second = plan_here ? moe_plan_second_list(nslots + (append_shared ? T : 0),
                                                             E + (append_shared ? 1 : 0), plan_bm) : 0;
+    const int64_t third = plan_here ? moe_plan_third_list(nslots + (append_shared ? T : 0),
+                                                          E + (append_shared ? 1 : 0), plan_bm) : 0;
     switch (bits) {
 #define CASE_SMALL(B)                                                                                   \
   case B:                                                                                               \
     small_dispatch_kernel<B><<<1, 1024, 0, st>>>(topk_idx, (int)nslots, k, E, (int)T, append_shared, counts, \
                                                  offsets, dest_row, src_token, plan_bm, ptiles, pntiles, \
-                                                 (int)plan_max_tiles, (int)second);                      \
+                                                 (int)plan_max_tiles, (int)second, (int)third);          \
     break;
       CASE_SMALL(1) CASE_SMALL(2) CASE_SMALL(3) CASE_SMALL(4) CASE_SMALL(5)
       CASE_SMALL(6) CASE_SMALL(7) CASE_SMALL(8) CASE_SMALL(9) CASE_SMALL(10)

@@ -61,6 +61,7 @@ namespace {
 constexpr int BN = 256, BK = 128;
 constexpr int NTHREADS = 512;
 constexpr int MIN_BM = 32;
+constexpr int SPLIT_BM = 128;   // tile height of the third list (short tiles of 256-row plans)
 
 template <int BM_, bool FP4 = false>
 struct Tile {
@@ -209,13 +210,16 @@ __device__ __forceinline__ int owner(const int* first, int groups, int t) {
 }
 
 // The tile list: group g's ceil(rows_g / bm) tiles, groups in order; entry {group, first row, first
-// tile of the unit-order block, tiles in the block}, the block being the group's tiles.  With
-// second != 0 a second list at tiles + second holds the same tiles with every group's full tiles
-// first (block: the group's full tiles) and then each group's short last tile (a block of its
-// own): the SwiGLU GEMM runs in that order (see run_planned).
+// tile of the unit-order block, tiles in the block}, the block being the group's tiles; its length
+// goes to ntiles[0].  With second != 0 a second list at tiles + second holds the same tiles with
+// every group's full tiles first (block: the group's full tiles) and then each group's short last
+// tile (a block of its own); its length goes to ntiles[1].  With third != 0 as well (256-row
+// plans), the second list keeps only the short tiles of more than SPLIT_BM rows, and a third list
+// at tiles + third holds one SPLIT_BM-row tile for each group whose short remainder has 1 ..
+// SPLIT_BM rows; its length goes to ntiles[2].  run_planned picks the lists.
 __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restrict__ offsets, int groups, int bm,
                                                         int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
-                                                        int max_tiles, int second) {
+                                                        int max_tiles, int second, int third) {
   __shared__ int part[1024];
   __shared__ int first[TILE_MAP_MAXG + 1];   // first[g] = tiles before group g; first[groups] = all
   __shared__ int carry;
@@ -238,12 +242,26 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
     tiles[second + t] = make_int4(lo, offsets[lo] + i * bm, first[lo], first[lo + 1] - first[lo]);
   }
   __syncthreads();
-  group_prefix(groups, [&](int g) { return (offsets[g + 1] - offsets[g]) % bm != 0 ? 1 : 0; }, first, part, &carry);
-  for (int t = nfull + threadIdx.x; t < total; t += 1024) {
+  auto short_rows = [&](int g) { return (offsets[g + 1] - offsets[g]) % bm; };
+  group_prefix(groups, [&](int g) { return short_rows(g) > (third ? SPLIT_BM : 0) ? 1 : 0; }, first, part, &carry);
+  const int n2 = min(nfull + first[groups], total);
+  for (int t = nfull + threadIdx.x; t < n2; t += 1024) {
     const int lo = owner(first, groups, t - nfull);
     const int nf = (offsets[lo + 1] - offsets[lo]) / bm;
     tiles[second + t] = make_int4(lo, offsets[lo] + nf * bm, t, 1);
   }
+  if (threadIdx.x == 0) ntiles[1] = n2;
+  if (!third) return;
+  __syncthreads();
+  group_prefix(groups, [&](int g) { return short_rows(g) > 0 && short_rows(g) <= SPLIT_BM ? 1 : 0; }, first, part,
+               &carry);
+  const int n3 = first[groups];   // at most groups: the host reserves that many entries
+  for (int t = threadIdx.x; t < n3; t += 1024) {
+    const int lo = owner(first, groups, t);
+    const int nf = (offsets[lo + 1] - offsets[lo]) / bm;
+    tiles[third + t] = make_int4(lo, offsets[lo] + nf * bm, t, 1);
+  }
+  if (threadIdx.x == 0) ntiles[2] = n3;
 }
 
 // wait until at most n of this wave's vector memory instructions are outstanding (n is
@@ -782,6 +800,21 @@ int64_t moe_plan_second_list(int64_t max_rows, int groups, int bm) {
   return bm >= 128 && 2 * mt <= max_tiles_for(max_rows, groups, MIN_BM) ? mt : 0;
 }
 
+// Where the plan's third tile list starts, in tiles from the first list, or 0 when there is none:
+// for 256-row plans whose workspace holds `groups` more entries after the second list.  Such a
+// GEMM runs as two launches: the second list (full tiles, then short tiles of more than SPLIT_BM
+// rows) with 256-row tiles, then the third (the short remainders of 1 .. SPLIT_BM rows) with
+// SPLIT_BM-row tiles.  A remainder of a few rows mostly streams its weight panel, and as a 256-row
+// tile at the end of the one launch it took longer than as a 128-row tile of a launch of its own.
+// Measured on the long-context chunk (65536 rows over 194 experts, 167 remainders of <= 128 rows):
+// SwiGLU GEMM 2700 -> 2492 us, store GEMM 1527 -> 1421 us; on the prefill routing (about 512 rows
+// per expert) the remainders over 128 rows stay in the first launch, where a 128-row tile would
+// stream their panel twice.
+int64_t moe_plan_third_list(int64_t max_rows, int groups, int bm) {
+  const int64_t second = moe_plan_second_list(max_rows, groups, bm);
+  return bm == 256 && second != 0 && 2 * second + groups <= max_tiles_for(max_rows, groups, MIN_BM) ? 2 * second : 0;
+}
+
 namespace {
 
 // Row-tile height when the caller leaves it open: the smallest height that holds twice the
@@ -954,7 +987,8 @@ extern "C" int moe_grouped_gemm_plan(const int32_t* offsets, int32_t groups, int
   int4* tiles = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(workspace) + 256);
   int32_t* ntiles = reinterpret_cast<int32_t*>(workspace);
   tile_map_kernel<<<1, 1024, 0, as_stream(stream)>>>(offsets, groups, bm, tiles, ntiles, (int)mt,
-                                                    (int)moe_plan_second_list(max_rows, groups, bm));
+                                                    (int)moe_plan_second_list(max_rows, groups, bm),
+                                                    (int)moe_plan_third_list(max_rows, groups, bm));
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -983,10 +1017,27 @@ int run_planned(const moe_gemm_plan* plan, const uint8_t* a, const int32_t* a_ro
   const int64_t nwg = mt * ny;
   if (nwg > INT32_MAX) return MOE_ERR_SHAPE;
   const int4* tiles = reinterpret_cast<const int4*>(reinterpret_cast<const uint8_t*>(plan->workspace) + 256);
-  if (epilogue == MOE_EPI_SWIGLU_QUANT) tiles += moe_plan_second_list(max_rows, groups, bm);   // full tiles first
   const int32_t* ntiles = reinterpret_cast<const int32_t*>(plan->workspace);
   const int cus = compute_units();
   if (cus <= 0) return MOE_ERR_HIP;
+  const int64_t second = moe_plan_second_list(max_rows, groups, bm);
+  const int64_t third = moe_plan_third_list(max_rows, groups, bm);
+  if (third) {
+    // two launches: the second list with 256-row tiles, then the third with SPLIT_BM-row tiles
+    // (one persistent workgroup per compute unit each, never more than the list can hold)
+    launch<256>((unsigned)std::min<int64_t>(nwg, cus), st, b_layout, epilogue, scale_mode, out_dtype, a, a_rows,
+                (int)a_count, as, offsets, tiles + second, ntiles + 1, ny, b, bs, N, K, out, out_scales, g_out);
+    MOE_CHECK_LAUNCH();
+    launch<SPLIT_BM>((unsigned)std::min<int64_t>((int64_t)groups * ny, cus), st, b_layout, epilogue, scale_mode,
+                     out_dtype, a, a_rows, (int)a_count, as, offsets, tiles + third, ntiles + 2, ny, b, bs, N, K, out,
+                     out_scales, g_out);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+  }
+  if (epilogue == MOE_EPI_SWIGLU_QUANT && second) {   // full tiles first
+    tiles += second;
+    ntiles += 1;
+  }
   // one persistent workgroup per compute unit (the LDS ring admits one per CU), never more than
   // the worst-case number of units
   const unsigned grid = (unsigned)std::min<int64_t>(nwg, cus);

@@ -263,7 +263,9 @@ int moe_grouped_gemm_fp8_noalloc(const uint8_t* a, const float* as, const int32_
                                  int out_dtype, float* out_scales, void* stream);
 
 /* Grouped GEMM in two steps, so that one tile plan serves several GEMMs over the same groups
- * (the layer's W1 and W2 GEMMs) and the GEMM launch itself is a single kernel.
+ * (the layer's W1 and W2 GEMMs) and the GEMM launch itself is one kernel (two for a plan of 256-row
+ * tiles: the groups' full tiles and short tiles of more than 128 rows, then the short remainders of
+ * up to 128 rows as 128-row tiles).
  * moe_grouped_gemm_plan writes the list of row tiles of `offsets` (device) into `workspace`
  * (>= moe_workspace_bytes(MOE_OP_GROUPED_GEMM, max_rows, 0, groups, 0, 0) bytes, caller-owned, and
  * holding the plan until the last GEMM that uses it has run) and fills `plan` (host) with the tile

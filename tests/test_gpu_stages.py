@@ -421,7 +421,8 @@ def test_dispatch_small_and_chunked_paths(T, k, E):
 @pytest.mark.parametrize("T,k,E,shared", [(256, 6, 64, False), (96, 8, 32, True), (1, 8, 256, True),
                                            (0, 6, 64, False), (2048, 8, 256, True),
                                            (3, 2, 1023, True), (4, 2, 1024, True),    # G = 1024, 1025
-                                           (1024, 8, 16, True), (1000, 8, 24, False)])  # one workgroup, both lists
+                                           (1024, 8, 16, True), (1000, 8, 24, False),   # one workgroup, all lists
+                                           (4096, 8, 64, False)])                      # plan kernel, all lists
 def test_dispatch_plan_equals_separate_plan(T, k, E, shared):
     """moe_dispatch_plan: the same dispatch outputs as moe_dispatch and the same tile list (every
     entry and the count) as moe_grouped_gemm_plan, for each tile height; the one-workgroup path
@@ -458,19 +459,28 @@ def test_dispatch_plan_equals_separate_plan(T, k, E, shared):
         assert_equal(f"tiles tile {tile}", host(gws[256:256 + 16 * nt]), host(gws2[256:256 + 16 * nt]))
         # both lists against their definition: group order, and (128- and 256-row tiles, when the
         # workspace holds it) every group's full tiles first, then the groups' short last tiles
-        l1, l2, second = _expected_tile_lists(host(ref.offsets), plan.tile_rows, max_rows, G)
+        l1, l2, l3, second, third = _expected_tile_lists(host(ref.offsets), plan.tile_rows, max_rows, G)
         assert nt == len(l1)
         got1 = host(gws[256:256 + 16 * nt].view(torch.int32)).reshape(-1, 4)
         assert_equal(f"list 1 tile {tile}", got1, np.array(l1, np.int32).reshape(-1, 4))
-        if second:
-            for w in (gws, gws2):
-                got2 = host(w[256 + 16 * second:256 + 16 * (second + nt)].view(torch.int32)).reshape(-1, 4)
+        for w in (gws, gws2):
+            head = host(w[:12].view(torch.int32))
+            if second:
+                assert int(head[1]) == len(l2), (tile, head, len(l2))
+                got2 = host(w[256 + 16 * second:256 + 16 * (second + len(l2))].view(torch.int32)).reshape(-1, 4)
                 assert_equal(f"list 2 tile {tile}", got2, np.array(l2, np.int32).reshape(-1, 4))
+            if third:
+                assert int(head[2]) == len(l3), (tile, head, len(l3))
+                got3 = host(w[256 + 16 * third:256 + 16 * (third + len(l3))].view(torch.int32)).reshape(-1, 4)
+                assert_equal(f"list 3 tile {tile}", got3, np.array(l3, np.int32).reshape(-1, 4))
 
 
 def _expected_tile_lists(offsets, bm, max_rows, G):
     """The grouped GEMM's tile lists from their definition: entries {group, first row, first tile of
-    the entry's block, tiles in the block}."""
+    the entry's block, tiles in the block}.  List 1: group order.  List 2 (128- and 256-row tiles,
+    when the workspace holds it): every group's full tiles, then the short last tiles; for 256-row
+    tiles with room for `groups` more entries, only the short tiles of more than 128 rows, the
+    others (1 .. 128 rows) forming list 3 as 128-row tiles.  Returns (l1, l2, l3, second, third)."""
     rows = np.diff(offsets[:G + 1])
     l1 = []
     for g in range(G):
@@ -478,17 +488,23 @@ def _expected_tile_lists(offsets, bm, max_rows, G):
         f = len(l1)
         l1 += [(g, int(offsets[g]) + i * bm, f, n) for i in range(n)]
     mt = -(-max_rows // bm) + G
-    second = mt if bm >= 128 and 2 * mt <= -(-max_rows // 32) + G else 0
-    l2 = []
+    cap = -(-max_rows // 32) + G
+    second = mt if bm >= 128 and 2 * mt <= cap else 0
+    third = 2 * second if bm == 256 and second and 2 * second + G <= cap else 0
+    l2, l3 = [], []
     if second:
         for g in range(G):
             n = int(rows[g]) // bm
             f = len(l2)
             l2 += [(g, int(offsets[g]) + i * bm, f, n) for i in range(n)]
         for g in range(G):
-            if rows[g] % bm:
-                l2.append((g, int(offsets[g]) + (int(rows[g]) // bm) * bm, len(l2), 1))
-    return l1, l2, second
+            r = int(rows[g]) % bm
+            start = int(offsets[g]) + (int(rows[g]) // bm) * bm
+            if r > (128 if third else 0):
+                l2.append((g, start, len(l2), 1))
+            elif third and r > 0:
+                l3.append((g, start, len(l3), 1))
+    return l1, l2, l3, second, third
 
 
 @pytest.mark.parametrize("H", [128, 1152, 8192, 8320])
@@ -580,6 +596,46 @@ def test_grouped_gemm_store(name, which, tile):
     assert e32 < 1e-3 and ebf < TOL
     del a, as_, b, bs, y32, ybf
     _cleanup()
+
+
+@pytest.mark.parametrize("epi", ["swiglu", "store"])
+def test_grouped_gemm_split_launches(epi):
+    """256-row plans run as two launches (full tiles and short tiles over 128 rows, then the short
+    remainders of 1 .. 128 rows as 128-row tiles).  Every tile height computes the same sums in the
+    same order, so the output equals the one-launch 128-row tiles' bit for bit on every row, with
+    group sizes around each boundary (0, 1, 127 .. 129, 255 .. 257, 383 .. 385 rows); sampled rows,
+    every remainder's first and last among them, against the oracle."""
+    counts = np.array([0, 1, 5, 31, 64, 100, 127, 128, 129, 200, 255, 256, 257, 300, 383, 384, 385, 511, 512,
+                       513, 700, 1000, 0, 1, 2, 90, 160, 1400, 30, 3, 250, 129, 128, 127, 640, 900, 17, 0, 64, 2000])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    G, rows = len(counts), int(offsets[-1])
+    N, K = 512, 256
+    a = synth.random_codes((rows, K), 9, 60, device=DEV)
+    as_ = synth.random_scales((rows, K // 128), 9, 61, device=DEV, lo=2.0 ** -10, hi=2.0 ** -6)
+    b = synth.random_codes((G, N, K), 9, 62, device=DEV)
+    bs = synth.random_scales((G, N // 128, K // 128), 9, 63, device=DEV, lo=2.0 ** -10, hi=2.0 ** -6)
+    goff = torch.from_numpy(offsets).to(DEV)
+    e = M.MOE_EPI_SWIGLU_QUANT if epi == "swiglu" else M.MOE_EPI_STORE
+    pk = M.moe_pack_weights_fp8(b, e)
+    # the plan has the third list, with the remainders of 1 .. 128 rows in it
+    ws = torch.empty(M.workspace_bytes(M.MOE_OP_GROUPED_GEMM, rows, 0, G, 0, 0), dtype=torch.uint8, device=DEV)
+    plan = M.moe_grouped_gemm_plan(goff, rows, ws, tile_rows=256)
+    n3 = int(host(ws[:12].view(torch.int32))[2])
+    assert plan.tile_rows == 256 and n3 == int(((counts % 256 > 0) & (counts % 256 <= 128)).sum())
+    outs = {}
+    for tile in (256, 128):
+        if e == M.MOE_EPI_STORE:
+            outs[tile] = (M.moe_grouped_gemm_fp8(a, as_, goff, pk, bs, e, torch.float32, tile_rows=tile),)
+        else:
+            outs[tile] = M.moe_grouped_gemm_fp8(a, as_, goff, pk, bs, e, tile_rows=tile)
+    for x, y in zip(outs[256], outs[128]):
+        assert_equal(f"{epi}: 256-row plan (two launches) against 128-row tiles", host(x), host(y))
+    if e == M.MOE_EPI_STORE:
+        rem0 = offsets[:-1] + counts // 256 * 256
+        edge = np.concatenate([rem0[counts % 256 > 0], offsets[1:][counts > 0] - 1])
+        smp = np.unique(np.concatenate([edge, synth.sample_tokens(rows, 40, 9)]))
+        ref, _ = _oracle_rows(a, as_, offsets, b, bs, smp)
+        assert rel_err(rows_host(outs[256][0], smp), ref) < 1e-3
 
 
 def test_grouped_gemm_exact_integers():
