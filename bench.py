@@ -211,16 +211,27 @@ def free_gpu():
     torch.cuda.empty_cache()
 
 
+def gemm_launch_heights(plan):
+    """Row-tile heights of the launches of one planned grouped GEMM call: a plan of 256-row tiles
+    runs as two launches (then the groups' short remainders of up to 128 rows as 128-row tiles)
+    when its workspace holds the third tile list, which it does whenever the average group has
+    85 rows or more (the library's rule: 2 * (ceil(rows/256) + G) + G <= ceil(rows/32) + G)."""
+    bm, rows, g = plan.tile_rows, plan.max_rows, plan.groups
+    mt = -(-rows // 256) + g
+    cap = -(-rows // 32) + g
+    return [256, 128] if bm == 256 and 2 * mt + g <= cap else [bm]
+
+
 def stage_kernel(stage, layer):
-    """The kernel a stage launches (the GEMM stages are one kernel each; the tile plan is part of
-    the dispatch stage)."""
+    """The kernel(s) a stage launches, joined by " + " (a grouped GEMM call is one or two launches;
+    the tile plan is part of the dispatch stage)."""
     import torch
     p2 = ", fp4" if layer.w.fp4 else ", pow2" if layer.w.pow2 else ""
     if stage == "gemm1_swiglu":
-        return f"grouped_gemm_kernel<{layer.plan.tile_rows}, swiglu_quant, packed{p2}>"
+        return " + ".join(f"grouped_gemm_kernel<{h}, swiglu_quant, packed{p2}>" for h in gemm_launch_heights(layer.plan))
     if stage == "gemm2":
         out = "bf16" if layer.act == torch.bfloat16 else "f32"
-        return f"grouped_gemm_kernel<{layer.plan.tile_rows}, store_{out}, packed{p2}>"
+        return " + ".join(f"grouped_gemm_kernel<{h}, store_{out}, packed{p2}>" for h in gemm_launch_heights(layer.plan))
     if stage == "route_quant":
         return "route_quant_kernel"
     if stage == "gate_logits":
@@ -768,7 +779,11 @@ def cpu_baseline_backward(cfg, x, dout, dev, pow2=False):
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3 counter runs
     (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's readings), or None when they were taken
-    on a different kernel source than the one built here."""
+    on a different kernel source than the one built here.  Kernels joined by " + " (one GEMM call
+    of two launches) add up, and give None if any of them has no entry."""
+    if " + " in kernel:
+        parts = [measured_traffic(k, workload) for k in kernel.split(" + ")]
+        return None if any(p is None for p in parts) else sum(parts)
     import hashlib
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
