@@ -271,6 +271,10 @@ def run_forward_workload(a, cfg, dev, steps, warmup, pow2=False, fp4=False, cpu=
 
     def step(copy, evs=None):
         lay = layers[copy]
+        if evs is None and C > 1:
+            # the stream: chunk c + 1's gate projection beside chunk c's combine (forward_chunks)
+            lay.forward_chunks(xs, outs)
+            return
         for c in range(C):
             lay.forward(xs[c], out=outs[c], events=None if evs is None else evs[c])
 

@@ -7,6 +7,8 @@ forward(x) enqueues, on the current stream and without any host synchronisation:
   scales, and the tile plan of both expert GEMMs) -> moe_grouped_gemm_fp8_gather (W1 on the rows of
   xq gathered through src_token, SwiGLU + 1x128 quantisation of h) -> moe_grouped_gemm_fp8_planned
   (W2) -> moe_combine.
+forward_chunks(xs, outs) runs independent token chunks through the same forward, each chunk's gate
+projection (after the first) on a second stream beside the previous chunk's combine.
 
 backward(x, dout, bw) enqueues the gradients of the last forward (its buffers must still hold its
 results): moe_combine_backward (dY codes, dw) -> moe_grouped_gemm_fp8 (dY, W2^T: dh) ->
@@ -187,6 +189,7 @@ class MoELayer:
         self.tile_rows = tile_rows
         self.bwd = None    # backward buffers, allocated by the first backward (or training forward)
         self.g_saved = False   # the last forward kept GEMM1's output in self.bwd["g"]
+        self._side = None      # second stream of forward_chunks (default priority), made on first use
 
     def _gemm1_a(self):
         """GEMM1's A operand: (codes, group-order scales)."""
@@ -197,7 +200,8 @@ class MoELayer:
 
     def forward(self, x: torch.Tensor, replay: Optional[torch.Tensor] = None, record: Optional[torch.Tensor] = None,
                 stream=None, events=None, fused_replay: bool = True, training: bool = False,
-                out: Optional[torch.Tensor] = None, residual_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                out: Optional[torch.Tensor] = None, residual_out: Optional[torch.Tensor] = None,
+                _gate_done: bool = False, _before_combine=None) -> torch.Tensor:
         """``events``: optional list of 7 timing events (torch.cuda.Event), recorded on the launch
         stream before the first stage and after each of the six stages (gate logits, routing with
         x's quantisation, dispatch, GEMM1, GEMM2, combine).  With ``replay`` and a
@@ -207,7 +211,9 @@ class MoELayer:
         output (default: the layer's own buffer), e.g. a chunk's rows of a longer sequence.
         ``residual_out``: the layer sits on a residual branch; the combine then writes
         act(x + output) there (it may be x itself) and returns it, and the layer output itself is
-        written only if ``out`` is given."""
+        written only if ``out`` is given.  (``_gate_done`` and ``_before_combine`` serve
+        forward_chunks: the logits of x are already in place; a call made once the second GEMM is
+        enqueued.)"""
         T = x.shape[0]
         if T != self.T_max:
             raise ValueError(f"layer buffers are sized for T={self.T_max}, got {T}")
@@ -223,7 +229,7 @@ class MoELayer:
         mark(0)
         fused = replay is not None and int(w.cfg.score_fn) == M.MOE_SCORE_SIGMOID and fused_replay
         self.logits_valid = not fused
-        if not fused:
+        if not fused and not _gate_done:
             M.moe_gate_logits(x, w.wg, w.bias, out=self.logits, stream=stream)
         mark(1)
         # routing stage: the routing decisions and x's 1x128 quantisation
@@ -255,6 +261,8 @@ class MoELayer:
         M.moe_grouped_gemm_fp8(self.hq, self.hs, self.disp.offsets, w.w2p or w.w2q, w.w2s, epilogue=M.MOE_EPI_STORE,
                                out_dtype=self.act, out=self.y, plan=plan, stream=stream, pow2=w.pow2)
         mark(5)
+        if _before_combine is not None:
+            _before_combine()
         shared_row = self.disp.offsets[w.E:w.E + 1] if w.shared else None
         if residual_out is not None:
             res = M.moe_combine_residual(self.y, self.disp.dest_row, self.wts, shared_row, x, x_next=residual_out,
@@ -265,6 +273,35 @@ class MoELayer:
         M.moe_combine(self.y, self.disp.dest_row, self.wts, shared_row, out=o, stream=stream)
         mark(6)
         return o
+
+    def forward_chunks(self, xs, outs, stream=None):
+        """Forward of independent token chunks in order (each of T_max tokens, e.g. the chunks of a
+        long sequence's prefill), chunk c's output into outs[c]; returns outs.  Chunk c + 1's gate
+        projection runs on a second stream while chunk c's combine runs: the projection is fp32
+        VALU work and the combine a stream through HBM, so they overlap, and the logits buffer the
+        projection writes has been read by chunk c's router once chunk c's second GEMM is done.
+        Chunk c + 1's router waits for both.  Every chunk's results are forward(xs[c])'s, bit for
+        bit.  Inference only: no replay, recording, training forward or residual form."""
+        main = torch.cuda.current_stream() if stream is None else stream
+        if self._side is None:
+            self._side = torch.cuda.Stream(device=self.device)
+        side, n = self._side, len(xs)
+        if len(outs) != n:
+            raise ValueError("one output per chunk")
+        gemm2_done = [torch.cuda.Event() for _ in range(n)]
+        gate_done = [torch.cuda.Event() for _ in range(n)]
+        for c in range(n):
+            hook = None
+            if c + 1 < n:
+                def hook(c=c):
+                    gemm2_done[c].record(main)
+                    side.wait_event(gemm2_done[c])
+                    M.moe_gate_logits(xs[c + 1], self.w.wg, self.w.bias, out=self.logits, stream=side)
+                    gate_done[c + 1].record(side)
+            if c > 0:
+                main.wait_event(gate_done[c])
+            self.forward(xs[c], stream=main, out=outs[c], _gate_done=c > 0, _before_combine=hook)
+        return outs
 
     def _backward_buffers(self):
         if self.bwd is not None:

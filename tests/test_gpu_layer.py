@@ -132,6 +132,42 @@ def test_layer_longctx_chunk_concatenation():
     _free()
 
 
+@pytest.mark.parametrize("name,chunks", [("decode", 5), ("longctx", 3)])
+def test_forward_chunks_equals_forward(name, chunks):
+    """forward_chunks (each chunk's gate projection after the first on a second stream, beside the
+    previous chunk's combine) gives every chunk the bits of forward(chunk): eagerly, and in a HIP
+    graph captured from it, on every replay with eager work and synchronisations in between."""
+    cfg = synth.CONFIGS[name]
+    gw = gpu_weights(cfg)
+    lay = MoELayer(gw, cfg.T, _act(cfg))
+    xs = [synth.make_x(cfg, DEV, chunk=c) for c in range(chunks)]
+    ref = [lay.forward(x).clone() for x in xs]
+    outs = [torch.full_like(r, 3.0) for r in ref]
+    lay.forward_chunks(xs, outs)
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+    for c in range(chunks):
+        assert torch.equal(bits(outs[c]), bits(ref[c])), f"eager chunk {c}"
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            lay.forward_chunks(xs, outs)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(5.0)
+        g.replay()
+        torch.cuda.synchronize()
+        for c in range(chunks):
+            assert torch.equal(bits(outs[c]), bits(ref[c])), f"replay {rep} chunk {c}"
+        lay.forward(xs[0])   # eager work on the same layer between replays
+        torch.cuda.synchronize()
+    del g, lay, gw, xs, ref, outs
+    _free()
+
+
 def _edge_payload(cfg, seed):
     """A routing payload [k, T] for router replay: slot 0 is expert 0 for every token but 7, 8
     and 9 (so group 0 has T - 3 rows and a ragged last tile), token 5 alone takes expert 1 (a
