@@ -321,7 +321,7 @@ __device__ __forceinline__ Unit unit_at(int u, int ny, const int4* __restrict__ 
 // Persistent workgroups: workgroup w takes units me(w), me(w) + G, me(w) + 2G, ... (G = grid size),
 // and its K steps over all of them form one stream: the DMA lookahead runs into the next unit while
 // the current unit's last steps and epilogue execute, so no unit pays the pipeline fill again.
-template <int BM, int EPI, bool OUT_BF16, bool PACKED, bool POW2, bool FP4 = false>
+template <int BM, int EPI, bool OUT_BF16, bool PACKED, bool POW2, bool FP4 = false, bool WNT = false>
 __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     const uint8_t* __restrict__ a, const int32_t* __restrict__ a_rows, int a_count, const float* __restrict__ as,
     const int32_t* __restrict__ offsets,
@@ -336,7 +336,9 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   constexpr int A_BYTES = T::A_BYTES, B_BYTES = T::B_BYTES, AS_W = T::AS_W;
   constexpr int WROWS = MS * 16;   // rows per wave
   constexpr int D = NSTAGE - 1;    // DMA lookahead in K steps
-  constexpr bool W_NT = BM <= 64;  // non-temporal weight loads for the short (weight-streaming) tiles
+  // non-temporal weight loads for the short (weight-streaming) tiles, and for every tile of a launch
+  // whose weight panels are each read by one tile (WNT: the short remainders of a 256-row plan)
+  constexpr bool W_NT = BM <= 64 || WNT;
   __shared__ __attribute__((aligned(1024))) uint8_t a_lds[NSTAGE][A_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t b_lds[NSTAGE][B_BYTES];
   __shared__ __attribute__((aligned(16))) float as_lds[4][AS_W];   // activation-scale ring: slot (step & 3)
@@ -828,41 +830,43 @@ int auto_tile_rows(int64_t max_rows, int groups) {
 }
 bool valid_tile_rows(int bm) { return bm == 32 || bm == 48 || bm == 64 || bm == 128 || bm == 256; }
 
-template <int BM, bool PACKED, bool POW2, bool FP4 = false>
+template <int BM, bool PACKED, bool POW2, bool FP4 = false, bool WNT = false>
 void launch3(unsigned grid, hipStream_t st, int epilogue, int out_dtype, const uint8_t* a, const int32_t* a_rows,
              int a_count, const float* as,
              const int32_t* offsets, const int4* tiles, const int32_t* ntiles, int ny, const uint8_t* b,
              const float* bs, int N, int K, void* out, float* out_scales, float* g_out) {
   if (epilogue == MOE_EPI_STORE) {
     if (out_dtype == MOE_BF16)
-      grouped_gemm_kernel<BM, 0, true, PACKED, POW2, FP4><<<grid, NTHREADS, 0, st>>>(
+      grouped_gemm_kernel<BM, 0, true, PACKED, POW2, FP4, WNT><<<grid, NTHREADS, 0, st>>>(
           a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, nullptr, nullptr);
     else
-      grouped_gemm_kernel<BM, 0, false, PACKED, POW2, FP4><<<grid, NTHREADS, 0, st>>>(
+      grouped_gemm_kernel<BM, 0, false, PACKED, POW2, FP4, WNT><<<grid, NTHREADS, 0, st>>>(
           a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, nullptr, nullptr);
   } else {
-    grouped_gemm_kernel<BM, 1, false, PACKED, POW2, FP4><<<grid, NTHREADS, 0, st>>>(
+    grouped_gemm_kernel<BM, 1, false, PACKED, POW2, FP4, WNT><<<grid, NTHREADS, 0, st>>>(
         a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K, out, out_scales, g_out);
   }
 }
 
-// b_layout: 0 row-major, 1 packed FP8, 2 packed FP4 (power-of-two scales only)
-template <int BM>
+// b_layout: 0 row-major, 1 packed FP8, 2 packed FP4 (power-of-two scales only).  WNT: every weight
+// panel of the launch is read by one tile (non-temporal weight loads; packed weights only).
+template <int BM, bool WNT = false>
 void launch(unsigned grid, hipStream_t st, int b_layout, int epilogue, int scale_mode, int out_dtype,
             const uint8_t* a, const int32_t* a_rows, int a_count, const float* as, const int32_t* offsets, const int4* tiles, const int32_t* ntiles,
             int ny, const uint8_t* b, const float* bs, int N, int K, void* out, float* out_scales, float* g_out) {
   const bool p2 = scale_mode == MOE_SCALE_POW2;
-  if constexpr (BM == 256) {
-    // 256-row tiles stream packed weights only (the host rejects row-major weights for them)
+  if constexpr (BM == 256 || WNT) {
+    // 256-row tiles, and the short remainders of a 256-row plan, stream packed weights only (the
+    // host rejects row-major weights for 256-row plans)
     if (b_layout == MOE_B_PACKED_FP4)
-      launch3<BM, true, true, true>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs,
-                                    N, K, out, out_scales, g_out);
+      launch3<BM, true, true, true, WNT>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny,
+                                         b, bs, N, K, out, out_scales, g_out);
     else if (p2)
-      launch3<BM, true, true>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N, K,
-                              out, out_scales, g_out);
+      launch3<BM, true, true, false, WNT>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny,
+                                          b, bs, N, K, out, out_scales, g_out);
     else
-      launch3<BM, true, false>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs, N,
-                               K, out, out_scales, g_out);
+      launch3<BM, true, false, false, WNT>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles,
+                                           ny, b, bs, N, K, out, out_scales, g_out);
   } else {
     if (b_layout == MOE_B_PACKED_FP4)
       launch3<BM, true, true, true>(grid, st, epilogue, out_dtype, a, a_rows, a_count, as, offsets, tiles, ntiles, ny, b, bs,
@@ -1028,9 +1032,11 @@ int run_planned(const moe_gemm_plan* plan, const uint8_t* a, const int32_t* a_ro
     launch<256>((unsigned)std::min<int64_t>(nwg, cus), st, b_layout, epilogue, scale_mode, out_dtype, a, a_rows,
                 (int)a_count, as, offsets, tiles + second, ntiles + 1, ny, b, bs, N, K, out, out_scales, g_out);
     MOE_CHECK_LAUNCH();
-    launch<SPLIT_BM>((unsigned)std::min<int64_t>((int64_t)groups * ny, cus), st, b_layout, epilogue, scale_mode,
-                     out_dtype, a, a_rows, (int)a_count, as, offsets, tiles + third, ntiles + 2, ny, b, bs, N, K, out,
-                     out_scales, g_out);
+    // each remainder is one tile, so each of its weight panels is read once: non-temporal weight
+    // loads (same box: store GEMM -2% on the long-context stream and at prefill)
+    launch<SPLIT_BM, true>((unsigned)std::min<int64_t>((int64_t)groups * ny, cus), st, b_layout, epilogue, scale_mode,
+                           out_dtype, a, a_rows, (int)a_count, as, offsets, tiles + third, ntiles + 2, ny, b, bs, N, K,
+                           out, out_scales, g_out);
     MOE_CHECK_LAUNCH();
     return MOE_OK;
   }
