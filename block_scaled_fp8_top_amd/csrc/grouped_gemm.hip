@@ -264,6 +264,21 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
   if (threadIdx.x == 0) ntiles[2] = n3;
 }
 
+// wait until M * v of this wave's vector memory instructions are outstanding, v one of LO .. HI:
+// a short chain of compares for the few counts a loop meets in its steady state
+template <int M, int LO, int HI>
+__device__ __forceinline__ void wait_vm_steady(int v) {
+  if constexpr (M == 0 || LO >= HI) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(M * LO < 63 ? M * LO : 63) : "memory");
+  } else {
+    if (v == LO) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(M * LO < 63 ? M * LO : 63) : "memory");
+      return;
+    }
+    wait_vm_steady<M, LO + 1, HI>(v);
+  }
+}
+
 // wait until at most n of this wave's vector memory instructions are outstanding (n is
 // wave-uniform; s_waitcnt takes an immediate)
 __device__ __forceinline__ void wait_vm(int n) {
@@ -379,6 +394,12 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
   const bool bscale_loader = wave == 8 - T::DW;
   const int per_stage =
       dma_wave ? (has_a ? T::A_PW : 0) + B_PW + (scale_loader ? 1 : 0) + (bscale_loader ? 1 : 0) : 0;
+  // the outstanding count of a steady-state step, per_stage * (D - 1), and the range of per_stage
+  // over the waves (every wave issues DMA; A only when the slice has an instruction for it; one
+  // scale load each for some waves)
+  const int steady = per_stage * (D - 1);
+  constexpr int PS_LO = (T::A_INSTR >= T::DW ? T::A_PW : 0) + B_PW, PS_HI = T::A_PW + B_PW + 2;
+  static_assert(T::DW == 8, "every wave issues DMA");
 
   // issue-side context of the unit whose steps are being issued: 32-bit byte offsets from a and
   // from the unit's group weights (both < 2^32 for every accepted shape); rows past the tile's end
@@ -553,7 +574,11 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(
     int later = per_stage * min(D - 1, total - 1 - s);
 #pragma unroll
     for (int j = 0; j < D; ++j) later += recent[j];
-    wait_vm(min(later, 63));
+    // the steady state (no epilogue stores in flight, not the last steps) meets one count per
+    // wave, per_stage * (D - 1): a short path for it; the 64-way switch compiles to a tree of
+    // compares and branches that every step would otherwise walk
+    if (later == steady && steady <= 63) wait_vm_steady<D - 1, PS_LO, PS_HI>(per_stage);
+    else wait_vm(min(later, 63));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
