@@ -305,16 +305,20 @@ __global__ __launch_bounds__(64) void gate_logits_chain_kernel(const void* __res
 
 // ------------------------------------------------------------------------------------------------
 // Many tokens, E of 64, 128 or 256, H a multiple of 32: x broadcast within 16-lane rows.
-// A wavefront owns TT tokens and every expert (lane l: experts l, l + 64, ..., TE = E / 64 of them),
-// so a Wg value read from LDS serves TT fmas (the tile kernel above reads an x value and a Wg value
-// from LDS for every TT x TE tile, twice the LDS bytes per fma at TT = TE = 4).  The x of a 32-column
+// A wavefront owns TT tokens and a slice of 64 TE experts (workgroup column blockIdx.y: experts
+// e0 = 64 TE blockIdx.y onwards; lane l: experts e0 + l, e0 + l + 64, ...), so a Wg value read from
+// LDS serves TT fmas (the tile kernel above reads an x value and a Wg value from LDS for every
+// TT x TE tile, twice the LDS bytes per fma at TT = TE = 4).  The x of a 32-column
 // chunk sits in two registers per token, lane 16 r + k holding columns 2k and 2k + 1, and the fma of
 // column h takes it from lane h / 2 of the lane's own row through a DPP row broadcast
 // (row_newbcast) fused into the fma, v_fmac_f32_dpp.  Chunks of Wg (E rows of 128 bytes, 16-byte
 // pieces XOR-swizzled by row so that eight rows' reads of one piece hit distinct banks) and of raw x
 // are copied global -> LDS by DMA (global_load_lds) into two buffers, one chunk ahead of the chain
 // (a deeper ring for x, which is read once from HBM, measured no faster).  Workgroup: NW wavefronts,
-// NW TT tokens.
+// NW TT tokens, one expert slice.  Slices of 128 experts (TE = 2) rather than all 256 keep the
+// workgroup's LDS at 34 KB, so four workgroups (16 wavefronts) share a CU; at 8192 tokens, H 6144,
+// 256 experts and bf16 x that measured 420 us against 446 us for whole-E workgroups (TE = 4), and
+// 423-438 us for 8 or 16 tokens per wavefront over 128 or 64 experts.
 //
 // A DPP source register needs two wait states after a VALU instruction writes it, which the
 // compiler does not insert for inline assembly: the widened x registers pass through an s_nop 1
@@ -360,8 +364,10 @@ template <int TT, int TE, int NW, bool BF16>
 __global__ __launch_bounds__(NW * 64) void gate_logits_bcast_kernel(const void* __restrict__ xv,
                                                                   const float* __restrict__ wg,
                                                                   const float* __restrict__ bias, int64_t T, int H,
-                                                                  float* __restrict__ z) {
-  constexpr int E = 64 * TE, BT = NW * TT;
+                                                                  int EALL, float* __restrict__ z) {
+  constexpr int E = 64 * TE, BT = NW * TT;   // E: experts of this workgroup's slice (of EALL)
+  const int e0 = blockIdx.y * E;
+  wg += (int64_t)e0 * H;
   constexpr int XB = BF16 ? 2 : 4;                    // bytes per x value
   constexpr int WBUF = E * BC_HC * 4;                 // bytes of a Wg chunk
   constexpr int XBUF = BT * BC_HC * XB;               // bytes of an x chunk
@@ -448,22 +454,22 @@ __global__ __launch_bounds__(NW * 64) void gate_logits_bcast_kernel(const void* 
     if (t >= T) continue;
 #pragma unroll
     for (int j = 0; j < TE; ++j) {
-      const int e = lane + 64 * j;
+      const int e = e0 + lane + 64 * j;
       float v = acc[i][j];
       if (bias) v = v + bias[e];
-      z[t * E + e] = v;
+      z[t * EALL + e] = v;
     }
   }
 }
 
 template <int TT, int TE, int NW>
-int launch_bcast(const void* x, bool bf16, const float* wg, const float* bias, int64_t T, int H, float* z,
+int launch_bcast(const void* x, bool bf16, const float* wg, const float* bias, int64_t T, int H, int E, float* z,
                  hipStream_t st) {
-  const unsigned grid = (unsigned)ceil_div64(T, NW * TT);
+  const dim3 grid((unsigned)ceil_div64(T, NW * TT), (unsigned)(E / (64 * TE)));
   if (bf16)
-    gate_logits_bcast_kernel<TT, TE, NW, true><<<grid, NW * 64, 0, st>>>(x, wg, bias, T, H, z);
+    gate_logits_bcast_kernel<TT, TE, NW, true><<<grid, NW * 64, 0, st>>>(x, wg, bias, T, H, E, z);
   else
-    gate_logits_bcast_kernel<TT, TE, NW, false><<<grid, NW * 64, 0, st>>>(x, wg, bias, T, H, z);
+    gate_logits_bcast_kernel<TT, TE, NW, false><<<grid, NW * 64, 0, st>>>(x, wg, bias, T, H, E, z);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -471,11 +477,9 @@ int launch_bcast(const void* x, bool bf16, const float* wg, const float* bias, i
 template <int TT, int NW>
 int launch_bcast_e(const void* x, bool bf16, const float* wg, const float* bias, int64_t T, int H, int E, float* z,
                    hipStream_t st) {
-  switch (E) {
-    case 64: return launch_bcast<TT, 1, NW>(x, bf16, wg, bias, T, H, z, st);
-    case 128: return launch_bcast<TT, 2, NW>(x, bf16, wg, bias, T, H, z, st);
-    default: return launch_bcast<TT, 4, NW>(x, bf16, wg, bias, T, H, z, st);
-  }
+  // slices of 128 experts where E allows (E = 128 or 256), else one slice of 64
+  if (E == 64) return launch_bcast<TT, 1, NW>(x, bf16, wg, bias, T, H, E, z, st);
+  return launch_bcast<TT, 2, NW>(x, bf16, wg, bias, T, H, E, z, st);
 }
 
 template <int TT, int TE>
@@ -517,10 +521,11 @@ extern "C" int moe_gate_logits(const void* x, int x_dtype, const float* wg, cons
   const int64_t wg22 = ceil_div64(T, 32) * ceil_div64(E, 32);
   if (wg84 >= 512) return launch<8, 4>(x, bf16, wg, bias, T, H, E, logits, st);
   // Below that, the x-broadcast kernel (4 tokens per wavefront, 4 wavefronts and a ring of two
-  // chunks per workgroup, so two workgroups share a CU) where its shape rules allow.  Measured at
-  // 8192 tokens, H 6144, 256 experts, bf16 x: 442 us against 483 us for the 4 x 4 tiles.  The 8 x 4
-  // tiles above stay ahead where they fill the chip (728 us against 804 us at 16384 tokens): their
-  // plain fmas issue faster than the DPP-fused ones, and 32 accumulators per thread hide more.
+  // chunks per workgroup, expert slices of 128, so four workgroups share a CU) where its shape rules
+  // allow.  Measured at 8192 tokens, H 6144, 256 experts, bf16 x: 420 us against 481 us for the
+  // 4 x 4 tiles and 571 us for the 8 x 4 tiles.  The 8 x 4 tiles above stay ahead where they fill
+  // the chip (732 us against 799 us at 16384 tokens): their plain fmas issue faster than the
+  // DPP-fused ones, and 32 accumulators per thread hide more.
   if (E % 64 == 0 && E <= 256 && H % BC_HC == 0 && T >= 8192)
     return launch_bcast_e<4, 4>(x, bf16, wg, bias, T, H, E, logits, st);
   if (wg44 >= 512) return launch<4, 4>(x, bf16, wg, bias, T, H, E, logits, st);

@@ -74,5 +74,5 @@ def test_gate_logits_dpp_sources_settled():
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-2000:]
     count, found = dpp_hazards(r.stdout)
-    assert count >= 3 * 2 * 128, count   # the broadcast kernels are all there (E 64/128/256, bf16/fp32)
+    assert count >= 2 * (128 + 256), count   # the broadcast kernels are all there (slices of 64 and 128 experts, bf16/fp32)
     assert not found, found[:5]
