@@ -4,7 +4,8 @@
 //   1. count:   the T*k slots are cut into chunks of CHUNK; each chunk's expert histogram goes to
 //               the workspace (LDS integer atomics: exact counts, order-free).
 //   2. scan:    one workgroup turns the per-chunk histograms into expert totals, the exclusive
-//               prefix `offsets`, and each chunk's starting row per expert.
+//               prefix `offsets`, and each chunk's starting row per expert (and, when asked, the
+//               grouped GEMM's tile lists).
 //   3. scatter: one wavefront per chunk walks its slots in order, 64 at a time; lanes holding the
 //               same expert find each other with ballots over the bits of the expert id, so each
 //               slot's row is (chunk base) + (earlier slots of the chunk with that expert) --
@@ -23,6 +24,98 @@ namespace {
 constexpr int CHUNK = 1024;   // slots per chunk
 constexpr int MAXE = 1024;
 
+// Inclusive scan of v over the 1024 threads of the workgroup (integers: the order of the additions
+// does not matter): a shuffle scan within each wavefront, then each wavefront adds the totals of
+// the wavefronts before it.  wsum: 16 ints of LDS.  Every thread calls it.
+__device__ __forceinline__ int block_scan_1024(int v, int* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int add = 0;
+  for (int w = 0; w < wave; ++w) add += wsum[w];
+  __syncthreads();   // wsum may be written again by the next call
+  return x + add;
+}
+
+// The grouped GEMM's tile lists for row tiles of bm, written by one workgroup of 1024 threads that
+// has the expert totals: thread e < E holds total = expert e's rows, part[] the inclusive block scan
+// of the totals over e, routed = part[E - 1]; the shared expert (append_shared) is group E with T
+// rows.  The entries are those the plan kernel of the grouped GEMM writes: {group, first row, the
+// block's first tile, the block's tile count}, at most max_tiles of them, and their number into
+// ntiles[0]; with second != 0 the second list at tiles + second (every group's full tiles first,
+// then the groups' short last tiles; with third != 0 only those over 128 rows) into ntiles[1], and
+// with third != 0 the third list at tiles + third (one 128-row tile per short remainder of 1 .. 128
+// rows) into ntiles[2].  Needs E + append_shared <= 1024.  tpart[16] and first[1025] are LDS
+// scratch.
+__device__ __forceinline__ void write_tile_lists(int tid, int E, int T, int append_shared, int total,
+                                                 const int* part, int routed, int bm, int4* __restrict__ tiles,
+                                                 int32_t* __restrict__ ntiles, int max_tiles, int second, int third,
+                                                 int* tpart, int* first) {
+  // tile plan: group g has ceil(rows / bm) tiles; a block scan gives each group's first tile, then
+  // every thread writes tiles, finding a tile's group by binary search over the first tiles
+  const int G = E + (append_shared ? 1 : 0);
+  const int rows_g = tid < E ? total : (tid == E && append_shared ? T : 0);
+  // first[0 .. G]: exclusive block scan over the groups of v (this thread's group's count)
+  auto scan_first = [&](int v) {
+    const int incl = block_scan_1024(v, tpart);
+    if (tid < G) first[tid] = incl - v;
+    if (tid == G - 1) first[G] = incl;
+    __syncthreads();
+  };
+  // the group owning position t: the last group whose first position is at or before t
+  auto owner = [&](int t) {
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (first[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
+  auto row_of = [&](int g) { return g < E ? (g == 0 ? 0 : part[g - 1]) : routed; };
+  scan_first((rows_g + bm - 1) / bm);
+  const int ntot = min(first[G], max_tiles);
+  for (int t = tid; t < ntot; t += 1024) {
+    const int lo = owner(t);
+    tiles[t] = make_int4(lo, row_of(lo) + (t - first[lo]) * bm, first[lo], first[lo + 1] - first[lo]);
+  }
+  if (tid == 0) *ntiles = ntot;
+  if (!second) return;
+  __syncthreads();
+  scan_first(rows_g / bm);                       // full tiles first
+  const int nfull = first[G];
+  for (int t = tid; t < min(nfull, ntot); t += 1024) {
+    const int lo = owner(t);
+    tiles[second + t] = make_int4(lo, row_of(lo) + (t - first[lo]) * bm, first[lo], first[lo + 1] - first[lo]);
+  }
+  __syncthreads();
+  // then every group's short last tile (with a third list, only those over 128 rows)
+  scan_first(rows_g % bm > (third ? 128 : 0) ? 1 : 0);
+  const int n2 = min(nfull + first[G], ntot);
+  for (int t = nfull + tid; t < n2; t += 1024) {
+    const int lo = owner(t - nfull);
+    const int g_rows = lo < E ? row_of(lo + 1) - row_of(lo) : T;
+    tiles[second + t] = make_int4(lo, row_of(lo) + (g_rows / bm) * bm, t, 1);
+  }
+  if (tid == 0) ntiles[1] = n2;
+  if (!third) return;
+  __syncthreads();
+  scan_first(rows_g % bm > 0 && rows_g % bm <= 128 ? 1 : 0);   // the third list: short remainders
+  const int n3 = first[G];
+  for (int t = tid; t < n3; t += 1024) {
+    const int lo = owner(t);
+    const int g_rows = lo < E ? row_of(lo + 1) - row_of(lo) : T;
+    tiles[third + t] = make_int4(lo, row_of(lo) + (g_rows / bm) * bm, t, 1);
+  }
+  if (tid == 0) ntiles[2] = n3;
+}
+
 __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ idx, int64_t nslots, int E,
                                                     int32_t* __restrict__ chunk_counts) {
   __shared__ int hist[MAXE];
@@ -40,11 +133,16 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
   for (int e = threadIdx.x; e < E; e += 256) chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
-// one workgroup of 1024 threads; thread e owns expert e
+// one workgroup of 1024 threads; thread e owns expert e.  With tiles != NULL it also writes the
+// grouped GEMM's tile lists (write_tile_lists), so no plan kernel has to read the offsets back.
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ chunk_counts, int nchunks, int E,
                                                     int append_shared, int64_t T, int32_t* __restrict__ chunk_base,
-                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                    int bm, int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                                    int max_tiles, int second, int third) {
   __shared__ int part[1024];
+  __shared__ int tpart[16];
+  __shared__ int first[1025];
   const int e = threadIdx.x;
   // expert e's total over the chunks: 16 independent loads in flight per step (a load-add chain
   // over 128 chunks would cost 128 memory round trips)
@@ -60,15 +158,9 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
     }
     for (; c < nchunks; ++c) total += chunk_counts[(int64_t)c * E + e];
   }
-  // inclusive block scan of totals over e (Hillis-Steele; integers, so order does not matter)
-  part[e] = total;
+  // inclusive block scan of totals over e
+  part[e] = block_scan_1024(total, tpart);
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int v = e >= o ? part[e - o] : 0;
-    __syncthreads();
-    part[e] += v;
-    __syncthreads();
-  }
   const int excl = part[e] - total;
   if (e < E) {
     counts[e] = total;
@@ -91,14 +183,17 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
       run += v;
     }
   }
+  const int routed = part[E - 1];
   if (e == 0) {
-    const int routed = part[E - 1];
     offsets[E] = routed;
     if (append_shared) {
       counts[E] = (int32_t)T;
       offsets[E + 1] = routed + (int32_t)T;
     }
   }
+  if (tiles)
+    write_tile_lists(e, E, (int)T, append_shared, total, part, routed, bm, tiles, ntiles, max_tiles, second, third,
+                     tpart, first);
 }
 
 template <int BITS>
@@ -166,30 +261,21 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint8_t* __restrict_
   }
 }
 
-// Scales only (the grouped GEMM gathers the codes through src_token): 16 lanes per row, 16-byte
-// pieces (H % 512 == 0, so a row's H/128 scales are whole pieces), 4 rows per wavefront, and each
-// lane's source rows looked up before any copy, so several rows' loads are in flight at once.
-constexpr int PS_ROWS = 4;   // rows per 16-lane group
+// Scales only (the grouped GEMM gathers the codes through src_token): one thread per (row, 16-byte
+// piece of the row's H/128 scales; H % 512 == 0), a row's pieces on consecutive threads.  Measured
+// at 65536 rows, H 6144: 4.5 us, against 18.3 us with 16 lanes per row and 4 rows per lane group.
 __global__ __launch_bounds__(256) void permute_scales_kernel(const float* __restrict__ xs, int H,
                                                              const int32_t* __restrict__ src_token,
                                                              const int32_t* __restrict__ total_rows, int64_t max_rows,
                                                              float* __restrict__ as) {
   const int64_t rows = min((int64_t)*total_rows, max_rows);
-  const int sub = threadIdx.x & 15;
   const int np = H / 512;   // 16-byte pieces per row
-  const int64_t r0 = ((int64_t)blockIdx.x * 16 + threadIdx.x / 16) * PS_ROWS;
-  int64_t t[PS_ROWS];
-#pragma unroll
-  for (int i = 0; i < PS_ROWS; ++i) t[i] = r0 + i < rows ? src_token[r0 + i] : -1;
-  for (int c = sub; c < np; c += 16) {
-    float4 v[PS_ROWS];
-#pragma unroll
-    for (int i = 0; i < PS_ROWS; ++i)
-      if (t[i] >= 0) v[i] = reinterpret_cast<const float4*>(xs + t[i] * (H / 128))[c];
-#pragma unroll
-    for (int i = 0; i < PS_ROWS; ++i)
-      if (t[i] >= 0) reinterpret_cast<float4*>(as + (r0 + i) * (H / 128))[c] = v[i];
-  }
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r = i / np;
+  if (r >= rows) return;
+  const int c = (int)(i - r * np);
+  const int64_t t = src_token[r];
+  reinterpret_cast<float4*>(as + r * (H / 128))[c] = reinterpret_cast<const float4*>(xs + t * (H / 128))[c];
 }
 
 constexpr int SMALL_MAX = 8192;       // slots
@@ -220,7 +306,7 @@ __global__ __launch_bounds__(1024) void small_dispatch_kernel(const int32_t* __r
   __shared__ uint8_t srank[SMALL_MAX];
   __shared__ int cnt[SMALL_CNT];      // [piece][e]
   __shared__ int part[1024];
-  __shared__ int tpart[1024];
+  __shared__ int tpart[16];
   __shared__ int first[1025];         // tile plan: the groups' first tiles, first[G] = all tiles
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int npiece = (nslots + 63) / 64;
@@ -256,14 +342,8 @@ __global__ __launch_bounds__(1024) void small_dispatch_kernel(const int32_t* __r
       total += c;
     }
   }
-  part[tid] = total;
+  part[tid] = block_scan_1024(total, tpart);
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
   const int routed = part[E - 1];
   if (tid < E) {
     counts[tid] = total;
@@ -287,71 +367,9 @@ __global__ __launch_bounds__(1024) void small_dispatch_kernel(const int32_t* __r
   }
   if (append_shared)
     for (int t = tid; t < T; t += 1024) src_token[routed + t] = t;
-  if (!tiles) return;
-  // tile plan: group g has ceil(rows / bm) tiles; a block scan gives each group's first tile, then
-  // every thread writes tiles, finding a tile's group by binary search over the first tiles
-  const int G = E + (append_shared ? 1 : 0);
-  const int rows_g = tid < E ? total : (tid == E && append_shared ? T : 0);
-  // first[0 .. G]: exclusive block scan over the groups of v (this thread's group's count)
-  auto scan_first = [&](int v) {
-    tpart[tid] = v;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {
-      const int u = tid >= o ? tpart[tid - o] : 0;
-      __syncthreads();
-      tpart[tid] += u;
-      __syncthreads();
-    }
-    if (tid < G) first[tid] = tpart[tid] - v;
-    if (tid == 0) first[G] = tpart[G - 1];
-    __syncthreads();
-  };
-  // the group owning position t: the last group whose first position is at or before t
-  auto owner = [&](int t) {
-    int lo = 0, hi = G - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (first[mid] <= t) lo = mid;
-      else hi = mid - 1;
-    }
-    return lo;
-  };
-  auto row_of = [&](int g) { return g < E ? (g == 0 ? 0 : part[g - 1]) : routed; };
-  scan_first((rows_g + bm - 1) / bm);
-  const int ntot = min(first[G], max_tiles);
-  for (int t = tid; t < ntot; t += 1024) {
-    const int lo = owner(t);
-    tiles[t] = make_int4(lo, row_of(lo) + (t - first[lo]) * bm, first[lo], first[lo + 1] - first[lo]);
-  }
-  if (tid == 0) *ntiles = ntot;
-  if (!second) return;
-  __syncthreads();
-  scan_first(rows_g / bm);                       // full tiles first
-  const int nfull = first[G];
-  for (int t = tid; t < min(nfull, ntot); t += 1024) {
-    const int lo = owner(t);
-    tiles[second + t] = make_int4(lo, row_of(lo) + (t - first[lo]) * bm, first[lo], first[lo + 1] - first[lo]);
-  }
-  __syncthreads();
-  // then every group's short last tile (with a third list, only those over 128 rows)
-  scan_first(rows_g % bm > (third ? 128 : 0) ? 1 : 0);
-  const int n2 = min(nfull + first[G], ntot);
-  for (int t = nfull + tid; t < n2; t += 1024) {
-    const int lo = owner(t - nfull);
-    const int g_rows = lo < E ? row_of(lo + 1) - row_of(lo) : T;
-    tiles[second + t] = make_int4(lo, row_of(lo) + (g_rows / bm) * bm, t, 1);
-  }
-  if (tid == 0) ntiles[1] = n2;
-  if (!third) return;
-  __syncthreads();
-  scan_first(rows_g % bm > 0 && rows_g % bm <= 128 ? 1 : 0);   // the third list: short remainders
-  const int n3 = first[G];
-  for (int t = tid; t < n3; t += 1024) {
-    const int lo = owner(t);
-    const int g_rows = lo < E ? row_of(lo + 1) - row_of(lo) : T;
-    tiles[third + t] = make_int4(lo, row_of(lo) + (g_rows / bm) * bm, t, 1);
-  }
-  if (tid == 0) ntiles[2] = n3;
+  if (tiles)
+    write_tile_lists(tid, E, T, append_shared, total, part, routed, bm, tiles, ntiles, max_tiles, second, third,
+                     tpart, first);
 }
 
 int64_t nchunks_for(int64_t T, int k) { return ceil_div64(T * k, CHUNK); }
@@ -369,8 +387,9 @@ int moe_plan_host(int32_t groups, int64_t max_rows, int32_t tile_rows, void* wor
 
 namespace {
 
-// The dispatch; with plan_ws != NULL and the one-workgroup path taken, that workgroup also writes
-// the tile list of plan_bm-row tiles into plan_ws (*planned is then set).
+// The dispatch; with plan_ws != NULL (and at most 1024 groups) its one-workgroup kernel -- the small
+// path's kernel, else the scan -- also writes the tile lists of plan_bm-row tiles into plan_ws
+// (*planned is then set).
 int dispatch_impl(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_t append_shared,
                   const uint8_t* xq, const float* xs, int32_t H, int32_t* counts, int32_t* offsets,
                   int32_t* dest_row, int32_t* src_token, uint8_t* aq, float* as, void* workspace,
@@ -393,14 +412,17 @@ int dispatch_impl(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int3
   const int64_t nslots = T * k;
   int bits = 1;
   while ((1 << bits) < E) ++bits;
-  if (nslots <= SMALL_MAX && ceil_div64(nslots, 64) * E <= SMALL_CNT) {
-    const bool plan_here = plan_ws && E + (append_shared ? 1 : 0) <= 1024 && plan_max_tiles <= INT32_MAX;
-    int4* ptiles = plan_here ? reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan_ws) + 256) : nullptr;
-    int32_t* pntiles = plan_here ? reinterpret_cast<int32_t*>(plan_ws) : nullptr;
-    const int64_t second = plan_here ? moe_plan_second_list(nslots + (append_shared ? T : 0),
-                                                            E + (append_shared ? 1 : 0), plan_bm) : 0;
-    const int64_t third = plan_here ? moe_plan_third_list(nslots + (append_shared ? T : 0),
+  // the tile plan is written by the dispatch's own one-workgroup kernel (the small path's, else
+  // the scan) when the groups fit its 1024 threads
+  const bool plan_here = plan_ws && E + (append_shared ? 1 : 0) <= 1024 && plan_max_tiles <= INT32_MAX &&
+                         nslots + (append_shared ? T : 0) <= INT32_MAX;
+  int4* ptiles = plan_here ? reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan_ws) + 256) : nullptr;
+  int32_t* pntiles = plan_here ? reinterpret_cast<int32_t*>(plan_ws) : nullptr;
+  const int64_t second = plan_here ? moe_plan_second_list(nslots + (append_shared ? T : 0),
                                                           E + (append_shared ? 1 : 0), plan_bm) : 0;
+  const int64_t third = plan_here ? moe_plan_third_list(nslots + (append_shared ? T : 0),
+                                                        E + (append_shared ? 1 : 0), plan_bm) : 0;
+  if (nslots <= SMALL_MAX && ceil_div64(nslots, 64) * E <= SMALL_CNT) {
     switch (bits) {
 #define CASE_SMALL(B)                                                                                   \
   case B:                                                                                               \
@@ -421,8 +443,10 @@ int dispatch_impl(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int3
     count_kernel<<<(unsigned)nch, 256, 0, st>>>(topk_idx, nslots, E, chunk_counts);
     MOE_CHECK_LAUNCH();
   }
-  scan_kernel<<<1, 1024, 0, st>>>(chunk_counts, (int)nch, E, append_shared, T, chunk_base, counts, offsets);
+  scan_kernel<<<1, 1024, 0, st>>>(chunk_counts, (int)nch, E, append_shared, T, chunk_base, counts, offsets, plan_bm,
+                                  ptiles, pntiles, (int)plan_max_tiles, (int)second, (int)third);
   MOE_CHECK_LAUNCH();
+  *planned = plan_here;
   if (nch > 0) {
     const unsigned g = (unsigned)nch;
     switch (bits) {
@@ -443,8 +467,8 @@ int dispatch_impl(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int3
   if (copy_rows && T > 0) {
     const int G = E + (append_shared ? 1 : 0);
     const int64_t max_rows = nslots + (append_shared ? T : 0);
-    if (!aq && H % 512 == 0 && ceil_div64(max_rows, 16 * PS_ROWS) <= INT32_MAX) {
-      const int64_t grid = ceil_div64(max_rows, 16 * PS_ROWS);
+    if (!aq && H % 512 == 0 && ceil_div64(max_rows * (H / 512), 256) <= INT32_MAX) {
+      const int64_t grid = ceil_div64(max_rows * (H / 512), 256);
       permute_scales_kernel<<<(unsigned)grid, 256, 0, st>>>(xs, H, src_token, offsets + G, max_rows, as);
     } else {
       const int64_t grid = std::min<int64_t>(ceil_div64(max_rows, 4), 65536);
