@@ -292,10 +292,10 @@ int moe_grouped_gemm_fp8_planned(const moe_gemm_plan* plan, const uint8_t* a, co
 
 /* Dispatch and tile plan in one call: moe_dispatch (same arguments and outputs) followed by
  * moe_grouped_gemm_plan(offsets, G, max_rows = T*k + (append_shared ? T : 0), tile_rows,
- * gemm_workspace, ...) for the G = E + (append_shared ? 1 : 0) groups it produces.  When the batch is
- * small enough for the one-workgroup dispatch (decode) and G <= 1024, that workgroup also writes the
- * tile list, which saves the plan's own launch; otherwise the plan kernel runs after the dispatch.
- * The plan is the same either way.
+ * gemm_workspace, ...) for the G = E + (append_shared ? 1 : 0) groups it produces.  With G <= 1024
+ * the dispatch's own one-workgroup kernel (the whole dispatch for decode-sized batches, else the
+ * scan of the chunk histograms) also writes the tile lists, which saves the plan's own launch;
+ * otherwise the plan kernel runs after the dispatch.  The plan is the same either way.
  * Errors: as moe_dispatch and moe_grouped_gemm_plan. */
 int moe_dispatch_plan(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_t append_shared,
                       const uint8_t* xq, const float* xs, int32_t H, int32_t* counts, int32_t* offsets,
