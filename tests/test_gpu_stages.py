@@ -422,11 +422,13 @@ def test_dispatch_small_and_chunked_paths(T, k, E):
                                            (0, 6, 64, False), (2048, 8, 256, True),
                                            (3, 2, 1023, True), (4, 2, 1024, True),    # G = 1024, 1025
                                            (1024, 8, 16, True), (1000, 8, 24, False),   # one workgroup, all lists
-                                           (4096, 8, 64, False)])                      # plan kernel, all lists
+                                           (4096, 8, 64, False), (4096, 8, 8, True),   # chunked: the scan writes them
+                                           (200, 8, 1023, True), (200, 8, 1024, True)])  # chunked, G = 1024, 1025
 def test_dispatch_plan_equals_separate_plan(T, k, E, shared):
     """moe_dispatch_plan: the same dispatch outputs as moe_dispatch and the same tile list (every
-    entry and the count) as moe_grouped_gemm_plan, for each tile height; the one-workgroup path
-    writes the plan itself, the chunked path (16384 slots) falls back to the plan kernel."""
+    entry and the count) as moe_grouped_gemm_plan, for each tile height.  The dispatch's own
+    one-workgroup kernel writes the plan (the whole dispatch for small batches, else the scan of the
+    chunk histograms) up to 1024 groups; with more, the plan kernel runs after the dispatch."""
     rng = np.random.default_rng(T + E)
     idx = torch.from_numpy(rng.integers(0, E, size=(T, k)).astype(np.int32)).to(DEV)
     H = 256
