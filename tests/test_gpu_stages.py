@@ -142,13 +142,14 @@ def test_gate_logits(name):
                                     (16383, 136, 260),   # 8x4 tiles, ragged T, E and last chunk
                                     (8200, 160, 64),     # x broadcast: 1 expert per lane, 5 chunks
                                     (8193, 96, 128),     # x broadcast: 2 per lane, 1 token in the last workgroup
-                                    (12007, 224, 256),   # x broadcast: 4 per lane, 7 chunks, ragged
+                                    (12007, 224, 256),   # x broadcast: 2 per lane, two 128-expert slices, 7 chunks
                                     (8192, 32, 256),     # x broadcast: one chunk
                                     (8250, 64, 512)])    # 512 experts: 8x4 tiles
 def test_gate_logits_ragged_all_paths(T, H, E):
     """T and E not multiples of the register tiles, H not a multiple of the LDS chunk; fp32 and bf16.
     From 8192 tokens with E of 64, 128 or 256 and H a multiple of 32 (below the 8x4 tiles' size),
-    the x-broadcast kernel runs: ragged last workgroups, 1-4 experts per lane, one to seven chunks."""
+    the x-broadcast kernel runs: ragged last workgroups, slices of 64 or 128 experts (1 or 2 per
+    lane, one or two slices), one to seven chunks."""
     x = synth.randn((T, H), 6, synth.STAGE, part=31, device=DEV)
     wg = synth.randn((E, H), 6, synth.STAGE, part=32, device=DEV, std=0.1)
     b = synth.randn((E,), 6, synth.STAGE, part=33, device=DEV)
