@@ -664,6 +664,33 @@ def test_grouped_gemm_exact_integers():
             [ai[offsets[g]:offsets[g + 1]].numpy() @ bi[g].numpy().T for g in range(G)]))
 
 
+def test_grouped_gemm_exact_integers_bf16_out():
+    """The bf16 store epilogue (the tile staged through LDS in rounds of up to 64 rows, each row
+    stored as one contiguous piece) on the exact-integer case with N = 384, whose second weight
+    panel has only 128 valid columns: every value equals the exact result rounded to bf16 (round to
+    nearest even), for every tile height, so no column past N is written (it would land in the next
+    row) and no row past a group's end."""
+    offsets = np.array([0, 130, 130, 131, 400, 657, 1357], np.int64)   # a 700-row group: 256-row units
+    G, N, K = 6, 384, 512
+    rows = int(offsets[-1])
+    a, ai = synth.integer_codes((rows, K), 61, 0, device=DEV)
+    b, bi = synth.integer_codes((G, N, K), 61, 1, device=DEV)
+    as_ = torch.full((rows, K // 128), 0.5, dtype=torch.float32, device=DEV)
+    bs = torch.full((G, N // 128, K // 128), 4.0, dtype=torch.float32, device=DEV)
+    goff = torch.from_numpy(offsets.astype(np.int32)).to(DEV)
+    exact = 2.0 * np.concatenate([ai[offsets[g]:offsets[g + 1]].numpy().astype(np.int64) @
+                                  bi[g].numpy().astype(np.int64).T for g in range(G)])
+    want = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+    packed = M.moe_pack_weights_fp8(b, M.MOE_EPI_STORE)
+    for tile in TILES:
+        for bw in (b, packed):
+            if tile == 256 and isinstance(bw, torch.Tensor):
+                continue                                              # 256-row tiles: packed weights only
+            y = M.moe_grouped_gemm_fp8(a, as_, goff, bw, bs, M.MOE_EPI_STORE, torch.bfloat16, tile_rows=tile)
+            assert_equal(f"exact integer GEMM, bf16 out (tile {tile}, {type(bw).__name__})",
+                         host(y.view(torch.int16)), want)
+
+
 def _expected_pack(b: np.ndarray, epi: int) -> np.ndarray:
     """The packed layout written out: block (g, panel, K step) = 2048 units of 16 bytes; unit
     64 i + L holds 16-byte chunk 2 (L // 16) + i % 2 of panel row r = 16 (i // 2) + L % 16."""
